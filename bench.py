@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the Nyström self-attention forward on one MI355X.
+
+One step = one ``nystrom_attn_fwd`` call over a whole batch (segment means,
+landmark softmaxes, pseudoinverse, B~V, W, output with the conv skip).  The
+default workload is batch 2 x 12 heads, n = 8192, d = 64, m = 64, bf16 I/O,
+6 iterations, conv kernel 33.
+
+Inputs are seeded synthetic tensors already resident in HBM.  The timed steps
+rotate over several independent input/output sets whose total exceeds the
+256 MB last-level cache, so every call reads its inputs from HBM.
+
+Prints one JSON line.  ``value`` is tokens/s (batch * n per step).
+``roofline`` is for the kernel with the largest share of GPU time: its
+algorithmic bytes per launch divided by its mean duration, timed with HIP
+events that the library records on the launch stream.  ``cpu_baseline`` is
+the fp64 CPU oracle timed on the host on whole calls of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, TFLOP/s
+METRIC = "Nyström attention fwd tokens/s at n=8192,m=64,d=64; % of HBM roofline"
+
+# Context from the paper's efficiency table (GTX 1080Ti, self-attention module
+# only, random inputs, precision and head shape not stated): at n = 8192 the
+# 64-landmark variant took 12.3 ms and 450 MB against 155.4 ms and 10,233 MB
+# for standard attention.
+PAGES_CONTEXT = {"hardware": "GTX 1080Ti (not comparable)", "n": 8192, "nystrom64_ms": 12.3,
+                 "standard_ms": 155.4, "nystrom64_MB": 450, "standard_MB": 10233,
+                 "speedup_vs_standard": 12.7, "memory_reduction_vs_standard": 22.8}
+
+
+def algorithmic_bytes(wl, kernel: str) -> int:
+    """Bytes each kernel must move per launch (per-head figure x heads)."""
+    e = wl.elem_bytes
+    per_head = wl.n * wl.d * e
+    heads = wl.batch * wl.heads
+    convw = 4 * wl.heads * wl.d * wl.conv_k
+    if kernel == "segment_mean":
+        return 2 * per_head * heads                  # read Q and K
+    if kernel == "landmark_bv":
+        return 2 * per_head * heads                  # read K and V
+    if kernel == "apply":
+        return 3 * per_head * heads + convw          # read Q, V; write O
+    if kernel == "fused":
+        return 4 * per_head * heads + convw          # read Q, K, V; write O
+    return 0
+
+
+def pinv_flops(wl) -> float:
+    return float(wl.batch * wl.heads) * (wl.iters * 8.0 * wl.m ** 3 + 2.0 * wl.m * wl.m * wl.d)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            return int(max(x.get("num_threads", 1) for x in info))
+    except Exception:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated in the timed loop (0: enough to exceed 512 MiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU-oracle leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the forward pass is independent per (batch, head), so a "
+              "multi-GPU run would only split the heads; run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch  # noqa: E402  (imported before the library so it binds torch's HIP runtime)
+    from efficient_transformer_attention_mean_amd import _lib
+    from efficient_transformer_attention_mean_amd.workloads import WORKLOADS, bf16_bits, bf16_bits_to_f32, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    io_bytes = wl.compulsory_bytes()
+    sets = args.sets or max(2, int(np.ceil(512 * 2 ** 20 / io_bytes)) + 1)
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    host0 = None
+    bufs = []
+    for i in range(sets):
+        inp = make_inputs(wl, seed=wl.seed + 1000 * i)
+        if i == 0:
+            host0 = inp
+        Q, K, V = (to_dev(inp[k]) for k in ("Q", "K", "V"))
+        W = None if inp["conv_w"] is None else torch.from_numpy(inp["conv_w"]).to(dev)
+        bufs.append((Q, K, V, W, torch.empty_like(Q)))
+    ws_bytes = _lib.nystrom_attn_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    code = _lib.NYS_BF16 if wl.dtype == "bf16" else _lib.NYS_F32
+    conv_k = wl.conv_k if wl.conv_k else 0
+
+    def step(i):
+        Q, K, V, W, O = bufs[i % sets]
+        rc = _lib.nystrom_attn_fwd(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, O, wl.batch, conv_k, code,
+                                   ws, ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    print(f"[bench] workload={wl.name} sets={sets} ({sets * io_bytes / 2**20:.0f} MiB) steps={args.steps} "
+          f"warmup={args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: whole steps, per-kernel HIP events recorded by the library
+    # on the same stream.
+    _lib.nystrom_timing_enable(True)
+    _lib.nystrom_timing_read()  # clear
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = _lib.nystrom_timing_read()
+    _lib.nystrom_timing_enable(False)
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    ms_per_step = 1e3 * gpu_s / args.steps
+    tokens = wl.batch * wl.n
+    value = tokens * args.steps / gpu_s
+
+    # Same loop without per-kernel events, to show what the events cost.
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_plain = ev0.elapsed_time(ev1) / args.steps
+
+    per_kernel = {}
+    for name, (ms, launches) in kern.items():
+        per_kernel[name] = {"ms_per_step": ms / args.steps, "launches_per_step": launches / args.steps,
+                            "avg_us_per_launch": 1e3 * ms / max(launches, 1)}
+    dom = max(kern.items(), key=lambda kv: kv[1][0])[0] if kern else None
+    roof = None
+    if dom is not None:
+        ms, launches = kern[dom]
+        avg_s = ms / launches / 1e3
+        ab = algorithmic_bytes(wl, dom)
+        if ab:
+            achieved = ab / avg_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "algorithmic_bytes": ab, "avg_us": round(avg_s * 1e6, 3)}
+        else:
+            fl = pinv_flops(wl)
+            achieved = fl / avg_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 6), "traffic": None,
+                    "kernel": dom, "algorithmic_flops": fl, "avg_us": round(avg_s * 1e6, 3)}
+
+    if args.copy_calibration:
+        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "n": wl.n, "d": wl.d, "m": wl.m,
+                   "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype, "input_sets": sets},
+        "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
+        "ms_per_step_without_kernel_events": round(ms_plain, 5),
+        "wall_s": round(wall, 4),
+        "roofline": roof,
+        "kernels": per_kernel,
+    }
+
+    if not args.no_cpu_baseline or not args.no_parity:
+        # CPU oracle: whole calls on set 0, repeated within the time budget.
+        from oracle import exact_attention, nystrom_attention
+        threads = blas_threads()
+        reps = 0
+        c0 = time.perf_counter()
+        O_ref = None
+        while True:
+            O_ref, inter = nystrom_attention(host0["Q"], host0["K"], host0["V"], wl.m, wl.iters, host0["conv_w"],
+                                             with_intermediates=True)
+            reps += 1
+            if args.no_cpu_baseline or time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - c0
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {
+                "value": round(tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{reps} whole call(s) of the workload (batch {wl.batch} x {wl.heads} heads, n={wl.n}), "
+                          f"fp64 NumPy, {cpu_s:.1f} s, host has {os.cpu_count()} logical CPUs"}
+        if not args.no_parity:
+            Q, K, V, W, O = bufs[0]
+            step(0)  # recompute set 0 into its own output
+            torch.cuda.synchronize()
+            if wl.dtype == "bf16":
+                out = bf16_bits_to_f32(O.view(torch.int16).cpu().numpy().view(np.uint16))
+            else:
+                out = O.float().cpu().numpy()
+            err = float(np.linalg.norm(out - O_ref) / np.linalg.norm(O_ref))
+            # Context: distance of the method from exact softmax attention on
+            # sampled query rows (attention part only, no skip).
+            rng = np.random.default_rng(7)
+            rows = np.sort(rng.choice(wl.n, size=min(256, wl.n), replace=False))
+            ex = np.stack([np.stack([exact_attention(host0["Q"][b, h][rows], host0["K"][b, h], host0["V"][b, h])
+                                     for h in range(wl.heads)]) for b in range(wl.batch)])
+            att = inter["O_att"][:, :, rows]
+            result["parity_rel_l2_vs_oracle"] = err
+            result["nystrom_vs_exact_attention_rel_l2_sampled_rows"] = float(
+                np.linalg.norm(att - ex) / np.linalg.norm(ex))
+    result["pages_context"] = PAGES_CONTEXT
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,94 @@
+"""Tensor-level wrappers over the C ABI (checks and allocation only).
+
+``attention`` and ``dconv`` validate torch tensors, allocate the output (and,
+if asked, a workspace), and call the library on the current torch stream.
+They raise ``NystromError`` on any non-zero return code.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.NYS_F32, torch.bfloat16: _lib.NYS_BF16}
+
+
+class NystromError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {_lib.nystrom_strerror(code)} (code {code})")
+        self.code = code
+
+
+def _check_io(*ts):
+    t0 = ts[0]
+    if t0.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t0.dtype}; use float32 or bfloat16")
+    for t in ts:
+        if t.device.type != "cuda":
+            raise ValueError("tensors must live on the GPU")
+        if t.dtype != t0.dtype or t.shape != t0.shape:
+            raise ValueError("Q, K, V must share shape and dtype")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if t0.dim() != 4:
+        raise ValueError("expected [batch, heads, n, d]")
+
+
+def workspace_bytes(batch, heads, n, d, m) -> int:
+    return _lib.nystrom_attn_workspace_bytes(batch, heads, n, d, m)
+
+
+def new_workspace(batch, heads, n, d, m, device="cuda") -> torch.Tensor:
+    nbytes = workspace_bytes(batch, heads, n, d, m)
+    if nbytes == 0:
+        raise NystromError(_lib.NYS_EUNSUPPORTED, "workspace")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attention(Q, K, V, m, iters=6, conv_w=None, out=None, workspace=None, stream=None):
+    """Nyström attention forward.  Q, K, V: [batch, heads, n, d] (fp32 or bf16);
+    conv_w: fp32 [heads, d, k] or None.  Returns ``out`` (same shape/dtype)."""
+    _check_io(Q, K, V)
+    batch, heads, n, d = Q.shape
+    conv_k = 0
+    if conv_w is not None:
+        if conv_w.dtype != torch.float32 or conv_w.dim() != 3 or tuple(conv_w.shape[:2]) != (heads, d):
+            raise ValueError("conv_w must be float32 [heads, d, k]")
+        if not conv_w.is_contiguous() or conv_w.device.type != "cuda":
+            raise ValueError("conv_w must be a contiguous GPU tensor")
+        conv_k = conv_w.shape[2]
+    if out is None:
+        out = torch.empty_like(Q)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.nystrom_attn_fwd(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, _DTYPES[Q.dtype],
+                               workspace, ws_bytes, stream)
+    if rc != _lib.NYS_OK:
+        raise NystromError(rc, "nystrom_attn_fwd")
+    return out
+
+
+def dconv(V, conv_w, out=None, stream=None):
+    """Depthwise-conv skip alone: out = DConv(V)."""
+    _check_io(V)
+    batch, heads, n, d = V.shape
+    if out is None:
+        out = torch.empty_like(V)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = _lib.nystrom_dconv_fwd(V, conv_w, n, d, heads, batch, conv_w.shape[2], _DTYPES[V.dtype], out, stream)
+    if rc != _lib.NYS_OK:
+        raise NystromError(rc, "nystrom_dconv_fwd")
+    return out
+
+
+def read_intermediate(workspace: torch.Tensor, which: int, batch, heads, n, d, m) -> torch.Tensor:
+    """View of an fp32 intermediate (NYS_WS_*) inside a workspace after a call."""
+    off = _lib.nystrom_attn_workspace_offset(which, batch, heads, n, d, m)
+    if off < 0:
+        raise NystromError(_lib.NYS_EINVAL, "workspace offset")
+    cols = m if which in (_lib.NYS_WS_A, _lib.NYS_WS_Z) else d
+    count = batch * heads * m * cols
+    flat = workspace[off:off + 4 * count].view(torch.float32)
+    return flat.view(batch, heads, m, cols)

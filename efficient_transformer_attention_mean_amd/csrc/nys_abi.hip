@@ -1,0 +1,112 @@
+// C ABI of the Nyström attention library: argument validation, workspace
+// contract and the stream-ordered launch of the kernels in nys_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/nystrom.h"
+#include "nys_internal.hpp"
+
+namespace {
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shared validation; returns NYS_OK or the code to report.
+int check_shape(int batch, int heads, int n, int d, int m, int iters) {
+  if (batch < 1 || heads < 1 || n < 1 || d < 1 || m < 1 || iters < 0) return NYS_EINVAL;
+  if (m > n || n % m != 0) return NYS_EINVAL;
+  if (!supported_d(d) || m > 256 || n > (1 << 24)) return NYS_EUNSUPPORTED;
+  if ((long long)batch * heads > 65535) return NYS_EUNSUPPORTED;  // batch*heads is a grid dimension
+  if ((long long)batch * heads * (long long)n * d > (1LL << 40)) return NYS_EUNSUPPORTED;
+  return NYS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nystrom_abi_version(void) { return 100; }
+
+const char* nystrom_strerror(int code) {
+  switch (code) {
+    case NYS_OK: return "success";
+    case NYS_EINVAL: return "invalid argument";
+    case NYS_EUNSUPPORTED: return "unsupported shape (d must be 16/32/64/128, m <= 256)";
+    case NYS_EWORKSPACE: return "workspace too small";
+    case NYS_EHIP: return "HIP runtime error";
+    case NYS_ENOTIMPL: return "not implemented";
+    default: return "unknown error code";
+  }
+}
+
+size_t nystrom_attn_workspace_bytes(int batch, int heads, int n, int d, int m) {
+  if (check_shape(batch, heads, n, d, m, 0) != NYS_OK) return 0;
+  nys::WsLayout L;
+  if (!nys::make_layout(batch, heads, n, d, m, &L)) return 0;
+  return L.total;
+}
+
+long long nystrom_attn_workspace_offset(int which, int batch, int heads, int n, int d, int m) {
+  if (check_shape(batch, heads, n, d, m, 0) != NYS_OK) return -1;
+  nys::WsLayout L;
+  if (!nys::make_layout(batch, heads, n, d, m, &L)) return -1;
+  switch (which) {
+    case NYS_WS_QT: return (long long)L.qt;
+    case NYS_WS_KT: return (long long)L.kt;
+    case NYS_WS_A: return (long long)L.a;
+    case NYS_WS_Z: return (long long)L.z;
+    case NYS_WS_BV: return (long long)L.bv;
+    case NYS_WS_W: return (long long)L.w;
+    default: return -1;
+  }
+}
+
+int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
+                     int heads, int iters, void* out, int batch, int conv_k, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  try {
+    if (!Q || !K || !V || !out) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    nys::WsLayout L;
+    if (!nys::make_layout(batch, heads, n, d, m, &L)) return NYS_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bool owned = false;
+    if (!ws) {
+      if (hipMallocAsync(reinterpret_cast<void**>(&ws), L.total, s) != hipSuccess) return NYS_EHIP;
+      owned = true;
+    } else if (workspace_bytes < L.total) {
+      return NYS_EWORKSPACE;
+    }
+    nys::Problem p{Q, K, V, conv_w, out, batch, heads, n, d, m, iters, conv_w ? conv_k : 0, dtype == NYS_BF16};
+    hipError_t e = nys::launch_forward(p, L, ws, s);
+    if (owned) {
+      hipError_t f = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = f;
+    }
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
+int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch, int conv_k, int dtype,
+                      void* out, void* stream) {
+  try {
+    if (!V || !conv_w || !out) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_k < 1 || conv_k % 2 == 0) return NYS_EINVAL;
+    if (batch < 1 || heads < 1 || n < 1 || d < 1) return NYS_EINVAL;
+    if (!supported_d(d) || n > (1 << 24) || (long long)batch * heads > 65535) return NYS_EUNSUPPORTED;
+    hipError_t e = nys::launch_dconv(V, conv_w, out, batch, heads, n, d, conv_k, dtype == NYS_BF16,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// Device helpers shared by the Nyström attention kernels (gfx950 / CDNA4).
+//
+// Matrix-core convention used throughout: v_mfma_f32_16x16x32_bf16, one wave
+// (64 lanes), lane l = 16*g + c with g = l >> 4 (0..3), c = l & 15:
+//   A operand (16 x 32, row-major M x K): lane holds A[c][8g .. 8g+7]
+//   B operand (32 x 16, K x N):          lane holds B[8g .. 8g+7][c]
+//   C / D     (16 x 16):                 lane holds D[4g .. 4g+3][c]
+// A contraction only needs A's k-slot q and B's k-slot q to name the same
+// index, so kernels may feed a permuted k order to both operands.
+//
+// Extra precision ("bf16x3"): an fp32 value x is split into hi = bf16(x) and
+// lo = bf16(x - hi), so x = hi + lo up to about 2^-16 |x|; a product is then
+// hi*hi + hi*lo + lo*hi on the matrix cores with fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nys {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+
+union B8 {
+  bf16x8_t v;
+  uint32_t u[4];
+  uint16_t h[8];
+  uint4 q;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest even (gfx950 has a hardware conversion; the cast uses it).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ void split8(const float (&x)[8], B8& hi, B8& lo) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) split_hi_lo(x[q], hi.h[q], lo.h[q]);
+}
+
+__device__ __forceinline__ void round8(const float (&x)[8], B8& hi) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) hi.h[q] = f32_to_bf16(x[q]);
+}
+
+__device__ __forceinline__ f32x4_t mfma(const B8& a, const B8& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+
+// acc += (ah + al)(bh + bl) without the lo*lo term.
+__device__ __forceinline__ f32x4_t mfma3(const B8& ah, const B8& al, const B8& bh, const B8& bl, f32x4_t c) {
+  c = mfma(al, bh, c);
+  c = mfma(ah, bl, c);
+  return mfma(ah, bh, c);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Three-way split x = hi + mid + lo (each bf16; both differences are exact in
+// fp32), leaving about 2^-24 |x|: fp32-grade products from six bf16 products.
+__device__ __forceinline__ void split8x3(const float (&x)[8], B8& hi, B8& mid, B8& lo) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    hi.h[q] = f32_to_bf16(x[q]);
+    const float r = x[q] - bf16_to_f32(hi.h[q]);
+    mid.h[q] = f32_to_bf16(r);
+    lo.h[q] = f32_to_bf16(r - bf16_to_f32(mid.h[q]));
+  }
+}
+
+// acc += a b for 8-element fp32 fragments (A: 16 x 32 row slice, B: 32 x 16).
+// P = 3: bf16x3 (about 2^-17 relative per product); P = 6: three-way split,
+// terms of order 2^-16 and above kept (about 2^-24).
+template <int P>
+__device__ __forceinline__ f32x4_t mma_f32(const float (&a)[8], const float (&b)[8], f32x4_t acc) {
+  if constexpr (P == 3) {
+    B8 ah, al, bh, bl;
+    split8(a, ah, al);
+    split8(b, bh, bl);
+    return mfma3(ah, al, bh, bl, acc);
+  } else {
+    B8 ah, am, al, bh, bm, bl;
+    split8x3(a, ah, am, al);
+    split8x3(b, bh, bm, bl);
+    acc = mfma(al, bh, acc);
+    acc = mfma(ah, bl, acc);
+    acc = mfma(am, bm, acc);
+    acc = mfma(am, bh, acc);
+    acc = mfma(ah, bm, acc);
+    return mfma(ah, bh, acc);
+  }
+}
+
+// Element types at the boundary.
+struct F32 {
+  using T = float;
+  static constexpr bool kBf16 = false;
+};
+struct BF16 {
+  using T = uint16_t;
+  static constexpr bool kBf16 = true;
+};
+
+template <typename IO>
+__device__ __forceinline__ float load_elem(const typename IO::T* p) {
+  if constexpr (IO::kBf16) return bf16_to_f32(*p); else return *p;
+}
+
+template <typename IO>
+__device__ __forceinline__ void store_elem(typename IO::T* p, float v) {
+  if constexpr (IO::kBf16) *p = f32_to_bf16(v); else *p = v;
+}
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) as floats.
+template <typename IO>
+__device__ __forceinline__ void load8f(const typename IO::T* p, float (&x)[8]) {
+  if constexpr (IO::kBf16) {
+    B8 b;
+    b.q = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = bf16_to_f32(b.h[q]);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 c = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+  }
+}
+
+// Cross-lane helpers within a wave of 64.
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float max_over_groups(float v) {  // over lanes c, c+16, c+32, c+48
+  v = fmaxf(v, shfl_xor(v, 16));
+  return fmaxf(v, shfl_xor(v, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += shfl_xor(v, 16);
+  return v + shfl_xor(v, 32);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace nys

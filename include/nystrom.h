@@ -1,0 +1,136 @@
+/*
+ * nystrom.h -- C ABI of the MI355X (gfx950) Nyström self-attention forward.
+ *
+ * What is computed (per batch b and head h, all indices 0-based):
+ *   Qt, Kt  segment means of Q and K over m contiguous blocks of l = n/m rows
+ *           ("Nyströmformer: A Nyström-Based Algorithm for Approximating
+ *           Self-Attention", sec. 3.4 "Landmark Selection: Segment-Means",
+ *           Eq. 16, divisor read as l);
+ *   F = softmax(Q Kt^T / sqrt(d)), A = softmax(Qt Kt^T / sqrt(d)),
+ *   B = softmax(Qt K^T / sqrt(d)), all row-wise (same page, Eq. 13);
+ *   Z = `iters` steps of Z <- Z (13I - AZ(15I - AZ(7I - AZ))) / 4 from
+ *       Z0 = A^T / (||A||_1 ||A||_inf) (same page, "Moore-Penrose
+ *       Pseudoinverse Computation", Lemma 1 and the initialisation);
+ *   out = F (Z (B V)) + DConv(V) (same page, "Putting It Together", Eq. 17
+ *       and the depthwise-convolution skip of Figure 4), where
+ *       DConv(V)[i, c] = sum_t w[h, c, t] V[i + t - (k-1)/2, c], zero outside.
+ * The n x n score matrix is never formed.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     keeps no state between calls and never frees caller memory.
+ *   - Q, K, V, out: [batch][heads][n][d], contiguous, element type `dtype`
+ *     (NYS_F32 = IEEE fp32, NYS_BF16 = bfloat16).  conv_w: fp32
+ *     [heads][d][conv_k], contiguous, or NULL for no skip.
+ *   - All arithmetic accumulates in fp32; the output is rounded to `dtype`
+ *     (round-to-nearest-even for bf16).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Arguments are validated on the host before anything is
+ *     enqueued; an invalid call returns a negative code and launches nothing.
+ *   - No exception crosses the ABI.  NaN/Inf inputs are not checked and
+ *     propagate.
+ */
+#ifndef NYSTROM_H
+#define NYSTROM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of Q, K, V and out. */
+typedef enum { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
+
+/* Return codes. */
+enum {
+  NYS_OK = 0,
+  NYS_EINVAL = -1,       /* bad argument: NULL tensor, size < 1, m > n, n % m != 0,
+                            iters < 0, even or non-positive conv_k with a filter,
+                            unknown dtype */
+  NYS_EUNSUPPORTED = -2, /* valid but outside what the kernels handle:
+                            d not in {16, 32, 64, 128}, m > 256, n > 2^24,
+                            batch * heads > 65535 */
+  NYS_EWORKSPACE = -3,   /* caller workspace smaller than nystrom_attn_workspace_bytes() */
+  NYS_EHIP = -4,         /* a HIP runtime call or launch failed */
+  NYS_ENOTIMPL = -5
+};
+
+/* Which intermediate to locate in the workspace (see nystrom_attn_workspace_offset). */
+enum {
+  NYS_WS_QT = 0, /* fp32 [batch*heads][m][d]   segment means of Q            */
+  NYS_WS_KT = 1, /* fp32 [batch*heads][m][d]   segment means of K            */
+  NYS_WS_A = 2,  /* fp32 [batch*heads][m][m]   softmax(Qt Kt^T / sqrt d)     */
+  NYS_WS_Z = 3,  /* fp32 [batch*heads][m][m]   pseudoinverse after `iters`   */
+  NYS_WS_BV = 4, /* fp32 [batch*heads][m][d]   softmax(Qt K^T / sqrt d) V    */
+  NYS_WS_W = 5,  /* fp32 [batch*heads][m][d]   Z (B V)                       */
+  NYS_WS_COUNT = 6
+};
+
+/* Bytes of device workspace nystrom_attn_fwd needs for this shape (the same
+ * for both dtypes), or 0 if the shape is invalid or unsupported. */
+size_t nystrom_attn_workspace_bytes(int batch, int heads, int n, int d, int m);
+
+/* Byte offset of intermediate `which` (NYS_WS_*) inside the workspace, or -1
+ * for an invalid shape or `which`.  After a completed nystrom_attn_fwd call
+ * the region holds that call's values, laid out as documented above. */
+long long nystrom_attn_workspace_offset(int which, int batch, int heads, int n, int d, int m);
+
+/* Nyström self-attention forward (the computation described at the top).
+ *   Q, K, V     inputs, [batch][heads][n][d] of `dtype`
+ *   conv_w      fp32 [heads][d][conv_k] depthwise filters, or NULL (no skip;
+ *               conv_k is then ignored)
+ *   n           sequence length, a multiple of m
+ *   d           head dimension, one of 16, 32, 64, 128
+ *   m           number of landmarks, 1 <= m <= min(n, 256)
+ *   heads       heads per batch entry
+ *   iters       pseudoinverse iterations (>= 0; 0 returns the start Z0)
+ *   out         output, [batch][heads][n][d] of `dtype`; must not alias inputs
+ *   batch       batch size
+ *   conv_k      odd filter length when conv_w != NULL
+ *   dtype       NYS_F32 or NYS_BF16 (Q, K, V and out share it)
+ *   workspace   device buffer of at least nystrom_attn_workspace_bytes(), or
+ *               NULL: the call then allocates and frees one in stream order
+ *               (hipMallocAsync / hipFreeAsync on `stream`)
+ *   workspace_bytes  size of `workspace` (ignored when it is NULL)
+ *   stream      hipStream_t the work is ordered on; NULL = default stream
+ * Returns NYS_OK, or a negative code (nothing was launched when validation
+ * fails). */
+int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* conv_w,
+                     int n, int d, int m, int heads, int iters, void* out,
+                     int batch, int conv_k, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Depthwise-convolution skip alone: out = DConv(V) with the filters and
+ * padding described at the top ("Putting It Together", Figure 4's DConv path).
+ *   V, out      [batch][heads][n][d] of `dtype` (out must not alias V)
+ *   conv_w      fp32 [heads][d][conv_k], non-NULL; conv_k odd, >= 1
+ *   d           one of 16, 32, 64, 128
+ * Returns NYS_OK or a negative code. */
+int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch,
+                      int conv_k, int dtype, void* out, void* stream);
+
+/* Diagnostics: per-kernel timing.  While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on the launch's stream
+ * (the library then holds those events between calls).  Returns the previous
+ * setting.  Intended for profiling runs, not production calls. */
+int nystrom_timing_enable(int on);
+
+/* Waits for the recorded events and reports, per kernel name, the summed
+ * milliseconds and the number of launches since the previous read; the
+ * accumulators are cleared.  Fills at most `max_entries` entries; the name
+ * pointers stay valid until the next read.  Returns the number of distinct
+ * kernels (which may exceed max_entries). */
+int nystrom_timing_read(int max_entries, const char** names, double* total_ms, long long* launches);
+
+/* Static, human-readable text for a return code. */
+const char* nystrom_strerror(int code);
+
+/* ABI version of this header (major * 100 + minor). */
+int nystrom_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NYSTROM_H */

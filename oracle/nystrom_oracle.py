@@ -218,19 +218,21 @@ def exact_attention(Q, K, V, row_chunk=1024):
     """Standard softmax attention softmax(Q K^T / sqrt(d)) V ([NF] Eq. 2),
     evaluated in row chunks so the n x n matrix is never held at once.
 
-    Q, K, V: (..., n, d).  Used only to report how far the approximation is
-    from exact attention, and for the m = n check of Lemma 2.
+    Q: (..., nq, d) query rows (a subset of rows is allowed); K, V: (..., n, d).
+    Used only to report how far the approximation is from exact attention,
+    and for the m = n check of Lemma 2.
     """
     Q, K, V = map(_f64, (Q, K, V))
     lead = Q.shape[:-2]
-    n, d = Q.shape[-2:]
-    Qf = Q.reshape((-1, n, d))
+    nq, d = Q.shape[-2:]
+    n = K.shape[-2]
+    Qf = Q.reshape((-1, nq, d))
     Kf = K.reshape((-1, n, d))
     Vf = V.reshape((-1, n, V.shape[-1]))
-    out = np.empty(Vf.shape[:1] + (n, V.shape[-1]))
+    out = np.empty(Vf.shape[:1] + (nq, V.shape[-1]))
     s = 1.0 / np.sqrt(d)
     for g in range(Qf.shape[0]):
-        for i0 in range(0, n, row_chunk):
+        for i0 in range(0, nq, row_chunk):
             S = s * (Qf[g, i0:i0 + row_chunk] @ Kf[g].T)
             out[g, i0:i0 + row_chunk] = row_softmax(S) @ Vf[g]
-    return out.reshape(lead + (n, V.shape[-1]))
+    return out.reshape(lead + (nq, V.shape[-1]))

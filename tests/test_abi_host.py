@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, and its host logic (workspace sizing,
+offsets, argument validation, error strings) behaves as documented.  No call
+here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_transformer_attention_mean_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nystrom.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nystrom_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libnystrom.so not built")
+    return _lib.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_strerror(lib):
+    assert _lib.nystrom_abi_version() == 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert isinstance(_lib.nystrom_strerror(code), str) and _lib.nystrom_strerror(code)
+    assert "unknown" in _lib.nystrom_strerror(-99)
+
+
+def test_workspace_sizes_and_offsets(lib):
+    B, H, n, d, m = 2, 12, 8192, 64, 64
+    total = _lib.nystrom_attn_workspace_bytes(B, H, n, d, m)
+    assert total > 0
+    md, mm = B * H * m * d * 4, B * H * m * m * 4
+    offs = [_lib.nystrom_attn_workspace_offset(w, B, H, n, d, m) for w in range(6)]
+    sizes = [md, md, mm, mm, md, md]
+    for o, s in zip(offs, sizes):
+        assert o >= 0 and o % 256 == 0 and o + s <= total
+    # regions do not overlap
+    spans = sorted(zip(offs, sizes))
+    for (o1, s1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 + s1 <= o2
+    assert _lib.nystrom_attn_workspace_offset(6, B, H, n, d, m) == -1
+    assert _lib.nystrom_attn_workspace_offset(-1, B, H, n, d, m) == -1
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 64, 16, 8), (8, 12, 512, 64, 64), (4, 12, 4096, 64, 64),
+    (2, 12, 8192, 64, 32), (1, 16, 32768, 128, 256), (1, 1, 48, 32, 3), (1, 1, 7, 16, 7),
+])
+def test_workspace_valid_shapes(lib, shape):
+    assert _lib.nystrom_attn_workspace_bytes(*shape) > 0
+
+
+@pytest.mark.parametrize("shape", [
+    (0, 1, 64, 16, 8), (1, 0, 64, 16, 8), (1, 1, 64, 16, 0), (1, 1, 64, 16, 65),
+    (1, 1, 63, 16, 8), (1, 1, 64, 24, 8), (1, 1, 64, 256, 8), (1, 1, 1024, 64, 512),
+])
+def test_workspace_invalid_shapes(lib, shape):
+    assert _lib.nystrom_attn_workspace_bytes(*shape) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every case below is rejected on the host
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.NYS_EINVAL),
+    (dict(out=None), _lib.NYS_EINVAL),
+    (dict(n=63), _lib.NYS_EINVAL),
+    (dict(m=0), _lib.NYS_EINVAL),
+    (dict(m=128, n=64), _lib.NYS_EINVAL),
+    (dict(iters=-1), _lib.NYS_EINVAL),
+    (dict(dtype=2), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=4), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=0), _lib.NYS_EINVAL),
+    (dict(batch=0), _lib.NYS_EINVAL),
+    (dict(heads=-2), _lib.NYS_EINVAL),
+    (dict(d=48), _lib.NYS_EUNSUPPORTED),
+    (dict(d=256), _lib.NYS_EUNSUPPORTED),
+    (dict(m=512, n=1024), _lib.NYS_EUNSUPPORTED),
+    (dict(workspace=FAKE, workspace_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_fwd_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, n=64, d=16, m=8, heads=1, iters=6, out=FAKE,
+                batch=1, conv_k=0, dtype=_lib.NYS_F32, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_fwd(**args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V=None), _lib.NYS_EINVAL),
+    (dict(conv_w=None), _lib.NYS_EINVAL),
+    (dict(conv_k=2), _lib.NYS_EINVAL),
+    (dict(dtype=5), _lib.NYS_EINVAL),
+    (dict(n=0), _lib.NYS_EINVAL),
+    (dict(d=24), _lib.NYS_EUNSUPPORTED),
+])
+def test_dconv_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(V=FAKE, conv_w=FAKE, n=64, d=16, heads=1, batch=1, conv_k=3, dtype=_lib.NYS_F32, out=FAKE,
+                stream=None)
+    args.update(kw)
+    assert _lib.nystrom_dconv_fwd(**args) == code

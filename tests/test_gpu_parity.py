@@ -1,0 +1,171 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars (relative L2 over the whole tensor): output <= 1e-4 for fp32 I/O and
+<= 2e-2 for bf16 I/O; intermediates to the tolerances in INTER_TOL, derived
+from the arithmetic each one goes through.  Every workload is compared in
+full (the oracle finishes each in seconds), with the conv skip and without it
+(attention-only), so the skip cannot hide attention errors."""
+import numpy as np
+import pytest
+
+from efficient_transformer_attention_mean_amd import _lib
+from efficient_transformer_attention_mean_amd.workloads import WORKLOADS, make_inputs
+from oracle import depthwise_conv_skip, exact_attention, nystrom_attention
+
+from ._gpu_util import dtype_code, rel_l2, run_forward, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Intermediate gates, from the arithmetic each value goes through:
+#  Qt, Kt: fp32 sums of exact inputs (~1e-7).
+#  A: scores from split-bf16 matrix-core products (fp32-grade for fp32 I/O,
+#     bf16x3 ~2^-17 for bf16 I/O) then an fp32 softmax.
+#  Z: 4 products per iteration; errors in the directions of small singular
+#     values of A grow by up to 13/4 per step (the slope of the iteration map
+#     at 0), so the bf16x3 gate is looser: 1e-5 x cond-driven growth.
+#  BV: bf16 probabilities x exact bf16 V (or split fp32) with fp32 accumulation.
+#  W = Z BV: sums with cancellation (|Z| entries up to ~300 when A is
+#     ill-conditioned), so it inherits Z's error times that growth.
+INTER_TOL = {
+    "f32": {"Qt": 1e-6, "Kt": 1e-6, "A": 1e-5, "Z": 5e-5, "BV": 5e-5, "W": 2e-3},
+    "bf16": {"Qt": 1e-6, "Kt": 1e-6, "A": 1e-5, "Z": 5e-3, "BV": 5e-5, "W": 2e-3},
+}
+
+_cache = {}
+
+
+def oracle_for(wl):
+    if wl.name not in _cache:
+        inp = make_inputs(wl)
+        O, inter = nystrom_attention(inp["Q"], inp["K"], inp["V"], wl.m, wl.iters, inp["conv_w"],
+                                     with_intermediates=True)
+        _cache[wl.name] = (inp, O, inter)
+    return _cache[wl.name]
+
+
+def check(wl, report=print):
+    inp, O, inter = oracle_for(wl)
+    out, got = run_forward(inp, wl.m, wl.iters, wl.dtype, use_conv=True)
+    errs = {"out": rel_l2(out, O)}
+    itol = INTER_TOL[wl.dtype]
+    for k in itol:
+        errs[k] = rel_l2(got[k], inter[k])
+    out_att, _ = run_forward(inp, wl.m, wl.iters, wl.dtype, use_conv=False)
+    errs["out_att_only"] = rel_l2(out_att, inter["O_att"])
+    report(f"{wl.name}: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    tol = OUT_TOL[wl.dtype]
+    assert errs["out"] <= tol, errs
+    assert errs["out_att_only"] <= tol, errs
+    for k, t in itol.items():
+        assert errs[k] <= t, (k, errs)
+    return errs
+
+
+@pytest.mark.parametrize("name", ["tiny", "bert", "long", "headline", "headline_m32", "stress"])
+def test_workload_parity(name):
+    check(WORKLOADS[name])
+
+
+def test_m_equals_n_matches_exact_attention():
+    # m = n with a converged pseudoinverse: the method is exact attention (Lemma 2).
+    wl = WORKLOADS["tiny_m_eq_n"]
+    errs = check(wl)
+    inp = oracle_for(wl)[0]
+    out, _ = run_forward(inp, wl.m, wl.iters, wl.dtype, use_conv=False)
+    ex = exact_attention(inp["Q"], inp["K"], inp["V"])
+    assert rel_l2(out, ex) <= 1e-4, errs
+
+
+EDGE = [
+    # (batch, heads, n, d, m, iters, conv_k, dtype)
+    (1, 1, 96, 32, 12, 6, 3, "f32"),      # n not a multiple of the 64-row tile
+    (2, 3, 100, 16, 10, 6, 5, "bf16"),    # ragged n, m = 10, d = 16
+    (1, 2, 48, 64, 3, 6, 0, "f32"),       # odd m, no skip
+    (1, 1, 64, 128, 1, 6, 1, "bf16"),     # m = 1 (rank one), k = 1
+    (1, 1, 640, 64, 80, 6, 33, "f32"),    # m > 64: global pseudoinverse path, m not a multiple of 32
+    (1, 2, 512, 32, 256, 8, 9, "bf16"),   # m = 256, segment length 2
+    (1, 1, 256, 64, 128, 6, 33, "f32"),   # m = 128
+    (2, 2, 128, 16, 32, 0, 7, "f32"),     # iters = 0: Z is the start Z0
+    (1, 1, 16, 16, 16, 30, 3, "f32"),     # m = n, tiny
+    (1, 1, 33, 16, 33, 30, 0, "f32"),     # m = n = 33, odd
+    (3, 1, 200, 64, 40, 6, 33, "bf16"),   # conv halo wider than the ragged tail
+    (1, 2, 256, 128, 64, 6, 33, "f32"),   # d = 128
+    (1, 2, 256, 32, 64, 6, 33, "bf16"),   # d = 32
+    (1, 1, 4096, 64, 64, 6, 33, "f32"),   # many key chunks in fp32
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}m{c[4]}it{c[5]}k{c[6]}{c[7]}" for c in EDGE])
+def test_edge_parity(case):
+    B, H, n, d, m, iters, k, dt = case
+    wl = WORKLOADS["tiny"].with_(name=f"edge{case}", batch=B, heads=H, n=n, d=d, m=m, iters=iters, conv_k=k,
+                                 dtype=dt, seed=100 + n + m)
+    check(wl)
+
+
+def test_determinism_bitwise():
+    wl = WORKLOADS["long"].with_(name="det", batch=1, heads=4, n=2048)
+    inp = make_inputs(wl)
+    a, ia = run_forward(inp, wl.m, wl.iters, wl.dtype)
+    b, ib = run_forward(inp, wl.m, wl.iters, wl.dtype)
+    assert np.array_equal(a, b)
+    for k in ia:
+        assert np.array_equal(ia[k], ib[k]), k
+
+
+def test_null_workspace_matches_caller_workspace():
+    wl = WORKLOADS["long"].with_(name="nullws", batch=1, heads=2, n=1024)
+    inp = make_inputs(wl)
+    a, _ = run_forward(inp, wl.m, wl.iters, wl.dtype, own_workspace=True)
+    b, _ = run_forward(inp, wl.m, wl.iters, wl.dtype, own_workspace=False)
+    assert np.array_equal(a, b)
+
+
+def test_side_stream():
+    import torch
+    wl = WORKLOADS["bert"].with_(name="stream", batch=1, heads=3)
+    inp, O, _ = oracle_for(wl)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, _ = run_forward(inp, wl.m, wl.iters, wl.dtype, stream=s)
+    assert rel_l2(out, O) <= OUT_TOL["f32"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n,d,k", [(100, 16, 1), (257, 64, 33), (64, 128, 5), (1000, 32, 33)])
+def test_dconv_standalone(dt, n, d, k):
+    import torch
+    rng = np.random.default_rng(n + d + k)
+    from efficient_transformer_attention_mean_amd.workloads import round_to_bf16
+    B, H = 2, 3
+    V = rng.standard_normal((B, H, n, d)).astype(np.float32)
+    if dt == "bf16":
+        V = round_to_bf16(V)
+    w = rng.normal(0, 0.5, (H, d, k)).astype(np.float32)
+    Vd = to_dev(V, dt)
+    out = torch.empty_like(Vd)
+    wd = torch.from_numpy(w).cuda()
+    rc = _lib.nystrom_dconv_fwd(Vd, wd, n, d, H, B, k, dtype_code(dt), out, torch.cuda.current_stream())
+    assert rc == 0
+    torch.cuda.synchronize()
+    ref = np.stack([np.stack([depthwise_conv_skip(V[b, h], w[h]) for h in range(H)]) for b in range(B)])
+    err = rel_l2(to_host(out), ref)
+    assert err <= (1e-6 if dt == "f32" else 8e-3), err
+
+
+def test_invalid_calls_leave_output_untouched():
+    import torch
+    Q = torch.randn(1, 1, 64, 16, device="cuda")
+    out = torch.full_like(Q, 7.0)
+    for kw, code in ((dict(m=5), _lib.NYS_EINVAL), (dict(d=24), _lib.NYS_EUNSUPPORTED)):
+        args = dict(n=64, d=16, m=8)
+        args.update(kw)
+        rc = _lib.nystrom_attn_fwd(Q, Q, Q, None, args["n"], args["d"], args["m"], 1, 6, out, 1, 0, _lib.NYS_F32,
+                                   None, 0, None)
+        assert rc == code
+    ws = torch.zeros(8, dtype=torch.uint8, device="cuda")
+    rc = _lib.nystrom_attn_fwd(Q, Q, Q, None, 64, 16, 8, 1, 6, out, 1, 0, _lib.NYS_F32, ws, 8, None)
+    assert rc == _lib.NYS_EWORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())

@@ -248,7 +248,10 @@ def _brute_exact_attention(Q, K, V):
 def test_exact_attention_brute_force():
     rng = np.random.default_rng(20)
     Q, K, V = (rng.standard_normal((9, 3)) for _ in range(3))
-    np.testing.assert_allclose(exact_attention(Q, K, V, row_chunk=4), _brute_exact_attention(Q, K, V), atol=1e-14)
+    full = _brute_exact_attention(Q, K, V)
+    np.testing.assert_allclose(exact_attention(Q, K, V, row_chunk=4), full, atol=1e-14)
+    rows = np.array([1, 4, 8])  # a subset of query rows against all keys
+    np.testing.assert_allclose(exact_attention(Q[rows], K, V, row_chunk=2), full[rows], atol=1e-14)
 
 
 def test_lemma2_m_equals_n_is_exact():
