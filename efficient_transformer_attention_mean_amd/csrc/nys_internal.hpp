@@ -1,23 +1,37 @@
-// Host-side view of the workspace and the launch sequence (internal to the library).
+// Host-side view of the workspace and the launch stages (internal to the library).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace nys {
 
-// Byte offsets of every region in the caller's workspace.  All regions are
-// fp32 (counters are u32) and 256-byte aligned.
+// Byte offsets of every region in the caller's workspace (256-byte aligned).
 struct WsLayout {
-  size_t qt, kt, a, z, bv, w;      // documented intermediates (NYS_WS_*)
-  size_t z2, x, t, u;              // pseudoinverse scratch for m > 64
-  size_t pacc, pmax, psum;         // split-n partials of softmax(Qt K^T) V
+  size_t qt, kt, a, z, bv, w;      // documented fp32 intermediates (NYS_WS_*)
+  size_t z2, x, t, u;              // fp32 pseudoinverse scratch for m > 64
+  size_t pacc, pmax, psum;         // fp32 split-n partials of softmax(Qt K^T) V
+  size_t kt_hi, kt_lo;             // bf16 planes of Kt, [bh][mpa][d]
+  size_t wt_hi, wt_lo;             // bf16 planes of W^T, [bh][d][mpa], landmark order permuted
   size_t total;
-  int nchunks, chunk;              // keys per landmark_bv block, blocks per head
+  int nchunks, chunk;              // split-n: blocks per head, keys per block
+  int mpa;                         // landmarks padded for the output stage: 32, 64, 128 or 256
 };
 
 // Returns false for shapes the kernels do not handle.
 bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L);
+
+// The same regions as device pointers.
+struct Ws {
+  float *Qt, *Kt, *A, *Z, *BV, *W;
+  float *Z2, *X, *T, *U;
+  float *pacc, *pmax, *psum;
+  uint16_t *kt_hi, *kt_lo, *wt_hi, *wt_lo;
+  int nchunks, chunk, mpa;
+};
+
+Ws resolve(const WsLayout& L, char* base);
 
 struct Problem {
   const void* Q;
@@ -43,6 +57,13 @@ class KernelTimer {
   hipStream_t s_;
   hipEvent_t start_ = nullptr;
 };
+
+// Stages of the forward pass, each enqueued on `s` in this order.
+hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  // Qt, Kt, Kt planes
+hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z
+hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s);             // B V
+hipError_t stage_w(const Problem& p, const Ws& w, hipStream_t s);              // W, W^T planes
+hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,

@@ -1,4 +1,4 @@
-// Nyström self-attention forward: HIP kernels for gfx950 (CDNA4).
+// Nyström self-attention forward, landmark side: HIP kernels for gfx950 (CDNA4).
 //
 // Method: "Nyströmformer: A Nyström-Based Algorithm for Approximating
 // Self-Attention" (paper deep-dive page, sec. 3.2 and 3.4).  Per (batch, head):
@@ -8,9 +8,8 @@
 //                                             k_landmark_softmax + k_pinv_start + k_mm chain
 //   B V = softmax(Qt K^T / sqrt d) V       -> k_landmark_bv (split over keys,
 //                                             online softmax) + k_bv_combine
-//   W = Z (B V)                            -> k_mm
-//   out = softmax(Q Kt^T / sqrt d) W + DConv(V) (Eq. 17 + Figure 4 skip)
-//                                          -> k_apply (dconv fused), k_dconv alone
+//   W = Z (B V)                            -> k_mm, then k_prep_w (bf16 planes)
+// The output stage (softmax(Q Kt^T / sqrt d) W + DConv(V)) is in nys_apply.hip.
 // Softmaxes run in base 2: scores are pre-multiplied by log2(e)/sqrt(d), which
 // leaves every softmax unchanged.
 #include <math.h>
@@ -24,11 +23,14 @@ namespace nys {
 // Segment means: grid (m, batch*heads, 2); z = 0 -> Q, z = 1 -> K.
 // One block per segment of l = n/m contiguous rows; 16-byte coalesced loads,
 // fp32 partial sums per thread, fixed-order reduction through LDS.
+// Key landmarks are also written as bf16 hi/lo planes [bh][mpa][D] (rows
+// m..mpa-1 zero), the operand layout of the output stage.
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __restrict__ Q,
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
-                                                      int n, int m) {
+                                                      uint16_t* __restrict__ kt_hi, uint16_t* __restrict__ kt_lo,
+                                                      int n, int m, int mpa) {
   using T = typename IO::T;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int SLOTS = D / VEC;
@@ -60,7 +62,21 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   if (threadIdx.x < D) {
     float s = 0.f;
     for (int p = 0; p < RS; ++p) s += part[p * D + threadIdx.x];
-    out[threadIdx.x] = s / (float)seg;
+    const float mean = s / (float)seg;
+    out[threadIdx.x] = mean;
+    if (blockIdx.z == 1) {
+      uint16_t hi, lo;
+      split_hi_lo(mean, hi, lo);
+      const size_t o = ((size_t)bh * mpa + j) * D + threadIdx.x;
+      kt_hi[o] = hi;
+      kt_lo[o] = lo;
+      if (j == m - 1) {
+        for (int r = m; r < mpa; ++r) {
+          kt_hi[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
+          kt_lo[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
+        }
+      }
+    }
   }
 }
 
@@ -581,329 +597,149 @@ __global__ __launch_bounds__(256) void k_bv_combine(const float* __restrict__ pa
   BV[((size_t)bh * m + j) * D + cc] = S / L;
 }
 
-// ---------------------------------------------------------------------------
-// Depthwise-conv skip for rows [row0, row0 + rows) of one head, one feature per
-// thread: v[r] += sum_t w[t] V[row0 + r + t - R], zero outside [0, n).
-template <typename IO>
-__device__ __forceinline__ float conv_at(const typename IO::T* __restrict__ Vh, const float* __restrict__ w,
-                                         int n, int D, int k, int row, int cc) {
-  const int R = (k - 1) / 2;
-  float v = 0.f;
-  const int t0 = max(0, R - row), t1 = min(k, n - row + R);
-  for (int t = t0; t < t1; ++t) v = fmaf(w[t], load_elem<IO>(Vh + (size_t)(row + t - R) * D + cc), v);
-  return v;
-}
 
-// out = softmax(Q Kt^T / sqrt d) W (+ DConv(V)).  grid (ceil(n/64), batch*heads).
-// Each wave handles 16 queries: scores transposed (landmarks x queries) on the
-// matrix cores, softmax over landmarks per query across lanes, then F W with
-// the landmark index permuted consistently in both operands.  The block's
-// attention output goes through LDS, where the conv epilogue adds the skip and
-// stores with one feature per lane.
-template <typename IO, int D, int NTM>
-__global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict__ Qin,
-                                               const typename IO::T* __restrict__ Vin,
-                                               const float* __restrict__ Kt, const float* __restrict__ Wm,
-                                               const float* __restrict__ conv_w, typename IO::T* __restrict__ out,
-                                               int n, int m, int heads, int conv_k, float sl2e) {
-  using T = typename IO::T;
-  constexpr int KC = (D + 31) / 32;
-  constexpr int ND = D / 16;
-  __shared__ __align__(16) float sO[64][D + 4];
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.x * 64, qw = q0 + wave * 16;
-  const T* Qh = Qin + (size_t)bh * n * D;
-  const float* kt = Kt + (size_t)bh * m * D;
-  const float* wm = Wm + (size_t)bh * m * D;
-
-  // Query operand (B of S^T = Kt Q^T): lane holds query qw + c.
-  B8 qh[KC], ql[KC];
-#pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int dd = kc * 32 + 8 * g;
-    float x[8];
-    if (qw + c < n && dd < D) {
-      load8f<IO>(Qh + (size_t)(qw + c) * D + dd, x);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = 0.f;
-    }
-    split8(x, qh[kc], ql[kc]);
-  }
-
-  f32x4_t s[NTM];
-#pragma unroll
-  for (int mt = 0; mt < NTM; ++mt) {
-    s[mt] = zero4();
-    const int lm = mt * 16 + c;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      float x[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int dd = kc * 32 + 8 * g + q;
-        x[q] = (lm < m && dd < D) ? kt[lm * D + dd] : 0.f;
-      }
-      B8 kh, kl;
-      split8(x, kh, kl);
-      if constexpr (IO::kBf16) {
-        s[mt] = mfma(kl, qh[kc], s[mt]);
-        s[mt] = mfma(kh, qh[kc], s[mt]);
-      } else {
-        s[mt] = mfma3(kh, kl, qh[kc], ql[kc], s[mt]);
-      }
-    }
-  }
-  // Softmax over landmarks (lane's query = qw + c; landmark = mt*16 + 4g + i).
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lm = mt * 16 + 4 * g + i;
-      s[mt][i] = (lm < m) ? s[mt][i] * sl2e : -INFINITY;
-      mx = fmaxf(mx, s[mt][i]);
-    }
-  mx = max_over_groups(mx);
-  float sum = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[mt][i] = exp2f(s[mt][i] - mx);
-      sum += s[mt][i];
-    }
-  sum = sum_over_groups(sum);
-  const float inv = 1.f / sum;
-
-  // O^T (d x queries) = W^T (d x landmarks) F^T (landmarks x queries): each lane
-  // ends up with 4 consecutive features of one query, stored to LDS in one
-  // 16-byte write.
-  f32x4_t o[ND];
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
-#pragma unroll
-  for (int kk = 0; kk < NTM / 2; ++kk) {
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = s[2 * kk][i] * inv;
-      f[4 + i] = s[2 * kk + 1][i] * inv;
-    }
-    B8 fh, fl;
-    split8(f, fh, fl);
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd) {
-      const int dd = nd * 16 + c;
-      float y[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int lm = kk * 32 + (q < 4 ? 4 * g + q : 16 + 4 * g + q - 4);
-        y[q] = (lm < m) ? wm[lm * D + dd] : 0.f;
-      }
-      B8 wh, wl;
-      split8(y, wh, wl);
-      o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
-    }
-  }
-#pragma unroll
-  for (int nd = 0; nd < ND; ++nd)
-    *reinterpret_cast<float4*>(&sO[wave * 16 + c][nd * 16 + 4 * g]) =
-        make_float4(o[nd][0], o[nd][1], o[nd][2], o[nd][3]);
-  __syncthreads();
-
-  // Epilogue: + DConv(V), round to the I/O type, store.
-  const int h = bh % heads;
-  const T* Vh = Vin + (size_t)bh * n * D;
-  const float* w = conv_w ? conv_w + ((size_t)h * D) * conv_k : nullptr;
-  const int cc = tid % D;
-  constexpr int RG = 256 / D;
-  constexpr int RPG = 64 / RG;
-  const int rbeg = (tid / D) * RPG;
-  T* oh = out + (size_t)bh * n * D;
-  for (int r = rbeg; r < rbeg + RPG; ++r) {
-    const int row = q0 + r;
-    if (row >= n) break;
-    float v = sO[r][cc];
-    if (w) v += conv_at<IO>(Vh, w + (size_t)cc * conv_k, n, D, conv_k, row, cc);
-    store_elem<IO>(oh + (size_t)row * D + cc, v);
-  }
-}
-
-// Standalone depthwise-conv skip.  grid (ceil(n/64), batch*heads).
-template <typename IO, int D>
-__global__ __launch_bounds__(256) void k_dconv(const typename IO::T* __restrict__ Vin, const float* __restrict__ conv_w,
-                                               typename IO::T* __restrict__ out, int n, int heads, int conv_k) {
-  using T = typename IO::T;
-  const int bh = blockIdx.y, tid = threadIdx.x;
-  const int q0 = blockIdx.x * 64;
-  const int h = bh % heads;
-  const T* Vh = Vin + (size_t)bh * n * D;
-  const float* w = conv_w + ((size_t)h * D) * conv_k;
-  const int cc = tid % D;
-  constexpr int RG = 256 / D;
-  constexpr int RPG = 64 / RG;
-  const int rbeg = (tid / D) * RPG;
-  T* oh = out + (size_t)bh * n * D;
-  for (int r = rbeg; r < rbeg + RPG; ++r) {
-    const int row = q0 + r;
-    if (row >= n) break;
-    store_elem<IO>(oh + (size_t)row * D + cc, conv_at<IO>(Vh, w + (size_t)cc * conv_k, n, D, conv_k, row, cc));
-  }
+// W (fp32 [bh][m][D]) -> bf16 hi/lo planes of W^T [bh][D][mpa], the A operand
+// of the output stage: within each chunk of 32 landmarks, position 8g + q
+// holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4), the order in
+// which that stage's softmax lanes hold their landmarks.  Padding is zero.
+// grid (ceil(D*mpa/256), batch*heads).
+__global__ __launch_bounds__(256) void k_prep_w(const float* __restrict__ W, uint16_t* __restrict__ wt_hi,
+                                                uint16_t* __restrict__ wt_lo, int m, int D, int mpa) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * mpa) return;
+  const int dd = e / mpa, pos = e % mpa;
+  const int kk = pos >> 5, r = pos & 31, g = r >> 3, q = r & 7;
+  const int lm = kk * 32 + (q < 4 ? 4 * g + q : 16 + 4 * g + q - 4);
+  const float v = lm < m ? W[((size_t)bh * m + lm) * D + dd] : 0.f;
+  uint16_t hi, lo;
+  split_hi_lo(v, hi, lo);
+  wt_hi[(size_t)bh * D * mpa + e] = hi;
+  wt_lo[(size_t)bh * D * mpa + e] = lo;
 }
 
 // ---------------------------------------------------------------------------
-// Host launch sequence.
+// Stage launchers.
 
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
-  if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n || n % m != 0) return false;
-  if (!(d == 16 || d == 32 || d == 64 || d == 128) || m > 256 || n > (1 << 24)) return false;
-  const long long BH = (long long)batch * heads;
-  // Key chunking for the split-n pass: aim for >= ~2 blocks per CU over 256 CUs,
-  // chunks a multiple of the 64-key tile.
-  int want = ceil_div(512, BH);
-  int maxch = ceil_div(n, 64);
-  int nch = want < 1 ? 1 : (want > maxch ? maxch : want);
-  int chunk = ceil_div(ceil_div(n, nch), 64) * 64;
-  nch = ceil_div(n, chunk);
-  L->nchunks = nch;
-  L->chunk = chunk;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return o;
-  };
-  const size_t md = (size_t)BH * m * d * 4, mm = (size_t)BH * m * m * 4;
-  L->qt = take(md);
-  L->kt = take(md);
-  L->a = take(mm);
-  L->z = take(mm);
-  L->bv = take(md);
-  L->w = take(md);
-  const bool big = m > 64;
-  L->z2 = take(big ? mm : 0);
-  L->x = take(big ? mm : 0);
-  L->t = take(big ? mm : 0);
-  L->u = take(big ? mm : 0);
-  L->pacc = take((size_t)BH * nch * m * d * 4);
-  L->pmax = take((size_t)BH * nch * m * 4);
-  L->psum = take((size_t)BH * nch * m * 4);
-  L->total = off;
-  return true;
+template <typename IO, int D>
+static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
+  using T = typename IO::T;
+  const int BH = p.batch * p.heads;
+  KernelTimer kt_("segment_mean", s);
+  k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
+                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.n, p.m, w.mpa);
 }
 
-template <typename IO, int D>
-static hipError_t forward_t(const Problem& p, const WsLayout& L, char* ws, hipStream_t s) {
-  using T = typename IO::T;
-  const int BH = p.batch * p.heads, n = p.n, m = p.m;
+hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
+  switch (p.d) {
+    case 16: p.bf16 ? seg_means_t<BF16, 16>(p, w, s) : seg_means_t<F32, 16>(p, w, s); break;
+    case 32: p.bf16 ? seg_means_t<BF16, 32>(p, w, s) : seg_means_t<F32, 32>(p, w, s); break;
+    case 64: p.bf16 ? seg_means_t<BF16, 64>(p, w, s) : seg_means_t<F32, 64>(p, w, s); break;
+    case 128: p.bf16 ? seg_means_t<BF16, 128>(p, w, s) : seg_means_t<F32, 128>(p, w, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Landmark-side m x m products: fp32-grade for fp32 I/O, bf16x3 for bf16 I/O
+// (where the output rounding dominates the error).
+template <int PR>
+static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads, m = p.m, D = p.d;
   const float sl2e = kLog2e / sqrtf((float)D);
-  // Landmark-side m x m products: fp32-grade for fp32 I/O, bf16x3 for bf16 I/O
-  // (where the output rounding dominates the error).
-  constexpr int PR = IO::kBf16 ? 3 : 6;
-  float* Qt = reinterpret_cast<float*>(ws + L.qt);
-  float* Kt = reinterpret_cast<float*>(ws + L.kt);
-  float* A = reinterpret_cast<float*>(ws + L.a);
-  float* Z = reinterpret_cast<float*>(ws + L.z);
-  float* BV = reinterpret_cast<float*>(ws + L.bv);
-  float* W = reinterpret_cast<float*>(ws + L.w);
-  const T* Q = static_cast<const T*>(p.Q);
-  const T* K = static_cast<const T*>(p.K);
-  const T* V = static_cast<const T*>(p.V);
-  T* out = static_cast<T*>(p.out);
-
-  { KernelTimer kt_("segment_mean", s); k_segment_mean<IO, D><<<dim3(m, BH, 2), 256, 0, s>>>(Q, K, Qt, Kt, n, m); }
-
   if (m <= 32) {
-    { KernelTimer kt_("pinv", s); k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(Qt, Kt, A, Z, m, D, sl2e, p.iters); }
+    KernelTimer kt_("pinv", s);
+    k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
   } else if (m <= 64) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_lds<64, PR>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        (int)sizeof(PinvSmem<64>));
     if (attr != hipSuccess) return attr;
-    { KernelTimer kt_("pinv", s); k_pinv_lds<64, PR><<<BH, 256, sizeof(PinvSmem<64>), s>>>(Qt, Kt, A, Z, m, D, sl2e, p.iters); }
+    KernelTimer kt_("pinv", s);
+    k_pinv_lds<64, PR><<<BH, 256, sizeof(PinvSmem<64>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
   } else {
-    float* Z2 = reinterpret_cast<float*>(ws + L.z2);
-    float* X = reinterpret_cast<float*>(ws + L.x);
-    float* Tm = reinterpret_cast<float*>(ws + L.t);
-    float* U = reinterpret_cast<float*>(ws + L.u);
-    { KernelTimer kt_("landmark_softmax", s); k_landmark_softmax<PR><<<dim3(ceil_div(m, 16), BH), 256, 0, s>>>(Qt, Kt, A, m, D, sl2e); }
+    {
+      KernelTimer kt_("landmark_softmax", s);
+      k_landmark_softmax<PR><<<dim3(ceil_div(m, 16), BH), 256, 0, s>>>(w.Qt, w.Kt, w.A, m, D, sl2e);
+    }
     // Ping-pong so that the last iterate lands in Z.
-    float* zc = (p.iters % 2 == 0) ? Z : Z2;
-    float* zn = (p.iters % 2 == 0) ? Z2 : Z;
-    { KernelTimer kt_("pinv_start", s); k_pinv_start<<<BH, 256, 0, s>>>(A, zc, m); }
+    float* zc = (p.iters % 2 == 0) ? w.Z : w.Z2;
+    float* zn = (p.iters % 2 == 0) ? w.Z2 : w.Z;
+    {
+      KernelTimer kt_("pinv_start", s);
+      k_pinv_start<<<BH, 256, 0, s>>>(w.A, zc, m);
+    }
     const long long st = (long long)m * m;
-    dim3 grid(ceil_div(m, 64), ceil_div(m, 64), BH);
+    const dim3 grid(ceil_div(m, 64), ceil_div(m, 64), BH);
     for (int it = 0; it < p.iters; ++it) {
-      { KernelTimer kt_("pinv_mm", s); k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{A, zc, X, Tm, m, m, m, st, st, st, 1.f, 0.f, -1.f, 7.f}); }
-      { KernelTimer kt_("pinv_mm", s); k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{X, Tm, U, nullptr, m, m, m, st, st, st, -1.f, 15.f, 0.f, 0.f}); }
-      { KernelTimer kt_("pinv_mm", s); k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{X, U, Tm, nullptr, m, m, m, st, st, st, -1.f, 13.f, 0.f, 0.f}); }
-      { KernelTimer kt_("pinv_mm", s); k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{zc, Tm, zn, nullptr, m, m, m, st, st, st, 0.25f, 0.f, 0.f, 0.f}); }
+      KernelTimer kt_("pinv_mm", s);
+      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.A, zc, w.X, w.T, m, m, m, st, st, st, 1.f, 0.f, -1.f, 7.f});
+      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.X, w.T, w.U, nullptr, m, m, m, st, st, st, -1.f, 15.f, 0.f, 0.f});
+      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.X, w.U, w.T, nullptr, m, m, m, st, st, st, -1.f, 13.f, 0.f, 0.f});
+      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{zc, w.T, zn, nullptr, m, m, m, st, st, st, 0.25f, 0.f, 0.f, 0.f});
       float* tmp = zc;
       zc = zn;
       zn = tmp;
     }
   }
-
-  float* pacc = reinterpret_cast<float*>(ws + L.pacc);
-  float* pmax = reinterpret_cast<float*>(ws + L.pmax);
-  float* psum = reinterpret_cast<float*>(ws + L.psum);
-  const dim3 gbv(L.nchunks, BH);
-  if (m <= 64)
-    { KernelTimer kt_("landmark_bv", s); k_landmark_bv<IO, D, 1><<<gbv, 256, 0, s>>>(K, V, Qt, pacc, pmax, psum, n, m, L.chunk, L.nchunks, sl2e); }
-  else if (m <= 128)
-    { KernelTimer kt_("landmark_bv", s); k_landmark_bv<IO, D, 2><<<gbv, 256, 0, s>>>(K, V, Qt, pacc, pmax, psum, n, m, L.chunk, L.nchunks, sl2e); }
-  else
-    { KernelTimer kt_("landmark_bv", s); k_landmark_bv<IO, D, 4><<<gbv, 256, 0, s>>>(K, V, Qt, pacc, pmax, psum, n, m, L.chunk, L.nchunks, sl2e); }
-  { KernelTimer kt_("bv_combine", s); k_bv_combine<<<dim3(ceil_div((long long)m * D, 256), BH), 256, 0, s>>>(pacc, pmax, psum, BV, m, D, L.nchunks); }
-
-  { KernelTimer kt_("w_mm", s); k_mm<PR><<<dim3(ceil_div(D, 64), ceil_div(m, 64), BH), 256, 0, s>>>(
-      MMArgs{Z, BV, W, nullptr, m, D, m, (long long)m * m, (long long)m * D, (long long)m * D, 1.f, 0.f, 0.f, 0.f}); }
-
-  const dim3 gap(ceil_div(n, 64), BH);
-  const int mp = ((m + 31) / 32) * 32;
-  if (mp <= 32)
-    { KernelTimer kt_("apply", s); k_apply<IO, D, 2><<<gap, 256, 0, s>>>(Q, V, Kt, W, p.conv_w, out, n, m, p.heads, p.conv_k, sl2e); }
-  else if (mp <= 64)
-    { KernelTimer kt_("apply", s); k_apply<IO, D, 4><<<gap, 256, 0, s>>>(Q, V, Kt, W, p.conv_w, out, n, m, p.heads, p.conv_k, sl2e); }
-  else if (mp <= 128)
-    { KernelTimer kt_("apply", s); k_apply<IO, D, 8><<<gap, 256, 0, s>>>(Q, V, Kt, W, p.conv_w, out, n, m, p.heads, p.conv_k, sl2e); }
-  else
-    { KernelTimer kt_("apply", s); k_apply<IO, D, 16><<<gap, 256, 0, s>>>(Q, V, Kt, W, p.conv_w, out, n, m, p.heads, p.conv_k, sl2e); }
   return hipGetLastError();
 }
 
-hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s) {
-  switch (p.d) {
-    case 16: return p.bf16 ? forward_t<BF16, 16>(p, L, ws, s) : forward_t<F32, 16>(p, L, ws, s);
-    case 32: return p.bf16 ? forward_t<BF16, 32>(p, L, ws, s) : forward_t<F32, 32>(p, L, ws, s);
-    case 64: return p.bf16 ? forward_t<BF16, 64>(p, L, ws, s) : forward_t<F32, 64>(p, L, ws, s);
-    case 128: return p.bf16 ? forward_t<BF16, 128>(p, L, ws, s) : forward_t<F32, 128>(p, L, ws, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
+  return p.bf16 ? pinv_t<3>(p, w, s) : pinv_t<6>(p, w, s);
 }
 
 template <typename IO, int D>
-static hipError_t dconv_t(const void* V, const float* w, void* out, int BH, int heads, int n, int k, hipStream_t s) {
+static void bv_t(const Problem& p, const Ws& w, hipStream_t s) {
   using T = typename IO::T;
-  { KernelTimer kt_("dconv", s); k_dconv<IO, D><<<dim3(ceil_div(n, 64), BH), 256, 0, s>>>(static_cast<const T*>(V), w, static_cast<T*>(out), n,
-                                                          heads, k); }
+  const int BH = p.batch * p.heads, m = p.m;
+  const float sl2e = kLog2e / sqrtf((float)D);
+  const T* K = static_cast<const T*>(p.K);
+  const T* V = static_cast<const T*>(p.V);
+  const dim3 g(w.nchunks, BH);
+  {
+    KernelTimer kt_("landmark_bv", s);
+    if (m <= 64)
+      k_landmark_bv<IO, D, 1><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+    else if (m <= 128)
+      k_landmark_bv<IO, D, 2><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+    else
+      k_landmark_bv<IO, D, 4><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+  }
+  KernelTimer kt_("bv_combine", s);
+  k_bv_combine<<<dim3(ceil_div((long long)m * D, 256), BH), 256, 0, s>>>(w.pacc, w.pmax, w.psum, w.BV, m, D,
+                                                                        w.nchunks);
+}
+
+hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s) {
+  switch (p.d) {
+    case 16: p.bf16 ? bv_t<BF16, 16>(p, w, s) : bv_t<F32, 16>(p, w, s); break;
+    case 32: p.bf16 ? bv_t<BF16, 32>(p, w, s) : bv_t<F32, 32>(p, w, s); break;
+    case 64: p.bf16 ? bv_t<BF16, 64>(p, w, s) : bv_t<F32, 64>(p, w, s); break;
+    case 128: p.bf16 ? bv_t<BF16, 128>(p, w, s) : bv_t<F32, 128>(p, w, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n, int d, int k,
-                        bool bf16, hipStream_t s) {
-  const int BH = batch * heads;
-  switch (d) {
-    case 16: return bf16 ? dconv_t<BF16, 16>(V, conv_w, out, BH, heads, n, k, s) : dconv_t<F32, 16>(V, conv_w, out, BH, heads, n, k, s);
-    case 32: return bf16 ? dconv_t<BF16, 32>(V, conv_w, out, BH, heads, n, k, s) : dconv_t<F32, 32>(V, conv_w, out, BH, heads, n, k, s);
-    case 64: return bf16 ? dconv_t<BF16, 64>(V, conv_w, out, BH, heads, n, k, s) : dconv_t<F32, 64>(V, conv_w, out, BH, heads, n, k, s);
-    case 128: return bf16 ? dconv_t<BF16, 128>(V, conv_w, out, BH, heads, n, k, s) : dconv_t<F32, 128>(V, conv_w, out, BH, heads, n, k, s);
+template <int PR>
+static void w_t(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads, m = p.m, D = p.d;
+  {
+    KernelTimer kt_("w_mm", s);
+    k_mm<PR><<<dim3(ceil_div(D, 64), ceil_div(m, 64), BH), 256, 0, s>>>(
+        MMArgs{w.Z, w.BV, w.W, nullptr, m, D, m, (long long)m * m, (long long)m * D, (long long)m * D, 1.f, 0.f,
+               0.f, 0.f});
   }
-  return hipErrorInvalidValue;
+  KernelTimer kt_("prep_w", s);
+  k_prep_w<<<dim3(ceil_div((long long)D * w.mpa, 256), BH), 256, 0, s>>>(w.W, w.wt_hi, w.wt_lo, m, D, w.mpa);
+}
+
+hipError_t stage_w(const Problem& p, const Ws& w, hipStream_t s) {
+  p.bf16 ? w_t<3>(p, w, s) : w_t<6>(p, w, s);
+  return hipGetLastError();
 }
 
 }  // namespace nys

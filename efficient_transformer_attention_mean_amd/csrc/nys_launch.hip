@@ -1,0 +1,86 @@
+// Workspace layout and the stream-ordered sequence of forward stages.
+#include "nys_internal.hpp"
+
+namespace nys {
+
+static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
+  if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n || n % m != 0) return false;
+  if (!(d == 16 || d == 32 || d == 64 || d == 128) || m > 256 || n > (1 << 24)) return false;
+  const long long BH = (long long)batch * heads;
+  // Key chunking for the split-n pass: aim for about 2 blocks per CU over 256
+  // CUs; chunks are a multiple of the 64-key tile.
+  long long want = cdiv(512, BH);
+  long long maxch = cdiv(n, 64);
+  long long nch = want < 1 ? 1 : (want > maxch ? maxch : want);
+  long long chunk = cdiv(cdiv(n, nch), 64) * 64;
+  nch = cdiv(n, chunk);
+  L->nchunks = (int)nch;
+  L->chunk = (int)chunk;
+  L->mpa = m <= 32 ? 32 : m <= 64 ? 64 : m <= 128 ? 128 : 256;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t md = (size_t)BH * m * d * 4, mm = (size_t)BH * m * m * 4;
+  L->qt = take(md);
+  L->kt = take(md);
+  L->a = take(mm);
+  L->z = take(mm);
+  L->bv = take(md);
+  L->w = take(md);
+  const bool big = m > 64;
+  L->z2 = take(big ? mm : 0);
+  L->x = take(big ? mm : 0);
+  L->t = take(big ? mm : 0);
+  L->u = take(big ? mm : 0);
+  L->pacc = take((size_t)BH * nch * m * d * 4);
+  L->pmax = take((size_t)BH * nch * m * 4);
+  L->psum = take((size_t)BH * nch * m * 4);
+  L->kt_hi = take((size_t)BH * L->mpa * d * 2);
+  L->kt_lo = take((size_t)BH * L->mpa * d * 2);
+  L->wt_hi = take((size_t)BH * d * L->mpa * 2);
+  L->wt_lo = take((size_t)BH * d * L->mpa * 2);
+  L->total = off;
+  return true;
+}
+
+Ws resolve(const WsLayout& L, char* b) {
+  Ws w;
+  w.Qt = reinterpret_cast<float*>(b + L.qt);
+  w.Kt = reinterpret_cast<float*>(b + L.kt);
+  w.A = reinterpret_cast<float*>(b + L.a);
+  w.Z = reinterpret_cast<float*>(b + L.z);
+  w.BV = reinterpret_cast<float*>(b + L.bv);
+  w.W = reinterpret_cast<float*>(b + L.w);
+  w.Z2 = reinterpret_cast<float*>(b + L.z2);
+  w.X = reinterpret_cast<float*>(b + L.x);
+  w.T = reinterpret_cast<float*>(b + L.t);
+  w.U = reinterpret_cast<float*>(b + L.u);
+  w.pacc = reinterpret_cast<float*>(b + L.pacc);
+  w.pmax = reinterpret_cast<float*>(b + L.pmax);
+  w.psum = reinterpret_cast<float*>(b + L.psum);
+  w.kt_hi = reinterpret_cast<uint16_t*>(b + L.kt_hi);
+  w.kt_lo = reinterpret_cast<uint16_t*>(b + L.kt_lo);
+  w.wt_hi = reinterpret_cast<uint16_t*>(b + L.wt_hi);
+  w.wt_lo = reinterpret_cast<uint16_t*>(b + L.wt_lo);
+  w.nchunks = L.nchunks;
+  w.chunk = L.chunk;
+  w.mpa = L.mpa;
+  return w;
+}
+
+hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s) {
+  const Ws w = resolve(L, ws);
+  hipError_t e;
+  if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_bv(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_w(p, w, s)) != hipSuccess) return e;
+  return stage_apply(p, w, s);
+}
+
+}  // namespace nys
