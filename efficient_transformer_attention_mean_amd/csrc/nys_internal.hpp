@@ -58,11 +58,12 @@ class KernelTimer {
   hipEvent_t start_ = nullptr;
 };
 
-// Stages of the forward pass, each enqueued on `s` in this order.
+// Stages of the forward pass.  The pseudoinverse depends only on the
+// landmarks, so it runs on a side stream beside the split-n pass.
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  // Qt, Kt, Kt planes
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z
-hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s);             // B V
-hipError_t stage_w(const Problem& p, const Ws& w, hipStream_t s);              // W, W^T planes
+hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s);             // split-n partials of B V
+hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      // B V, W, W^T planes (needs Z)
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);

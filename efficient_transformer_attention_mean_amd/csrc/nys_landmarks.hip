@@ -4,11 +4,12 @@
 // Self-Attention" (paper deep-dive page, sec. 3.2 and 3.4).  Per (batch, head):
 //   segment means Qt, Kt (Eq. 16)         -> k_segment_mean
 //   A = softmax(Qt Kt^T / sqrt d), Z = Lemma-1 iterations from the
-//   Pan-Schreiber start                    -> k_pinv_lds (m <= 64) or
+//   Pan-Schreiber start                    -> k_pinv_planes (m <= 64, bf16 I/O),
+//                                             k_pinv_lds (m <= 64, fp32 I/O) or
 //                                             k_landmark_softmax + k_pinv_start + k_mm chain
 //   B V = softmax(Qt K^T / sqrt d) V       -> k_landmark_bv (split over keys,
-//                                             online softmax) + k_bv_combine
-//   W = Z (B V)                            -> k_mm, then k_prep_w (bf16 planes)
+//                                             online softmax), then k_bv_finish
+//   W = Z (B V), W^T bf16 planes           -> k_bv_finish
 // The output stage (softmax(Q Kt^T / sqrt d) W + DConv(V)) is in nys_apply.hip.
 // Softmaxes run in base 2: scores are pre-multiplied by log2(e)/sqrt(d), which
 // leaves every softmax unchanged.
@@ -33,9 +34,9 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
                                                       int n, int m, int mpa) {
   using T = typename IO::T;
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int SLOTS = D / VEC;
-  constexpr int RS = 256 / SLOTS;
-  __shared__ float part[RS * D];
+  constexpr int SLOTS = D / VEC;   // 16-byte vectors per row
+  constexpr int RS = 256 / SLOTS;  // rows covered per pass
+  __shared__ float part[4][D];
   const int j = blockIdx.x, bh = blockIdx.y;
   const int seg = n / m;
   const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
@@ -44,24 +45,43 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   float acc[VEC];
 #pragma unroll
   for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
-  for (int r = r0; r < seg; r += RS) {
-    const T* p = X + (size_t)r * D + slot * VEC;
-    if constexpr (IO::kBf16) {
-      B8 b;
-      b.q = *reinterpret_cast<const uint4*>(p);
+  // 8 independent 16-byte loads in flight per thread, accumulated in row order.
+  for (int r = r0; r < seg; r += 8 * RS) {
+    uint4 v[8];
 #pragma unroll
-      for (int q = 0; q < VEC; ++q) acc[q] += bf16_to_f32(b.h[q]);
-    } else {
-      const float4 a = *reinterpret_cast<const float4*>(p);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    for (int u = 0; u < 8; ++u) {
+      const int rr = r + u * RS;
+      v[u] = rr < seg ? *reinterpret_cast<const uint4*>(X + (size_t)rr * D + slot * VEC) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (IO::kBf16) {
+        B8 b;
+        b.q = v[u];
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) acc[q] += bf16_to_f32(b.h[q]);
+      } else {
+        acc[0] += __uint_as_float(v[u].x);
+        acc[1] += __uint_as_float(v[u].y);
+        acc[2] += __uint_as_float(v[u].z);
+        acc[3] += __uint_as_float(v[u].w);
+      }
     }
   }
+  // Butterfly over the lanes of a wave that share a slot (lane = r*SLOTS + slot),
+  // then a fixed-order sum over the 4 waves.
 #pragma unroll
-  for (int q = 0; q < VEC; ++q) part[r0 * D + slot * VEC + q] = acc[q];
+  for (int o = SLOTS; o < 64; o <<= 1)
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) acc[q] += shfl_xor(acc[q], o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < SLOTS) {
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) part[wave][slot * VEC + q] = acc[q];
+  }
   __syncthreads();
   if (threadIdx.x < D) {
-    float s = 0.f;
-    for (int p = 0; p < RS; ++p) s += part[p * D + threadIdx.x];
+    const float s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
     const float mean = s / (float)seg;
     out[threadIdx.x] = mean;
     if (blockIdx.z == 1) {
@@ -241,6 +261,219 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 }
 
 // ---------------------------------------------------------------------------
+// Pseudoinverse for m <= 64 with bf16x3 products (bf16 I/O): every iterate is
+// kept in LDS only as bf16 hi/lo planes, written once by the wave that
+// produces it in the layout its consumers read, so a matrix-core fragment is
+// one 16-byte LDS read per plane.  In C = P Q, P is read row-major ([row][k])
+// and Q column-major ([col][k]).  A wave's result tile holds 4 consecutive
+// rows of one column: column-major outputs are 8-byte writes, row-major ones
+// 2-byte writes.
+//   1. X  = A Z      -> X row-major, T1 = 7I - X column-major
+//   2. U  = X T1     -> T3 = 15I - U column-major
+//   3. V  = X T3     -> T5 = 13I - V column-major
+//   4. Z' = Z T5 / 4 -> Z' row-major and column-major
+// Row buffers: A, R0, R1 (X and Z alternate); column buffers K0, K1, K2
+// (Z^T and the two T's rotate).
+template <int MP>
+struct PinvPlanes {
+  static constexpr int LD = MP + 8;  // plane row pitch (bf16): rows stay 16-byte aligned
+  static constexpr int PL = MP * LD;
+  __align__(16) uint16_t rowb[3][2][PL];
+  __align__(16) uint16_t colb[3][2][PL];
+  float red[2][MP];
+};
+
+template <int MP>
+__device__ __forceinline__ void put_split(uint16_t* hi, uint16_t* lo, int idx, float v) {
+  uint16_t h, l;
+  split_hi_lo(v, h, l);
+  hi[idx] = h;
+  lo[idx] = l;
+}
+
+// C = P Q (MP x MP) from planes; epi(ti, tj, acc) gets the tile whose lane
+// (c, g) holds C[ti*16 + 4g + i][tj*16 + c], i = 0..3.
+template <int MP, typename Epi>
+__device__ __forceinline__ void planes_mm(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Qh,
+                                          const uint16_t* Ql, Epi epi) {
+  constexpr int LD = PinvPlanes<MP>::LD, NT = MP / 16, TPW = NT * NT / 4, KC = MP / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int ti = (wave * TPW) / NT;  // every tile of a wave shares its row block
+  B8 ah[KC], al[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const int o = (ti * 16 + c) * LD + kc * 32 + 8 * g;
+    ah[kc].q = *reinterpret_cast<const uint4*>(Ph + o);
+    al[kc].q = *reinterpret_cast<const uint4*>(Pl + o);
+  }
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tj = (wave * TPW + tt) % NT;
+    f32x4_t acc = zero4();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int o = (tj * 16 + c) * LD + kc * 32 + 8 * g;
+      B8 bh, bl;
+      bh.q = *reinterpret_cast<const uint4*>(Qh + o);
+      bl.q = *reinterpret_cast<const uint4*>(Ql + o);
+      acc = mfma3(ah[kc], al[kc], bh, bl, acc);
+    }
+    epi(ti, tj, acc);
+  }
+}
+
+// Writers for a result tile (lane (c, g): rows ti*16+4g+i, column tj*16+c)
+// of alpha*I + scale*acc.
+template <int MP>
+__device__ __forceinline__ void put_col(uint16_t* h, uint16_t* l, int ti, int tj, const f32x4_t& acc, float scale,
+                                        float alpha) {
+  constexpr int LD = PinvPlanes<MP>::LD;
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int col = tj * 16 + c, row0 = ti * 16 + 4 * g;
+  B8 hv, lv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split_hi_lo(scale * acc[i] + (row0 + i == col ? alpha : 0.f), hv.h[i], lv.h[i]);
+  *reinterpret_cast<uint2*>(h + col * LD + row0) = make_uint2(hv.u[0], hv.u[1]);
+  *reinterpret_cast<uint2*>(l + col * LD + row0) = make_uint2(lv.u[0], lv.u[1]);
+}
+
+template <int MP>
+__device__ __forceinline__ void put_row(uint16_t* h, uint16_t* l, int ti, int tj, const f32x4_t& acc, float scale,
+                                        float alpha) {
+  constexpr int LD = PinvPlanes<MP>::LD;
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int col = tj * 16 + c, row0 = ti * 16 + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) put_split<MP>(h, l, (row0 + i) * LD + col, scale * acc[i] + (row0 + i == col ? alpha : 0.f));
+}
+
+template <int MP>
+__global__ __launch_bounds__(256) void k_pinv_planes(const float* __restrict__ Qt, const float* __restrict__ Kt,
+                                                     float* __restrict__ Aout, float* __restrict__ Zout, int m,
+                                                     int d, float sl2e, int iters) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  using SM = PinvPlanes<MP>;
+  constexpr int LD = SM::LD, NT = MP / 16, SP = MP + 4;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  // fp32 scratch for the scores / A, aliased on column buffers K1, K2.
+  float* S = reinterpret_cast<float*>(&sm.colb[1][0][0]);
+  static_assert(sizeof(float) * MP * SP <= sizeof(uint16_t) * 4 * SM::PL, "scratch does not fit");
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const float* qt = Qt + (size_t)bh * m * d;
+  const float* kt = Kt + (size_t)bh * m * d;
+
+  // Scaled scores (Kt Qt^T)^T: lane ends with row ti*16+c, columns tj*16+4g..+3.
+  for (int t = wave; t < NT * NT; t += 4) {
+    const int ti = t / NT, tj = t % NT;
+    const int rq = ti * 16 + c, rk = tj * 16 + c;
+    f32x4_t acc = zero4();
+    for (int kc = 0; kc < d; kc += 32) {
+      float a[8], b[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int kk = kc + 8 * g + q;
+        a[q] = (rk < m && kk < d) ? kt[rk * d + kk] : 0.f;
+        b[q] = (rq < m && kk < d) ? qt[rq * d + kk] : 0.f;
+      }
+      acc = mma_f32<3>(a, b, acc);
+    }
+    *reinterpret_cast<float4*>(&S[rq * SP + tj * 16 + 4 * g]) =
+        make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
+  }
+  __syncthreads();
+  // Row softmax over the m real columns; padded rows/columns are 0.
+  {
+    constexpr int TPR = 256 / MP;
+    const int r = tid / TPR, sub = tid % TPR;
+    float mx = -INFINITY;
+    for (int j = sub; j < m; j += TPR) mx = fmaxf(mx, S[r * SP + j]);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+    float s = 0.f;
+    for (int j = sub; j < MP; j += TPR) {
+      const float e = (r < m && j < m) ? exp2f(S[r * SP + j] - mx) : 0.f;
+      S[r * SP + j] = e;
+      s += e;
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) s += shfl_xor(s, o);
+    if (r < m) {
+      const float inv = 1.f / s;
+      for (int j = sub; j < m; j += TPR) S[r * SP + j] *= inv;
+    }
+  }
+  __syncthreads();
+  if (tid < MP) {
+    float cs = 0.f, rs = 0.f;
+    for (int i = 0; i < MP; ++i) {
+      cs += fabsf(S[i * SP + tid]);
+      rs += fabsf(S[tid * SP + i]);
+    }
+    sm.red[0][tid] = cs;
+    sm.red[1][tid] = rs;
+  }
+  __syncthreads();
+  float n1 = 0.f, ninf = 0.f;
+  for (int i = 0; i < MP; ++i) {
+    n1 = fmaxf(n1, sm.red[0][i]);
+    ninf = fmaxf(ninf, sm.red[1][i]);
+  }
+  const float cz = 1.f / (n1 * ninf);
+  // A -> row planes (buffer 0) and the output; Z0 = cz A^T -> row planes R0 and
+  // column planes K0 (Z0^T = cz A, i.e. K0[j][i] = cz A[j][i]).
+  float* ao = Aout + (size_t)bh * m * m;
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    const float a = S[i * SP + j];
+    put_split<MP>(sm.rowb[0][0], sm.rowb[0][1], i * LD + j, a);
+    put_split<MP>(sm.colb[0][0], sm.colb[0][1], i * LD + j, cz * a);
+    put_split<MP>(sm.rowb[1][0], sm.rowb[1][1], j * LD + i, cz * a);
+    if (i < m && j < m) ao[i * m + j] = a;
+  }
+  __syncthreads();
+
+  int zr = 1, xr = 2;          // row buffers holding Z and X
+  int zc = 0, ta = 1, tb = 2;  // column buffers holding Z^T and the two T's
+  for (int it = 0; it < iters; ++it) {
+    planes_mm<MP>(sm.rowb[0][0], sm.rowb[0][1], sm.colb[zc][0], sm.colb[zc][1],
+                  [&](int ti, int tj, const f32x4_t& v) {
+                    put_row<MP>(sm.rowb[xr][0], sm.rowb[xr][1], ti, tj, v, 1.f, 0.f);
+                    put_col<MP>(sm.colb[ta][0], sm.colb[ta][1], ti, tj, v, -1.f, 7.f);
+                  });
+    __syncthreads();
+    planes_mm<MP>(sm.rowb[xr][0], sm.rowb[xr][1], sm.colb[ta][0], sm.colb[ta][1],
+                  [&](int ti, int tj, const f32x4_t& v) {
+                    put_col<MP>(sm.colb[tb][0], sm.colb[tb][1], ti, tj, v, -1.f, 15.f);
+                  });
+    __syncthreads();
+    planes_mm<MP>(sm.rowb[xr][0], sm.rowb[xr][1], sm.colb[tb][0], sm.colb[tb][1],
+                  [&](int ti, int tj, const f32x4_t& v) {
+                    put_col<MP>(sm.colb[ta][0], sm.colb[ta][1], ti, tj, v, -1.f, 13.f);
+                  });
+    __syncthreads();
+    // Z' = Z T5 / 4 into the dead X row buffer and the dead T3 column buffer.
+    planes_mm<MP>(sm.rowb[zr][0], sm.rowb[zr][1], sm.colb[ta][0], sm.colb[ta][1],
+                  [&](int ti, int tj, const f32x4_t& v) {
+                    put_row<MP>(sm.rowb[xr][0], sm.rowb[xr][1], ti, tj, v, 0.25f, 0.f);
+                    put_col<MP>(sm.colb[tb][0], sm.colb[tb][1], ti, tj, v, 0.25f, 0.f);
+                  });
+    __syncthreads();
+    const int t0 = zr;
+    zr = xr;
+    xr = t0;
+    const int t1 = zc;
+    zc = tb;
+    tb = t1;
+  }
+  float* zo = Zout + (size_t)bh * m * m;
+  for (int e = tid; e < m * m; e += 256) {
+    const int i = e / m, j = e % m;
+    zo[e] = bf16_to_f32(sm.rowb[zr][0][i * LD + j]) + bf16_to_f32(sm.rowb[zr][1][i * LD + j]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pseudoinverse for 64 < m <= 256, step 1: A rows.  grid (ceil(m/16), batch*heads).
 // Each block computes 16 rows of the scaled scores with the matrix cores,
 // then row softmax in LDS.
@@ -391,11 +624,19 @@ __global__ __launch_bounds__(256) void k_mm(MMArgs a) {
 // Wave w owns landmark tiles w*NTW .. w*NTW+NTW-1 (16 landmarks each).
 template <typename IO, int D>
 struct BvSmem {
-  static constexpr int KP = D + 8;   // K row pitch (bf16 elements)
-  static constexpr int VP = 64 + 8;  // V^T row pitch
+  static constexpr int KP = D + 8;   // K row pitch (bf16 elements; rows 16-byte aligned)
+  static constexpr int VP = 64 + 2;  // V^T row pitch: 33 dwords spreads the 2-row writes over all banks
   static constexpr int PL = IO::kBf16 ? 1 : 2;  // planes: bf16 input is exact, fp32 is split hi/lo
-  uint16_t k[PL][64 * KP];
-  uint16_t vt[PL][D * VP];
+  __align__(16) uint16_t k[PL][64 * KP];
+  __align__(16) uint16_t vt[PL][D * VP];
+};
+
+// One staging task = 2 consecutive keys x 8 features of K and of V.
+template <typename IO>
+struct BvStage {
+  using T = typename IO::T;
+  static constexpr int W = IO::kBf16 ? 1 : 2;  // uint4 per 8 elements
+  uint4 k[2][W], v[2][W];
 };
 
 template <typename IO, int D, int NTW>
@@ -443,31 +684,73 @@ __global__ __launch_bounds__(256) void k_landmark_bv(const typename IO::T* __res
     for (int md = 0; md < MD; ++md) acc[t][md] = zero4();
   }
 
-  for (int k0 = kbeg; k0 < kend; k0 += 64) {
-    // Stage 64 keys of K (row-major) and V (transposed) in LDS, zero past kend.
-    constexpr int SLOTS = D / 8;
-    for (int e = tid; e < 64 * SLOTS; e += 256) {
-      const int r = e / SLOTS, s8 = (e % SLOTS) * 8;
-      float kx[8], vx[8];
-      if (k0 + r < kend) {
-        load8f<IO>(Kh + (size_t)(k0 + r) * D + s8, kx);
-        load8f<IO>(Vh + (size_t)(k0 + r) * D + s8, vx);
-      } else {
+  // Staging is software-pipelined: the next tile's K and V rows are loaded
+  // into registers while the current tile is computed from LDS.
+  constexpr int SLOTS = D / 8;
+  constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
+  constexpr int TPT = (TASKS + 255) / 256;         // tasks per thread
+  BvStage<IO> st[TPT];
+  auto load_tile = [&](int k0) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) kx[q] = vx[q] = 0.f;
-      }
-      B8 kh, kl, vh, vl;
-      split8(kx, kh, kl);
-      split8(vx, vh, vl);
-      *reinterpret_cast<uint4*>(&sm.k[0][r * SM::KP + s8]) = kh.q;
-      if constexpr (SM::PL == 2) *reinterpret_cast<uint4*>(&sm.k[1][r * SM::KP + s8]) = kl.q;
+    for (int u = 0; u < TPT; ++u) {
+      const int e = tid + 256 * u;
+      const int rp = e / SLOTS, s8 = (e % SLOTS) * 8;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        sm.vt[0][(s8 + q) * SM::VP + r] = vh.h[q];
-        if constexpr (SM::PL == 2) sm.vt[1][(s8 + q) * SM::VP + r] = vl.h[q];
+      for (int h = 0; h < 2; ++h) {
+        const int key = k0 + 2 * rp + h;
+        const bool in = e < TASKS && key < kend;
+#pragma unroll
+        for (int w = 0; w < BvStage<IO>::W; ++w) {
+          st[u].k[h][w] = in ? reinterpret_cast<const uint4*>(Kh + (size_t)key * D + s8)[w] : make_uint4(0, 0, 0, 0);
+          st[u].v[h][w] = in ? reinterpret_cast<const uint4*>(Vh + (size_t)key * D + s8)[w] : make_uint4(0, 0, 0, 0);
+        }
       }
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int e = tid + 256 * u;
+      if (e >= TASKS) continue;
+      const int rp = e / SLOTS, s8 = (e % SLOTS) * 8;
+      B8 kh[2], kl[2], vh[2], vl[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (IO::kBf16) {
+          kh[h].q = st[u].k[h][0];
+          vh[h].q = st[u].v[h][0];
+        } else {
+          float kx[8], vx[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            kx[q] = __uint_as_float((&st[u].k[h][0].x)[q]);
+            kx[4 + q] = __uint_as_float((&st[u].k[h][1].x)[q]);
+            vx[q] = __uint_as_float((&st[u].v[h][0].x)[q]);
+            vx[4 + q] = __uint_as_float((&st[u].v[h][1].x)[q]);
+          }
+          split8(kx, kh[h], kl[h]);
+          split8(vx, vh[h], vl[h]);
+        }
+        *reinterpret_cast<uint4*>(&sm.k[0][(2 * rp + h) * SM::KP + s8]) = kh[h].q;
+        if constexpr (SM::PL == 2) *reinterpret_cast<uint4*>(&sm.k[1][(2 * rp + h) * SM::KP + s8]) = kl[h].q;
+      }
+      // V^T: feature s8+q, keys 2rp and 2rp+1 packed in one dword.
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        *reinterpret_cast<uint32_t*>(&sm.vt[0][(s8 + q) * SM::VP + 2 * rp]) =
+            (uint32_t)vh[0].h[q] | ((uint32_t)vh[1].h[q] << 16);
+        if constexpr (SM::PL == 2)
+          *reinterpret_cast<uint32_t*>(&sm.vt[1][(s8 + q) * SM::VP + 2 * rp]) =
+              (uint32_t)vl[0].h[q] | ((uint32_t)vl[1].h[q] << 16);
+      }
+    }
+  };
+
+  load_tile(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += 64) {
+    store_tile();
     __syncthreads();
+    if (k0 + 64 < kend) load_tile(k0 + 64);
 
     // K operand fragments for the 4 key tiles of 16 (shared by all landmark tiles).
 #pragma unroll
@@ -577,45 +860,81 @@ __global__ __launch_bounds__(256) void k_landmark_bv(const typename IO::T* __res
   }
 }
 
-// Fixed-order combine of the split-n partials.  grid (ceil(m*D/256), batch*heads).
-__global__ __launch_bounds__(256) void k_bv_combine(const float* __restrict__ pacc, const float* __restrict__ pmax,
-                                                    const float* __restrict__ psum, float* __restrict__ BV, int m,
-                                                    int D, int nchunks) {
-  const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= m * D) return;
-  const int j = e / D, cc = e % D;
-  const size_t b0 = (size_t)bh * nchunks * m + j;
-  float M = -INFINITY;
-  for (int ch = 0; ch < nchunks; ++ch) M = fmaxf(M, pmax[b0 + (size_t)ch * m]);
-  float L = 0.f, S = 0.f;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const float w = exp2f(pmax[b0 + (size_t)ch * m] - M);
-    L += psum[b0 + (size_t)ch * m] * w;
-    S += pacc[(b0 + (size_t)ch * m) * D + cc] * w;
+// Finish of the split-n pass, one block per (16-feature slice, head):
+//   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
+//   (M_j = max_c pmax_c[j]; chunks in fixed order), then W = Z BV for the
+//   slice in fp32, then the slice's rows of the W^T bf16 planes [bh][D][mpa],
+//   the A operand of the output stage: within each chunk of 32 landmarks,
+//   position 8g + q holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4),
+//   the order in which that stage's softmax lanes hold their landmarks;
+//   padding is zero.  grid (D/16, batch*heads).
+template <bool ZLDS>
+__global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pacc, const float* __restrict__ pmax,
+                                                    const float* __restrict__ psum, const float* __restrict__ Z,
+                                                    float* __restrict__ BV, float* __restrict__ W,
+                                                    uint16_t* __restrict__ wt_hi, uint16_t* __restrict__ wt_lo, int m,
+                                                    int D, int nchunks, int mpa) {
+  __shared__ float sbv[256][17];
+  __shared__ float sw[256][17];
+  __shared__ __align__(16) float sz[ZLDS ? 64 * 68 : 4];
+  const int bh = blockIdx.y, f0 = blockIdx.x * 16, tid = threadIdx.x;
+  const int f = tid & 15;
+  const float* z = Z + (size_t)bh * m * m;
+  if constexpr (ZLDS) {
+    for (int e = tid; e < m * m; e += 1024) sz[(e / m) * 68 + e % m] = z[e];
   }
-  BV[((size_t)bh * m + j) * D + cc] = S / L;
-}
-
-
-// W (fp32 [bh][m][D]) -> bf16 hi/lo planes of W^T [bh][D][mpa], the A operand
-// of the output stage: within each chunk of 32 landmarks, position 8g + q
-// holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4), the order in
-// which that stage's softmax lanes hold their landmarks.  Padding is zero.
-// grid (ceil(D*mpa/256), batch*heads).
-__global__ __launch_bounds__(256) void k_prep_w(const float* __restrict__ W, uint16_t* __restrict__ wt_hi,
-                                                uint16_t* __restrict__ wt_lo, int m, int D, int mpa) {
-  const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= D * mpa) return;
-  const int dd = e / mpa, pos = e % mpa;
-  const int kk = pos >> 5, r = pos & 31, g = r >> 3, q = r & 7;
-  const int lm = kk * 32 + (q < 4 ? 4 * g + q : 16 + 4 * g + q - 4);
-  const float v = lm < m ? W[((size_t)bh * m + lm) * D + dd] : 0.f;
-  uint16_t hi, lo;
-  split_hi_lo(v, hi, lo);
-  wt_hi[(size_t)bh * D * mpa + e] = hi;
-  wt_lo[(size_t)bh * D * mpa + e] = lo;
+  const size_t pb = (size_t)bh * nchunks * m;
+  for (int j = tid >> 4; j < m; j += 64) {
+    // Online combine over the chunks in fixed order, 8 chunks' loads in flight.
+    float M = -INFINITY, L = 0.f, S = 0.f;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      float pm[8], ps[8], pa[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = c0 + u < nchunks;
+        const size_t o = pb + (size_t)(in ? c0 + u : 0) * m + j;
+        pm[u] = in ? pmax[o] : -INFINITY;
+        ps[u] = in ? psum[o] : 0.f;
+        pa[u] = in ? pacc[o * D + f0 + f] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunks) {
+          const float Mn = fmaxf(M, pm[u]);
+          const float a = exp2f(M - Mn), b = exp2f(pm[u] - Mn);
+          L = L * a + ps[u] * b;
+          S = S * a + pa[u] * b;
+          M = Mn;
+        }
+      }
+    }
+    const float v = S / L;
+    sbv[j][f] = v;
+    BV[((size_t)bh * m + j) * D + f0 + f] = v;
+  }
+  __syncthreads();
+  for (int i = tid >> 4; i < m; i += 64) {
+    float acc = 0.f;
+    if constexpr (ZLDS) {
+      for (int k = 0; k < m; ++k) acc = fmaf(sz[i * 68 + k], sbv[k][f], acc);
+    } else {
+      for (int k = 0; k < m; ++k) acc = fmaf(z[(size_t)i * m + k], sbv[k][f], acc);
+    }
+    sw[i][f] = acc;
+    W[((size_t)bh * m + i) * D + f0 + f] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < 16 * mpa; e += 1024) {
+    const int ff = e / mpa, pos = e % mpa;
+    const int kk = pos >> 5, r = pos & 31, g = r >> 3, q = r & 7;
+    const int lm = kk * 32 + (q < 4 ? 4 * g + q : 16 + 4 * g + q - 4);
+    const float v = lm < m ? sw[lm][ff] : 0.f;
+    uint16_t hi, lo;
+    split_hi_lo(v, hi, lo);
+    const size_t o = ((size_t)bh * D + f0 + ff) * mpa + pos;
+    wt_hi[o] = hi;
+    wt_lo[o] = lo;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -645,11 +964,30 @@ hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
 
 // Landmark-side m x m products: fp32-grade for fp32 I/O, bf16x3 for bf16 I/O
 // (where the output rounding dominates the error).
+template <int MP>
+static hipError_t pinv_planes_t(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads;
+  const float sl2e = kLog2e / sqrtf((float)p.d);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_planes<MP>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)sizeof(PinvPlanes<MP>));
+  if (attr != hipSuccess) return attr;
+  KernelTimer kt_("pinv", s);
+  k_pinv_planes<MP><<<BH, 256, sizeof(PinvPlanes<MP>), s>>>(w.Qt, w.Kt, w.A, w.Z, p.m, p.d, sl2e, p.iters);
+  return hipSuccess;
+}
+
 template <int PR>
 static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads, m = p.m, D = p.d;
   const float sl2e = kLog2e / sqrtf((float)D);
-  if (m <= 32) {
+  if (PR == 3 && m <= 32) {
+    hipError_t e = pinv_planes_t<32>(p, w, s);
+    return e != hipSuccess ? e : hipGetLastError();
+  } else if (PR == 3 && m <= 64) {
+    hipError_t e = pinv_planes_t<64>(p, w, s);
+    return e != hipSuccess ? e : hipGetLastError();
+  } else if (m <= 32) {
     KernelTimer kt_("pinv", s);
     k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
   } else if (m <= 64) {
@@ -699,18 +1037,13 @@ static void bv_t(const Problem& p, const Ws& w, hipStream_t s) {
   const T* K = static_cast<const T*>(p.K);
   const T* V = static_cast<const T*>(p.V);
   const dim3 g(w.nchunks, BH);
-  {
-    KernelTimer kt_("landmark_bv", s);
-    if (m <= 64)
-      k_landmark_bv<IO, D, 1><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
-    else if (m <= 128)
-      k_landmark_bv<IO, D, 2><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
-    else
-      k_landmark_bv<IO, D, 4><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
-  }
-  KernelTimer kt_("bv_combine", s);
-  k_bv_combine<<<dim3(ceil_div((long long)m * D, 256), BH), 256, 0, s>>>(w.pacc, w.pmax, w.psum, w.BV, m, D,
-                                                                        w.nchunks);
+  KernelTimer kt_("landmark_bv", s);
+  if (m <= 64)
+    k_landmark_bv<IO, D, 1><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+  else if (m <= 128)
+    k_landmark_bv<IO, D, 2><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+  else
+    k_landmark_bv<IO, D, 4><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
 }
 
 hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s) {
@@ -724,21 +1057,15 @@ hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int PR>
-static void w_t(const Problem& p, const Ws& w, hipStream_t s) {
-  const int BH = p.batch * p.heads, m = p.m, D = p.d;
-  {
-    KernelTimer kt_("w_mm", s);
-    k_mm<PR><<<dim3(ceil_div(D, 64), ceil_div(m, 64), BH), 256, 0, s>>>(
-        MMArgs{w.Z, w.BV, w.W, nullptr, m, D, m, (long long)m * m, (long long)m * D, (long long)m * D, 1.f, 0.f,
-               0.f, 0.f});
-  }
-  KernelTimer kt_("prep_w", s);
-  k_prep_w<<<dim3(ceil_div((long long)D * w.mpa, 256), BH), 256, 0, s>>>(w.W, w.wt_hi, w.wt_lo, m, D, w.mpa);
-}
-
-hipError_t stage_w(const Problem& p, const Ws& w, hipStream_t s) {
-  p.bf16 ? w_t<3>(p, w, s) : w_t<6>(p, w, s);
+hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads;
+  KernelTimer kt_("bv_finish", s);
+  if (p.m <= 64)
+    k_bv_finish<true><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi, w.wt_lo,
+                                                         p.m, p.d, w.nchunks, w.mpa);
+  else
+    k_bv_finish<false><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi, w.wt_lo,
+                                                          p.m, p.d, w.nchunks, w.mpa);
   return hipGetLastError();
 }
 
