@@ -261,215 +261,287 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 }
 
 // ---------------------------------------------------------------------------
-// Pseudoinverse for m <= 64 with bf16x3 products (bf16 I/O): every iterate is
-// kept in LDS only as bf16 hi/lo planes, written once by the wave that
-// produces it in the layout its consumers read, so a matrix-core fragment is
-// one 16-byte LDS read per plane.  In C = P Q, P is read row-major ([row][k])
-// and Q column-major ([col][k]).  A wave's result tile holds 4 consecutive
-// rows of one column: column-major outputs are 8-byte writes, row-major ones
-// 2-byte writes.
-//   1. X  = A Z      -> X row-major, T1 = 7I - X column-major
-//   2. U  = X T1     -> T3 = 15I - U column-major
-//   3. V  = X T3     -> T5 = 13I - V column-major
-//   4. Z' = Z T5 / 4 -> Z' row-major and column-major
-// Row buffers: A, R0, R1 (X and Z alternate); column buffers K0, K1, K2
-// (Z^T and the two T's rotate).
+// Pseudoinverse for m <= 64 with bf16x3 products (bf16 I/O).  One block of
+// MP/16 waves per head; wave j owns column block j (16 columns, all MP rows)
+// of every iterate.  In C = P R the right operand's column block comes from
+// the wave's own registers: a result in the matrix-core C layout (lane (c, g)
+// holds rows 4g..4g+3 of column c of each 16-row tile) is already a B operand
+// once the contraction index of every 32-chunk is taken in the order
+//   slot 8g + q  <->  k = 4g + q (q < 4),  16 + 4g + (q - 4) (q >= 4).
+// Only the left operands X = A Z and Z, which every wave needs whole, go
+// through LDS, as bf16 hi/lo planes, row-major with each row's columns stored
+// in that slot order (so a left-operand fragment is one 16-byte read per
+// plane).  A stays in registers.  One iteration
+//   X = A Z;  T = 7I - X;  T = 15I - X T;  T = 13I - X T;  Z = Z T / 4
+// has a single barrier (after X is stored): the X and Z planes are
+// double-buffered, and every buffer is rewritten only after all waves have
+// passed the barrier that follows its last read.
 template <int MP>
-struct PinvPlanes {
+struct PinvSmem2 {
   static constexpr int LD = MP + 8;  // plane row pitch (bf16): rows stay 16-byte aligned
   static constexpr int PL = MP * LD;
-  __align__(16) uint16_t rowb[3][2][PL];
-  __align__(16) uint16_t colb[3][2][PL];
-  float red[2][MP];
+  static constexpr int SP = MP + 4;  // fp32 score row pitch
+  __align__(16) uint16_t xp[2][2][PL];  // X planes [buffer][hi, lo]
+  __align__(16) uint16_t zp[2][2][PL];  // Z planes [buffer][hi, lo]
+  __align__(16) float S[MP * SP];       // scaled scores, then A
+  float colp[4][MP];                    // partial column sums of A
+  float rows[MP];                       // row sums of A
 };
 
+// B operand (chunks kc) of this wave's column block j from C-layout tiles v:
+// slot q of chunk kc is element q % 4 of tile 2kc + q / 4, as
+// scale * v + alpha * (row == column), split into bf16 hi/lo.
 template <int MP>
-__device__ __forceinline__ void put_split(uint16_t* hi, uint16_t* lo, int idx, float v) {
-  uint16_t h, l;
-  split_hi_lo(v, h, l);
-  hi[idx] = h;
-  lo[idx] = l;
-}
-
-// C = P Q (MP x MP) from planes; epi(ti, tj, acc) gets the tile whose lane
-// (c, g) holds C[ti*16 + 4g + i][tj*16 + c], i = 0..3.
-template <int MP, typename Epi>
-__device__ __forceinline__ void planes_mm(const uint16_t* Ph, const uint16_t* Pl, const uint16_t* Qh,
-                                          const uint16_t* Ql, Epi epi) {
-  constexpr int LD = PinvPlanes<MP>::LD, NT = MP / 16, TPW = NT * NT / 4, KC = MP / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
-  const int ti = (wave * TPW) / NT;  // every tile of a wave shares its row block
-  B8 ah[KC], al[KC];
+__device__ __forceinline__ void to_bop(const f32x4_t (&v)[MP / 16], float scale, float alpha, int j,
+                                       B8 (&bh)[MP / 32], B8 (&bl)[MP / 32]) {
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int col = 16 * j + c;
 #pragma unroll
-  for (int kc = 0; kc < KC; ++kc) {
-    const int o = (ti * 16 + c) * LD + kc * 32 + 8 * g;
-    ah[kc].q = *reinterpret_cast<const uint4*>(Ph + o);
-    al[kc].q = *reinterpret_cast<const uint4*>(Pl + o);
-  }
+  for (int kc = 0; kc < MP / 32; ++kc)
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tj = (wave * TPW + tt) % NT;
-    f32x4_t acc = zero4();
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int o = (tj * 16 + c) * LD + kc * 32 + 8 * g;
-      B8 bh, bl;
-      bh.q = *reinterpret_cast<const uint4*>(Qh + o);
-      bl.q = *reinterpret_cast<const uint4*>(Ql + o);
-      acc = mfma3(ah[kc], al[kc], bh, bl, acc);
+    for (int q = 0; q < 8; ++q) {
+      const int t = 2 * kc + q / 4, i = q % 4;
+      const float x = scale * v[t][i] + (16 * t + 4 * g + i == col ? alpha : 0.f);
+      split_hi_lo(x, bh[kc].h[q], bl[kc].h[q]);
     }
-    epi(ti, tj, acc);
+}
+
+// Stores a column block held as B-operand planes into row-major planes with
+// slot-ordered columns (2-byte writes).
+template <int MP>
+__device__ __forceinline__ void store_bop(uint16_t* h, uint16_t* l, const B8 (&bh)[MP / 32],
+                                          const B8 (&bl)[MP / 32], int j) {
+  constexpr int LD = PinvSmem2<MP>::LD;
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int slot = 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3);
+#pragma unroll
+  for (int kc = 0; kc < MP / 32; ++kc)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int o = (16 * (2 * kc + q / 4) + 4 * g + q % 4) * LD + slot;
+      h[o] = bh[kc].h[q];
+      l[o] = bl[kc].h[q];
+    }
+}
+
+// Left-operand fragments of all row tiles from slot-ordered planes.
+template <int MP>
+__device__ __forceinline__ void load_aop(const uint16_t* h, const uint16_t* l, B8 (&ah)[MP / 16][MP / 32],
+                                         B8 (&al)[MP / 16][MP / 32]) {
+  constexpr int LD = PinvSmem2<MP>::LD;
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < MP / 16; ++t)
+#pragma unroll
+    for (int kc = 0; kc < MP / 32; ++kc) {
+      const int o = (16 * t + c) * LD + 32 * kc + 8 * g;
+      ah[t][kc].q = *reinterpret_cast<const uint4*>(h + o);
+      al[t][kc].q = *reinterpret_cast<const uint4*>(l + o);
+    }
+}
+
+// acc[t] = P(t) R for every row tile t (bf16x3).
+template <int MP>
+__device__ __forceinline__ void chain_mm(const B8 (&ph)[MP / 16][MP / 32], const B8 (&pl)[MP / 16][MP / 32],
+                                         const B8 (&rh)[MP / 32], const B8 (&rl)[MP / 32],
+                                         f32x4_t (&acc)[MP / 16]) {
+#pragma unroll
+  for (int t = 0; t < MP / 16; ++t) {
+    acc[t] = zero4();
+#pragma unroll
+    for (int kc = 0; kc < MP / 32; ++kc) acc[t] = mfma3(ph[t][kc], pl[t][kc], rh[kc], rl[kc], acc[t]);
   }
 }
 
-// Writers for a result tile (lane (c, g): rows ti*16+4g+i, column tj*16+c)
-// of alpha*I + scale*acc.
-template <int MP>
-__device__ __forceinline__ void put_col(uint16_t* h, uint16_t* l, int ti, int tj, const f32x4_t& acc, float scale,
-                                        float alpha) {
-  constexpr int LD = PinvPlanes<MP>::LD;
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-  const int col = tj * 16 + c, row0 = ti * 16 + 4 * g;
-  B8 hv, lv;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) split_hi_lo(scale * acc[i] + (row0 + i == col ? alpha : 0.f), hv.h[i], lv.h[i]);
-  *reinterpret_cast<uint2*>(h + col * LD + row0) = make_uint2(hv.u[0], hv.u[1]);
-  *reinterpret_cast<uint2*>(l + col * LD + row0) = make_uint2(lv.u[0], lv.u[1]);
-}
-
-template <int MP>
-__device__ __forceinline__ void put_row(uint16_t* h, uint16_t* l, int ti, int tj, const f32x4_t& acc, float scale,
-                                        float alpha) {
-  constexpr int LD = PinvPlanes<MP>::LD;
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-  const int col = tj * 16 + c, row0 = ti * 16 + 4 * g;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) put_split<MP>(h, l, (row0 + i) * LD + col, scale * acc[i] + (row0 + i == col ? alpha : 0.f));
-}
-
-template <int MP>
-__global__ __launch_bounds__(256) void k_pinv_planes(const float* __restrict__ Qt, const float* __restrict__ Kt,
-                                                     float* __restrict__ Aout, float* __restrict__ Zout, int m,
-                                                     int d, float sl2e, int iters) {
+// grid (batch*heads), block 64 * MP/16.
+template <int MP, int D>
+__global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict__ Qt, const float* __restrict__ Kt,
+                                                        float* __restrict__ Aout, float* __restrict__ Zout, int m,
+                                                        float sl2e, int iters) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  using SM = PinvPlanes<MP>;
-  constexpr int LD = SM::LD, NT = MP / 16, SP = MP + 4;
+  using SM = PinvSmem2<MP>;
+  constexpr int SP = SM::SP, RT = MP / 16, KC = MP / 32, CPT = MP / 4;
+  constexpr int KCD = (D + 31) / 32;  // 32-wide chunks of the head dimension
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  // fp32 scratch for the scores / A, aliased on column buffers K1, K2.
-  float* S = reinterpret_cast<float*>(&sm.colb[1][0][0]);
-  static_assert(sizeof(float) * MP * SP <= sizeof(uint16_t) * 4 * SM::PL, "scratch does not fit");
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const float* qt = Qt + (size_t)bh * m * d;
-  const float* kt = Kt + (size_t)bh * m * d;
+  const float* qt = Qt + (size_t)bh * m * D;
+  const float* kt = Kt + (size_t)bh * m * D;
 
-  // Scaled scores (Kt Qt^T)^T: lane ends with row ti*16+c, columns tj*16+4g..+3.
-  for (int t = wave; t < NT * NT; t += 4) {
-    const int ti = t / NT, tj = t % NT;
-    const int rq = ti * 16 + c, rk = tj * 16 + c;
-    f32x4_t acc = zero4();
-    for (int kc = 0; kc < d; kc += 32) {
-      float a[8], b[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kk = kc + 8 * g + q;
-        a[q] = (rk < m && kk < d) ? kt[rk * d + kk] : 0.f;
-        b[q] = (rq < m && kk < d) ? qt[rq * d + kk] : 0.f;
-      }
-      acc = mma_f32<3>(a, b, acc);
-    }
-    *reinterpret_cast<float4*>(&S[rq * SP + tj * 16 + 4 * g]) =
-        make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
-  }
-  __syncthreads();
-  // Row softmax over the m real columns; padded rows/columns are 0.
+  // Scaled scores of row block `wave`, computed transposed ((Kt Qt^T)^T) so
+  // that lane (c, g) of tile tj ends with row 16*wave+c, columns 16tj+4g..+3.
+  // Every fragment load is issued before the first product (rows and columns
+  // are clamped in bounds and masked to zero outside).
   {
-    constexpr int TPR = 256 / MP;
-    const int r = tid / TPR, sub = tid % TPR;
-    float mx = -INFINITY;
-    for (int j = sub; j < m; j += TPR) mx = fmaxf(mx, S[r * SP + j]);
+    const int rq = 16 * wave + c;
+    float4 qv[KCD][2], kv[RT][KCD][2];
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
-    float s = 0.f;
-    for (int j = sub; j < MP; j += TPR) {
-      const float e = (r < m && j < m) ? exp2f(S[r * SP + j] - mx) : 0.f;
-      S[r * SP + j] = e;
-      s += e;
-    }
+    for (int kc = 0; kc < KCD; ++kc) {
+      const int k0 = min(32 * kc + 8 * g, D - 8);
+      const float* src = qt + (size_t)min(rq, m - 1) * D + k0;
+      qv[kc][0] = *reinterpret_cast<const float4*>(src);
+      qv[kc][1] = *reinterpret_cast<const float4*>(src + 4);
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) s += shfl_xor(s, o);
-    if (r < m) {
-      const float inv = 1.f / s;
-      for (int j = sub; j < m; j += TPR) S[r * SP + j] *= inv;
+      for (int tj = 0; tj < RT; ++tj) {
+        const float* ks = kt + (size_t)min(16 * tj + c, m - 1) * D + k0;
+        kv[tj][kc][0] = *reinterpret_cast<const float4*>(ks);
+        kv[tj][kc][1] = *reinterpret_cast<const float4*>(ks + 4);
+      }
     }
-  }
-  __syncthreads();
-  if (tid < MP) {
-    float cs = 0.f, rs = 0.f;
-    for (int i = 0; i < MP; ++i) {
-      cs += fabsf(S[i * SP + tid]);
-      rs += fabsf(S[tid * SP + i]);
+    auto frag = [](const float4 (&v)[2], bool ok, B8& h, B8& l) {
+      const float x[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+      float y[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[q] = ok ? x[q] : 0.f;
+      split8(y, h, l);
+    };
+    B8 qh[KCD], ql[KCD];
+#pragma unroll
+    for (int kc = 0; kc < KCD; ++kc) frag(qv[kc], rq < m && 32 * kc + 8 * g < D, qh[kc], ql[kc]);
+#pragma unroll
+    for (int tj = 0; tj < RT; ++tj) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KCD; ++kc) {
+        B8 kh, kl;
+        frag(kv[tj][kc], 16 * tj + c < m && 32 * kc + 8 * g < D, kh, kl);
+        acc = mfma3(kh, kl, qh[kc], ql[kc], acc);
+      }
+      *reinterpret_cast<float4*>(&sm.S[rq * SP + 16 * tj + 4 * g]) =
+          make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
     }
-    sm.red[0][tid] = cs;
-    sm.red[1][tid] = rs;
-  }
-  __syncthreads();
-  float n1 = 0.f, ninf = 0.f;
-  for (int i = 0; i < MP; ++i) {
-    n1 = fmaxf(n1, sm.red[0][i]);
-    ninf = fmaxf(ninf, sm.red[1][i]);
-  }
-  const float cz = 1.f / (n1 * ninf);
-  // A -> row planes (buffer 0) and the output; Z0 = cz A^T -> row planes R0 and
-  // column planes K0 (Z0^T = cz A, i.e. K0[j][i] = cz A[j][i]).
-  float* ao = Aout + (size_t)bh * m * m;
-  for (int e = tid; e < MP * MP; e += 256) {
-    const int i = e / MP, j = e % MP;
-    const float a = S[i * SP + j];
-    put_split<MP>(sm.rowb[0][0], sm.rowb[0][1], i * LD + j, a);
-    put_split<MP>(sm.colb[0][0], sm.colb[0][1], i * LD + j, cz * a);
-    put_split<MP>(sm.rowb[1][0], sm.rowb[1][1], j * LD + i, cz * a);
-    if (i < m && j < m) ao[i * m + j] = a;
   }
   __syncthreads();
 
-  int zr = 1, xr = 2;          // row buffers holding Z and X
-  int zc = 0, ta = 1, tb = 2;  // column buffers holding Z^T and the two T's
-  for (int it = 0; it < iters; ++it) {
-    planes_mm<MP>(sm.rowb[0][0], sm.rowb[0][1], sm.colb[zc][0], sm.colb[zc][1],
-                  [&](int ti, int tj, const f32x4_t& v) {
-                    put_row<MP>(sm.rowb[xr][0], sm.rowb[xr][1], ti, tj, v, 1.f, 0.f);
-                    put_col<MP>(sm.colb[ta][0], sm.colb[ta][1], ti, tj, v, -1.f, 7.f);
-                  });
-    __syncthreads();
-    planes_mm<MP>(sm.rowb[xr][0], sm.rowb[xr][1], sm.colb[ta][0], sm.colb[ta][1],
-                  [&](int ti, int tj, const f32x4_t& v) {
-                    put_col<MP>(sm.colb[tb][0], sm.colb[tb][1], ti, tj, v, -1.f, 15.f);
-                  });
-    __syncthreads();
-    planes_mm<MP>(sm.rowb[xr][0], sm.rowb[xr][1], sm.colb[tb][0], sm.colb[tb][1],
-                  [&](int ti, int tj, const f32x4_t& v) {
-                    put_col<MP>(sm.colb[ta][0], sm.colb[ta][1], ti, tj, v, -1.f, 13.f);
-                  });
-    __syncthreads();
-    // Z' = Z T5 / 4 into the dead X row buffer and the dead T3 column buffer.
-    planes_mm<MP>(sm.rowb[zr][0], sm.rowb[zr][1], sm.colb[ta][0], sm.colb[ta][1],
-                  [&](int ti, int tj, const f32x4_t& v) {
-                    put_row<MP>(sm.rowb[xr][0], sm.rowb[xr][1], ti, tj, v, 0.25f, 0.f);
-                    put_col<MP>(sm.colb[tb][0], sm.colb[tb][1], ti, tj, v, 0.25f, 0.f);
-                  });
-    __syncthreads();
-    const int t0 = zr;
-    zr = xr;
-    xr = t0;
-    const int t1 = zc;
-    zc = tb;
-    tb = t1;
+  // Row softmax: four adjacent lanes per row, CPT columns each.  Padded rows
+  // and columns become 0.
+  {
+    const int r = tid >> 2, sub = tid & 3, j0 = sub * CPT;
+    float a[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u) {
+      const float4 v = *reinterpret_cast<const float4*>(&sm.S[r * SP + j0 + 4 * u]);
+      a[4 * u] = v.x; a[4 * u + 1] = v.y; a[4 * u + 2] = v.z; a[4 * u + 3] = v.w;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      if (j0 + q < m) mx = fmaxf(mx, a[q]);
+    mx = fmaxf(mx, shfl_xor(mx, 1));
+    mx = fmaxf(mx, shfl_xor(mx, 2));
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      a[q] = (r < m && j0 + q < m) ? exp2f(a[q] - mx) : 0.f;
+      sum += a[q];
+    }
+    sum += shfl_xor(sum, 1);
+    sum += shfl_xor(sum, 2);
+    const float inv = r < m ? 1.f / sum : 0.f;
+    float rs = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      a[q] *= inv;
+      rs += a[q];
+    }
+    rs += shfl_xor(rs, 1);
+    rs += shfl_xor(rs, 2);
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u)
+      *reinterpret_cast<float4*>(&sm.S[r * SP + j0 + 4 * u]) = make_float4(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
+    if (sub == 0) sm.rows[r] = rs;
   }
-  float* zo = Zout + (size_t)bh * m * m;
-  for (int e = tid; e < m * m; e += 256) {
-    const int i = e / m, j = e % m;
-    zo[e] = bf16_to_f32(sm.rowb[zr][0][i * LD + j]) + bf16_to_f32(sm.rowb[zr][1][i * LD + j]);
+  __syncthreads();
+  {  // partial column sums over quarters of the rows
+    const int col = tid % MP, part = tid / MP;
+    float s = 0.f;
+#pragma unroll 4
+    for (int rr = 0; rr < MP / 4; ++rr) s += sm.S[(part * (MP / 4) + rr) * SP + col];
+    sm.colp[part][col] = s;
+  }
+  __syncthreads();
+  // ||A||_1 (max column sum) and ||A||_inf (max row sum; entries are >= 0).
+  float cz;
+  {
+    const int k = lane % MP;
+    float cs = sm.colp[0][k] + sm.colp[1][k] + sm.colp[2][k] + sm.colp[3][k];
+    float rm = sm.rows[k];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      cs = fmaxf(cs, shfl_xor(cs, o));
+      rm = fmaxf(rm, shfl_xor(rm, o));
+    }
+    cz = 1.f / (cs * rm);
+  }
+
+  // A as register-resident left operand (all row tiles, slot-ordered
+  // columns); Z0 = cz A^T, column block `wave` = cz * (row block `wave` of A).
+  B8 Ah[RT][KC], Al[RT][KC];
+  B8 Zh[KC], Zl[KC];
+  f32x4_t zf[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const float* src = &sm.S[(16 * t + c) * SP + 32 * kc + 4 * g];
+      const float4 u0 = *reinterpret_cast<const float4*>(src);
+      const float4 u1 = *reinterpret_cast<const float4*>(src + 16);
+      const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+      split8(x, Ah[t][kc], Al[t][kc]);
+      if (t == wave) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float z = cz * x[q];
+          split_hi_lo(z, Zh[kc].h[q], Zl[kc].h[q]);
+          zf[2 * kc + q / 4][q % 4] = z;
+        }
+      }
+    }
+  store_bop<MP>(sm.zp[0][0], sm.zp[0][1], Zh, Zl, wave);
+
+  for (int it = 0; it < iters; ++it) {
+    const int p = it & 1;
+    f32x4_t acc[RT];
+    B8 Th[KC], Tl[KC];
+    // X = A Z: store X for every wave; keep T1 = 7I - X (own columns).
+    chain_mm<MP>(Ah, Al, Zh, Zl, acc);
+    {
+      B8 xh[KC], xl[KC];
+      to_bop<MP>(acc, 1.f, 0.f, wave, xh, xl);
+      store_bop<MP>(sm.xp[p][0], sm.xp[p][1], xh, xl, wave);
+    }
+    to_bop<MP>(acc, -1.f, 7.f, wave, Th, Tl);
+    __syncthreads();
+    B8 Ph[RT][KC], Pl[RT][KC], Rh[RT][KC], Rl[RT][KC];
+    load_aop<MP>(sm.xp[p][0], sm.xp[p][1], Ph, Pl);
+    load_aop<MP>(sm.zp[p][0], sm.zp[p][1], Rh, Rl);  // in flight during the two X products
+    chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T1
+    to_bop<MP>(acc, -1.f, 15.f, wave, Th, Tl);
+    chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T3
+    to_bop<MP>(acc, -1.f, 13.f, wave, Th, Tl);
+    chain_mm<MP>(Rh, Rl, Th, Tl, acc);  // Z T5
+#pragma unroll
+    for (int t = 0; t < RT; ++t) zf[t] = acc[t] * 0.25f;
+    to_bop<MP>(zf, 1.f, 0.f, wave, Zh, Zl);
+    store_bop<MP>(sm.zp[p ^ 1][0], sm.zp[p ^ 1][1], Zh, Zl, wave);
+  }
+
+  // A (kept in LDS; global stores are left to the end so that no barrier
+  // waits on them) and Z in fp32 straight from the last product.
+  {
+    float* ao = Aout + (size_t)bh * m * m;
+    for (int e = tid; e < m * m; e += 4 * MP) ao[e] = sm.S[(e / m) * SP + e % m];
+  }
+  const int col = 16 * wave + c;
+  if (col < m) {
+    float* zo = Zout + (size_t)bh * m * m;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * t + 4 * g + i;
+        if (row < m) zo[(size_t)row * m + col] = zf[t][i];
+      }
   }
 }
 
@@ -964,17 +1036,28 @@ hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
 
 // Landmark-side m x m products: fp32-grade for fp32 I/O, bf16x3 for bf16 I/O
 // (where the output rounding dominates the error).
-template <int MP>
-static hipError_t pinv_planes_t(const Problem& p, const Ws& w, hipStream_t s) {
+template <int MP, int D>
+static hipError_t pinv_planes_launch(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
-  const float sl2e = kLog2e / sqrtf((float)p.d);
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_planes<MP>),
+  const float sl2e = kLog2e / sqrtf((float)D);
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_planes<MP, D>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)sizeof(PinvPlanes<MP>));
+                                                     (int)sizeof(PinvSmem2<MP>));
   if (attr != hipSuccess) return attr;
   KernelTimer kt_("pinv", s);
-  k_pinv_planes<MP><<<BH, 256, sizeof(PinvPlanes<MP>), s>>>(w.Qt, w.Kt, w.A, w.Z, p.m, p.d, sl2e, p.iters);
+  k_pinv_planes<MP, D><<<BH, 4 * MP, sizeof(PinvSmem2<MP>), s>>>(w.Qt, w.Kt, w.A, w.Z, p.m, sl2e, p.iters);
   return hipSuccess;
+}
+
+template <int MP>
+static hipError_t pinv_planes_t(const Problem& p, const Ws& w, hipStream_t s) {
+  switch (p.d) {
+    case 16: return pinv_planes_launch<MP, 16>(p, w, s);
+    case 32: return pinv_planes_launch<MP, 32>(p, w, s);
+    case 64: return pinv_planes_launch<MP, 64>(p, w, s);
+    case 128: return pinv_planes_launch<MP, 128>(p, w, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int PR>
