@@ -6,21 +6,25 @@
 // Figure 4).  The same kernel with the attention part switched off is the
 // standalone depthwise-conv entry point.
 //
-// One block = TQ consecutive rows (queries) of one (batch, head), 4 waves:
-//   A. stage the V rows the skip needs (tile plus a 16-row halo) in LDS,
-//      feature-major (Vt[feature][row]);
-//   B. each wave: scores for its queries against all landmarks on the matrix
-//      cores, transposed (landmarks x queries) so that a query's scores sit in
-//      one lane column; softmax across lanes; then O = F W, whose result tiles
-//      give each lane 4 consecutive queries of one feature -> feature-major
-//      LDS tile Ot[feature][row] (fp32), one 16-byte write per tile;
-//   C. the skip.  bf16 I/O: on the matrix cores with the 16-block 4x4x4
-//      instruction, one block per feature: A = a 4 x 4 band of that feature's
-//      taps (Toeplitz), B = 4 consecutive V rows, 9 steps of 4 taps cover 33
-//      taps for 16 output rows; each lane ends with 4 consecutive rows of one
-//      feature and adds them to Ot with one 16-byte read-modify-write.  fp32
-//      I/O, or one tap: fp32 FMAs by a register sliding window;
-//   D. Ot -> output rows, one 16-byte store per lane, coalesced per row.
+// One block = 64 consecutive rows (queries) of one (batch, head), 4 waves.
+// Blocks are numbered so that each XCD (block L runs on XCD L % 8) takes a
+// contiguous run of tiles: neighbouring tiles share their halo rows and the
+// tiles of a head share Kt/W operands through that XCD's L2.
+//   0. every global load of the tile is issued first (V rows with a 16-row
+//      halo, Q fragments), so that they are in flight during the attention;
+//   1. each wave: scores of its 16 queries against all landmarks on the
+//      matrix cores, transposed (landmarks x queries), so a query's scores sit
+//      in one lane column; softmax across lanes; then O^T = W^T F^T, whose
+//      result tiles give each lane 4 consecutive features of one query ->
+//      row-major fp32 tile Ot[row][feature], one 16-byte write per tile;
+//   2. the V rows -> LDS, feature-major (Vt[feature][row]);
+//   3. the skip, added into Ot.  bf16 I/O: on the matrix cores with the
+//      16-block 4x4x4 instruction, one block per feature: A = a 4 x 4 band of
+//      that feature's taps (Toeplitz; operands prepared once per call by
+//      k_conv_ops), B = 4 consecutive V rows, 9 steps of 4 taps cover 33 taps
+//      for 16 output rows; each lane ends with 4 consecutive rows of one
+//      feature.  fp32 I/O, or one tap: fp32 FMAs by a register sliding window;
+//   4. Ot -> output rows, one 16-byte store per lane, coalesced per row.
 #include <math.h>
 
 #include "nys_common.hpp"
@@ -32,32 +36,98 @@ namespace {
 
 typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 
-template <int D>
-struct ApplyShape {
-  static constexpr int TQ = D >= 128 ? 64 : 128;  // rows per block
-  static constexpr int NQ = TQ / 64;              // 16-query tiles per wave
-  static constexpr int KC = (D + 31) / 32;        // 32-wide chunks of the head dim
-  static constexpr int ND = D / 16;               // 16-feature tiles
-};
+constexpr int kTQ = 64;     // rows per tile: 4 waves x 16 queries
+constexpr int kConvNS = 9;  // 4-tap steps of the matrix-core skip (33 taps)
 
+// Shared-memory layout (bytes) of one block.
 // KW: 0 = no skip, 1 = one tap, 33 = up to 33 taps (zero-padded, centred),
 //     -1 = wider filters (taps and rows read from global memory; slow path).
-template <typename IO, int D, int KW>
-struct ApplySmem {
+template <typename IO, int D, int NTM, int KW, bool ATT>
+struct ApplyLayout {
   using T = typename IO::T;
-  static constexpr int TQ = ApplyShape<D>::TQ;
+  static constexpr int MPA = 16 * NTM;
   static constexpr int HALO = KW == 33 ? 16 : 0;
-  static constexpr int VCOLS = TQ + 2 * HALO;
+  static constexpr int VCOLS = kTQ + 2 * HALO;
   static constexpr bool STAGE = KW == 1 || KW == 33;
-  // Vt row pitch (elements): a multiple of 4 elements for 8/16-byte accesses.
-  static constexpr int VP = VCOLS + (IO::kBf16 ? 16 : 4);
-  static constexpr int OP = TQ + 4;  // Ot row pitch (floats)
-  __align__(16) T vt[STAGE ? D * VP : 4];
-  __align__(16) float ot[D * OP];
+  static constexpr int VP = VCOLS + 4;  // Vt row pitch (elements; 8/16-byte aligned rows)
+  static constexpr int OP = D + 4;      // Ot row pitch (floats)
+  static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
+  static constexpr int WP = MPA + 8;    // W^T plane row pitch (bf16)
+  // The Kt and W^T planes of the current head are kept in LDS when they fit.
+  static constexpr bool KWL = ATT && (4 * MPA * KP + 4 * D * WP) <= 72 * 1024;
+  static constexpr int OT = 0;
+  static constexpr int VT = OT + 4 * kTQ * OP;
+  static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
+  static constexpr int WT = KT + (KWL ? 4 * MPA * KP : 0);
+  static constexpr int BYTES = WT + (KWL ? 4 * D * WP : 0);
+  // V tile loads: task = 4 rows x one 16-byte chunk.
+  static constexpr int FPC = IO::kBf16 ? 8 : 4;  // features per 16-byte chunk
+  static constexpr int NCH = D / FPC;
+  static constexpr int TASKS = (VCOLS / 4) * NCH;
+  static constexpr int NTK = STAGE ? (TASKS + 255) / 256 : 1;
+  static constexpr int QW = IO::kBf16 ? 1 : 2;  // 16-byte words per 8 head-dim elements
 };
+
+// Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) (zero outside
+// [0, n)) into registers.
+template <typename LY, typename T>
+__device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], const T* __restrict__ Vh, int t0, int n) {
+  constexpr int D = LY::NCH * LY::FPC;
+  const bool interior = t0 - LY::HALO >= 0 && t0 + kTQ + LY::HALO <= n;
+#pragma unroll
+  for (int k = 0; k < LY::NTK; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    const int rq = e / LY::NCH, oc = e % LY::NCH;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = t0 - LY::HALO + 4 * rq + q;
+      const bool ok = e < LY::TASKS && (interior || (row >= 0 && row < n));
+      vr[k][q] = ok ? *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + LY::FPC * oc) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Issues the loads of this lane's query fragments (row qrow, head-dim
+// elements 32kc + 8g .. +7 for every chunk kc), zero past n or past D.
+template <typename LY, int D, typename T>
+__device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], const T* __restrict__ Qh, int qrow, int n) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int kc = 0; kc < (D + 31) / 32; ++kc) {
+    const int dd = kc * 32 + 8 * g;
+    const bool ok = qrow < n && (D % 32 == 0 || dd < D);
+#pragma unroll
+    for (int w = 0; w < LY::QW; ++w)
+      qr[kc][w] = ok ? *reinterpret_cast<const uint4*>(Qh + (size_t)qrow * D + dd + 4 * w) : make_uint4(0, 0, 0, 0);
+  }
+}
 
 }  // namespace
 
+// Matrix-core operands of the skip filters for the 16-block 4x4x4 product.
+// Entry ((h * d + f) * 4 + i) * 9 + s holds taps 4s + k - i - off (k = 0..3)
+// of filter (h, f) as bf16 hi (k = 0..3) then bf16 lo, where off =
+// (33 - conv_k) / 2 centres a filter of conv_k <= 33 taps in 33 slots.
+__global__ __launch_bounds__(256) void k_conv_ops(const float* __restrict__ conv_w, uint4* __restrict__ ops,
+                                                  int total, int conv_k) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int st = idx % kConvNS, i = (idx / kConvNS) % 4, hf = idx / (4 * kConvNS);
+  const int off = (33 - conv_k) / 2;
+  B8 hl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int tt = 4 * st + k - i - off;
+    const float w = (tt >= 0 && tt < conv_k) ? conv_w[(size_t)hf * conv_k + tt] : 0.f;
+    split_hi_lo(w, hl.h[k], hl.h[4 + k]);
+  }
+  ops[idx] = hl.q;
+}
+
+// Persistent blocks: block `rank` (XCD-contiguous numbering) processes the
+// run of 64-row tiles [rank * total / G, (rank + 1) * total / G) of the
+// (batch*head)-major tile list; the next tile's V rows and Q fragments are
+// loaded while the current tile is computed.
 template <typename IO, int D, int NTM, int KW, bool ATT>
 __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
@@ -65,213 +135,55 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
                                                const uint16_t* __restrict__ kt_lo,
                                                const uint16_t* __restrict__ wt_hi,
                                                const uint16_t* __restrict__ wt_lo,
-                                               const float* __restrict__ conv_w, typename IO::T* __restrict__ out,
-                                               int n, int m, int mpa, int heads, int conv_k, float sl2e) {
+                                               const float* __restrict__ conv_w, const uint4* __restrict__ cwop,
+                                               typename IO::T* __restrict__ out, int n, int m, int heads,
+                                               int conv_k, float sl2e, int ntile, long long ntotal) {
   using T = typename IO::T;
-  using S = ApplyShape<D>;
-  using SM = ApplySmem<IO, D, KW>;
-  constexpr int TQ = S::TQ, NQ = S::NQ, KC = S::KC, ND = S::ND;
-  constexpr int HALO = SM::HALO, VP = SM::VP, OP = SM::OP;
-  __shared__ SM sm;
-  const int bh = blockIdx.y, tid = threadIdx.x;
+  using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
+  constexpr int KC = (D + 31) / 32;  // 32-wide chunks of the head dimension
+  constexpr int ND = D / 16;         // 16-feature tiles
+  constexpr bool KFULL = D % 32 == 0;
+  constexpr int MPA = LY::MPA, VP = LY::VP, OP = LY::OP, KP = LY::KP, WP = LY::WP;
+  constexpr int NCH = LY::NCH, TASKS = LY::TASKS, NTK = LY::NTK;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  float* ot = reinterpret_cast<float*>(smem_raw + LY::OT);
+  T* vt = reinterpret_cast<T*>(smem_raw + LY::VT);
+  uint16_t* kp = reinterpret_cast<uint16_t*>(smem_raw + LY::KT);  // [hi, lo][MPA][KP]
+  uint16_t* wp = reinterpret_cast<uint16_t*>(smem_raw + LY::WT);  // [hi, lo][D][WP]
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * TQ;
-  const int h = bh % heads;
-  const T* Vh = Vin + (size_t)bh * n * D;
 
-  // A. V rows [t0 - HALO, t0 + TQ + HALO) -> Vt (feature-major), zero outside [0, n).
-  if constexpr (SM::STAGE) {
-    if constexpr (IO::kBf16) {
-      // Task: 4 rows x 8 features -> 8 writes of 4 rows each.
-      constexpr int TASKS = (SM::VCOLS / 4) * (D / 8);
-      for (int e = tid; e < TASKS; e += 256) {
-        const int rq = e / (D / 8), oc = e % (D / 8);
-        uint4 r[4];
+  // Run of tiles of this block.
+  const long long G = gridDim.x, L = blockIdx.x;
+  const long long xcd = L & 7, per = G >> 3, rem = G & 7;
+  const long long rank = xcd * per + (xcd < rem ? xcd : rem) + (L >> 3);
+  const long long tbeg = rank * ntotal / G, tend = (rank + 1) * ntotal / G;
+  if (tbeg >= tend) return;
+
+  // Skip filter operands (matrix-core path): one 16-feature group per
+  // segment; kept in registers across tiles of one head when a wave has a
+  // single segment.
+  constexpr int FG = D / 16, RB = kTQ / 16, UPW = FG * RB / 4;
+  constexpr int NRB = UPW >= RB ? RB : UPW;  // consecutive row blocks per segment
+  constexpr int NSEG = UPW / NRB;
+  constexpr bool MMCONV = KW == 33 && IO::kBf16;
+  bf16x4_t ah[kConvNS], al[kConvNS];
+  auto conv_operands = [&](int h, int seg) {
+    const int b = lane >> 2, q4 = lane & 3;
+    const int f = ((wave * UPW + seg * NRB) / RB) * 16 + b;
+    if constexpr (ATT) {
+      const uint4* src = cwop + ((size_t)(h * D + f) * 4 + q4) * kConvNS;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = t0 - HALO + 4 * rq + q;
-          r[q] = (row >= 0 && row < n) ? *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * oc)
-                                       : make_uint4(0, 0, 0, 0);
-        }
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-        for (int dw = 0; dw < 4; ++dw) {
-          // features 8*oc + 2*dw (low halves) and 8*oc + 2*dw + 1 (high halves)
-          const uint2 lo = make_uint2((w0[dw] & 0xffffu) | (w1[dw] << 16), (w2[dw] & 0xffffu) | (w3[dw] << 16));
-          const uint2 hi = make_uint2((w0[dw] >> 16) | (w1[dw] & 0xffff0000u), (w2[dw] >> 16) | (w3[dw] & 0xffff0000u));
-          *reinterpret_cast<uint2*>(&sm.vt[(8 * oc + 2 * dw) * VP + 4 * rq]) = lo;
-          *reinterpret_cast<uint2*>(&sm.vt[(8 * oc + 2 * dw + 1) * VP + 4 * rq]) = hi;
-        }
+      for (int st = 0; st < kConvNS; ++st) {
+        const uint4 v = src[st];
+        ah[st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.x, v.y));
+        al[st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.z, v.w));
       }
     } else {
-      // Task: 4 rows x 4 features -> 4 writes of 4 rows each.
-      constexpr int TASKS = (SM::VCOLS / 4) * (D / 4);
-      for (int e = tid; e < TASKS; e += 256) {
-        const int rq = e / (D / 4), qc = e % (D / 4);
-        float4 r[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = t0 - HALO + 4 * rq + q;
-          r[q] = (row >= 0 && row < n) ? *reinterpret_cast<const float4*>(Vh + (size_t)row * D + 4 * qc)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        *reinterpret_cast<float4*>(&sm.vt[(4 * qc + 0) * VP + 4 * rq]) = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
-        *reinterpret_cast<float4*>(&sm.vt[(4 * qc + 1) * VP + 4 * rq]) = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
-        *reinterpret_cast<float4*>(&sm.vt[(4 * qc + 2) * VP + 4 * rq]) = make_float4(r[0].z, r[1].z, r[2].z, r[3].z);
-        *reinterpret_cast<float4*>(&sm.vt[(4 * qc + 3) * VP + 4 * rq]) = make_float4(r[0].w, r[1].w, r[2].w, r[3].w);
-      }
-    }
-  }
-
-  // B. Attention for this wave's NQ x 16 queries -> Ot; or zeros.
-  if constexpr (ATT) {
-    const T* Qh = Qin + (size_t)bh * n * D;
-    const int qw = t0 + wave * 16 * NQ;
-    B8 qh[NQ][KC], ql[NQ][KC];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int row = qw + 16 * u + c, dd = kc * 32 + 8 * g;
-        if constexpr (IO::kBf16) {
-          qh[u][kc].q = (row < n && dd < D) ? *reinterpret_cast<const uint4*>(Qh + (size_t)row * D + dd)
-                                            : make_uint4(0, 0, 0, 0);
-        } else {
-          float x[8];
-          if (row < n && dd < D) {
-            load8f<IO>(Qh + (size_t)row * D + dd, x);
-          } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] = 0.f;
-          }
-          split8(x, qh[u][kc], ql[u][kc]);
-        }
-      }
-
-    // S^T (landmarks x queries) = Kt Q^T.
-    f32x4_t sc[NQ][NTM];
-    const uint16_t* kth = kt_hi + (size_t)bh * mpa * D;
-    const uint16_t* ktl = kt_lo + (size_t)bh * mpa * D;
-#pragma unroll
-    for (int mt = 0; mt < NTM; ++mt) {
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) sc[u][mt] = zero4();
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int dd = kc * 32 + 8 * g;
-        B8 kh, kl;
-        if (dd < D) {
-          const size_t o = (size_t)(mt * 16 + c) * D + dd;
-          kh.q = *reinterpret_cast<const uint4*>(kth + o);
-          kl.q = *reinterpret_cast<const uint4*>(ktl + o);
-        } else {
-          kh.q = make_uint4(0, 0, 0, 0);
-          kl.q = make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-          if constexpr (IO::kBf16) {
-            sc[u][mt] = mfma(kl, qh[u][kc], sc[u][mt]);
-            sc[u][mt] = mfma(kh, qh[u][kc], sc[u][mt]);
-          } else {
-            sc[u][mt] = mfma3(kh, kl, qh[u][kc], ql[u][kc], sc[u][mt]);
-          }
-        }
-      }
-    }
-    // Softmax over landmarks (lane's query = 16u + c; landmark = mt*16 + 4g + i).
-    float inv[NQ];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int lm = mt * 16 + 4 * g + i;
-          sc[u][mt][i] = (lm < m) ? sc[u][mt][i] * sl2e : -INFINITY;
-          mx = fmaxf(mx, sc[u][mt][i]);
-        }
-      mx = max_over_groups(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[u][mt][i] = exp2f(sc[u][mt][i] - mx);
-          sum += sc[u][mt][i];
-        }
-      inv[u] = 1.f / sum_over_groups(sum);
-    }
-
-    // O (queries x features) = F W.  The W^T planes hold each 32-landmark chunk
-    // in the order {4g..4g+3, 16+4g..16+4g+3}, the order the lanes hold F in.
-    f32x4_t o[NQ][ND];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u)
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) o[u][nd] = zero4();
-    const uint16_t* wth = wt_hi + (size_t)bh * D * mpa;
-    const uint16_t* wtl = wt_lo + (size_t)bh * D * mpa;
-#pragma unroll
-    for (int kk = 0; kk < NTM / 2; ++kk) {
-      B8 fh[NQ], fl[NQ];
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[i] = sc[u][2 * kk][i] * inv[u];
-          f[4 + i] = sc[u][2 * kk + 1][i] * inv[u];
-        }
-        split8(f, fh[u], fl[u]);
-      }
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        const size_t off = (size_t)(nd * 16 + c) * mpa + kk * 32 + 8 * g;
-        B8 wh, wl;
-        wh.q = *reinterpret_cast<const uint4*>(wth + off);
-        wl.q = *reinterpret_cast<const uint4*>(wtl + off);
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) o[u][nd] = mfma3(fh[u], fl[u], wh, wl, o[u][nd]);
-      }
-    }
-    // Lane holds O[16u + 4g + i][nd*16 + c]: 4 consecutive rows of one feature.
-#pragma unroll
-    for (int u = 0; u < NQ; ++u)
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd)
-        *reinterpret_cast<float4*>(&sm.ot[(nd * 16 + c) * OP + wave * 16 * NQ + 16 * u + 4 * g]) =
-            make_float4(o[u][nd][0], o[u][nd][1], o[u][nd][2], o[u][nd][3]);
-  } else {
-    for (int e = tid; e < D * TQ / 4; e += 256) {
-      const int f = e / (TQ / 4), r4 = e % (TQ / 4);
-      *reinterpret_cast<float4*>(&sm.ot[f * OP + 4 * r4]) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  __syncthreads();
-
-  // C. The skip, added into Ot.
-  if constexpr (KW == 33 && IO::kBf16) {
-    constexpr int FG = D / 16, RB = TQ / 16, UPW = FG * RB / 4;
-    constexpr int NS = 9;  // 4-tap steps covering 33 taps for 4 rows
-    const int b = lane >> 2, q4 = lane & 3;
-    const int off = (33 - conv_k) / 2;
-#pragma unroll
-    for (int seg = 0; seg < (UPW >= RB ? UPW / RB : 1); ++seg) {
-      const int u0 = wave * UPW + seg * RB;
-      const int fg = u0 / RB;
-      const int rb0 = u0 % RB;
-      constexpr int NRB = UPW >= RB ? RB : UPW;
-      const int f = fg * 16 + b;
-      // A_s (hi/lo) for lane row i = q4: taps 4s + k' - i, centred in 33 slots.
+      const int off = (33 - conv_k) / 2;
       const float* wf = conv_w + ((size_t)h * D + f) * conv_k;
-      bf16x4_t ah[NS], al[NS];
 #pragma unroll
-      for (int st = 0; st < NS; ++st)
+      for (int st = 0; st < kConvNS; ++st)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int tt = 4 * st + k - q4 - off;
@@ -281,114 +193,295 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           ah[st][k] = (short)hi;
           al[st][k] = (short)lo;
         }
-      // B_s for lane column j = q4: Vt[f][rb*16 + 4(j + s) .. +3]; consecutive
-      // row blocks share 5 of 9 operands.
-      const T* vf = &sm.vt[f * VP];
-      bf16x4_t bw[NS + 4 * (NRB - 1)];
-#pragma unroll
-      for (int st = 0; st < NS + 4 * (NRB - 1); ++st) {
-        const uint2 v = *reinterpret_cast<const uint2*>(vf + rb0 * 16 + 4 * (q4 + st));
-        bw[st] = __builtin_bit_cast(bf16x4_t, v);
-      }
-#pragma unroll
-      for (int r = 0; r < NRB; ++r) {
-        f32x4_t acc = zero4();
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(al[st], bw[4 * r + st], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ah[st], bw[4 * r + st], acc, 0, 0, 0);
+    }
+  };
+
+  uint4 vr[NTK][4];
+  uint4 qr[KC][LY::QW];
+  {
+    const int bh = (int)(tbeg / ntile), t0 = (int)(tbeg % ntile) * kTQ;
+    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)bh * n * D, t0, n);
+    if constexpr (ATT) load_q<LY, D>(qr, Qin + (size_t)bh * n * D, t0 + 16 * wave + c, n);
+  }
+  int cur = -1;
+  for (long long t = tbeg; t < tend; ++t) {
+    const int bh = (int)(t / ntile), t0 = (int)(t % ntile) * kTQ, h = bh % heads;
+    if (bh != cur) {
+      // New head: its Kt / W^T planes -> LDS (the previous tile's readers
+      // are past the barrier that follows the attention), filter operands.
+      if constexpr (LY::KWL) {
+        const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
+                              reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
+        for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
+          const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
+          *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
         }
-        float4* dst = reinterpret_cast<float4*>(&sm.ot[f * OP + (rb0 + r) * 16 + 4 * q4]);
-        float4 cur = *dst;
-        cur.x += acc[0];
-        cur.y += acc[1];
-        cur.z += acc[2];
-        cur.w += acc[3];
-        *dst = cur;
+        const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
+                              reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
+        for (int e = tid; e < 2 * D * MPA / 8; e += 256) {
+          const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
+          *reinterpret_cast<uint4*>(wp + (pl * D + r) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
+        }
+      }
+      if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
+      cur = bh;
+    }
+    __syncthreads();  // previous tile's skip and store are done; planes visible
+
+    // V rows -> Vt (feature-major); then the next tile's V rows are loaded.
+    if constexpr (LY::STAGE) {
+#pragma unroll
+      for (int k = 0; k < NTK; ++k) {
+        const int e = tid + 256 * k;
+        if (e >= TASKS) continue;
+        const int rq = e / NCH, oc = e % NCH;
+        if constexpr (IO::kBf16) {
+          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[k][0]);
+          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[k][1]);
+          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[k][2]);
+          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[k][3]);
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+            // features 8*oc + 2*dw (low halves) and 8*oc + 2*dw + 1 (high halves)
+            const uint2 lo = make_uint2((w0[dw] & 0xffffu) | (w1[dw] << 16), (w2[dw] & 0xffffu) | (w3[dw] << 16));
+            const uint2 hi =
+                make_uint2((w0[dw] >> 16) | (w1[dw] & 0xffff0000u), (w2[dw] >> 16) | (w3[dw] & 0xffff0000u));
+            *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw) * VP + 4 * rq]) = lo;
+            *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw + 1) * VP + 4 * rq]) = hi;
+          }
+        } else {
+          const float4 r0 = __builtin_bit_cast(float4, vr[k][0]), r1 = __builtin_bit_cast(float4, vr[k][1]);
+          const float4 r2 = __builtin_bit_cast(float4, vr[k][2]), r3 = __builtin_bit_cast(float4, vr[k][3]);
+          *reinterpret_cast<float4*>(&vt[(4 * oc + 0) * VP + 4 * rq]) = make_float4(r0.x, r1.x, r2.x, r3.x);
+          *reinterpret_cast<float4*>(&vt[(4 * oc + 1) * VP + 4 * rq]) = make_float4(r0.y, r1.y, r2.y, r3.y);
+          *reinterpret_cast<float4*>(&vt[(4 * oc + 2) * VP + 4 * rq]) = make_float4(r0.z, r1.z, r2.z, r3.z);
+          *reinterpret_cast<float4*>(&vt[(4 * oc + 3) * VP + 4 * rq]) = make_float4(r0.w, r1.w, r2.w, r3.w);
+        }
       }
     }
-  } else if constexpr (KW == 33 || KW == 1) {
-    // fp32 sliding window: thread = (feature pair fp, row group rg).
-    constexpr int P = D / 2, RG = 256 / P, RPT = TQ / RG;
-    constexpr int NT = KW;
-    const int rg = tid % RG, fp = tid / RG, r0 = rg * RPT;
-    const int off = (NT - conv_k) / 2;
-    const float* w0p = conv_w + ((size_t)h * D + 2 * fp) * conv_k;
-    const float* w1p = w0p + conv_k;
-    float w0[NT], w1[NT];
+    const bool more = t + 1 < tend;
+    const int nbh = (int)((t + 1) / ntile), nt0 = (int)((t + 1) % ntile) * kTQ;
+    if constexpr (LY::STAGE)
+      if (more) load_v<LY>(vr, Vin + (size_t)nbh * n * D, nt0, n);
+
+    // Attention for this wave's 16 queries -> Ot; or zeros.
+    if constexpr (ATT) {
+      B8 qh[KC], ql[KC];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tt = t - off;
-      const bool in = tt >= 0 && tt < conv_k;
-      w0[t] = in ? w0p[tt] : 0.f;
-      w1[t] = in ? w1p[tt] : 0.f;
-    }
-    float a0[RPT], a1[RPT];
-#pragma unroll
-    for (int r = 0; r < RPT; r += 4) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&sm.ot[(2 * fp) * OP + r0 + r]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&sm.ot[(2 * fp + 1) * OP + r0 + r]);
-      a0[r] = x0.x; a0[r + 1] = x0.y; a0[r + 2] = x0.z; a0[r + 3] = x0.w;
-      a1[r] = x1.x; a1[r + 1] = x1.y; a1[r + 2] = x1.z; a1[r + 3] = x1.w;
-    }
-    const T* v0p = &sm.vt[(2 * fp) * VP + r0];
-    const T* v1p = &sm.vt[(2 * fp + 1) * VP + r0];
-    // Output row r0 + r reads Vt columns r0 + r + t (t = 0 .. NT-1).
-#pragma unroll
-    for (int j = 0; j < RPT + NT - 1; ++j) {
-      float v0, v1;
-      if constexpr (IO::kBf16) {
-        v0 = bf16_to_f32(v0p[j]);
-        v1 = bf16_to_f32(v1p[j]);
-      } else {
-        v0 = v0p[j];
-        v1 = v1p[j];
+      for (int kc = 0; kc < KC; ++kc) {
+        if constexpr (IO::kBf16) {
+          qh[kc].q = qr[kc][0];
+        } else {
+          const float4 a = __builtin_bit_cast(float4, qr[kc][0]), b = __builtin_bit_cast(float4, qr[kc][LY::QW - 1]);
+          const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          split8(x, qh[kc], ql[kc]);
+        }
       }
+      // S^T (landmarks x queries) = Kt Q^T from the Kt planes.
+      const uint16_t* kth = LY::KWL ? kp : kt_hi + (size_t)bh * MPA * D;
+      const uint16_t* ktl = LY::KWL ? kp + MPA * KP : kt_lo + (size_t)bh * MPA * D;
+      constexpr int KPI = LY::KWL ? KP : D;
+      f32x4_t sc[NTM];
+#pragma unroll
+      for (int mt = 0; mt < NTM; ++mt) {
+        sc[mt] = zero4();
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int dd = kc * 32 + 8 * g;
+          B8 kh, kl;
+          const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
+          kh.q = *reinterpret_cast<const uint4*>(kth + o);
+          kl.q = *reinterpret_cast<const uint4*>(ktl + o);
+          if (!KFULL && dd >= D) {
+            kh.q = make_uint4(0, 0, 0, 0);
+            kl.q = make_uint4(0, 0, 0, 0);
+          }
+          if constexpr (IO::kBf16) {
+            sc[mt] = mfma(kl, qh[kc], sc[mt]);
+            sc[mt] = mfma(kh, qh[kc], sc[mt]);
+          } else {
+            sc[mt] = mfma3(kh, kl, qh[kc], ql[kc], sc[mt]);
+          }
+        }
+      }
+      if (more) load_q<LY, D>(qr, Qin + (size_t)nbh * n * D, nt0 + 16 * wave + c, n);
+      // Softmax over landmarks (lane's query = c; landmark = mt*16 + 4g + i).
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[mt][i] = (mt * 16 + 4 * g + i < m) ? sc[mt][i] * sl2e : -INFINITY;
+          mx = fmaxf(mx, sc[mt][i]);
+        }
+      mx = max_over_groups(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc[mt][i] = __builtin_amdgcn_exp2f(sc[mt][i] - mx);  // arguments <= 0; exp2(-inf) = 0
+          sum += sc[mt][i];
+        }
+      const float inv = 1.f / sum_over_groups(sum);
+
+      // O^T (features x queries) = W^T F^T.  The W^T planes hold each
+      // 32-landmark chunk in the order {4g..4g+3, 16+4g..16+4g+3}, the order
+      // this lane holds its query's probabilities in.
+      const uint16_t* wth = LY::KWL ? wp : wt_hi + (size_t)bh * D * MPA;
+      const uint16_t* wtl = LY::KWL ? wp + D * WP : wt_lo + (size_t)bh * D * MPA;
+      constexpr int WPI = LY::KWL ? WP : MPA;
+      f32x4_t o[ND];
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < NTM / 2; ++kk) {
+        B8 fh, fl;
+        {
+          float f[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[i] = sc[2 * kk][i] * inv;
+            f[4 + i] = sc[2 * kk + 1][i] * inv;
+          }
+          split8(f, fh, fl);
+        }
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) {
+          const int off = (nd * 16 + c) * WPI + kk * 32 + 8 * g;
+          B8 wh, wl;
+          wh.q = *reinterpret_cast<const uint4*>(wth + off);
+          wl.q = *reinterpret_cast<const uint4*>(wtl + off);
+          o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
+        }
+      }
+      // Lane holds O[query 16*wave + c][features nd*16 + 4g .. +3].
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+        *reinterpret_cast<float4*>(&ot[(16 * wave + c) * OP + nd * 16 + 4 * g]) =
+            make_float4(o[nd][0], o[nd][1], o[nd][2], o[nd][3]);
+    } else {
+      for (int e = tid; e < kTQ * OP / 4; e += 256)
+        *reinterpret_cast<float4*>(&ot[4 * e]) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+
+    // The skip, added into Ot.
+    if constexpr (MMCONV) {
+      const int b = lane >> 2, q4 = lane & 3;
+#pragma unroll
+      for (int seg = 0; seg < NSEG; ++seg) {
+        if constexpr (NSEG > 1) conv_operands(h, seg);
+        const int u0 = wave * UPW + seg * NRB;
+        const int fg = u0 / RB, rb0 = u0 % RB;
+        const int f = fg * 16 + b;
+        // B_s for lane column j = q4: Vt[f][rb*16 + 4(j + s) .. +3];
+        // consecutive row blocks share 5 of 9 operands.
+        const T* vf = &vt[f * VP];
+        bf16x4_t bw[kConvNS + 4 * (NRB - 1)];
+#pragma unroll
+        for (int st = 0; st < kConvNS + 4 * (NRB - 1); ++st)
+          bw[st] = __builtin_bit_cast(bf16x4_t, *reinterpret_cast<const uint2*>(vf + rb0 * 16 + 4 * (q4 + st)));
+#pragma unroll
+        for (int r = 0; r < NRB; ++r) {
+          f32x4_t acc = zero4();
+#pragma unroll
+          for (int st = 0; st < kConvNS; ++st) {
+            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(al[st], bw[4 * r + st], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ah[st], bw[4 * r + st], acc, 0, 0, 0);
+          }
+          // Lane (b, q4) holds rows (rb0 + r)*16 + 4*q4 + i of feature f.
+          float* dst = &ot[((rb0 + r) * 16 + 4 * q4) * OP + f];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i * OP] += acc[i];
+        }
+      }
+    } else if constexpr (KW == 33 || KW == 1) {
+      // fp32 sliding window: thread = (feature pair fp, row group rg).
+      constexpr int P = D / 2, RG = 256 / P, RPT = kTQ / RG;
+      constexpr int NT = KW;
+      const int rg = tid % RG, fp = tid / RG, r0 = rg * RPT;
+      const int off = (NT - conv_k) / 2;
+      const float* w0p = conv_w + ((size_t)h * D + 2 * fp) * conv_k;
+      const float* w1p = w0p + conv_k;
+      float w0[NT], w1[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const int ti = tt - off;
+        const bool in = ti >= 0 && ti < conv_k;
+        w0[tt] = in ? w0p[ti] : 0.f;
+        w1[tt] = in ? w1p[ti] : 0.f;
+      }
+      float a0[RPT], a1[RPT];
 #pragma unroll
       for (int r = 0; r < RPT; ++r) {
-        const int t = j - r;
-        if (t >= 0 && t < NT) {
-          a0[r] = fmaf(w0[t], v0, a0[r]);
-          a1[r] = fmaf(w1[t], v1, a1[r]);
+        const float2 x = *reinterpret_cast<const float2*>(&ot[(r0 + r) * OP + 2 * fp]);
+        a0[r] = x.x;
+        a1[r] = x.y;
+      }
+      const T* v0p = &vt[(2 * fp) * VP + r0];
+      const T* v1p = &vt[(2 * fp + 1) * VP + r0];
+      // Output row r0 + r reads Vt columns r0 + r + tt (tt = 0 .. NT-1).
+#pragma unroll
+      for (int j = 0; j < RPT + NT - 1; ++j) {
+        float v0, v1;
+        if constexpr (IO::kBf16) {
+          v0 = bf16_to_f32(v0p[j]);
+          v1 = bf16_to_f32(v1p[j]);
+        } else {
+          v0 = v0p[j];
+          v1 = v1p[j];
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          const int tt = j - r;
+          if (tt >= 0 && tt < NT) {
+            a0[r] = fmaf(w0[tt], v0, a0[r]);
+            a1[r] = fmaf(w1[tt], v1, a1[r]);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int r = 0; r < RPT; r += 4) {
-      *reinterpret_cast<float4*>(&sm.ot[(2 * fp) * OP + r0 + r]) = make_float4(a0[r], a0[r + 1], a0[r + 2], a0[r + 3]);
-      *reinterpret_cast<float4*>(&sm.ot[(2 * fp + 1) * OP + r0 + r]) =
-          make_float4(a1[r], a1[r + 1], a1[r + 2], a1[r + 3]);
+      for (int r = 0; r < RPT; ++r) *reinterpret_cast<float2*>(&ot[(r0 + r) * OP + 2 * fp]) = make_float2(a0[r], a1[r]);
     }
-  }
-  if constexpr (KW == 33 || KW == 1) __syncthreads();
+    if constexpr (KW == 33 || KW == 1) __syncthreads();
 
-  // D. Ot -> output rows: 16 bytes (8 bf16 or 4 fp32 features) per lane.
-  constexpr int FPL = IO::kBf16 ? 8 : 4;  // features per lane
-  constexpr int GPR = D / FPL;            // lanes per row
-  T* oh = out + (size_t)bh * n * D;
-  for (int e = tid; e < TQ * GPR; e += 256) {
-    const int p = e / GPR, fc = (e % GPR) * FPL;
-    const int row = t0 + p;
-    if (row >= n) continue;
-    float v[FPL];
+    // Ot -> output rows: 16 bytes (8 bf16 or 4 fp32 features) per lane.
+    constexpr int FPL = IO::kBf16 ? 8 : 4;  // features per lane
+    constexpr int GPR = D / FPL;            // lanes per row
+    const T* Vh = Vin + (size_t)bh * n * D;
+    T* oh = out + (size_t)bh * n * D;
+    for (int e = tid; e < kTQ * GPR; e += 256) {
+      const int p = e / GPR, fc = (e % GPR) * FPL;
+      const int row = t0 + p;
+      if (row >= n) continue;
+      float v[FPL];
 #pragma unroll
-    for (int q = 0; q < FPL; ++q) v[q] = sm.ot[(fc + q) * OP + p];
-    if constexpr (KW == -1) {
-      const int R = (conv_k - 1) / 2;
-      const int tb = max(0, R - row), te = min(conv_k, n - row + R);
-#pragma unroll
-      for (int q = 0; q < FPL; ++q) {
-        const float* wq = conv_w + ((size_t)h * D + fc + q) * conv_k;
-        for (int t = tb; t < te; ++t) v[q] = fmaf(wq[t], load_elem<IO>(Vh + (size_t)(row + t - R) * D + fc + q), v[q]);
+      for (int q = 0; q < FPL; q += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(&ot[p * OP + fc + q]);
+        v[q] = x.x;
+        v[q + 1] = x.y;
+        v[q + 2] = x.z;
+        v[q + 3] = x.w;
       }
-    }
-    if constexpr (IO::kBf16) {
-      B8 o8;
+      if constexpr (KW == -1) {
+        const int R = (conv_k - 1) / 2;
+        const int tb = max(0, R - row), te = min(conv_k, n - row + R);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o8.h[q] = f32_to_bf16(v[q]);
-      *reinterpret_cast<uint4*>(oh + (size_t)row * D + fc) = o8.q;
-    } else {
-      *reinterpret_cast<float4*>(oh + (size_t)row * D + fc) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int q = 0; q < FPL; ++q) {
+          const float* wq = conv_w + ((size_t)h * D + fc + q) * conv_k;
+          for (int tt = tb; tt < te; ++tt)
+            v[q] = fmaf(wq[tt], load_elem<IO>(Vh + (size_t)(row + tt - R) * D + fc + q), v[q]);
+        }
+      }
+      if constexpr (IO::kBf16) {
+        B8 o8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o8.h[q] = f32_to_bf16(v[q]);
+        *reinterpret_cast<uint4*>(oh + (size_t)row * D + fc) = o8.q;
+      } else {
+        *reinterpret_cast<float4*>(oh + (size_t)row * D + fc) = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
   }
 }
@@ -398,69 +491,104 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
 
 static int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+static bool conv_uses_ops(const Problem& p) { return p.bf16 && p.conv_w && p.conv_k > 1 && p.conv_k <= 33; }
+
+hipError_t stage_conv_ops(const Problem& p, const Ws& w, hipStream_t s) {
+  if (!conv_uses_ops(p)) return hipSuccess;
+  const int total = p.heads * p.d * 4 * kConvNS;
+  KernelTimer kt_("conv_ops", s);
+  k_conv_ops<<<cdiv(total, 256), 256, 0, s>>>(p.conv_w, w.cwop, total, p.conv_k);
+  return hipGetLastError();
+}
+
+// Blocks per CU the persistent grid is sized for (LDS and registers allow it
+// for the common shapes; more resident blocks only queue).
+static int multiprocessors() {
+  static const int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return v > 0 ? v : 256;
+  }();
+  return cus;
+}
+
 template <typename IO, int D, int NTM, int KW, bool ATT>
-static void launch_one(const Problem& p, const Ws* w, hipStream_t s) {
+static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   using T = typename IO::T;
-  constexpr int TQ = ApplyShape<D>::TQ;
-  const int BH = p.batch * p.heads;
-  const dim3 grid(cdiv(p.n, TQ), BH);
-  k_apply<IO, D, NTM, KW, ATT><<<grid, 256, 0, s>>>(
-      static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr, w ? w->kt_lo : nullptr,
-      w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w, static_cast<T*>(p.out), p.n, p.m,
-      w ? w->mpa : 0, p.heads, p.conv_k, kLog2e / sqrtf((float)D));
+  using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
+  auto kern = &k_apply<IO, D, NTM, KW, ATT>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
+  if (attr != hipSuccess) return attr;
+  static const int per_cu = [&] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), 256, LY::BYTES) !=
+            hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  const int ntile = cdiv(p.n, kTQ);
+  const long long total = (long long)ntile * p.batch * p.heads;
+  const long long want = (long long)per_cu * multiprocessors();
+  const int grid = (int)(total < want ? total : want);
+  kern<<<grid, 256, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
+                                    w ? w->kt_lo : nullptr, w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w,
+                                    w ? w->cwop : nullptr, static_cast<T*>(p.out), p.n, p.m, p.heads, p.conv_k,
+                                    kLog2e / sqrtf((float)D), ntile, total);
+  return hipSuccess;
 }
 
 template <typename IO, int D, int NTM, bool ATT>
-static void pick_kw(const Problem& p, const Ws* w, hipStream_t s) {
-  if (!p.conv_w || p.conv_k <= 0)
-    launch_one<IO, D, NTM, 0, ATT>(p, w, s);
-  else if (p.conv_k == 1)
-    launch_one<IO, D, NTM, 1, ATT>(p, w, s);
-  else if (p.conv_k <= 33)
-    launch_one<IO, D, NTM, 33, ATT>(p, w, s);
-  else
-    launch_one<IO, D, NTM, -1, ATT>(p, w, s);
+static hipError_t pick_kw(const Problem& p, const Ws* w, hipStream_t s) {
+  if (!p.conv_w || p.conv_k <= 0) return launch_one<IO, D, NTM, 0, ATT>(p, w, s);
+  if (p.conv_k == 1) return launch_one<IO, D, NTM, 1, ATT>(p, w, s);
+  if (p.conv_k <= 33) return launch_one<IO, D, NTM, 33, ATT>(p, w, s);
+  return launch_one<IO, D, NTM, -1, ATT>(p, w, s);
 }
 
 template <typename IO, int D>
-static void apply_t(const Problem& p, const Ws& w, hipStream_t s) {
+static hipError_t apply_t(const Problem& p, const Ws& w, hipStream_t s) {
   KernelTimer kt_("apply", s);
   switch (w.mpa) {  // landmark tiles of 16 = mpa / 16
-    case 32: pick_kw<IO, D, 2, true>(p, &w, s); break;
-    case 64: pick_kw<IO, D, 4, true>(p, &w, s); break;
-    case 128: pick_kw<IO, D, 8, true>(p, &w, s); break;
-    default: pick_kw<IO, D, 16, true>(p, &w, s); break;
+    case 32: return pick_kw<IO, D, 2, true>(p, &w, s);
+    case 64: return pick_kw<IO, D, 4, true>(p, &w, s);
+    case 128: return pick_kw<IO, D, 8, true>(p, &w, s);
+    default: return pick_kw<IO, D, 16, true>(p, &w, s);
   }
 }
 
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s) {
+  hipError_t e;
   switch (p.d) {
-    case 16: p.bf16 ? apply_t<BF16, 16>(p, w, s) : apply_t<F32, 16>(p, w, s); break;
-    case 32: p.bf16 ? apply_t<BF16, 32>(p, w, s) : apply_t<F32, 32>(p, w, s); break;
-    case 64: p.bf16 ? apply_t<BF16, 64>(p, w, s) : apply_t<F32, 64>(p, w, s); break;
-    case 128: p.bf16 ? apply_t<BF16, 128>(p, w, s) : apply_t<F32, 128>(p, w, s); break;
+    case 16: e = p.bf16 ? apply_t<BF16, 16>(p, w, s) : apply_t<F32, 16>(p, w, s); break;
+    case 32: e = p.bf16 ? apply_t<BF16, 32>(p, w, s) : apply_t<F32, 32>(p, w, s); break;
+    case 64: e = p.bf16 ? apply_t<BF16, 64>(p, w, s) : apply_t<F32, 64>(p, w, s); break;
+    case 128: e = p.bf16 ? apply_t<BF16, 128>(p, w, s) : apply_t<F32, 128>(p, w, s); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 template <typename IO, int D>
-static void dconv_t(const Problem& p, hipStream_t s) {
+static hipError_t dconv_t(const Problem& p, hipStream_t s) {
   KernelTimer kt_("dconv", s);
-  pick_kw<IO, D, 2, false>(p, nullptr, s);
+  return pick_kw<IO, D, 2, false>(p, nullptr, s);
 }
 
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n, int d, int k,
                         bool bf16, hipStream_t s) {
   Problem p{nullptr, nullptr, V, conv_w, out, batch, heads, n, d, 1, 0, k, bf16};
+  hipError_t e;
   switch (d) {
-    case 16: bf16 ? dconv_t<BF16, 16>(p, s) : dconv_t<F32, 16>(p, s); break;
-    case 32: bf16 ? dconv_t<BF16, 32>(p, s) : dconv_t<F32, 32>(p, s); break;
-    case 64: bf16 ? dconv_t<BF16, 64>(p, s) : dconv_t<F32, 64>(p, s); break;
-    case 128: bf16 ? dconv_t<BF16, 128>(p, s) : dconv_t<F32, 128>(p, s); break;
+    case 16: e = bf16 ? dconv_t<BF16, 16>(p, s) : dconv_t<F32, 16>(p, s); break;
+    case 32: e = bf16 ? dconv_t<BF16, 32>(p, s) : dconv_t<F32, 32>(p, s); break;
+    case 64: e = bf16 ? dconv_t<BF16, 64>(p, s) : dconv_t<F32, 64>(p, s); break;
+    case 128: e = bf16 ? dconv_t<BF16, 128>(p, s) : dconv_t<F32, 128>(p, s); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace nys

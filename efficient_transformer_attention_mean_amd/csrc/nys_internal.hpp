@@ -14,6 +14,7 @@ struct WsLayout {
   size_t pacc, pmax, psum;         // fp32 split-n partials of softmax(Qt K^T) V
   size_t kt_hi, kt_lo;             // bf16 planes of Kt, [bh][mpa][d]
   size_t wt_hi, wt_lo;             // bf16 planes of W^T, [bh][d][mpa], landmark order permuted
+  size_t cwop;                     // matrix-core operands of the skip filters, [heads][d][4][9] x 16 B
   size_t total;
   int nchunks, chunk;              // split-n: blocks per head, keys per block
   int mpa;                         // landmarks padded for the output stage: 32, 64, 128 or 256
@@ -28,6 +29,7 @@ struct Ws {
   float *Z2, *X, *T, *U;
   float *pacc, *pmax, *psum;
   uint16_t *kt_hi, *kt_lo, *wt_hi, *wt_lo;
+  uint4* cwop;
   int nchunks, chunk, mpa;
 };
 
@@ -61,6 +63,7 @@ class KernelTimer {
 // Stages of the forward pass.  The pseudoinverse depends only on the
 // landmarks, so it runs on a side stream beside the split-n pass.
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  // Qt, Kt, Kt planes
+hipError_t stage_conv_ops(const Problem& p, const Ws& w, hipStream_t s);       // skip-filter operands
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z
 hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s);             // split-n partials of B V
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      // B V, W, W^T planes (needs Z)

@@ -47,6 +47,7 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   L->kt_lo = take((size_t)BH * L->mpa * d * 2);
   L->wt_hi = take((size_t)BH * d * L->mpa * 2);
   L->wt_lo = take((size_t)BH * d * L->mpa * 2);
+  L->cwop = take((size_t)heads * d * 4 * 9 * 16);
   L->total = off;
   return true;
 }
@@ -70,6 +71,7 @@ Ws resolve(const WsLayout& L, char* b) {
   w.kt_lo = reinterpret_cast<uint16_t*>(b + L.kt_lo);
   w.wt_hi = reinterpret_cast<uint16_t*>(b + L.wt_hi);
   w.wt_lo = reinterpret_cast<uint16_t*>(b + L.wt_lo);
+  w.cwop = reinterpret_cast<uint4*>(b + L.cwop);
   w.nchunks = L.nchunks;
   w.chunk = L.chunk;
   w.mpa = L.mpa;
@@ -128,9 +130,11 @@ hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStre
   if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
   Side* sd = nullptr;
   if ((e = acquire_side(&sd)) != hipSuccess) return e;
-  // Fork: the pseudoinverse (landmarks only) beside the split-n pass over K, V.
+  // Fork: the pseudoinverse (landmarks only) and the skip-filter operands
+  // beside the split-n pass over K, V.
   if ((e = hipEventRecord(sd->fork, s)) == hipSuccess && (e = hipStreamWaitEvent(sd->stream, sd->fork, 0)) == hipSuccess &&
-      (e = stage_pinv(p, w, sd->stream)) == hipSuccess && (e = hipEventRecord(sd->join, sd->stream)) == hipSuccess &&
+      (e = stage_conv_ops(p, w, sd->stream)) == hipSuccess && (e = stage_pinv(p, w, sd->stream)) == hipSuccess &&
+      (e = hipEventRecord(sd->join, sd->stream)) == hipSuccess &&
       (e = stage_bv(p, w, s)) == hipSuccess) {
     e = hipStreamWaitEvent(s, sd->join, 0);
   }
