@@ -53,12 +53,16 @@ struct ApplyLayout {
   static constexpr int OP = D + 4;      // Ot row pitch (floats)
   static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
   static constexpr int WP = MPA + 8;    // W^T plane row pitch (bf16)
-  // The Kt and W^T planes of the current head are kept in LDS when they fit.
-  static constexpr bool KWL = ATT && (4 * MPA * KP + 4 * D * WP) <= 72 * 1024;
+  // The current head's Kt fragments stay in registers when they are few
+  // (KREG); otherwise the Kt planes, like the W^T planes, are kept in LDS
+  // when they fit (KWL), else read from global memory.
+  static constexpr int KC = (D + 31) / 32;
+  static constexpr bool KREG = ATT && NTM * KC <= 8;
+  static constexpr bool KWL = ATT && ((KREG ? 0 : 4 * MPA * KP) + 4 * D * WP) <= 72 * 1024;
   static constexpr int OT = 0;
   static constexpr int VT = OT + 4 * kTQ * OP;
   static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
-  static constexpr int WT = KT + (KWL ? 4 * MPA * KP : 0);
+  static constexpr int WT = KT + (KWL && !KREG ? 4 * MPA * KP : 0);
   static constexpr int BYTES = WT + (KWL ? 4 * D * WP : 0);
   // V tile loads: task = 4 rows x one 16-byte chunk.
   static constexpr int FPC = IO::kBf16 ? 8 : 4;  // features per 16-byte chunk
@@ -68,38 +72,50 @@ struct ApplyLayout {
   static constexpr int QW = IO::kBf16 ? 1 : 2;  // 16-byte words per 8 head-dim elements
 };
 
-// Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) (zero outside
-// [0, n)) into registers.
+// Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) into registers.
+// Every load is unconditional (row and task clamped in range, so the
+// compiler keeps exact counts of loads in flight); rows outside [0, n) are
+// zeroed when staged (v_row_ok).
 template <typename LY, typename T>
 __device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], const T* __restrict__ Vh, int t0, int n) {
   constexpr int D = LY::NCH * LY::FPC;
-  const bool interior = t0 - LY::HALO >= 0 && t0 + kTQ + LY::HALO <= n;
 #pragma unroll
   for (int k = 0; k < LY::NTK; ++k) {
-    const int e = threadIdx.x + 256 * k;
+    const int e = min((int)threadIdx.x + 256 * k, LY::TASKS - 1);
     const int rq = e / LY::NCH, oc = e % LY::NCH;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = t0 - LY::HALO + 4 * rq + q;
-      const bool ok = e < LY::TASKS && (interior || (row >= 0 && row < n));
-      vr[k][q] = ok ? *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + LY::FPC * oc) : make_uint4(0, 0, 0, 0);
+      const int row = min(max(t0 - LY::HALO + 4 * rq + q, 0), n - 1);
+      vr[k][q] = *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + LY::FPC * oc);
     }
   }
 }
 
+template <typename LY>
+__device__ __forceinline__ bool v_row_ok(int t0, int n, int rq, int q) {
+  const int row = t0 - LY::HALO + 4 * rq + q;
+  return row >= 0 && row < n;
+}
+
 // Issues the loads of this lane's query fragments (row qrow, head-dim
-// elements 32kc + 8g .. +7 for every chunk kc), zero past n or past D.
+// elements 32kc + 8g .. +7 for every chunk kc), clamped in range; q_ok tells
+// which are real.
 template <typename LY, int D, typename T>
 __device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], const T* __restrict__ Qh, int qrow, int n) {
   const int g = (threadIdx.x & 63) >> 4;
+  const int r = min(qrow, n - 1);
 #pragma unroll
   for (int kc = 0; kc < (D + 31) / 32; ++kc) {
-    const int dd = kc * 32 + 8 * g;
-    const bool ok = qrow < n && (D % 32 == 0 || dd < D);
+    const int dd = min(kc * 32 + 8 * g, D - 8);
 #pragma unroll
-    for (int w = 0; w < LY::QW; ++w)
-      qr[kc][w] = ok ? *reinterpret_cast<const uint4*>(Qh + (size_t)qrow * D + dd + 4 * w) : make_uint4(0, 0, 0, 0);
+    for (int w = 0; w < LY::QW; ++w) qr[kc][w] = *reinterpret_cast<const uint4*>(Qh + (size_t)r * D + dd + 4 * w);
   }
+}
+
+template <int D>
+__device__ __forceinline__ bool q_ok(int qrow, int n, int kc) {
+  const int g = (threadIdx.x & 63) >> 4;
+  return qrow < n && (D % 32 == 0 || kc * 32 + 8 * g < D);
 }
 
 }  // namespace
@@ -126,8 +142,8 @@ __global__ __launch_bounds__(256) void k_conv_ops(const float* __restrict__ conv
 
 // Persistent blocks: block `rank` (XCD-contiguous numbering) processes the
 // run of 64-row tiles [rank * total / G, (rank + 1) * total / G) of the
-// (batch*head)-major tile list; the next tile's V rows and Q fragments are
-// loaded while the current tile is computed.
+// (batch*head)-major tile list; the V rows and Q fragments of the next two
+// tiles are in flight while the current tile is computed.
 template <typename IO, int D, int NTM, int KW, bool ATT>
 __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
@@ -137,7 +153,7 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
                                                const uint16_t* __restrict__ wt_lo,
                                                const float* __restrict__ conv_w, const uint4* __restrict__ cwop,
                                                typename IO::T* __restrict__ out, int n, int m, int heads,
-                                               int conv_k, float sl2e, int ntile, long long ntotal) {
+                                               int conv_k, int ntile, long long ntotal) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
   constexpr int KC = (D + 31) / 32;  // 32-wide chunks of the head dimension
@@ -196,25 +212,55 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
     }
   };
 
-  uint4 vr[NTK][4];
-  uint4 qr[KC][LY::QW];
-  {
-    const int bh = (int)(tbeg / ntile), t0 = (int)(tbeg % ntile) * kTQ;
-    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)bh * n * D, t0, n);
-    if constexpr (ATT) load_q<LY, D>(qr, Qin + (size_t)bh * n * D, t0 + 16 * wave + c, n);
-  }
+  B8 kreg[LY::KREG ? NTM : 1][LY::KREG ? KC : 1][2];  // Kt fragments (hi, lo) of the current head
+  // Two register sets of tile inputs: tile t is computed while the loads of
+  // tiles t + 1 and t + 2 are in flight.
+  uint4 vra[NTK][4], vrb[NTK][4];
+  uint4 qra[KC][LY::QW], qrb[KC][LY::QW];
+  // Tile positions: (batch*head, tile within the head), stepped without division.
+  struct Pos {
+    int bh, ti;
+  };
+  auto step = [&](Pos q) {
+    if (++q.ti == ntile) {
+      q.ti = 0;
+      ++q.bh;
+    }
+    return q;
+  };
+  const Pos pfirst{(int)(tbeg / ntile), (int)(tbeg % ntile)};
+  const Pos plast{(int)((tend - 1) / ntile), (int)((tend - 1) % ntile)};
+  auto issue = [&](Pos q, uint4 (&vr)[NTK][4], uint4 (&qr)[KC][LY::QW]) {
+    const int t0 = q.ti * kTQ;
+    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)q.bh * n * D, t0, n);
+    if constexpr (ATT) load_q<LY, D>(qr, Qin + (size_t)q.bh * n * D, t0 + 16 * wave + c, n);
+  };
+  issue(pfirst, vra, qra);
+  issue(tbeg + 1 < tend ? step(pfirst) : pfirst, vrb, qrb);
   int cur = -1;
-  for (long long t = tbeg; t < tend; ++t) {
-    const int bh = (int)(t / ntile), t0 = (int)(t % ntile) * kTQ, h = bh % heads;
+  auto tile = [&](long long t, Pos pos, uint4 (&vr)[NTK][4], uint4 (&qr)[KC][LY::QW]) {
+    const int bh = pos.bh, t0 = pos.ti * kTQ, h = bh % heads;
     if (bh != cur) {
       // New head: its Kt / W^T planes -> LDS (the previous tile's readers
       // are past the barrier that follows the attention), filter operands.
+      if constexpr (LY::KREG) {
+#pragma unroll
+        for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const size_t o = (size_t)bh * MPA * D + (size_t)(mt * 16 + c) * D + min(kc * 32 + 8 * g, D - 8);
+            kreg[mt][kc][0].q = *reinterpret_cast<const uint4*>(kt_hi + o);
+            kreg[mt][kc][1].q = *reinterpret_cast<const uint4*>(kt_lo + o);
+          }
+      }
       if constexpr (LY::KWL) {
-        const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
-                              reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
-        for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
-          const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
-          *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
+        if constexpr (!LY::KREG) {
+          const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
+                                reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
+          for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
+            const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
+            *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
+          }
         }
         const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
                               reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
@@ -225,6 +271,9 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
       }
       if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
       cur = bh;
+      // Rare path: settle its loads here so that the counts of the tile loads
+      // in flight stay exact past the merge.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
     __syncthreads();  // previous tile's skip and store are done; planes visible
 
@@ -235,6 +284,11 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         const int e = tid + 256 * k;
         if (e >= TASKS) continue;
         const int rq = e / NCH, oc = e % NCH;
+        if (!(t0 - LY::HALO >= 0 && t0 + kTQ + LY::HALO <= n)) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (!v_row_ok<LY>(t0, n, rq, q)) vr[k][q] = make_uint4(0, 0, 0, 0);
+        }
         if constexpr (IO::kBf16) {
           const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[k][0]);
           const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[k][1]);
@@ -259,21 +313,24 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         }
       }
     }
-    const bool more = t + 1 < tend;
-    const int nbh = (int)((t + 1) / ntile), nt0 = (int)((t + 1) % ntile) * kTQ;
-    if constexpr (LY::STAGE)
-      if (more) load_v<LY>(vr, Vin + (size_t)nbh * n * D, nt0, n);
+    // Tile t + 2 (or the last one again near the end: loads stay unconditional).
+    const Pos pn = t + 2 < tend ? step(step(pos)) : plast;
+    const int nbh = pn.bh, nt0 = pn.ti * kTQ;
+    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)nbh * n * D, nt0, n);
 
     // Attention for this wave's 16 queries -> Ot; or zeros.
     if constexpr (ATT) {
       B8 qh[KC], ql[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
+        const bool ok = q_ok<D>(t0 + 16 * wave + c, n, kc);
         if constexpr (IO::kBf16) {
-          qh[kc].q = qr[kc][0];
+          qh[kc].q = ok ? qr[kc][0] : make_uint4(0, 0, 0, 0);
         } else {
           const float4 a = __builtin_bit_cast(float4, qr[kc][0]), b = __builtin_bit_cast(float4, qr[kc][LY::QW - 1]);
-          const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
           split8(x, qh[kc], ql[kc]);
         }
       }
@@ -281,6 +338,8 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
       const uint16_t* kth = LY::KWL ? kp : kt_hi + (size_t)bh * MPA * D;
       const uint16_t* ktl = LY::KWL ? kp + MPA * KP : kt_lo + (size_t)bh * MPA * D;
       constexpr int KPI = LY::KWL ? KP : D;
+      (void)kth;
+      (void)ktl;
       f32x4_t sc[NTM];
 #pragma unroll
       for (int mt = 0; mt < NTM; ++mt) {
@@ -289,9 +348,14 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         for (int kc = 0; kc < KC; ++kc) {
           const int dd = kc * 32 + 8 * g;
           B8 kh, kl;
-          const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
-          kh.q = *reinterpret_cast<const uint4*>(kth + o);
-          kl.q = *reinterpret_cast<const uint4*>(ktl + o);
+          if constexpr (LY::KREG) {
+            kh = kreg[mt][kc][0];
+            kl = kreg[mt][kc][1];
+          } else {
+            const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
+            kh.q = *reinterpret_cast<const uint4*>(kth + o);
+            kl.q = *reinterpret_cast<const uint4*>(ktl + o);
+          }
           if (!KFULL && dd >= D) {
             kh.q = make_uint4(0, 0, 0, 0);
             kl.q = make_uint4(0, 0, 0, 0);
@@ -304,16 +368,21 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           }
         }
       }
-      if (more) load_q<LY, D>(qr, Qin + (size_t)nbh * n * D, nt0 + 16 * wave + c, n);
+      load_q<LY, D>(qr, Qin + (size_t)nbh * n * D, nt0 + 16 * wave + c, n);
       // Softmax over landmarks (lane's query = c; landmark = mt*16 + 4g + i).
+      // Scores are already in base-2 units (the Kt planes carry log2(e)/sqrt(d)).
+      if (m < MPA) {
+#pragma unroll
+        for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (mt * 16 + 4 * g + i >= m) sc[mt][i] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < NTM; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[mt][i] = (mt * 16 + 4 * g + i < m) ? sc[mt][i] * sl2e : -INFINITY;
-          mx = fmaxf(mx, sc[mt][i]);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[mt][i]);
       mx = max_over_groups(mx);
       float sum = 0.f;
 #pragma unroll
@@ -483,7 +552,16 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         *reinterpret_cast<float4*>(oh + (size_t)row * D + fc) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
+  };
+  long long t = tbeg;
+  Pos pos = pfirst;
+  for (; t + 1 < tend; t += 2) {
+    tile(t, pos, vra, qra);
+    pos = step(pos);
+    tile(t + 1, pos, vrb, qrb);
+    pos = step(pos);
   }
+  if (t < tend) tile(t, pos, vra, qra);
 }
 
 // ---------------------------------------------------------------------------
@@ -536,7 +614,7 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   kern<<<grid, 256, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
                                     w ? w->kt_lo : nullptr, w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w,
                                     w ? w->cwop : nullptr, static_cast<T*>(p.out), p.n, p.m, p.heads, p.conv_k,
-                                    kLog2e / sqrtf((float)D), ntile, total);
+                                    ntile, total);
   return hipSuccess;
 }
 

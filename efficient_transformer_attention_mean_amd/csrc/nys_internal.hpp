@@ -12,7 +12,7 @@ struct WsLayout {
   size_t qt, kt, a, z, bv, w;      // documented fp32 intermediates (NYS_WS_*)
   size_t z2, x, t, u;              // fp32 pseudoinverse scratch for m > 64
   size_t pacc, pmax, psum;         // fp32 split-n partials of softmax(Qt K^T) V
-  size_t kt_hi, kt_lo;             // bf16 planes of Kt, [bh][mpa][d]
+  size_t kt_hi, kt_lo;             // bf16 planes of Kt * log2(e)/sqrt(d), [bh][mpa][d]
   size_t wt_hi, wt_lo;             // bf16 planes of W^T, [bh][d][mpa], landmark order permuted
   size_t cwop;                     // matrix-core operands of the skip filters, [heads][d][4][9] x 16 B
   size_t total;

@@ -24,14 +24,15 @@ namespace nys {
 // Segment means: grid (m, batch*heads, 2); z = 0 -> Q, z = 1 -> K.
 // One block per segment of l = n/m contiguous rows; 16-byte coalesced loads,
 // fp32 partial sums per thread, fixed-order reduction through LDS.
-// Key landmarks are also written as bf16 hi/lo planes [bh][mpa][D] (rows
-// m..mpa-1 zero), the operand layout of the output stage.
+// Key landmarks are also written, pre-multiplied by log2(e)/sqrt(d), as bf16
+// hi/lo planes [bh][mpa][D] (rows m..mpa-1 zero), the operand layout of the
+// output stage, whose scores then come out in base-2 units.
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __restrict__ Q,
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
                                                       uint16_t* __restrict__ kt_hi, uint16_t* __restrict__ kt_lo,
-                                                      int n, int m, int mpa) {
+                                                      int n, int m, int mpa, float sl2e) {
   using T = typename IO::T;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int SLOTS = D / VEC;   // 16-byte vectors per row
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
     out[threadIdx.x] = mean;
     if (blockIdx.z == 1) {
       uint16_t hi, lo;
-      split_hi_lo(mean, hi, lo);
+      split_hi_lo(mean * sl2e, hi, lo);
       const size_t o = ((size_t)bh * mpa + j) * D + threadIdx.x;
       kt_hi[o] = hi;
       kt_lo[o] = lo;
@@ -1020,7 +1021,8 @@ static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   KernelTimer kt_("segment_mean", s);
   k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
-                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.n, p.m, w.mpa);
+                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.n, p.m, w.mpa,
+                                                         kLog2e / sqrtf((float)D));
 }
 
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
