@@ -10,11 +10,16 @@ Inputs are seeded synthetic tensors already resident in HBM.  The timed steps
 rotate over several independent input/output sets whose total exceeds the
 256 MB last-level cache, so every call reads its inputs from HBM.
 
-Prints one JSON line.  ``value`` is tokens/s (batch * n per step).
-``roofline`` is for the kernel with the largest share of GPU time: its
-algorithmic bytes per launch divided by its mean duration, timed with HIP
-events that the library records on the launch stream.  ``cpu_baseline`` is
-the fp64 CPU oracle timed on the host on whole calls of the same workload.
+Prints one JSON line.  ``value`` is tokens/s (batch * n per step) over exactly
+``--steps`` calls timed with two events on the launch stream; a second pass
+records an event between calls (``per_call_us``: median, p10, p90) and a
+third has the library bracket every kernel with events.  ``roofline`` is for
+the kernel with the largest share of GPU time: its algorithmic bytes per
+launch divided by its mean event-timed duration; ``traffic`` is that
+kernel's scaled HBM bytes per launch from the committed counter summary
+``profiles/hbm_traffic_<workload>.txt`` when it was made from the current
+kernel sources, else null.  ``cpu_baseline`` is the fp64 CPU oracle timed on
+the host on whole calls of the same workload.
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, TFLOP/s
 METRIC = "Nyström attention fwd tokens/s at n=8192,m=64,d=64; % of HBM roofline"
@@ -134,10 +140,8 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: whole steps, per-kernel HIP events recorded by the library
-    # on the same stream.
-    _lib.nystrom_timing_enable(True)
-    _lib.nystrom_timing_read()  # clear
+    # Timed region: exactly `steps` whole calls between two events on the
+    # launch stream, synchronised on both sides.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -147,21 +151,31 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern = _lib.nystrom_timing_read()
-    _lib.nystrom_timing_enable(False)
     gpu_s = ev0.elapsed_time(ev1) / 1e3
     ms_per_step = 1e3 * gpu_s / args.steps
     tokens = wl.batch * wl.n
     value = tokens * args.steps / gpu_s
 
-    # Same loop without per-kernel events, to show what the events cost.
+    # Per-call distribution: an event between consecutive calls.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_plain = ev0.elapsed_time(ev1) / args.steps
+    per_call_us = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+
+    # Per-kernel durations: HIP events the library records around each launch
+    # on the stream it launches on (the side-stream pseudoinverse included).
+    _lib.nystrom_timing_enable(True)
+    _lib.nystrom_timing_read()  # clear
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = _lib.nystrom_timing_read()
+    _lib.nystrom_timing_enable(False)
 
     per_kernel = {}
     for name, (ms, launches) in kern.items():
@@ -174,10 +188,12 @@ def main() -> int:
         avg_s = ms / launches / 1e3
         ab = algorithmic_bytes(wl, dom)
         if ab:
+            from efficient_transformer_attention_mean_amd.profiling import read_traffic
             achieved = ab / avg_s / 1e9
+            tr = read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{wl.name}.txt"), dom)
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                    "algorithmic_bytes": ab, "avg_us": round(avg_s * 1e6, 3)}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
+                    "kernel": dom, "algorithmic_bytes": ab, "avg_us": round(avg_s * 1e6, 3)}
         else:
             fl = pinv_flops(wl)
             achieved = fl / avg_s / 1e12
@@ -186,10 +202,12 @@ def main() -> int:
                     "kernel": dom, "algorithmic_flops": fl, "avg_us": round(avg_s * 1e6, 3)}
 
     if args.copy_calibration:
-        src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        # A plain copy of known size for scaling the HBM byte counters:
+        # reads and writes 256 MiB (fp32 elementwise add).
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
 
     result = {
@@ -199,7 +217,10 @@ def main() -> int:
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "n": wl.n, "d": wl.d, "m": wl.m,
                    "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype, "input_sets": sets},
         "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
-        "ms_per_step_without_kernel_events": round(ms_plain, 5),
+        "compulsory_bytes": io_bytes,
+        "per_call_us": {"median": round(float(np.median(per_call_us)), 2),
+                        "p10": round(float(np.percentile(per_call_us, 10)), 2),
+                        "p90": round(float(np.percentile(per_call_us, 90)), 2)},
         "wall_s": round(wall, 4),
         "roofline": roof,
         "kernels": per_kernel,
