@@ -20,8 +20,8 @@
 //   2. the V rows -> LDS, feature-major (Vt[feature][row]);
 //   3. the skip, added into Ot.  bf16 I/O: on the matrix cores with the
 //      16-block 4x4x4 instruction, one block per feature: A = a 4 x 4 band of
-//      that feature's taps (Toeplitz; operands prepared once per call by
-//      k_conv_ops), B = 4 consecutive V rows, 9 steps of 4 taps cover 33 taps
+//      that feature's taps (Toeplitz; operands prepared once per call in
+//      the landmark pass), B = 4 consecutive V rows, 9 steps of 4 taps cover 33 taps
 //      for 16 output rows; each lane ends with 4 consecutive rows of one
 //      feature.  fp32 I/O, or one tap: fp32 FMAs by a register sliding window;
 //   4. Ot -> output rows, one 16-byte store per lane, coalesced per row.
@@ -119,26 +119,6 @@ __device__ __forceinline__ bool q_ok(int qrow, int n, int kc) {
 }
 
 }  // namespace
-
-// Matrix-core operands of the skip filters for the 16-block 4x4x4 product.
-// Entry ((h * d + f) * 4 + i) * 9 + s holds taps 4s + k - i - off (k = 0..3)
-// of filter (h, f) as bf16 hi (k = 0..3) then bf16 lo, where off =
-// (33 - conv_k) / 2 centres a filter of conv_k <= 33 taps in 33 slots.
-__global__ __launch_bounds__(256) void k_conv_ops(const float* __restrict__ conv_w, uint4* __restrict__ ops,
-                                                  int total, int conv_k) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int st = idx % kConvNS, i = (idx / kConvNS) % 4, hf = idx / (4 * kConvNS);
-  const int off = (33 - conv_k) / 2;
-  B8 hl;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int tt = 4 * st + k - i - off;
-    const float w = (tt >= 0 && tt < conv_k) ? conv_w[(size_t)hf * conv_k + tt] : 0.f;
-    split_hi_lo(w, hl.h[k], hl.h[4 + k]);
-  }
-  ops[idx] = hl.q;
-}
 
 // Persistent blocks: block `rank` (XCD-contiguous numbering) processes the
 // run of 64-row tiles [rank * total / G, (rank + 1) * total / G) of the
@@ -568,16 +548,6 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
 // Launchers.
 
 static int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
-
-static bool conv_uses_ops(const Problem& p) { return p.bf16 && p.conv_w && p.conv_k > 1 && p.conv_k <= 33; }
-
-hipError_t stage_conv_ops(const Problem& p, const Ws& w, hipStream_t s) {
-  if (!conv_uses_ops(p)) return hipSuccess;
-  const int total = p.heads * p.d * 4 * kConvNS;
-  KernelTimer kt_("conv_ops", s);
-  k_conv_ops<<<cdiv(total, 256), 256, 0, s>>>(p.conv_w, w.cwop, total, p.conv_k);
-  return hipGetLastError();
-}
 
 // Blocks per CU the persistent grid is sized for (LDS and registers allow it
 // for the common shapes; more resident blocks only queue).

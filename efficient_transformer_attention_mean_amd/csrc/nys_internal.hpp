@@ -60,12 +60,12 @@ class KernelTimer {
   hipEvent_t start_ = nullptr;
 };
 
-// Stages of the forward pass.  The pseudoinverse depends only on the
-// landmarks, so it runs on a side stream beside the split-n pass.
+// Stages of the forward pass, in stream order.
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  // Qt, Kt, Kt planes
-hipError_t stage_conv_ops(const Problem& p, const Ws& w, hipStream_t s);       // skip-filter operands
-hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z
-hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s);             // split-n partials of B V
+// Split-n partials of B V; with bf16 I/O and m <= 64 also A and Z (the
+// pseudoinverse blocks run beside the key pass) and the skip-filter operands.
+hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s);
+hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z when not in the pass above
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      // B V, W, W^T planes (needs Z)
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 

@@ -4,11 +4,11 @@
 // Self-Attention" (paper deep-dive page, sec. 3.2 and 3.4).  Per (batch, head):
 //   segment means Qt, Kt (Eq. 16)         -> k_segment_mean
 //   A = softmax(Qt Kt^T / sqrt d), Z = Lemma-1 iterations from the
-//   Pan-Schreiber start                    -> k_pinv_planes (m <= 64, bf16 I/O),
-//                                             k_pinv_lds (m <= 64, fp32 I/O) or
+//   Pan-Schreiber start                    -> pinv_head inside k_landmark_pass (m <= 64,
+//                                             bf16 I/O), k_pinv_lds (m <= 64, fp32 I/O) or
 //                                             k_landmark_softmax + k_pinv_start + k_mm chain
-//   B V = softmax(Qt K^T / sqrt d) V       -> k_landmark_bv (split over keys,
-//                                             online softmax), then k_bv_finish
+//   B V = softmax(Qt K^T / sqrt d) V       -> bv_chunk inside k_landmark_pass (split over
+//                                             keys, online softmax), then k_bv_finish
 //   W = Z (B V), W^T bf16 planes           -> k_bv_finish
 // The output stage (softmax(Q Kt^T / sqrt d) W + DConv(V)) is in nys_apply.hip.
 // Softmaxes run in base 2: scores are pre-multiplied by log2(e)/sqrt(d), which
@@ -274,19 +274,19 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 // in that slot order (so a left-operand fragment is one 16-byte read per
 // plane).  A stays in registers.  One iteration
 //   X = A Z;  T = 7I - X;  T = 15I - X T;  T = 13I - X T;  Z = Z T / 4
-// has a single barrier (after X is stored): the X and Z planes are
-// double-buffered, and every buffer is rewritten only after all waves have
-// passed the barrier that follows its last read.
+// has two barriers: after X is stored, and after every wave has loaded the X
+// and Z fragments it needs (before Z is overwritten).
 template <int MP>
 struct PinvSmem2 {
   static constexpr int LD = MP + 8;  // plane row pitch (bf16): rows stay 16-byte aligned
   static constexpr int PL = MP * LD;
   static constexpr int SP = MP + 4;  // fp32 score row pitch
-  __align__(16) uint16_t xp[2][2][PL];  // X planes [buffer][hi, lo]
-  __align__(16) uint16_t zp[2][2][PL];  // Z planes [buffer][hi, lo]
-  __align__(16) float S[MP * SP];       // scaled scores, then A
-  float colp[4][MP];                    // partial column sums of A
-  float rows[MP];                       // row sums of A
+  __align__(16) uint16_t xp[2][PL];  // X planes [hi, lo]; the fp32 scores alias them before the iterations
+  __align__(16) uint16_t zp[2][PL];  // Z planes [hi, lo]
+  float colp[4][MP];                 // partial column sums of A
+  float rows[MP];                    // row sums of A
+  __device__ float* S() { return reinterpret_cast<float*>(&xp[0][0]); }
+  static_assert(sizeof(float) * MP * SP <= sizeof(uint16_t) * 2 * PL, "scores do not fit the X planes");
 };
 
 // B operand (chunks kc) of this wave's column block j from C-layout tiles v:
@@ -354,17 +354,16 @@ __device__ __forceinline__ void chain_mm(const B8 (&ph)[MP / 16][MP / 32], const
   }
 }
 
-// grid (batch*heads), block 64 * MP/16.
+// Pseudoinverse of one head, run by a block of 4 * MP threads.
 template <int MP, int D>
-__global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict__ Qt, const float* __restrict__ Kt,
-                                                        float* __restrict__ Aout, float* __restrict__ Zout, int m,
-                                                        float sl2e, int iters) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+__device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float* __restrict__ Qt,
+                                          const float* __restrict__ Kt, float* __restrict__ Aout,
+                                          float* __restrict__ Zout, int m, float sl2e, int iters) {
   using SM = PinvSmem2<MP>;
   constexpr int SP = SM::SP, RT = MP / 16, KC = MP / 32, CPT = MP / 4;
   constexpr int KCD = (D + 31) / 32;  // 32-wide chunks of the head dimension
-  SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  float* const S = sm.S();
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const float* qt = Qt + (size_t)bh * m * D;
   const float* kt = Kt + (size_t)bh * m * D;
@@ -408,7 +407,7 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
         frag(kv[tj][kc], 16 * tj + c < m && 32 * kc + 8 * g < D, kh, kl);
         acc = mfma3(kh, kl, qh[kc], ql[kc], acc);
       }
-      *reinterpret_cast<float4*>(&sm.S[rq * SP + 16 * tj + 4 * g]) =
+      *reinterpret_cast<float4*>(&S[rq * SP + 16 * tj + 4 * g]) =
           make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
     }
   }
@@ -421,7 +420,7 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
     float a[CPT];
 #pragma unroll
     for (int u = 0; u < CPT / 4; ++u) {
-      const float4 v = *reinterpret_cast<const float4*>(&sm.S[r * SP + j0 + 4 * u]);
+      const float4 v = *reinterpret_cast<const float4*>(&S[r * SP + j0 + 4 * u]);
       a[4 * u] = v.x; a[4 * u + 1] = v.y; a[4 * u + 2] = v.z; a[4 * u + 3] = v.w;
     }
     float mx = -INFINITY;
@@ -449,15 +448,27 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
     rs += shfl_xor(rs, 2);
 #pragma unroll
     for (int u = 0; u < CPT / 4; ++u)
-      *reinterpret_cast<float4*>(&sm.S[r * SP + j0 + 4 * u]) = make_float4(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
+      *reinterpret_cast<float4*>(&S[r * SP + j0 + 4 * u]) = make_float4(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
     if (sub == 0) sm.rows[r] = rs;
+    if (r < m) {
+      float* ao = Aout + (size_t)bh * m * m + (size_t)r * m;
+      if (m == MP) {
+#pragma unroll
+        for (int u = 0; u < CPT / 4; ++u)
+          *reinterpret_cast<float4*>(ao + j0 + 4 * u) = make_float4(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q)
+          if (j0 + q < m) ao[j0 + q] = a[q];
+      }
+    }
   }
   __syncthreads();
   {  // partial column sums over quarters of the rows
     const int col = tid % MP, part = tid / MP;
     float s = 0.f;
 #pragma unroll 4
-    for (int rr = 0; rr < MP / 4; ++rr) s += sm.S[(part * (MP / 4) + rr) * SP + col];
+    for (int rr = 0; rr < MP / 4; ++rr) s += S[(part * (MP / 4) + rr) * SP + col];
     sm.colp[part][col] = s;
   }
   __syncthreads();
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const float* src = &sm.S[(16 * t + c) * SP + 32 * kc + 4 * g];
+      const float* src = &S[(16 * t + c) * SP + 32 * kc + 4 * g];
       const float4 u0 = *reinterpret_cast<const float4*>(src);
       const float4 u1 = *reinterpret_cast<const float4*>(src + 16);
       const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -498,10 +509,10 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
         }
       }
     }
-  store_bop<MP>(sm.zp[0][0], sm.zp[0][1], Zh, Zl, wave);
+  store_bop<MP>(sm.zp[0], sm.zp[1], Zh, Zl, wave);
+  __syncthreads();  // every wave has read the scores before X overwrites them
 
   for (int it = 0; it < iters; ++it) {
-    const int p = it & 1;
     f32x4_t acc[RT];
     B8 Th[KC], Tl[KC];
     // X = A Z: store X for every wave; keep T1 = 7I - X (own columns).
@@ -509,13 +520,13 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
     {
       B8 xh[KC], xl[KC];
       to_bop<MP>(acc, 1.f, 0.f, wave, xh, xl);
-      store_bop<MP>(sm.xp[p][0], sm.xp[p][1], xh, xl, wave);
+      store_bop<MP>(sm.xp[0], sm.xp[1], xh, xl, wave);
     }
     to_bop<MP>(acc, -1.f, 7.f, wave, Th, Tl);
     __syncthreads();
     B8 Ph[RT][KC], Pl[RT][KC], Rh[RT][KC], Rl[RT][KC];
-    load_aop<MP>(sm.xp[p][0], sm.xp[p][1], Ph, Pl);
-    load_aop<MP>(sm.zp[p][0], sm.zp[p][1], Rh, Rl);  // in flight during the two X products
+    load_aop<MP>(sm.xp[0], sm.xp[1], Ph, Pl);
+    load_aop<MP>(sm.zp[0], sm.zp[1], Rh, Rl);  // in flight during the two X products
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T1
     to_bop<MP>(acc, -1.f, 15.f, wave, Th, Tl);
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T3
@@ -524,15 +535,11 @@ __global__ __launch_bounds__(4 * MP) void k_pinv_planes(const float* __restrict_
 #pragma unroll
     for (int t = 0; t < RT; ++t) zf[t] = acc[t] * 0.25f;
     to_bop<MP>(zf, 1.f, 0.f, wave, Zh, Zl);
-    store_bop<MP>(sm.zp[p ^ 1][0], sm.zp[p ^ 1][1], Zh, Zl, wave);
+    __syncthreads();  // every wave holds its X and Z fragments
+    store_bop<MP>(sm.zp[0], sm.zp[1], Zh, Zl, wave);
   }
 
-  // A (kept in LDS; global stores are left to the end so that no barrier
-  // waits on them) and Z in fp32 straight from the last product.
-  {
-    float* ao = Aout + (size_t)bh * m * m;
-    for (int e = tid; e < m * m; e += 4 * MP) ao[e] = sm.S[(e / m) * SP + e % m];
-  }
+  // Z in fp32 straight from the last product.
   const int col = 16 * wave + c;
   if (col < m) {
     float* zo = Zout + (size_t)bh * m * m;
@@ -712,18 +719,18 @@ struct BvStage {
   uint4 k[2][W], v[2][W];
 };
 
+// One (key chunk, head) of the split-n pass, run by a block of 256 threads.
 template <typename IO, int D, int NTW>
-__global__ __launch_bounds__(256) void k_landmark_bv(const typename IO::T* __restrict__ Kin,
-                                                     const typename IO::T* __restrict__ Vin,
-                                                     const float* __restrict__ Qt, float* __restrict__ pacc,
-                                                     float* __restrict__ pmax, float* __restrict__ psum,
-                                                     int n, int m, int chunk, int nchunks, float sl2e) {
+__device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, const typename IO::T* __restrict__ Kin,
+                                         const typename IO::T* __restrict__ Vin, const float* __restrict__ Qt,
+                                         float* __restrict__ pacc, float* __restrict__ pmax,
+                                         float* __restrict__ psum, int n, int m, int chunk, int nchunks,
+                                         float sl2e) {
   using T = typename IO::T;
   using SM = BvSmem<IO, D>;
   constexpr int KC = (D + 31) / 32;  // 32-wide k chunks over the head dimension
   constexpr int MD = D / 16;         // 16-row tiles of V^T
-  __shared__ SM sm;
-  const int ch = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
   const T* Kh = Kin + (size_t)bh * n * D;
@@ -933,6 +940,73 @@ __global__ __launch_bounds__(256) void k_landmark_bv(const typename IO::T* __res
   }
 }
 
+// Skip-filter operands for the matrix-core conv of the output stage.
+// Entry ((h * d + f) * 4 + i) * 9 + s holds taps 4s + k - i - off (k = 0..3)
+// of filter (h, f) as bf16 hi (k = 0..3) then bf16 lo, where off =
+// (33 - conv_k) / 2 centres a filter of conv_k <= 33 taps in 33 slots.
+__device__ __forceinline__ void conv_operand(const float* __restrict__ conv_w, uint4* __restrict__ ops, int idx,
+                                             int conv_k) {
+  constexpr int NS = 9;
+  const int st = idx % NS, i = (idx / NS) % 4, hf = idx / (4 * NS);
+  const int off = (33 - conv_k) / 2;
+  B8 hl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int tt = 4 * st + k - i - off;
+    const float w = (tt >= 0 && tt < conv_k) ? conv_w[(size_t)hf * conv_k + tt] : 0.f;
+    split_hi_lo(w, hl.h[k], hl.h[4 + k]);
+  }
+  ops[idx] = hl.q;
+}
+
+// The landmark-side pass in one launch.  Blocks [0, npinv): the
+// pseudoinverse of head blockIdx.x (it depends only on the landmarks);
+// then nconv blocks of skip-filter operands; then the split-n pass, block
+// (bh * nchunks + chunk).  The pseudoinverse blocks come first so that they
+// are placed while the key-pass blocks fill the rest of the machine.
+struct LandmarkPassArgs {
+  const void* K;
+  const void* V;
+  const float *Qt, *Kt;
+  float *A, *Z, *pacc, *pmax, *psum;
+  const float* conv_w;
+  uint4* cwop;
+  int n, m, chunk, nchunks, iters, npinv, nconv, conv_total, conv_k;
+  float sl2e;
+};
+
+template <bool PINV, typename B>
+union LandmarkPassSmem {
+  PinvSmem2<64> p;
+  B b;
+};
+template <typename B>
+union LandmarkPassSmem<false, B> {
+  B b;
+};
+
+template <typename IO, int D, int NTW, bool PINV>
+__global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
+  using T = typename IO::T;
+  __shared__ LandmarkPassSmem<PINV, BvSmem<IO, D>> sm;
+  int blk = blockIdx.x;
+  if constexpr (PINV) {
+    if (blk < a.npinv) {
+      pinv_head<64, D>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters);
+      return;
+    }
+    blk -= a.npinv;
+  }
+  if (blk < a.nconv) {
+    const int idx = blk * 256 + (int)threadIdx.x;
+    if (idx < a.conv_total) conv_operand(a.conv_w, a.cwop, idx, a.conv_k);
+    return;
+  }
+  blk -= a.nconv;
+  bv_chunk<IO, D, NTW>(sm.b, blk % a.nchunks, blk / a.nchunks, static_cast<const T*>(a.K), static_cast<const T*>(a.V),
+                       a.Qt, a.pacc, a.pmax, a.psum, a.n, a.m, a.chunk, a.nchunks, a.sl2e);
+}
+
 // Finish of the split-n pass, one block per (16-feature slice, head):
 //   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
 //   (M_j = max_c pmax_c[j]; chunks in fixed order), then W = Z BV for the
@@ -1038,41 +1112,11 @@ hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
 
 // Landmark-side m x m products: fp32-grade for fp32 I/O, bf16x3 for bf16 I/O
 // (where the output rounding dominates the error).
-template <int MP, int D>
-static hipError_t pinv_planes_launch(const Problem& p, const Ws& w, hipStream_t s) {
-  const int BH = p.batch * p.heads;
-  const float sl2e = kLog2e / sqrtf((float)D);
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_planes<MP, D>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)sizeof(PinvSmem2<MP>));
-  if (attr != hipSuccess) return attr;
-  KernelTimer kt_("pinv", s);
-  k_pinv_planes<MP, D><<<BH, 4 * MP, sizeof(PinvSmem2<MP>), s>>>(w.Qt, w.Kt, w.A, w.Z, p.m, sl2e, p.iters);
-  return hipSuccess;
-}
-
-template <int MP>
-static hipError_t pinv_planes_t(const Problem& p, const Ws& w, hipStream_t s) {
-  switch (p.d) {
-    case 16: return pinv_planes_launch<MP, 16>(p, w, s);
-    case 32: return pinv_planes_launch<MP, 32>(p, w, s);
-    case 64: return pinv_planes_launch<MP, 64>(p, w, s);
-    case 128: return pinv_planes_launch<MP, 128>(p, w, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 template <int PR>
 static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads, m = p.m, D = p.d;
   const float sl2e = kLog2e / sqrtf((float)D);
-  if (PR == 3 && m <= 32) {
-    hipError_t e = pinv_planes_t<32>(p, w, s);
-    return e != hipSuccess ? e : hipGetLastError();
-  } else if (PR == 3 && m <= 64) {
-    hipError_t e = pinv_planes_t<64>(p, w, s);
-    return e != hipSuccess ? e : hipGetLastError();
-  } else if (m <= 32) {
+  if (m <= 32) {
     KernelTimer kt_("pinv", s);
     k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
   } else if (m <= 64) {
@@ -1110,33 +1154,64 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool pinv_in_landmark_pass(const Problem& p) { return p.bf16 && p.m <= 64; }
+
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
+  if (pinv_in_landmark_pass(p)) return hipSuccess;
   return p.bf16 ? pinv_t<3>(p, w, s) : pinv_t<6>(p, w, s);
 }
 
-template <typename IO, int D>
-static void bv_t(const Problem& p, const Ws& w, hipStream_t s) {
-  using T = typename IO::T;
-  const int BH = p.batch * p.heads, m = p.m;
-  const float sl2e = kLog2e / sqrtf((float)D);
-  const T* K = static_cast<const T*>(p.K);
-  const T* V = static_cast<const T*>(p.V);
-  const dim3 g(w.nchunks, BH);
-  KernelTimer kt_("landmark_bv", s);
-  if (m <= 64)
-    k_landmark_bv<IO, D, 1><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
-  else if (m <= 128)
-    k_landmark_bv<IO, D, 2><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
-  else
-    k_landmark_bv<IO, D, 4><<<g, 256, 0, s>>>(K, V, w.Qt, w.pacc, w.pmax, w.psum, p.n, m, w.chunk, w.nchunks, sl2e);
+static bool conv_uses_ops(const Problem& p) { return p.bf16 && p.conv_w && p.conv_k > 1 && p.conv_k <= 33; }
+
+template <typename IO, int D, int NTW, bool PINV>
+static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads;
+  LandmarkPassArgs a;
+  a.K = p.K;
+  a.V = p.V;
+  a.Qt = w.Qt;
+  a.Kt = w.Kt;
+  a.A = w.A;
+  a.Z = w.Z;
+  a.pacc = w.pacc;
+  a.pmax = w.pmax;
+  a.psum = w.psum;
+  a.conv_w = p.conv_w;
+  a.cwop = w.cwop;
+  a.n = p.n;
+  a.m = p.m;
+  a.chunk = w.chunk;
+  a.nchunks = w.nchunks;
+  a.iters = p.iters;
+  a.npinv = PINV ? BH : 0;
+  a.conv_total = conv_uses_ops(p) ? p.heads * p.d * 4 * 9 : 0;
+  a.nconv = ceil_div(a.conv_total, 256);
+  a.conv_k = p.conv_k;
+  a.sl2e = kLog2e / sqrtf((float)D);
+  const int grid = a.npinv + a.nconv + w.nchunks * BH;
+  KernelTimer kt_("landmark_pass", s);
+  k_landmark_pass<IO, D, NTW, PINV><<<grid, 256, 0, s>>>(a);
 }
 
-hipError_t stage_bv(const Problem& p, const Ws& w, hipStream_t s) {
+template <typename IO, int D>
+static void landmark_pass_t(const Problem& p, const Ws& w, hipStream_t s) {
+  if constexpr (IO::kBf16) {
+    if (p.m <= 64) return landmark_pass_launch<IO, D, 1, true>(p, w, s);
+  }
+  if (p.m <= 64)
+    landmark_pass_launch<IO, D, 1, false>(p, w, s);
+  else if (p.m <= 128)
+    landmark_pass_launch<IO, D, 2, false>(p, w, s);
+  else
+    landmark_pass_launch<IO, D, 4, false>(p, w, s);
+}
+
+hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {
   switch (p.d) {
-    case 16: p.bf16 ? bv_t<BF16, 16>(p, w, s) : bv_t<F32, 16>(p, w, s); break;
-    case 32: p.bf16 ? bv_t<BF16, 32>(p, w, s) : bv_t<F32, 32>(p, w, s); break;
-    case 64: p.bf16 ? bv_t<BF16, 64>(p, w, s) : bv_t<F32, 64>(p, w, s); break;
-    case 128: p.bf16 ? bv_t<BF16, 128>(p, w, s) : bv_t<F32, 128>(p, w, s); break;
+    case 16: p.bf16 ? landmark_pass_t<BF16, 16>(p, w, s) : landmark_pass_t<F32, 16>(p, w, s); break;
+    case 32: p.bf16 ? landmark_pass_t<BF16, 32>(p, w, s) : landmark_pass_t<F32, 32>(p, w, s); break;
+    case 64: p.bf16 ? landmark_pass_t<BF16, 64>(p, w, s) : landmark_pass_t<F32, 64>(p, w, s); break;
+    case 128: p.bf16 ? landmark_pass_t<BF16, 128>(p, w, s) : landmark_pass_t<F32, 128>(p, w, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,7 +1,4 @@
 // Workspace layout and the stream-ordered sequence of forward stages.
-#include <mutex>
-#include <vector>
-
 #include "nys_internal.hpp"
 
 namespace nys {
@@ -12,9 +9,10 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n || n % m != 0) return false;
   if (!(d == 16 || d == 32 || d == 64 || d == 128) || m > 256 || n > (1 << 24)) return false;
   const long long BH = (long long)batch * heads;
-  // Key chunking for the split-n pass: aim for about 2 blocks per CU over 256
-  // CUs; chunks are a multiple of the 64-key tile.
-  long long want = cdiv(512, BH);
+  // Key chunking for the split-n pass: about 2 blocks per CU over 256 CUs
+  // together with the one pseudoinverse block per head that shares the
+  // launch; chunks are a multiple of the 64-key tile.
+  long long want = (512 - (BH < 256 ? BH : 256)) / BH;
   long long maxch = cdiv(n, 64);
   long long nch = want < 1 ? 1 : (want > maxch ? maxch : want);
   long long chunk = cdiv(cdiv(n, nch), 64) * 64;
@@ -78,68 +76,12 @@ Ws resolve(const WsLayout& L, char* b) {
   return w;
 }
 
-namespace {
-
-// A side stream (default priority, non-blocking) and two events, reused
-// across calls on one device.  Enqueued waits capture an event's state when
-// they are enqueued, so an entry can be handed to the next call as soon as
-// the join has been enqueued.
-struct Side {
-  int device;
-  hipStream_t stream;
-  hipEvent_t fork, join;
-};
-std::mutex g_side_mu;
-std::vector<Side*> g_side_free;
-
-hipError_t acquire_side(Side** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    for (size_t i = 0; i < g_side_free.size(); ++i) {
-      if (g_side_free[i]->device == dev) {
-        *out = g_side_free[i];
-        g_side_free.erase(g_side_free.begin() + i);
-        return hipSuccess;
-      }
-    }
-  }
-  Side* sd = new Side{dev, nullptr, nullptr, nullptr};
-  if ((e = hipStreamCreateWithFlags(&sd->stream, hipStreamNonBlocking)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&sd->fork, hipEventDisableTiming)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&sd->join, hipEventDisableTiming)) != hipSuccess) {
-    delete sd;  // handles created so far are kept alive by the runtime until exit
-    return e;
-  }
-  *out = sd;
-  return hipSuccess;
-}
-
-void release_side(Side* sd) {
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  g_side_free.push_back(sd);
-}
-
-}  // namespace
-
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s) {
   const Ws w = resolve(L, ws);
   hipError_t e;
   if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
-  Side* sd = nullptr;
-  if ((e = acquire_side(&sd)) != hipSuccess) return e;
-  // Fork: the pseudoinverse (landmarks only) and the skip-filter operands
-  // beside the split-n pass over K, V.
-  if ((e = hipEventRecord(sd->fork, s)) == hipSuccess && (e = hipStreamWaitEvent(sd->stream, sd->fork, 0)) == hipSuccess &&
-      (e = stage_conv_ops(p, w, sd->stream)) == hipSuccess && (e = stage_pinv(p, w, sd->stream)) == hipSuccess &&
-      (e = hipEventRecord(sd->join, sd->stream)) == hipSuccess &&
-      (e = stage_bv(p, w, s)) == hipSuccess) {
-    e = hipStreamWaitEvent(s, sd->join, 0);
-  }
-  release_side(sd);
-  if (e != hipSuccess) return e;
+  if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
   if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
   return stage_apply(p, w, s);
 }

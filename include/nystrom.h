@@ -18,11 +18,8 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     keeps no data between calls and never frees caller memory.  On first
- *     use per device it creates one non-blocking side stream (default
- *     priority) and two events, which it reuses: the pseudoinverse, which
- *     needs only the landmarks, runs on that stream beside the pass over K
- *     and V, joined back into `stream` before the output stage.
+ *     keeps no data between calls, never frees caller memory and creates no
+ *     streams: every kernel runs on `stream`, in order.
  *   - Q, K, V, out: [batch][heads][n][d], contiguous, element type `dtype`
  *     (NYS_F32 = IEEE fp32, NYS_BF16 = bfloat16).  conv_w: fp32
  *     [heads][d][conv_k], contiguous, or NULL for no skip.
