@@ -737,7 +737,9 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   const T* Vh = Vin + (size_t)bh * n * D;
   const float* qt = Qt + (size_t)bh * m * D;
 
-  // Landmark-query operands (B of S^T = K Qt^T), split hi/lo, in registers.
+  // Landmark-query operands (B of S^T = K Qt^T), pre-multiplied by
+  // log2(e)/sqrt(d) so that scores come out in base-2 units, split hi/lo,
+  // in registers.
   B8 qh[NTW][KC], ql[NTW][KC];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
@@ -748,7 +750,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int dd = kc * 32 + 8 * g + q;
-        x[q] = (lm < m && dd < D) ? qt[lm * D + dd] : 0.f;
+        x[q] = (lm < m && dd < D) ? qt[lm * D + dd] * sl2e : 0.f;
       }
       split8(x, qh[t][kc], ql[t][kc]);
     }
@@ -859,25 +861,30 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
           }
         }
       }
-      // Online softmax over this tile's keys for landmark (wave*NTW+t)*16 + c.
+      // Online softmax over this tile's keys for landmark (wave*NTW+t)*16 + c;
+      // scores are in base-2 units; keys past the chunk end only in its
+      // last tile.
+      if (k0 + 64 > kend) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + mt * 16 + 4 * g + i >= kend) s[mt][i] = -INFINITY;
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + mt * 16 + 4 * g + i;
-          s[mt][i] = (key < kend) ? s[mt][i] * sl2e : -INFINITY;
-          tmax = fmaxf(tmax, s[mt][i]);
-        }
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[mt][i]);
       tmax = max_over_groups(tmax);
       const float nmax = fmaxf(run_max[t], tmax);
-      const float corr = exp2f(run_max[t] - nmax);
+      const float corr = __builtin_amdgcn_exp2f(run_max[t] - nmax);  // arguments <= 0; exp2(-inf) = 0
       float psum_l = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[mt][i] = exp2f(s[mt][i] - nmax);
+          s[mt][i] = __builtin_amdgcn_exp2f(s[mt][i] - nmax);
           psum_l += s[mt][i];
         }
       run_sum[t] = run_sum[t] * corr + sum_over_groups(psum_l);
@@ -1027,46 +1034,113 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
   const int bh = blockIdx.y, f0 = blockIdx.x * 16, tid = threadIdx.x;
   const int f = tid & 15;
   const float* z = Z + (size_t)bh * m * m;
+  // Z (m <= 64: at most 4 values per thread) is loaded first, beside the
+  // partials, and stored to LDS after the combine.
+  float zv[4];
   if constexpr (ZLDS) {
-    for (int e = tid; e < m * m; e += 1024) sz[(e / m) * 68 + e % m] = z[e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) zv[u] = z[min(tid + 1024 * u, m * m - 1)];
   }
   const size_t pb = (size_t)bh * nchunks * m;
-  for (int j = tid >> 4; j < m; j += 64) {
-    // Online combine over the chunks in fixed order, 8 chunks' loads in flight.
-    float M = -INFINITY, L = 0.f, S = 0.f;
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {
-      float pm[8], ps[8], pa[8];
+  // Combine over the chunks.  Thread (part, j, q): chunk subset `part` (of 4,
+  // interleaved), landmark j, features f0 + 4q .. +3 (16-byte loads); each
+  // part folds its chunks in order (running max per batch of NB), then part
+  // 0 folds the 4 parts in order, so the result does not depend on timing.
+  __shared__ float red[4][64][2];        // per part and landmark: max, sum
+  __shared__ float reds[4][64][4][4];    // per part, landmark, feature quad: accumulator
+  {
+    const int part = tid >> 8, r = tid & 255, jl = r >> 2, q = r & 3;
+    for (int j0 = 0; j0 < m; j0 += 64) {
+      const int j = j0 + jl;
+      const int jc = min(j, m - 1);
+      constexpr int NB = 8;
+      float M = -INFINITY, L = 0.f, S[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = part; c0 < nchunks; c0 += 4 * NB) {
+        float pm[NB], ps[NB];
+        float4 pa[NB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = c0 + u < nchunks;
-        const size_t o = pb + (size_t)(in ? c0 + u : 0) * m + j;
-        pm[u] = in ? pmax[o] : -INFINITY;
-        ps[u] = in ? psum[o] : 0.f;
-        pa[u] = in ? pacc[o * D + f0 + f] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (c0 + u < nchunks) {
-          const float Mn = fmaxf(M, pm[u]);
-          const float a = exp2f(M - Mn), b = exp2f(pm[u] - Mn);
-          L = L * a + ps[u] * b;
-          S = S * a + pa[u] * b;
-          M = Mn;
+        for (int u = 0; u < NB; ++u) {
+          const int cc = min(c0 + 4 * u, nchunks - 1);
+          const size_t o = pb + (size_t)cc * m + jc;
+          pm[u] = pmax[o];
+          ps[u] = psum[o];
+          pa[u] = *reinterpret_cast<const float4*>(&pacc[o * D + f0 + 4 * q]);
         }
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+          if (c0 + 4 * u < nchunks) Mb = fmaxf(Mb, pm[u]);
+        const float a = __builtin_amdgcn_exp2f(M - Mb);  // arguments <= 0; 0 while M = -inf
+        L *= a;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) S[k] *= a;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          if (c0 + 4 * u < nchunks) {
+            const float e = __builtin_amdgcn_exp2f(pm[u] - Mb);
+            L += ps[u] * e;
+            S[0] += pa[u].x * e;
+            S[1] += pa[u].y * e;
+            S[2] += pa[u].z * e;
+            S[3] += pa[u].w * e;
+          }
+        }
+        M = Mb;
       }
+      // Parts with no chunk (nchunks < 4) keep M = -inf, L = S = 0.
+      if (q == 0) {
+        red[part][jl][0] = M;
+        red[part][jl][1] = L;
+      }
+      *reinterpret_cast<float4*>(&reds[part][jl][q][0]) = make_float4(S[0], S[1], S[2], S[3]);
+      __syncthreads();
+      if (part == 0 && j < m) {
+        float Mt = -INFINITY;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) Mt = fmaxf(Mt, red[pp][jl][0]);
+        float Lt = 0.f, St[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float e = __builtin_amdgcn_exp2f(red[pp][jl][0] - Mt);  // exp2(-inf) = 0 for empty parts
+          Lt += red[pp][jl][1] * e;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) St[k] += reds[pp][jl][q][k] * e;
+        }
+        const float inv = 1.f / Lt;
+        float4 v = make_float4(St[0] * inv, St[1] * inv, St[2] * inv, St[3] * inv);
+        sbv[j][4 * q] = v.x;
+        sbv[j][4 * q + 1] = v.y;
+        sbv[j][4 * q + 2] = v.z;
+        sbv[j][4 * q + 3] = v.w;
+        *reinterpret_cast<float4*>(&BV[((size_t)bh * m + j) * D + f0 + 4 * q]) = v;
+      }
+      __syncthreads();
     }
-    const float v = S / L;
-    sbv[j][f] = v;
-    BV[((size_t)bh * m + j) * D + f0 + f] = v;
+  }
+  if constexpr (ZLDS) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 1024 * u;
+      if (e < m * m) sz[(e / m) * 68 + e % m] = zv[u];
+    }
   }
   __syncthreads();
   for (int i = tid >> 4; i < m; i += 64) {
-    float acc = 0.f;
+    // Four interleaved partial sums (fixed order) keep the LDS reads in flight.
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
     if constexpr (ZLDS) {
-      for (int k = 0; k < m; ++k) acc = fmaf(sz[i * 68 + k], sbv[k][f], acc);
+      for (int k = 0; k < (m & ~3); k += 4) {
+        const float4 zr = *reinterpret_cast<const float4*>(&sz[i * 68 + k]);
+        acc4[0] = fmaf(zr.x, sbv[k][f], acc4[0]);
+        acc4[1] = fmaf(zr.y, sbv[k + 1][f], acc4[1]);
+        acc4[2] = fmaf(zr.z, sbv[k + 2][f], acc4[2]);
+        acc4[3] = fmaf(zr.w, sbv[k + 3][f], acc4[3]);
+      }
+      for (int k = m & ~3; k < m; ++k) acc4[0] = fmaf(sz[i * 68 + k], sbv[k][f], acc4[0]);
     } else {
-      for (int k = 0; k < m; ++k) acc = fmaf(z[(size_t)i * m + k], sbv[k][f], acc);
+      for (int k = 0; k < m; ++k) acc4[k & 3] = fmaf(z[(size_t)i * m + k], sbv[k][f], acc4[k & 3]);
     }
+    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     sw[i][f] = acc;
     W[((size_t)bh * m + i) * D + f0 + f] = acc;
   }
