@@ -53,16 +53,13 @@ struct ApplyLayout {
   static constexpr int OP = D + 4;      // Ot row pitch (floats)
   static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
   static constexpr int WP = MPA + 8;    // W^T plane row pitch (bf16)
-  // The current head's Kt fragments stay in registers when they are few
-  // (KREG); otherwise the Kt planes, like the W^T planes, are kept in LDS
-  // when they fit (KWL), else read from global memory.
-  static constexpr int KC = (D + 31) / 32;
-  static constexpr bool KREG = ATT && NTM * KC <= 8;
-  static constexpr bool KWL = ATT && ((KREG ? 0 : 4 * MPA * KP) + 4 * D * WP) <= 72 * 1024;
+  // The current head's Kt and W^T planes are kept in LDS when they fit
+  // (KWL), else read from global memory.
+  static constexpr bool KWL = ATT && (4 * MPA * KP + 4 * D * WP) <= 72 * 1024;
   static constexpr int OT = 0;
   static constexpr int VT = OT + 4 * kTQ * OP;
   static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
-  static constexpr int WT = KT + (KWL && !KREG ? 4 * MPA * KP : 0);
+  static constexpr int WT = KT + (KWL ? 4 * MPA * KP : 0);
   static constexpr int BYTES = WT + (KWL ? 4 * D * WP : 0);
   // V tile loads: task = 4 rows x one 16-byte chunk.
   static constexpr int FPC = IO::kBf16 ? 8 : 4;  // features per 16-byte chunk
@@ -192,7 +189,6 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
     }
   };
 
-  B8 kreg[LY::KREG ? NTM : 1][LY::KREG ? KC : 1][2];  // Kt fragments (hi, lo) of the current head
   // Two register sets of tile inputs: tile t is computed while the loads of
   // tiles t + 1 and t + 2 are in flight.
   uint4 vra[NTK][4], vrb[NTK][4];
@@ -223,24 +219,12 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
     if (bh != cur) {
       // New head: its Kt / W^T planes -> LDS (the previous tile's readers
       // are past the barrier that follows the attention), filter operands.
-      if constexpr (LY::KREG) {
-#pragma unroll
-        for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            const size_t o = (size_t)bh * MPA * D + (size_t)(mt * 16 + c) * D + min(kc * 32 + 8 * g, D - 8);
-            kreg[mt][kc][0].q = *reinterpret_cast<const uint4*>(kt_hi + o);
-            kreg[mt][kc][1].q = *reinterpret_cast<const uint4*>(kt_lo + o);
-          }
-      }
       if constexpr (LY::KWL) {
-        if constexpr (!LY::KREG) {
-          const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
-                                reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
-          for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
-            const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
-            *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
-          }
+        const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
+                              reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
+        for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
+          const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
+          *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
         }
         const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
                               reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
@@ -276,10 +260,12 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[k][3]);
 #pragma unroll
           for (int dw = 0; dw < 4; ++dw) {
-            // features 8*oc + 2*dw (low halves) and 8*oc + 2*dw + 1 (high halves)
-            const uint2 lo = make_uint2((w0[dw] & 0xffffu) | (w1[dw] << 16), (w2[dw] & 0xffffu) | (w3[dw] << 16));
-            const uint2 hi =
-                make_uint2((w0[dw] >> 16) | (w1[dw] & 0xffff0000u), (w2[dw] >> 16) | (w3[dw] & 0xffff0000u));
+            // features 8*oc + 2*dw (low halves) and 8*oc + 2*dw + 1 (high halves);
+            // byte selects: 0x05040100 = {b.lo16, a.lo16}, 0x07060302 = {b.hi16, a.hi16}.
+            const uint2 lo = make_uint2(__builtin_amdgcn_perm(w1[dw], w0[dw], 0x05040100u),
+                                        __builtin_amdgcn_perm(w3[dw], w2[dw], 0x05040100u));
+            const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[dw], w0[dw], 0x07060302u),
+                                        __builtin_amdgcn_perm(w3[dw], w2[dw], 0x07060302u));
             *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw) * VP + 4 * rq]) = lo;
             *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw + 1) * VP + 4 * rq]) = hi;
           }
@@ -301,9 +287,10 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
     // Attention for this wave's 16 queries -> Ot; or zeros.
     if constexpr (ATT) {
       B8 qh[KC], ql[KC];
+      const bool qtail = t0 + kTQ > n || !KFULL;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const bool ok = q_ok<D>(t0 + 16 * wave + c, n, kc);
+        const bool ok = !qtail || q_ok<D>(t0 + 16 * wave + c, n, kc);
         if constexpr (IO::kBf16) {
           qh[kc].q = ok ? qr[kc][0] : make_uint4(0, 0, 0, 0);
         } else {
@@ -318,8 +305,6 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
       const uint16_t* kth = LY::KWL ? kp : kt_hi + (size_t)bh * MPA * D;
       const uint16_t* ktl = LY::KWL ? kp + MPA * KP : kt_lo + (size_t)bh * MPA * D;
       constexpr int KPI = LY::KWL ? KP : D;
-      (void)kth;
-      (void)ktl;
       f32x4_t sc[NTM];
 #pragma unroll
       for (int mt = 0; mt < NTM; ++mt) {
@@ -328,14 +313,9 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         for (int kc = 0; kc < KC; ++kc) {
           const int dd = kc * 32 + 8 * g;
           B8 kh, kl;
-          if constexpr (LY::KREG) {
-            kh = kreg[mt][kc][0];
-            kl = kreg[mt][kc][1];
-          } else {
-            const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
-            kh.q = *reinterpret_cast<const uint4*>(kth + o);
-            kl.q = *reinterpret_cast<const uint4*>(ktl + o);
-          }
+          const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
+          kh.q = *reinterpret_cast<const uint4*>(kth + o);
+          kl.q = *reinterpret_cast<const uint4*>(ktl + o);
           if (!KFULL && dd >= D) {
             kh.q = make_uint4(0, 0, 0, 0);
             kl.q = make_uint4(0, 0, 0, 0);
@@ -372,7 +352,7 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           sc[mt][i] = __builtin_amdgcn_exp2f(sc[mt][i] - mx);  // arguments <= 0; exp2(-inf) = 0
           sum += sc[mt][i];
         }
-      const float inv = 1.f / sum_over_groups(sum);
+      const float inv = __builtin_amdgcn_rcpf(sum_over_groups(sum));  // sum >= 1 (the max term is 1)
 
       // O^T (features x queries) = W^T F^T.  The W^T planes hold each
       // 32-landmark chunk in the order {4g..4g+3, 16+4g..16+4g+3}, the order
