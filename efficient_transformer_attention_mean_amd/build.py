@@ -26,6 +26,8 @@ FLAGS = [
     f"--offload-arch={ARCH}",
     # Packed fp32 ops (v_pk_fma_f32 and friends) are kept out of every kernel.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in ordinary VGPRs: no copies to and from AGPRs.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result",
     "-I", os.path.join(ROOT, "include"),
 ]
