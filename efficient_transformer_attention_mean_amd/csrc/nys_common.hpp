@@ -138,13 +138,26 @@ __device__ __forceinline__ void load8f(const typename IO::T* p, float (&x)[8]) {
 // Cross-lane helpers within a wave of 64.
 __device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-__device__ __forceinline__ float max_over_groups(float v) {  // over lanes c, c+16, c+32, c+48
-  v = fmaxf(v, shfl_xor(v, 16));
-  return fmaxf(v, shfl_xor(v, 32));
+// Reductions over lanes c, c+16, c+32, c+48 with gfx950's row swaps
+// (v_permlane16_swap / v_permlane32_swap, no LDS round trip).  With both
+// operands equal, the 16-swap returns {rows 0,0,2,2} and {rows 1,1,3,3} and
+// the 32-swap {low half twice} and {high half twice}; every lane of a group
+// ends with the same bits ((x0 op x1) op (x2 op x3)).
+__device__ __forceinline__ float max_over_groups(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const uint32_t b2 = __float_as_uint(v);
+  const auto q = __builtin_amdgcn_permlane32_swap(b2, b2, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += shfl_xor(v, 16);
-  return v + shfl_xor(v, 32);
+  const uint32_t b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const uint32_t b2 = __float_as_uint(v);
+  const auto q = __builtin_amdgcn_permlane32_swap(b2, b2, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -816,14 +816,20 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
         *reinterpret_cast<uint4*>(&sm.k[0][(2 * rp + h) * SM::KP + s8]) = kh[h].q;
         if constexpr (SM::PL == 2) *reinterpret_cast<uint4*>(&sm.k[1][(2 * rp + h) * SM::KP + s8]) = kl[h].q;
       }
-      // V^T: feature s8+q, keys 2rp and 2rp+1 packed in one dword.
+      // V^T: feature s8+q, keys 2rp and 2rp+1 packed in one dword (byte
+      // selects 0x05040100 = low halves, 0x07060302 = high halves).
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        *reinterpret_cast<uint32_t*>(&sm.vt[0][(s8 + q) * SM::VP + 2 * rp]) =
-            (uint32_t)vh[0].h[q] | ((uint32_t)vh[1].h[q] << 16);
-        if constexpr (SM::PL == 2)
-          *reinterpret_cast<uint32_t*>(&sm.vt[1][(s8 + q) * SM::VP + 2 * rp]) =
-              (uint32_t)vl[0].h[q] | ((uint32_t)vl[1].h[q] << 16);
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<uint32_t*>(&sm.vt[0][(s8 + 2 * j) * SM::VP + 2 * rp]) =
+            __builtin_amdgcn_perm(vh[1].u[j], vh[0].u[j], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.vt[0][(s8 + 2 * j + 1) * SM::VP + 2 * rp]) =
+            __builtin_amdgcn_perm(vh[1].u[j], vh[0].u[j], 0x07060302u);
+        if constexpr (SM::PL == 2) {
+          *reinterpret_cast<uint32_t*>(&sm.vt[1][(s8 + 2 * j) * SM::VP + 2 * rp]) =
+              __builtin_amdgcn_perm(vl[1].u[j], vl[0].u[j], 0x05040100u);
+          *reinterpret_cast<uint32_t*>(&sm.vt[1][(s8 + 2 * j + 1) * SM::VP + 2 * rp]) =
+              __builtin_amdgcn_perm(vl[1].u[j], vl[0].u[j], 0x07060302u);
+        }
       }
     }
   };
