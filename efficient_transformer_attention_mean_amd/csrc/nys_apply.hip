@@ -53,14 +53,17 @@ struct ApplyLayout {
   static constexpr int OP = D + 4;      // Ot row pitch (floats)
   static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
   static constexpr int WP = MPA + 8;    // W^T plane row pitch (bf16)
+  // Operand planes per matrix: bf16 I/O takes single bf16 products with
+  // fp32 accumulation (hi plane only), fp32 I/O the three-product split.
+  static constexpr int NPL = IO::kBf16 ? 1 : 2;
   // The current head's Kt and W^T planes are kept in LDS when they fit
   // (KWL), else read from global memory.
-  static constexpr bool KWL = ATT && (4 * MPA * KP + 4 * D * WP) <= 72 * 1024;
+  static constexpr bool KWL = ATT && 2 * NPL * (MPA * KP + D * WP) <= 72 * 1024;
   static constexpr int OT = 0;
   static constexpr int VT = OT + 4 * kTQ * OP;
   static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
-  static constexpr int WT = KT + (KWL ? 4 * MPA * KP : 0);
-  static constexpr int BYTES = WT + (KWL ? 4 * D * WP : 0);
+  static constexpr int WT = KT + (KWL ? 2 * NPL * MPA * KP : 0);
+  static constexpr int BYTES = WT + (KWL ? 2 * NPL * D * WP : 0);
   // V tile loads: task = 4 rows x one 16-byte chunk.
   static constexpr int FPC = IO::kBf16 ? 8 : 4;  // features per 16-byte chunk
   static constexpr int NCH = D / FPC;
@@ -222,13 +225,13 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
       if constexpr (LY::KWL) {
         const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
                               reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
-        for (int e = tid; e < 2 * MPA * D / 8; e += 256) {
+        for (int e = tid; e < LY::NPL * MPA * D / 8; e += 256) {
           const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
           *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
         }
         const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
                               reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
-        for (int e = tid; e < 2 * D * MPA / 8; e += 256) {
+        for (int e = tid; e < LY::NPL * D * MPA / 8; e += 256) {
           const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
           *reinterpret_cast<uint4*>(wp + (pl * D + r) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
         }
@@ -315,13 +318,12 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           B8 kh, kl;
           const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
           kh.q = *reinterpret_cast<const uint4*>(kth + o);
-          kl.q = *reinterpret_cast<const uint4*>(ktl + o);
+          if constexpr (!IO::kBf16) kl.q = *reinterpret_cast<const uint4*>(ktl + o);
           if (!KFULL && dd >= D) {
             kh.q = make_uint4(0, 0, 0, 0);
             kl.q = make_uint4(0, 0, 0, 0);
           }
           if constexpr (IO::kBf16) {
-            sc[mt] = mfma(kl, qh[kc], sc[mt]);
             sc[mt] = mfma(kh, qh[kc], sc[mt]);
           } else {
             sc[mt] = mfma3(kh, kl, qh[kc], ql[kc], sc[mt]);
@@ -373,15 +375,19 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
             f[i] = sc[2 * kk][i] * inv;
             f[4 + i] = sc[2 * kk + 1][i] * inv;
           }
-          split8(f, fh, fl);
+          if constexpr (IO::kBf16) round8(f, fh); else split8(f, fh, fl);
         }
 #pragma unroll
         for (int nd = 0; nd < ND; ++nd) {
           const int off = (nd * 16 + c) * WPI + kk * 32 + 8 * g;
           B8 wh, wl;
           wh.q = *reinterpret_cast<const uint4*>(wth + off);
-          wl.q = *reinterpret_cast<const uint4*>(wtl + off);
-          o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
+          if constexpr (IO::kBf16) {
+            o[nd] = mfma(wh, fh, o[nd]);
+          } else {
+            wl.q = *reinterpret_cast<const uint4*>(wtl + off);
+            o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
+          }
         }
       }
       // Lane holds O[query 16*wave + c][features nd*16 + 4g .. +3].

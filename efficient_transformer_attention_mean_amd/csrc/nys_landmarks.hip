@@ -738,8 +738,9 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   const float* qt = Qt + (size_t)bh * m * D;
 
   // Landmark-query operands (B of S^T = K Qt^T), pre-multiplied by
-  // log2(e)/sqrt(d) so that scores come out in base-2 units, split hi/lo,
-  // in registers.
+  // log2(e)/sqrt(d) so that scores come out in base-2 units, in registers:
+  // rounded to bf16 for bf16 I/O (single bf16 products, fp32 accumulation),
+  // split hi/lo for fp32 I/O.
   B8 qh[NTW][KC], ql[NTW][KC];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
@@ -752,7 +753,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
         const int dd = kc * 32 + 8 * g + q;
         x[q] = (lm < m && dd < D) ? qt[lm * D + dd] * sl2e : 0.f;
       }
-      split8(x, qh[t][kc], ql[t][kc]);
+      if constexpr (IO::kBf16) round8(x, qh[t][kc]); else split8(x, qh[t][kc], ql[t][kc]);
     }
   }
 
@@ -862,7 +863,6 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
           if constexpr (SM::PL == 2) {
             s[mt] = mfma3(kh, kl, qh[t][kc], ql[t][kc], s[mt]);
           } else {
-            s[mt] = mfma(kh, ql[t][kc], s[mt]);
             s[mt] = mfma(kh, qh[t][kc], s[mt]);
           }
         }
@@ -908,7 +908,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
           p[4 + i] = s[2 * kk + 1][i];
         }
         B8 ph, pl;
-        split8(p, ph, pl);
+        if constexpr (SM::PL == 2) split8(p, ph, pl); else round8(p, ph);
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
           const int dd = md * 16 + c;
@@ -926,7 +926,6 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
             vl.u[3] = *reinterpret_cast<const uint32_t*>(r1 + 18);
             acc[t][md] = mfma3(vh, vl, ph, pl, acc[t][md]);
           } else {
-            acc[t][md] = mfma(vh, pl, acc[t][md]);
             acc[t][md] = mfma(vh, ph, acc[t][md]);
           }
         }

@@ -24,12 +24,18 @@ OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
 #  Z: 4 products per iteration; errors in the directions of small singular
 #     values of A grow by up to 13/4 per step (the slope of the iteration map
 #     at 0), so the bf16x3 gate is looser: 1e-5 x cond-driven growth.
-#  BV: bf16 probabilities x exact bf16 V (or split fp32) with fp32 accumulation.
+#  BV: fp32 I/O: split-fp32 products (~1e-6).  bf16 I/O: single bf16
+#     products with fp32 accumulation, as in bf16 attention kernels: every
+#     probability is rounded to bf16 (relative error <= 2^-9, RMS
+#     2^-9/sqrt(3) ~ 1.1e-3), and the weighted average of V keeps that
+#     relative size (measured 1.3e-3 .. 2.0e-3), gated at 5e-3.
 #  W = Z BV: sums with cancellation (|Z| entries up to ~300 when A is
-#     ill-conditioned), so it inherits Z's error times that growth.
+#     ill-conditioned), so it inherits BV's and Z's errors times that growth
+#     (bf16 I/O measured up to 6e-3 at the stress shape; gated at the output
+#     bar, 2e-2).
 INTER_TOL = {
     "f32": {"Qt": 1e-6, "Kt": 1e-6, "A": 1e-5, "Z": 5e-5, "BV": 5e-5, "W": 2e-3},
-    "bf16": {"Qt": 1e-6, "Kt": 1e-6, "A": 1e-5, "Z": 5e-3, "BV": 5e-5, "W": 2e-3},
+    "bf16": {"Qt": 1e-6, "Kt": 1e-6, "A": 1e-5, "Z": 5e-3, "BV": 5e-3, "W": 2e-2},
 }
 
 _cache = {}
