@@ -16,6 +16,7 @@ int check_shape(int batch, int heads, int n, int d, int m, int iters) {
   if (batch < 1 || heads < 1 || n < 1 || d < 1 || m < 1 || iters < 0) return NYS_EINVAL;
   if (m > n || n % m != 0) return NYS_EINVAL;
   if (!supported_d(d) || m > 256 || n > (1 << 24)) return NYS_EUNSUPPORTED;
+  if ((long long)n * d >= (1LL << 29)) return NYS_EUNSUPPORTED;  // one head's rows as fp32 stay under 2 GiB
   if ((long long)batch * heads > 65535) return NYS_EUNSUPPORTED;  // batch*heads is a grid dimension
   if ((long long)batch * heads * (long long)n * d > (1LL << 40)) return NYS_EUNSUPPORTED;
   return NYS_OK;
@@ -101,6 +102,7 @@ int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int head
     if (conv_k < 1 || conv_k % 2 == 0) return NYS_EINVAL;
     if (batch < 1 || heads < 1 || n < 1 || d < 1) return NYS_EINVAL;
     if (!supported_d(d) || n > (1 << 24) || (long long)batch * heads > 65535) return NYS_EUNSUPPORTED;
+    if ((long long)n * d >= (1LL << 29)) return NYS_EUNSUPPORTED;
     hipError_t e = nys::launch_dconv(V, conv_w, out, batch, heads, n, d, conv_k, dtype == NYS_BF16,
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NYS_OK : NYS_EHIP;

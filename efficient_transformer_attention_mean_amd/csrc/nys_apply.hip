@@ -39,6 +39,32 @@ typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 constexpr int kTQ = 64;     // rows per tile: 4 waves x 16 queries
 constexpr int kConvNS = 9;  // 4-tap steps of the matrix-core skip (33 taps)
 
+// Buffer resource over the rows of one head: 32-bit byte offsets, range
+// checked by the hardware (loads at offsets >= `bytes` return zero, stores
+// there are dropped; a negative offset reads as a huge unsigned one).  The
+// third word sets a 32-bit data format, under which untyped dword accesses
+// are range checked.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (unsigned)off, 0, 0));
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (unsigned)off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (unsigned)off, 0, 0);
+}
+
 // Shared-memory layout (bytes) of one block.
 // KW: 0 = no skip, 1 = one tap, 33 = up to 33 taps (zero-padded, centred),
 //     -1 = wider filters (taps and rows read from global memory; slow path).
@@ -48,7 +74,7 @@ struct ApplyLayout {
   static constexpr int MPA = 16 * NTM;
   static constexpr int HALO = KW == 33 ? 16 : 0;
   static constexpr int VCOLS = kTQ + 2 * HALO;
-  static constexpr bool STAGE = KW == 1 || KW == 33;
+  static constexpr bool STAGE = KW == 1 || KW == 33;  // V rows staged in LDS; the skip goes through Ot
   static constexpr int VP = VCOLS + 4;  // Vt row pitch (elements; 8/16-byte aligned rows)
   static constexpr int OP = D + 4;      // Ot row pitch (floats)
   static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
@@ -60,10 +86,10 @@ struct ApplyLayout {
   // (KWL), else read from global memory.
   static constexpr bool KWL = ATT && 2 * NPL * (MPA * KP + D * WP) <= 72 * 1024;
   static constexpr int OT = 0;
-  static constexpr int VT = OT + 4 * kTQ * OP;
+  static constexpr int VT = OT + (STAGE ? 4 * kTQ * OP : 0);
   static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
   static constexpr int WT = KT + (KWL ? 2 * NPL * MPA * KP : 0);
-  static constexpr int BYTES = WT + (KWL ? 2 * NPL * D * WP : 0);
+  static constexpr int BYTES = WT + (KWL ? 2 * NPL * D * WP : 0) + 16;
   // V tile loads: task = 4 rows x one 16-byte chunk.
   static constexpr int FPC = IO::kBf16 ? 8 : 4;  // features per 16-byte chunk
   static constexpr int NCH = D / FPC;
@@ -72,60 +98,60 @@ struct ApplyLayout {
   static constexpr int QW = IO::kBf16 ? 1 : 2;  // 16-byte words per 8 head-dim elements
 };
 
-// Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) into registers.
-// Every load is unconditional (row and task clamped in range, so the
-// compiler keeps exact counts of loads in flight); rows outside [0, n) are
-// zeroed when staged (v_row_ok).
-template <typename LY, typename T>
-__device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], const T* __restrict__ Vh, int t0, int n) {
+// Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) of one head into
+// registers; rows outside the head read as zero (buffer range check).  Every
+// load is unconditional, so the compiler keeps exact counts of loads in flight.
+template <typename LY>
+__device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], __amdgpu_buffer_rsrc_t rs, int t0) {
   constexpr int D = LY::NCH * LY::FPC;
+  constexpr int ES = 16 / LY::FPC;
 #pragma unroll
   for (int k = 0; k < LY::NTK; ++k) {
     const int e = min((int)threadIdx.x + 256 * k, LY::TASKS - 1);
     const int rq = e / LY::NCH, oc = e % LY::NCH;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int row = min(max(t0 - LY::HALO + 4 * rq + q, 0), n - 1);
-      vr[k][q] = *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + LY::FPC * oc);
+      // Each row's offset stays in the address register: the range check
+      // then sees the row itself (a row past the end inside a group of four
+      // must not be reached through the instruction's immediate offset).
+      int off = ((t0 - LY::HALO + 4 * rq + q) * D + LY::FPC * oc) * ES;
+      asm volatile("" : "+v"(off));
+      vr[k][q] = buf_load16(rs, off);
     }
   }
 }
 
-template <typename LY>
-__device__ __forceinline__ bool v_row_ok(int t0, int n, int rq, int q) {
-  const int row = t0 - LY::HALO + 4 * rq + q;
-  return row >= 0 && row < n;
-}
-
 // Issues the loads of this lane's query fragments (row qrow, head-dim
-// elements 32kc + 8g .. +7 for every chunk kc), clamped in range; q_ok tells
-// which are real.
-template <typename LY, int D, typename T>
-__device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], const T* __restrict__ Qh, int qrow, int n) {
+// elements 32kc + 8g .. +7 for every chunk kc); rows past the end read as zero.
+template <typename LY, int D>
+__device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amdgpu_buffer_rsrc_t rs, int qrow) {
+  constexpr int ES = 16 / LY::FPC;
   const int g = (threadIdx.x & 63) >> 4;
-  const int r = min(qrow, n - 1);
 #pragma unroll
   for (int kc = 0; kc < (D + 31) / 32; ++kc) {
     const int dd = min(kc * 32 + 8 * g, D - 8);
 #pragma unroll
-    for (int w = 0; w < LY::QW; ++w) qr[kc][w] = *reinterpret_cast<const uint4*>(Qh + (size_t)r * D + dd + 4 * w);
+    for (int w = 0; w < LY::QW; ++w) qr[kc][w] = buf_load16(rs, (qrow * D + dd) * ES + 16 * w);
   }
-}
-
-template <int D>
-__device__ __forceinline__ bool q_ok(int qrow, int n, int kc) {
-  const int g = (threadIdx.x & 63) >> 4;
-  return qrow < n && (D % 32 == 0 || kc * 32 + 8 * g < D);
 }
 
 }  // namespace
 
 // Persistent blocks: block `rank` (XCD-contiguous numbering) processes the
 // run of 64-row tiles [rank * total / G, (rank + 1) * total / G) of the
-// (batch*head)-major tile list; the V rows and Q fragments of the next two
-// tiles are in flight while the current tile is computed.
-template <typename IO, int D, int NTM, int KW, bool ATT>
-__global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict__ Qin,
+// (batch*head)-major tile list.  Per tile, between two barriers:
+//   region 1 (after the first barrier): the skip of the tile from the
+//     feature-major V rows in LDS -> Ot (fp32, row-major), and, independent
+//     of it, each wave's attention for its 16 queries into registers, so the
+//     two interleave;
+//   region 2 (after the second barrier): each lane adds its Ot values to its
+//     attention values and stores them; then the next tile's V rows (loaded
+//     two tiles ahead) go to LDS and the loads for the tile after next are
+//     issued.
+// The Q fragments of a tile are likewise loaded two tiles ahead.
+// WPE: waves per SIMD the register allocation is held to (1 = no limit).
+template <typename IO, int D, int NTM, int KW, bool ATT, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
                                                const uint16_t* __restrict__ kt_hi,
                                                const uint16_t* __restrict__ kt_lo,
@@ -138,16 +164,19 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
   constexpr int KC = (D + 31) / 32;  // 32-wide chunks of the head dimension
   constexpr int ND = D / 16;         // 16-feature tiles
+  constexpr int FPG = D / 4;         // output features per lane (lane group g owns [g FPG, (g+1) FPG))
   constexpr bool KFULL = D % 32 == 0;
+  constexpr int ES = sizeof(T);
   constexpr int MPA = LY::MPA, VP = LY::VP, OP = LY::OP, KP = LY::KP, WP = LY::WP;
   constexpr int NCH = LY::NCH, TASKS = LY::TASKS, NTK = LY::NTK;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* ot = reinterpret_cast<float*>(smem_raw + LY::OT);
   T* vt = reinterpret_cast<T*>(smem_raw + LY::VT);
-  uint16_t* kp = reinterpret_cast<uint16_t*>(smem_raw + LY::KT);  // [hi, lo][MPA][KP]
-  uint16_t* wp = reinterpret_cast<uint16_t*>(smem_raw + LY::WT);  // [hi, lo][D][WP]
+  uint16_t* kp = reinterpret_cast<uint16_t*>(smem_raw + LY::KT);  // [hi (, lo)][MPA][KP]
+  uint16_t* wp = reinterpret_cast<uint16_t*>(smem_raw + LY::WT);  // [hi (, lo)][D][WP]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int head_bytes = n * D * ES;
 
   // Run of tiles of this block.
   const long long G = gridDim.x, L = blockIdx.x;
@@ -192,8 +221,7 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
     }
   };
 
-  // Two register sets of tile inputs: tile t is computed while the loads of
-  // tiles t + 1 and t + 2 are in flight.
+  // Two register sets of tile inputs, each two tiles ahead of its use.
   uint4 vra[NTK][4], vrb[NTK][4];
   uint4 qra[KC][LY::QW], qrb[KC][LY::QW];
   // Tile positions: (batch*head, tile within the head), stepped without division.
@@ -209,53 +237,30 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
   };
   const Pos pfirst{(int)(tbeg / ntile), (int)(tbeg % ntile)};
   const Pos plast{(int)((tend - 1) / ntile), (int)((tend - 1) % ntile)};
-  auto issue = [&](Pos q, uint4 (&vr)[NTK][4], uint4 (&qr)[KC][LY::QW]) {
-    const int t0 = q.ti * kTQ;
-    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)q.bh * n * D, t0, n);
-    if constexpr (ATT) load_q<LY, D>(qr, Qin + (size_t)q.bh * n * D, t0 + 16 * wave + c, n);
+  const int count = (int)(tend - tbeg);  // tiles of this block
+  // Position of the block's tile i + k, or its last tile past the end (loads
+  // stay unconditional).  Positions are wave-uniform; readfirstlane says so
+  // to the compiler, so buffer descriptors built from them stay scalar.
+  auto ahead = [&](int i, Pos q, int k) {
+    if (i + k >= count) return plast;
+    for (int j = 0; j < k; ++j) q = step(q);
+    return Pos{__builtin_amdgcn_readfirstlane(q.bh), __builtin_amdgcn_readfirstlane(q.ti)};
   };
-  issue(pfirst, vra, qra);
-  issue(tbeg + 1 < tend ? step(pfirst) : pfirst, vrb, qrb);
-  int cur = -1;
-  auto tile = [&](long long t, Pos pos, uint4 (&vr)[NTK][4], uint4 (&qr)[KC][LY::QW]) {
-    const int bh = pos.bh, t0 = pos.ti * kTQ, h = bh % heads;
-    if (bh != cur) {
-      // New head: its Kt / W^T planes -> LDS (the previous tile's readers
-      // are past the barrier that follows the attention), filter operands.
-      if constexpr (LY::KWL) {
-        const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
-                              reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
-        for (int e = tid; e < LY::NPL * MPA * D / 8; e += 256) {
-          const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
-          *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
-        }
-        const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
-                              reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
-        for (int e = tid; e < LY::NPL * D * MPA / 8; e += 256) {
-          const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
-          *reinterpret_cast<uint4*>(wp + (pl * D + r) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
-        }
-      }
-      if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
-      cur = bh;
-      // Rare path: settle its loads here so that the counts of the tile loads
-      // in flight stay exact past the merge.
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    }
-    __syncthreads();  // previous tile's skip and store are done; planes visible
+  auto issue_v = [&](Pos q, uint4 (&vr)[NTK][4]) {
+    if constexpr (LY::STAGE) load_v<LY>(vr, head_rsrc(Vin + (size_t)q.bh * n * D, head_bytes), q.ti * kTQ);
+  };
+  auto issue_q = [&](Pos q, uint4 (&qr)[KC][LY::QW]) {
+    if constexpr (ATT) load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, head_bytes), q.ti * kTQ + 16 * wave + c);
+  };
 
-    // V rows -> Vt (feature-major); then the next tile's V rows are loaded.
+  // V rows (registers) -> Vt[feature][row].
+  auto stage = [&](uint4 (&vr)[NTK][4]) {
     if constexpr (LY::STAGE) {
 #pragma unroll
       for (int k = 0; k < NTK; ++k) {
         const int e = tid + 256 * k;
         if (e >= TASKS) continue;
         const int rq = e / NCH, oc = e % NCH;
-        if (!(t0 - LY::HALO >= 0 && t0 + kTQ + LY::HALO <= n)) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (!v_row_ok<LY>(t0, n, rq, q)) vr[k][q] = make_uint4(0, 0, 0, 0);
-        }
         if constexpr (IO::kBf16) {
           const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[k][0]);
           const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[k][1]);
@@ -282,127 +287,16 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
         }
       }
     }
-    // Tile t + 2 (or the last one again near the end: loads stay unconditional).
-    const Pos pn = t + 2 < tend ? step(step(pos)) : plast;
-    const int nbh = pn.bh, nt0 = pn.ti * kTQ;
-    if constexpr (LY::STAGE) load_v<LY>(vr, Vin + (size_t)nbh * n * D, nt0, n);
+  };
 
-    // Attention for this wave's 16 queries -> Ot; or zeros.
-    if constexpr (ATT) {
-      B8 qh[KC], ql[KC];
-      const bool qtail = t0 + kTQ > n || !KFULL;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const bool ok = !qtail || q_ok<D>(t0 + 16 * wave + c, n, kc);
-        if constexpr (IO::kBf16) {
-          qh[kc].q = ok ? qr[kc][0] : make_uint4(0, 0, 0, 0);
-        } else {
-          const float4 a = __builtin_bit_cast(float4, qr[kc][0]), b = __builtin_bit_cast(float4, qr[kc][LY::QW - 1]);
-          float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
-          split8(x, qh[kc], ql[kc]);
-        }
-      }
-      // S^T (landmarks x queries) = Kt Q^T from the Kt planes.
-      const uint16_t* kth = LY::KWL ? kp : kt_hi + (size_t)bh * MPA * D;
-      const uint16_t* ktl = LY::KWL ? kp + MPA * KP : kt_lo + (size_t)bh * MPA * D;
-      constexpr int KPI = LY::KWL ? KP : D;
-      f32x4_t sc[NTM];
-#pragma unroll
-      for (int mt = 0; mt < NTM; ++mt) {
-        sc[mt] = zero4();
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const int dd = kc * 32 + 8 * g;
-          B8 kh, kl;
-          const int o = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
-          kh.q = *reinterpret_cast<const uint4*>(kth + o);
-          if constexpr (!IO::kBf16) kl.q = *reinterpret_cast<const uint4*>(ktl + o);
-          if (!KFULL && dd >= D) {
-            kh.q = make_uint4(0, 0, 0, 0);
-            kl.q = make_uint4(0, 0, 0, 0);
-          }
-          if constexpr (IO::kBf16) {
-            sc[mt] = mfma(kh, qh[kc], sc[mt]);
-          } else {
-            sc[mt] = mfma3(kh, kl, qh[kc], ql[kc], sc[mt]);
-          }
-        }
-      }
-      load_q<LY, D>(qr, Qin + (size_t)nbh * n * D, nt0 + 16 * wave + c, n);
-      // Softmax over landmarks (lane's query = c; landmark = mt*16 + 4g + i).
-      // Scores are already in base-2 units (the Kt planes carry log2(e)/sqrt(d)).
-      if (m < MPA) {
-#pragma unroll
-        for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (mt * 16 + 4 * g + i >= m) sc[mt][i] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[mt][i]);
-      mx = max_over_groups(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < NTM; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[mt][i] = __builtin_amdgcn_exp2f(sc[mt][i] - mx);  // arguments <= 0; exp2(-inf) = 0
-          sum += sc[mt][i];
-        }
-      const float inv = __builtin_amdgcn_rcpf(sum_over_groups(sum));  // sum >= 1 (the max term is 1)
-
-      // O^T (features x queries) = W^T F^T.  The W^T planes hold each
-      // 32-landmark chunk in the order {4g..4g+3, 16+4g..16+4g+3}, the order
-      // this lane holds its query's probabilities in.
-      const uint16_t* wth = LY::KWL ? wp : wt_hi + (size_t)bh * D * MPA;
-      const uint16_t* wtl = LY::KWL ? wp + D * WP : wt_lo + (size_t)bh * D * MPA;
-      constexpr int WPI = LY::KWL ? WP : MPA;
-      f32x4_t o[ND];
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < NTM / 2; ++kk) {
-        B8 fh, fl;
-        {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[i] = sc[2 * kk][i] * inv;
-            f[4 + i] = sc[2 * kk + 1][i] * inv;
-          }
-          if constexpr (IO::kBf16) round8(f, fh); else split8(f, fh, fl);
-        }
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const int off = (nd * 16 + c) * WPI + kk * 32 + 8 * g;
-          B8 wh, wl;
-          wh.q = *reinterpret_cast<const uint4*>(wth + off);
-          if constexpr (IO::kBf16) {
-            o[nd] = mfma(wh, fh, o[nd]);
-          } else {
-            wl.q = *reinterpret_cast<const uint4*>(wtl + off);
-            o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
-          }
-        }
-      }
-      // Lane holds O[query 16*wave + c][features nd*16 + 4g .. +3].
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd)
-        *reinterpret_cast<float4*>(&ot[(16 * wave + c) * OP + nd * 16 + 4 * g]) =
-            make_float4(o[nd][0], o[nd][1], o[nd][2], o[nd][3]);
-    } else {
-      for (int e = tid; e < kTQ * OP / 4; e += 256)
-        *reinterpret_cast<float4*>(&ot[4 * e]) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-
-    // The skip, added into Ot.
+  // The skip of the staged tile -> Ot (plain stores).
+  auto skip = [&](int h) {
     if constexpr (MMCONV) {
+      // bf16: on the matrix cores with the 16-block 4x4x4 instruction, one
+      // block per feature: A = a 4 x 4 band of that feature's taps
+      // (Toeplitz), B = 4 consecutive V rows; 9 steps of 4 taps cover 33 taps
+      // for 16 output rows, and each lane ends with 4 consecutive rows of
+      // one feature.  hi and lo tap planes accumulate separately.
       const int b = lane >> 2, q4 = lane & 3;
 #pragma unroll
       for (int seg = 0; seg < NSEG; ++seg) {
@@ -428,7 +322,7 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
           // Lane (b, q4) holds rows (rb0 + r)*16 + 4*q4 + i of feature f.
           float* dst = &ot[((rb0 + r) * 16 + 4 * q4) * OP + f];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i * OP] += acc[i];
+          for (int i = 0; i < 4; ++i) dst[i * OP] = acc[i];
         }
       }
     } else if constexpr (KW == 33 || KW == 1) {
@@ -449,11 +343,7 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
       }
       float a0[RPT], a1[RPT];
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const float2 x = *reinterpret_cast<const float2*>(&ot[(r0 + r) * OP + 2 * fp]);
-        a0[r] = x.x;
-        a1[r] = x.y;
-      }
+      for (int r = 0; r < RPT; ++r) a0[r] = a1[r] = 0.f;
       const T* v0p = &vt[(2 * fp) * VP + r0];
       const T* v1p = &vt[(2 * fp + 1) * VP + r0];
       // Output row r0 + r reads Vt columns r0 + r + tt (tt = 0 .. NT-1).
@@ -479,55 +369,234 @@ __global__ __launch_bounds__(256) void k_apply(const typename IO::T* __restrict_
 #pragma unroll
       for (int r = 0; r < RPT; ++r) *reinterpret_cast<float2*>(&ot[(r0 + r) * OP + 2 * fp]) = make_float2(a0[r], a1[r]);
     }
-    if constexpr (KW == 33 || KW == 1) __syncthreads();
+  };
 
-    // Ot -> output rows: 16 bytes (8 bf16 or 4 fp32 features) per lane.
-    constexpr int FPL = IO::kBf16 ? 8 : 4;  // features per lane
-    constexpr int GPR = D / FPL;            // lanes per row
-    const T* Vh = Vin + (size_t)bh * n * D;
-    T* oh = out + (size_t)bh * n * D;
-    for (int e = tid; e < kTQ * GPR; e += 256) {
-      const int p = e / GPR, fc = (e % GPR) * FPL;
-      const int row = t0 + p;
-      if (row >= n) continue;
-      float v[FPL];
+  // Attention of this wave's 16 queries: lane (c, g) ends with query
+  // 16*wave + c, features g*FPG + 4*nd + i in o[nd][i].  Issues the Q loads
+  // of tile `pq` once its own fragments are consumed.
+  auto attention = [&](int bh, int t0, Pos pq, uint4 (&qr)[KC][LY::QW], f32x4_t (&o)[ND]) {
+    B8 qh[KC], ql[KC];
 #pragma unroll
-      for (int q = 0; q < FPL; q += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(&ot[p * OP + fc + q]);
-        v[q] = x.x;
-        v[q + 1] = x.y;
-        v[q + 2] = x.z;
-        v[q + 3] = x.w;
+    for (int kc = 0; kc < KC; ++kc) {
+      const bool ok = KFULL || kc * 32 + 8 * g < D;
+      if constexpr (IO::kBf16) {
+        qh[kc].q = ok ? qr[kc][0] : make_uint4(0, 0, 0, 0);
+      } else {
+        const float4 a = __builtin_bit_cast(float4, qr[kc][0]), b = __builtin_bit_cast(float4, qr[kc][LY::QW - 1]);
+        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
+        split8(x, qh[kc], ql[kc]);
       }
-      if constexpr (KW == -1) {
-        const int R = (conv_k - 1) / 2;
-        const int tb = max(0, R - row), te = min(conv_k, n - row + R);
+    }
+    // S^T (landmarks x queries) = Kt Q^T from the Kt planes.
+    const uint16_t* kth = LY::KWL ? kp : kt_hi + (size_t)bh * MPA * D;
+    const uint16_t* ktl = LY::KWL ? kp + MPA * KP : kt_lo + (size_t)bh * MPA * D;
+    constexpr int KPI = LY::KWL ? KP : D;
+    f32x4_t sc[NTM];
 #pragma unroll
-        for (int q = 0; q < FPL; ++q) {
-          const float* wq = conv_w + ((size_t)h * D + fc + q) * conv_k;
-          for (int tt = tb; tt < te; ++tt)
-            v[q] = fmaf(wq[tt], load_elem<IO>(Vh + (size_t)(row + tt - R) * D + fc + q), v[q]);
+    for (int mt = 0; mt < NTM; ++mt) {
+      sc[mt] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int dd = kc * 32 + 8 * g;
+        B8 kh, kl;
+        const int o_ = (mt * 16 + c) * KPI + (KFULL ? dd : min(dd, D - 8));
+        kh.q = *reinterpret_cast<const uint4*>(kth + o_);
+        if constexpr (!IO::kBf16) kl.q = *reinterpret_cast<const uint4*>(ktl + o_);
+        if (!KFULL && dd >= D) {
+          kh.q = make_uint4(0, 0, 0, 0);
+          kl.q = make_uint4(0, 0, 0, 0);
+        }
+        if constexpr (IO::kBf16) {
+          sc[mt] = mfma(kh, qh[kc], sc[mt]);
+        } else {
+          sc[mt] = mfma3(kh, kl, qh[kc], ql[kc], sc[mt]);
         }
       }
-      if constexpr (IO::kBf16) {
-        B8 o8;
+    }
+    issue_q(pq, qr);
+    // Softmax over landmarks (lane's query = c; landmark = mt*16 + 4g + i).
+    // Scores are already in base-2 units (the Kt planes carry log2(e)/sqrt(d)).
+    if (m < MPA) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o8.h[q] = f32_to_bf16(v[q]);
-        *reinterpret_cast<uint4*>(oh + (size_t)row * D + fc) = o8.q;
-      } else {
-        *reinterpret_cast<float4*>(oh + (size_t)row * D + fc) = make_float4(v[0], v[1], v[2], v[3]);
+      for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (mt * 16 + 4 * g + i >= m) sc[mt][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[mt][i]);
+    mx = max_over_groups(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NTM; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[mt][i] = __builtin_amdgcn_exp2f(sc[mt][i] - mx);  // arguments <= 0; exp2(-inf) = 0
+        sum += sc[mt][i];
+      }
+    const float inv = __builtin_amdgcn_rcpf(sum_over_groups(sum));  // sum >= 1 (the max term is 1)
+
+    // O^T (features x queries) = W^T F^T.  The W^T planes hold each
+    // 32-landmark chunk in the order {4g..4g+3, 16+4g..16+4g+3}, the order
+    // this lane holds its query's probabilities in.  Row c of tile nd is
+    // feature (c/4)*FPG + 4nd + c%4, so that a lane's output features are
+    // contiguous.
+    const uint16_t* wth = LY::KWL ? wp : wt_hi + (size_t)bh * D * MPA;
+    const uint16_t* wtl = LY::KWL ? wp + D * WP : wt_lo + (size_t)bh * D * MPA;
+    constexpr int WPI = LY::KWL ? WP : MPA;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NTM / 2; ++kk) {
+      B8 fh, fl;
+      {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = sc[2 * kk][i] * inv;
+          f[4 + i] = sc[2 * kk + 1][i] * inv;
+        }
+        if constexpr (IO::kBf16) round8(f, fh); else split8(f, fh, fl);
+      }
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const int frow = (c >> 2) * FPG + 4 * nd + (c & 3);
+        const int off = frow * WPI + kk * 32 + 8 * g;
+        B8 wh, wl;
+        wh.q = *reinterpret_cast<const uint4*>(wth + off);
+        if constexpr (IO::kBf16) {
+          o[nd] = mfma(wh, fh, o[nd]);
+        } else {
+          wl.q = *reinterpret_cast<const uint4*>(wtl + off);
+          o[nd] = mfma3(wh, wl, fh, fl, o[nd]);
+        }
       }
     }
   };
-  long long t = tbeg;
+
+  // Attention + Ot (+ wide-filter skip) -> output row 16*wave + c of the
+  // tile, features g*FPG .. +FPG-1: 16-byte stores (8-byte for bf16 at
+  // d = 16); rows past the end are dropped by the range check.
+  auto epilogue = [&](int bh, int h, int t0, const f32x4_t (&o)[ND]) {
+    const int p = 16 * wave + c, row = t0 + p, f0 = g * FPG;
+    float v[FPG];
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (ATT) v[4 * nd + i] = o[nd][i]; else v[4 * nd + i] = 0.f;
+      }
+    if constexpr (LY::STAGE) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        const float4 x = *reinterpret_cast<const float4*>(&ot[p * OP + f0 + 4 * nd]);
+        v[4 * nd] += x.x;
+        v[4 * nd + 1] += x.y;
+        v[4 * nd + 2] += x.z;
+        v[4 * nd + 3] += x.w;
+      }
+    }
+    if constexpr (KW == -1) {
+      if (row < n) {
+        const T* Vh = Vin + (size_t)bh * n * D;
+        const int R = (conv_k - 1) / 2;
+        const int tb = max(0, R - row), te = min(conv_k, n - row + R);
+        for (int q = 0; q < FPG; ++q) {
+          const float* wq = conv_w + ((size_t)h * D + f0 + q) * conv_k;
+          float s = 0.f;
+          for (int tt = tb; tt < te; ++tt) s = fmaf(wq[tt], load_elem<IO>(Vh + (size_t)(row + tt - R) * D + f0 + q), s);
+          v[q] += s;
+        }
+      }
+    }
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, head_bytes);
+    const int base = (row * D + f0) * ES;
+    if constexpr (IO::kBf16) {
+      if constexpr (FPG >= 8) {
+#pragma unroll
+        for (int j = 0; j < FPG / 8; ++j) {
+          B8 o8;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) o8.h[q] = f32_to_bf16(v[8 * j + q]);
+          buf_store16(ro, base + 16 * j, o8.q);
+        }
+      } else {
+        B8 o8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o8.h[q] = f32_to_bf16(v[q]);
+        buf_store8(ro, base, make_uint2(o8.u[0], o8.u[1]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FPG / 4; ++j)
+        buf_store16(ro, base + 16 * j,
+                    __builtin_bit_cast(uint4, make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3])));
+    }
+  };
+
+  int cur = -1;
+  // Tile t at `pos`: Q fragments in qr (two tiles ahead); vn holds the V rows
+  // of tile t + 1, staged at the end, then refilled with tile t + 3's.
+  auto tile = [&](int t, Pos pos, uint4 (&qr)[KC][LY::QW], uint4 (&vn)[NTK][4]) {
+    const int bh = pos.bh, t0 = pos.ti * kTQ, h = bh % heads;
+    if (bh != cur) {
+      // New head: its Kt / W^T planes -> LDS (the previous tile's readers
+      // are past its second barrier), filter operands.
+      if constexpr (LY::KWL) {
+        const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
+                              reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
+        for (int e = tid; e < LY::NPL * MPA * D / 8; e += 256) {
+          const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
+          *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
+        }
+        const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
+                              reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
+        for (int e = tid; e < LY::NPL * D * MPA / 8; e += 256) {
+          const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
+          *reinterpret_cast<uint4*>(wp + (pl * D + r) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
+        }
+      }
+      if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
+      cur = bh;
+      // Rare path: settle its loads here so that the counts of the tile loads
+      // in flight stay exact past the merge.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();  // Vt of this tile and the planes visible; the previous epilogue's Ot reads done
+
+    skip(h);
+    f32x4_t o[ND];
+    if constexpr (ATT) attention(bh, t0, ahead(t, pos, 2), qr, o);
+    __syncthreads();  // Ot visible; the skip's Vt reads and the attention's plane reads done
+
+    epilogue(bh, h, t0, o);
+    if constexpr (LY::STAGE) {
+      stage(vn);
+      issue_v(ahead(t, pos, 3), vn);
+    }
+  };
+
+  issue_v(pfirst, vra);
+  issue_q(pfirst, qra);
+  const Pos p1 = ahead(0, pfirst, 1);
+  issue_v(p1, vrb);
+  issue_q(p1, qrb);
+  stage(vra);
+  issue_v(ahead(0, pfirst, 2), vra);
+  int t = 0;
   Pos pos = pfirst;
-  for (; t + 1 < tend; t += 2) {
-    tile(t, pos, vra, qra);
+  for (; t + 1 < count; t += 2) {
+    tile(t, pos, qra, vrb);
     pos = step(pos);
-    tile(t + 1, pos, vrb, qrb);
+    tile(t + 1, pos, qrb, vra);
     pos = step(pos);
   }
-  if (t < tend) tile(t, pos, vra, qra);
+  if (t < count) tile(t, pos, qra, vrb);
 }
 
 // ---------------------------------------------------------------------------
@@ -551,7 +620,11 @@ template <typename IO, int D, int NTM, int KW, bool ATT>
 static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
-  auto kern = &k_apply<IO, D, NTM, KW, ATT>;
+  // bf16 with the matrix-core skip at d <= 64, m <= 64 fits three blocks per
+  // CU (LDS ~48 KB) when the registers are held to 168 per lane, without
+  // spills; other instantiations keep the compiler's choice.
+  constexpr int WPE = (IO::kBf16 && KW == 33 && ATT && D <= 64 && NTM <= 4) ? 3 : 1;
+  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
   if (attr != hipSuccess) return attr;

@@ -51,7 +51,9 @@ enum {
                             unknown dtype */
   NYS_EUNSUPPORTED = -2, /* valid but outside what the kernels handle:
                             d not in {16, 32, 64, 128}, m > 256, n > 2^24,
-                            batch * heads > 65535 */
+                            n * d >= 2^29 (one head's rows as fp32 reach
+                            2 GiB: the kernels use 32-bit byte offsets
+                            within a head), batch * heads > 65535 */
   NYS_EWORKSPACE = -3,   /* caller workspace smaller than nystrom_attn_workspace_bytes() */
   NYS_EHIP = -4,         /* a HIP runtime call or launch failed */
   NYS_ENOTIMPL = -5

@@ -95,6 +95,7 @@ FAKE = 0x10000  # never dereferenced: every case below is rejected on the host
     (dict(d=48), _lib.NYS_EUNSUPPORTED),
     (dict(d=256), _lib.NYS_EUNSUPPORTED),
     (dict(m=512, n=1024), _lib.NYS_EUNSUPPORTED),
+    (dict(n=1 << 22, d=128, m=64), _lib.NYS_EUNSUPPORTED),
     (dict(workspace=FAKE, workspace_bytes=16), _lib.NYS_EWORKSPACE),
 ])
 def test_fwd_rejects_bad_arguments_before_launch(lib, kw, code):
@@ -111,6 +112,7 @@ def test_fwd_rejects_bad_arguments_before_launch(lib, kw, code):
     (dict(dtype=5), _lib.NYS_EINVAL),
     (dict(n=0), _lib.NYS_EINVAL),
     (dict(d=24), _lib.NYS_EUNSUPPORTED),
+    (dict(n=1 << 22, d=128), _lib.NYS_EUNSUPPORTED),
 ])
 def test_dconv_rejects_bad_arguments_before_launch(lib, kw, code):
     args = dict(V=FAKE, conv_w=FAKE, n=64, d=16, heads=1, batch=1, conv_k=3, dtype=_lib.NYS_F32, out=FAKE,

@@ -99,6 +99,8 @@ EDGE = [
     (1, 2, 256, 128, 64, 6, 33, "f32"),   # d = 128
     (1, 2, 256, 32, 64, 6, 33, "bf16"),   # d = 32
     (1, 1, 4096, 64, 64, 6, 33, "f32"),   # many key chunks in fp32
+    (2, 2, 222, 64, 6, 6, 33, "bf16"),    # n = 2 mod 4: the last group of 4 staged rows crosses the head's end
+    (1, 3, 134, 32, 2, 6, 33, "f32"),     # the same with fp32 rows
 ]
 
 
