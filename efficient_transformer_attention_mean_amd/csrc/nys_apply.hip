@@ -212,7 +212,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int tt = 4 * st + k - q4 - off;
-          const float wv = (tt >= 0 && tt < conv_k) ? wf[tt] : 0.f;
+          const float wl = wf[min(max(tt, 0), conv_k - 1)];  // clamped: no branch per load
+          const float wv = (tt >= 0 && tt < conv_k) ? wl : 0.f;
           uint16_t hi, lo;
           split_hi_lo(wv, hi, lo);
           ah[st][k] = (short)hi;

@@ -41,14 +41,28 @@ __device__ __forceinline__ void split_hi_lo(float x, uint16_t& hi, uint16_t& lo)
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two values rounded to bf16 (RNE) in one packed conversion: x0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+}
+
+// split_hi_lo for a pair, on packed conversions.
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+}
+
 __device__ __forceinline__ void split8(const float (&x)[8], B8& hi, B8& lo) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) split_hi_lo(x[q], hi.h[q], lo.h[q]);
+  for (int q = 0; q < 4; ++q) split_pair(x[2 * q], x[2 * q + 1], hi.u[q], lo.u[q]);
 }
 
 __device__ __forceinline__ void round8(const float (&x)[8], B8& hi) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) hi.h[q] = f32_to_bf16(x[q]);
+  for (int q = 0; q < 4; ++q) hi.u[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
 }
 
 __device__ __forceinline__ f32x4_t mfma(const B8& a, const B8& b, f32x4_t c) {
@@ -133,6 +147,21 @@ __device__ __forceinline__ void load8f(const typename IO::T* p, float (&x)[8]) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
   }
+}
+
+// x = base[row][col0 .. col0+7] (row pitch ld), zero where row >= rows or
+// col0 >= cols; cols and col0 are multiples of 8.  Both 16-byte loads are
+// issued from clamped, in-bounds addresses without a branch, so the loads of
+// several calls are in flight together.
+__device__ __forceinline__ void load8_masked(const float* __restrict__ base, int row, int rows, int col0, int cols,
+                                             int ld, float (&x)[8]) {
+  const float* src = base + (size_t)min(row, rows - 1) * ld + min(col0, cols - 8);
+  const float4 u0 = *reinterpret_cast<const float4*>(src);
+  const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+  const bool ok = row < rows && col0 < cols;
+  const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+  for (int q = 0; q < 8; ++q) x[q] = ok ? v[q] : 0.f;
 }
 
 // Cross-lane helpers within a wave of 64.

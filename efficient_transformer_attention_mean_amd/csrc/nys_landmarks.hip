@@ -167,12 +167,8 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
     f32x4_t acc = zero4();
     for (int kc = 0; kc < d; kc += 32) {
       float a[8], b[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kk = kc + 8 * g + q;
-        a[q] = (rk < m && kk < d) ? kt[rk * d + kk] : 0.f;
-        b[q] = (rq < m && kk < d) ? qt[rq * d + kk] : 0.f;
-      }
+      load8_masked(kt, rk, m, kc + 8 * g, d, d, a);
+      load8_masked(qt, rq, m, kc + 8 * g, d, d, b);
       acc = mma_f32<PR>(a, b, acc);
     }
     *reinterpret_cast<float4*>(&sm.A[rq][tj * 16 + 4 * g]) =
@@ -574,12 +570,8 @@ __global__ __launch_bounds__(256) void k_landmark_softmax(const float* __restric
     f32x4_t acc = zero4();
     for (int kc = 0; kc < d; kc += 32) {
       float a[8], b[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kk = kc + 8 * g + q;
-        a[q] = (rk < m && kk < d) ? kt[rk * d + kk] : 0.f;
-        b[q] = (rq < m && kk < d) ? qt[rq * d + kk] : 0.f;
-      }
+      load8_masked(kt, rk, m, kc + 8 * g, d, d, a);
+      load8_masked(qt, rq, m, kc + 8 * g, d, d, b);
       acc = mma_f32<PR>(a, b, acc);
     }
     *reinterpret_cast<float4*>(&S[c][tj * 16 + 4 * g]) =
@@ -705,7 +697,10 @@ __global__ __launch_bounds__(256) void k_mm(MMArgs a) {
 template <typename IO, int D>
 struct BvSmem {
   static constexpr int KP = D + 8;   // K row pitch (bf16 elements; rows 16-byte aligned)
-  static constexpr int VP = 64 + 2;  // V^T row pitch: 33 dwords spreads the 2-row writes over all banks
+  // V^T row pitch: 70 elements (35 dwords) keeps both the packed 2-key
+  // staging writes and the P V operand reads (lanes c, g at column 4g of row
+  // c) at most 3 deep in any bank.
+  static constexpr int VP = 64 + 6;
   static constexpr int PL = IO::kBf16 ? 1 : 2;  // planes: bf16 input is exact, fp32 is split hi/lo
   __align__(16) uint16_t k[PL][64 * KP];
   __align__(16) uint16_t vt[PL][D * VP];
@@ -748,11 +743,9 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       float x[8];
+      load8_masked(qt, lm, m, kc * 32 + 8 * g, D, D, x);  // branch-free: all loads in flight together
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int dd = kc * 32 + 8 * g + q;
-        x[q] = (lm < m && dd < D) ? qt[lm * D + dd] * sl2e : 0.f;
-      }
+      for (int q = 0; q < 8; ++q) x[q] *= sl2e;
       if constexpr (IO::kBf16) round8(x, qh[t][kc]); else split8(x, qh[t][kc], ql[t][kc]);
     }
   }
@@ -965,7 +958,8 @@ __device__ __forceinline__ void conv_operand(const float* __restrict__ conv_w, u
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int tt = 4 * st + k - i - off;
-    const float w = (tt >= 0 && tt < conv_k) ? conv_w[(size_t)hf * conv_k + tt] : 0.f;
+    const float wl = conv_w[(size_t)hf * conv_k + min(max(tt, 0), conv_k - 1)];  // clamped: no branch per load
+    const float w = (tt >= 0 && tt < conv_k) ? wl : 0.f;
     split_hi_lo(w, hl.h[k], hl.h[4 + k]);
   }
   ops[idx] = hl.q;
