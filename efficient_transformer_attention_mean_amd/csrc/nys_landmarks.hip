@@ -1016,12 +1016,15 @@ __global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
 // Finish of the split-n pass, one block per (16-feature slice, head):
 //   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
 //   (M_j = max_c pmax_c[j]; chunks in fixed order), then W = Z BV for the
-//   slice in fp32, then the slice's rows of the W^T bf16 planes [bh][D][mpa],
-//   the A operand of the output stage: within each chunk of 32 landmarks,
-//   position 8g + q holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4),
-//   the order in which that stage's softmax lanes hold their landmarks;
-//   padding is zero.  grid (D/16, batch*heads).
-template <bool ZLDS>
+//   slice, then the slice's rows of the W^T bf16 planes [bh][D][mpa], the A
+//   operand of the output stage: within each chunk of 32 landmarks, position
+//   8g + q holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4), the
+//   order in which that stage's softmax lanes hold their landmarks; padding
+//   is zero.  grid (D/16, batch*heads).
+// ZLDS (m <= 64): Z staged in LDS and W on the matrix cores, PR = 3 (bf16x3,
+// bf16 I/O: hi plane only) or 6 (three-way split, fp32 I/O: hi and lo
+// planes); otherwise fp32 FMAs from global Z.
+template <bool ZLDS, int PR>
 __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pacc, const float* __restrict__ pmax,
                                                     const float* __restrict__ psum, const float* __restrict__ Z,
                                                     float* __restrict__ BV, float* __restrict__ W,
@@ -1122,23 +1125,45 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
       const int e = tid + 1024 * u;
       if (e < m * m) sz[(e / m) * 68 + e % m] = zv[u];
     }
+    __syncthreads();
+    // W slice (64 x 16, rows >= m zero) = Z (64 x 64) BV slice (64 x 16): wave
+    // ti < 4 computes row tile ti; lane (c, g) ends with W[16ti + 4g + i][f0 + c].
+    const int lane = tid & 63, ti = tid >> 6, c = lane & 15, g = lane >> 4;
+    if (ti < 4 && 16 * ti < mpa) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        float a[8], b[8];
+        const int r = 16 * ti + c;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int k = 32 * kc + 8 * g + q;
+          a[q] = (r < m && k < m) ? sz[r * 68 + k] : 0.f;
+          b[q] = k < m ? sbv[k][c] : 0.f;
+        }
+        acc = mma_f32<PR>(a, b, acc);
+      }
+      const int fo = f0 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ti + 4 * g + i;
+        if (r < m) W[((size_t)bh * m + r) * D + fo] = acc[i];
+      }
+      // Landmarks 16ti + 4g .. +3 sit at positions 32(ti/2) + 8g + 4(ti%2) .. +3.
+      const size_t o = ((size_t)bh * D + fo) * mpa + 32 * (ti >> 1) + 8 * g + 4 * (ti & 1);
+      uint2 hv, lv;
+      split_pair(acc[0], acc[1], hv.x, lv.x);
+      split_pair(acc[2], acc[3], hv.y, lv.y);
+      *reinterpret_cast<uint2*>(&wt_hi[o]) = hv;
+      if constexpr (PR == 6) *reinterpret_cast<uint2*>(&wt_lo[o]) = lv;
+    }
+    return;
   }
   __syncthreads();
   for (int i = tid >> 4; i < m; i += 64) {
-    // Four interleaved partial sums (fixed order) keep the LDS reads in flight.
+    // Four interleaved partial sums (fixed order) keep the loads in flight.
     float acc4[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (ZLDS) {
-      for (int k = 0; k < (m & ~3); k += 4) {
-        const float4 zr = *reinterpret_cast<const float4*>(&sz[i * 68 + k]);
-        acc4[0] = fmaf(zr.x, sbv[k][f], acc4[0]);
-        acc4[1] = fmaf(zr.y, sbv[k + 1][f], acc4[1]);
-        acc4[2] = fmaf(zr.z, sbv[k + 2][f], acc4[2]);
-        acc4[3] = fmaf(zr.w, sbv[k + 3][f], acc4[3]);
-      }
-      for (int k = m & ~3; k < m; ++k) acc4[0] = fmaf(sz[i * 68 + k], sbv[k][f], acc4[0]);
-    } else {
-      for (int k = 0; k < m; ++k) acc4[k & 3] = fmaf(z[(size_t)i * m + k], sbv[k][f], acc4[k & 3]);
-    }
+    for (int k = 0; k < m; ++k) acc4[k & 3] = fmaf(z[(size_t)i * m + k], sbv[k][f], acc4[k & 3]);
     const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
     sw[i][f] = acc;
     W[((size_t)bh * m + i) * D + f0 + f] = acc;
@@ -1293,12 +1318,15 @@ hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   KernelTimer kt_("bv_finish", s);
-  if (p.m <= 64)
-    k_bv_finish<true><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi, w.wt_lo,
-                                                         p.m, p.d, w.nchunks, w.mpa);
+  if (p.m <= 64 && p.bf16)
+    k_bv_finish<true, 3><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi,
+                                                            w.wt_lo, p.m, p.d, w.nchunks, w.mpa);
+  else if (p.m <= 64)
+    k_bv_finish<true, 6><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi,
+                                                            w.wt_lo, p.m, p.d, w.nchunks, w.mpa);
   else
-    k_bv_finish<false><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi, w.wt_lo,
-                                                          p.m, p.d, w.nchunks, w.mpa);
+    k_bv_finish<false, 6><<<dim3(p.d / 16, BH), 1024, 0, s>>>(w.pacc, w.pmax, w.psum, w.Z, w.BV, w.W, w.wt_hi,
+                                                             w.wt_lo, p.m, p.d, w.nchunks, w.mpa);
   return hipGetLastError();
 }
 
