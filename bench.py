@@ -53,8 +53,8 @@ def algorithmic_bytes(wl, kernel: str) -> int:
     convw = 4 * wl.heads * wl.d * wl.conv_k
     if kernel == "segment_mean":
         return 2 * per_head * heads                  # read Q and K
-    if kernel == "landmark_bv":
-        return 2 * per_head * heads                  # read K and V
+    if kernel in ("landmark_bv", "landmark_pass"):
+        return 2 * per_head * heads                  # read K and V (the m x m pseudoinverse beside it moves no n-sized data)
     if kernel == "apply":
         return 3 * per_head * heads + convw          # read Q, V; write O
     if kernel == "fused":
