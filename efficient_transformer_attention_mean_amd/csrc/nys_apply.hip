@@ -523,14 +523,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         for (int j = 0; j < FPG / 8; ++j) {
           B8 o8;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) o8.h[q] = f32_to_bf16(v[8 * j + q]);
+          for (int q = 0; q < 4; ++q) o8.u[q] = pack_bf16x2(v[8 * j + 2 * q], v[8 * j + 2 * q + 1]);
           buf_store16(ro, base + 16 * j, o8.q);
         }
       } else {
-        B8 o8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o8.h[q] = f32_to_bf16(v[q]);
-        buf_store8(ro, base, make_uint2(o8.u[0], o8.u[1]));
+        buf_store8(ro, base, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
       }
     } else {
 #pragma unroll
