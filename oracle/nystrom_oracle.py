@@ -40,7 +40,13 @@ the design notes):
   odd-length filter per (head, feature): weights ``conv_w[h, c, t]``, "same"
   zero padding of (k-1)/2 on each side, no flip, no bias ([NF] "Putting It
   Together", Figure 4 "DConv k x 1"; [HF] "How do we select landmarks?").
-* No masking ([HF] leaves masking out of its excerpt).
+* n not a multiple of m: the sequence is padded at its end with zero rows
+  to n' = m * ceil(n/m) ([NF] "Landmark Selection: Segment-Means" assumes
+  divisibility and says padding provides it).  Every segment, the last one
+  included, is divided by its padded length l = n'/m, so the pad rows count
+  as zeros in the means.  The pad rows are not tokens: they are masked out
+  as keys (B~ spans the n real keys only) and produce no output rows.
+* No other masking ([HF] leaves masking out of its excerpt).
 
 Parity pins: every function here is pinned in ``tests/test_oracle_pins.py``
 against closed forms, brute force on tiny inputs, or library routines.
@@ -72,16 +78,19 @@ def segment_means(X, m):
     Eq. 16, with the divisor read as the segment length; [HF] "How do we
     select landmarks?").
 
-    X: (n, d).  Returns (m, d): row j is the mean of rows j*l .. j*l+l-1,
-    l = n/m.  n must be a multiple of m ([NF] assumes divisibility, "ensured
-    by padding").
+    X: (n, d), 1 <= m <= n.  X is first padded at its end with zero rows to
+    n' = m * ceil(n/m) (the section assumes n divisible by m and says padding
+    ensures it); with l = n'/m, row j of the result is the mean of padded
+    rows j*l .. j*l+l-1.  For n divisible by m there is no pad.
     """
     X = _f64(X)
     n, d = X.shape
-    if m < 1 or n % m != 0:
-        raise ValueError("n must be a positive multiple of m")
-    seg = n // m
-    return X.reshape(m, seg, d).mean(axis=1)
+    if m < 1 or m > n:
+        raise ValueError("need 1 <= m <= n")
+    seg = -(-n // m)
+    Xp = np.zeros((m * seg, d))
+    Xp[:n] = X
+    return Xp.reshape(m, seg, d).mean(axis=1)
 
 
 def row_softmax(S):
@@ -171,6 +180,10 @@ def nystrom_head(Q, K, V, m, iters, w=None):
       3. Z = ``iters`` steps of Lemma 1 on A.
       4. BV = B V;  W = Z BV;  O = F W   (never forms n x n).
       5. O += DConv(V) if a filter is given.
+
+    When n is not a multiple of m, step 1 sees the zero-padded sequence;
+    step 2 takes the n real rows only, so the pad is masked out of B's keys
+    and has no rows in F or O.
 
     Returns (O, dict of intermediates).
     """

@@ -61,7 +61,36 @@ def test_segment_means_special_cases():
     C = np.repeat(rng.standard_normal((2, 4)), 8, axis=0)
     np.testing.assert_allclose(segment_means(C, 2), C[::8], atol=1e-15)
     with pytest.raises(ValueError):
-        segment_means(X, 3)
+        segment_means(X, 17)  # more landmarks than rows
+    with pytest.raises(ValueError):
+        segment_means(X, 0)
+
+
+def test_segment_means_padded_by_hand():
+    # n not a multiple of m: zero rows are appended up to m * ceil(n/m) and
+    # every segment is divided by the padded length (a divisor counting only
+    # the real rows of the last segment would give 4.5 below).
+    X = np.array([[1.0], [2.0], [3.0], [4.0], [5.0]])
+    np.testing.assert_array_equal(segment_means(X, 2), [[2.0], [3.0]])              # l = 3
+    np.testing.assert_array_equal(segment_means(X, 3), [[1.5], [3.5], [2.5]])       # l = 2
+    np.testing.assert_array_equal(segment_means(X, 4), [[1.5], [3.5], [2.5], [0.0]])  # a segment of pad only
+    np.testing.assert_array_equal(segment_means(X, 5), X)                            # divisible: no pad
+
+
+def test_segment_means_padded_brute_force():
+    rng = np.random.default_rng(14)
+    for n, m in ((23, 5), (100, 8), (65, 64), (130, 64)):
+        d = 3
+        X = rng.standard_normal((n, d))
+        seg = -(-n // m)
+        expect = np.zeros((m, d))
+        for j in range(m):
+            for c in range(d):
+                acc = 0.0
+                for i in range(j * seg, (j + 1) * seg):
+                    acc += X[i, c] if i < n else 0.0
+                expect[j, c] = acc / seg
+        np.testing.assert_allclose(segment_means(X, m), expect, rtol=0, atol=1e-15)
 
 
 # ---------------------------------------------------------------- softmax
@@ -280,6 +309,21 @@ def test_segment_constant_inputs_are_exact():
     V = rng.standard_normal((n, d))
     O, _ = nystrom_head(Q, K, V, m=m, iters=60)
     assert rel_l2(O, _brute_exact_attention(Q, K, V)) < 1e-10
+
+
+def test_zero_queries_give_the_mean_of_the_real_values():
+    # Q = 0 makes every softmax uniform: A = 11^T/m is idempotent with unit
+    # norms, so Z0 = A and Lemma 1 maps A to A; BV rows are the mean of the
+    # value rows over the keys, and O = F Z BV is that mean in every row, for
+    # any K.  With n not a multiple of m the pad keys must not count: taking
+    # them as zero-valued keys would give sum(V) / (m ceil(n/m)) instead.
+    rng = np.random.default_rng(27)
+    for n, m in ((23, 5), (100, 8), (65, 64), (24, 4)):
+        d = 3
+        K, V = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+        O, inter = nystrom_head(np.zeros((n, d)), K, V, m, 6)
+        assert inter["B"].shape == (m, n)
+        np.testing.assert_allclose(O, np.broadcast_to(V.mean(0), (n, d)), rtol=0, atol=1e-13)
 
 
 def test_key_shift_invariance():
