@@ -22,8 +22,10 @@ namespace nys {
 
 // ---------------------------------------------------------------------------
 // Segment means: grid (m, batch*heads, 2); z = 0 -> Q, z = 1 -> K.
-// One block per segment of l = n/m contiguous rows; 16-byte coalesced loads,
-// fp32 partial sums per thread, fixed-order reduction through LDS.
+// One block per segment of l = ceil(n/m) contiguous rows; 16-byte coalesced
+// loads, fp32 partial sums per thread, fixed-order reduction through LDS.
+// When m does not divide n the sequence counts as padded with zero rows to
+// m*l: a segment reads only its rows below n and still divides by l.
 // Key landmarks are also written, pre-multiplied by log2(e)/sqrt(d), as bf16
 // hi/lo planes [bh][mpa][D] (rows m..mpa-1 zero), the operand layout of the
 // output stage, whose scores then come out in base-2 units.
@@ -39,7 +41,8 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   constexpr int RS = 256 / SLOTS;  // rows covered per pass
   __shared__ float part[4][D];
   const int j = blockIdx.x, bh = blockIdx.y;
-  const int seg = n / m;
+  const int seg = (n + m - 1) / m;
+  const int rows = max(0, min(seg, n - j * seg));  // real rows of this segment
   const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
   float* out = (blockIdx.z == 0 ? Qt : Kt) + ((size_t)bh * m + j) * D;
   const int slot = threadIdx.x % SLOTS, r0 = threadIdx.x / SLOTS;
@@ -47,12 +50,12 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
 #pragma unroll
   for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
   // 8 independent 16-byte loads in flight per thread, accumulated in row order.
-  for (int r = r0; r < seg; r += 8 * RS) {
+  for (int r = r0; r < rows; r += 8 * RS) {
     uint4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int rr = r + u * RS;
-      v[u] = rr < seg ? *reinterpret_cast<const uint4*>(X + (size_t)rr * D + slot * VEC) : make_uint4(0, 0, 0, 0);
+      v[u] = rr < rows ? *reinterpret_cast<const uint4*>(X + (size_t)rr * D + slot * VEC) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {

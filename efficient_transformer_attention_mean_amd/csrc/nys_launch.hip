@@ -6,7 +6,7 @@ namespace nys {
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
 bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
-  if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n || n % m != 0) return false;
+  if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n) return false;
   if (!(d == 16 || d == 32 || d == 64 || d == 128) || m > 256 || n > (1 << 24)) return false;
   const long long BH = (long long)batch * heads;
   // Key chunking for the split-n pass: about 2 blocks per CU over 256 CUs

@@ -5,7 +5,11 @@
  *   Qt, Kt  segment means of Q and K over m contiguous blocks of l = n/m rows
  *           ("Nyströmformer: A Nyström-Based Algorithm for Approximating
  *           Self-Attention", sec. 3.4 "Landmark Selection: Segment-Means",
- *           Eq. 16, divisor read as l);
+ *           Eq. 16, divisor read as l).  That section assumes m divides n
+ *           and says padding provides it: otherwise the sequence counts as
+ *           padded at its end with zero rows up to m * ceil(n/m), l is
+ *           ceil(n/m), and the pad rows, which are not tokens, are masked
+ *           out of B's keys and produce no output rows;
  *   F = softmax(Q Kt^T / sqrt(d)), A = softmax(Qt Kt^T / sqrt(d)),
  *   B = softmax(Qt K^T / sqrt(d)), all row-wise (same page, Eq. 13);
  *   Z = `iters` steps of Z <- Z (13I - AZ(15I - AZ(7I - AZ))) / 4 from
@@ -46,7 +50,7 @@ typedef enum { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
 /* Return codes. */
 enum {
   NYS_OK = 0,
-  NYS_EINVAL = -1,       /* bad argument: NULL tensor, size < 1, m > n, n % m != 0,
+  NYS_EINVAL = -1,       /* bad argument: NULL tensor, size < 1, m > n,
                             iters < 0, even or non-positive conv_k with a filter,
                             unknown dtype */
   NYS_EUNSUPPORTED = -2, /* valid but outside what the kernels handle:
@@ -83,7 +87,8 @@ long long nystrom_attn_workspace_offset(int which, int batch, int heads, int n, 
  *   Q, K, V     inputs, [batch][heads][n][d] of `dtype`
  *   conv_w      fp32 [heads][d][conv_k] depthwise filters, or NULL (no skip;
  *               conv_k is then ignored)
- *   n           sequence length, a multiple of m
+ *   n           sequence length, n >= m (padded as described at the top
+ *               when m does not divide it)
  *   d           head dimension, one of 16, 32, 64, 128
  *   m           number of landmarks, 1 <= m <= min(n, 256)
  *   heads       heads per batch entry

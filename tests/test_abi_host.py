@@ -64,6 +64,7 @@ def test_workspace_sizes_and_offsets(lib):
 @pytest.mark.parametrize("shape", [
     (1, 1, 64, 16, 8), (8, 12, 512, 64, 64), (4, 12, 4096, 64, 64),
     (2, 12, 8192, 64, 32), (1, 16, 32768, 128, 256), (1, 1, 48, 32, 3), (1, 1, 7, 16, 7),
+    (1, 1, 63, 16, 8), (2, 12, 8191, 64, 64), (1, 1, 100, 16, 64),  # n not a multiple of m: padded
 ])
 def test_workspace_valid_shapes(lib, shape):
     assert _lib.nystrom_attn_workspace_bytes(*shape) > 0
@@ -71,7 +72,7 @@ def test_workspace_valid_shapes(lib, shape):
 
 @pytest.mark.parametrize("shape", [
     (0, 1, 64, 16, 8), (1, 0, 64, 16, 8), (1, 1, 64, 16, 0), (1, 1, 64, 16, 65),
-    (1, 1, 63, 16, 8), (1, 1, 64, 24, 8), (1, 1, 64, 256, 8), (1, 1, 1024, 64, 512),
+    (1, 1, 7, 16, 8), (1, 1, 64, 24, 8), (1, 1, 64, 256, 8), (1, 1, 1024, 64, 512),
 ])
 def test_workspace_invalid_shapes(lib, shape):
     assert _lib.nystrom_attn_workspace_bytes(*shape) == 0
@@ -83,7 +84,7 @@ FAKE = 0x10000  # never dereferenced: every case below is rejected on the host
 @pytest.mark.parametrize("kw,code", [
     (dict(Q=None), _lib.NYS_EINVAL),
     (dict(out=None), _lib.NYS_EINVAL),
-    (dict(n=63), _lib.NYS_EINVAL),
+    (dict(n=7), _lib.NYS_EINVAL),  # m = 8 > n
     (dict(m=0), _lib.NYS_EINVAL),
     (dict(m=128, n=64), _lib.NYS_EINVAL),
     (dict(iters=-1), _lib.NYS_EINVAL),

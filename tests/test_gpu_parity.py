@@ -101,6 +101,14 @@ EDGE = [
     (1, 1, 4096, 64, 64, 6, 33, "f32"),   # many key chunks in fp32
     (2, 2, 222, 64, 6, 6, 33, "bf16"),    # n = 2 mod 4: the last group of 4 staged rows crosses the head's end
     (1, 3, 134, 32, 2, 6, 33, "f32"),     # the same with fp32 rows
+    # n not a multiple of m: zero pad to m*ceil(n/m), pad keys masked
+    (2, 2, 100, 16, 8, 6, 5, "f32"),      # l = 13, last segment 9 real rows
+    (1, 2, 1000, 64, 64, 6, 33, "bf16"),  # l = 16, one segment of pad only
+    (1, 1, 203, 32, 10, 6, 7, "f32"),     # l = 21, 14 real rows in the last segment
+    (1, 2, 777, 128, 96, 8, 33, "f32"),   # m > 64 path, l = 9
+    (2, 3, 8191, 64, 64, 6, 33, "bf16"),  # headline shape less one row
+    (1, 2, 4097, 64, 32, 6, 33, "f32"),   # one real row in the last segment
+    (1, 1, 130, 32, 64, 6, 3, "bf16"),    # l = 3: 20 segments of pad only (equal rows in A)
 ]
 
 
@@ -166,7 +174,7 @@ def test_invalid_calls_leave_output_untouched():
     import torch
     Q = torch.randn(1, 1, 64, 16, device="cuda")
     out = torch.full_like(Q, 7.0)
-    for kw, code in ((dict(m=5), _lib.NYS_EINVAL), (dict(d=24), _lib.NYS_EUNSUPPORTED)):
+    for kw, code in ((dict(m=65), _lib.NYS_EINVAL), (dict(d=24), _lib.NYS_EUNSUPPORTED)):
         args = dict(n=64, d=16, m=8)
         args.update(kw)
         rc = _lib.nystrom_attn_fwd(Q, Q, Q, None, args["n"], args["d"], args["m"], 1, 6, out, 1, 0, _lib.NYS_F32,
