@@ -46,7 +46,10 @@ the design notes):
   included, is divided by its padded length l = n'/m, so the pad rows count
   as zeros in the means.  The pad rows are not tokens: they are masked out
   as keys (B~ spans the n real keys only) and produce no output rows.
-* No other masking ([HF] leaves masking out of its excerpt).
+* Key-padding mask ([HF] leaves masking out of its excerpt): a batch of
+  right-padded sequences is given by one length L_b per batch entry, and
+  entry b is the method on its first L_b rows alone; its pad rows are never
+  read and their output rows are zero (``nystrom_attention``'s ``lengths``).
 
 Parity pins: every function here is pinned in ``tests/test_oracle_pins.py``
 against closed forms, brute force on tiny inputs, or library routines.
@@ -202,26 +205,38 @@ def nystrom_head(Q, K, V, m, iters, w=None):
     return O, inter
 
 
-def nystrom_attention(Q, K, V, m, iters, conv_w=None, with_intermediates=False):
+def nystrom_attention(Q, K, V, m, iters, conv_w=None, with_intermediates=False, lengths=None):
     """Nyström attention over a batch of heads.
 
     Q, K, V: (batch, heads, n, d).  conv_w: (heads, d, k) or None.
+    lengths: None, or one sequence length per batch entry for a batch of
+    right-padded sequences (a key-padding mask).  The pages leave masking
+    out ([HF] "How is Nyströmformer implemented?"); the reading taken is
+    that padding tokens are not part of the sequence: entry b is the method
+    on its first L_b rows alone (with the zero padding to a multiple of m of
+    ``segment_means`` when m does not divide L_b), its rows L_b .. n-1 are
+    never read, and its output rows there are zero.  Each L_b is clamped to
+    [m, n].
     Returns O of shape (batch, heads, n, d) in fp64 and, if asked, a dict of
     stacked intermediates (each with leading (batch, heads) axes).
     """
     Q, K, V = map(_f64, (Q, K, V))
     Bt, H, n, d = Q.shape
-    O = np.empty((Bt, H, n, d))
+    O = np.zeros((Bt, H, n, d))
     inter_all = {}
     for b in range(Bt):
+        L = n if lengths is None else int(min(max(int(lengths[b]), m), n))
         for h in range(H):
             w = None if conv_w is None else _f64(conv_w)[h]
-            O[b, h], inter = nystrom_head(Q[b, h], K[b, h], V[b, h], m, iters, w)
+            O[b, h, :L], inter = nystrom_head(Q[b, h, :L], K[b, h, :L], V[b, h, :L], m, iters, w)
             if with_intermediates:
                 for key, val in inter.items():
                     if key in ("F", "B"):  # n x m / m x n: skipped to save memory
                         continue
-                    inter_all.setdefault(key, np.empty((Bt, H) + val.shape))[b, h] = val
+                    if key == "O_att":  # rows past L_b stay zero, as in O
+                        inter_all.setdefault(key, np.zeros((Bt, H, n, d)))[b, h, :L] = val
+                    else:
+                        inter_all.setdefault(key, np.empty((Bt, H) + val.shape))[b, h] = val
     if with_intermediates:
         return O, inter_all
     return O

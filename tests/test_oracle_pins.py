@@ -400,3 +400,48 @@ def test_approximation_error_is_reported_not_gated():
     O, _ = nystrom_head(Q, K, V, 8, 6)
     err = rel_l2(O, exact_attention(Q, K, V))
     assert np.isfinite(err) and 0.0 < err < 10.0
+
+
+# ---------------------------------------------------------------- key-padding mask
+
+def test_lengths_zero_queries_give_the_mean_of_each_sequence():
+    # As in the zero-query case above, per batch entry: rows below L_b are the
+    # mean of that entry's first L_b value rows, rows from L_b on are zero.
+    rng = np.random.default_rng(28)
+    Bt, H, n, d, m = 3, 2, 40, 3, 4
+    K, V = rng.standard_normal((Bt, H, n, d)), rng.standard_normal((Bt, H, n, d))
+    lengths = [40, 23, 9]
+    O = nystrom_attention(np.zeros((Bt, H, n, d)), K, V, m, 6, lengths=lengths)
+    for b, L in enumerate(lengths):
+        for h in range(H):
+            np.testing.assert_allclose(O[b, h, :L], np.broadcast_to(V[b, h, :L].mean(0), (L, d)), rtol=0, atol=1e-13)
+            assert not O[b, h, L:].any()
+
+
+def test_lengths_pad_rows_are_never_read():
+    rng = np.random.default_rng(29)
+    Bt, H, n, d, m = 2, 2, 48, 4, 8
+    Q, K, V = (rng.standard_normal((Bt, H, n, d)) for _ in range(3))
+    w = rng.standard_normal((H, d, 5)) * 0.2
+    lengths = [30, 48]
+    O1, i1 = nystrom_attention(Q, K, V, m, 6, w, with_intermediates=True, lengths=lengths)
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    for X in (Q2, K2, V2):
+        X[0, :, 30:] = np.nan
+    O2, i2 = nystrom_attention(Q2, K2, V2, m, 6, w, with_intermediates=True, lengths=lengths)
+    np.testing.assert_array_equal(O1, O2)
+    for key in i1:
+        np.testing.assert_array_equal(i1[key], i2[key])
+    # The skip sees zeros past L_b: its last output row differs from the
+    # unmasked call's, which reads the rows past 30.
+    O3 = nystrom_attention(Q, K, V, m, 6, w)
+    assert not np.allclose(O1[0, :, 29], O3[0, :, 29])
+    np.testing.assert_array_equal(O1[1], O3[1])  # full length: same as no mask
+
+
+def test_lengths_are_clamped_to_m_and_n():
+    rng = np.random.default_rng(30)
+    Bt, H, n, d, m = 2, 1, 20, 2, 5
+    Q, K, V = (rng.standard_normal((Bt, H, n, d)) for _ in range(3))
+    np.testing.assert_array_equal(nystrom_attention(Q, K, V, m, 6, lengths=[2, 99]),
+                                  nystrom_attention(Q, K, V, m, 6, lengths=[5, 20]))
