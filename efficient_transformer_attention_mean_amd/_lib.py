@@ -27,6 +27,7 @@ EXPORTS = (
     "nystrom_attn_workspace_bytes",
     "nystrom_attn_workspace_offset",
     "nystrom_attn_fwd",
+    "nystrom_attn_fwd_masked",
     "nystrom_dconv_fwd",
     "nystrom_strerror",
     "nystrom_abi_version",
@@ -53,6 +54,8 @@ def load():
     lib.nystrom_attn_workspace_offset.restype = ctypes.c_longlong
     lib.nystrom_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, sz, vp]
     lib.nystrom_attn_fwd.restype = i
+    lib.nystrom_attn_fwd_masked.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, vp, sz, vp]
+    lib.nystrom_attn_fwd_masked.restype = i
     lib.nystrom_dconv_fwd.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp]
     lib.nystrom_dconv_fwd.restype = i
     lib.nystrom_strerror.argtypes = [i]
@@ -102,6 +105,13 @@ def nystrom_attn_fwd(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k,
     return int(load().nystrom_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), n, d, m, heads, iters,
                                        _ptr(out), batch, conv_k, dtype, _ptr(workspace), workspace_bytes,
                                        _stream(stream)))
+
+
+def nystrom_attn_fwd_masked(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype, lengths,
+                            workspace=None, workspace_bytes=0, stream=None) -> int:
+    return int(load().nystrom_attn_fwd_masked(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), n, d, m, heads, iters,
+                                              _ptr(out), batch, conv_k, dtype, _ptr(lengths), _ptr(workspace),
+                                              workspace_bytes, _stream(stream)))
 
 
 def nystrom_dconv_fwd(V, conv_w, n, d, heads, batch, conv_k, dtype, out, stream=None) -> int:

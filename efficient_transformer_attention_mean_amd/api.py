@@ -45,9 +45,11 @@ def new_workspace(batch, heads, n, d, m, device="cuda") -> torch.Tensor:
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def attention(Q, K, V, m, iters=6, conv_w=None, out=None, workspace=None, stream=None):
+def attention(Q, K, V, m, iters=6, conv_w=None, out=None, workspace=None, stream=None, lengths=None):
     """Nyström attention forward.  Q, K, V: [batch, heads, n, d] (fp32 or bf16);
-    conv_w: fp32 [heads, d, k] or None.  Returns ``out`` (same shape/dtype)."""
+    conv_w: fp32 [heads, d, k] or None; lengths: None, or int32 [batch] on
+    the GPU, the tokens of each right-padded sequence (key-padding mask).
+    Returns ``out`` (same shape/dtype)."""
     _check_io(Q, K, V)
     batch, heads, n, d = Q.shape
     conv_k = 0
@@ -62,10 +64,19 @@ def attention(Q, K, V, m, iters=6, conv_w=None, out=None, workspace=None, stream
     if stream is None:
         stream = torch.cuda.current_stream()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = _lib.nystrom_attn_fwd(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, _DTYPES[Q.dtype],
-                               workspace, ws_bytes, stream)
+    if lengths is None:
+        rc = _lib.nystrom_attn_fwd(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, _DTYPES[Q.dtype],
+                                   workspace, ws_bytes, stream)
+        if rc != _lib.NYS_OK:
+            raise NystromError(rc, "nystrom_attn_fwd")
+        return out
+    if (lengths.dtype != torch.int32 or tuple(lengths.shape) != (batch,) or lengths.device.type != "cuda"
+            or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 GPU tensor of shape [batch]")
+    rc = _lib.nystrom_attn_fwd_masked(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k,
+                                      _DTYPES[Q.dtype], lengths, workspace, ws_bytes, stream)
     if rc != _lib.NYS_OK:
-        raise NystromError(rc, "nystrom_attn_fwd")
+        raise NystromError(rc, "nystrom_attn_fwd_masked")
     return out
 
 

@@ -62,9 +62,13 @@ long long nystrom_attn_workspace_offset(int which, int batch, int heads, int n, 
   }
 }
 
-int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
-                     int heads, int iters, void* out, int batch, int conv_k, int dtype, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int forward(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m, int heads,
+            int iters, void* out, int batch, int conv_k, int dtype, const int* lengths, void* workspace,
+            size_t workspace_bytes, void* stream) {
   try {
     if (!Q || !K || !V || !out) return NYS_EINVAL;
     if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
@@ -82,7 +86,8 @@ int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* c
     } else if (workspace_bytes < L.total) {
       return NYS_EWORKSPACE;
     }
-    nys::Problem p{Q, K, V, conv_w, out, batch, heads, n, d, m, iters, conv_w ? conv_k : 0, dtype == NYS_BF16};
+    nys::Problem p{Q, K, V, conv_w, out, batch, heads, n, d, m, iters, conv_w ? conv_k : 0, dtype == NYS_BF16,
+                   lengths};
     hipError_t e = nys::launch_forward(p, L, ws, s);
     if (owned) {
       hipError_t f = hipFreeAsync(ws, s);
@@ -92,6 +97,24 @@ int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* c
   } catch (...) {
     return NYS_EHIP;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
+                     int heads, int iters, void* out, int batch, int conv_k, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return forward(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype, nullptr, workspace,
+                 workspace_bytes, stream);
+}
+
+int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
+                            int heads, int iters, void* out, int batch, int conv_k, int dtype, const int* lengths,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return forward(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype, lengths, workspace,
+                 workspace_bytes, stream);
 }
 
 int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch, int conv_k, int dtype,

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                                const uint16_t* __restrict__ wt_hi,
                                                const uint16_t* __restrict__ wt_lo,
                                                const float* __restrict__ conv_w, const uint4* __restrict__ cwop,
-                                               typename IO::T* __restrict__ out, int n, int m, int heads,
+                                               typename IO::T* __restrict__ out,
+                                               const int* __restrict__ lens, int n, int m, int heads,
                                                int conv_k, int ntile, long long ntotal) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
@@ -176,7 +177,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   uint16_t* wp = reinterpret_cast<uint16_t*>(smem_raw + LY::WT);  // [hi (, lo)][D][WP]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int head_bytes = n * D * ES;
+  // Bytes of head bh's rows that hold tokens (the row pitch of a head is n
+  // rows; with per-sequence lengths only the first ones are real): Q and V
+  // rows past them read as zero through the range check.
+  auto token_bytes = [&](int bh) { return (lens ? min(max(lens[bh / heads], m), n) : n) * (D * ES); };
 
   // Run of tiles of this block.
   const long long G = gridDim.x, L = blockIdx.x;
@@ -248,10 +252,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     return Pos{__builtin_amdgcn_readfirstlane(q.bh), __builtin_amdgcn_readfirstlane(q.ti)};
   };
   auto issue_v = [&](Pos q, uint4 (&vr)[NTK][4]) {
-    if constexpr (LY::STAGE) load_v<LY>(vr, head_rsrc(Vin + (size_t)q.bh * n * D, head_bytes), q.ti * kTQ);
+    if constexpr (LY::STAGE) load_v<LY>(vr, head_rsrc(Vin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * kTQ);
   };
   auto issue_q = [&](Pos q, uint4 (&qr)[KC][LY::QW]) {
-    if constexpr (ATT) load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, head_bytes), q.ti * kTQ + 16 * wave + c);
+    if constexpr (ATT)
+      load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * kTQ + 16 * wave + c);
   };
 
   // V rows (registers) -> Vt[feature][row].
@@ -482,7 +487,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 
   // Attention + Ot (+ wide-filter skip) -> output row 16*wave + c of the
   // tile, features g*FPG .. +FPG-1: 16-byte stores (8-byte for bf16 at
-  // d = 16); rows past the end are dropped by the range check.
+  // d = 16); rows past the head's tokens are dropped by the range check
+  // (with per-sequence lengths, k_zero_pad_rows writes those rows).
   auto epilogue = [&](int bh, int h, int t0, const f32x4_t (&o)[ND]) {
     const int p = 16 * wave + c, row = t0 + p, f0 = g * FPG;
     float v[FPG];
@@ -503,10 +509,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
     if constexpr (KW == -1) {
-      if (row < n) {
+      const int nb = seq_rows(lens, bh / heads, n, m);
+      if (row < nb) {
         const T* Vh = Vin + (size_t)bh * n * D;
         const int R = (conv_k - 1) / 2;
-        const int tb = max(0, R - row), te = min(conv_k, n - row + R);
+        const int tb = max(0, R - row), te = min(conv_k, nb - row + R);
         for (int q = 0; q < FPG; ++q) {
           const float* wq = conv_w + ((size_t)h * D + f0 + q) * conv_k;
           float s = 0.f;
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
       }
     }
-    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, token_bytes(bh));
     const int base = (row * D + f0) * ES;
     if constexpr (IO::kBf16) {
       if constexpr (FPG >= 8) {
@@ -640,7 +647,7 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   const int grid = (int)(total < want ? total : want);
   kern<<<grid, 256, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
                                     w ? w->kt_lo : nullptr, w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w,
-                                    w ? w->cwop : nullptr, static_cast<T*>(p.out), p.n, p.m, p.heads, p.conv_k,
+                                    w ? w->cwop : nullptr, static_cast<T*>(p.out), p.lens, p.n, p.m, p.heads, p.conv_k,
                                     ntile, total);
   return hipSuccess;
 }
@@ -674,6 +681,27 @@ hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return e != hipSuccess ? e : hipGetLastError();
+}
+
+// Rows L_b .. n-1 of every head of batch entry b (that sequence's padding)
+// set to zero: grid (blocks over a head's 16-byte vectors, batch*heads).
+__global__ __launch_bounds__(256) void k_zero_pad_rows(uint4* __restrict__ out, const int* __restrict__ lens, int n,
+                                                       int m, int heads, int row_vecs) {
+  const int bh = blockIdx.y;
+  const int nb = seq_rows(lens, bh / heads, n, m);
+  const int per_head = n * row_vecs;  // < 2^27: n * d < 2^29
+  const int e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e < nb * row_vecs || e >= per_head) return;
+  out[(size_t)bh * per_head + e] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t stage_zero_pad(const Problem& p, hipStream_t s) {
+  if (!p.lens) return hipSuccess;
+  const int row_vecs = p.d * (p.bf16 ? 2 : 4) / 16;
+  const dim3 grid(cdiv((long long)p.n * row_vecs, 256), p.batch * p.heads);
+  KernelTimer kt_("zero_pad", s);
+  k_zero_pad_rows<<<grid, 256, 0, s>>>(static_cast<uint4*>(p.out), p.lens, p.n, p.m, p.heads, row_vecs);
+  return hipGetLastError();
 }
 
 template <typename IO, int D>

@@ -191,4 +191,10 @@ __device__ __forceinline__ float sum_over_groups(float v) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Rows of batch entry b that are tokens: lens[b] clamped to [m, n] for a
+// batch of right-padded sequences, n without lengths (lens == nullptr).
+__device__ __forceinline__ int seq_rows(const int* __restrict__ lens, int b, int n, int m) {
+  return lens ? min(max(lens[b], m), n) : n;
+}
+
 }  // namespace nys

@@ -25,7 +25,9 @@ namespace nys {
 // One block per segment of l = ceil(n/m) contiguous rows; 16-byte coalesced
 // loads, fp32 partial sums per thread, fixed-order reduction through LDS.
 // When m does not divide n the sequence counts as padded with zero rows to
-// m*l: a segment reads only its rows below n and still divides by l.
+// m*l: a segment reads only its rows below n and still divides by l.  With
+// per-sequence lengths, n is that batch entry's length (the row pitch of a
+// head stays the buffer's n).
 // Key landmarks are also written, pre-multiplied by log2(e)/sqrt(d), as bf16
 // hi/lo planes [bh][mpa][D] (rows m..mpa-1 zero), the operand layout of the
 // output stage, whose scores then come out in base-2 units.
@@ -34,15 +36,17 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
                                                       uint16_t* __restrict__ kt_hi, uint16_t* __restrict__ kt_lo,
-                                                      int n, int m, int mpa, float sl2e) {
+                                                      const int* __restrict__ lens, int heads, int n, int m,
+                                                      int mpa, float sl2e) {
   using T = typename IO::T;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int SLOTS = D / VEC;   // 16-byte vectors per row
   constexpr int RS = 256 / SLOTS;  // rows covered per pass
   __shared__ float part[4][D];
   const int j = blockIdx.x, bh = blockIdx.y;
-  const int seg = (n + m - 1) / m;
-  const int rows = max(0, min(seg, n - j * seg));  // real rows of this segment
+  const int nb = seq_rows(lens, bh / heads, n, m);
+  const int seg = (nb + m - 1) / m;
+  const int rows = max(0, min(seg, nb - j * seg));  // real rows of this segment
   const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
   float* out = (blockIdx.z == 0 ? Qt : Kt) + ((size_t)bh * m + j) * D;
   const int slot = threadIdx.x % SLOTS, r0 = threadIdx.x / SLOTS;
@@ -722,7 +726,7 @@ template <typename IO, int D, int NTW>
 __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, const typename IO::T* __restrict__ Kin,
                                          const typename IO::T* __restrict__ Vin, const float* __restrict__ Qt,
                                          float* __restrict__ pacc, float* __restrict__ pmax,
-                                         float* __restrict__ psum, int n, int m, int chunk, int nchunks,
+                                         float* __restrict__ psum, int n, int nb, int m, int chunk, int nchunks,
                                          float sl2e) {
   using T = typename IO::T;
   using SM = BvSmem<IO, D>;
@@ -730,7 +734,9 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   constexpr int MD = D / 16;         // 16-row tiles of V^T
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  // Keys [kbeg, kend) of this chunk; nb <= n is the head's number of real
+  // keys (chunks past it are empty and leave max -inf, sum 0).
+  const int kbeg = ch * chunk, kend = min(nb, kbeg + chunk);
   const T* Kh = Kin + (size_t)bh * n * D;
   const T* Vh = Vin + (size_t)bh * n * D;
   const float* qt = Qt + (size_t)bh * m * D;
@@ -980,7 +986,8 @@ struct LandmarkPassArgs {
   float *A, *Z, *pacc, *pmax, *psum;
   const float* conv_w;
   uint4* cwop;
-  int n, m, chunk, nchunks, iters, npinv, nconv, conv_total, conv_k;
+  const int* lens;  // tokens per sequence, or nullptr
+  int n, heads, m, chunk, nchunks, iters, npinv, nconv, conv_total, conv_k;
   float sl2e;
 };
 
@@ -1012,8 +1019,10 @@ __global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
     return;
   }
   blk -= a.nconv;
-  bv_chunk<IO, D, NTW>(sm.b, blk % a.nchunks, blk / a.nchunks, static_cast<const T*>(a.K), static_cast<const T*>(a.V),
-                       a.Qt, a.pacc, a.pmax, a.psum, a.n, a.m, a.chunk, a.nchunks, a.sl2e);
+  const int bh = blk / a.nchunks;
+  bv_chunk<IO, D, NTW>(sm.b, blk % a.nchunks, bh, static_cast<const T*>(a.K), static_cast<const T*>(a.V), a.Qt,
+                       a.pacc, a.pmax, a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n, a.m), a.m, a.chunk,
+                       a.nchunks, a.sl2e);
 }
 
 // Finish of the split-n pass, one block per (16-feature slice, head):
@@ -1075,14 +1084,17 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
 #pragma unroll
         for (int u = 0; u < NB; ++u)
           if (c0 + 4 * u < nchunks) Mb = fmaxf(Mb, pm[u]);
-        const float a = __builtin_amdgcn_exp2f(M - Mb);  // arguments <= 0; 0 while M = -inf
+        // Arguments <= 0; 0 while M = -inf.  Chunks past a sequence's end are
+        // empty (max -inf): a batch of only those keeps M = Mb = -inf and must
+        // not form -inf - -inf.
+        const float a = M == Mb ? 1.f : __builtin_amdgcn_exp2f(M - Mb);
         L *= a;
 #pragma unroll
         for (int k = 0; k < 4; ++k) S[k] *= a;
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           if (c0 + 4 * u < nchunks) {
-            const float e = __builtin_amdgcn_exp2f(pm[u] - Mb);
+            const float e = pm[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm[u] - Mb);
             L += ps[u] * e;
             S[0] += pa[u].x * e;
             S[1] += pa[u].y * e;
@@ -1196,7 +1208,8 @@ static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   KernelTimer kt_("segment_mean", s);
   k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
-                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.n, p.m, w.mpa,
+                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.lens, p.heads, p.n,
+                                                         p.m, w.mpa,
                                                          kLog2e / sqrtf((float)D));
 }
 
@@ -1279,7 +1292,9 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.psum = w.psum;
   a.conv_w = p.conv_w;
   a.cwop = w.cwop;
+  a.lens = p.lens;
   a.n = p.n;
+  a.heads = p.heads;
   a.m = p.m;
   a.chunk = w.chunk;
   a.nchunks = w.nchunks;

@@ -109,6 +109,27 @@ int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* c
                      int batch, int conv_k, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Nyström self-attention forward over a batch of right-padded sequences, the
+ * key-padding mask given as one length per batch entry.  The pages leave
+ * masking out ("Approximating self-attention in linear time and memory via
+ * the Nyström method", "How is Nyströmformer implemented?"); the reading
+ * taken is that padding tokens are not part of a sequence: batch entry b is
+ * what nystrom_attn_fwd computes for its first L_b rows alone (padded to a
+ * multiple of m as described at the top when m does not divide L_b).
+ *   lengths     DEVICE pointer to int32 [batch], L_b = tokens of entry b;
+ *               read on the device only, each clamped to [m, n] there (the
+ *               host cannot check them without a synchronisation).  NULL =
+ *               every entry has n tokens, the same as nystrom_attn_fwd.
+ * Rows L_b .. n-1 of Q, K and V are never read (they may hold anything);
+ * rows L_b .. n-1 of out are written as zero; the workspace intermediates of
+ * entry b are those of its own sequence.  All other arguments, the workspace
+ * size, the return codes and the stream behaviour are those of
+ * nystrom_attn_fwd. */
+int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const float* conv_w,
+                            int n, int d, int m, int heads, int iters, void* out,
+                            int batch, int conv_k, int dtype, const int* lengths,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Depthwise-convolution skip alone: out = DConv(V) with the filters and
  * padding described at the top ("Putting It Together", Figure 4's DConv path).
  *   V, out      [batch][heads][n][d] of `dtype` (out must not alias V)

@@ -32,8 +32,13 @@ def dtype_code(dtype: str) -> int:
     return _lib.NYS_BF16 if dtype == "bf16" else _lib.NYS_F32
 
 
-def run_forward(inp, m, iters, dtype, use_conv=True, own_workspace=True, stream=None):
-    """Run nystrom_attn_fwd on the seeded inputs; returns (out, intermediates dict)."""
+_UNSET = object()
+
+
+def run_forward(inp, m, iters, dtype, use_conv=True, own_workspace=True, stream=None, lengths=_UNSET):
+    """Run nystrom_attn_fwd on the seeded inputs, or nystrom_attn_fwd_masked
+    when ``lengths`` is given (a sequence of per-entry lengths, or None for a
+    NULL lengths pointer); returns (out, intermediates dict)."""
     import torch
     Q, K, V = (to_dev(inp[k], dtype) for k in ("Q", "K", "V"))
     B, H, n, d = inp["Q"].shape
@@ -48,7 +53,13 @@ def run_forward(inp, m, iters, dtype, use_conv=True, own_workspace=True, stream=
         assert nbytes > 0
         ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream() if stream is None else stream
-    rc = _lib.nystrom_attn_fwd(Q, K, V, wdev, n, d, m, H, iters, out, B, conv_k, dtype_code(dtype), ws, nbytes, s)
+    if lengths is _UNSET:
+        rc = _lib.nystrom_attn_fwd(Q, K, V, wdev, n, d, m, H, iters, out, B, conv_k, dtype_code(dtype), ws, nbytes,
+                                   s)
+    else:
+        lens = None if lengths is None else torch.tensor(list(lengths), dtype=torch.int32, device="cuda")
+        rc = _lib.nystrom_attn_fwd_masked(Q, K, V, wdev, n, d, m, H, iters, out, B, conv_k, dtype_code(dtype), lens,
+                                          ws, nbytes, s)
     assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
     torch.cuda.synchronize()
     inter = {}

@@ -185,3 +185,59 @@ def test_invalid_calls_leave_output_untouched():
     assert rc == _lib.NYS_EWORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+# Key-padding mask: a batch of right-padded sequences, one length per entry.
+# The pad rows of Q, K and V are filled with NaN, so any read of them would
+# show in the output; the output's pad rows must come back exactly zero.
+MASKED = [
+    # (batch, heads, n, d, m, iters, conv_k, dtype, lengths)
+    (3, 2, 300, 64, 16, 6, 33, "bf16", (300, 173, 40)),
+    (2, 2, 1000, 32, 64, 6, 33, "f32", (1000, 517)),
+    (4, 1, 256, 16, 8, 6, 5, "f32", (3, 999, 129, 64)),      # clamped to m and to n
+    (2, 3, 640, 128, 80, 6, 33, "f32", (640, 333)),          # m > 64 path
+    (2, 12, 8192, 64, 64, 6, 33, "bf16", (8192, 5000)),      # headline shape, one entry padded
+    (2, 2, 4096, 64, 32, 6, 0, "bf16", (1, 4096)),           # no skip; entry 0 clamped to m rows
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}m{c[4]}k{c[6]}{c[7]}L{'-'.join(map(str, c[8]))}"
+                                              for c in MASKED])
+def test_masked_parity(case):
+    B, H, n, d, m, iters, k, dt, lengths = case
+    wl = WORKLOADS["tiny"].with_(name=f"masked{case}", batch=B, heads=H, n=n, d=d, m=m, iters=iters, conv_k=k,
+                                 dtype=dt, seed=200 + n + m)
+    inp = dict(make_inputs(wl))
+    eff = [min(max(L, m), n) for L in lengths]
+    for key in ("Q", "K", "V"):
+        x = np.array(inp[key], copy=True)
+        for b, L in enumerate(eff):
+            x[b, :, L:] = np.nan
+        inp[key] = x
+    O, inter = nystrom_attention(inp["Q"], inp["K"], inp["V"], m, iters, inp["conv_w"], with_intermediates=True,
+                                 lengths=lengths)
+    out, got = run_forward(inp, m, iters, dt, use_conv=k > 0, lengths=lengths)
+    for b, L in enumerate(eff):
+        assert np.all(out[b, :, L:] == 0.0), b
+    errs = {"out": rel_l2(out, O)}
+    for key, t in INTER_TOL[dt].items():
+        errs[key] = rel_l2(got[key], inter[key])
+    out_att, _ = run_forward(inp, m, iters, dt, use_conv=False, lengths=lengths)
+    errs["out_att_only"] = rel_l2(out_att, inter["O_att"])
+    print(f"masked {case}: " + ", ".join(f"{kk}={v:.2e}" for kk, v in errs.items()))
+    assert errs["out"] <= OUT_TOL[dt], errs
+    assert errs["out_att_only"] <= OUT_TOL[dt], errs
+    for key, t in INTER_TOL[dt].items():
+        assert errs[key] <= t, (key, errs)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_masked_full_lengths_equal_unmasked_bitwise(dt):
+    wl = WORKLOADS["long"].with_(name=f"masked_full_{dt}", batch=2, heads=3, n=1500, dtype=dt)
+    inp = make_inputs(wl)
+    a, ia = run_forward(inp, wl.m, wl.iters, dt)
+    b, ib = run_forward(inp, wl.m, wl.iters, dt, lengths=None)
+    c, ic = run_forward(inp, wl.m, wl.iters, dt, lengths=(1500, 1500))
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    for key in ia:
+        assert np.array_equal(ia[key], ib[key]) and np.array_equal(ia[key], ic[key]), key
