@@ -10,7 +10,8 @@ Inputs are seeded synthetic tensors already resident in HBM.  The timed steps
 rotate over several independent input/output sets whose total exceeds the
 256 MB last-level cache, so every call reads its inputs from HBM.
 
-Prints one JSON line.  ``value`` is tokens/s (batch * n per step) over exactly
+Prints one JSON line.  ``value`` is tokens/s (batch * n per step; with
+``--lengths``, a batch of right-padded sequences, the real tokens) over exactly
 ``--steps`` calls timed with two events on the launch stream; a second pass
 records an event between calls (``per_call_us``: median, p10, p90) and a
 third has the library bracket every kernel with events.  ``roofline`` is for
@@ -45,20 +46,21 @@ PAGES_CONTEXT = {"hardware": "GTX 1080Ti (not comparable)", "n": 8192, "nystrom6
                  "speedup_vs_standard": 12.7, "memory_reduction_vs_standard": 22.8}
 
 
-def algorithmic_bytes(wl, kernel: str) -> int:
-    """Bytes each kernel must move per launch (per-head figure x heads)."""
+def algorithmic_bytes(wl, kernel: str, token_rows=None) -> int:
+    """Bytes each kernel must move per launch: the per-row figure times the
+    token rows over all heads (batch * heads * n, or the sum of the
+    per-sequence lengths times heads with a key-padding mask)."""
     e = wl.elem_bytes
-    per_head = wl.n * wl.d * e
-    heads = wl.batch * wl.heads
+    all_rows = wl.batch * wl.heads * wl.n
+    rows = all_rows if token_rows is None else token_rows
+    row = wl.d * e
     convw = 4 * wl.heads * wl.d * wl.conv_k
     if kernel == "segment_mean":
-        return 2 * per_head * heads                  # read Q and K
+        return 2 * row * rows                  # read Q and K
     if kernel in ("landmark_bv", "landmark_pass"):
-        return 2 * per_head * heads                  # read K and V (the m x m pseudoinverse beside it moves no n-sized data)
+        return 2 * row * rows                  # read K and V (the m x m pseudoinverse beside it moves no n-sized data)
     if kernel == "apply":
-        return 3 * per_head * heads + convw          # read Q, V; write O
-    if kernel == "fused":
-        return 4 * per_head * heads + convw          # read Q, K, V; write O
+        return (2 * rows + all_rows) * row + convw  # read Q, V (token rows); write every row of O
     return 0
 
 
@@ -87,6 +89,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="wall time budget of the CPU-oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--lengths", default=None,
+                    help="tokens of each batch entry, comma-separated: a batch of right-padded sequences "
+                         "(key-padding mask, nystrom_attn_fwd_masked); value then counts real tokens")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -104,7 +109,17 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    io_bytes = wl.compulsory_bytes()
+    lengths = None
+    eff = [wl.n] * wl.batch
+    if args.lengths:
+        lengths = [int(x) for x in args.lengths.split(",")]
+        if len(lengths) != wl.batch:
+            print(f"--lengths needs {wl.batch} values for workload {wl.name}", file=sys.stderr)
+            return 2
+        eff = [min(max(x, wl.m), wl.n) for x in lengths]
+    token_rows = sum(eff) * wl.heads
+    # Read Q, K, V token rows once, write every row of O once, plus the filters.
+    io_bytes = wl.compulsory_bytes() - 3 * (wl.batch * wl.n * wl.heads - token_rows) * wl.d * wl.elem_bytes
     sets = args.sets or max(2, int(np.ceil(512 * 2 ** 20 / io_bytes)) + 1)
 
     def to_dev(x):
@@ -126,11 +141,16 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     code = _lib.NYS_BF16 if wl.dtype == "bf16" else _lib.NYS_F32
     conv_k = wl.conv_k if wl.conv_k else 0
+    lens_dev = None if lengths is None else torch.tensor(lengths, dtype=torch.int32, device=dev)
 
     def step(i):
         Q, K, V, W, O = bufs[i % sets]
-        rc = _lib.nystrom_attn_fwd(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, O, wl.batch, conv_k, code,
-                                   ws, ws_bytes, stream)
+        if lens_dev is None:
+            rc = _lib.nystrom_attn_fwd(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, O, wl.batch, conv_k, code,
+                                       ws, ws_bytes, stream)
+        else:
+            rc = _lib.nystrom_attn_fwd_masked(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, O, wl.batch, conv_k,
+                                              code, lens_dev, ws, ws_bytes, stream)
         if rc != 0:
             raise RuntimeError(_lib.nystrom_strerror(rc))
 
@@ -153,7 +173,7 @@ def main() -> int:
     wall = time.perf_counter() - t0
     gpu_s = ev0.elapsed_time(ev1) / 1e3
     ms_per_step = 1e3 * gpu_s / args.steps
-    tokens = wl.batch * wl.n
+    tokens = sum(eff)
     value = tokens * args.steps / gpu_s
 
     # Per-call distribution: an event between consecutive calls.
@@ -186,7 +206,7 @@ def main() -> int:
     if dom is not None:
         ms, launches = kern[dom]
         avg_s = ms / launches / 1e3
-        ab = algorithmic_bytes(wl, dom)
+        ab = algorithmic_bytes(wl, dom, token_rows)
         if ab:
             from efficient_transformer_attention_mean_amd.profiling import read_traffic
             achieved = ab / avg_s / 1e9
@@ -215,7 +235,8 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "n": wl.n, "d": wl.d, "m": wl.m,
-                   "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype, "input_sets": sets},
+                   "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype, "input_sets": sets,
+                   **({} if lengths is None else {"lengths": lengths})},
         "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
         "compulsory_bytes": io_bytes,
         "per_call_us": {"median": round(float(np.median(per_call_us)), 2),
@@ -235,7 +256,7 @@ def main() -> int:
         O_ref = None
         while True:
             O_ref, inter = nystrom_attention(host0["Q"], host0["K"], host0["V"], wl.m, wl.iters, host0["conv_w"],
-                                             with_intermediates=True)
+                                             with_intermediates=True, lengths=lengths)
             reps += 1
             if args.no_cpu_baseline or time.perf_counter() - c0 >= args.cpu_seconds:
                 break
@@ -243,7 +264,8 @@ def main() -> int:
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = {
                 "value": round(tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": f"{reps} whole call(s) of the workload (batch {wl.batch} x {wl.heads} heads, n={wl.n}), "
+                "sample": f"{reps} whole call(s) of the workload (batch {wl.batch} x {wl.heads} heads, n={wl.n}"
+                          f"{'' if lengths is None else ', lengths ' + args.lengths}), "
                           f"fp64 NumPy, {cpu_s:.1f} s, host has {os.cpu_count()} logical CPUs"}
         if not args.no_parity:
             Q, K, V, W, O = bufs[0]
@@ -257,8 +279,9 @@ def main() -> int:
             # Context: distance of the method from exact softmax attention on
             # sampled query rows (attention part only, no skip).
             rng = np.random.default_rng(7)
-            rows = np.sort(rng.choice(wl.n, size=min(256, wl.n), replace=False))
-            ex = np.stack([np.stack([exact_attention(host0["Q"][b, h][rows], host0["K"][b, h], host0["V"][b, h])
+            rows = np.sort(rng.choice(min(eff), size=min(256, min(eff)), replace=False))
+            ex = np.stack([np.stack([exact_attention(host0["Q"][b, h][rows], host0["K"][b, h, :eff[b]],
+                                                     host0["V"][b, h, :eff[b]])
                                      for h in range(wl.heads)]) for b in range(wl.batch)])
             att = inter["O_att"][:, :, rows]
             result["parity_rel_l2_vs_oracle"] = err

@@ -487,9 +487,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 
   // Attention + Ot (+ wide-filter skip) -> output row 16*wave + c of the
   // tile, features g*FPG .. +FPG-1: 16-byte stores (8-byte for bf16 at
-  // d = 16); rows past the head's tokens are dropped by the range check
-  // (with per-sequence lengths, k_zero_pad_rows writes those rows).
-  auto epilogue = [&](int bh, int h, int t0, const f32x4_t (&o)[ND]) {
+  // d = 16); rows past the end are dropped by the range check, rows of a
+  // sequence's padding (nb <= row < n) are written as zero.
+  auto epilogue = [&](int bh, int h, int t0, int nb, const f32x4_t (&o)[ND]) {
     const int p = 16 * wave + c, row = t0 + p, f0 = g * FPG;
     float v[FPG];
 #pragma unroll
@@ -509,7 +509,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
     }
     if constexpr (KW == -1) {
-      const int nb = seq_rows(lens, bh / heads, n, m);
       if (row < nb) {
         const T* Vh = Vin + (size_t)bh * n * D;
         const int R = (conv_k - 1) / 2;
@@ -522,7 +521,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         }
       }
     }
-    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, token_bytes(bh));
+    if (row >= nb) {
+#pragma unroll
+      for (int q = 0; q < FPG; ++q) v[q] = 0.f;
+    }
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, n * D * ES);
     const int base = (row * D + f0) * ES;
     if constexpr (IO::kBf16) {
       if constexpr (FPG >= 8) {
@@ -574,12 +577,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
     __syncthreads();  // Vt of this tile and the planes visible; the previous epilogue's Ot reads done
 
-    skip(h);
+    // A tile wholly inside a sequence's padding only writes zeros (its loads
+    // past the tokens read zeros and move no data).
+    const int nb = seq_rows(lens, bh / heads, n, m);
+    const bool live = t0 < nb;
+    if (live) skip(h);
     f32x4_t o[ND];
-    if constexpr (ATT) attention(bh, t0, ahead(t, pos, 2), qr, o);
+    if constexpr (ATT) {
+      if (live) {
+        attention(bh, t0, ahead(t, pos, 2), qr, o);
+      } else {
+        issue_q(ahead(t, pos, 2), qr);
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
+      }
+    }
     __syncthreads();  // Ot visible; the skip's Vt reads and the attention's plane reads done
 
-    epilogue(bh, h, t0, o);
+    epilogue(bh, h, t0, nb, o);
     if constexpr (LY::STAGE) {
       stage(vn);
       issue_v(ahead(t, pos, 3), vn);
@@ -681,27 +696,6 @@ hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return e != hipSuccess ? e : hipGetLastError();
-}
-
-// Rows L_b .. n-1 of every head of batch entry b (that sequence's padding)
-// set to zero: grid (blocks over a head's 16-byte vectors, batch*heads).
-__global__ __launch_bounds__(256) void k_zero_pad_rows(uint4* __restrict__ out, const int* __restrict__ lens, int n,
-                                                       int m, int heads, int row_vecs) {
-  const int bh = blockIdx.y;
-  const int nb = seq_rows(lens, bh / heads, n, m);
-  const int per_head = n * row_vecs;  // < 2^27: n * d < 2^29
-  const int e = blockIdx.x * 256 + (int)threadIdx.x;
-  if (e < nb * row_vecs || e >= per_head) return;
-  out[(size_t)bh * per_head + e] = make_uint4(0, 0, 0, 0);
-}
-
-hipError_t stage_zero_pad(const Problem& p, hipStream_t s) {
-  if (!p.lens) return hipSuccess;
-  const int row_vecs = p.d * (p.bf16 ? 2 : 4) / 16;
-  const dim3 grid(cdiv((long long)p.n * row_vecs, 256), p.batch * p.heads);
-  KernelTimer kt_("zero_pad", s);
-  k_zero_pad_rows<<<grid, 256, 0, s>>>(static_cast<uint4*>(p.out), p.lens, p.n, p.m, p.heads, row_vecs);
-  return hipGetLastError();
 }
 
 template <typename IO, int D>

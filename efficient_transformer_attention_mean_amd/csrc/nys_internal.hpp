@@ -68,8 +68,7 @@ hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  /
 hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s);
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z when not in the pass above
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      // B V, W, W^T planes (needs Z)
-hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out (token rows)
-hipError_t stage_zero_pad(const Problem& p, hipStream_t s);                    // out rows past each length
+hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,

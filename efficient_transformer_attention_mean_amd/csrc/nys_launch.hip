@@ -83,8 +83,7 @@ hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStre
   if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
   if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
   if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
-  if ((e = stage_apply(p, w, s)) != hipSuccess) return e;
-  return stage_zero_pad(p, s);
+  return stage_apply(p, w, s);
 }
 
 }  // namespace nys

@@ -75,6 +75,8 @@ WORKLOADS = {
                      note="long sequence, bf16 I/O"),
     "headline": Workload("headline", 2, 12, 8192, 64, 64, 6, 33, "bf16", 3,
                          note="n=8192, m=64, d=64, bf16 I/O"),
+    "headline_ragged": Workload("headline_ragged", 2, 12, 8191, 64, 64, 6, 33, "bf16", 3,
+                                note="the headline shape less one row: m does not divide n"),
     "headline_m32": Workload("headline_m32", 2, 12, 8192, 64, 32, 6, 33, "bf16", 3,
                              note="n=8192, m=32, d=64, bf16 I/O"),
     "stress": Workload("stress", 1, 16, 32768, 128, 256, 8, 33, "bf16", 4, sharpen_keys=True,

@@ -68,7 +68,7 @@ def check(wl, report=print):
     return errs
 
 
-@pytest.mark.parametrize("name", ["tiny", "bert", "long", "headline", "headline_m32", "stress"])
+@pytest.mark.parametrize("name", ["tiny", "bert", "long", "headline", "headline_ragged", "headline_m32", "stress"])
 def test_workload_parity(name):
     check(WORKLOADS[name])
 
