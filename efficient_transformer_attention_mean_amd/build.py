@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnystrom.so")
 
-SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_launch.hip", "nys_abi.hip", "nys_timing.hip"]
+SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_backward.hip", "nys_launch.hip", "nys_abi.hip", "nys_timing.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -117,6 +117,47 @@ int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const f
                  workspace_bytes, stream);
 }
 
+size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k) {
+  if (check_shape(batch, heads, n, d, m, iters) != NYS_OK) return 0;
+  nys::BwdLayout L;
+  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, conv_k < 0 ? 0 : conv_k, &L)) return 0;
+  return L.total;
+}
+
+int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d,
+                     int m, int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    const int ck = conv_w ? conv_k : 0;
+    nys::BwdLayout L;
+    if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, &L)) return NYS_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bool owned = false;
+    if (!ws) {
+      if (hipMallocAsync(reinterpret_cast<void**>(&ws), L.total, s) != hipSuccess) return NYS_EHIP;
+      owned = true;
+    } else if (workspace_bytes < L.total) {
+      return NYS_EWORKSPACE;
+    }
+    nys::BwdProblem p{{Q, K, V, conv_w, nullptr, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16}, dO, dQ, dK,
+                      dV, conv_w ? dconv_w : nullptr};
+    hipError_t e = nys::launch_backward(p, L, ws, s);
+    if (owned) {
+      hipError_t f = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = f;
+    }
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
 int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch, int conv_k, int dtype,
                       void* out, void* stream) {
   try {

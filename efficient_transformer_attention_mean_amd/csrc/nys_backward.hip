@@ -1,0 +1,797 @@
+// Nyström self-attention backward: HIP kernels for gfx950 (CDNA4).
+//
+// Gradients of the forward pass ("Nyströmformer: A Nyström-Based Algorithm
+// for Approximating Self-Attention", paper deep-dive page, sec. 3.4: Eq. 13,
+// Eq. 16, Lemma 1 and its initialisation, Eq. 17 and the DConv skip of
+// Figure 4) with respect to Q, K, V and the skip filters.  The pages train
+// through the fixed number of pseudoinverse steps; the derivative here is
+// that of the forward computation as written, step by step in reverse.
+//
+// Per (batch, head), with s = 1/sqrt(d), P' = softmax backward
+// (dS = P * (dP - rowsum(dP * P))):
+//   dW = F^T dO,  dF = dO W^T,  dS_F = F'(dF)               -> k_bwd_rows (partials)
+//   dZ = dW BV^T, dBV = Z^T dW, dA = Lemma-1 backward,
+//   dS_A = A'(dA), dKt = s dS_F^T Q + s dS_A^T Qt, dQt_A = s dS_A Kt
+//                                                           -> k_bwd_land
+//   B = softmax(s Qt K^T) from the forward's row statistics, dB = dBV V^T,
+//   dS_B = B'(dB), dK = s dS_B^T Qt + seg^T dKt, dV = B^T dBV + DConv^T(dO),
+//   dQt_B = s dS_B K, dw = sum dO (x) V                      -> k_bwd_key (+ partials)
+//   dQt = dQt_A + dQt_B, dw summed over batch and chunks     -> k_bwd_finish
+//   dQ = s dS_F Kt + seg^T dQt                               -> k_bwd_rows
+// where seg^T spreads landmark j's gradient over the real rows of segment j,
+// divided by the (padded) segment length.  The landmark-side forward values
+// (Qt, Kt, A, Z, BV, W and the split-n softmax statistics of B) are
+// recomputed by the forward's own kernels at the start of the call.
+//
+// The n-sized passes run in fp32 on the vector units with their operands in
+// LDS; the m x m products of the pseudoinverse backward use the matrix cores
+// with split-bf16 operands (bf16x3 for bf16 I/O, three-way for fp32 I/O).
+#include <math.h>
+
+#include "nys_common.hpp"
+#include "nys_internal.hpp"
+
+namespace nys {
+
+namespace {
+
+constexpr int kRowTile = 32;  // query rows per tile of k_bwd_rows
+constexpr int kKeyTile = 16;  // key rows per tile of k_bwd_key
+
+template <typename IO>
+__device__ __forceinline__ float ld(const typename IO::T* p) {
+  return load_elem<IO>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Query side.  Grid (chunks, batch*heads); each block walks tiles of 32 rows
+// of its chunk.  Per row i (thread group of 8 lanes, landmarks jl + 8u):
+//   F_i = softmax(s Q_i Kt^T), dF_i = dO_i W^T, dS_i = F_i * (dF_i - F_i . dF_i).
+// DQ = false: accumulates dW = sum_i F_i^T dO_i and dKt_F = s sum_i dS_i^T Q_i
+//             per chunk (fixed order) and writes the chunk's partials.
+// DQ = true:  writes dQ_i = s dS_i Kt + dQt[seg(i)] / l.
+template <typename IO, int D, bool DQ>
+__global__ __launch_bounds__(256) void k_bwd_rows(const typename IO::T* __restrict__ Q,
+                                                  const typename IO::T* __restrict__ dO,
+                                                  const float* __restrict__ Kt, const float* __restrict__ W,
+                                                  const float* __restrict__ dqt, typename IO::T* __restrict__ dQ,
+                                                  float* __restrict__ pdw, float* __restrict__ pdkt, int n, int m,
+                                                  int chunk, int nchunks, float sl2e, float scale) {
+  constexpr int P = D + 1;  // LDS pitch of d-wide rows
+  constexpr int NE = 64 * D / 256;
+  extern __shared__ __align__(16) float lds[];
+  float* kt = lds;                  // [64][P]
+  float* ws = kt + 64 * P;          // [64][P]
+  float* qs = ws + 64 * P;          // [kRowTile][P]
+  float* gs = qs + kRowTile * P;    // [kRowTile][P]
+  float* fs = gs + kRowTile * P;    // [kRowTile][65]
+  float* ds = fs + kRowTile * 65;   // [kRowTile][65]
+  const int tid = threadIdx.x, ch = blockIdx.x, bh = blockIdx.y;
+  const int r = tid >> 3, jl = tid & 7;
+  const size_t hoff = (size_t)bh * n * D;
+
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int j = e / D, c = e % D;
+    kt[j * P + c] = j < m ? Kt[((size_t)bh * m + j) * D + c] : 0.f;
+    ws[j * P + c] = j < m ? W[((size_t)bh * m + j) * D + c] : 0.f;
+  }
+  float aw[NE], ak[NE];
+#pragma unroll
+  for (int v = 0; v < NE; ++v) aw[v] = ak[v] = 0.f;
+  const int seg = (n + m - 1) / m;
+  const float inv_seg = 1.f / (float)seg;
+
+  const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
+  for (int t0 = rbeg; t0 < rend; t0 += kRowTile) {
+    __syncthreads();  // previous tile's readers done (and the landmark rows visible)
+    for (int e = tid; e < kRowTile * D; e += 256) {
+      const int rr = e / D, c = e % D, row = t0 + rr;
+      const bool in = row < rend;
+      qs[rr * P + c] = in ? ld<IO>(Q + hoff + (size_t)row * D + c) : 0.f;
+      gs[rr * P + c] = in ? ld<IO>(dO + hoff + (size_t)row * D + c) : 0.f;
+    }
+    __syncthreads();
+
+    float sc[8], df[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sc[u] = df[u] = 0.f;
+    for (int k = 0; k < D; ++k) {
+      const float q = qs[r * P + k], gv = gs[r * P + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sc[u] = fmaf(q, kt[(jl + 8 * u) * P + k], sc[u]);
+        df[u] = fmaf(gv, ws[(jl + 8 * u) * P + k], df[u]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sc[u] = (jl + 8 * u < m) ? sc[u] * sl2e : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sc[u] = exp2f(sc[u] - mx);  // 0 for the padding landmarks
+      sum += sc[u];
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) sum += shfl_xor(sum, o);
+    const float inv = 1.f / sum;
+    float delta = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sc[u] *= inv;  // F
+      delta = fmaf(sc[u], df[u], delta);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) delta += shfl_xor(delta, o);
+    const bool live = t0 + r < rend;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = jl + 8 * u;
+      if (j < 64) {
+        fs[r * 65 + j] = live ? sc[u] : 0.f;
+        ds[r * 65 + j] = live ? sc[u] * (df[u] - delta) : 0.f;
+      }
+    }
+    __syncthreads();
+
+    if constexpr (DQ) {
+      // dQ row r, features c = jl + 8w.
+      const int row = t0 + r;
+      if (row < rend) {
+        const float* qtr = dqt + ((size_t)bh * m + row / seg) * D;
+        for (int c = jl; c < D; c += 8) {
+          float acc = 0.f;
+          for (int j = 0; j < m; ++j) acc = fmaf(ds[r * 65 + j], kt[j * P + c], acc);
+          store_elem<IO>(dQ + hoff + (size_t)row * D + c, fmaf(scale, acc, qtr[c] * inv_seg));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < NE; ++v) {
+        const int e = tid + 256 * v, j = e / D, c = e % D;
+        float a0 = aw[v], a1 = ak[v];
+#pragma unroll 4
+        for (int rr = 0; rr < kRowTile; ++rr) {
+          a0 = fmaf(fs[rr * 65 + j], gs[rr * P + c], a0);
+          a1 = fmaf(ds[rr * 65 + j], qs[rr * P + c], a1);
+        }
+        aw[v] = a0;
+        ak[v] = a1;
+      }
+    }
+  }
+  if constexpr (!DQ) {
+    const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+    for (int v = 0; v < NE; ++v) {
+      const int e = tid + 256 * v, j = e / D;
+      if (j < m) {
+        pdw[base + e] = aw[v];
+        pdkt[base + e] = scale * ak[v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Landmark side, one block per head (256 threads, m <= MP <= 64, matrices in
+// LDS with pitch MP + 4).
+
+template <int MP>
+struct LandSmem {
+  static constexpr int LP = MP + 4;
+  float A[MP][LP], dA[MP][LP], dZ[MP][LP], T2[MP][LP], Zk[MP][LP], X[MP][LP], T1[MP][LP], dT2[MP][LP],
+      dX[MP][LP];
+  float col[MP], row[MP], red[8];
+};
+
+// C = op(P) op(Q) on MP x MP LDS matrices (pitch MP + 4), where op(P) =
+// pa * P' + pb * I on the first m diagonal entries (P' = P or P^T) and the
+// same for Q.  Wave w owns tiles t = w + 4q (q < NT*NT/4); its lane (c, g)
+// gets rows ti*16 + 4g + i, column tj*16 + c of each, and epi(q, row0, col,
+// v) receives them.
+template <int MP>
+struct LandTiles {
+  static constexpr int NT = MP / 16, PER = NT * NT / 4;  // tiles per wave
+};
+
+template <int MP, int PR, bool TPa, bool TQa, typename Epi>
+__device__ __forceinline__ void land_mm(const float (*Pm)[MP + 4], float pa, float pb, const float (*Qm)[MP + 4],
+                                        float qa, float qb, int m, Epi epi) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  constexpr int NT = LandTiles<MP>::NT;
+#pragma unroll
+  for (int q = 0; q < LandTiles<MP>::PER; ++q) {
+    const int t = wave + 4 * q;
+    const int ti = t / NT, tj = t % NT;
+    const int i = ti * 16 + c, j = tj * 16 + c;
+    f32x4_t acc = zero4();
+#pragma unroll
+    for (int kc = 0; kc < MP; kc += 32) {
+      float a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = kc + 8 * g + u;
+        const float pv = TPa ? Pm[k][i] : Pm[i][k];
+        const float qv = TQa ? Qm[j][k] : Qm[k][j];
+        a[u] = pa * pv + ((i == k && k < m) ? pb : 0.f);
+        b[u] = qa * qv + ((k == j && k < m) ? qb : 0.f);
+      }
+      acc = mma_f32<PR>(a, b, acc);
+    }
+    epi(q, ti * 16 + 4 * g, tj * 16 + c, acc);
+  }
+}
+
+// Stores per-wave tile results kept by an earlier land_mm into M.
+template <int MP>
+__device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&keep)[LandTiles<MP>::PER]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  constexpr int NT = LandTiles<MP>::NT;
+#pragma unroll
+  for (int q = 0; q < LandTiles<MP>::PER; ++q) {
+    const int t = wave + 4 * q;
+    const int r0 = (t / NT) * 16 + 4 * g, cc = (t % NT) * 16 + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[r0 + i][cc] = keep[q][i];
+  }
+}
+
+template <int MP, int PR>
+__global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, const float* __restrict__ Kt,
+                                                  const float* __restrict__ Aw, const float* __restrict__ Zw,
+                                                  const float* __restrict__ BV, const float* __restrict__ pdw,
+                                                  const float* __restrict__ pdkt, float* __restrict__ dWg,
+                                                  float* __restrict__ dBV, float* __restrict__ dKt,
+                                                  float* __restrict__ dQtA, float* __restrict__ zs, int m, int D,
+                                                  int nchunks, int iters, float scale) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
+  using Mat = float (*)[MP + 4];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m;
+
+  // dW and dKt_F: fixed-order sums of the query-side partials.
+  for (int e = tid; e < m * D; e += 256) {
+    float a = 0.f, b = 0.f;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const size_t o = ((size_t)bh * nchunks + ch) * m * D + e;
+      a += pdw[o];
+      b += pdkt[o];
+    }
+    dWg[md + e] = a;
+    dKt[md + e] = b;
+  }
+  // A (zero padded) and the final iterate Z.
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    const bool in = i < m && j < m;
+    sm.A[i][j] = in ? Aw[mm + i * m + j] : 0.f;
+    sm.X[i][j] = in ? Zw[mm + i * m + j] : 0.f;
+  }
+  __syncthreads();
+
+  // dZ = dW BV^T and dBV = Z^T dW (fp32, contraction over d / m).
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    float a = 0.f;
+    if (i < m && j < m)
+      for (int c = 0; c < D; ++c) a = fmaf(dWg[md + (size_t)i * D + c], BV[md + (size_t)j * D + c], a);
+    sm.dZ[i][j] = a;
+  }
+  for (int e = tid; e < m * D; e += 256) {
+    const int j = e / D, c = e % D;
+    float a = 0.f;
+    for (int i = 0; i < m; ++i) a = fmaf(sm.X[i][j], dWg[md + (size_t)i * D + c], a);
+    dBV[md + e] = a;
+  }
+
+  // Start Z0 = c A^T; column and row sums of A (entries are positive).
+  if (tid < MP) {
+    float cs = 0.f, rs = 0.f;
+    for (int i = 0; i < MP; ++i) {
+      cs += sm.A[i][tid];
+      rs += sm.A[tid][i];
+    }
+    sm.col[tid] = cs;
+    sm.row[tid] = rs;
+  }
+  __syncthreads();
+  float n1 = 0.f, ninf = 0.f;
+  int jstar = 0;
+  for (int i = 0; i < m; ++i) {
+    if (sm.col[i] > n1) {
+      n1 = sm.col[i];
+      jstar = i;
+    }
+    ninf = fmaxf(ninf, sm.row[i]);
+  }
+  const float cz = 1.f / (n1 * ninf);
+  float* zsh = zs + (size_t)bh * iters * MP * MP;
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    sm.Zk[i][j] = cz * sm.A[j][i];
+  }
+  __syncthreads();
+
+  // Forward iterates Z_0 .. Z_{iters-1} -> zs (Z_k in sm.Zk at step k).
+  for (int k = 0; k < iters; ++k) {
+    for (int e = tid; e < MP * MP; e += 256) zsh[(size_t)k * MP * MP + e] = sm.Zk[e / MP][e % MP];
+    if (k + 1 == iters) break;
+    land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.X, -1.f, 7.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.T1[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.T2[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.Zk, 0.25f, 0.f, sm.T2, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    for (int e = tid; e < MP * MP; e += 256) sm.Zk[e / MP][e % MP] = sm.dT2[e / MP][e % MP];
+    __syncthreads();
+  }
+  for (int e = tid; e < MP * MP; e += 256) sm.dA[e / MP][e % MP] = 0.f;
+  __syncthreads();
+
+  // Reverse through the steps.  Mat pointers let dZ and T2 trade places.
+  Mat dZ = sm.dZ, T2 = sm.T2;
+  for (int k = iters - 1; k >= 0; --k) {
+    for (int e = tid; e < MP * MP; e += 256) sm.Zk[e / MP][e % MP] = zsh[(size_t)k * MP * MP + e];
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.X, -1.f, 7.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.T1[r0 + i][cc] = v[i];  // T1 = X (7I - X)
+    });
+    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) T2[r0 + i][cc] = v[i];  // T2 = X (15I - T1)
+    });
+    // dT2 = -Z_k^T dZ / 4 (reads Zk, dZ; T2 is not read).
+    land_mm<MP, PR, true, false>(sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    // dZ_k (through the factor Z_k) = dZ (13I - T2)^T / 4, into the T2 slot.
+    {
+      f32x4_t keep[LandTiles<MP>::PER];
+      land_mm<MP, PR, false, true>(dZ, 0.25f, 0.f, T2, -1.f, 13.f, m,
+                                   [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
+      __syncthreads();
+      land_store<MP>(T2, keep);
+      Mat tmp = dZ;
+      dZ = T2;
+      T2 = tmp;
+    }
+    // dX = dT2 (15I - T1)^T.
+    land_mm<MP, PR, false, true>(sm.dT2, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.dX[r0 + i][cc] = v[i];
+    });
+    __syncthreads();
+    // dT1 = -X^T dT2, in place of dT2.
+    {
+      f32x4_t keep[LandTiles<MP>::PER];
+      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, sm.dT2, 1.f, 0.f, m,
+                                   [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
+      __syncthreads();
+      land_store<MP>(sm.dT2, keep);
+    }
+    __syncthreads();
+    // dX += dT1 (7I - X)^T - X^T dT1.
+    {
+      f32x4_t keep[LandTiles<MP>::PER];
+      land_mm<MP, PR, false, true>(sm.dT2, 1.f, 0.f, sm.X, -1.f, 7.f, m,
+                                   [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
+      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, sm.dT2, 1.f, 0.f, m,
+                                   [&](int q, int r0, int cc, const f32x4_t& v) {
+                                     for (int i = 0; i < 4; ++i) sm.dX[r0 + i][cc] += keep[q][i] + v[i];
+                                   });
+    }
+    __syncthreads();
+    // dA += dX Z_k^T;  dZ_k += A^T dX.
+    land_mm<MP, PR, false, true>(sm.dX, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.dA[r0 + i][cc] += v[i];
+    });
+    land_mm<MP, PR, true, false>(sm.A, 1.f, 0.f, sm.dX, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) dZ[r0 + i][cc] += v[i];
+    });
+    __syncthreads();
+  }
+
+  // The start Z0 = cz A^T: dA += cz dZ^T, and through cz = 1/(n1 ninf):
+  // dcz = sum dZ * A^T; n1 = column sum jstar adds -dcz cz / n1 to column
+  // jstar.  The ninf term is constant along a row and cancels in the softmax
+  // backward below, so it is left out.
+  float part = 0.f;
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    part = fmaf(dZ[i][j], sm.A[j][i], part);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) part += shfl_xor(part, o);
+  if ((tid & 63) == 0) sm.red[tid >> 6] = part;
+  __syncthreads();
+  const float dcz = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    if (i < m && j < m) sm.dA[i][j] += cz * dZ[j][i] + (j == jstar ? -dcz * cz / n1 : 0.f);
+  }
+  __syncthreads();
+  // dS_A = A * (dA - rowsum(dA * A)), in place of dA.
+  if (tid < MP) {
+    float s = 0.f;
+    for (int j = 0; j < m; ++j) s = fmaf(sm.dA[tid][j], sm.A[tid][j], s);
+    sm.row[tid] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < MP * MP; e += 256) {
+    const int i = e / MP, j = e % MP;
+    sm.dA[i][j] = sm.A[i][j] * (sm.dA[i][j] - sm.row[i]);
+  }
+  __syncthreads();
+  // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt.
+  for (int e = tid; e < m * D; e += 256) {
+    const int j = e / D, c = e % D;
+    float a = 0.f, b = 0.f;
+    for (int k = 0; k < m; ++k) {
+      a = fmaf(sm.dA[j][k], Kt[md + (size_t)k * D + c], a);
+      b = fmaf(sm.dA[k][j], Qt[md + (size_t)k * D + c], b);
+    }
+    dQtA[md + e] = scale * a;
+    dKt[md + e] += scale * b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side.  Grid (chunks, batch*heads); tiles of 16 keys with a halo of R =
+// (conv_k - 1)/2 rows of V and dO for the skip.  Per key i (16 lanes,
+// landmarks jl + 16u):
+//   B_:i = 2^(s' Qt K_i - M) / L (the forward's row statistics of B),
+//   dB_:i = dBV V_i, dS_:i = B_:i * (dB_:i - delta), delta_j = dBV_j . BV_j.
+// Writes dK_i = s dS_:i^T Qt + dKt[seg(i)] / l and dV_i = B_:i^T dBV +
+// DConv^T(dO)_i; partials of dQt_B = s sum_i dS_:i K_i and of the filter
+// gradient dw[c][t] = sum_i dO[i][c] V[i + t - R][c].
+template <typename IO, int D>
+__global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restrict__ K,
+                                                 const typename IO::T* __restrict__ V,
+                                                 const typename IO::T* __restrict__ dO,
+                                                 const float* __restrict__ conv_w, const float* __restrict__ Qt,
+                                                 const float* __restrict__ BV, const float* __restrict__ dBVg,
+                                                 const float* __restrict__ dKt, const float* __restrict__ pmax,
+                                                 const float* __restrict__ psum, typename IO::T* __restrict__ dK,
+                                                 typename IO::T* __restrict__ dV, float* __restrict__ pdqt,
+                                                 float* __restrict__ pdwc, int n, int m, int heads, int conv_k,
+                                                 int chunk, int nchunks, int fchunks, float sl2e, float scale) {
+  constexpr int P = D + 1;
+  constexpr int NE = 64 * D / 256;
+  const int R = conv_k > 0 ? (conv_k - 1) / 2 : 0;
+  const int HR = kKeyTile + 2 * R;  // rows of the V / dO tiles
+  extern __shared__ __align__(16) float lds[];
+  float* qt = lds;                     // [64][P]  Qt (unscaled)
+  float* db = qt + 64 * P;             // [64][P]  dBV
+  float* kk = db + 64 * P;             // [kKeyTile][P]
+  float* vv = kk + kKeyTile * P;       // [HR][P]
+  float* gg = vv + 48 * P;             // [HR][P]
+  float* bs = gg + 48 * P;             // [kKeyTile][65]
+  float* dss = bs + kKeyTile * 65;     // [kKeyTile][65]
+  float* stm = dss + kKeyTile * 65;    // [64] M
+  float* stl = stm + 64;               // [64] 1/L
+  float* dlt = stl + 64;               // [64] delta
+  float* wsh = dlt + 64;               // [D][conv_k]
+  const int tid = threadIdx.x, ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
+  const size_t hoff = (size_t)bh * n * D, md = (size_t)bh * m * D;
+
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int j = e / D, c = e % D;
+    qt[j * P + c] = j < m ? Qt[md + e] : 0.f;
+    db[j * P + c] = j < m ? dBVg[md + e] : 0.f;
+  }
+  for (int e = tid; e < D * conv_k; e += 256) wsh[e] = conv_w[(size_t)h * D * conv_k + e];
+  if (tid < 64) {
+    // Row statistics of B from the forward's split-n partials (same fixed
+    // order as its finish) and delta_j = dBV_j . BV_j.
+    const int j = tid;
+    float M = -INFINITY, L = 0.f, dl = 0.f;
+    if (j < m) {
+      for (int c = 0; c < fchunks; ++c) M = fmaxf(M, pmax[((size_t)bh * fchunks + c) * m + j]);
+      for (int c = 0; c < fchunks; ++c) {
+        const float pm = pmax[((size_t)bh * fchunks + c) * m + j];
+        if (pm != -INFINITY) L += psum[((size_t)bh * fchunks + c) * m + j] * exp2f(pm - M);
+      }
+      for (int c = 0; c < D; ++c) dl = fmaf(dBVg[md + (size_t)j * D + c], BV[md + (size_t)j * D + c], dl);
+    }
+    stm[j] = M;
+    stl[j] = j < m ? 1.f / L : 0.f;
+    dlt[j] = dl;
+  }
+  float aq[NE];
+#pragma unroll
+  for (int v = 0; v < NE; ++v) aq[v] = 0.f;
+  float awc[17];  // filter-gradient entries tid + 256 v (d * conv_k <= 128 * 33)
+#pragma unroll
+  for (int v = 0; v < 17; ++v) awc[v] = 0.f;
+  const int seg = (n + m - 1) / m;
+  const float inv_seg = 1.f / (float)seg;
+  const int r = tid >> 4, jl = tid & 15;
+
+  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  for (int i0 = kbeg; i0 < kend; i0 += kKeyTile) {
+    __syncthreads();
+    for (int e = tid; e < kKeyTile * D; e += 256) {
+      const int rr = e / D, c = e % D, row = i0 + rr;
+      kk[rr * P + c] = row < kend ? ld<IO>(K + hoff + (size_t)row * D + c) : 0.f;
+    }
+    for (int e = tid; e < HR * D; e += 256) {
+      const int rr = e / D, c = e % D, row = i0 - R + rr;
+      const bool in = row >= 0 && row < n;
+      vv[rr * P + c] = in ? ld<IO>(V + hoff + (size_t)row * D + c) : 0.f;
+      gg[rr * P + c] = in ? ld<IO>(dO + hoff + (size_t)row * D + c) : 0.f;
+    }
+    __syncthreads();
+
+    float sc[4], dbv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = dbv[u] = 0.f;
+    for (int k = 0; k < D; ++k) {
+      const float kv = kk[r * P + k], vk = vv[(R + r) * P + k];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u] = fmaf(kv, qt[(jl + 16 * u) * P + k], sc[u]);
+        dbv[u] = fmaf(vk, db[(jl + 16 * u) * P + k], dbv[u]);
+      }
+    }
+    const bool live = i0 + r < kend;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = jl + 16 * u;
+      const float b = (live && j < m) ? exp2f(sc[u] * sl2e - stm[j]) * stl[j] : 0.f;
+      bs[r * 65 + j] = b;
+      dss[r * 65 + j] = b * (dbv[u] - dlt[j]);
+    }
+    __syncthreads();
+
+    {
+      const int row = i0 + r;
+      if (row < kend) {
+        const float* ktr = dKt + md + (size_t)(row / seg) * D;
+        for (int c = jl; c < D; c += 16) {
+          float a = 0.f, b = 0.f;
+          for (int j = 0; j < m; ++j) {
+            a = fmaf(dss[r * 65 + j], qt[j * P + c], a);
+            b = fmaf(bs[r * 65 + j], db[j * P + c], b);
+          }
+          // Skip transpose: dV[i][c] += sum_t w[c][t] dO[i - t + R][c].
+          for (int t = 0; t < conv_k; ++t) b = fmaf(wsh[c * conv_k + t], gg[(r - t + 2 * R) * P + c], b);
+          store_elem<IO>(dK + hoff + (size_t)row * D + c, fmaf(scale, a, ktr[c] * inv_seg));
+          store_elem<IO>(dV + hoff + (size_t)row * D + c, b);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NE; ++v) {
+      const int e = tid + 256 * v, j = e / D, c = e % D;
+      float a = aq[v];
+#pragma unroll 4
+      for (int rr = 0; rr < kKeyTile; ++rr) a = fmaf(dss[rr * 65 + j], kk[rr * P + c], a);
+      aq[v] = a;
+    }
+#pragma unroll
+    for (int v = 0; v < 17; ++v) {
+      const int e = tid + 256 * v;
+      if (e < D * conv_k) {
+        const int c = e / conv_k, t = e % conv_k;
+        float a = awc[v];
+#pragma unroll 4
+        for (int rr = 0; rr < kKeyTile; ++rr)
+          if (i0 + rr < kend) a = fmaf(gg[(R + rr) * P + c], vv[(rr + t) * P + c], a);
+        awc[v] = a;
+      }
+    }
+  }
+  {
+    const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+    for (int v = 0; v < NE; ++v) {
+      const int e = tid + 256 * v, j = e / D;
+      if (j < m) pdqt[base + e] = scale * aq[v];
+    }
+    const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+#pragma unroll
+    for (int v = 0; v < 17; ++v) {
+      const int e = tid + 256 * v;
+      if (e < D * conv_k) pdwc[wb + e] = awc[v];
+    }
+  }
+}
+
+// dQt = dQt_A + sum of the key-side partials (chunk order); grid batch*heads.
+__global__ __launch_bounds__(256) void k_bwd_qt_finish(const float* __restrict__ dQtA, const float* __restrict__ pdqt,
+                                                       float* __restrict__ dQt, int md, int nchunks) {
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < md; e += 256) {
+    float a = dQtA[(size_t)bh * md + e];
+    for (int ch = 0; ch < nchunks; ++ch) a += pdqt[((size_t)bh * nchunks + ch) * md + e];
+    dQt[(size_t)bh * md + e] = a;
+  }
+}
+
+// dconv_w[h] = sum over batch entries and key chunks (fixed order); grid heads.
+__global__ __launch_bounds__(256) void k_bwd_dw_finish(const float* __restrict__ pdwc, float* __restrict__ dw,
+                                                       int batch, int heads, int nchunks, int dk) {
+  const int h = blockIdx.x;
+  for (int e = threadIdx.x; e < dk; e += 256) {
+    float a = 0.f;
+    for (int b = 0; b < batch; ++b)
+      for (int ch = 0; ch < nchunks; ++ch) a += pdwc[(((size_t)(b * heads + h)) * nchunks + ch) * dk + e];
+    dw[(size_t)h * dk + e] = a;
+  }
+}
+
+static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Chunks per head for the split passes: about two blocks per CU overall.
+static int split_chunks(long long rows, long long bh, int tile) {
+  long long want = (512 + bh - 1) / bh;
+  long long maxc = (rows + tile - 1) / tile;
+  if (want < 1) want = 1;
+  if (want > maxc) want = maxc;
+  return (int)want;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Workspace of the backward pass: the forward's regions, then its own.
+
+bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, BwdLayout* L) {
+  if (!make_layout(batch, heads, n, d, m, &L->fwd)) return false;
+  if (m > 64 || conv_k > 33) return false;
+  const long long BH = (long long)batch * heads;
+  const int tq = split_chunks(n, BH, kRowTile);
+  L->qchunk = cdivi(cdivi(n, tq), kRowTile) * kRowTile;
+  L->nq = cdivi(n, L->qchunk);
+  const int tk = split_chunks(n, BH, kKeyTile);
+  L->kchunk = cdivi(cdivi(n, tk), kKeyTile) * kKeyTile;
+  L->nk = cdivi(n, L->kchunk);
+  L->mp = m <= 32 ? 32 : 64;
+  size_t off = L->fwd.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t md = (size_t)BH * m * d * 4;
+  L->pdw = take(md * L->nq);
+  L->pdkt = take(md * L->nq);
+  L->dw = take(md);
+  L->dbv = take(md);
+  L->dkt = take(md);
+  L->dqta = take(md);
+  L->pdqt = take(md * L->nk);
+  L->dqt = take(md);
+  L->pdwc = take((size_t)BH * L->nk * d * (conv_k > 0 ? conv_k : 1) * 4);
+  L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * L->mp * L->mp * 4);
+  L->total = off;
+  return true;
+}
+
+template <typename IO, int D>
+static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s) {
+  using T = typename IO::T;
+  const Problem& p = bp.fwd;
+  const Ws w = resolve(L.fwd, ws);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  const int BH = p.batch * p.heads;
+  const float sl2e = kLog2e / sqrtf((float)D), scale = 1.f / sqrtf((float)D);
+  constexpr int P = D + 1;
+
+  // Query side, partials of dW and dKt_F.
+  {
+    const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
+    auto kern = &k_bwd_rows<IO, D, false>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess) return attr;
+    KernelTimer kt_("bwd_rows_reduce", s);
+    kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(bp.dO), w.Kt, w.W,
+                                            nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk, L.nq, sl2e,
+                                            scale);
+  }
+  // Landmark side.
+  {
+    hipError_t e;
+    KernelTimer kt_("bwd_landmarks", s);
+    if (L.mp == 32) {
+      auto kern = &k_bwd_land<32, 3>;
+      if (!IO::kBf16) kern = &k_bwd_land<32, 6>;
+      const int bytes = (int)sizeof(LandSmem<32>);
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   bytes)) != hipSuccess)
+        return e;
+      kern<<<BH, 256, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
+                                  F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
+    } else {
+      auto kern = &k_bwd_land<64, 3>;
+      if (!IO::kBf16) kern = &k_bwd_land<64, 6>;
+      const int bytes = (int)sizeof(LandSmem<64>);
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   bytes)) != hipSuccess)
+        return e;
+      kern<<<BH, 256, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
+                                  F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
+    }
+  }
+  // Key side: dK, dV and the partials of dQt_B and the filter gradient.
+  {
+    const int ck = p.conv_w ? p.conv_k : 0;
+    const int bytes = (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 + 3 * 64 + D * (ck > 0 ? ck : 1)) * 4;
+    auto kern = &k_bwd_key<IO, D>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 +
+                                                        3 * 64 + D * 33) * 4);
+    if (attr != hipSuccess) return attr;
+    KernelTimer kt_("bwd_keys", s);
+    kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const T*>(p.K), static_cast<const T*>(p.V),
+                                            static_cast<const T*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv), F(L.dkt),
+                                            w.pmax, w.psum, static_cast<T*>(bp.dK), static_cast<T*>(bp.dV),
+                                            F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads, ck, L.kchunk, L.nk,
+                                            w.nchunks, sl2e, scale);
+  }
+  {
+    KernelTimer kt_("bwd_finish", s);
+    k_bwd_qt_finish<<<BH, 256, 0, s>>>(F(L.dqta), F(L.pdqt), F(L.dqt), p.m * D, L.nk);
+    if (p.conv_w && bp.dconv_w)
+      k_bwd_dw_finish<<<p.heads, 256, 0, s>>>(F(L.pdwc), bp.dconv_w, p.batch, p.heads, L.nk, D * p.conv_k);
+  }
+  // Query side again: dQ.
+  {
+    const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
+    auto kern = &k_bwd_rows<IO, D, true>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess) return attr;
+    const int nt = cdivi(p.n, kRowTile);
+    KernelTimer kt_("bwd_rows_dq", s);
+    kern<<<dim3(nt, BH), 256, bytes, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(bp.dO), w.Kt, w.W,
+                                          F(L.dqt), static_cast<T*>(bp.dQ), nullptr, nullptr, p.n, p.m, kRowTile,
+                                          nt, sl2e, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s) {
+  const Problem& p = bp.fwd;
+  const Ws w = resolve(L.fwd, ws);
+  hipError_t e;
+  // The forward's landmark side: Qt, Kt, A, Z, BV, W and B's statistics.
+  if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
+  if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
+  switch (p.d) {
+    case 16: return p.bf16 ? bwd_t<BF16, 16>(bp, L, ws, s) : bwd_t<F32, 16>(bp, L, ws, s);
+    case 32: return p.bf16 ? bwd_t<BF16, 32>(bp, L, ws, s) : bwd_t<F32, 32>(bp, L, ws, s);
+    case 64: return p.bf16 ? bwd_t<BF16, 64>(bp, L, ws, s) : bwd_t<F32, 64>(bp, L, ws, s);
+    case 128: return p.bf16 ? bwd_t<BF16, 128>(bp, L, ws, s) : bwd_t<F32, 128>(bp, L, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace nys

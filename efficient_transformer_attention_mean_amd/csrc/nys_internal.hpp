@@ -71,6 +71,35 @@ hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      /
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);
+
+// Backward pass: the forward's workspace regions (recomputed landmark side)
+// followed by its own (byte offsets, 256-byte aligned).
+struct BwdLayout {
+  WsLayout fwd;
+  size_t pdw, pdkt;    // fp32 [bh][nq][m][d] query-side partials of dW and dKt
+  size_t dw, dbv;      // fp32 [bh][m][d] dW, dBV
+  size_t dkt, dqta;    // fp32 [bh][m][d] dKt (total), the landmark-side part of dQt
+  size_t pdqt, dqt;    // fp32 [bh][nk][m][d] key-side partials of dQt; dQt (total)
+  size_t pdwc;         // fp32 [bh][nk][d][conv_k] partials of the filter gradient
+  size_t zs;           // fp32 [bh][iters][mp][mp] pseudoinverse iterates Z_0 .. Z_{iters-1}
+  size_t total;
+  int qchunk, nq;      // query rows per block of the reduction pass, blocks per head
+  int kchunk, nk;      // keys per block of the key pass, blocks per head
+  int mp;              // landmarks padded to 32 or 64
+};
+
+// Returns false for shapes the backward kernels do not handle (m > 64,
+// conv_k > 33, or anything the forward rejects).
+bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, BwdLayout* L);
+
+struct BwdProblem {
+  Problem fwd;
+  const void* dO;
+  void *dQ, *dK, *dV;
+  float* dconv_w;  // fp32 [heads][d][conv_k] or nullptr
+};
+
+hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, char* ws, hipStream_t s);
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,
                         int d, int conv_k, bool bf16, hipStream_t s);
 

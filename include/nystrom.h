@@ -130,6 +130,35 @@ int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const f
                             int batch, int conv_k, int dtype, const int* lengths,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass: gradients of nystrom_attn_fwd's output with respect to Q,
+ * K, V and the skip filters, given dO = dL/d(out).  The pages train through
+ * the fixed number of pseudoinverse steps ("Nyströmformer: ...", sec. 3.4,
+ * "Moore-Penrose Pseudoinverse Computation"); this is the exact derivative of
+ * the forward computation described at the top, taken through every step
+ * (segment means with their padding, the three softmaxes, the `iters`
+ * Lemma-1 steps and the Pan-Schreiber start, W = Z (B V), the skip).  The
+ * derivative of each maximum in the start is taken at its first maximiser.
+ * The landmark side of the forward pass is recomputed inside the call.
+ *   Q, K, V, conv_w, n, d, m, heads, iters, batch, conv_k, dtype: as for
+ *               nystrom_attn_fwd (the same values as the forward call)
+ *   dO          [batch][heads][n][d] of `dtype`, the upstream gradient
+ *   dQ, dK, dV  outputs, [batch][heads][n][d] of `dtype`, written (not
+ *               accumulated); must not alias any input
+ *   dconv_w     fp32 [heads][d][conv_k], written with the filter gradient
+ *               summed over the batch, or NULL to skip it; ignored when
+ *               conv_w is NULL
+ *   workspace   device buffer of at least nystrom_attn_bwd_workspace_bytes(),
+ *               or NULL (allocated and freed in stream order)
+ * Supported: m <= 64 and conv_k <= 33 (NYS_EUNSUPPORTED otherwise), every d
+ * and n of the forward.  Return codes and stream behaviour as for
+ * nystrom_attn_fwd. */
+size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k);
+int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
+                     int n, int d, int m, int heads, int iters,
+                     void* dQ, void* dK, void* dV, float* dconv_w,
+                     int batch, int conv_k, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Depthwise-convolution skip alone: out = DConv(V) with the filters and
  * padding described at the top ("Putting It Together", Figure 4's DConv path).
  *   V, out      [batch][heads][n][d] of `dtype` (out must not alias V)

@@ -1,0 +1,104 @@
+"""Parity of the HIP backward pass (through the C ABI) against the fp64 CPU
+oracle of the gradients (itself pinned by finite differences).
+
+Bars (relative L2 over each whole gradient tensor): 1e-4 for fp32 I/O and
+2e-2 for bf16 I/O, the forward's output bars.  The bf16 path inherits the
+forward's single-bf16 landmark-side products (B's row statistics and BV,
+about 2^-9 relative) and rounds every gradient to bf16 (2^-9 relative), so
+its error is of the order 1e-3; the fp32 path runs its n-sized passes in
+fp32 and the pseudoinverse backward with three-way split products."""
+import numpy as np
+import pytest
+import torch
+
+from efficient_transformer_attention_mean_amd import _lib
+from efficient_transformer_attention_mean_amd.workloads import WORKLOADS, make_inputs, round_to_bf16
+from oracle import nystrom_attention_backward
+
+from ._gpu_util import dtype_code, rel_l2, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def upstream(wl, seed):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((wl.batch, wl.heads, wl.n, wl.d)).astype(np.float32)
+    return round_to_bf16(g) if wl.dtype == "bf16" else g
+
+
+def run_backward(inp, dO, m, iters, dtype, use_conv=True, own_workspace=True, want_dw=True):
+    Q, K, V, G = (to_dev(x, dtype) for x in (inp["Q"], inp["K"], inp["V"], dO))
+    B, H, n, d = inp["Q"].shape
+    w = inp["conv_w"] if use_conv else None
+    wdev = None if w is None else torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    conv_k = 0 if w is None else w.shape[2]
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    dW = None if (w is None or not want_dw) else torch.full_like(wdev, 7.0)
+    ws, nbytes = None, 0
+    if own_workspace:
+        nbytes = _lib.nystrom_attn_bwd_workspace_bytes(B, H, n, d, m, iters, conv_k)
+        assert nbytes > 0
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rc = _lib.nystrom_attn_bwd(Q, K, V, wdev, G, n, d, m, H, iters, dQ, dK, dV, dW, B, conv_k, dtype_code(dtype),
+                               ws, nbytes, torch.cuda.current_stream())
+    assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+    torch.cuda.synchronize()
+    return to_host(dQ), to_host(dK), to_host(dV), None if dW is None else dW.cpu().numpy()
+
+
+CASES = [
+    # (batch, heads, n, d, m, iters, conv_k, dtype)
+    (1, 1, 64, 16, 8, 6, 3, "f32"),
+    (2, 2, 100, 16, 10, 6, 5, "bf16"),      # ragged n: padded segments
+    (1, 2, 256, 32, 32, 6, 33, "f32"),
+    (2, 2, 1000, 64, 64, 6, 33, "bf16"),    # one segment of pad only
+    (1, 1, 96, 128, 16, 6, 0, "f32"),       # d = 128, no skip
+    (1, 2, 512, 64, 64, 0, 9, "f32"),       # iters = 0: the start only
+    (1, 1, 64, 32, 64, 8, 3, "f32"),        # m = n
+    (2, 12, 512, 64, 64, 6, 33, "f32"),     # BERT-base-shaped layer
+    (1, 3, 777, 32, 48, 6, 33, "bf16"),     # m = 48 (padded to 64), ragged
+    (2, 12, 8192, 64, 64, 6, 33, "bf16"),   # headline shape
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}m{c[4]}it{c[5]}k{c[6]}{c[7]}"
+                                             for c in CASES])
+def test_backward_parity(case):
+    B, H, n, d, m, iters, k, dt = case
+    wl = WORKLOADS["tiny"].with_(name=f"bwd{case}", batch=B, heads=H, n=n, d=d, m=m, iters=iters, conv_k=k,
+                                 dtype=dt, seed=300 + n + m)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 900 + n)
+    ref = nystrom_attention_backward(inp["Q"], inp["K"], inp["V"], m, iters, dO, inp["conv_w"])
+    got = run_backward(inp, dO, m, iters, dt, use_conv=k > 0)
+    names = ("dQ", "dK", "dV", "dconv_w")
+    errs = {nm: rel_l2(g, r) for nm, g, r in zip(names, got, ref) if r is not None}
+    print(f"backward {case}: " + ", ".join(f"{kk}={v:.2e}" for kk, v in errs.items()))
+    for nm, e in errs.items():
+        assert e <= TOL[dt], (nm, errs)
+
+
+def test_backward_deterministic_and_workspace_forms():
+    wl = WORKLOADS["long"].with_(name="bwd_det", batch=1, heads=3, n=1500)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 5)
+    a = run_backward(inp, dO, wl.m, wl.iters, wl.dtype)
+    b = run_backward(inp, dO, wl.m, wl.iters, wl.dtype, own_workspace=False)
+    c = run_backward(inp, dO, wl.m, wl.iters, wl.dtype, want_dw=False)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for x, y in zip(a[:3], c[:3]):
+        assert np.array_equal(x, y)
+    assert c[3] is None
+
+
+def test_backward_rejects_unsupported():
+    Q = torch.zeros(1, 1, 128, 16, device="cuda")
+    out = torch.empty_like(Q)
+    # m > 64 is outside the backward kernels; the forward accepts it.
+    rc = _lib.nystrom_attn_bwd(Q, Q, Q, None, Q, 128, 16, 80, 1, 6, out, out, out, None, 1, 0, _lib.NYS_F32,
+                               None, 0, None)
+    assert rc == _lib.NYS_EUNSUPPORTED
+    assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 128, 16, 80, 6, 0) == 0
