@@ -35,6 +35,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # fp32 vector ALUs, TFLOP/s
 METRIC = "Nyström attention fwd tokens/s at n=8192,m=64,d=64; % of HBM roofline"
 
 # Context from the paper's efficiency table (GTX 1080Ti, self-attention module
@@ -62,6 +63,20 @@ def algorithmic_bytes(wl, kernel: str, token_rows=None) -> int:
     if kernel == "apply":
         return (2 * rows + all_rows) * row + convw  # read Q, V (token rows); write every row of O
     return 0
+
+
+def backward_flops(wl, kernel: str) -> float:
+    """fp32 vector flops each backward kernel performs per launch (2 per
+    multiply-add; per-row figure x rows over all heads)."""
+    rows = float(wl.batch * wl.heads * wl.n)
+    md, kd = wl.m * wl.d, wl.conv_k * wl.d
+    if kernel == "bwd_rows_reduce":
+        return rows * 2 * 4 * md           # scores, dO W^T, F^T dO, dS^T Q
+    if kernel == "bwd_keys":
+        return rows * 2 * (5 * md + 2 * kd)  # scores, dBV V^T, dS^T Qt, B^T dBV, dS K; skip transpose, filter gradient
+    if kernel == "bwd_rows_dq":
+        return rows * 2 * 3 * md           # scores, dO W^T, dS Kt
+    return 0.0
 
 
 def pinv_flops(wl) -> float:
@@ -92,6 +107,8 @@ def main() -> int:
     ap.add_argument("--lengths", default=None,
                     help="tokens of each batch entry, comma-separated: a batch of right-padded sequences "
                          "(key-padding mask, nystrom_attn_fwd_masked); value then counts real tokens")
+    ap.add_argument("--backward", action="store_true",
+                    help="time nystrom_attn_bwd (gradients of Q, K, V and the filters) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -109,6 +126,8 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.backward:
+        return backward_bench(args, wl, dev)
     lengths = None
     eff = [wl.n] * wl.batch
     if args.lengths:
@@ -288,6 +307,141 @@ def main() -> int:
             result["nystrom_vs_exact_attention_rel_l2_sampled_rows"] = float(
                 np.linalg.norm(att - ex) / np.linalg.norm(ex))
     result["pages_context"] = PAGES_CONTEXT
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def backward_bench(args, wl, dev) -> int:
+    """One step = one nystrom_attn_bwd call over the workload (the landmark
+    side of the forward is recomputed inside it)."""
+    import torch
+    from efficient_transformer_attention_mean_amd import _lib
+    from efficient_transformer_attention_mean_amd.workloads import bf16_bits, bf16_bits_to_f32, make_inputs, \
+        round_to_bf16
+
+    e = wl.elem_bytes
+    io_bytes = 7 * wl.batch * wl.heads * wl.n * wl.d * e + (8 * wl.heads * wl.d * wl.conv_k if wl.conv_k else 0)
+    sets = args.sets or max(2, int(np.ceil(512 * 2 ** 20 / io_bytes)) + 1)
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    def upstream(seed):
+        g = np.random.default_rng(seed).standard_normal((wl.batch, wl.heads, wl.n, wl.d)).astype(np.float32)
+        return round_to_bf16(g) if wl.dtype == "bf16" else g
+
+    host0, g0 = None, None
+    bufs = []
+    for i in range(sets):
+        inp = make_inputs(wl, seed=wl.seed + 1000 * i)
+        g = upstream(wl.seed + 1000 * i + 1)
+        if i == 0:
+            host0, g0 = inp, g
+        Q, K, V, G = (to_dev(x) for x in (inp["Q"], inp["K"], inp["V"], g))
+        W = None if inp["conv_w"] is None else torch.from_numpy(inp["conv_w"]).to(dev)
+        dW = None if W is None else torch.empty_like(W)
+        bufs.append((Q, K, V, G, W, torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V), dW))
+    conv_k = wl.conv_k if wl.conv_k else 0
+    ws_bytes = _lib.nystrom_attn_bwd_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m, wl.iters, conv_k)
+    if ws_bytes == 0:
+        print(f"workload {wl.name} is outside the backward kernels (m <= 64, conv_k <= 33)", file=sys.stderr)
+        return 2
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    code = _lib.NYS_BF16 if wl.dtype == "bf16" else _lib.NYS_F32
+
+    def step(i):
+        Q, K, V, G, W, dQ, dK, dV, dW = bufs[i % sets]
+        rc = _lib.nystrom_attn_bwd(Q, K, V, W, G, wl.n, wl.d, wl.m, wl.heads, wl.iters, dQ, dK, dV, dW, wl.batch,
+                                   conv_k, code, ws, ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    print(f"[bench] backward workload={wl.name} sets={sets} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    ms_per_step = 1e3 * gpu_s / args.steps
+    tokens = wl.batch * wl.n
+    value = tokens * args.steps / gpu_s
+
+    _lib.nystrom_timing_enable(True)
+    _lib.nystrom_timing_read()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = _lib.nystrom_timing_read()
+    _lib.nystrom_timing_enable(False)
+    per_kernel = {name: {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                         "avg_us_per_launch": 1e3 * ms / max(n, 1)} for name, (ms, n) in kern.items()}
+    dom = max(kern.items(), key=lambda kv: kv[1][0])[0] if kern else None
+    roof = None
+    if dom is not None:
+        ms, launches = kern[dom]
+        avg_s = ms / launches / 1e3
+        fl = backward_flops(wl, dom)
+        if fl:
+            achieved = fl / avg_s / 1e12
+            roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": dom, "algorithmic_flops": fl, "avg_us": round(avg_s * 1e6, 3)}
+        else:
+            roof = {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None,
+                    "traffic": None, "kernel": dom, "avg_us": round(avg_s * 1e6, 3)}
+
+    result = {
+        "metric": "Nyström attention bwd tokens/s (gradients of Q, K, V and the filters)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "backward", "batch": wl.batch, "heads": wl.heads, "n": wl.n,
+                   "d": wl.d, "m": wl.m, "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype,
+                   "input_sets": sets},
+        "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
+        "compulsory_bytes": io_bytes, "wall_s": round(wall, 4), "roofline": roof, "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline or not args.no_parity:
+        from oracle import nystrom_attention_backward
+        threads = blas_threads()
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            ref = nystrom_attention_backward(host0["Q"], host0["K"], host0["V"], wl.m, wl.iters, g0,
+                                             host0["conv_w"])
+            reps += 1
+            if args.no_cpu_baseline or time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - c0
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {
+                "value": round(tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{reps} whole backward call(s) of the workload (batch {wl.batch} x {wl.heads} heads, "
+                          f"n={wl.n}), fp64 NumPy, {cpu_s:.1f} s, host has {os.cpu_count()} logical CPUs"}
+        if not args.no_parity:
+            step(0)
+            torch.cuda.synchronize()
+            Q, K, V, G, W, dQ, dK, dV, dW = bufs[0]
+
+            def host(t):
+                if t.dtype == torch.bfloat16:
+                    return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+                return t.float().cpu().numpy()
+            got = (host(dQ), host(dK), host(dV), None if dW is None else dW.cpu().numpy())
+            result["parity_rel_l2_vs_oracle"] = {
+                nm: float(np.linalg.norm(g - r) / np.linalg.norm(r))
+                for nm, g, r in zip(("dQ", "dK", "dV", "dconv_w"), got, ref) if r is not None}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const typename IO::T* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Landmark side, one block per head (256 threads, m <= MP <= 64, matrices in
+// Landmark side, one block per head (one wave per 16 x 16 tile of an MP x MP
+// matrix: 1024 threads for MP = 64, 256 for MP = 32; m <= MP, matrices in
 // LDS with pitch MP + 4).
 
 template <int MP>
@@ -187,7 +188,7 @@ struct LandSmem {
   static constexpr int LP = MP + 4;
   float A[MP][LP], dA[MP][LP], dZ[MP][LP], T2[MP][LP], Zk[MP][LP], X[MP][LP], T1[MP][LP], dT2[MP][LP],
       dX[MP][LP];
-  float col[MP], row[MP], red[8];
+  float col[MP], row[MP], red[16];
 };
 
 // C = op(P) op(Q) on MP x MP LDS matrices (pitch MP + 4), where op(P) =
@@ -197,7 +198,7 @@ struct LandSmem {
 // v) receives them.
 template <int MP>
 struct LandTiles {
-  static constexpr int NT = MP / 16, PER = NT * NT / 4;  // tiles per wave
+  static constexpr int NT = MP / 16, NW = NT * NT, NTH = 64 * NW, PER = 1;  // one tile per wave
 };
 
 template <int MP, int PR, bool TPa, bool TQa, typename Epi>
@@ -208,11 +209,11 @@ __device__ __forceinline__ void land_mm(const float (*Pm)[MP + 4], float pa, flo
   constexpr int NT = LandTiles<MP>::NT;
 #pragma unroll
   for (int q = 0; q < LandTiles<MP>::PER; ++q) {
-    const int t = wave + 4 * q;
+    const int t = wave + LandTiles<MP>::NW * q;
     const int ti = t / NT, tj = t % NT;
     const int i = ti * 16 + c, j = tj * 16 + c;
     f32x4_t acc = zero4();
-#pragma unroll
+#pragma unroll 1
     for (int kc = 0; kc < MP; kc += 32) {
       float a[8], b[8];
 #pragma unroll
@@ -237,7 +238,7 @@ __device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&k
   constexpr int NT = LandTiles<MP>::NT;
 #pragma unroll
   for (int q = 0; q < LandTiles<MP>::PER; ++q) {
-    const int t = wave + 4 * q;
+    const int t = wave + LandTiles<MP>::NW * q;
     const int r0 = (t / NT) * 16 + 4 * g, cc = (t % NT) * 16 + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) M[r0 + i][cc] = keep[q][i];
@@ -245,7 +246,7 @@ __device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&k
 }
 
 template <int MP, int PR>
-__global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, const float* __restrict__ Kt,
+__global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(const float* __restrict__ Qt, const float* __restrict__ Kt,
                                                   const float* __restrict__ Aw, const float* __restrict__ Zw,
                                                   const float* __restrict__ BV, const float* __restrict__ pdw,
                                                   const float* __restrict__ pdkt, float* __restrict__ dWg,
@@ -255,11 +256,12 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
   using Mat = float (*)[MP + 4];
+  constexpr int NTH = LandTiles<MP>::NTH;
   const int bh = blockIdx.x, tid = threadIdx.x;
   const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m;
 
   // dW and dKt_F: fixed-order sums of the query-side partials.
-  for (int e = tid; e < m * D; e += 256) {
+  for (int e = tid; e < m * D; e += NTH) {
     float a = 0.f, b = 0.f;
     for (int ch = 0; ch < nchunks; ++ch) {
       const size_t o = ((size_t)bh * nchunks + ch) * m * D + e;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
     dKt[md + e] = b;
   }
   // A (zero padded) and the final iterate Z.
-  for (int e = tid; e < MP * MP; e += 256) {
+  for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     const bool in = i < m && j < m;
     sm.A[i][j] = in ? Aw[mm + i * m + j] : 0.f;
@@ -278,19 +280,45 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
   }
   __syncthreads();
 
-  // dZ = dW BV^T and dBV = Z^T dW (fp32, contraction over d / m).
-  for (int e = tid; e < MP * MP; e += 256) {
-    const int i = e / MP, j = e % MP;
-    float a = 0.f;
-    if (i < m && j < m)
-      for (int c = 0; c < D; ++c) a = fmaf(dWg[md + (size_t)i * D + c], BV[md + (size_t)j * D + c], a);
-    sm.dZ[i][j] = a;
-  }
-  for (int e = tid; e < m * D; e += 256) {
-    const int j = e / D, c = e % D;
-    float a = 0.f;
-    for (int i = 0; i < m; ++i) a = fmaf(sm.X[i][j], dWg[md + (size_t)i * D + c], a);
-    dBV[md + e] = a;
+  // dZ = dW BV^T and dBV = Z^T dW (fp32), over 32-feature slices staged in
+  // LDS (the T1 and dT2 slots are free until the iterates): T1[i][cc] =
+  // dW[i][c0 + cc], dT2[cc][j] = BV[j][c0 + cc].
+  {
+    constexpr int NZ = MP * MP / NTH;
+    float zacc[NZ];
+#pragma unroll
+    for (int q = 0; q < NZ; ++q) zacc[q] = 0.f;
+    for (int c0 = 0; c0 < D; c0 += 32) {
+      for (int e = tid; e < MP * 32; e += NTH) {
+        const int i = e / 32, cc = e % 32;
+        const bool in = i < m && c0 + cc < D;
+        sm.T1[i][cc] = in ? dWg[md + (size_t)i * D + c0 + cc] : 0.f;
+        sm.dT2[cc][i] = in ? BV[md + (size_t)i * D + c0 + cc] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < NZ; ++q) {
+        const int e = tid + NTH * q, i = e / MP, j = e % MP;
+        float a = zacc[q];
+#pragma unroll 4
+        for (int cc = 0; cc < 32; ++cc) a = fmaf(sm.T1[i][cc], sm.dT2[cc][j], a);
+        zacc[q] = a;
+      }
+      for (int e = tid; e < m * 32; e += NTH) {
+        const int j = e / 32, cc = e % 32;
+        if (c0 + cc < D) {
+          float a = 0.f;
+          for (int i = 0; i < m; ++i) a = fmaf(sm.X[i][j], sm.T1[i][cc], a);
+          dBV[md + (size_t)j * D + c0 + cc] = a;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < NZ; ++q) {
+      const int e = tid + NTH * q;
+      sm.dZ[e / MP][e % MP] = zacc[q];
+    }
   }
 
   // Start Z0 = c A^T; column and row sums of A (entries are positive).
@@ -315,7 +343,7 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
   }
   const float cz = 1.f / (n1 * ninf);
   float* zsh = zs + (size_t)bh * iters * MP * MP;
-  for (int e = tid; e < MP * MP; e += 256) {
+  for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     sm.Zk[i][j] = cz * sm.A[j][i];
   }
@@ -323,7 +351,7 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
 
   // Forward iterates Z_0 .. Z_{iters-1} -> zs (Z_k in sm.Zk at step k).
   for (int k = 0; k < iters; ++k) {
-    for (int e = tid; e < MP * MP; e += 256) zsh[(size_t)k * MP * MP + e] = sm.Zk[e / MP][e % MP];
+    for (int e = tid; e < MP * MP; e += NTH) zsh[(size_t)k * MP * MP + e] = sm.Zk[e / MP][e % MP];
     if (k + 1 == iters) break;
     land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
@@ -341,16 +369,16 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
       for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
     });
     __syncthreads();
-    for (int e = tid; e < MP * MP; e += 256) sm.Zk[e / MP][e % MP] = sm.dT2[e / MP][e % MP];
+    for (int e = tid; e < MP * MP; e += NTH) sm.Zk[e / MP][e % MP] = sm.dT2[e / MP][e % MP];
     __syncthreads();
   }
-  for (int e = tid; e < MP * MP; e += 256) sm.dA[e / MP][e % MP] = 0.f;
+  for (int e = tid; e < MP * MP; e += NTH) sm.dA[e / MP][e % MP] = 0.f;
   __syncthreads();
 
   // Reverse through the steps.  Mat pointers let dZ and T2 trade places.
   Mat dZ = sm.dZ, T2 = sm.T2;
   for (int k = iters - 1; k >= 0; --k) {
-    for (int e = tid; e < MP * MP; e += 256) sm.Zk[e / MP][e % MP] = zsh[(size_t)k * MP * MP + e];
+    for (int e = tid; e < MP * MP; e += NTH) sm.Zk[e / MP][e % MP] = zsh[(size_t)k * MP * MP + e];
     __syncthreads();
     land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
@@ -419,7 +447,7 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
   // jstar.  The ninf term is constant along a row and cancels in the softmax
   // backward below, so it is left out.
   float part = 0.f;
-  for (int e = tid; e < MP * MP; e += 256) {
+  for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     part = fmaf(dZ[i][j], sm.A[j][i], part);
   }
@@ -427,8 +455,9 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
   for (int o = 1; o < 64; o <<= 1) part += shfl_xor(part, o);
   if ((tid & 63) == 0) sm.red[tid >> 6] = part;
   __syncthreads();
-  const float dcz = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
-  for (int e = tid; e < MP * MP; e += 256) {
+  float dcz = 0.f;
+  for (int w = 0; w < LandTiles<MP>::NW; ++w) dcz += sm.red[w];
+  for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     if (i < m && j < m) sm.dA[i][j] += cz * dZ[j][i] + (j == jstar ? -dcz * cz / n1 : 0.f);
   }
@@ -440,21 +469,35 @@ __global__ __launch_bounds__(256) void k_bwd_land(const float* __restrict__ Qt, 
     sm.row[tid] = s;
   }
   __syncthreads();
-  for (int e = tid; e < MP * MP; e += 256) {
+  for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     sm.dA[i][j] = sm.A[i][j] * (sm.dA[i][j] - sm.row[i]);
   }
   __syncthreads();
-  // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt.
-  for (int e = tid; e < m * D; e += 256) {
-    const int j = e / D, c = e % D;
-    float a = 0.f, b = 0.f;
-    for (int k = 0; k < m; ++k) {
-      a = fmaf(sm.dA[j][k], Kt[md + (size_t)k * D + c], a);
-      b = fmaf(sm.dA[k][j], Qt[md + (size_t)k * D + c], b);
+  // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt, over 32-feature slices of Kt
+  // and Qt staged in the T1 and dT2 slots.
+  for (int c0 = 0; c0 < D; c0 += 32) {
+    for (int e = tid; e < MP * 32; e += NTH) {
+      const int k = e / 32, cc = e % 32;
+      const bool in = k < m && c0 + cc < D;
+      sm.T1[k][cc] = in ? Kt[md + (size_t)k * D + c0 + cc] : 0.f;
+      sm.dT2[k][cc] = in ? Qt[md + (size_t)k * D + c0 + cc] : 0.f;
     }
-    dQtA[md + e] = scale * a;
-    dKt[md + e] += scale * b;
+    __syncthreads();
+    for (int e = tid; e < m * 32; e += NTH) {
+      const int j = e / 32, cc = e % 32;
+      if (c0 + cc < D) {
+        float a = 0.f, b = 0.f;
+        for (int k = 0; k < m; ++k) {
+          a = fmaf(sm.dA[j][k], sm.T1[k][cc], a);
+          b = fmaf(sm.dA[k][j], sm.dT2[k][cc], b);
+        }
+        const size_t o = md + (size_t)j * D + c0 + cc;
+        dQtA[o] = scale * a;
+        dKt[o] += scale * b;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -620,27 +663,27 @@ __global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restric
   }
 }
 
-// dQt = dQt_A + sum of the key-side partials (chunk order); grid batch*heads.
+// dQt = dQt_A + sum of the key-side partials (chunk order); grid
+// (entries / 256, batch*heads), one entry per thread.
 __global__ __launch_bounds__(256) void k_bwd_qt_finish(const float* __restrict__ dQtA, const float* __restrict__ pdqt,
                                                        float* __restrict__ dQt, int md, int nchunks) {
-  const int bh = blockIdx.x;
-  for (int e = threadIdx.x; e < md; e += 256) {
-    float a = dQtA[(size_t)bh * md + e];
-    for (int ch = 0; ch < nchunks; ++ch) a += pdqt[((size_t)bh * nchunks + ch) * md + e];
-    dQt[(size_t)bh * md + e] = a;
-  }
+  const int bh = blockIdx.y, e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= md) return;
+  float a = dQtA[(size_t)bh * md + e];
+  for (int ch = 0; ch < nchunks; ++ch) a += pdqt[((size_t)bh * nchunks + ch) * md + e];
+  dQt[(size_t)bh * md + e] = a;
 }
 
-// dconv_w[h] = sum over batch entries and key chunks (fixed order); grid heads.
+// dconv_w[h] = sum over batch entries and key chunks (fixed order); grid
+// (entries / 256, heads).
 __global__ __launch_bounds__(256) void k_bwd_dw_finish(const float* __restrict__ pdwc, float* __restrict__ dw,
                                                        int batch, int heads, int nchunks, int dk) {
-  const int h = blockIdx.x;
-  for (int e = threadIdx.x; e < dk; e += 256) {
-    float a = 0.f;
-    for (int b = 0; b < batch; ++b)
-      for (int ch = 0; ch < nchunks; ++ch) a += pdwc[(((size_t)(b * heads + h)) * nchunks + ch) * dk + e];
-    dw[(size_t)h * dk + e] = a;
-  }
+  const int h = blockIdx.y, e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= dk) return;
+  float a = 0.f;
+  for (int b = 0; b < batch; ++b)
+    for (int ch = 0; ch < nchunks; ++ch) a += pdwc[(((size_t)(b * heads + h)) * nchunks + ch) * dk + e];
+  dw[(size_t)h * dk + e] = a;
 }
 
 static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -724,7 +767,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
       if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                    bytes)) != hipSuccess)
         return e;
-      kern<<<BH, 256, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
+      kern<<<BH, LandTiles<32>::NTH, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
                                   F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
     } else {
       auto kern = &k_bwd_land<64, 3>;
@@ -733,7 +776,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
       if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                    bytes)) != hipSuccess)
         return e;
-      kern<<<BH, 256, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
+      kern<<<BH, LandTiles<64>::NTH, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
                                   F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
     }
   }
@@ -756,9 +799,10 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   }
   {
     KernelTimer kt_("bwd_finish", s);
-    k_bwd_qt_finish<<<BH, 256, 0, s>>>(F(L.dqta), F(L.pdqt), F(L.dqt), p.m * D, L.nk);
+    k_bwd_qt_finish<<<dim3(cdivi(p.m * D, 256), BH), 256, 0, s>>>(F(L.dqta), F(L.pdqt), F(L.dqt), p.m * D, L.nk);
     if (p.conv_w && bp.dconv_w)
-      k_bwd_dw_finish<<<p.heads, 256, 0, s>>>(F(L.pdwc), bp.dconv_w, p.batch, p.heads, L.nk, D * p.conv_k);
+      k_bwd_dw_finish<<<dim3(cdivi(D * p.conv_k, 256), p.heads), 256, 0, s>>>(F(L.pdwc), bp.dconv_w, p.batch,
+                                                                               p.heads, L.nk, D * p.conv_k);
   }
   // Query side again: dQ.
   {
