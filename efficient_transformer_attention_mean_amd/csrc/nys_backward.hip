@@ -663,6 +663,402 @@ __global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core versions of the n-sized passes for bf16 I/O at d = 32 or 64
+// (single bf16 products with fp32 accumulation, as in the forward's output
+// stage).  Matrix-core convention of nys_common.hpp: lane (c, g) holds
+// A[c][8g..8g+7], B[8g..8g+7][c] and C[4g..4g+3][c].  Score-type products
+// are computed transposed (landmarks x rows) so that a lane holds 16
+// landmarks of one row; such a C tile is the B operand of the next product
+// when the landmark axis is taken, within each chunk of 32, in the order
+// {4g..4g+3, 16+4g..16+4g+3}; the A operands of those products are stored
+// in LDS in that order (mm_slot).
+
+constexpr int kMmTile = 64;  // rows (keys or queries) per tile, 16 per wave
+
+// Position of landmark j in the permuted order of its chunk of 32.
+__device__ __forceinline__ int mm_slot(int j) {
+  const int jj = j & 31;
+  return (j & ~31) + 8 * ((jj & 15) >> 2) + (jj & 3) + ((jj & 16) ? 4 : 0);
+}
+
+__device__ __forceinline__ uint16_t bf(float x) { return f32_to_bf16(x); }
+
+__device__ __forceinline__ B8 lds8(const uint16_t* p) {
+  B8 b;
+  b.q = *reinterpret_cast<const uint4*>(p);
+  return b;
+}
+
+// C-layout values of landmark tiles 2kk and 2kk+1 as a B operand.
+__device__ __forceinline__ B8 pack_b(const f32x4_t& lo, const f32x4_t& hi) {
+  B8 b;
+  b.u[0] = pack_bf16x2(lo[0], lo[1]);
+  b.u[1] = pack_bf16x2(lo[2], lo[3]);
+  b.u[2] = pack_bf16x2(hi[0], hi[1]);
+  b.u[3] = pack_bf16x2(hi[2], hi[3]);
+  return b;
+}
+
+template <int D>
+struct KeyMmSmem {
+  static constexpr int PD = D + 8, PK = 64 + 8, HR = kMmTile + 32;
+  uint16_t qa[64][PD];   // Qt * log2(e)/sqrt(d), landmark rows (A of the scores)
+  uint16_t da[64][PD];   // dBV rows (A of dB)
+  uint16_t qT[D][PK];    // Qt^T, landmarks in mm_slot order (A of dK^T)
+  uint16_t dT[D][PK];    // dBV^T, mm_slot order (A of dV^T)
+  uint16_t kr[kMmTile][PD];  // key rows of the tile
+  uint16_t kT[D][PK];        // the same transposed (B of dQt)
+  uint16_t vh[HR][PD];       // V rows with the skip halo
+  uint16_t gh[HR][PD];       // dO rows with the skip halo
+  uint16_t sT[64][PK];       // dS^T of the tile (A of dQt)
+  float stm[64], stl[64], dlt[64];
+  float wsh[D * 33];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                    const uint16_t* __restrict__ dO, const float* __restrict__ conv_w,
+                                                    const float* __restrict__ Qt, const float* __restrict__ BV,
+                                                    const float* __restrict__ dBVg, const float* __restrict__ dKt,
+                                                    const float* __restrict__ pmax, const float* __restrict__ psum,
+                                                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                                    float* __restrict__ pdqt, float* __restrict__ pdwc, int n, int m,
+                                                    int heads, int conv_k, int chunk, int nchunks, int fchunks,
+                                                    float sl2e, float scale) {
+  using SM = KeyMmSmem<D>;
+  constexpr int KC = D / 32, ND = D / 16, PER = ND;  // dQt tiles per wave: 4 * ND / 4
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
+  const size_t hoff = (size_t)bh * n * D, md = (size_t)bh * m * D;
+  const int R = conv_k > 0 ? (conv_k - 1) / 2 : 0;
+
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int j = e / D, f = e % D;
+    const float q = j < m ? Qt[md + e] : 0.f, db = j < m ? dBVg[md + e] : 0.f;
+    sm.qa[j][f] = bf(q * sl2e);
+    sm.da[j][f] = bf(db);
+    sm.qT[f][mm_slot(j)] = bf(q);
+    sm.dT[f][mm_slot(j)] = bf(db);
+  }
+  for (int e = tid; e < D * conv_k; e += 256) sm.wsh[e] = conv_w[(size_t)h * D * conv_k + e];
+  if (tid < 64) {
+    const int j = tid;
+    float M = -INFINITY, L = 0.f, dl = 0.f;
+    if (j < m) {
+      for (int q = 0; q < fchunks; ++q) M = fmaxf(M, pmax[((size_t)bh * fchunks + q) * m + j]);
+      for (int q = 0; q < fchunks; ++q) {
+        const float pm = pmax[((size_t)bh * fchunks + q) * m + j];
+        if (pm != -INFINITY) L += psum[((size_t)bh * fchunks + q) * m + j] * exp2f(pm - M);
+      }
+      for (int f = 0; f < D; ++f) dl = fmaf(dBVg[md + (size_t)j * D + f], BV[md + (size_t)j * D + f], dl);
+    }
+    sm.stm[j] = j < m ? M : 0.f;
+    sm.stl[j] = j < m ? 1.f / L : 0.f;
+    sm.dlt[j] = dl;
+  }
+  f32x4_t aq[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) aq[u] = zero4();
+  constexpr int NTB = 5;  // taps in groups of 8 (conv_k <= 33)
+  float awc[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) awc[a][u] = 0.f;
+  const int seg = (n + m - 1) / m;
+  const float inv_seg = 1.f / (float)seg;
+
+  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
+    __syncthreads();
+    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
+      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, key = i0 + rr;
+      B8 v;
+      v.q = key < kend ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.kr[rr][c8]) = v.q;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) sm.kT[c8 + q][rr] = v.h[q];
+    }
+    for (int e = tid; e < (kMmTile + 2 * R) * (D / 8); e += 256) {
+      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 - R + rr;
+      const bool in = row >= 0 && row < n;
+      *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) =
+          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) =
+          in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+
+    // Scores S'^T and dB^T for this wave's 16 keys (key = i0 + 16 wave + c).
+    const int kl = 16 * wave + c, key = i0 + kl;
+    const bool live = key < kend;
+    f32x4_t pb[4], ds[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4_t s = zero4(), db = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const B8 kb = lds8(&sm.kr[kl][kc * 32 + 8 * g]);
+        const B8 vb = lds8(&sm.vh[R + kl][kc * 32 + 8 * g]);
+        s = mfma(lds8(&sm.qa[mt * 16 + c][kc * 32 + 8 * g]), kb, s);
+        db = mfma(lds8(&sm.da[mt * 16 + c][kc * 32 + 8 * g]), vb, db);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = mt * 16 + 4 * g + i;
+        const float b = (live && j < m) ? exp2f(s[i] - sm.stm[j]) * sm.stl[j] : 0.f;
+        pb[mt][i] = b;
+        ds[mt][i] = b * (db[i] - sm.dlt[j]);
+      }
+    }
+    // dK^T = Qt^T dS^T and dV^T = dBV^T B^T (+ the skip transpose).
+    const float* dkt = dKt + md + (size_t)min(key / seg, m - 1) * D;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) {
+      f32x4_t ak = zero4(), av = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        ak = mfma(lds8(&sm.qT[nd * 16 + c][kk * 32 + 8 * g]), pack_b(ds[2 * kk], ds[2 * kk + 1]), ak);
+        av = mfma(lds8(&sm.dT[nd * 16 + c][kk * 32 + 8 * g]), pack_b(pb[2 * kk], pb[2 * kk + 1]), av);
+      }
+      if (live) {
+        const int f0 = nd * 16 + 4 * g;
+        const float4 kt4 = *reinterpret_cast<const float4*>(dkt + f0);
+        const float ktv[4] = {kt4.x, kt4.y, kt4.z, kt4.w};
+        float vk[4], vv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vk[i] = fmaf(scale, ak[i], ktv[i] * inv_seg);
+          float acc = av[i];
+          for (int t = 0; t < conv_k; ++t)
+            acc = fmaf(sm.wsh[(f0 + i) * conv_k + t], bf16_to_f32(sm.gh[kl - t + 2 * R][f0 + i]), acc);
+          vv[i] = acc;
+        }
+        *reinterpret_cast<uint2*>(dK + hoff + (size_t)key * D + f0) =
+            make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
+        *reinterpret_cast<uint2*>(dV + hoff + (size_t)key * D + f0) =
+            make_uint2(pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3]));
+      }
+    }
+    // dS^T of the tile -> LDS, then dQt_B += dS^T K over the tile's keys.
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.sT[mt * 16 + 4 * g + i][kl] = bf(ds[mt][i]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+        aq[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.kT[nd * 16 + c][kc * 32 + 8 * g]), aq[u]);
+    }
+    // Filter gradient: item (f, tap group tb), taps 8 tb + u.
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int item = tid + 256 * a;
+      if (item < D * NTB) {
+        const int f = item % D, t0 = 8 * (item / D);
+        if (t0 < conv_k) {
+          const int rows = min(kMmTile, kend - i0);
+          for (int r = 0; r < rows; ++r) {
+            const float gv = bf16_to_f32(sm.gh[R + r][f]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, bf16_to_f32(sm.vh[min(r + t0 + u, SM::HR - 1)][f]), awc[a][u]);
+          }
+        }
+      }
+    }
+  }
+  const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = mt * 16 + 4 * g + i;
+      if (j < m) pdqt[base + (size_t)j * D + nd * 16 + c] = scale * aq[u][i];
+    }
+  }
+  const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int item = tid + 256 * a;
+    if (item < D * NTB) {
+      const int f = item % D, t0 = 8 * (item / D);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t0 + u < conv_k) pdwc[wb + (size_t)f * conv_k + t0 + u] = awc[a][u];
+    }
+  }
+}
+
+template <int D, bool DQ>
+struct RowMmSmem {
+  static constexpr int PD = D + 8, PK = 64 + 8;
+  uint16_t ka[64][PD];   // Kt * log2(e)/sqrt(d) rows (A of the scores)
+  uint16_t wa[64][PD];   // W rows (A of dF)
+  uint16_t kT[D][PK];    // Kt^T in mm_slot order (A of dQ^T)
+  uint16_t qr[kMmTile][PD], gr[kMmTile][PD];  // Q and dO rows of the tile
+  uint16_t qT[DQ ? 1 : D][PK], gT[DQ ? 1 : D][PK];  // the same transposed (B of dKt, dW)
+  uint16_t fT[DQ ? 1 : 64][PK], sT[DQ ? 1 : 64][PK];  // F^T, dS^T of the tile (A of dW, dKt)
+};
+
+template <int D, bool DQ>
+__global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+                                                     const float* __restrict__ Kt, const float* __restrict__ W,
+                                                     const float* __restrict__ dqt, uint16_t* __restrict__ dQ,
+                                                     float* __restrict__ pdw, float* __restrict__ pdkt, int n, int m,
+                                                     int chunk, int nchunks, float sl2e, float scale) {
+  using SM = RowMmSmem<D, DQ>;
+  constexpr int KC = D / 32, ND = D / 16, PER = ND;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int ch = blockIdx.x, bh = blockIdx.y;
+  const size_t hoff = (size_t)bh * n * D, md = (size_t)bh * m * D;
+
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int j = e / D, f = e % D;
+    const float k = j < m ? Kt[md + e] : 0.f;
+    sm.ka[j][f] = bf(k * sl2e);
+    sm.wa[j][f] = bf(j < m ? W[md + e] : 0.f);
+    sm.kT[f][mm_slot(j)] = bf(k);
+  }
+  f32x4_t aw[PER], ak[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) aw[u] = ak[u] = zero4();
+  const int seg = (n + m - 1) / m;
+  const float inv_seg = 1.f / (float)seg;
+
+  const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
+  for (int t0 = rbeg; t0 < rend; t0 += kMmTile) {
+    __syncthreads();
+    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
+      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 + rr;
+      const bool in = row < rend;
+      B8 q, gv;
+      q.q = in ? *reinterpret_cast<const uint4*>(Q + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      gv.q = in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.qr[rr][c8]) = q.q;
+      *reinterpret_cast<uint4*>(&sm.gr[rr][c8]) = gv.q;
+      if constexpr (!DQ) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          sm.qT[c8 + u][rr] = q.h[u];
+          sm.gT[c8 + u][rr] = gv.h[u];
+        }
+      }
+    }
+    __syncthreads();
+
+    const int rl = 16 * wave + c, row = t0 + rl;
+    const bool live = row < rend;
+    f32x4_t sc[4], df[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      sc[mt] = zero4();
+      df[mt] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        sc[mt] = mfma(lds8(&sm.ka[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.qr[rl][kc * 32 + 8 * g]), sc[mt]);
+        df[mt] = mfma(lds8(&sm.wa[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.gr[rl][kc * 32 + 8 * g]), df[mt]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (mt * 16 + 4 * g + i >= m) sc[mt][i] = -INFINITY;
+        mx = fmaxf(mx, sc[mt][i]);
+      }
+    mx = max_over_groups(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[mt][i] = exp2f(sc[mt][i] - mx);
+        sum += sc[mt][i];
+      }
+    const float inv = 1.f / sum_over_groups(sum);
+    float delta = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[mt][i] *= inv;  // F
+        delta = fmaf(sc[mt][i], df[mt][i], delta);
+      }
+    delta = sum_over_groups(delta);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        df[mt][i] = live ? sc[mt][i] * (df[mt][i] - delta) : 0.f;  // dS
+        if (!live) sc[mt][i] = 0.f;
+      }
+
+    if constexpr (DQ) {
+      // The products run on every lane (a matrix-core instruction reads the
+      // operands of the whole wave); only the stores are per row.
+      const float* qtr = dqt + md + (size_t)min(row / seg, m - 1) * D;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) {
+        f32x4_t a = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          a = mfma(lds8(&sm.kT[nd * 16 + c][kk * 32 + 8 * g]), pack_b(df[2 * kk], df[2 * kk + 1]), a);
+        if (live) {
+          const int f0 = nd * 16 + 4 * g;
+          const float4 q4 = *reinterpret_cast<const float4*>(qtr + f0);
+          const float v0 = fmaf(scale, a[0], q4.x * inv_seg), v1 = fmaf(scale, a[1], q4.y * inv_seg);
+          const float v2 = fmaf(scale, a[2], q4.z * inv_seg), v3 = fmaf(scale, a[3], q4.w * inv_seg);
+          *reinterpret_cast<uint2*>(dQ + hoff + (size_t)row * D + f0) =
+              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm.fT[mt * 16 + 4 * g + i][rl] = bf(sc[mt][i]);
+          sm.sT[mt * 16 + 4 * g + i][rl] = bf(df[mt][i]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          aw[u] = mfma(lds8(&sm.fT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.gT[nd * 16 + c][kc * 32 + 8 * g]), aw[u]);
+          ak[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.qT[nd * 16 + c][kc * 32 + 8 * g]), ak[u]);
+        }
+      }
+    }
+  }
+  if constexpr (!DQ) {
+    const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = mt * 16 + 4 * g + i;
+        if (j < m) {
+          pdw[base + (size_t)j * D + nd * 16 + c] = aw[u][i];
+          pdkt[base + (size_t)j * D + nd * 16 + c] = scale * ak[u][i];
+        }
+      }
+    }
+  }
+}
+
 // dQt = dQt_A + sum of the key-side partials (chunk order); grid
 // (entries / 256, batch*heads), one entry per thread.
 __global__ __launch_bounds__(256) void k_bwd_qt_finish(const float* __restrict__ dQtA, const float* __restrict__ pdqt,
@@ -706,11 +1102,12 @@ bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int c
   if (!make_layout(batch, heads, n, d, m, &L->fwd)) return false;
   if (m > 64 || conv_k > 33) return false;
   const long long BH = (long long)batch * heads;
-  const int tq = split_chunks(n, BH, kRowTile);
-  L->qchunk = cdivi(cdivi(n, tq), kRowTile) * kRowTile;
+  // Chunks are multiples of 64 rows, a whole number of tiles for every pass.
+  const int tq = split_chunks(n, BH, kMmTile);
+  L->qchunk = cdivi(cdivi(n, tq), kMmTile) * kMmTile;
   L->nq = cdivi(n, L->qchunk);
-  const int tk = split_chunks(n, BH, kKeyTile);
-  L->kchunk = cdivi(cdivi(n, tk), kKeyTile) * kKeyTile;
+  const int tk = split_chunks(n, BH, kMmTile);
+  L->kchunk = cdivi(cdivi(n, tk), kMmTile) * kMmTile;
   L->nk = cdivi(n, L->kchunk);
   L->mp = m <= 32 ? 32 : 64;
   size_t off = L->fwd.total;
@@ -744,8 +1141,19 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   const float sl2e = kLog2e / sqrtf((float)D), scale = 1.f / sqrtf((float)D);
   constexpr int P = D + 1;
 
+  constexpr bool MM = IO::kBf16 && (D == 32 || D == 64);  // matrix-core n-sized passes
   // Query side, partials of dW and dKt_F.
-  {
+  if constexpr (MM) {
+    const int bytes = (int)sizeof(RowMmSmem<D, false>);
+    auto kern = &k_bwd_rows_mm<D, false>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess) return attr;
+    KernelTimer kt_("bwd_rows_reduce", s);
+    kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
+                                            w.Kt, w.W, nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk,
+                                            L.nq, sl2e, scale);
+  } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, false>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -781,7 +1189,20 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     }
   }
   // Key side: dK, dV and the partials of dQt_B and the filter gradient.
-  {
+  if constexpr (MM) {
+    const int ck = p.conv_w ? p.conv_k : 0;
+    const int bytes = (int)sizeof(KeyMmSmem<D>);
+    auto kern = &k_bwd_key_mm<D>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess) return attr;
+    KernelTimer kt_("bwd_keys", s);
+    kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
+                                            static_cast<const uint16_t*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv),
+                                            F(L.dkt), w.pmax, w.psum, static_cast<uint16_t*>(bp.dK),
+                                            static_cast<uint16_t*>(bp.dV), F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads,
+                                            ck, L.kchunk, L.nk, w.nchunks, sl2e, scale);
+  } else {
     const int ck = p.conv_w ? p.conv_k : 0;
     const int bytes = (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 + 3 * 64 + D * (ck > 0 ? ck : 1)) * 4;
     auto kern = &k_bwd_key<IO, D>;
@@ -805,7 +1226,18 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                                                                p.heads, L.nk, D * p.conv_k);
   }
   // Query side again: dQ.
-  {
+  if constexpr (MM) {
+    const int bytes = (int)sizeof(RowMmSmem<D, true>);
+    auto kern = &k_bwd_rows_mm<D, true>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (attr != hipSuccess) return attr;
+    const int nt = cdivi(p.n, kMmTile);
+    KernelTimer kt_("bwd_rows_dq", s);
+    kern<<<dim3(nt, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
+                                          w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), nullptr, nullptr, p.n,
+                                          p.m, kMmTile, nt, sl2e, scale);
+  } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, true>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
