@@ -394,9 +394,13 @@ def backward_bench(args, wl, dev) -> int:
         avg_s = ms / launches / 1e3
         fl = backward_flops(wl, dom)
         if fl:
+            # bf16 I/O at d = 32, 64 runs the products on the matrix cores
+            # (bf16 peak); otherwise they are fp32 vector work.
+            mm = wl.dtype == "bf16" and wl.d in (32, 64)
+            peak = MFMA_BF16_PEAK_TFLOPS if mm else FP32_VECTOR_PEAK_TFLOPS
             achieved = fl / avg_s / 1e12
-            roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+            roof = {"bound": "mfma" if mm else "alu", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
                     "kernel": dom, "algorithmic_flops": fl, "avg_us": round(avg_s * 1e6, 3)}
         else:
             roof = {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None,

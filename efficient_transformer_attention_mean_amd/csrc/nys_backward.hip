@@ -712,8 +712,9 @@ struct KeyMmSmem {
   uint16_t vh[HR][PD];       // V rows with the skip halo
   uint16_t gh[HR][PD];       // dO rows with the skip halo
   uint16_t sT[64][PK];       // dS^T of the tile (A of dQt)
+  float cv[kMmTile][D + 4];  // skip-transpose part of dV for the tile
   float stm[64], stl[64], dlt[64];
-  float wsh[D * 33];
+  float wsh[D * 33];         // filters centred in 33 taps (zero outside)
 };
 
 template <int D>
@@ -733,7 +734,11 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
   const size_t hoff = (size_t)bh * n * D, md = (size_t)bh * m * D;
-  const int R = conv_k > 0 ? (conv_k - 1) / 2 : 0;
+  // A filter of conv_k <= 33 taps is centred in 33 (offset off): tap t of
+  // 33 reads row i - t + 16 in the transpose and V row i + t - 16 in the
+  // filter gradient, so the halo is always 16 rows.
+  const bool conv = conv_k > 0;
+  const int R = conv ? 16 : 0, off = conv ? (33 - conv_k) / 2 : 0;
 
   for (int e = tid; e < 64 * D; e += 256) {
     const int j = e / D, f = e % D;
@@ -743,7 +748,10 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
     sm.qT[f][mm_slot(j)] = bf(q);
     sm.dT[f][mm_slot(j)] = bf(db);
   }
-  for (int e = tid; e < D * conv_k; e += 256) sm.wsh[e] = conv_w[(size_t)h * D * conv_k + e];
+  for (int e = tid; e < D * 33; e += 256) {
+    const int f = e / 33, t = e % 33 - off;
+    sm.wsh[e] = (conv && t >= 0 && t < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + t] : 0.f;
+  }
   if (tid < 64) {
     const int j = tid;
     float M = -INFINITY, L = 0.f, dl = 0.f;
@@ -792,6 +800,29 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
     }
     __syncthreads();
 
+    if (conv) {
+      // Skip transpose for keys r0 .. r0 + KPT - 1 of feature f: out[u] =
+      // sum_t w[f][t] dO[r0 + u - t + 16], from a register window of the
+      // KPT + 32 dO values it reads.
+      constexpr int KPT = kMmTile * D / 256;
+      const int f = tid % D, r0 = (tid / D) * KPT;
+      float w33[33], win[KPT + 32], out[KPT];
+#pragma unroll
+      for (int t = 0; t < 33; ++t) w33[t] = sm.wsh[f * 33 + t];
+#pragma unroll
+      for (int p = 0; p < KPT + 32; ++p) win[p] = bf16_to_f32(sm.gh[r0 + p][f]);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int t = 0; t < 33; ++t) a = fmaf(w33[t], win[u - t + 32], a);
+        out[u] = a;
+      }
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) sm.cv[r0 + u][f] = out[u];
+      __syncthreads();
+    }
+
     // Scores S'^T and dB^T for this wave's 16 keys (key = i0 + 16 wave + c).
     const int kl = 16 * wave + c, key = i0 + kl;
     const bool live = key < kend;
@@ -832,10 +863,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           vk[i] = fmaf(scale, ak[i], ktv[i] * inv_seg);
-          float acc = av[i];
-          for (int t = 0; t < conv_k; ++t)
-            acc = fmaf(sm.wsh[(f0 + i) * conv_k + t], bf16_to_f32(sm.gh[kl - t + 2 * R][f0 + i]), acc);
-          vv[i] = acc;
+          vv[i] = conv ? av[i] + sm.cv[kl][f0 + i] : av[i];
         }
         *reinterpret_cast<uint2*>(dK + hoff + (size_t)key * D + f0) =
             make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
@@ -856,18 +884,26 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       for (int kc = 0; kc < 2; ++kc)
         aq[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.kT[nd * 16 + c][kc * 32 + 8 * g]), aq[u]);
     }
-    // Filter gradient: item (f, tap group tb), taps 8 tb + u.
+    // Filter gradient: item (f, tap group tb), taps 8 tb + u of 33:
+    // dw[f][t] += sum_r dO[r][f] V[r + t - 16][f], with a sliding register
+    // window over the V rows (taps past 32 read clamped rows and are dropped).
+    if (conv) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int item = tid + 256 * a;
-      if (item < D * NTB) {
-        const int f = item % D, t0 = 8 * (item / D);
-        if (t0 < conv_k) {
+      for (int a = 0; a < 2; ++a) {
+        const int item = tid + 256 * a;
+        if (item < D * NTB) {
+          const int f = item % D, t0 = 8 * (item / D);
           const int rows = min(kMmTile, kend - i0);
-          for (int r = 0; r < rows; ++r) {
-            const float gv = bf16_to_f32(sm.gh[R + r][f]);
+          float vw[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, bf16_to_f32(sm.vh[min(r + t0 + u, SM::HR - 1)][f]), awc[a][u]);
+          for (int u = 0; u < 8; ++u) vw[u] = bf16_to_f32(sm.vh[min(t0 + u, SM::HR - 1)][f]);
+          for (int r = 0; r < rows; ++r) {
+            const float gv = bf16_to_f32(sm.gh[16 + r][f]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, vw[u], awc[a][u]);
+#pragma unroll
+            for (int u = 0; u < 7; ++u) vw[u] = vw[u + 1];
+            vw[7] = bf16_to_f32(sm.vh[min(r + 1 + t0 + 7, SM::HR - 1)][f]);
           }
         }
       }
@@ -883,15 +919,19 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       if (j < m) pdqt[base + (size_t)j * D + nd * 16 + c] = scale * aq[u][i];
     }
   }
-  const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+  if (conv) {
+    const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int item = tid + 256 * a;
-    if (item < D * NTB) {
-      const int f = item % D, t0 = 8 * (item / D);
+    for (int a = 0; a < 2; ++a) {
+      const int item = tid + 256 * a;
+      if (item < D * NTB) {
+        const int f = item % D, t0 = 8 * (item / D);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (t0 + u < conv_k) pdwc[wb + (size_t)f * conv_k + t0 + u] = awc[a][u];
+        for (int u = 0; u < 8; ++u) {
+          const int t = t0 + u - off;  // tap of the conv_k-tap filter
+          if (t >= 0 && t < conv_k) pdwc[wb + (size_t)f * conv_k + t] = awc[a][u];
+        }
+      }
     }
   }
 }
