@@ -53,7 +53,7 @@ def sources_digest() -> str:
 
 def short_name(name: str) -> str:
     """Kernel name without the argument list and namespace."""
-    base = name.split("(")[0]
+    base = name.replace("(anonymous namespace)::", "").split("(")[0]
     base = re.sub(r"^void ", "", base)
     return base.replace("nys::", "")
 

@@ -120,3 +120,32 @@ def test_dconv_rejects_bad_arguments_before_launch(lib, kw, code):
                 stream=None)
     args.update(kw)
     assert _lib.nystrom_dconv_fwd(**args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), _lib.NYS_EINVAL),
+    (dict(dK=None), _lib.NYS_EINVAL),
+    (dict(m=0), _lib.NYS_EINVAL),
+    (dict(iters=-1), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=4), _lib.NYS_EINVAL),
+    (dict(dtype=3), _lib.NYS_EINVAL),
+    (dict(m=80, n=640), _lib.NYS_EUNSUPPORTED),       # the backward handles m <= 64
+    (dict(conv_w=FAKE, conv_k=35), _lib.NYS_EUNSUPPORTED),
+    (dict(d=24), _lib.NYS_EUNSUPPORTED),
+    (dict(workspace=FAKE, workspace_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_bwd_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, dO=FAKE, n=64, d=16, m=8, heads=1, iters=6, dQ=FAKE, dK=FAKE,
+                dV=FAKE, dconv_w=None, batch=1, conv_k=0, dtype=_lib.NYS_F32, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_bwd(**args) == code
+
+
+def test_bwd_workspace_covers_the_forward_layout(lib):
+    for shape in ((1, 1, 64, 16, 8), (2, 12, 8192, 64, 64), (1, 3, 777, 32, 48)):
+        fwd = _lib.nystrom_attn_workspace_bytes(*shape)
+        bwd = _lib.nystrom_attn_bwd_workspace_bytes(*shape, 6, 33)
+        assert bwd > fwd > 0
+    assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 640, 64, 80, 6, 0) == 0
+    assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 64, 16, 8, 6, 35) == 0

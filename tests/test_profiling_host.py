@@ -56,3 +56,6 @@ def test_stats_summary_and_names(tmp_path):
     assert lines[1].startswith("| k_segment_mean<BF16, 64> | 4 | 0.25 |")
     assert profiling.family(APPLY) == "apply"
     assert profiling.family("void nys::k_pinv_planes<64, 64>(float const*)") == "pinv_planes"
+    anon = "void nys::(anonymous namespace)::k_bwd_key_mm<64>(unsigned short const*, float const*)"
+    assert profiling.short_name(anon) == "k_bwd_key_mm<64>"
+    assert profiling.family(anon) == "bwd_key_mm"
