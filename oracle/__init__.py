@@ -2,3 +2,4 @@
 CPU-baseline leg may import this package; the product path never does."""
 from .nystrom_oracle import *  # noqa: F401,F403
 from .nystrom_backward import *  # noqa: F401,F403
+from .nystrom_layer import *  # noqa: F401,F403
