@@ -109,6 +109,9 @@ def main() -> int:
                          "(key-padding mask, nystrom_attn_fwd_masked); value then counts real tokens")
     ap.add_argument("--backward", action="store_true",
                     help="time nystrom_attn_bwd (gradients of Q, K, V and the filters) instead of the forward")
+    ap.add_argument("--layer", action="store_true",
+                    help="time nystrom_layer_fwd (QKV projection, heads, attention, output projection) on "
+                         "X [batch][n][heads*d]")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -128,6 +131,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.backward:
         return backward_bench(args, wl, dev)
+    if args.layer:
+        return layer_bench(args, wl, dev)
     lengths = None
     eff = [wl.n] * wl.batch
     if args.lengths:
@@ -307,6 +312,140 @@ def main() -> int:
             result["nystrom_vs_exact_attention_rel_l2_sampled_rows"] = float(
                 np.linalg.norm(att - ex) / np.linalg.norm(ex))
     result["pages_context"] = PAGES_CONTEXT
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def layer_bench(args, wl, dev) -> int:
+    """One step = one nystrom_layer_fwd call: X [batch][n][E] -> Y, with
+    random projections of the layer's shape (E = heads * d)."""
+    import torch
+    from efficient_transformer_attention_mean_amd import _lib
+    from efficient_transformer_attention_mean_amd.workloads import bf16_bits, bf16_bits_to_f32, round_to_bf16
+
+    E, rows = wl.heads * wl.d, wl.batch * wl.n
+    e = wl.elem_bytes
+    io_bytes = 2 * rows * E * e + 4 * E * E * e + (4 * wl.heads * wl.d * wl.conv_k if wl.conv_k else 0)
+    sets = args.sets or max(2, int(np.ceil(512 * 2 ** 20 / io_bytes)) + 1)
+
+    def draw(seed):
+        rng = np.random.default_rng(seed)
+        X = rng.standard_normal((wl.batch, wl.n, E)).astype(np.float32)
+        Wqkv = (rng.standard_normal((E, 3 * E)) / np.sqrt(E)).astype(np.float32)
+        Wo = (rng.standard_normal((E, E)) / np.sqrt(E)).astype(np.float32)
+        w = rng.normal(0, 0.02, (wl.heads, wl.d, wl.conv_k)).astype(np.float32) if wl.conv_k else None
+        if wl.dtype == "bf16":
+            X, Wqkv, Wo = round_to_bf16(X), round_to_bf16(Wqkv), round_to_bf16(Wo)
+        return X, Wqkv, Wo, w
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    host0 = None
+    bufs = []
+    for i in range(sets):
+        X, Wqkv, Wo, w = draw(wl.seed + 1000 * i)
+        if i == 0:
+            host0 = (X, Wqkv, Wo, w)
+        Xd = to_dev(X)
+        bufs.append((Xd, to_dev(Wqkv), to_dev(Wo), None if w is None else torch.from_numpy(w).to(dev),
+                     torch.empty_like(Xd)))
+    conv_k = wl.conv_k if wl.conv_k else 0
+    code = _lib.NYS_BF16 if wl.dtype == "bf16" else _lib.NYS_F32
+    ws_bytes = _lib.nystrom_layer_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        Xd, Wd, Wod, wd, Y = bufs[i % sets]
+        rc = _lib.nystrom_layer_fwd(Xd, Wd, Wod, wd, wl.n, wl.d, wl.m, wl.heads, wl.iters, Y, wl.batch, conv_k, code,
+                                    ws, ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    print(f"[bench] layer workload={wl.name} sets={sets} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+          flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = ev0.elapsed_time(ev1) / 1e3
+    ms_per_step = 1e3 * gpu_s / args.steps
+    tokens = rows
+    value = tokens * args.steps / gpu_s
+
+    _lib.nystrom_timing_enable(True)
+    _lib.nystrom_timing_read()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kern = _lib.nystrom_timing_read()
+    _lib.nystrom_timing_enable(False)
+    per_kernel = {name: {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                         "avg_us_per_launch": 1e3 * ms / max(n, 1)} for name, (ms, n) in kern.items()}
+    dom = max(kern.items(), key=lambda kv: kv[1][0])[0] if kern else None
+    roof = None
+    if dom is not None:
+        ms, launches = kern[dom]
+        avg_s = ms / launches / 1e3
+        gemm_flops = {"qkv_gemm": 2.0 * rows * E * 3 * E, "out_gemm": 2.0 * rows * E * E}
+        if dom in gemm_flops:
+            peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+            achieved = gemm_flops[dom] / avg_s / 1e12
+            roof = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                    "algorithmic_flops": gemm_flops[dom], "avg_us": round(avg_s * 1e6, 3)}
+        else:
+            ab = {"split_heads": 6 * rows * E * e, "merge_heads": 2 * rows * E * e}.get(dom) or \
+                algorithmic_bytes(wl, dom)
+            if ab:
+                achieved = ab / avg_s / 1e9
+                roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                        "algorithmic_bytes": ab, "avg_us": round(avg_s * 1e6, 3)}
+    result = {
+        "metric": "Nyström attention layer fwd tokens/s (QKV projection, heads, attention + skip, output projection)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "layer", "batch": wl.batch, "heads": wl.heads, "n": wl.n, "d": wl.d,
+                   "embed": E, "m": wl.m, "iters": wl.iters, "conv_k": wl.conv_k, "io": wl.dtype,
+                   "input_sets": sets},
+        "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
+        "compulsory_bytes": io_bytes, "wall_s": round(wall, 4), "roofline": roof, "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline or not args.no_parity:
+        from oracle import nystrom_layer
+        threads = blas_threads()
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            ref = nystrom_layer(host0[0], host0[1], host0[2], wl.heads, wl.m, wl.iters, host0[3])
+            reps += 1
+            if args.no_cpu_baseline or time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        cpu_s = time.perf_counter() - c0
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {
+                "value": round(tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": f"{reps} whole layer call(s) (batch {wl.batch}, n={wl.n}, E={E}), fp64 NumPy, "
+                          f"{cpu_s:.1f} s, host has {os.cpu_count()} logical CPUs"}
+        if not args.no_parity:
+            step(0)
+            torch.cuda.synchronize()
+            Y = bufs[0][4]
+            got = (bf16_bits_to_f32(Y.view(torch.int16).cpu().numpy().view(np.uint16)) if wl.dtype == "bf16"
+                   else Y.float().cpu().numpy())
+            result["parity_rel_l2_vs_oracle"] = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     print(json.dumps(result), flush=True)
     return 0
 

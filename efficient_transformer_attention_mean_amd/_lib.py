@@ -30,6 +30,8 @@ EXPORTS = (
     "nystrom_attn_fwd_masked",
     "nystrom_attn_bwd_workspace_bytes",
     "nystrom_attn_bwd",
+    "nystrom_layer_workspace_bytes",
+    "nystrom_layer_fwd",
     "nystrom_dconv_fwd",
     "nystrom_strerror",
     "nystrom_abi_version",
@@ -62,6 +64,10 @@ def load():
     lib.nystrom_attn_bwd_workspace_bytes.restype = sz
     lib.nystrom_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.nystrom_attn_bwd.restype = i
+    lib.nystrom_layer_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.nystrom_layer_workspace_bytes.restype = sz
+    lib.nystrom_layer_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, sz, vp]
+    lib.nystrom_layer_fwd.restype = i
     lib.nystrom_dconv_fwd.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp]
     lib.nystrom_dconv_fwd.restype = i
     lib.nystrom_strerror.argtypes = [i]
@@ -129,6 +135,16 @@ def nystrom_attn_bwd(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dco
     return int(load().nystrom_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), _ptr(dO), n, d, m, heads, iters,
                                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dconv_w), batch, conv_k, dtype,
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def nystrom_layer_workspace_bytes(batch, heads, n, d, m, dtype) -> int:
+    return int(load().nystrom_layer_workspace_bytes(batch, heads, n, d, m, dtype))
+
+
+def nystrom_layer_fwd(X, Wqkv, Wo, conv_w, n, d, m, heads, iters, Y, batch, conv_k, dtype, workspace=None,
+                      workspace_bytes=0, stream=None) -> int:
+    return int(load().nystrom_layer_fwd(_ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(conv_w), n, d, m, heads, iters, _ptr(Y),
+                                        batch, conv_k, dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def nystrom_dconv_fwd(V, conv_w, n, d, heads, batch, conv_k, dtype, out, stream=None) -> int:

@@ -15,7 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnystrom.so")
 
-SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_backward.hip", "nys_launch.hip", "nys_abi.hip", "nys_timing.hip"]
+SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_backward.hip", "nys_layer.hip", "nys_launch.hip", "nys_abi.hip",
+           "nys_timing.hip"]
+ROCM_LIB = "/opt/rocm/lib"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -56,7 +58,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp])
+    # The layer's two projections are plain GEMMs on rocBLAS.
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, f"-L{ROCM_LIB}",
+          f"-Wl,-rpath,{ROCM_LIB}", "-lrocblas", "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

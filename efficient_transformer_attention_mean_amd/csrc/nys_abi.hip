@@ -158,6 +158,49 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
   }
 }
 
+size_t nystrom_layer_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype) {
+  if (check_shape(batch, heads, n, d, m, 0) != NYS_OK) return 0;
+  if (dtype != NYS_F32 && dtype != NYS_BF16) return 0;
+  nys::LayerLayout L;
+  if (!nys::make_layer_layout(batch, heads, n, d, m, dtype == NYS_BF16, &L)) return 0;
+  return L.total;
+}
+
+int nystrom_layer_fwd(const void* X, const void* Wqkv, const void* Wo, const float* conv_w, int n, int d, int m,
+                      int heads, int iters, void* Y, int batch, int conv_k, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  try {
+    if (!X || !Wqkv || !Wo || !Y) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    if ((long long)batch * n * heads * d * 3 >= (1LL << 31)) return NYS_EUNSUPPORTED;  // GEMM sizes are 32-bit
+    nys::LayerLayout L;
+    if (!nys::make_layer_layout(batch, heads, n, d, m, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bool owned = false;
+    if (!ws) {
+      if (hipMallocAsync(reinterpret_cast<void**>(&ws), L.total, s) != hipSuccess) return NYS_EHIP;
+      owned = true;
+    } else if (workspace_bytes < L.total) {
+      return NYS_EWORKSPACE;
+    }
+    nys::LayerProblem p{{nullptr, nullptr, nullptr, conv_w, nullptr, batch, heads, n, d, m, iters, conv_w ? conv_k : 0,
+                         dtype == NYS_BF16},
+                        X, Wqkv, Wo, Y};
+    hipError_t e = nys::launch_layer(p, L, ws, s);
+    if (owned) {
+      hipError_t f = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = f;
+    }
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
 int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch, int conv_k, int dtype,
                       void* out, void* stream) {
   try {

@@ -100,6 +100,27 @@ struct BwdProblem {
 };
 
 hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, char* ws, hipStream_t s);
+
+// Full layer (projections around the attention): the forward's regions, then
+// the fused QKV projection (reused for the attention output and the merged
+// heads) and the per-head Q, K, V.
+struct LayerLayout {
+  WsLayout fwd;
+  size_t qkv, q, k, v;
+  size_t total;
+};
+
+bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, LayerLayout* L);
+
+struct LayerProblem {
+  Problem attn;      // shape, iters, filters, dtype (its Q, K, V, out are set inside)
+  const void* X;     // [batch][n][heads*d]
+  const void* Wqkv;  // [heads*d][3*heads*d], column blocks W_Q | W_K | W_V
+  const void* Wo;    // [heads*d][heads*d]
+  void* Y;           // [batch][n][heads*d]
+};
+
+hipError_t launch_layer(const LayerProblem& p, const LayerLayout& L, char* ws, hipStream_t s);
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,
                         int d, int conv_k, bool bf16, hipStream_t s);
 

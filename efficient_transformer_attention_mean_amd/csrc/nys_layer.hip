@@ -1,0 +1,150 @@
+// Nyström self-attention layer: the learned projections around the
+// attention ("Nyströmformer: A Nyström-Based Algorithm for Approximating
+// Self-Attention", paper deep-dive page, "Standard Self-Attention":
+// Q = X W_Q, K = X W_K, V = X W_V; the attention-output projection the page
+// mentions in its discussion of the skip connection).
+//
+// For a batch of sequences X [batch][n][E], E = heads * d:
+//   QKV = X [W_Q | W_K | W_V]            one library GEMM, [batch*n][3E]
+//   Q, K, V = per-head split              k_split_heads -> [batch][heads][n][d]
+//   O = Nyström attention + DConv skip    the forward kernels
+//   Y = concat_heads(O) W_O               k_merge_heads, one library GEMM
+// The two projections are plain GEMMs and run on rocBLAS (bf16 operands with
+// fp32 accumulation for bf16 I/O, fp32 otherwise); the head split and merge
+// are 16-byte streaming copies.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+
+#include "nys_common.hpp"
+#include "nys_internal.hpp"
+
+namespace nys {
+
+namespace {
+
+// One rocBLAS handle per device, created on first use and kept for the life
+// of the process (creating one per call costs milliseconds).
+rocblas_handle handle_for_current_device(hipStream_t s) {
+  static std::mutex mu;
+  static rocblas_handle handles[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!handles[dev]) {
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
+    // No atomics: a GEMM gives the same bits on every call.
+    if (rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed) != rocblas_status_success) {
+      rocblas_destroy_handle(h);
+      return nullptr;
+    }
+    handles[dev] = h;
+  }
+  if (handles[dev] && rocblas_set_stream(handles[dev], s) != rocblas_status_success) return nullptr;
+  return handles[dev];
+}
+
+// Row-major C[rows][cols] = A[rows][k] B[k][cols], as the column-major
+// product C^T = B^T A^T.
+bool gemm_rm(rocblas_handle h, bool bf16, int rows, int cols, int k, const void* A, const void* B, void* C) {
+  const float one = 1.f, zero = 0.f;
+  const rocblas_datatype t = bf16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+  return rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, cols, rows, k, &one, B, t, cols, A, t, k,
+                         &zero, C, t, cols, C, t, cols, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0,
+                         0) == rocblas_status_success;
+}
+
+// QKV [batch*n][3][heads][d] -> Q, K, V [batch][heads][n][d]; one 16-byte
+// vector per thread, read in source order (coalesced), written per head row.
+__global__ __launch_bounds__(256) void k_split_heads(const uint4* __restrict__ qkv, uint4* __restrict__ q,
+                                                     uint4* __restrict__ k, uint4* __restrict__ v, int n, int heads,
+                                                     int dv, long long total) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int jv = (int)(e % dv);
+  long long r = e / dv;
+  const int h = (int)(r % heads);
+  r /= heads;
+  const int which = (int)(r % 3);
+  const long long tok = r / 3;  // b * n + i
+  const long long b = tok / n, i = tok % n;
+  uint4* dst = which == 0 ? q : (which == 1 ? k : v);
+  dst[((b * heads + h) * n + i) * dv + jv] = qkv[e];
+}
+
+// O [batch][heads][n][d] -> [batch*n][heads][d]; written in destination order.
+__global__ __launch_bounds__(256) void k_merge_heads(const uint4* __restrict__ o, uint4* __restrict__ oc, int n,
+                                                     int heads, int dv, long long total) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int jv = (int)(e % dv);
+  long long r = e / dv;
+  const int h = (int)(r % heads);
+  const long long tok = r / heads;
+  const long long b = tok / n, i = tok % n;
+  oc[e] = o[((b * heads + h) * n + i) * dv + jv];
+}
+
+}  // namespace
+
+bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, LayerLayout* L) {
+  if (!make_layout(batch, heads, n, d, m, &L->fwd)) return false;
+  const size_t elems = (size_t)batch * n * heads * d, es = bf16 ? 2 : 4;
+  size_t off = L->fwd.total;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  L->qkv = take(3 * elems * es);  // later: O (first third) and the merged heads (second third)
+  L->q = take(elems * es);
+  L->k = take(elems * es);
+  L->v = take(elems * es);
+  L->total = off;
+  return true;
+}
+
+hipError_t launch_layer(const LayerProblem& lp, const LayerLayout& L, char* ws, hipStream_t s) {
+  const Problem& p = lp.attn;
+  const int E = p.heads * p.d, rows = p.batch * p.n;
+  const size_t es = p.bf16 ? 2 : 4, elems = (size_t)rows * E;
+  const int dv = (int)(p.d * es / 16);
+  rocblas_handle h = handle_for_current_device(s);
+  if (!h) return hipErrorUnknown;
+  char* qkv = ws + L.qkv;
+  {
+    KernelTimer kt_("qkv_gemm", s);
+    if (!gemm_rm(h, p.bf16, rows, 3 * E, E, lp.X, lp.Wqkv, qkv)) return hipErrorUnknown;
+  }
+  {
+    const long long total = 3 * (long long)elems * es / 16;
+    KernelTimer kt_("split_heads", s);
+    k_split_heads<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(qkv), reinterpret_cast<uint4*>(ws + L.q), reinterpret_cast<uint4*>(ws + L.k),
+        reinterpret_cast<uint4*>(ws + L.v), p.n, p.heads, dv, total);
+  }
+  Problem a = p;
+  a.Q = ws + L.q;
+  a.K = ws + L.k;
+  a.V = ws + L.v;
+  a.out = qkv;  // O reuses the first third of the QKV region
+  hipError_t e = launch_forward(a, L.fwd, ws, s);
+  if (e != hipSuccess) return e;
+  char* oc = qkv + elems * es;
+  {
+    const long long total = (long long)elems * es / 16;
+    KernelTimer kt_("merge_heads", s);
+    k_merge_heads<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(reinterpret_cast<const uint4*>(qkv),
+                                                                  reinterpret_cast<uint4*>(oc), p.n, p.heads, dv,
+                                                                  total);
+  }
+  {
+    KernelTimer kt_("out_gemm", s);
+    if (!gemm_rm(h, p.bf16, rows, E, E, oc, lp.Wo, lp.Y)) return hipErrorUnknown;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nys

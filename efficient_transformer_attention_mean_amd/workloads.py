@@ -71,6 +71,8 @@ WORKLOADS = {
                             note="m = n = 64: with a converged pseudoinverse this is exact attention"),
     "bert": Workload("bert", 8, 12, 512, 64, 64, 6, 33, "f32", 1,
                      note="BERT-base-shaped layer, fp32 I/O"),
+    "bert_bf16": Workload("bert_bf16", 8, 12, 512, 64, 64, 6, 33, "bf16", 1,
+                          note="BERT-base-shaped layer, bf16 I/O"),
     "long": Workload("long", 4, 12, 4096, 64, 64, 6, 33, "bf16", 2,
                      note="long sequence, bf16 I/O"),
     "headline": Workload("headline", 2, 12, 8192, 64, 64, 6, 33, "bf16", 3,

@@ -159,6 +159,32 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
                      int batch, int conv_k, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Full self-attention layer: the learned projections around the attention
+ * ("Nyströmformer: ...", "Standard Self-Attention": Q = X W_Q, K = X W_K,
+ * V = X W_V, with no bias; the attention-output projection the page mentions
+ * with the skip connection).  With E = heads * d:
+ *   QKV = X [W_Q | W_K | W_V], split into heads (head h owns columns
+ *   h*d .. h*d+d-1 of each block), Nyström attention with the DConv skip per
+ *   head as in nystrom_attn_fwd, heads concatenated, Y = O W_O.
+ *   X           [batch][n][E] of `dtype`
+ *   Wqkv        [E][3E] of `dtype`, row-major, column blocks W_Q | W_K | W_V
+ *   Wo          [E][E] of `dtype`, row-major
+ *   Y           [batch][n][E] of `dtype`, written; must not alias the inputs
+ *   conv_w, n, d, m, heads, iters, batch, conv_k, dtype: as for nystrom_attn_fwd
+ *   workspace   device buffer of at least nystrom_layer_workspace_bytes(), or
+ *               NULL (allocated and freed in stream order)
+ * The two projections run on rocBLAS (bf16 operands with fp32 accumulation
+ * for NYS_BF16, fp32 otherwise); the library keeps one rocBLAS handle per
+ * device for the life of the process, and calls on one device from several
+ * host threads at once are not supported.  Return codes as for
+ * nystrom_attn_fwd (a rocBLAS failure is NYS_EHIP); NYS_EUNSUPPORTED also for
+ * 3 * batch * n * E >= 2^31. */
+size_t nystrom_layer_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype);
+int nystrom_layer_fwd(const void* X, const void* Wqkv, const void* Wo, const float* conv_w,
+                      int n, int d, int m, int heads, int iters, void* Y,
+                      int batch, int conv_k, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Depthwise-convolution skip alone: out = DConv(V) with the filters and
  * padding described at the top ("Putting It Together", Figure 4's DConv path).
  *   V, out      [batch][heads][n][d] of `dtype` (out must not alias V)
