@@ -69,6 +69,7 @@ __all__ = [
     "nystrom_head",
     "nystrom_attention",
     "exact_attention",
+    "approximation_error",
 ]
 
 
@@ -264,3 +265,21 @@ def exact_attention(Q, K, V, row_chunk=1024):
             S = s * (Qf[g, i0:i0 + row_chunk] @ Kf[g].T)
             out[g, i0:i0 + row_chunk] = row_softmax(S) @ Vf[g]
     return out.reshape(lead + (nq, V.shape[-1]))
+
+
+def approximation_error(Q, K, V, m, iters):
+    """Per-(batch, head) relative error of the method's attention output
+    against exact softmax attention ([NF] Eq. 2 for the exact output; the
+    page's closing discussion proposes measuring ||S - S^|| per example):
+    ||O_att - O_exact||_F / ||O_exact||_F, skip excluded (it is exact).
+
+    Q, K, V: (batch, heads, n, d).  Returns (batch, heads) fp64."""
+    Q, K, V = map(_f64, (Q, K, V))
+    Bt, H = Q.shape[:2]
+    err = np.empty((Bt, H))
+    for b in range(Bt):
+        for h in range(H):
+            O, _ = nystrom_head(Q[b, h], K[b, h], V[b, h], m, iters)
+            ex = exact_attention(Q[b, h], K[b, h], V[b, h])
+            err[b, h] = np.linalg.norm(O - ex) / np.linalg.norm(ex)
+    return err

@@ -445,3 +445,25 @@ def test_lengths_are_clamped_to_m_and_n():
     Q, K, V = (rng.standard_normal((Bt, H, n, d)) for _ in range(3))
     np.testing.assert_array_equal(nystrom_attention(Q, K, V, m, 6, lengths=[2, 99]),
                                   nystrom_attention(Q, K, V, m, 6, lengths=[5, 20]))
+
+
+# ---------------------------------------------------------------- approximation error
+
+def test_approximation_error_special_cases():
+    from oracle import approximation_error
+    rng = np.random.default_rng(60)
+    n, d = 16, 4
+    Q, K, V = (rng.standard_normal((1, 2, n, d)) for _ in range(3))
+    # m = n with a converged pseudoinverse is exact attention (Lemma 2).
+    assert approximation_error(Q, K, V, n, 60).max() < 1e-10
+    # Segment-constant queries and keys: exact for m dividing n.
+    m = 4
+    Qc = np.repeat(rng.standard_normal((1, 2, m, d)), n // m, axis=2)
+    Kc = np.repeat(rng.standard_normal((1, 2, m, d)), n // m, axis=2)
+    assert approximation_error(Qc, Kc, V, m, 60).max() < 1e-10
+    # Otherwise a visible error, equal to its definition on one head.
+    e = approximation_error(Q, K, V, 4, 6)
+    O, _ = nystrom_head(Q[0, 1], K[0, 1], V[0, 1], 4, 6)
+    ex = _brute_exact_attention(Q[0, 1], K[0, 1], V[0, 1])
+    assert abs(e[0, 1] - np.linalg.norm(O - ex) / np.linalg.norm(ex)) < 1e-12
+    assert e.min() > 1e-3
