@@ -112,6 +112,8 @@ def main() -> int:
     ap.add_argument("--layer", action="store_true",
                     help="time nystrom_layer_fwd (QKV projection, heads, attention, output projection) on "
                          "X [batch][n][heads*d]")
+    ap.add_argument("--error", action="store_true",
+                    help="time nystrom_attn_error (per-head error of the method against exact attention, on device)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -133,6 +135,8 @@ def main() -> int:
         return backward_bench(args, wl, dev)
     if args.layer:
         return layer_bench(args, wl, dev)
+    if args.error:
+        return error_bench(args, wl, dev)
     lengths = None
     eff = [wl.n] * wl.batch
     if args.lengths:
@@ -312,6 +316,80 @@ def main() -> int:
             result["nystrom_vs_exact_attention_rel_l2_sampled_rows"] = float(
                 np.linalg.norm(att - ex) / np.linalg.norm(ex))
     result["pages_context"] = PAGES_CONTEXT
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def error_bench(args, wl, dev) -> int:
+    """One step = one nystrom_attn_error call: the method's attention output
+    and exact softmax attention for every head, and their relative distance."""
+    import torch
+    from efficient_transformer_attention_mean_amd import _lib
+    from efficient_transformer_attention_mean_amd.workloads import bf16_bits, make_inputs
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+    inp = make_inputs(wl)
+    Q, K, V = (to_dev(inp[k]) for k in ("Q", "K", "V"))
+    code = _lib.NYS_BF16 if wl.dtype == "bf16" else _lib.NYS_F32
+    ws_bytes = _lib.nystrom_attn_error_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    err = torch.empty(wl.batch, wl.heads, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = _lib.nystrom_attn_error(Q, K, V, wl.n, wl.d, wl.m, wl.heads, wl.iters, err, wl.batch, code, ws,
+                                     ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    _lib.nystrom_timing_enable(True)
+    _lib.nystrom_timing_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = _lib.nystrom_timing_read()
+    _lib.nystrom_timing_enable(False)
+    per_kernel = {name: {"avg_us_per_launch": 1e3 * ms / max(n, 1)} for name, (ms, n) in kern.items()}
+    roof = None
+    if "exact_error" in kern:
+        ms, launches = kern["exact_error"]
+        avg_s = ms / launches / 1e3
+        fl = 4.0 * wl.batch * wl.heads * wl.n * wl.n * wl.d  # Q K^T and P V
+        peak = MFMA_BF16_PEAK_TFLOPS
+        achieved = fl / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": "exact_error",
+                "algorithmic_flops": fl, "avg_us": round(avg_s * 1e6, 3)}
+    e = err.cpu().numpy()
+    result = {
+        "metric": "Nyström attention approximation-error diagnostic, heads/s (method vs exact attention, on device)",
+        "value": round(wl.batch * wl.heads / (ms_per_step / 1e3), 1), "unit": "heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "error", "batch": wl.batch, "heads": wl.heads, "n": wl.n, "d": wl.d,
+                   "m": wl.m, "iters": wl.iters, "io": wl.dtype},
+        "roofline": roof, "kernels": per_kernel,
+        "rel_error_per_head": {"mean": float(e.mean()), "min": float(e.min()), "max": float(e.max())},
+    }
+    if not args.no_parity:
+        from oracle import approximation_error
+        b0 = min(wl.batch, 1)
+        ref = approximation_error(inp["Q"][:b0], inp["K"][:b0], inp["V"][:b0], wl.m, wl.iters)
+        result["parity_max_abs_vs_oracle_first_batch_entry"] = float(np.abs(e[:b0] - ref).max())
     print(json.dumps(result), flush=True)
     return 0
 

@@ -32,6 +32,8 @@ EXPORTS = (
     "nystrom_attn_bwd",
     "nystrom_layer_workspace_bytes",
     "nystrom_layer_fwd",
+    "nystrom_attn_error_workspace_bytes",
+    "nystrom_attn_error",
     "nystrom_dconv_fwd",
     "nystrom_strerror",
     "nystrom_abi_version",
@@ -68,6 +70,10 @@ def load():
     lib.nystrom_layer_workspace_bytes.restype = sz
     lib.nystrom_layer_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, sz, vp]
     lib.nystrom_layer_fwd.restype = i
+    lib.nystrom_attn_error_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.nystrom_attn_error_workspace_bytes.restype = sz
+    lib.nystrom_attn_error.argtypes = [vp, vp, vp, i, i, i, i, i, vp, i, i, vp, sz, vp]
+    lib.nystrom_attn_error.restype = i
     lib.nystrom_dconv_fwd.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp]
     lib.nystrom_dconv_fwd.restype = i
     lib.nystrom_strerror.argtypes = [i]
@@ -145,6 +151,16 @@ def nystrom_layer_fwd(X, Wqkv, Wo, conv_w, n, d, m, heads, iters, Y, batch, conv
                       workspace_bytes=0, stream=None) -> int:
     return int(load().nystrom_layer_fwd(_ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(conv_w), n, d, m, heads, iters, _ptr(Y),
                                         batch, conv_k, dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def nystrom_attn_error_workspace_bytes(batch, heads, n, d, m, dtype) -> int:
+    return int(load().nystrom_attn_error_workspace_bytes(batch, heads, n, d, m, dtype))
+
+
+def nystrom_attn_error(Q, K, V, n, d, m, heads, iters, err, batch, dtype, workspace=None, workspace_bytes=0,
+                       stream=None) -> int:
+    return int(load().nystrom_attn_error(_ptr(Q), _ptr(K), _ptr(V), n, d, m, heads, iters, _ptr(err), batch, dtype,
+                                         _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def nystrom_dconv_fwd(V, conv_w, n, d, heads, batch, conv_k, dtype, out, stream=None) -> int:

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnystrom.so")
 
-SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_backward.hip", "nys_layer.hip", "nys_launch.hip", "nys_abi.hip",
-           "nys_timing.hip"]
+SOURCES = ["nys_landmarks.hip", "nys_apply.hip", "nys_backward.hip", "nys_layer.hip", "nys_error.hip", "nys_launch.hip",
+           "nys_abi.hip", "nys_timing.hip"]
 ROCM_LIB = "/opt/rocm/lib"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

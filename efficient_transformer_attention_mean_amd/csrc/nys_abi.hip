@@ -201,6 +201,44 @@ int nystrom_layer_fwd(const void* X, const void* Wqkv, const void* Wo, const flo
   }
 }
 
+size_t nystrom_attn_error_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype) {
+  if (check_shape(batch, heads, n, d, m, 0) != NYS_OK) return 0;
+  if (dtype != NYS_F32 && dtype != NYS_BF16) return 0;
+  nys::ErrLayout L;
+  if (!nys::make_error_layout(batch, heads, n, d, m, dtype == NYS_BF16, &L)) return 0;
+  return L.total;
+}
+
+int nystrom_attn_error(const void* Q, const void* K, const void* V, int n, int d, int m, int heads, int iters,
+                       float* err, int batch, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!Q || !K || !V || !err) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    nys::ErrLayout L;
+    if (!nys::make_error_layout(batch, heads, n, d, m, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    bool owned = false;
+    if (!ws) {
+      if (hipMallocAsync(reinterpret_cast<void**>(&ws), L.total, s) != hipSuccess) return NYS_EHIP;
+      owned = true;
+    } else if (workspace_bytes < L.total) {
+      return NYS_EWORKSPACE;
+    }
+    nys::Problem p{Q, K, V, nullptr, nullptr, batch, heads, n, d, m, iters, 0, dtype == NYS_BF16};
+    hipError_t e = nys::launch_error(p, L, ws, err, s);
+    if (owned) {
+      hipError_t f = hipFreeAsync(ws, s);
+      if (e == hipSuccess) e = f;
+    }
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
 int nystrom_dconv_fwd(const void* V, const float* conv_w, int n, int d, int heads, int batch, int conv_k, int dtype,
                       void* out, void* stream) {
   try {

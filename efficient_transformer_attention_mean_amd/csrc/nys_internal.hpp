@@ -121,6 +121,18 @@ struct LayerProblem {
 };
 
 hipError_t launch_layer(const LayerProblem& p, const LayerLayout& L, char* ws, hipStream_t s);
+
+// Approximation-error diagnostic: the forward's regions, the attention
+// output without the skip ([bh][n][d], I/O type) and per-block partial sums.
+struct ErrLayout {
+  WsLayout fwd;
+  size_t onys, part;
+  size_t total;
+  int ntile;  // 64-query blocks per head
+};
+
+bool make_error_layout(int batch, int heads, int n, int d, int m, bool bf16, ErrLayout* L);
+hipError_t launch_error(const Problem& p, const ErrLayout& L, char* ws, float* err, hipStream_t s);
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,
                         int d, int conv_k, bool bf16, hipStream_t s);
 

@@ -185,6 +185,25 @@ int nystrom_layer_fwd(const void* X, const void* Wqkv, const void* Wo, const flo
                       int batch, int conv_k, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Approximation-error diagnostic: for every (batch, head), the relative
+ * Frobenius distance between the attention output of nystrom_attn_fwd (skip
+ * excluded: it is exact) and exact softmax attention softmax(Q K^T / sqrt d) V
+ * ("Nyströmformer: ...", Eq. 2; the page's closing discussion proposes
+ * measuring the approximation error per example):
+ *   err[b * heads + h] = ||O_nys - O_exact||_F / ||O_exact||_F
+ *   Q, K, V, n, d, m, heads, iters, batch, dtype: as for nystrom_attn_fwd
+ *   err         DEVICE pointer, fp32 [batch][heads], written
+ *   workspace   at least nystrom_attn_error_workspace_bytes(), or NULL
+ * The exact attention costs O(n^2 d) per head (matrix cores, online softmax,
+ * no n x n matrix is stored).  O_nys is rounded to `dtype` as the forward's
+ * output is; for NYS_BF16 the exact side uses bf16 operands with fp32
+ * accumulation, so err carries an absolute uncertainty of about 2e-3.
+ * Return codes and stream behaviour as for nystrom_attn_fwd. */
+size_t nystrom_attn_error_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype);
+int nystrom_attn_error(const void* Q, const void* K, const void* V, int n, int d, int m, int heads,
+                       int iters, float* err, int batch, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Depthwise-convolution skip alone: out = DConv(V) with the filters and
  * padding described at the top ("Putting It Together", Figure 4's DConv path).
  *   V, out      [batch][heads][n][d] of `dtype` (out must not alias V)
