@@ -76,6 +76,12 @@ def backward_flops(wl, kernel: str) -> float:
         return rows * 2 * (5 * md + 2 * kd)  # scores, dBV V^T, dS^T Qt, B^T dBV, dS K; skip transpose, filter gradient
     if kernel == "bwd_rows_dq":
         return rows * 2 * 3 * md           # scores, dO W^T, dS Kt
+    if kernel == "bwd_landmarks":
+        # per head: 4 products per recomputed forward step, 11 per step of the
+        # reverse pass (m x m x m each), dZ, dBV, dQt_A, dKt_A (m x m x d each)
+        m3, steps = float(wl.m) ** 3, wl.iters
+        per_head = 2 * m3 * (11 * steps + 4 * max(steps - 1, 0)) + 8.0 * wl.m * wl.m * wl.d
+        return wl.batch * wl.heads * per_head
     return 0.0
 
 
@@ -612,8 +618,9 @@ def backward_bench(args, wl, dev) -> int:
         fl = backward_flops(wl, dom)
         if fl:
             # bf16 I/O at d = 32, 64 runs the products on the matrix cores
-            # (bf16 peak); otherwise they are fp32 vector work.
-            mm = wl.dtype == "bf16" and wl.d in (32, 64)
+            # (bf16 peak); otherwise they are fp32 vector work.  The
+            # landmark-side block always uses the matrix cores.
+            mm = (wl.dtype == "bf16" and wl.d in (32, 64)) or dom == "bwd_landmarks"
             peak = MFMA_BF16_PEAK_TFLOPS if mm else FP32_VECTOR_PEAK_TFLOPS
             achieved = fl / avg_s / 1e12
             roof = {"bound": "mfma" if mm else "alu", "achieved": round(achieved, 2), "peak": peak,

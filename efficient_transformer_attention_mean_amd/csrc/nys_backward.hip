@@ -700,45 +700,151 @@ __device__ __forceinline__ B8 pack_b(const f32x4_t& lo, const f32x4_t& hi) {
   return b;
 }
 
+// The skip's share of the backward, per tile of 64 rows with a 16-row halo:
+// dV = DConv^T(dO) (written as the initial dV, bf16) and the partials of the
+// filter gradient dw[f][t] = sum_i dO[i][f] V[i + t - R][f].  A filter of
+// conv_k <= 33 taps is centred in 33 (offset off), so tap t of 33 reads row
+// i - t + 16 in the transpose and V row i + t - 16 in the filter gradient.
 template <int D>
-struct KeyMmSmem {
-  static constexpr int PD = D + 8, PK = 64 + 8, HR = kMmTile + 32;
-  uint16_t qa[64][PD];   // Qt * log2(e)/sqrt(d), landmark rows (A of the scores)
-  uint16_t da[64][PD];   // dBV rows (A of dB)
-  uint16_t qT[D][PK];    // Qt^T, landmarks in mm_slot order (A of dK^T)
-  uint16_t dT[D][PK];    // dBV^T, mm_slot order (A of dV^T)
-  uint16_t kr[kMmTile][PD];  // key rows of the tile
-  uint16_t kT[D][PK];        // the same transposed (B of dQt)
-  uint16_t vh[HR][PD];       // V rows with the skip halo
-  uint16_t gh[HR][PD];       // dO rows with the skip halo
-  uint16_t sT[64][PK];       // dS^T of the tile (A of dQt)
-  float cv[kMmTile][D + 4];  // skip-transpose part of dV for the tile
-  float stm[64], stl[64], dlt[64];
+struct SkipSmem {
+  static constexpr int PD = D + 8, HR = kMmTile + 32;
+  uint16_t vh[HR][PD];       // V rows with the halo
+  uint16_t gh[HR][PD];       // dO rows with the halo
+  float cv[kMmTile][D + 4];  // DConv^T(dO) of the tile
   float wsh[D * 33];         // filters centred in 33 taps (zero outside)
 };
 
 template <int D>
+__global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                  const float* __restrict__ conv_w, uint16_t* __restrict__ dV,
+                                                  float* __restrict__ pdwc, int n, int heads, int conv_k, int chunk,
+                                                  int nchunks) {
+  using SM = SkipSmem<D>;
+  constexpr int NTB = 5;                  // tap groups of 8 (conv_k <= 33)
+  constexpr int KPT = kMmTile * D / 256;  // transpose rows per thread
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  const int tid = threadIdx.x, ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
+  const size_t hoff = (size_t)bh * n * D;
+  const int off = (33 - conv_k) / 2;
+  for (int e = tid; e < D * 33; e += 256) {
+    const int f = e / 33, t = e % 33 - off;
+    sm.wsh[e] = (t >= 0 && t < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + t] : 0.f;
+  }
+  float awc[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) awc[a][u] = 0.f;
+
+  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
+    __syncthreads();
+    for (int e = tid; e < SM::HR * (D / 8); e += 256) {
+      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 - 16 + rr;
+      const bool in = row >= 0 && row < n;
+      *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) =
+          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) =
+          in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    {
+      // Transpose for rows r0 .. r0 + KPT - 1 of feature f from a register
+      // window of the KPT + 32 dO values they read.
+      const int f = tid % D, r0 = (tid / D) * KPT;
+      float w33[33], win[KPT + 32];
+#pragma unroll
+      for (int t = 0; t < 33; ++t) w33[t] = sm.wsh[f * 33 + t];
+#pragma unroll
+      for (int p = 0; p < KPT + 32; ++p) win[p] = bf16_to_f32(sm.gh[r0 + p][f]);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        float a = 0.f;
+#pragma unroll
+        for (int t = 0; t < 33; ++t) a = fmaf(w33[t], win[u - t + 32], a);
+        sm.cv[r0 + u][f] = a;
+      }
+    }
+    // Filter gradient with a sliding window over the V rows (taps past 32
+    // read clamped rows and are dropped).
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int item = tid + 256 * a;
+      if (item < D * NTB) {
+        const int f = item % D, t0 = 8 * (item / D);
+        const int rows = min(kMmTile, kend - i0);
+        float vw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vw[u] = bf16_to_f32(sm.vh[min(t0 + u, SM::HR - 1)][f]);
+        for (int r = 0; r < rows; ++r) {
+          const float gv = bf16_to_f32(sm.gh[16 + r][f]);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, vw[u], awc[a][u]);
+#pragma unroll
+          for (int u = 0; u < 7; ++u) vw[u] = vw[u + 1];
+          vw[7] = bf16_to_f32(sm.vh[min(r + 1 + t0 + 7, SM::HR - 1)][f]);
+        }
+      }
+    }
+    __syncthreads();
+    // dV (skip part) rows of the tile, 16-byte stores.
+    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
+      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 + rr;
+      if (row < kend) {
+        B8 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o.u[q] = pack_bf16x2(sm.cv[rr][c8 + 2 * q], sm.cv[rr][c8 + 2 * q + 1]);
+        *reinterpret_cast<uint4*>(dV + hoff + (size_t)row * D + c8) = o.q;
+      }
+    }
+  }
+  const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int item = tid + 256 * a;
+    if (item < D * NTB) {
+      const int f = item % D, t0 = 8 * (item / D);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = t0 + u - off;  // tap of the conv_k-tap filter
+        if (t >= 0 && t < conv_k) pdwc[wb + (size_t)f * conv_k + t] = awc[a][u];
+      }
+    }
+  }
+}
+
+template <int D>
+struct KeyMmSmem {
+  static constexpr int PD = D + 8, PK = 64 + 8;
+  uint16_t qa[64][PD];       // Qt * log2(e)/sqrt(d), landmark rows (A of the scores)
+  uint16_t da[64][PD];       // dBV rows (A of dB)
+  uint16_t qT[D][PK];        // Qt^T, landmarks in mm_slot order (A of dK^T)
+  uint16_t dT[D][PK];        // dBV^T, mm_slot order (A of dV^T)
+  uint16_t kr[kMmTile][PD];  // key rows of the tile
+  uint16_t kT[D][PK];        // the same transposed (B of dQt)
+  uint16_t vr[kMmTile][PD];  // V rows of the tile
+  uint16_t sT[64][PK];       // dS^T of the tile (A of dQt)
+  float stm[64], stl[64], dlt[64];
+};
+
+// skip_in_dv: dV already holds the skip's part (k_bwd_skip ran first) and the
+// attention part is added to it.
+template <int D>
 __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                                    const uint16_t* __restrict__ dO, const float* __restrict__ conv_w,
                                                     const float* __restrict__ Qt, const float* __restrict__ BV,
                                                     const float* __restrict__ dBVg, const float* __restrict__ dKt,
                                                     const float* __restrict__ pmax, const float* __restrict__ psum,
                                                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                                                    float* __restrict__ pdqt, float* __restrict__ pdwc, int n, int m,
-                                                    int heads, int conv_k, int chunk, int nchunks, int fchunks,
-                                                    float sl2e, float scale) {
+                                                    float* __restrict__ pdqt, int n, int m, int skip_in_dv, int chunk,
+                                                    int nchunks, int fchunks, float sl2e, float scale) {
   using SM = KeyMmSmem<D>;
   constexpr int KC = D / 32, ND = D / 16, PER = ND;  // dQt tiles per wave: 4 * ND / 4
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
+  const int ch = blockIdx.x, bh = blockIdx.y;
   const size_t hoff = (size_t)bh * n * D, md = (size_t)bh * m * D;
-  // A filter of conv_k <= 33 taps is centred in 33 (offset off): tap t of
-  // 33 reads row i - t + 16 in the transpose and V row i + t - 16 in the
-  // filter gradient, so the halo is always 16 rows.
-  const bool conv = conv_k > 0;
-  const int R = conv ? 16 : 0, off = conv ? (33 - conv_k) / 2 : 0;
 
   for (int e = tid; e < 64 * D; e += 256) {
     const int j = e / D, f = e % D;
@@ -747,10 +853,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
     sm.da[j][f] = bf(db);
     sm.qT[f][mm_slot(j)] = bf(q);
     sm.dT[f][mm_slot(j)] = bf(db);
-  }
-  for (int e = tid; e < D * 33; e += 256) {
-    const int f = e / 33, t = e % 33 - off;
-    sm.wsh[e] = (conv && t >= 0 && t < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + t] : 0.f;
   }
   if (tid < 64) {
     const int j = tid;
@@ -770,12 +872,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
   f32x4_t aq[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) aq[u] = zero4();
-  constexpr int NTB = 5;  // taps in groups of 8 (conv_k <= 33)
-  float awc[2][8];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) awc[a][u] = 0.f;
   const int seg = (n + m - 1) / m;
   const float inv_seg = 1.f / (float)seg;
 
@@ -784,44 +880,16 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
     __syncthreads();
     for (int e = tid; e < kMmTile * (D / 8); e += 256) {
       const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, key = i0 + rr;
+      const bool in = key < kend;
       B8 v;
-      v.q = key < kend ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+      v.q = in ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(&sm.kr[rr][c8]) = v.q;
 #pragma unroll
       for (int q = 0; q < 8; ++q) sm.kT[c8 + q][rr] = v.h[q];
-    }
-    for (int e = tid; e < (kMmTile + 2 * R) * (D / 8); e += 256) {
-      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 - R + rr;
-      const bool in = row >= 0 && row < n;
-      *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) =
-          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) =
-          in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.vr[rr][c8]) =
+          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
-
-    if (conv) {
-      // Skip transpose for keys r0 .. r0 + KPT - 1 of feature f: out[u] =
-      // sum_t w[f][t] dO[r0 + u - t + 16], from a register window of the
-      // KPT + 32 dO values it reads.
-      constexpr int KPT = kMmTile * D / 256;
-      const int f = tid % D, r0 = (tid / D) * KPT;
-      float w33[33], win[KPT + 32], out[KPT];
-#pragma unroll
-      for (int t = 0; t < 33; ++t) w33[t] = sm.wsh[f * 33 + t];
-#pragma unroll
-      for (int p = 0; p < KPT + 32; ++p) win[p] = bf16_to_f32(sm.gh[r0 + p][f]);
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        float a = 0.f;
-#pragma unroll
-        for (int t = 0; t < 33; ++t) a = fmaf(w33[t], win[u - t + 32], a);
-        out[u] = a;
-      }
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) sm.cv[r0 + u][f] = out[u];
-      __syncthreads();
-    }
 
     // Scores S'^T and dB^T for this wave's 16 keys (key = i0 + 16 wave + c).
     const int kl = 16 * wave + c, key = i0 + kl;
@@ -833,7 +901,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const B8 kb = lds8(&sm.kr[kl][kc * 32 + 8 * g]);
-        const B8 vb = lds8(&sm.vh[R + kl][kc * 32 + 8 * g]);
+        const B8 vb = lds8(&sm.vr[kl][kc * 32 + 8 * g]);
         s = mfma(lds8(&sm.qa[mt * 16 + c][kc * 32 + 8 * g]), kb, s);
         db = mfma(lds8(&sm.da[mt * 16 + c][kc * 32 + 8 * g]), vb, db);
       }
@@ -845,7 +913,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
         ds[mt][i] = b * (db[i] - sm.dlt[j]);
       }
     }
-    // dK^T = Qt^T dS^T and dV^T = dBV^T B^T (+ the skip transpose).
+    // dK^T = Qt^T dS^T and dV^T = dBV^T B^T (added to the skip's part).
     const float* dkt = dKt + md + (size_t)min(key / seg, m - 1) * D;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
@@ -859,16 +927,24 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
         const int f0 = nd * 16 + 4 * g;
         const float4 kt4 = *reinterpret_cast<const float4*>(dkt + f0);
         const float ktv[4] = {kt4.x, kt4.y, kt4.z, kt4.w};
+        uint2* vdst = reinterpret_cast<uint2*>(dV + hoff + (size_t)key * D + f0);
+        float sk[4] = {0.f, 0.f, 0.f, 0.f};
+        if (skip_in_dv) {
+          const uint2 prev = *vdst;
+          sk[0] = __uint_as_float(prev.x << 16);
+          sk[1] = __uint_as_float(prev.x & 0xffff0000u);
+          sk[2] = __uint_as_float(prev.y << 16);
+          sk[3] = __uint_as_float(prev.y & 0xffff0000u);
+        }
         float vk[4], vv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           vk[i] = fmaf(scale, ak[i], ktv[i] * inv_seg);
-          vv[i] = conv ? av[i] + sm.cv[kl][f0 + i] : av[i];
+          vv[i] = av[i] + sk[i];
         }
         *reinterpret_cast<uint2*>(dK + hoff + (size_t)key * D + f0) =
             make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
-        *reinterpret_cast<uint2*>(dV + hoff + (size_t)key * D + f0) =
-            make_uint2(pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3]));
+        *vdst = make_uint2(pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3]));
       }
     }
     // dS^T of the tile -> LDS, then dQt_B += dS^T K over the tile's keys.
@@ -884,30 +960,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       for (int kc = 0; kc < 2; ++kc)
         aq[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.kT[nd * 16 + c][kc * 32 + 8 * g]), aq[u]);
     }
-    // Filter gradient: item (f, tap group tb), taps 8 tb + u of 33:
-    // dw[f][t] += sum_r dO[r][f] V[r + t - 16][f], with a sliding register
-    // window over the V rows (taps past 32 read clamped rows and are dropped).
-    if (conv) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int item = tid + 256 * a;
-        if (item < D * NTB) {
-          const int f = item % D, t0 = 8 * (item / D);
-          const int rows = min(kMmTile, kend - i0);
-          float vw[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) vw[u] = bf16_to_f32(sm.vh[min(t0 + u, SM::HR - 1)][f]);
-          for (int r = 0; r < rows; ++r) {
-            const float gv = bf16_to_f32(sm.gh[16 + r][f]);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, vw[u], awc[a][u]);
-#pragma unroll
-            for (int u = 0; u < 7; ++u) vw[u] = vw[u + 1];
-            vw[7] = bf16_to_f32(sm.vh[min(r + 1 + t0 + 7, SM::HR - 1)][f]);
-          }
-        }
-      }
-    }
   }
   const size_t base = ((size_t)bh * nchunks + ch) * m * D;
 #pragma unroll
@@ -917,21 +969,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
     for (int i = 0; i < 4; ++i) {
       const int j = mt * 16 + 4 * g + i;
       if (j < m) pdqt[base + (size_t)j * D + nd * 16 + c] = scale * aq[u][i];
-    }
-  }
-  if (conv) {
-    const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int item = tid + 256 * a;
-      if (item < D * NTB) {
-        const int f = item % D, t0 = 8 * (item / D);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int t = t0 + u - off;  // tap of the conv_k-tap filter
-          if (t >= 0 && t < conv_k) pdwc[wb + (size_t)f * conv_k + t] = awc[a][u];
-        }
-      }
     }
   }
 }
@@ -1231,6 +1268,17 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   // Key side: dK, dV and the partials of dQt_B and the filter gradient.
   if constexpr (MM) {
     const int ck = p.conv_w ? p.conv_k : 0;
+    if (ck > 0) {
+      const int bytes = (int)sizeof(SkipSmem<D>);
+      auto kern = &k_bwd_skip<D>;
+      static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (attr != hipSuccess) return attr;
+      KernelTimer kt_("bwd_skip", s);
+      kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO),
+                                              p.conv_w, static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck,
+                                              L.kchunk, L.nk);
+    }
     const int bytes = (int)sizeof(KeyMmSmem<D>);
     auto kern = &k_bwd_key_mm<D>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1238,10 +1286,9 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("bwd_keys", s);
     kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
-                                            static_cast<const uint16_t*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv),
-                                            F(L.dkt), w.pmax, w.psum, static_cast<uint16_t*>(bp.dK),
-                                            static_cast<uint16_t*>(bp.dV), F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads,
-                                            ck, L.kchunk, L.nk, w.nchunks, sl2e, scale);
+                                            w.Qt, w.BV, F(L.dbv), F(L.dkt), w.pmax, w.psum,
+                                            static_cast<uint16_t*>(bp.dK), static_cast<uint16_t*>(bp.dV), F(L.pdqt),
+                                            p.n, p.m, ck > 0 ? 1 : 0, L.kchunk, L.nk, w.nchunks, sl2e, scale);
   } else {
     const int ck = p.conv_w ? p.conv_k : 0;
     const int bytes = (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 + 3 * 64 + D * (ck > 0 ? ck : 1)) * 4;
