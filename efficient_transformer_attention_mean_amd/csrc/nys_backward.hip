@@ -342,29 +342,38 @@ __global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(const float* __
     ninf = fmaxf(ninf, sm.row[i]);
   }
   const float cz = 1.f / (n1 * ninf);
-  float* zsh = zs + (size_t)bh * iters * MP * MP;
+  float* zsh = zs + (size_t)bh * iters * 4 * MP * MP;
   for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     sm.Zk[i][j] = cz * sm.A[j][i];
   }
   __syncthreads();
 
-  // Forward iterates Z_0 .. Z_{iters-1} -> zs (Z_k in sm.Zk at step k).
+  // Forward steps: Z_k, X_k = A Z_k, T1_k = X_k (7I - X_k), T2_k = X_k (15I -
+  // T1_k) -> zs[k][0..3] for k < iters (the reverse pass reads them back),
+  // and Z_{k+1} = Z_k (13I - T2_k) / 4 in sm.Zk.
+  const size_t MM2 = (size_t)MP * MP;
+  auto save = [&](float (*M)[MP + 4], int k, int which) {
+    for (int e = tid; e < MP * MP; e += NTH) zsh[((size_t)k * 4 + which) * MM2 + e] = M[e / MP][e % MP];
+  };
   for (int k = 0; k < iters; ++k) {
-    for (int e = tid; e < MP * MP; e += NTH) zsh[(size_t)k * MP * MP + e] = sm.Zk[e / MP][e % MP];
-    if (k + 1 == iters) break;
+    save(sm.Zk, k, 0);
     land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
     });
     __syncthreads();
+    save(sm.X, k, 1);
     land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.X, -1.f, 7.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.T1[r0 + i][cc] = v[i];
     });
     __syncthreads();
+    save(sm.T1, k, 2);
     land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.T2[r0 + i][cc] = v[i];
     });
     __syncthreads();
+    save(sm.T2, k, 3);
+    if (k + 1 == iters) break;
     land_mm<MP, PR, false, false>(sm.Zk, 0.25f, 0.f, sm.T2, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
     });
@@ -378,19 +387,15 @@ __global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(const float* __
   // Reverse through the steps.  Mat pointers let dZ and T2 trade places.
   Mat dZ = sm.dZ, T2 = sm.T2;
   for (int k = iters - 1; k >= 0; --k) {
-    for (int e = tid; e < MP * MP; e += NTH) sm.Zk[e / MP][e % MP] = zsh[(size_t)k * MP * MP + e];
+    // Z_k, X_k, T1_k, T2_k of the forward step back from zs.
+    for (int e = tid; e < MP * MP; e += NTH) {
+      const int i = e / MP, j = e % MP;
+      sm.Zk[i][j] = zsh[((size_t)k * 4 + 0) * MM2 + e];
+      sm.X[i][j] = zsh[((size_t)k * 4 + 1) * MM2 + e];
+      sm.T1[i][j] = zsh[((size_t)k * 4 + 2) * MM2 + e];
+      T2[i][j] = zsh[((size_t)k * 4 + 3) * MM2 + e];
+    }
     __syncthreads();
-    land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
-    });
-    __syncthreads();
-    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.X, -1.f, 7.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.T1[r0 + i][cc] = v[i];  // T1 = X (7I - X)
-    });
-    __syncthreads();
-    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) T2[r0 + i][cc] = v[i];  // T2 = X (15I - T1)
-    });
     // dT2 = -Z_k^T dZ / 4 (reads Zk, dZ; T2 is not read).
     land_mm<MP, PR, true, false>(sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
@@ -1203,7 +1208,7 @@ bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int c
   L->pdqt = take(md * L->nk);
   L->dqt = take(md);
   L->pdwc = take((size_t)BH * L->nk * d * (conv_k > 0 ? conv_k : 1) * 4);
-  L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * L->mp * L->mp * 4);
+  L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * 4 * L->mp * L->mp * 4);
   L->total = off;
   return true;
 }
