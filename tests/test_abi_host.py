@@ -149,3 +149,47 @@ def test_bwd_workspace_covers_the_forward_layout(lib):
         assert bwd > fwd > 0
     assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 640, 64, 80, 6, 0) == 0
     assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 64, 16, 8, 6, 35) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), _lib.NYS_EINVAL),
+    (dict(Wo=None), _lib.NYS_EINVAL),
+    (dict(dtype=7), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=2), _lib.NYS_EINVAL),
+    (dict(m=0), _lib.NYS_EINVAL),
+    (dict(d=48), _lib.NYS_EUNSUPPORTED),
+    (dict(workspace=FAKE, workspace_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_layer_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(X=FAKE, Wqkv=FAKE, Wo=FAKE, conv_w=None, n=64, d=16, m=8, heads=2, iters=6, Y=FAKE, batch=1,
+                conv_k=0, dtype=_lib.NYS_BF16, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    assert _lib.nystrom_layer_fwd(**args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.NYS_EINVAL),
+    (dict(err=None), _lib.NYS_EINVAL),
+    (dict(dtype=2), _lib.NYS_EINVAL),
+    (dict(m=65), _lib.NYS_EINVAL),
+    (dict(d=12), _lib.NYS_EUNSUPPORTED),
+    (dict(workspace=FAKE, workspace_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_error_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, n=64, d=16, m=8, heads=1, iters=6, err=FAKE, batch=1, dtype=_lib.NYS_F32,
+                workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_error(**args) == code
+
+
+def test_layer_and_error_workspaces_cover_the_forward(lib):
+    for shape in ((1, 1, 64, 16, 8), (8, 12, 512, 64, 64), (1, 3, 777, 32, 48)):
+        fwd = _lib.nystrom_attn_workspace_bytes(*shape)
+        for dt, es in ((_lib.NYS_F32, 4), (_lib.NYS_BF16, 2)):
+            B, H, n, d, m = shape
+            lay = _lib.nystrom_layer_workspace_bytes(*shape, dt)
+            err = _lib.nystrom_attn_error_workspace_bytes(*shape, dt)
+            assert lay >= fwd + 6 * B * H * n * d * es
+            assert err >= fwd + B * H * n * d * es
+    assert _lib.nystrom_layer_workspace_bytes(1, 1, 64, 16, 8, 9) == 0
+    assert _lib.nystrom_attn_error_workspace_bytes(1, 1, 64, 24, 8, 0) == 0
