@@ -246,18 +246,17 @@ __device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&k
 }
 
 template <int MP, int PR>
-__global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(const float* __restrict__ Qt, const float* __restrict__ Kt,
-                                                  const float* __restrict__ Aw, const float* __restrict__ Zw,
-                                                  const float* __restrict__ BV, const float* __restrict__ pdw,
-                                                  const float* __restrict__ pdkt, float* __restrict__ dWg,
-                                                  float* __restrict__ dBV, float* __restrict__ dKt,
-                                                  float* __restrict__ dQtA, float* __restrict__ zs, int m, int D,
-                                                  int nchunks, int iters, float scale) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+__device__ __forceinline__ void land_body(const float* __restrict__ Qt, const float* __restrict__ Kt,
+                                          const float* __restrict__ Aw, const float* __restrict__ Zw,
+                                          const float* __restrict__ BV, const float* __restrict__ pdw,
+                                          const float* __restrict__ pdkt, float* __restrict__ dWg,
+                                          float* __restrict__ dBV, float* __restrict__ dKt, float* __restrict__ dQtA,
+                                          float* __restrict__ zs, int m, int D, int nchunks, int iters, float scale,
+                                          int bh, unsigned char* smem_raw) {
   LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
   using Mat = float (*)[MP + 4];
   constexpr int NTH = LandTiles<MP>::NTH;
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m;
 
   // dW and dKt_F: fixed-order sums of the query-side partials.
@@ -719,33 +718,33 @@ struct SkipSmem {
   float wsh[D * 33];         // filters centred in 33 taps (zero outside)
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                                  const float* __restrict__ conv_w, uint16_t* __restrict__ dV,
-                                                  float* __restrict__ pdwc, int n, int heads, int conv_k, int chunk,
-                                                  int nchunks) {
+template <int D, int NTH>
+__device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                          const float* __restrict__ conv_w, uint16_t* __restrict__ dV,
+                                          float* __restrict__ pdwc, int n, int heads, int conv_k, int chunk,
+                                          int nchunks, int ch, int bh, unsigned char* smem_raw) {
   using SM = SkipSmem<D>;
-  constexpr int NTB = 5;                  // tap groups of 8 (conv_k <= 33)
-  constexpr int KPT = kMmTile * D / 256;  // transpose rows per thread
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+  constexpr int NTB = 5;                             // tap groups of 8 (conv_k <= 33)
+  constexpr int KPT = kMmTile * D / NTH;             // transpose rows per thread
+  constexpr int NIT = (D * NTB + NTH - 1) / NTH;     // filter-gradient items per thread
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, ch = blockIdx.x, bh = blockIdx.y, h = bh % heads;
+  const int tid = threadIdx.x, h = bh % heads;
   const size_t hoff = (size_t)bh * n * D;
   const int off = (33 - conv_k) / 2;
-  for (int e = tid; e < D * 33; e += 256) {
+  for (int e = tid; e < D * 33; e += NTH) {
     const int f = e / 33, t = e % 33 - off;
     sm.wsh[e] = (t >= 0 && t < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + t] : 0.f;
   }
-  float awc[2][8];
+  float awc[NIT][8];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NIT; ++a)
 #pragma unroll
     for (int u = 0; u < 8; ++u) awc[a][u] = 0.f;
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
   for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
     __syncthreads();
-    for (int e = tid; e < SM::HR * (D / 8); e += 256) {
+    for (int e = tid; e < SM::HR * (D / 8); e += NTH) {
       const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 - 16 + rr;
       const bool in = row >= 0 && row < n;
       *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) =
@@ -774,8 +773,8 @@ __global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V
     // Filter gradient with a sliding window over the V rows (taps past 32
     // read clamped rows and are dropped).
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int item = tid + 256 * a;
+    for (int a = 0; a < NIT; ++a) {
+      const int item = tid + NTH * a;
       if (item < D * NTB) {
         const int f = item % D, t0 = 8 * (item / D);
         const int rows = min(kMmTile, kend - i0);
@@ -794,7 +793,7 @@ __global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V
     }
     __syncthreads();
     // dV (skip part) rows of the tile, 16-byte stores.
-    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
+    for (int e = tid; e < kMmTile * (D / 8); e += NTH) {
       const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 + rr;
       if (row < kend) {
         B8 o;
@@ -806,8 +805,8 @@ __global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V
   }
   const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int item = tid + 256 * a;
+  for (int a = 0; a < NIT; ++a) {
+    const int item = tid + NTH * a;
     if (item < D * NTB) {
       const int f = item % D, t0 = 8 * (item / D);
 #pragma unroll
@@ -816,6 +815,38 @@ __global__ __launch_bounds__(256) void k_bwd_skip(const uint16_t* __restrict__ V
         if (t >= 0 && t < conv_k) pdwc[wb + (size_t)f * conv_k + t] = awc[a][u];
       }
     }
+  }
+}
+
+// Landmark-side blocks [0, bh_count) and, for DS > 0, the skip's blocks after
+// them in the same launch: the skip needs no landmark-side result, so its
+// blocks run on the CUs the per-head blocks leave idle.
+struct LandArgs {
+  const float *Qt, *Kt, *Aw, *Zw, *BV, *pdw, *pdkt;
+  float *dWg, *dBV, *dKt, *dQtA, *zs;
+  int m, D, nchunks, iters;
+  float scale;
+};
+struct SkipArgs {
+  const uint16_t *V, *dO;
+  const float* conv_w;
+  uint16_t* dV;
+  float* pdwc;
+  int n, heads, conv_k, chunk, nchunks;
+};
+
+template <int MP, int PR, int DS>
+__global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(LandArgs a, SkipArgs k, int bh_count) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  if ((int)blockIdx.x < bh_count) {
+    land_body<MP, PR>(a.Qt, a.Kt, a.Aw, a.Zw, a.BV, a.pdw, a.pdkt, a.dWg, a.dBV, a.dKt, a.dQtA, a.zs, a.m, a.D,
+                      a.nchunks, a.iters, a.scale, (int)blockIdx.x, smem_raw);
+    return;
+  }
+  if constexpr (DS > 0) {
+    const int b = (int)blockIdx.x - bh_count;
+    skip_body<DS, LandTiles<MP>::NTH>(k.V, k.dO, k.conv_w, k.dV, k.pdwc, k.n, k.heads, k.conv_k, k.chunk, k.nchunks,
+                                      b % k.nchunks, b / k.nchunks, smem_raw);
   }
 }
 
@@ -833,8 +864,8 @@ struct KeyMmSmem {
   float stm[64], stl[64], dlt[64];
 };
 
-// skip_in_dv: dV already holds the skip's part (k_bwd_skip ran first) and the
-// attention part is added to it.
+// skip_in_dv: dV already holds the skip's part (written by the skip blocks of
+// the landmark-side launch) and the attention part is added to it.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                     const float* __restrict__ Qt, const float* __restrict__ BV,
@@ -1246,44 +1277,39 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                             nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk, L.nq, sl2e,
                                             scale);
   }
-  // Landmark side.
+  // Landmark side (and, on the matrix-core path with a skip, the skip's
+  // transpose and filter gradient in the same launch).
   {
+    const int ck = p.conv_w ? p.conv_k : 0;
+    constexpr int DS = MM ? D : 0;
+    const int nskip = (MM && ck > 0) ? L.nk * BH : 0;
+    const LandArgs la{w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt), F(L.dqta),
+                      F(L.zs), p.m, D, L.nq, p.iters, scale};
+    const SkipArgs sa{static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), p.conv_w,
+                      static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck, L.kchunk, L.nk};
+    auto launch = [&](auto kern, int nth, int lbytes) -> hipError_t {
+      constexpr int DSZ = DS > 0 ? DS : 32;
+      const int sbytes = DS > 0 ? (int)sizeof(SkipSmem<DSZ>) : 0;
+      const int bytes = lbytes > sbytes ? lbytes : sbytes;
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (e != hipSuccess) return e;
+      KernelTimer kt_("bwd_landmarks", s);
+      kern<<<BH + nskip, nth, bytes, s>>>(la, sa, BH);
+      return hipSuccess;
+    };
     hipError_t e;
-    KernelTimer kt_("bwd_landmarks", s);
-    if (L.mp == 32) {
-      auto kern = &k_bwd_land<32, 3>;
-      if (!IO::kBf16) kern = &k_bwd_land<32, 6>;
-      const int bytes = (int)sizeof(LandSmem<32>);
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   bytes)) != hipSuccess)
-        return e;
-      kern<<<BH, LandTiles<32>::NTH, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
-                                  F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
-    } else {
-      auto kern = &k_bwd_land<64, 3>;
-      if (!IO::kBf16) kern = &k_bwd_land<64, 6>;
-      const int bytes = (int)sizeof(LandSmem<64>);
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   bytes)) != hipSuccess)
-        return e;
-      kern<<<BH, LandTiles<64>::NTH, bytes, s>>>(w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt),
-                                  F(L.dqta), F(L.zs), p.m, D, L.nq, p.iters, scale);
-    }
+    if (L.mp == 32)
+      e = IO::kBf16 ? launch(&k_bwd_land<32, 3, DS>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>))
+                    : launch(&k_bwd_land<32, 6, DS>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>));
+    else
+      e = IO::kBf16 ? launch(&k_bwd_land<64, 3, DS>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>))
+                    : launch(&k_bwd_land<64, 6, DS>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>));
+    if (e != hipSuccess) return e;
   }
   // Key side: dK, dV and the partials of dQt_B and the filter gradient.
   if constexpr (MM) {
     const int ck = p.conv_w ? p.conv_k : 0;
-    if (ck > 0) {
-      const int bytes = (int)sizeof(SkipSmem<D>);
-      auto kern = &k_bwd_skip<D>;
-      static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (attr != hipSuccess) return attr;
-      KernelTimer kt_("bwd_skip", s);
-      kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO),
-                                              p.conv_w, static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck,
-                                              L.kchunk, L.nk);
-    }
     const int bytes = (int)sizeof(KeyMmSmem<D>);
     auto kern = &k_bwd_key_mm<D>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
