@@ -14,7 +14,8 @@
 //           V^T P^T with V^T stored in the permuted chunk order);
 //   err   = sqrt(sum (O_nys - O_ex)^2 / sum O_ex^2), partial sums per block
 //           folded in block order by k_error_finish.
-// Products: single bf16 operands for bf16 I/O, bf16x3 splits for fp32 I/O.
+// Products: single bf16 operands for bf16 I/O, bf16x3 splits for fp32 I/O;
+// the operands sit in LDS as ready bf16 planes (one 16-byte read per fragment).
 #include <math.h>
 
 #include "nys_common.hpp"
@@ -34,17 +35,37 @@ __device__ __forceinline__ int err_slot(int j) {
   return (j & ~31) + 8 * ((jj & 15) >> 2) + (jj & 3) + ((jj & 16) ? 4 : 0);
 }
 
-template <int PR>
-__device__ __forceinline__ f32x4_t mm8(const float (&a)[8], const float (&b)[8], f32x4_t acc) {
-  if constexpr (PR == 1) {
-    B8 ah, bh;
-    round8(a, ah);
-    round8(b, bh);
-    return mfma(ah, bh, acc);
-  } else {
-    return mma_f32<3>(a, b, acc);
-  }
+// Operand planes in LDS: bf16 rows (hi, and lo for fp32 I/O where every
+// product is the bf16x3 sum hi*hi + hi*lo + lo*hi), written once per tile so
+// that each fragment is one 16-byte read.
+template <int NPL, int ROWS, int COLS>
+struct Planes {
+  static constexpr int P = COLS + 8;
+  uint16_t v[NPL][ROWS][P];
+};
+
+template <int NPL, int ROWS, int COLS>
+__device__ __forceinline__ void put(Planes<NPL, ROWS, COLS>& pl, int r, int c, float x) {
+  const uint16_t h = f32_to_bf16(x);
+  pl.v[0][r][c] = h;
+  if constexpr (NPL == 2) pl.v[1][r][c] = f32_to_bf16(x - bf16_to_f32(h));
 }
+
+template <int NPL, int ROWS, int COLS>
+__device__ __forceinline__ void frag(const Planes<NPL, ROWS, COLS>& pl, int r, int c0, B8& h, B8& l) {
+  h.q = *reinterpret_cast<const uint4*>(&pl.v[0][r][c0]);
+  if constexpr (NPL == 2) l.q = *reinterpret_cast<const uint4*>(&pl.v[1][r][c0]);
+}
+
+template <typename IO, int D>
+struct ErrSmem {
+  static constexpr int NPL = IO::kBf16 ? 1 : 2;
+  static constexpr int DP = D < 32 ? 32 : D;  // feature axis padded to a whole 32-wide chunk
+  Planes<NPL, kQT, DP> q;   // Q * log2(e)/sqrt(d), query rows
+  Planes<NPL, kKT, DP> k;   // key rows of the tile
+  Planes<NPL, D, kKT> vT;   // V^T of the tile, keys in err_slot order
+  float red[8];
+};
 
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_exact_error(const typename IO::T* __restrict__ Q,
@@ -52,20 +73,18 @@ __global__ __launch_bounds__(256) void k_exact_error(const typename IO::T* __res
                                                      const typename IO::T* __restrict__ V,
                                                      const typename IO::T* __restrict__ Onys,
                                                      float* __restrict__ part, int n, int ntile, float sl2e) {
-  constexpr int PR = IO::kBf16 ? 1 : 3;
-  constexpr int P = D + 4, KC = (D + 31) / 32, ND = D / 16;
-  extern __shared__ __align__(16) float lds[];
-  float* qs = lds;              // [kQT][P]   Q * log2(e)/sqrt(d)
-  float* ks = qs + kQT * P;     // [kKT][P]
-  float* vT = ks + kKT * P;     // [D][kKT + 4], keys in err_slot order
-  float* red = vT + D * (kKT + 4);  // [2][4]
+  using SM = ErrSmem<IO, D>;
+  constexpr int NPL = SM::NPL, DP = SM::DP, KC = DP / 32, ND = D / 16;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int qt = blockIdx.x, bh = blockIdx.y, q0 = qt * kQT;
   const size_t hoff = (size_t)bh * n * D;
 
-  for (int e = tid; e < kQT * D; e += 256) {
-    const int r = e / D, f = e % D, row = q0 + r;
-    qs[r * P + f] = row < n ? load_elem<IO>(Q + hoff + (size_t)row * D + f) * sl2e : 0.f;
+  for (int e = tid; e < kQT * DP; e += 256) {
+    const int r = e / DP, f = e % DP, row = q0 + r;
+    put(sm.q, r, f, (row < n && f < D) ? load_elem<IO>(Q + hoff + (size_t)row * D + f) * sl2e : 0.f);
+    if (DP > D && f >= D) put(sm.k, r, f, 0.f);  // padding columns of the key planes stay zero
   }
   const int ql = 16 * wave + c;  // this lane's query within the block
   float mrun = -INFINITY, lrun = 0.f;
@@ -73,32 +92,71 @@ __global__ __launch_bounds__(256) void k_exact_error(const typename IO::T* __res
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) acc[nd] = zero4();
 
+  // Key and value rows travel as 16-byte vectors; the next tile's vectors
+  // are fetched into registers while the current tile is computed.
+  using T = typename IO::T;
+  constexpr int VEC = 16 / (int)sizeof(T), RV = D / VEC, NV = kKT * RV, VPT = (NV + 255) / 256;
+  uint4 kv[VPT], vv[VPT];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int e = tid + 256 * u, key = k0 + e / RV, c0 = (e % RV) * VEC;
+      const bool in = e < NV && key < n;
+      kv[u] = in ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c0) : make_uint4(0, 0, 0, 0);
+      vv[u] = in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + c0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int e = tid + 256 * u;
+      if (e >= NV) continue;
+      const int r = e / RV, c0 = (e % RV) * VEC, slot = err_slot(r);
+      float xk[VEC], xv[VEC];
+      if constexpr (IO::kBf16) {
+        B8 a, b;
+        a.q = kv[u];
+        b.q = vv[u];
+        *reinterpret_cast<uint4*>(&sm.k.v[0][r][c0]) = kv[u];  // one plane: the bits themselves
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) sm.vT.v[0][c0 + q][slot] = b.h[q];
+        (void)xk;
+        (void)xv;
+        (void)a;
+      } else {
+        const float4 a = __builtin_bit_cast(float4, kv[u]), b = __builtin_bit_cast(float4, vv[u]);
+        xk[0] = a.x; xk[1] = a.y; xk[2] = a.z; xk[3] = a.w;
+        xv[0] = b.x; xv[1] = b.y; xv[2] = b.z; xv[3] = b.w;
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) {
+          put(sm.k, r, c0 + q, xk[q]);
+          put(sm.vT, c0 + q, slot, xv[q]);
+        }
+      }
+    }
+  };
+  fetch(0);
+
   for (int k0 = 0; k0 < n; k0 += kKT) {
     __syncthreads();
-    for (int e = tid; e < kKT * D; e += 256) {
-      const int r = e / D, f = e % D, key = k0 + r;
-      const bool in = key < n;
-      ks[r * P + f] = in ? load_elem<IO>(K + hoff + (size_t)key * D + f) : 0.f;
-      vT[f * (kKT + 4) + err_slot(r)] = in ? load_elem<IO>(V + hoff + (size_t)key * D + f) : 0.f;
-    }
+    stage();
     __syncthreads();
+    if (k0 + kKT < n) fetch(k0 + kKT);
 
     // S^T (keys x queries) for 4 tiles of 16 keys.
+    B8 bq[KC], bql[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) frag(sm.q, ql, kc * 32 + 8 * g, bq[kc], bql[kc]);
     f32x4_t s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = zero4();
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        float a[8], b[8];
-        const int f0 = kc * 32 + 8 * g;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const bool ok = f0 + u < D;
-          a[u] = ok ? ks[(kt * 16 + c) * P + f0 + u] : 0.f;
-          b[u] = ok ? qs[ql * P + f0 + u] : 0.f;
-        }
-        s[kt] = mm8<PR>(a, b, s[kt]);
+        B8 ah, al;
+        frag(sm.k, kt * 16 + c, kc * 32 + 8 * g, ah, al);
+        if constexpr (NPL == 2) s[kt] = mfma3(ah, al, bq[kc], bql[kc], s[kt]);
+        else s[kt] = mfma(ah, bq[kc], s[kt]);
       }
     }
     float mx = -INFINITY;
@@ -123,20 +181,26 @@ __global__ __launch_bounds__(256) void k_exact_error(const typename IO::T* __res
     lrun = lrun * corr + sum_over_groups(ps);
     mrun = mnew;
     // O^T += V^T P^T over the tile's keys.
+    B8 ph[2], pl[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float b[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[i] = s[2 * kk][i];
+        b[4 + i] = s[2 * kk + 1][i];
+      }
+      if constexpr (NPL == 2) split8(b, ph[kk], pl[kk]); else round8(b, ph[kk]);
+    }
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       acc[nd] *= corr;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        float a[8], b[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) a[u] = vT[(nd * 16 + c) * (kKT + 4) + kk * 32 + 8 * g + u];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          b[i] = s[2 * kk][i];
-          b[4 + i] = s[2 * kk + 1][i];
-        }
-        acc[nd] = mm8<PR>(a, b, acc[nd]);
+        B8 ah, al;
+        frag(sm.vT, nd * 16 + c, kk * 32 + 8 * g, ah, al);
+        if constexpr (NPL == 2) acc[nd] = mfma3(ah, al, ph[kk], pl[kk], acc[nd]);
+        else acc[nd] = mfma(ah, ph[kk], acc[nd]);
       }
     }
   }
@@ -162,13 +226,13 @@ __global__ __launch_bounds__(256) void k_exact_error(const typename IO::T* __res
     esum += shfl_xor(esum, o);
   }
   if (lane == 0) {
-    red[wave] = dsum;
-    red[4 + wave] = esum;
+    sm.red[wave] = dsum;
+    sm.red[4 + wave] = esum;
   }
   __syncthreads();
   if (tid == 0) {
-    part[((size_t)bh * ntile + qt) * 2] = (red[0] + red[1]) + (red[2] + red[3]);
-    part[((size_t)bh * ntile + qt) * 2 + 1] = (red[4] + red[5]) + (red[6] + red[7]);
+    part[((size_t)bh * ntile + qt) * 2] = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+    part[((size_t)bh * ntile + qt) * 2 + 1] = (sm.red[4] + sm.red[5]) + (sm.red[6] + sm.red[7]);
   }
 }
 
@@ -206,7 +270,7 @@ bool make_error_layout(int batch, int heads, int n, int d, int m, bool bf16, Err
 template <typename IO, int D>
 static hipError_t error_t(const Problem& p, const ErrLayout& L, char* ws, float* err, hipStream_t s) {
   using T = typename IO::T;
-  const int bytes = (kQT * (D + 4) + kKT * (D + 4) + D * (kKT + 4) + 8) * 4;
+  const int bytes = (int)sizeof(ErrSmem<IO, D>);
   auto kern = &k_exact_error<IO, D>;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
