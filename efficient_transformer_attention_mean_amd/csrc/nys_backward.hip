@@ -1014,7 +1014,7 @@ struct RowMmSmem {
   static constexpr int PD = D + 8, PK = 64 + 8;
   uint16_t ka[64][PD];   // Kt * log2(e)/sqrt(d) rows (A of the scores)
   uint16_t wa[64][PD];   // W rows (A of dF)
-  uint16_t kT[D][PK];    // Kt^T in mm_slot order (A of dQ^T)
+  uint16_t kT[DQ ? D : 1][PK];  // Kt^T in mm_slot order (A of dQ^T; the dQ pass only)
   uint16_t qr[kMmTile][PD], gr[kMmTile][PD];  // Q and dO rows of the tile
   uint16_t qT[DQ ? 1 : D][PK], gT[DQ ? 1 : D][PK];  // the same transposed (B of dKt, dW)
   uint16_t fT[DQ ? 1 : 64][PK], sT[DQ ? 1 : 64][PK];  // F^T, dS^T of the tile (A of dW, dKt)
@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
     const float k = j < m ? Kt[md + e] : 0.f;
     sm.ka[j][f] = bf(k * sl2e);
     sm.wa[j][f] = bf(j < m ? W[md + e] : 0.f);
-    sm.kT[f][mm_slot(j)] = bf(k);
+    if constexpr (DQ) sm.kT[f][mm_slot(j)] = bf(k);
   }
   f32x4_t aw[PER], ak[PER];
 #pragma unroll
@@ -1350,11 +1350,12 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (attr != hipSuccess) return attr;
-    const int nt = cdivi(p.n, kMmTile);
+    // One chunk of rows per block, as in the reduction pass: the landmark
+    // planes are built once per block rather than once per 64-row tile.
     KernelTimer kt_("bwd_rows_dq", s);
-    kern<<<dim3(nt, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                          w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), nullptr, nullptr, p.n,
-                                          p.m, kMmTile, nt, sl2e, scale);
+    kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
+                                            w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), nullptr, nullptr,
+                                            p.n, p.m, L.qchunk, L.nq, sl2e, scale);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, true>;
