@@ -77,11 +77,11 @@ def backward_flops(wl, kernel: str) -> float:
     if kernel == "bwd_rows_dq":
         return rows * 2 * 3 * md           # scores, dO W^T, dS Kt
     if kernel == "bwd_landmarks":
-        # per head: the recomputed forward steps (3 products each, 4 with the
-        # Z update), 8 products per step of the reverse pass (m x m x m each),
-        # dZ, dBV, dQt_A, dKt_A (m x m x d each)
+        # per head: 8 products per step of the reverse pass (m x m x m each;
+        # the forward steps are saved by the recomputed forward), dZ, dBV,
+        # dQt_A, dKt_A (m x m x d each)
         m3, steps = float(wl.m) ** 3, wl.iters
-        per_head = 2 * m3 * (8 * steps + 3 * steps + max(steps - 1, 0)) + 8.0 * wl.m * wl.m * wl.d
+        per_head = 2 * m3 * 8 * steps + 8.0 * wl.m * wl.m * wl.d
         return wl.batch * wl.heads * per_head
     return 0.0
 

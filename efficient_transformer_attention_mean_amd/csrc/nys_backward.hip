@@ -251,8 +251,8 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
                                           const float* __restrict__ BV, const float* __restrict__ pdw,
                                           const float* __restrict__ pdkt, float* __restrict__ dWg,
                                           float* __restrict__ dBV, float* __restrict__ dKt, float* __restrict__ dQtA,
-                                          float* __restrict__ zs, int m, int D, int nchunks, int iters, float scale,
-                                          int bh, unsigned char* smem_raw) {
+                                          const float* __restrict__ zs, int m, int D, int nchunks, int iters,
+                                          float scale, int bh, unsigned char* smem_raw) {
   LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
   using Mat = float (*)[MP + 4];
   constexpr int NTH = LandTiles<MP>::NTH;
@@ -341,45 +341,12 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     ninf = fmaxf(ninf, sm.row[i]);
   }
   const float cz = 1.f / (n1 * ninf);
-  float* zsh = zs + (size_t)bh * iters * 4 * MP * MP;
-  for (int e = tid; e < MP * MP; e += NTH) {
-    const int i = e / MP, j = e % MP;
-    sm.Zk[i][j] = cz * sm.A[j][i];
-  }
-  __syncthreads();
+  const float* zsh = zs + (size_t)bh * iters * 4 * MP * MP;
 
-  // Forward steps: Z_k, X_k = A Z_k, T1_k = X_k (7I - X_k), T2_k = X_k (15I -
-  // T1_k) -> zs[k][0..3] for k < iters (the reverse pass reads them back),
-  // and Z_{k+1} = Z_k (13I - T2_k) / 4 in sm.Zk.
+  // The forward steps Z_k, X_k, T1_k = X_k (7I - X_k), T2_k = X_k (15I -
+  // T1_k) for k < iters were saved to zs by the forward's pseudoinverse
+  // kernel (recomputed at the start of the call); the reverse pass reads them.
   const size_t MM2 = (size_t)MP * MP;
-  auto save = [&](float (*M)[MP + 4], int k, int which) {
-    for (int e = tid; e < MP * MP; e += NTH) zsh[((size_t)k * 4 + which) * MM2 + e] = M[e / MP][e % MP];
-  };
-  for (int k = 0; k < iters; ++k) {
-    save(sm.Zk, k, 0);
-    land_mm<MP, PR, false, false>(sm.A, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.X[r0 + i][cc] = v[i];
-    });
-    __syncthreads();
-    save(sm.X, k, 1);
-    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.X, -1.f, 7.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.T1[r0 + i][cc] = v[i];
-    });
-    __syncthreads();
-    save(sm.T1, k, 2);
-    land_mm<MP, PR, false, false>(sm.X, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.T2[r0 + i][cc] = v[i];
-    });
-    __syncthreads();
-    save(sm.T2, k, 3);
-    if (k + 1 == iters) break;
-    land_mm<MP, PR, false, false>(sm.Zk, 0.25f, 0.f, sm.T2, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
-    });
-    __syncthreads();
-    for (int e = tid; e < MP * MP; e += NTH) sm.Zk[e / MP][e % MP] = sm.dT2[e / MP][e % MP];
-    __syncthreads();
-  }
   for (int e = tid; e < MP * MP; e += NTH) sm.dA[e / MP][e % MP] = 0.f;
   __syncthreads();
 
@@ -1371,7 +1338,11 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s) {
+hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s) {
+  // The forward's pseudoinverse kernel also saves its steps for the reverse pass.
+  BwdProblem bp = bp0;
+  bp.fwd.zsave = reinterpret_cast<float*>(ws + L.zs);
+  bp.fwd.zmp = L.mp;
   const Problem& p = bp.fwd;
   const Ws w = resolve(L.fwd, ws);
   hipError_t e;

@@ -44,6 +44,10 @@ struct Problem {
   int batch, heads, n, d, m, iters, conv_k;
   bool bf16;
   const int* lens = nullptr;  // device int32 [batch]: tokens per sequence (right padding), or none
+  // Backward pass only: where the pseudoinverse kernels save each step
+  // (Z_k, X_k, T1_k, T2_k as fp32 [zmp][zmp], per head and step), or none.
+  float* zsave = nullptr;
+  int zmp = 0;
 };
 
 // Brackets the kernel launched inside its scope with events when per-kernel

@@ -157,7 +157,8 @@ __device__ __forceinline__ float4 plus_diag(int row, int col0, const f32x4_t& v,
 template <int MP, int PR>
 __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, const float* __restrict__ Kt,
                                                   float* __restrict__ Aout, float* __restrict__ Zout, int m,
-                                                  int d, float sl2e, int iters) {
+                                                  int d, float sl2e, int iters, float* __restrict__ zsave,
+                                                  int zmp) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PinvSmem<MP>& sm = *reinterpret_cast<PinvSmem<MP>*>(smem_raw);
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -246,6 +247,20 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
       *reinterpret_cast<float4*>(&sm.T[r][c0]) = plus_diag(r, c0, v, -1.f, 13.f);
     });
     __syncthreads();
+    if (zsave) {
+      // For the backward pass: Z_k, X_k, T1_k = 15I - U, T2_k = 13I - T
+      // ([zmp][zmp] fp32 each, zero beyond m).
+      float* zs = zsave + ((size_t)bh * iters + it) * 4 * zmp * zmp;
+      for (int e = tid; e < zmp * zmp; e += 256) {
+        const int i = e / zmp, j = e % zmp;
+        const bool in = i < MP && j < MP;
+        const float dg = i == j ? 1.f : 0.f;
+        zs[e] = in ? Z[i][j] : 0.f;
+        zs[zmp * zmp + e] = in ? Xb[i][j] : 0.f;
+        zs[2 * zmp * zmp + e] = in ? 15.f * dg - sm.U[i][j] : 0.f;
+        zs[3 * zmp * zmp + e] = in ? 13.f * dg - sm.T[i][j] : 0.f;
+      }
+    }
     lds_mm<MP, PR>(Z, sm.T, [&](int r, int c0, const f32x4_t& v) {
       *reinterpret_cast<float4*>(&Xb[r][c0]) = plus_diag(r, c0, v, 0.25f, 0.f);
     });
@@ -361,7 +376,8 @@ __device__ __forceinline__ void chain_mm(const B8 (&ph)[MP / 16][MP / 32], const
 template <int MP, int D>
 __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float* __restrict__ Qt,
                                           const float* __restrict__ Kt, float* __restrict__ Aout,
-                                          float* __restrict__ Zout, int m, float sl2e, int iters) {
+                                          float* __restrict__ Zout, int m, float sl2e, int iters,
+                                          float* __restrict__ zsave, int zmp) {
   using SM = PinvSmem2<MP>;
   constexpr int SP = SM::SP, RT = MP / 16, KC = MP / 32, CPT = MP / 4;
   constexpr int KCD = (D + 31) / 32;  // 32-wide chunks of the head dimension
@@ -515,11 +531,26 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
   store_bop<MP>(sm.zp[0], sm.zp[1], Zh, Zl, wave);
   __syncthreads();  // every wave has read the scores before X overwrites them
 
+  // For the backward pass: the column block `wave` of Z_k, X_k, T1_k =
+  // X_k (7I - X_k) and T2_k = X_k (15I - T1_k), fp32 [zmp][zmp] each.
+  auto save = [&](const f32x4_t (&v)[RT], int it, int which) {
+    float* zs = zsave + (((size_t)bh * iters + it) * 4 + which) * zmp * zmp;
+    const int col = 16 * wave + c;
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * t + 4 * g + i;
+        if (row < zmp && col < zmp) zs[(size_t)row * zmp + col] = v[t][i];
+      }
+  };
   for (int it = 0; it < iters; ++it) {
     f32x4_t acc[RT];
     B8 Th[KC], Tl[KC];
+    if (zsave) save(zf, it, 0);
     // X = A Z: store X for every wave; keep T1 = 7I - X (own columns).
     chain_mm<MP>(Ah, Al, Zh, Zl, acc);
+    if (zsave) save(acc, it, 1);
     {
       B8 xh[KC], xl[KC];
       to_bop<MP>(acc, 1.f, 0.f, wave, xh, xl);
@@ -531,8 +562,10 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
     load_aop<MP>(sm.xp[0], sm.xp[1], Ph, Pl);
     load_aop<MP>(sm.zp[0], sm.zp[1], Rh, Rl);  // in flight during the two X products
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T1
+    if (zsave) save(acc, it, 2);
     to_bop<MP>(acc, -1.f, 15.f, wave, Th, Tl);
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T3
+    if (zsave) save(acc, it, 3);
     to_bop<MP>(acc, -1.f, 13.f, wave, Th, Tl);
     chain_mm<MP>(Rh, Rl, Th, Tl, acc);  // Z T5
 #pragma unroll
@@ -982,6 +1015,8 @@ __device__ __forceinline__ void conv_operand(const float* __restrict__ conv_w, u
 struct LandmarkPassArgs {
   const void* K;
   const void* V;
+  float* zsave;  // the pseudoinverse steps for the backward pass, or nullptr
+  int zmp;
   const float *Qt, *Kt;
   float *A, *Z, *pacc, *pmax, *psum;
   const float* conv_w;
@@ -1008,7 +1043,7 @@ __global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
   int blk = blockIdx.x;
   if constexpr (PINV) {
     if (blk < a.npinv) {
-      pinv_head<64, D>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters);
+      pinv_head<64, D>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters, a.zsave, a.zmp);
       return;
     }
     blk -= a.npinv;
@@ -1232,14 +1267,16 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   const float sl2e = kLog2e / sqrtf((float)D);
   if (m <= 32) {
     KernelTimer kt_("pinv", s);
-    k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
+    k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
+                                                             p.zmp);
   } else if (m <= 64) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_lds<64, PR>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        (int)sizeof(PinvSmem<64>));
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("pinv", s);
-    k_pinv_lds<64, PR><<<BH, 256, sizeof(PinvSmem<64>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters);
+    k_pinv_lds<64, PR><<<BH, 256, sizeof(PinvSmem<64>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
+                                                             p.zmp);
   } else {
     {
       KernelTimer kt_("landmark_softmax", s);
@@ -1283,6 +1320,8 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   LandmarkPassArgs a;
   a.K = p.K;
   a.V = p.V;
+  a.zsave = p.zsave;
+  a.zmp = p.zmp;
   a.Qt = w.Qt;
   a.Kt = w.Kt;
   a.A = w.A;
