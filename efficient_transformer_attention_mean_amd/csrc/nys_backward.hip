@@ -215,14 +215,33 @@ __device__ __forceinline__ void land_mm(const float (*Pm)[MP + 4], float pa, flo
     f32x4_t acc = zero4();
 #pragma unroll 1
     for (int kc = 0; kc < MP; kc += 32) {
+      // Row-contiguous operands (P untransposed, Q transposed) are read as
+      // two 16-byte vectors; the others one element per k.
+      float pv[8], qv[8];
+      if constexpr (!TPa) {
+        const float4 u0 = *reinterpret_cast<const float4*>(&Pm[i][kc + 8 * g]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&Pm[i][kc + 8 * g + 4]);
+        pv[0] = u0.x; pv[1] = u0.y; pv[2] = u0.z; pv[3] = u0.w;
+        pv[4] = u1.x; pv[5] = u1.y; pv[6] = u1.z; pv[7] = u1.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pv[u] = Pm[kc + 8 * g + u][i];
+      }
+      if constexpr (TQa) {
+        const float4 u0 = *reinterpret_cast<const float4*>(&Qm[j][kc + 8 * g]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&Qm[j][kc + 8 * g + 4]);
+        qv[0] = u0.x; qv[1] = u0.y; qv[2] = u0.z; qv[3] = u0.w;
+        qv[4] = u1.x; qv[5] = u1.y; qv[6] = u1.z; qv[7] = u1.w;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qv[u] = Qm[kc + 8 * g + u][j];
+      }
       float a[8], b[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = kc + 8 * g + u;
-        const float pv = TPa ? Pm[k][i] : Pm[i][k];
-        const float qv = TQa ? Qm[j][k] : Qm[k][j];
-        a[u] = pa * pv + ((i == k && k < m) ? pb : 0.f);
-        b[u] = qa * qv + ((k == j && k < m) ? qb : 0.f);
+        a[u] = pa * pv[u] + ((i == k && k < m) ? pb : 0.f);
+        b[u] = qa * qv[u] + ((k == j && k < m) ? qb : 0.f);
       }
       acc = mma_f32<PR>(a, b, acc);
     }
@@ -350,8 +369,11 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
   for (int e = tid; e < MP * MP; e += NTH) sm.dA[e / MP][e % MP] = 0.f;
   __syncthreads();
 
-  // Reverse through the steps.  Mat pointers let dZ and T2 trade places.
-  Mat dZ = sm.dZ, T2 = sm.T2;
+  // Reverse through the steps, four dependency levels of two independent
+  // products each, one barrier per level.  dZ and three free slots rotate
+  // among the dZ, T2, dT2 and dX slots (fa receives T2_k, fb and fc the
+  // level-1 results, the old dZ slot dX).
+  Mat dZ = sm.dZ, fa = sm.T2, fb = sm.dT2, fc = sm.dX;
   for (int k = iters - 1; k >= 0; --k) {
     // Z_k, X_k, T1_k, T2_k of the forward step back from zs.
     for (int e = tid; e < MP * MP; e += NTH) {
@@ -359,58 +381,48 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
       sm.Zk[i][j] = zsh[((size_t)k * 4 + 0) * MM2 + e];
       sm.X[i][j] = zsh[((size_t)k * 4 + 1) * MM2 + e];
       sm.T1[i][j] = zsh[((size_t)k * 4 + 2) * MM2 + e];
-      T2[i][j] = zsh[((size_t)k * 4 + 3) * MM2 + e];
+      fa[i][j] = zsh[((size_t)k * 4 + 3) * MM2 + e];
     }
     __syncthreads();
-    // dT2 = -Z_k^T dZ / 4 (reads Zk, dZ; T2 is not read).
+    // Level 1: dT2 = -Z_k^T dZ / 4 -> fb;  dZ_k = dZ (13I - T2)^T / 4 -> fc.
     land_mm<MP, PR, true, false>(sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.dT2[r0 + i][cc] = v[i];
+      for (int i = 0; i < 4; ++i) fb[r0 + i][cc] = v[i];
+    });
+    land_mm<MP, PR, false, true>(dZ, 0.25f, 0.f, fa, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) fc[r0 + i][cc] = v[i];
     });
     __syncthreads();
-    // dZ_k (through the factor Z_k) = dZ (13I - T2)^T / 4, into the T2 slot.
-    {
-      f32x4_t keep[LandTiles<MP>::PER];
-      land_mm<MP, PR, false, true>(dZ, 0.25f, 0.f, T2, -1.f, 13.f, m,
-                                   [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
-      __syncthreads();
-      land_store<MP>(T2, keep);
-      Mat tmp = dZ;
-      dZ = T2;
-      T2 = tmp;
-    }
-    // dX = dT2 (15I - T1)^T.
-    land_mm<MP, PR, false, true>(sm.dT2, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.dX[r0 + i][cc] = v[i];
+    // Level 2: dX = dT2 (15I - T1)^T -> the old dZ slot;  dT1 = -X^T dT2 -> fa.
+    Mat dX = dZ;
+    land_mm<MP, PR, false, true>(fb, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) dX[r0 + i][cc] = v[i];
+    });
+    land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, fb, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) fa[r0 + i][cc] = v[i];
     });
     __syncthreads();
-    // dT1 = -X^T dT2, in place of dT2.
+    // Level 3: dX += dT1 (7I - X)^T - X^T dT1.
     {
       f32x4_t keep[LandTiles<MP>::PER];
-      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, sm.dT2, 1.f, 0.f, m,
+      land_mm<MP, PR, false, true>(fa, 1.f, 0.f, sm.X, -1.f, 7.f, m,
                                    [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
-      __syncthreads();
-      land_store<MP>(sm.dT2, keep);
+      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, fa, 1.f, 0.f, m, [&](int q, int r0, int cc, const f32x4_t& v) {
+        for (int i = 0; i < 4; ++i) dX[r0 + i][cc] += keep[q][i] + v[i];
+      });
     }
     __syncthreads();
-    // dX += dT1 (7I - X)^T - X^T dT1.
-    {
-      f32x4_t keep[LandTiles<MP>::PER];
-      land_mm<MP, PR, false, true>(sm.dT2, 1.f, 0.f, sm.X, -1.f, 7.f, m,
-                                   [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
-      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, sm.dT2, 1.f, 0.f, m,
-                                   [&](int q, int r0, int cc, const f32x4_t& v) {
-                                     for (int i = 0; i < 4; ++i) sm.dX[r0 + i][cc] += keep[q][i] + v[i];
-                                   });
-    }
-    __syncthreads();
-    // dA += dX Z_k^T;  dZ_k += A^T dX.
-    land_mm<MP, PR, false, true>(sm.dX, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    // Level 4: dA += dX Z_k^T;  dZ_k += A^T dX.
+    land_mm<MP, PR, false, true>(dX, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.dA[r0 + i][cc] += v[i];
     });
-    land_mm<MP, PR, true, false>(sm.A, 1.f, 0.f, sm.dX, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) dZ[r0 + i][cc] += v[i];
+    land_mm<MP, PR, true, false>(sm.A, 1.f, 0.f, dX, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) fc[r0 + i][cc] += v[i];
     });
     __syncthreads();
+    // dZ_k becomes the incoming gradient of the next (earlier) step.
+    Mat old_dz = dZ;
+    dZ = fc;
+    fc = old_dz;
   }
 
   // The start Z0 = cz A^T: dA += cz dZ^T, and through cz = 1/(n1 ninf):
