@@ -119,9 +119,12 @@ int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const f
 
 size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k) {
   if (check_shape(batch, heads, n, d, m, iters) != NYS_OK) return 0;
-  nys::BwdLayout L;
-  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, conv_k < 0 ? 0 : conv_k, &L)) return 0;
-  return L.total;
+  // Enough for either dtype (their chunkings differ).
+  nys::BwdLayout L, Lb;
+  const int ck = conv_k < 0 ? 0 : conv_k;
+  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, false, &L)) return 0;
+  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, true, &Lb)) return 0;
+  return L.total > Lb.total ? L.total : Lb.total;
 }
 
 int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d,
@@ -135,7 +138,7 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
     if (rc != NYS_OK) return rc;
     const int ck = conv_w ? conv_k : 0;
     nys::BwdLayout L;
-    if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, &L)) return NYS_EUNSUPPORTED;
+    if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     bool owned = false;

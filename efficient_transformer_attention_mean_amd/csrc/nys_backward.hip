@@ -10,9 +10,9 @@
 // Per (batch, head), with s = 1/sqrt(d), P' = softmax backward
 // (dS = P * (dP - rowsum(dP * P))):
 //   dW = F^T dO,  dF = dO W^T,  dS_F = F'(dF)               -> k_bwd_rows (partials)
-//   dZ = dW BV^T, dBV = Z^T dW, dA = Lemma-1 backward,
-//   dS_A = A'(dA), dKt = s dS_F^T Q + s dS_A^T Qt, dQt_A = s dS_A Kt
-//                                                           -> k_bwd_land
+//   dW, dKt_F = s dS_F^T Q summed, dBV = Z^T dW              -> k_bwd_land_prep
+//   dZ = dW BV^T, dA = Lemma-1 backward, dS_A = A'(dA),
+//   dKt = dKt_F + s dS_A^T Qt, dQt_A = s dS_A Kt             -> k_bwd_land
 //   B = softmax(s Qt K^T) from the forward's row statistics, dB = dBV V^T,
 //   dS_B = B'(dB), dK = s dS_B^T Qt + seg^T dKt, dV = B^T dBV + DConv^T(dO),
 //   dQt_B = s dS_B K, dw = sum dO (x) V                      -> k_bwd_key (+ partials)
@@ -23,10 +23,17 @@
 // (Qt, Kt, A, Z, BV, W and the split-n softmax statistics of B) are
 // recomputed by the forward's own kernels at the start of the call.
 //
+// On the matrix-core path (bf16 I/O, d = 32 or 64) the key side needs only
+// dBV, so it runs on a second stream beside k_bwd_land (one block per head):
+// the skip's share (k_bwd_skip), then k_bwd_key_mm, which leaves out the
+// seg^T dKt term of dK; the dQ pass adds that term once dKt is complete.
+//
 // The n-sized passes run in fp32 on the vector units with their operands in
 // LDS; the m x m products of the pseudoinverse backward use the matrix cores
 // with split-bf16 operands (bf16x3 for bf16 I/O, three-way for fp32 I/O).
 #include <math.h>
+
+#include <mutex>
 
 #include "nys_common.hpp"
 #include "nys_internal.hpp"
@@ -266,47 +273,32 @@ __device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&k
 
 template <int MP, int PR>
 __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const float* __restrict__ Kt,
-                                          const float* __restrict__ Aw, const float* __restrict__ Zw,
-                                          const float* __restrict__ BV, const float* __restrict__ pdw,
-                                          const float* __restrict__ pdkt, float* __restrict__ dWg,
-                                          float* __restrict__ dBV, float* __restrict__ dKt, float* __restrict__ dQtA,
-                                          const float* __restrict__ zs, int m, int D, int nchunks, int iters,
-                                          float scale, int bh, unsigned char* smem_raw) {
+                                          const float* __restrict__ Aw, const float* __restrict__ BV,
+                                          const float* __restrict__ dWg, float* __restrict__ dKt,
+                                          float* __restrict__ dQtA, const float* __restrict__ zs, int m, int D,
+                                          int iters, float scale, int bh, unsigned char* smem_raw) {
   LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
   using Mat = float (*)[MP + 4];
   constexpr int NTH = LandTiles<MP>::NTH;
   const int tid = threadIdx.x;
   const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m;
 
-  // dW and dKt_F: fixed-order sums of the query-side partials.
-  for (int e = tid; e < m * D; e += NTH) {
-    float a = 0.f, b = 0.f;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const size_t o = ((size_t)bh * nchunks + ch) * m * D + e;
-      a += pdw[o];
-      b += pdkt[o];
-    }
-    dWg[md + e] = a;
-    dKt[md + e] = b;
-  }
-  // A (zero padded) and the final iterate Z.
+  // A, zero padded.
   for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
-    const bool in = i < m && j < m;
-    sm.A[i][j] = in ? Aw[mm + i * m + j] : 0.f;
-    sm.X[i][j] = in ? Zw[mm + i * m + j] : 0.f;
+    sm.A[i][j] = (i < m && j < m) ? Aw[mm + i * m + j] : 0.f;
   }
-  __syncthreads();
 
-  // dZ = dW BV^T and dBV = Z^T dW (fp32), over 32-feature slices staged in
-  // LDS (the T1 and dT2 slots are free until the iterates): T1[i][cc] =
-  // dW[i][c0 + cc], dT2[cc][j] = BV[j][c0 + cc].
+  // dZ = dW BV^T (fp32; dW is the sum of the query-side partials), over
+  // 32-feature slices staged in LDS (the T1 and dT2 slots are free until the
+  // iterates): T1[i][cc] = dW[i][c0 + cc], dT2[cc][j] = BV[j][c0 + cc].
   {
     constexpr int NZ = MP * MP / NTH;
     float zacc[NZ];
 #pragma unroll
     for (int q = 0; q < NZ; ++q) zacc[q] = 0.f;
     for (int c0 = 0; c0 < D; c0 += 32) {
+      __syncthreads();
       for (int e = tid; e < MP * 32; e += NTH) {
         const int i = e / 32, cc = e % 32;
         const bool in = i < m && c0 + cc < D;
@@ -322,15 +314,6 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
         for (int cc = 0; cc < 32; ++cc) a = fmaf(sm.T1[i][cc], sm.dT2[cc][j], a);
         zacc[q] = a;
       }
-      for (int e = tid; e < m * 32; e += NTH) {
-        const int j = e / 32, cc = e % 32;
-        if (c0 + cc < D) {
-          float a = 0.f;
-          for (int i = 0; i < m; ++i) a = fmaf(sm.X[i][j], sm.T1[i][cc], a);
-          dBV[md + (size_t)j * D + c0 + cc] = a;
-        }
-      }
-      __syncthreads();
     }
 #pragma unroll
     for (int q = 0; q < NZ; ++q) {
@@ -688,13 +671,16 @@ __device__ __forceinline__ B8 pack_b(const f32x4_t& lo, const f32x4_t& hi) {
 // filter gradient dw[f][t] = sum_i dO[i][f] V[i + t - R][f].  A filter of
 // conv_k <= 33 taps is centred in 33 (offset off), so tap t of 33 reads row
 // i - t + 16 in the transpose and V row i + t - 16 in the filter gradient.
+// Thread (f, rg) owns feature f and rows rg*KPT .. rg*KPT + KPT - 1 of each
+// tile; it holds the KPT + 32 dO and V values its rows reach in registers and
+// accumulates its share of all 33 taps there, summed over the row groups in
+// LDS (fixed-order tree) after the last tile.
 template <int D>
 struct SkipSmem {
   static constexpr int PD = D + 8, HR = kMmTile + 32;
   uint16_t vh[HR][PD];       // V rows with the halo
   uint16_t gh[HR][PD];       // dO rows with the halo
-  float cv[kMmTile][D + 4];  // DConv^T(dO) of the tile
-  float wsh[D * 33];         // filters centred in 33 taps (zero outside)
+  float cv[kMmTile][D + 4];  // DConv^T(dO) of the tile; the tap sums at the end
 };
 
 template <int D, int NTH>
@@ -703,22 +689,22 @@ __device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const 
                                           float* __restrict__ pdwc, int n, int heads, int conv_k, int chunk,
                                           int nchunks, int ch, int bh, unsigned char* smem_raw) {
   using SM = SkipSmem<D>;
-  constexpr int NTB = 5;                             // tap groups of 8 (conv_k <= 33)
-  constexpr int KPT = kMmTile * D / NTH;             // transpose rows per thread
-  constexpr int NIT = (D * NTB + NTH - 1) / NTH;     // filter-gradient items per thread
+  constexpr int KPT = kMmTile * D / NTH;  // rows per thread and tile
+  constexpr int RG = NTH / D;             // row groups (a power of two)
+  constexpr int WN = KPT + 32;            // rows a thread's KPT rows reach
+  static_assert(KPT * RG == kMmTile && (RG & (RG - 1)) == 0, "row groups");
+  static_assert((RG / 2) * D * 33 * 4 <= (int)sizeof(SM), "tap-sum scratch");
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, h = bh % heads;
+  const int tid = threadIdx.x, h = bh % heads, f = tid % D, rg = tid / D, r0 = rg * KPT;
   const size_t hoff = (size_t)bh * n * D;
   const int off = (33 - conv_k) / 2;
-  for (int e = tid; e < D * 33; e += NTH) {
-    const int f = e / 33, t = e % 33 - off;
-    sm.wsh[e] = (t >= 0 && t < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + t] : 0.f;
+  float w33[33], acc[33];
+#pragma unroll
+  for (int t = 0; t < 33; ++t) {
+    const int tt = t - off;  // tap of the conv_k-tap filter
+    w33[t] = (tt >= 0 && tt < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + tt] : 0.f;
+    acc[t] = 0.f;
   }
-  float awc[NIT][8];
-#pragma unroll
-  for (int a = 0; a < NIT; ++a)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) awc[a][u] = 0.f;
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
   for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
@@ -732,43 +718,27 @@ __device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const 
           in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
-    {
-      // Transpose for rows r0 .. r0 + KPT - 1 of feature f from a register
-      // window of the KPT + 32 dO values they read.
-      const int f = tid % D, r0 = (tid / D) * KPT;
-      float w33[33], win[KPT + 32];
+    float gw[WN], vw[WN];
 #pragma unroll
-      for (int t = 0; t < 33; ++t) w33[t] = sm.wsh[f * 33 + t];
-#pragma unroll
-      for (int p = 0; p < KPT + 32; ++p) win[p] = bf16_to_f32(sm.gh[r0 + p][f]);
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        float a = 0.f;
-#pragma unroll
-        for (int t = 0; t < 33; ++t) a = fmaf(w33[t], win[u - t + 32], a);
-        sm.cv[r0 + u][f] = a;
-      }
+    for (int p = 0; p < WN; ++p) {
+      gw[p] = bf16_to_f32(sm.gh[r0 + p][f]);
+      vw[p] = bf16_to_f32(sm.vh[r0 + p][f]);
     }
-    // Filter gradient with a sliding window over the V rows (taps past 32
-    // read clamped rows and are dropped).
+    // Transpose: row r0 + u (LDS row r0 + u + 16) takes dO rows r0 + u - t + 32.
 #pragma unroll
-    for (int a = 0; a < NIT; ++a) {
-      const int item = tid + NTH * a;
-      if (item < D * NTB) {
-        const int f = item % D, t0 = 8 * (item / D);
-        const int rows = min(kMmTile, kend - i0);
-        float vw[8];
+    for (int u = 0; u < KPT; ++u) {
+      float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) vw[u] = bf16_to_f32(sm.vh[min(t0 + u, SM::HR - 1)][f]);
-        for (int r = 0; r < rows; ++r) {
-          const float gv = bf16_to_f32(sm.gh[16 + r][f]);
+      for (int t = 0; t < 33; ++t) a = fmaf(w33[t], gw[u - t + 32], a);
+      sm.cv[r0 + u][f] = a;
+    }
+    // Filter gradient over the rows of this chunk (rows past kend belong to
+    // the next chunk): tap t pairs dO row r0 + u + 16 with V row r0 + u + t.
 #pragma unroll
-          for (int u = 0; u < 8; ++u) awc[a][u] = fmaf(gv, vw[u], awc[a][u]);
+    for (int u = 0; u < KPT; ++u) {
+      const float gv = (i0 + r0 + u < kend) ? gw[u + 16] : 0.f;
 #pragma unroll
-          for (int u = 0; u < 7; ++u) vw[u] = vw[u + 1];
-          vw[7] = bf16_to_f32(sm.vh[min(r + 1 + t0 + 7, SM::HR - 1)][f]);
-        }
-      }
+      for (int t = 0; t < 33; ++t) acc[t] = fmaf(gv, vw[u + t], acc[t]);
     }
     __syncthreads();
     // dV (skip part) rows of the tile, 16-byte stores.
@@ -782,30 +752,95 @@ __device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const 
       }
     }
   }
-  const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+  // Sum the row groups' taps: group rg + half hands its sums to group rg.
+  float* red = reinterpret_cast<float*>(smem_raw);  // [RG / 2][D][33]
 #pragma unroll
-  for (int a = 0; a < NIT; ++a) {
-    const int item = tid + NTH * a;
-    if (item < D * NTB) {
-      const int f = item % D, t0 = 8 * (item / D);
+  for (int half = RG / 2; half >= 1; half /= 2) {
+    __syncthreads();
+    if (rg >= half && rg < 2 * half) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = t0 + u - off;  // tap of the conv_k-tap filter
-        if (t >= 0 && t < conv_k) pdwc[wb + (size_t)f * conv_k + t] = awc[a][u];
-      }
+      for (int t = 0; t < 33; ++t) red[((rg - half) * D + f) * 33 + t] = acc[t];
+    }
+    __syncthreads();
+    if (rg < half) {
+#pragma unroll
+      for (int t = 0; t < 33; ++t) acc[t] += red[(rg * D + f) * 33 + t];
+    }
+  }
+  if (rg == 0) {
+    const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
+#pragma unroll
+    for (int t = 0; t < 33; ++t) {
+      const int tt = t - off;
+      if (tt >= 0 && tt < conv_k) pdwc[wb + (size_t)f * conv_k + tt] = acc[t];
     }
   }
 }
 
-// Landmark-side blocks [0, bh_count) and, for DS > 0, the skip's blocks after
-// them in the same launch: the skip needs no landmark-side result, so its
-// blocks run on the CUs the per-head blocks leave idle.
+// Fixed-order sum over chunks of p[ch * stride], sixteen loads in flight at
+// a time (the loads past the last chunk read nothing and add zero, which
+// leaves the sum's bits unchanged).
+__device__ __forceinline__ float chunk_sum(const float* __restrict__ p, size_t stride, int nchunks, float a) {
+  for (int ch = 0; ch < nchunks; ch += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = ch + u < nchunks ? p[(size_t)(ch + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a += x[u];
+  }
+  return a;
+}
+
+// dW = sum of the query-side partials of F^T dO, dKt_F likewise (fixed chunk
+// order), and dBV = Z^T dW.  Grid (D / 16, batch*heads), 1024 threads;
+// thread (j, cl) owns landmark j and feature 16 * blockIdx.x + cl.  The key
+// side needs only dBV, so it can start before the pseudoinverse backward.
+__global__ __launch_bounds__(1024) void k_bwd_land_prep(const float* __restrict__ Zw, const float* __restrict__ pdw,
+                                                        const float* __restrict__ pdkt, float* __restrict__ dWg,
+                                                        float* __restrict__ dKt, float* __restrict__ dBV, int m, int D,
+                                                        int nchunks) {
+  __shared__ float zl[64][65];
+  __shared__ float wl[64][17];
+  const int tid = threadIdx.x, bh = blockIdx.y, c0 = blockIdx.x * 16;
+  const int j = tid >> 4, cl = tid & 15;
+  const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m, stride = (size_t)m * D;
+  for (int e = tid; e < 64 * 64; e += 1024) {
+    const int r = e / 64, cc = e % 64;
+    zl[r][cc] = (r < m && cc < m) ? Zw[mm + (size_t)r * m + cc] : 0.f;
+  }
+  float a = 0.f;
+  if (j < m) {
+    const size_t o = (size_t)bh * nchunks * stride + (size_t)j * D + c0 + cl;
+    a = chunk_sum(pdw + o, stride, nchunks, 0.f);
+    dWg[md + (size_t)j * D + c0 + cl] = a;
+    dKt[md + (size_t)j * D + c0 + cl] = chunk_sum(pdkt + o, stride, nchunks, 0.f);
+  }
+  wl[j][cl] = a;
+  __syncthreads();
+  if (j < m) {
+    float b = 0.f;
+    for (int i = 0; i < m; ++i) b = fmaf(zl[i][j], wl[i][cl], b);
+    dBV[md + (size_t)j * D + c0 + cl] = b;
+  }
+}
+
+// Landmark side: one block per (batch, head).
 struct LandArgs {
-  const float *Qt, *Kt, *Aw, *Zw, *BV, *pdw, *pdkt;
-  float *dWg, *dBV, *dKt, *dQtA, *zs;
-  int m, D, nchunks, iters;
+  const float *Qt, *Kt, *Aw, *BV, *dWg;
+  float *dKt, *dQtA;
+  const float* zs;
+  int m, D, iters;
   float scale;
 };
+
+template <int MP, int PR>
+__global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(LandArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  land_body<MP, PR>(a.Qt, a.Kt, a.Aw, a.BV, a.dWg, a.dKt, a.dQtA, a.zs, a.m, a.D, a.iters, a.scale,
+                    (int)blockIdx.x, smem_raw);
+}
+
+// The skip's share on the matrix-core path: one block per (key chunk, batch*head).
 struct SkipArgs {
   const uint16_t *V, *dO;
   const float* conv_w;
@@ -814,19 +849,11 @@ struct SkipArgs {
   int n, heads, conv_k, chunk, nchunks;
 };
 
-template <int MP, int PR, int DS>
-__global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(LandArgs a, SkipArgs k, int bh_count) {
+template <int D, int NTH>
+__global__ __launch_bounds__(NTH) void k_bwd_skip(SkipArgs k) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  if ((int)blockIdx.x < bh_count) {
-    land_body<MP, PR>(a.Qt, a.Kt, a.Aw, a.Zw, a.BV, a.pdw, a.pdkt, a.dWg, a.dBV, a.dKt, a.dQtA, a.zs, a.m, a.D,
-                      a.nchunks, a.iters, a.scale, (int)blockIdx.x, smem_raw);
-    return;
-  }
-  if constexpr (DS > 0) {
-    const int b = (int)blockIdx.x - bh_count;
-    skip_body<DS, LandTiles<MP>::NTH>(k.V, k.dO, k.conv_w, k.dV, k.pdwc, k.n, k.heads, k.conv_k, k.chunk, k.nchunks,
-                                      b % k.nchunks, b / k.nchunks, smem_raw);
-  }
+  skip_body<D, NTH>(k.V, k.dO, k.conv_w, k.dV, k.pdwc, k.n, k.heads, k.conv_k, k.chunk, k.nchunks, (int)blockIdx.x,
+                    (int)blockIdx.y, smem_raw);
 }
 
 template <int D>
@@ -843,13 +870,14 @@ struct KeyMmSmem {
   float stm[64], stl[64], dlt[64];
 };
 
-// skip_in_dv: dV already holds the skip's part (written by the skip blocks of
-// the landmark-side launch) and the attention part is added to it.
+// Writes dK without the landmark term seg^T dKt (the dQ pass adds it once the
+// pseudoinverse backward, which runs beside this kernel, has produced dKt).
+// skip_in_dv: dV already holds the skip's part (written by k_bwd_skip) and the
+// attention part is added to it.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                     const float* __restrict__ Qt, const float* __restrict__ BV,
-                                                    const float* __restrict__ dBVg, const float* __restrict__ dKt,
-                                                    const float* __restrict__ pmax, const float* __restrict__ psum,
+                                                    const float* __restrict__ dBVg, const float* __restrict__ pmax, const float* __restrict__ psum,
                                                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                                     float* __restrict__ pdqt, int n, int m, int skip_in_dv, int chunk,
                                                     int nchunks, int fchunks, float sl2e, float scale) {
@@ -929,7 +957,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       }
     }
     // dK^T = Qt^T dS^T and dV^T = dBV^T B^T (added to the skip's part).
-    const float* dkt = dKt + md + (size_t)min(key / seg, m - 1) * D;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) {
       f32x4_t ak = zero4(), av = zero4();
@@ -940,8 +967,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       }
       if (live) {
         const int f0 = nd * 16 + 4 * g;
-        const float4 kt4 = *reinterpret_cast<const float4*>(dkt + f0);
-        const float ktv[4] = {kt4.x, kt4.y, kt4.z, kt4.w};
         uint2* vdst = reinterpret_cast<uint2*>(dV + hoff + (size_t)key * D + f0);
         float sk[4] = {0.f, 0.f, 0.f, 0.f};
         if (skip_in_dv) {
@@ -954,7 +979,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
         float vk[4], vv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          vk[i] = fmaf(scale, ak[i], ktv[i] * inv_seg);
+          vk[i] = scale * ak[i];
           vv[i] = av[i] + sk[i];
         }
         *reinterpret_cast<uint2*>(dK + hoff + (size_t)key * D + f0) =
@@ -1003,6 +1028,7 @@ template <int D, bool DQ>
 __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ Kt, const float* __restrict__ W,
                                                      const float* __restrict__ dqt, uint16_t* __restrict__ dQ,
+                                                     const float* __restrict__ dkt, uint16_t* __restrict__ dK,
                                                      float* __restrict__ pdw, float* __restrict__ pdkt, int n, int m,
                                                      int chunk, int nchunks, float sl2e, float scale) {
   using SM = RowMmSmem<D, DQ>;
@@ -1098,7 +1124,9 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
     if constexpr (DQ) {
       // The products run on every lane (a matrix-core instruction reads the
       // operands of the whole wave); only the stores are per row.
-      const float* qtr = dqt + md + (size_t)min(row / seg, m - 1) * D;
+      const size_t sro = md + (size_t)min(row / seg, m - 1) * D;
+      const float* qtr = dqt + sro;
+      const float* ktr = dkt + sro;
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
         f32x4_t a = zero4();
@@ -1112,6 +1140,15 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
           const float v2 = fmaf(scale, a[2], q4.z * inv_seg), v3 = fmaf(scale, a[3], q4.w * inv_seg);
           *reinterpret_cast<uint2*>(dQ + hoff + (size_t)row * D + f0) =
               make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          // dK of key `row` += dKt[seg(row)] / l (the key pass wrote the rest).
+          const float4 k4 = *reinterpret_cast<const float4*>(ktr + f0);
+          uint2* kd = reinterpret_cast<uint2*>(dK + hoff + (size_t)row * D + f0);
+          const uint2 kp = *kd;
+          const float k0 = __uint_as_float(kp.x << 16) + k4.x * inv_seg;
+          const float k1 = __uint_as_float(kp.x & 0xffff0000u) + k4.y * inv_seg;
+          const float k2 = __uint_as_float(kp.y << 16) + k4.z * inv_seg;
+          const float k3 = __uint_as_float(kp.y & 0xffff0000u) + k4.w * inv_seg;
+          *kd = make_uint2(pack_bf16x2(k0, k1), pack_bf16x2(k2, k3));
         }
       }
     } else {
@@ -1157,9 +1194,7 @@ __global__ __launch_bounds__(256) void k_bwd_qt_finish(const float* __restrict__
                                                        float* __restrict__ dQt, int md, int nchunks) {
   const int bh = blockIdx.y, e = blockIdx.x * 256 + (int)threadIdx.x;
   if (e >= md) return;
-  float a = dQtA[(size_t)bh * md + e];
-  for (int ch = 0; ch < nchunks; ++ch) a += pdqt[((size_t)bh * nchunks + ch) * md + e];
-  dQt[(size_t)bh * md + e] = a;
+  dQt[(size_t)bh * md + e] = chunk_sum(pdqt + (size_t)bh * nchunks * md + e, md, nchunks, dQtA[(size_t)bh * md + e]);
 }
 
 // dconv_w[h] = sum over batch entries and key chunks (fixed order); grid
@@ -1169,16 +1204,55 @@ __global__ __launch_bounds__(256) void k_bwd_dw_finish(const float* __restrict__
   const int h = blockIdx.y, e = blockIdx.x * 256 + (int)threadIdx.x;
   if (e >= dk) return;
   float a = 0.f;
-  for (int b = 0; b < batch; ++b)
-    for (int ch = 0; ch < nchunks; ++ch) a += pdwc[(((size_t)(b * heads + h)) * nchunks + ch) * dk + e];
+  for (int b = 0; b < batch; ++b) a = chunk_sum(pdwc + ((size_t)(b * heads + h)) * nchunks * dk + e, dk, nchunks, a);
   dw[(size_t)h * dk + e] = a;
 }
 
 static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Chunks per head for the split passes: about two blocks per CU overall.
-static int split_chunks(long long rows, long long bh, int tile) {
-  long long want = (512 + bh - 1) / bh;
+// A second stream per device, on which the matrix-core path's key side runs
+// beside the landmark-side kernel (fork and join by events on the caller's
+// stream); created on first use and kept for the life of the process.  One
+// call's fork and join are enqueued under the lock, so that calls from
+// several host threads cannot take each other's event records.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream_locked(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (!ss.st) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
+      if (f) (void)hipEventDestroy(f);
+      (void)hipStreamDestroy(st);
+      return e;
+    }
+    ss.fork = f;
+    ss.join = j;
+    ss.st = st;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
+// Chunks per head for the split passes: at most `slots` blocks in all, so
+// that every block starts in the first round (a second round of a few
+// full-length blocks would double the pass's time).  The passes hold two
+// blocks per CU (their LDS); the key side shares the chip with the
+// landmark-side blocks, one per head, whose LDS fills their CUs.
+static int split_chunks(long long rows, long long bh, int tile, long long slots) {
+  long long want = slots / bh;
   long long maxc = (rows + tile - 1) / tile;
   if (want < 1) want = 1;
   if (want > maxc) want = maxc;
@@ -1190,15 +1264,17 @@ static int split_chunks(long long rows, long long bh, int tile) {
 // ---------------------------------------------------------------------------
 // Workspace of the backward pass: the forward's regions, then its own.
 
-bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, BwdLayout* L) {
+bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, bool bf16, BwdLayout* L) {
   if (!make_layout(batch, heads, n, d, m, &L->fwd)) return false;
   if (m > 64 || conv_k > 33) return false;
   const long long BH = (long long)batch * heads;
   // Chunks are multiples of 64 rows, a whole number of tiles for every pass.
-  const int tq = split_chunks(n, BH, kMmTile);
+  const int tq = split_chunks(n, BH, kMmTile, 2 * 256);
   L->qchunk = cdivi(cdivi(n, tq), kMmTile) * kMmTile;
   L->nq = cdivi(n, L->qchunk);
-  const int tk = split_chunks(n, BH, kMmTile);
+  // On the matrix-core path the key side runs beside the landmark-side blocks.
+  const bool side = bf16 && (d == 32 || d == 64);
+  const int tk = split_chunks(n, BH, kMmTile, side ? 2 * (256 - (BH < 128 ? BH : 128)) : 2 * 256);
   L->kchunk = cdivi(cdivi(n, tk), kMmTile) * kMmTile;
   L->nk = cdivi(n, L->kchunk);
   L->mp = m <= 32 ? 32 : 64;
@@ -1243,8 +1319,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("bwd_rows_reduce", s);
     kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                            w.Kt, w.W, nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk,
-                                            L.nq, sl2e, scale);
+                                            w.Kt, w.W, nullptr, nullptr, nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n,
+                                            p.m, L.qchunk, L.nq, sl2e, scale);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, false>;
@@ -1256,51 +1332,82 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                             nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk, L.nq, sl2e,
                                             scale);
   }
-  // Landmark side (and, on the matrix-core path with a skip, the skip's
-  // transpose and filter gradient in the same launch).
+  // dW, dKt_F and dBV from the partials.
   {
-    const int ck = p.conv_w ? p.conv_k : 0;
-    constexpr int DS = MM ? D : 0;
-    const int nskip = (MM && ck > 0) ? L.nk * BH : 0;
-    const LandArgs la{w.Qt, w.Kt, w.A, w.Z, w.BV, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dbv), F(L.dkt), F(L.dqta),
-                      F(L.zs), p.m, D, L.nq, p.iters, scale};
-    const SkipArgs sa{static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), p.conv_w,
-                      static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck, L.kchunk, L.nk};
-    auto launch = [&](auto kern, int nth, int lbytes) -> hipError_t {
-      constexpr int DSZ = DS > 0 ? DS : 32;
-      const int sbytes = DS > 0 ? (int)sizeof(SkipSmem<DSZ>) : 0;
-      const int bytes = lbytes > sbytes ? lbytes : sbytes;
+    KernelTimer kt_("bwd_land_prep", s);
+    k_bwd_land_prep<<<dim3(D / 16, BH), 1024, 0, s>>>(w.Z, F(L.pdw), F(L.pdkt), F(L.dw), F(L.dkt), F(L.dbv), p.m, D,
+                                                     L.nq);
+  }
+  // Landmark side: the pseudoinverse backward, dKt and dQt_A.
+  const LandArgs la{w.Qt, w.Kt, w.A, w.BV, F(L.dw), F(L.dkt), F(L.dqta), F(L.zs), p.m, D, p.iters, scale};
+  auto land = [&]() -> hipError_t {
+    auto go = [&](auto kern, int nth, int bytes) -> hipError_t {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (e != hipSuccess) return e;
       KernelTimer kt_("bwd_landmarks", s);
-      kern<<<BH + nskip, nth, bytes, s>>>(la, sa, BH);
+      kern<<<BH, nth, bytes, s>>>(la);
       return hipSuccess;
     };
-    hipError_t e;
     if (L.mp == 32)
-      e = IO::kBf16 ? launch(&k_bwd_land<32, 3, DS>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>))
-                    : launch(&k_bwd_land<32, 6, DS>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>));
-    else
-      e = IO::kBf16 ? launch(&k_bwd_land<64, 3, DS>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>))
-                    : launch(&k_bwd_land<64, 6, DS>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>));
-    if (e != hipSuccess) return e;
-  }
-  // Key side: dK, dV and the partials of dQt_B and the filter gradient.
+      return IO::kBf16 ? go(&k_bwd_land<32, 3>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>))
+                       : go(&k_bwd_land<32, 6>, LandTiles<32>::NTH, (int)sizeof(LandSmem<32>));
+    return IO::kBf16 ? go(&k_bwd_land<64, 3>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>))
+                     : go(&k_bwd_land<64, 6>, LandTiles<64>::NTH, (int)sizeof(LandSmem<64>));
+  };
+  const int ck = p.conv_w ? p.conv_k : 0;
+  auto dw_finish = [&](hipStream_t st) {
+    if (ck > 0 && bp.dconv_w) {
+      KernelTimer kt_("bwd_dw_finish", st);
+      k_bwd_dw_finish<<<dim3(cdivi(D * p.conv_k, 256), p.heads), 256, 0, st>>>(F(L.pdwc), bp.dconv_w, p.batch,
+                                                                                p.heads, L.nk, D * p.conv_k);
+    }
+  };
   if constexpr (MM) {
-    const int ck = p.conv_w ? p.conv_k : 0;
-    const int bytes = (int)sizeof(KeyMmSmem<D>);
-    auto kern = &k_bwd_key_mm<D>;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (attr != hipSuccess) return attr;
-    KernelTimer kt_("bwd_keys", s);
-    kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
-                                            w.Qt, w.BV, F(L.dbv), F(L.dkt), w.pmax, w.psum,
-                                            static_cast<uint16_t*>(bp.dK), static_cast<uint16_t*>(bp.dV), F(L.pdqt),
-                                            p.n, p.m, ck > 0 ? 1 : 0, L.kchunk, L.nk, w.nchunks, sl2e, scale);
+    // The key side (the skip's share, then dK, dV and the dQt_B partials)
+    // needs only dBV: it runs on the side stream while the landmark-side
+    // blocks, one per head, run on this one.
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = nullptr;
+    hipError_t e = side_stream_locked(&ss);
+    if (e != hipSuccess) return e;
+    if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(ss->st, ss->fork, 0)) != hipSuccess) return e;
+    const hipStream_t ks = ss->st;
+    if (ck > 0) {
+      const SkipArgs sa{static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), p.conv_w,
+                        static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck, L.kchunk, L.nk};
+      const int bytes = (int)sizeof(SkipSmem<D>);
+      constexpr int SNTH = 256;
+      static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_skip<D, SNTH>),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (attr != hipSuccess) return attr;
+      KernelTimer kt_("bwd_skip", ks);
+      k_bwd_skip<D, SNTH><<<dim3(L.nk, BH), SNTH, bytes, ks>>>(sa);
+    }
+    {
+      const int bytes = (int)sizeof(KeyMmSmem<D>);
+      auto kern = &k_bwd_key_mm<D>;
+      static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      if (attr != hipSuccess) return attr;
+      KernelTimer kt_("bwd_keys", ks);
+      kern<<<dim3(L.nk, BH), 256, bytes, ks>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
+                                               w.Qt, w.BV, F(L.dbv), w.pmax, w.psum, static_cast<uint16_t*>(bp.dK),
+                                               static_cast<uint16_t*>(bp.dV), F(L.pdqt), p.n, p.m, ck > 0 ? 1 : 0,
+                                               L.kchunk, L.nk, w.nchunks, sl2e, scale);
+    }
+    dw_finish(ks);
+    if ((e = hipEventRecord(ss->join, ks)) != hipSuccess) return e;
+    const hipError_t el = land();
+    // Join even when the launch above failed: the caller's stream must not
+    // run ahead of the side stream's work.
+    if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
+    if (el != hipSuccess) return el;
   } else {
-    const int ck = p.conv_w ? p.conv_k : 0;
+    hipError_t e = land();
+    if (e != hipSuccess) return e;
+    // Key side: dK, dV and the partials of dQt_B and the filter gradient.
     const int bytes = (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 + 3 * 64 + D * (ck > 0 ? ck : 1)) * 4;
     auto kern = &k_bwd_key<IO, D>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1308,19 +1415,19 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                                        (2 * 64 * P + kKeyTile * P + 2 * 48 * P + 2 * kKeyTile * 65 +
                                                         3 * 64 + D * 33) * 4);
     if (attr != hipSuccess) return attr;
-    KernelTimer kt_("bwd_keys", s);
-    kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const T*>(p.K), static_cast<const T*>(p.V),
-                                            static_cast<const T*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv), F(L.dkt),
-                                            w.pmax, w.psum, static_cast<T*>(bp.dK), static_cast<T*>(bp.dV),
-                                            F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads, ck, L.kchunk, L.nk,
-                                            w.nchunks, sl2e, scale);
+    {
+      KernelTimer kt_("bwd_keys", s);
+      kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const T*>(p.K), static_cast<const T*>(p.V),
+                                              static_cast<const T*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv), F(L.dkt),
+                                              w.pmax, w.psum, static_cast<T*>(bp.dK), static_cast<T*>(bp.dV),
+                                              F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads, ck, L.kchunk, L.nk,
+                                              w.nchunks, sl2e, scale);
+    }
+    dw_finish(s);
   }
   {
     KernelTimer kt_("bwd_finish", s);
     k_bwd_qt_finish<<<dim3(cdivi(p.m * D, 256), BH), 256, 0, s>>>(F(L.dqta), F(L.pdqt), F(L.dqt), p.m * D, L.nk);
-    if (p.conv_w && bp.dconv_w)
-      k_bwd_dw_finish<<<dim3(cdivi(D * p.conv_k, 256), p.heads), 256, 0, s>>>(F(L.pdwc), bp.dconv_w, p.batch,
-                                                                               p.heads, L.nk, D * p.conv_k);
   }
   // Query side again: dQ.
   if constexpr (MM) {
@@ -1333,8 +1440,9 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     // planes are built once per block rather than once per 64-row tile.
     KernelTimer kt_("bwd_rows_dq", s);
     kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                            w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), nullptr, nullptr,
-                                            p.n, p.m, L.qchunk, L.nq, sl2e, scale);
+                                            w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), F(L.dkt),
+                                            static_cast<uint16_t*>(bp.dK), nullptr, nullptr, p.n, p.m, L.qchunk,
+                                            L.nq, sl2e, scale);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, true>;

@@ -94,7 +94,8 @@ struct BwdLayout {
 
 // Returns false for shapes the backward kernels do not handle (m > 64,
 // conv_k > 33, or anything the forward rejects).
-bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, BwdLayout* L);
+bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int conv_k, bool bf16,
+                     BwdLayout* L);
 
 struct BwdProblem {
   Problem fwd;

@@ -151,7 +151,10 @@ int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const f
  *               or NULL (allocated and freed in stream order)
  * Supported: m <= 64 and conv_k <= 33 (NYS_EUNSUPPORTED otherwise), every d
  * and n of the forward.  Return codes and stream behaviour as for
- * nystrom_attn_fwd. */
+ * nystrom_attn_fwd.  For bf16 with d = 32 or 64 part of the work runs on a
+ * second stream that the library keeps per device, forked from and joined
+ * back to `stream` by events: the call stays ordered with the caller's other
+ * work on `stream`, and can be captured into a graph with it. */
 size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k);
 int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
                      int n, int d, int m, int heads, int iters,
