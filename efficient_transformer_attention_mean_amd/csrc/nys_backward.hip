@@ -707,17 +707,32 @@ __device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const 
   }
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  // V and dO rows of a tile with its halo, 16 bytes per load; the next
+  // tile's are in flight while the current one is computed.
+  constexpr int NV = SM::HR * (D / 8), NL = (NV + NTH - 1) / NTH;
+  uint4 vn[NL], gn[NL];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 - 16 + rr;
+      const bool in = e < NV && row >= 0 && row < n;
+      vn[l] = in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      gn[l] = in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(kbeg);
   for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
     __syncthreads();
-    for (int e = tid; e < SM::HR * (D / 8); e += NTH) {
-      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 - 16 + rr;
-      const bool in = row >= 0 && row < n;
-      *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) =
-          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) =
-          in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      if (e < NV) {
+        *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) = vn[l];
+        *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) = gn[l];
+      }
     }
     __syncthreads();
+    if (i0 + kMmTile < kend) fetch(i0 + kMmTile);
     float gw[WN], vw[WN];
 #pragma unroll
     for (int p = 0; p < WN; ++p) {
@@ -919,24 +934,44 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
   const float inv_seg = 1.f / (float)seg;
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  // K and V rows of a tile, 16 bytes per load; the next tile's are in flight
+  // while the current one is computed.
+  constexpr int NL = kMmTile * (D / 8) / 256;
+  uint4 kn[NL], vn[NL];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + 256 * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, key = t0 + rr;
+      const bool in = key < kend;
+      kn[l] = in ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+      vn[l] = in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(kbeg);
   for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
     __syncthreads();
-    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
-      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, key = i0 + rr;
-      const bool in = key < kend;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + 256 * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
       B8 v;
-      v.q = in ? *reinterpret_cast<const uint4*>(K + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+      v.q = kn[l];
       *reinterpret_cast<uint4*>(&sm.kr[rr][c8]) = v.q;
 #pragma unroll
       for (int q = 0; q < 8; ++q) sm.kT[c8 + q][rr] = v.h[q];
-      *reinterpret_cast<uint4*>(&sm.vr[rr][c8]) =
-          in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)key * D + c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&sm.vr[rr][c8]) = vn[l];
     }
     __syncthreads();
+    if (i0 + kMmTile < kend) fetch(i0 + kMmTile);
 
     // Scores S'^T and dB^T for this wave's 16 keys (key = i0 + 16 wave + c).
     const int kl = 16 * wave + c, key = i0 + kl;
     const bool live = key < kend;
+    // The skip's part of dV for these keys, read now and added at the end.
+    uint2 skp[ND];
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+      skp[nd] = (skip_in_dv && live) ? *reinterpret_cast<const uint2*>(dV + hoff + (size_t)key * D + nd * 16 + 4 * g)
+                                     : make_uint2(0, 0);
     f32x4_t pb[4], ds[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -968,14 +1003,9 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       if (live) {
         const int f0 = nd * 16 + 4 * g;
         uint2* vdst = reinterpret_cast<uint2*>(dV + hoff + (size_t)key * D + f0);
-        float sk[4] = {0.f, 0.f, 0.f, 0.f};
-        if (skip_in_dv) {
-          const uint2 prev = *vdst;
-          sk[0] = __uint_as_float(prev.x << 16);
-          sk[1] = __uint_as_float(prev.x & 0xffff0000u);
-          sk[2] = __uint_as_float(prev.y << 16);
-          sk[3] = __uint_as_float(prev.y & 0xffff0000u);
-        }
+        const uint2 prev = skp[nd];  // zero without a skip
+        const float sk[4] = {__uint_as_float(prev.x << 16), __uint_as_float(prev.x & 0xffff0000u),
+                             __uint_as_float(prev.y << 16), __uint_as_float(prev.y & 0xffff0000u)};
         float vk[4], vv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1053,14 +1083,28 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
   const float inv_seg = 1.f / (float)seg;
 
   const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
+  // Q and dO rows of a tile, 16 bytes per load; the next tile's are in
+  // flight while the current one is computed.
+  constexpr int NL = kMmTile * (D / 8) / 256;
+  uint4 qn[NL], gn[NL];
+  auto fetch = [&](int r0) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + 256 * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = r0 + rr;
+      const bool in = row < rend;
+      qn[l] = in ? *reinterpret_cast<const uint4*>(Q + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      gn[l] = in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(rbeg);
   for (int t0 = rbeg; t0 < rend; t0 += kMmTile) {
     __syncthreads();
-    for (int e = tid; e < kMmTile * (D / 8); e += 256) {
-      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 + rr;
-      const bool in = row < rend;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const int e = tid + 256 * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
       B8 q, gv;
-      q.q = in ? *reinterpret_cast<const uint4*>(Q + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
-      gv.q = in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      q.q = qn[l];
+      gv.q = gn[l];
       *reinterpret_cast<uint4*>(&sm.qr[rr][c8]) = q.q;
       *reinterpret_cast<uint4*>(&sm.gr[rr][c8]) = gv.q;
       if constexpr (!DQ) {
@@ -1072,9 +1116,17 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
       }
     }
     __syncthreads();
+    if (t0 + kMmTile < rend) fetch(t0 + kMmTile);
 
     const int rl = 16 * wave + c, row = t0 + rl;
     const bool live = row < rend;
+    // dQ pass: the key pass's dK of key `row`, read now, updated at the end.
+    uint2 kp[DQ ? ND : 1];
+    if constexpr (DQ) {
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd)
+        kp[nd] = live ? *reinterpret_cast<const uint2*>(dK + hoff + (size_t)row * D + nd * 16 + 4 * g) : make_uint2(0, 0);
+    }
     f32x4_t sc[4], df[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -1143,11 +1195,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
           // dK of key `row` += dKt[seg(row)] / l (the key pass wrote the rest).
           const float4 k4 = *reinterpret_cast<const float4*>(ktr + f0);
           uint2* kd = reinterpret_cast<uint2*>(dK + hoff + (size_t)row * D + f0);
-          const uint2 kp = *kd;
-          const float k0 = __uint_as_float(kp.x << 16) + k4.x * inv_seg;
-          const float k1 = __uint_as_float(kp.x & 0xffff0000u) + k4.y * inv_seg;
-          const float k2 = __uint_as_float(kp.y << 16) + k4.z * inv_seg;
-          const float k3 = __uint_as_float(kp.y & 0xffff0000u) + k4.w * inv_seg;
+          const float k0 = __uint_as_float(kp[nd].x << 16) + k4.x * inv_seg;
+          const float k1 = __uint_as_float(kp[nd].x & 0xffff0000u) + k4.y * inv_seg;
+          const float k2 = __uint_as_float(kp[nd].y << 16) + k4.z * inv_seg;
+          const float k3 = __uint_as_float(kp[nd].y & 0xffff0000u) + k4.w * inv_seg;
           *kd = make_uint2(pack_bf16x2(k0, k1), pack_bf16x2(k2, k3));
         }
       }
