@@ -24,9 +24,11 @@
 // recomputed by the forward's own kernels at the start of the call.
 //
 // On the matrix-core path (bf16 I/O, d = 32 or 64) the key side needs only
-// dBV, so it runs on a second stream beside k_bwd_land (one block per head):
-// the skip's share (k_bwd_skip), then k_bwd_key_mm, which leaves out the
-// seg^T dKt term of dK; the dQ pass adds that term once dKt is complete.
+// dBV, so it runs on a second stream beside k_bwd_land (one block per head),
+// after the skip's share, forked there at the start of the call (it reads
+// only inputs): dV = DConv^T(dO) by the forward's convolution with the taps
+// reversed, and the filter gradient (k_bwd_skip_grad).  k_bwd_key_mm leaves
+// out the seg^T dKt term of dK; the dQ pass adds it once dKt is complete.
 //
 // The n-sized passes run in fp32 on the vector units with their operands in
 // LDS; the m x m products of the pseudoinverse backward use the matrix cores
@@ -289,59 +291,63 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     sm.A[i][j] = (i < m && j < m) ? Aw[mm + i * m + j] : 0.f;
   }
 
-  // dZ = dW BV^T (fp32; dW is the sum of the query-side partials), over
-  // 32-feature slices staged in LDS (the T1 and dT2 slots are free until the
-  // iterates): T1[i][cc] = dW[i][c0 + cc], dT2[cc][j] = BV[j][c0 + cc].
-  {
-    constexpr int NZ = MP * MP / NTH;
-    float zacc[NZ];
-#pragma unroll
-    for (int q = 0; q < NZ; ++q) zacc[q] = 0.f;
-    for (int c0 = 0; c0 < D; c0 += 32) {
-      __syncthreads();
-      for (int e = tid; e < MP * 32; e += NTH) {
-        const int i = e / 32, cc = e % 32;
-        const bool in = i < m && c0 + cc < D;
-        sm.T1[i][cc] = in ? dWg[md + (size_t)i * D + c0 + cc] : 0.f;
-        sm.dT2[cc][i] = in ? BV[md + (size_t)i * D + c0 + cc] : 0.f;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < NZ; ++q) {
-        const int e = tid + NTH * q, i = e / MP, j = e % MP;
-        float a = zacc[q];
-#pragma unroll 4
-        for (int cc = 0; cc < 32; ++cc) a = fmaf(sm.T1[i][cc], sm.dT2[cc][j], a);
-        zacc[q] = a;
-      }
+  // dZ = dW BV^T (dW is the sum of the query-side partials) on the matrix
+  // cores, over MP-feature slices staged in LDS (the T1 and dT2 slots are
+  // free until the iterates): T1[i][cc] = dW[i][c0 + cc], dT2[j][cc] =
+  // BV[j][c0 + cc], zero padded.
+  for (int c0 = 0; c0 < D; c0 += MP) {
+    __syncthreads();
+    for (int e = tid; e < MP * MP; e += NTH) {
+      const int i = e / MP, cc = e % MP;
+      const bool in = i < m && c0 + cc < D;
+      sm.T1[i][cc] = in ? dWg[md + (size_t)i * D + c0 + cc] : 0.f;
+      sm.dT2[i][cc] = in ? BV[md + (size_t)i * D + c0 + cc] : 0.f;
     }
-#pragma unroll
-    for (int q = 0; q < NZ; ++q) {
-      const int e = tid + NTH * q;
-      sm.dZ[e / MP][e % MP] = zacc[q];
-    }
+    __syncthreads();
+    land_mm<MP, PR, false, true>(sm.T1, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      for (int i = 0; i < 4; ++i) sm.dZ[r0 + i][cc] = (c0 == 0 ? 0.f : sm.dZ[r0 + i][cc]) + v[i];
+    });
   }
 
-  // Start Z0 = c A^T; column and row sums of A (entries are positive).
-  if (tid < MP) {
-    float cs = 0.f, rs = 0.f;
-    for (int i = 0; i < MP; ++i) {
-      cs += sm.A[i][tid];
-      rs += sm.A[tid][i];
+  // Start Z0 = c A^T; column and row sums of A (entries are positive), one
+  // wave per row and column, lane = the summed index.
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int r = wave; r < MP; r += NTH / 64) {
+    float rs = lane < MP ? sm.A[r][lane] : 0.f, cs = lane < MP ? sm.A[lane][r] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      rs += shfl_xor(rs, o);
+      cs += shfl_xor(cs, o);
     }
-    sm.col[tid] = cs;
-    sm.row[tid] = rs;
+    if (lane == 0) {
+      sm.row[r] = rs;
+      sm.col[r] = cs;
+    }
   }
   __syncthreads();
-  float n1 = 0.f, ninf = 0.f;
-  int jstar = 0;
-  for (int i = 0; i < m; ++i) {
-    if (sm.col[i] > n1) {
-      n1 = sm.col[i];
-      jstar = i;
+  // n1 = the largest column sum (first maximiser jstar), ninf = the largest row sum.
+  if (wave == 0) {
+    float cv = lane < m ? sm.col[lane] : -1.f, rv = lane < m ? sm.row[lane] : 0.f;
+    int ci = lane;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float ov = shfl_xor(cv, o);
+      const int oi = __shfl_xor(ci, o, 64);
+      if (ov > cv || (ov == cv && oi < ci)) {
+        cv = ov;
+        ci = oi;
+      }
+      rv = fmaxf(rv, shfl_xor(rv, o));
     }
-    ninf = fmaxf(ninf, sm.row[i]);
+    if (lane == 0) {
+      sm.red[0] = cv;
+      sm.red[1] = rv;
+      sm.red[2] = __int_as_float(ci);
+    }
   }
+  __syncthreads();
+  const float n1 = sm.red[0], ninf = sm.red[1];
+  const int jstar = __float_as_int(sm.red[2]);
   const float cz = 1.f / (n1 * ninf);
   const float* zsh = zs + (size_t)bh * iters * 4 * MP * MP;
 
@@ -357,16 +363,27 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
   // among the dZ, T2, dT2 and dX slots (fa receives T2_k, fb and fc the
   // level-1 results, the old dZ slot dX).
   Mat dZ = sm.dZ, fa = sm.T2, fb = sm.dT2, fc = sm.dX;
+  // Z_k, X_k, T1_k, T2_k of step k, read one step ahead into registers.
+  constexpr int ZPT = MP * MP / NTH;
+  float zr[4][ZPT];
+  auto zfetch = [&](int k) {
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) zr[t][q] = zsh[((size_t)k * 4 + t) * MM2 + tid + NTH * q];
+  };
+  if (iters > 0) zfetch(iters - 1);
   for (int k = iters - 1; k >= 0; --k) {
-    // Z_k, X_k, T1_k, T2_k of the forward step back from zs.
-    for (int e = tid; e < MP * MP; e += NTH) {
-      const int i = e / MP, j = e % MP;
-      sm.Zk[i][j] = zsh[((size_t)k * 4 + 0) * MM2 + e];
-      sm.X[i][j] = zsh[((size_t)k * 4 + 1) * MM2 + e];
-      sm.T1[i][j] = zsh[((size_t)k * 4 + 2) * MM2 + e];
-      fa[i][j] = zsh[((size_t)k * 4 + 3) * MM2 + e];
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q) {
+      const int e = tid + NTH * q, i = e / MP, j = e % MP;
+      sm.Zk[i][j] = zr[0][q];
+      sm.X[i][j] = zr[1][q];
+      sm.T1[i][j] = zr[2][q];
+      fa[i][j] = zr[3][q];
     }
     __syncthreads();
+    if (k > 0) zfetch(k - 1);
     // Level 1: dT2 = -Z_k^T dZ / 4 -> fb;  dZ_k = dZ (13I - T2)^T / 4 -> fc.
     land_mm<MP, PR, true, false>(sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) fb[r0 + i][cc] = v[i];
@@ -428,42 +445,39 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     if (i < m && j < m) sm.dA[i][j] += cz * dZ[j][i] + (j == jstar ? -dcz * cz / n1 : 0.f);
   }
   __syncthreads();
-  // dS_A = A * (dA - rowsum(dA * A)), in place of dA.
-  if (tid < MP) {
-    float s = 0.f;
-    for (int j = 0; j < m; ++j) s = fmaf(sm.dA[tid][j], sm.A[tid][j], s);
-    sm.row[tid] = s;
+  // dS_A = A * (dA - rowsum(dA * A)), in place of dA; one wave per row.
+  for (int r = wave; r < MP; r += NTH / 64) {
+    float v = lane < MP ? sm.dA[r][lane] * sm.A[r][lane] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += shfl_xor(v, o);
+    if (lane == 0) sm.row[r] = v;
   }
   __syncthreads();
   for (int e = tid; e < MP * MP; e += NTH) {
     const int i = e / MP, j = e % MP;
     sm.dA[i][j] = sm.A[i][j] * (sm.dA[i][j] - sm.row[i]);
   }
-  __syncthreads();
-  // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt, over 32-feature slices of Kt
-  // and Qt staged in the T1 and dT2 slots.
-  for (int c0 = 0; c0 < D; c0 += 32) {
-    for (int e = tid; e < MP * 32; e += NTH) {
-      const int k = e / 32, cc = e % 32;
+  // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt, on the matrix cores over
+  // MP-feature slices of Kt and Qt staged in the T1 and dT2 slots.
+  for (int c0 = 0; c0 < D; c0 += MP) {
+    __syncthreads();
+    for (int e = tid; e < MP * MP; e += NTH) {
+      const int k = e / MP, cc = e % MP;
       const bool in = k < m && c0 + cc < D;
       sm.T1[k][cc] = in ? Kt[md + (size_t)k * D + c0 + cc] : 0.f;
       sm.dT2[k][cc] = in ? Qt[md + (size_t)k * D + c0 + cc] : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < m * 32; e += NTH) {
-      const int j = e / 32, cc = e % 32;
-      if (c0 + cc < D) {
-        float a = 0.f, b = 0.f;
-        for (int k = 0; k < m; ++k) {
-          a = fmaf(sm.dA[j][k], sm.T1[k][cc], a);
-          b = fmaf(sm.dA[k][j], sm.dT2[k][cc], b);
-        }
-        const size_t o = md + (size_t)j * D + c0 + cc;
-        dQtA[o] = scale * a;
-        dKt[o] += scale * b;
-      }
-    }
-    __syncthreads();
+    land_mm<MP, PR, false, false>(sm.dA, 1.f, 0.f, sm.T1, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      if (c0 + cc < D)
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < m) dQtA[md + (size_t)(r0 + i) * D + c0 + cc] = scale * v[i];
+    });
+    land_mm<MP, PR, true, false>(sm.dA, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+      if (c0 + cc < D)
+        for (int i = 0; i < 4; ++i)
+          if (r0 + i < m) dKt[md + (size_t)(r0 + i) * D + c0 + cc] += scale * v[i];
+    });
   }
 }
 
@@ -666,106 +680,82 @@ __device__ __forceinline__ B8 pack_b(const f32x4_t& lo, const f32x4_t& hi) {
   return b;
 }
 
-// The skip's share of the backward, per tile of 64 rows with a 16-row halo:
-// dV = DConv^T(dO) (written as the initial dV, bf16) and the partials of the
-// filter gradient dw[f][t] = sum_i dO[i][f] V[i + t - R][f].  A filter of
-// conv_k <= 33 taps is centred in 33 (offset off), so tap t of 33 reads row
-// i - t + 16 in the transpose and V row i + t - 16 in the filter gradient.
-// Thread (f, rg) owns feature f and rows rg*KPT .. rg*KPT + KPT - 1 of each
-// tile; it holds the KPT + 32 dO and V values its rows reach in registers and
-// accumulates its share of all 33 taps there, summed over the row groups in
-// LDS (fixed-order tree) after the last tile.
+// The skip's filter gradient on the matrix-core path: partials over a chunk
+// of rows of dw[f][t] = sum_i dO[i][f] V[i + t - 16][f], a filter of
+// conv_k <= 33 taps centred in 33 (offset off).  Tiles of 64 rows with a
+// 16-row halo of V; thread (f, rg) owns feature f and rows rg*16 ..
+// rg*16 + 15 of each tile, holds those 16 dO values and the 48 V values they
+// pair with in registers and accumulates all 33 taps there; the four row
+// groups are summed in LDS (fixed-order tree) after the last tile.  Grid
+// (chunks, batch*heads), 4*D threads.
 template <int D>
 struct SkipSmem {
   static constexpr int PD = D + 8, HR = kMmTile + 32;
   uint16_t vh[HR][PD];       // V rows with the halo
-  uint16_t gh[HR][PD];       // dO rows with the halo
-  float cv[kMmTile][D + 4];  // DConv^T(dO) of the tile; the tap sums at the end
+  uint16_t gh[kMmTile][PD];  // dO rows of the tile
 };
 
-template <int D, int NTH>
-__device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                                          const float* __restrict__ conv_w, uint16_t* __restrict__ dV,
-                                          float* __restrict__ pdwc, int n, int heads, int conv_k, int chunk,
-                                          int nchunks, int ch, int bh, unsigned char* smem_raw) {
+template <int D>
+__global__ __launch_bounds__(4 * D) void k_bwd_skip_grad(const uint16_t* __restrict__ V,
+                                                         const uint16_t* __restrict__ dO, float* __restrict__ pdwc,
+                                                         int n, int conv_k, int chunk, int nchunks) {
   using SM = SkipSmem<D>;
-  constexpr int KPT = kMmTile * D / NTH;  // rows per thread and tile
-  constexpr int RG = NTH / D;             // row groups (a power of two)
-  constexpr int WN = KPT + 32;            // rows a thread's KPT rows reach
-  static_assert(KPT * RG == kMmTile && (RG & (RG - 1)) == 0, "row groups");
+  constexpr int NTH = 4 * D, KPT = 16, RG = 4, WN = KPT + 32;
+  constexpr int NV = SM::HR * (D / 8) / NTH, NG = kMmTile * (D / 8) / NTH;
+  static_assert(KPT * RG == kMmTile && NV * NTH == SM::HR * (D / 8) && NG * NTH == kMmTile * (D / 8), "tiling");
   static_assert((RG / 2) * D * 33 * 4 <= (int)sizeof(SM), "tap-sum scratch");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int tid = threadIdx.x, h = bh % heads, f = tid % D, rg = tid / D, r0 = rg * KPT;
+  const int tid = threadIdx.x, f = tid % D, rg = tid / D, r0 = rg * KPT;
+  const int ch = blockIdx.x, bh = blockIdx.y;
   const size_t hoff = (size_t)bh * n * D;
-  const int off = (33 - conv_k) / 2;
-  float w33[33], acc[33];
+  float acc[33];
 #pragma unroll
-  for (int t = 0; t < 33; ++t) {
-    const int tt = t - off;  // tap of the conv_k-tap filter
-    w33[t] = (tt >= 0 && tt < conv_k) ? conv_w[((size_t)h * D + f) * conv_k + tt] : 0.f;
-    acc[t] = 0.f;
-  }
+  for (int t = 0; t < 33; ++t) acc[t] = 0.f;
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
-  // V and dO rows of a tile with its halo, 16 bytes per load; the next
-  // tile's are in flight while the current one is computed.
-  constexpr int NV = SM::HR * (D / 8), NL = (NV + NTH - 1) / NTH;
-  uint4 vn[NL], gn[NL];
+  // V rows (with the halo) and dO rows of a tile, 16 bytes per load; dO rows
+  // past the chunk's end belong to the next chunk and read as zero.  The
+  // next tile's are in flight while the current one is computed.
+  uint4 vn[NV], gn[NG];
   auto fetch = [&](int t0) {
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
+    for (int l = 0; l < NV; ++l) {
       const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 - 16 + rr;
-      const bool in = e < NV && row >= 0 && row < n;
-      vn[l] = in ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
-      gn[l] = in ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
+      vn[l] = (row >= 0 && row < n) ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8)
+                                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int l = 0; l < NG; ++l) {
+      const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 + rr;
+      gn[l] = row < kend ? *reinterpret_cast<const uint4*>(dO + hoff + (size_t)row * D + c8) : make_uint4(0, 0, 0, 0);
     }
   };
   fetch(kbeg);
   for (int i0 = kbeg; i0 < kend; i0 += kMmTile) {
     __syncthreads();
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-      if (e < NV) {
-        *reinterpret_cast<uint4*>(&sm.vh[rr][c8]) = vn[l];
-        *reinterpret_cast<uint4*>(&sm.gh[rr][c8]) = gn[l];
-      }
+    for (int l = 0; l < NV; ++l) {
+      const int e = tid + NTH * l;
+      *reinterpret_cast<uint4*>(&sm.vh[e / (D / 8)][(e % (D / 8)) * 8]) = vn[l];
+    }
+#pragma unroll
+    for (int l = 0; l < NG; ++l) {
+      const int e = tid + NTH * l;
+      *reinterpret_cast<uint4*>(&sm.gh[e / (D / 8)][(e % (D / 8)) * 8]) = gn[l];
     }
     __syncthreads();
     if (i0 + kMmTile < kend) fetch(i0 + kMmTile);
-    float gw[WN], vw[WN];
+    // dO row r0 + u pairs with V row r0 + u + t - 16 (halo row r0 + u + t).
+    float gw[KPT], vw[WN];
 #pragma unroll
-    for (int p = 0; p < WN; ++p) {
-      gw[p] = bf16_to_f32(sm.gh[r0 + p][f]);
-      vw[p] = bf16_to_f32(sm.vh[r0 + p][f]);
-    }
-    // Transpose: row r0 + u (LDS row r0 + u + 16) takes dO rows r0 + u - t + 32.
+    for (int u = 0; u < KPT; ++u) gw[u] = bf16_to_f32(sm.gh[r0 + u][f]);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      float a = 0.f;
+    for (int p = 0; p < WN; ++p) vw[p] = bf16_to_f32(sm.vh[r0 + p][f]);
 #pragma unroll
-      for (int t = 0; t < 33; ++t) a = fmaf(w33[t], gw[u - t + 32], a);
-      sm.cv[r0 + u][f] = a;
-    }
-    // Filter gradient over the rows of this chunk (rows past kend belong to
-    // the next chunk): tap t pairs dO row r0 + u + 16 with V row r0 + u + t.
+    for (int u = 0; u < KPT; ++u)
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const float gv = (i0 + r0 + u < kend) ? gw[u + 16] : 0.f;
-#pragma unroll
-      for (int t = 0; t < 33; ++t) acc[t] = fmaf(gv, vw[u + t], acc[t]);
-    }
-    __syncthreads();
-    // dV (skip part) rows of the tile, 16-byte stores.
-    for (int e = tid; e < kMmTile * (D / 8); e += NTH) {
-      const int rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = i0 + rr;
-      if (row < kend) {
-        B8 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o.u[q] = pack_bf16x2(sm.cv[rr][c8 + 2 * q], sm.cv[rr][c8 + 2 * q + 1]);
-        *reinterpret_cast<uint4*>(dV + hoff + (size_t)row * D + c8) = o.q;
-      }
-    }
+      for (int t = 0; t < 33; ++t) acc[t] = fmaf(gw[u], vw[u + t], acc[t]);
   }
   // Sum the row groups' taps: group rg + half hands its sums to group rg.
   float* red = reinterpret_cast<float*>(smem_raw);  // [RG / 2][D][33]
@@ -783,13 +773,25 @@ __device__ __forceinline__ void skip_body(const uint16_t* __restrict__ V, const 
     }
   }
   if (rg == 0) {
+    const int off = (33 - conv_k) / 2;
     const size_t wb = ((size_t)bh * nchunks + ch) * D * conv_k;
 #pragma unroll
     for (int t = 0; t < 33; ++t) {
-      const int tt = t - off;
+      const int tt = t - off;  // tap of the conv_k-tap filter
       if (tt >= 0 && tt < conv_k) pdwc[wb + (size_t)f * conv_k + tt] = acc[t];
     }
   }
+}
+
+// Filters with their taps reversed: the transposed depthwise convolution
+// DConv^T(dO)[i] = sum_t w[t] dO[i - t + R] is the convolution of dO with
+// the reversed filter.  One thread per tap.
+__global__ __launch_bounds__(256) void k_flip_taps(const float* __restrict__ w, float* __restrict__ wf, int k,
+                                                   int total) {
+  const int e = blockIdx.x * 256 + (int)threadIdx.x;
+  if (e >= total) return;
+  const int t = e % k;
+  wf[e] = w[e - t + (k - 1 - t)];
 }
 
 // Fixed-order sum over chunks of p[ch * stride], sixteen loads in flight at
@@ -855,22 +857,6 @@ __global__ __launch_bounds__(LandTiles<MP>::NTH) void k_bwd_land(LandArgs a) {
                     (int)blockIdx.x, smem_raw);
 }
 
-// The skip's share on the matrix-core path: one block per (key chunk, batch*head).
-struct SkipArgs {
-  const uint16_t *V, *dO;
-  const float* conv_w;
-  uint16_t* dV;
-  float* pdwc;
-  int n, heads, conv_k, chunk, nchunks;
-};
-
-template <int D, int NTH>
-__global__ __launch_bounds__(NTH) void k_bwd_skip(SkipArgs k) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  skip_body<D, NTH>(k.V, k.dO, k.conv_w, k.dV, k.pdwc, k.n, k.heads, k.conv_k, k.chunk, k.nchunks, (int)blockIdx.x,
-                    (int)blockIdx.y, smem_raw);
-}
-
 template <int D>
 struct KeyMmSmem {
   static constexpr int PD = D + 8, PK = 64 + 8;
@@ -887,8 +873,8 @@ struct KeyMmSmem {
 
 // Writes dK without the landmark term seg^T dKt (the dQ pass adds it once the
 // pseudoinverse backward, which runs beside this kernel, has produced dKt).
-// skip_in_dv: dV already holds the skip's part (written by k_bwd_skip) and the
-// attention part is added to it.
+// skip_in_dv: dV already holds the skip's part (the transposed convolution,
+// written earlier on the same stream) and the attention part is added to it.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                     const float* __restrict__ Qt, const float* __restrict__ BV,
@@ -1268,7 +1254,13 @@ static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
 // several host threads cannot take each other's event records.
 struct SideStream {
   hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t start = nullptr, fork = nullptr, join = nullptr;
+};
+// One call's use of the side stream: `pending` while work forked onto it has
+// not been joined back to the caller's stream.
+struct SideCall {
+  SideStream* ss = nullptr;
+  bool pending = false;
 };
 std::mutex g_side_mu;
 SideStream g_side[64];
@@ -1281,16 +1273,18 @@ hipError_t side_stream_locked(SideStream** out) {
   SideStream& ss = g_side[dev];
   if (!ss.st) {
     hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) {
-      if (f) (void)hipEventDestroy(f);
-      (void)hipStreamDestroy(st);
-      return e;
+    for (int i = 0; i < 3; ++i) {
+      if ((e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming)) != hipSuccess) {
+        for (int k = 0; k < i; ++k) (void)hipEventDestroy(ev[k]);
+        (void)hipStreamDestroy(st);
+        return e;
+      }
     }
-    ss.fork = f;
-    ss.join = j;
+    ss.start = ev[0];
+    ss.fork = ev[1];
+    ss.join = ev[2];
     ss.st = st;
   }
   *out = &ss;
@@ -1346,12 +1340,13 @@ bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int c
   L->dqt = take(md);
   L->pdwc = take((size_t)BH * L->nk * d * (conv_k > 0 ? conv_k : 1) * 4);
   L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * 4 * L->mp * L->mp * 4);
+  L->wflip = take((size_t)heads * d * (conv_k > 0 ? conv_k : 1) * 4);
   L->total = off;
   return true;
 }
 
 template <typename IO, int D>
-static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s) {
+static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc) {
   using T = typename IO::T;
   const Problem& p = bp.fwd;
   const Ws w = resolve(L.fwd, ws);
@@ -1415,27 +1410,15 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     }
   };
   if constexpr (MM) {
-    // The key side (the skip's share, then dK, dV and the dQt_B partials)
-    // needs only dBV: it runs on the side stream while the landmark-side
-    // blocks, one per head, run on this one.
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* ss = nullptr;
-    hipError_t e = side_stream_locked(&ss);
-    if (e != hipSuccess) return e;
+    // The key side (dK, dV and the dQt_B partials) needs only dBV: it runs
+    // on the side stream, after the skip's share forked there at the start
+    // of the call, while the landmark-side blocks, one per head, run on this
+    // one.
+    SideStream* ss = sc.ss;
+    hipError_t e;
     if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(ss->st, ss->fork, 0)) != hipSuccess) return e;
     const hipStream_t ks = ss->st;
-    if (ck > 0) {
-      const SkipArgs sa{static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), p.conv_w,
-                        static_cast<uint16_t*>(bp.dV), F(L.pdwc), p.n, p.heads, ck, L.kchunk, L.nk};
-      const int bytes = (int)sizeof(SkipSmem<D>);
-      constexpr int SNTH = 256;
-      static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_skip<D, SNTH>),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-      if (attr != hipSuccess) return attr;
-      KernelTimer kt_("bwd_skip", ks);
-      k_bwd_skip<D, SNTH><<<dim3(L.nk, BH), SNTH, bytes, ks>>>(sa);
-    }
     {
       const int bytes = (int)sizeof(KeyMmSmem<D>);
       auto kern = &k_bwd_key_mm<D>;
@@ -1454,6 +1437,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     // Join even when the launch above failed: the caller's stream must not
     // run ahead of the side stream's work.
     if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
+    sc.pending = false;
     if (el != hipSuccess) return el;
   } else {
     hipError_t e = land();
@@ -1509,26 +1493,74 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s) {
-  // The forward's pseudoinverse kernel also saves its steps for the reverse pass.
-  BwdProblem bp = bp0;
-  bp.fwd.zsave = reinterpret_cast<float*>(ws + L.zs);
-  bp.fwd.zmp = L.mp;
+// The skip's share of the matrix-core path, on the side stream: dV =
+// DConv^T(dO) (the forward's convolution with the taps reversed, written as
+// the initial dV) and the filter-gradient partials.  It reads only inputs.
+template <int D>
+static hipError_t skip_side(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
+  const Problem& p = bp.fwd;
+  float* wf = reinterpret_cast<float*>(ws + L.wflip);
+  const int total = p.heads * D * p.conv_k;
+  k_flip_taps<<<cdivi(total, 256), 256, 0, ks>>>(p.conv_w, wf, p.conv_k, total);
+  hipError_t e = launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks);
+  if (e != hipSuccess) return e;
+  KernelTimer kt_("bwd_skip_grad", ks);
+  k_bwd_skip_grad<D><<<dim3(L.nk, p.batch * p.heads), 4 * D, (int)sizeof(SkipSmem<D>), ks>>>(
+      static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), reinterpret_cast<float*>(ws + L.pdwc),
+      p.n, p.conv_k, L.kchunk, L.nk);
+  return hipSuccess;
+}
+
+static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc) {
   const Problem& p = bp.fwd;
   const Ws w = resolve(L.fwd, ws);
   hipError_t e;
+  if (sc.ss) {
+    // Fork: the skip's share needs only the inputs, so it runs beside the
+    // forward's stages and the query-side reduction.
+    if ((e = hipEventRecord(sc.ss->start, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sc.ss->st, sc.ss->start, 0)) != hipSuccess) return e;
+    sc.pending = true;
+    if (p.conv_w && p.conv_k > 0) {
+      e = p.d == 32 ? skip_side<32>(bp, L, ws, sc.ss->st) : skip_side<64>(bp, L, ws, sc.ss->st);
+      if (e != hipSuccess) return e;
+    }
+  }
   // The forward's landmark side: Qt, Kt, A, Z, BV, W and B's statistics.
   if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
   if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
   if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
   if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
   switch (p.d) {
-    case 16: return p.bf16 ? bwd_t<BF16, 16>(bp, L, ws, s) : bwd_t<F32, 16>(bp, L, ws, s);
-    case 32: return p.bf16 ? bwd_t<BF16, 32>(bp, L, ws, s) : bwd_t<F32, 32>(bp, L, ws, s);
-    case 64: return p.bf16 ? bwd_t<BF16, 64>(bp, L, ws, s) : bwd_t<F32, 64>(bp, L, ws, s);
-    case 128: return p.bf16 ? bwd_t<BF16, 128>(bp, L, ws, s) : bwd_t<F32, 128>(bp, L, ws, s);
+    case 16: return p.bf16 ? bwd_t<BF16, 16>(bp, L, ws, s, sc) : bwd_t<F32, 16>(bp, L, ws, s, sc);
+    case 32: return p.bf16 ? bwd_t<BF16, 32>(bp, L, ws, s, sc) : bwd_t<F32, 32>(bp, L, ws, s, sc);
+    case 64: return p.bf16 ? bwd_t<BF16, 64>(bp, L, ws, s, sc) : bwd_t<F32, 64>(bp, L, ws, s, sc);
+    case 128: return p.bf16 ? bwd_t<BF16, 128>(bp, L, ws, s, sc) : bwd_t<F32, 128>(bp, L, ws, s, sc);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s) {
+  // The forward's pseudoinverse kernel also saves its steps for the reverse pass.
+  BwdProblem bp = bp0;
+  bp.fwd.zsave = reinterpret_cast<float*>(ws + L.zs);
+  bp.fwd.zmp = L.mp;
+  const Problem& p = bp.fwd;
+  if (!(p.bf16 && (p.d == 32 || p.d == 64))) {
+    SideCall none;
+    return backward_body(bp, L, ws, s, none);
+  }
+  // Matrix-core path: this call's forks and joins are enqueued under the lock.
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideCall sc;
+  hipError_t e = side_stream_locked(&sc.ss);
+  if (e != hipSuccess) return e;
+  e = backward_body(bp, L, ws, s, sc);
+  if (sc.pending) {
+    // An error left work on the side stream: join it all the same.
+    if (hipEventRecord(sc.ss->join, sc.ss->st) == hipSuccess) (void)hipStreamWaitEvent(s, sc.ss->join, 0);
+  }
+  return e;
 }
 
 }  // namespace nys

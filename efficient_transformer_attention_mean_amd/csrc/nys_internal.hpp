@@ -86,6 +86,7 @@ struct BwdLayout {
   size_t pdqt, dqt;    // fp32 [bh][nk][m][d] key-side partials of dQt; dQt (total)
   size_t pdwc;         // fp32 [bh][nk][d][conv_k] partials of the filter gradient
   size_t zs;           // fp32 [bh][iters][4][mp][mp] forward steps: Z_k, X_k, T1_k, T2_k
+  size_t wflip;        // fp32 [heads][d][conv_k] skip filters with their taps reversed
   size_t total;
   int qchunk, nq;      // query rows per block of the reduction pass, blocks per head
   int kchunk, nk;      // keys per block of the key pass, blocks per head
