@@ -188,9 +188,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const typename IO::T* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Landmark side, one block per head (one wave per 16 x 16 tile of an MP x MP
-// matrix: 1024 threads for MP = 64, 256 for MP = 32; m <= MP, matrices in
-// LDS with pitch MP + 4).
+// Landmark side, one block per head (512 threads for MP = 64, 256 for
+// MP = 32; m <= MP, MP x MP matrices in LDS with pitch MP + 4).
 
 template <int MP>
 struct LandSmem {
@@ -202,28 +201,38 @@ struct LandSmem {
 
 // C = op(P) op(Q) on MP x MP LDS matrices (pitch MP + 4), where op(P) =
 // pa * P' + pb * I on the first m diagonal entries (P' = P or P^T) and the
-// same for Q.  Wave w owns tiles t = w + 4q (q < NT*NT/4); its lane (c, g)
-// gets rows ti*16 + 4g + i, column tj*16 + c of each, and epi(q, row0, col,
-// v) receives them.
+// same for Q.  Computed by the NQ = (MP/32)^2 waves [w0, w0 + NQ) of the
+// block, each one 32 x 32 quadrant as 2 x 2 tiles of 16 x 16, so that each
+// operand row or column is read from LDS by NQ1 = MP/32 waves rather than
+// by every tile; the other waves return at once (the test is wave-uniform,
+// so every matrix-core instruction runs on whole waves).  Lane (c, g) of a
+// tile gets rows row0 + 4g + i, column col + c, and epi(t, row0, col, v)
+// receives them, t = 2 * (tile row) + (tile column) within the quadrant.
 template <int MP>
 struct LandTiles {
-  static constexpr int NT = MP / 16, NW = NT * NT, NTH = 64 * NW, PER = 1;  // one tile per wave
+  static constexpr int NQ1 = MP / 32, NQ = NQ1 * NQ1;     // quadrant waves per product
+  static constexpr int NTH = MP == 64 ? 512 : 256, NW = NTH / 64;  // two products at once
 };
 
 template <int MP, int PR, bool TPa, bool TQa, typename Epi>
-__device__ __forceinline__ void land_mm(const float (*Pm)[MP + 4], float pa, float pb, const float (*Qm)[MP + 4],
-                                        float qa, float qb, int m, Epi epi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void land_mm(int w0, const float (*Pm)[MP + 4], float pa, float pb,
+                                        const float (*Qm)[MP + 4], float qa, float qb, int m, Epi epi) {
+  constexpr int NQ1 = LandTiles<MP>::NQ1, NQ = LandTiles<MP>::NQ;
+  const int lane = threadIdx.x & 63, qw = (int)(threadIdx.x >> 6) - w0;
+  if (qw < 0 || qw >= NQ) return;
   const int c = lane & 15, g = lane >> 4;
-  constexpr int NT = LandTiles<MP>::NT;
+  const int bi = (qw / NQ1) * 32, bj = (qw % NQ1) * 32;
+  f32x4_t acc[2][2];
 #pragma unroll
-  for (int q = 0; q < LandTiles<MP>::PER; ++q) {
-    const int t = wave + LandTiles<MP>::NW * q;
-    const int ti = t / NT, tj = t % NT;
-    const int i = ti * 16 + c, j = tj * 16 + c;
-    f32x4_t acc = zero4();
+  for (int si = 0; si < 2; ++si)
+#pragma unroll
+    for (int sj = 0; sj < 2; ++sj) acc[si][sj] = zero4();
 #pragma unroll 1
-    for (int kc = 0; kc < MP; kc += 32) {
+  for (int kc = 0; kc < MP; kc += 32) {
+    float a[2][8], b[2][8];
+#pragma unroll
+    for (int sx = 0; sx < 2; ++sx) {
+      const int i = bi + 16 * sx + c, j = bj + 16 * sx + c;
       // Row-contiguous operands (P untransposed, Q transposed) are read as
       // two 16-byte vectors; the others one element per k.
       float pv[8], qv[8];
@@ -245,32 +254,22 @@ __device__ __forceinline__ void land_mm(const float (*Pm)[MP + 4], float pa, flo
 #pragma unroll
         for (int u = 0; u < 8; ++u) qv[u] = Qm[kc + 8 * g + u][j];
       }
-      float a[8], b[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = kc + 8 * g + u;
-        a[u] = pa * pv[u] + ((i == k && k < m) ? pb : 0.f);
-        b[u] = qa * qv[u] + ((k == j && k < m) ? qb : 0.f);
+        a[sx][u] = pa * pv[u] + ((i == k && k < m) ? pb : 0.f);
+        b[sx][u] = qa * qv[u] + ((k == j && k < m) ? qb : 0.f);
       }
-      acc = mma_f32<PR>(a, b, acc);
     }
-    epi(q, ti * 16 + 4 * g, tj * 16 + c, acc);
-  }
-}
-
-// Stores per-wave tile results kept by an earlier land_mm into M.
-template <int MP>
-__device__ __forceinline__ void land_store(float (*M)[MP + 4], const f32x4_t (&keep)[LandTiles<MP>::PER]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  constexpr int NT = LandTiles<MP>::NT;
 #pragma unroll
-  for (int q = 0; q < LandTiles<MP>::PER; ++q) {
-    const int t = wave + LandTiles<MP>::NW * q;
-    const int r0 = (t / NT) * 16 + 4 * g, cc = (t % NT) * 16 + c;
+    for (int si = 0; si < 2; ++si)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) M[r0 + i][cc] = keep[q][i];
+      for (int sj = 0; sj < 2; ++sj) acc[si][sj] = mma_f32<PR>(a[si], b[sj], acc[si][sj]);
   }
+#pragma unroll
+  for (int si = 0; si < 2; ++si)
+#pragma unroll
+    for (int sj = 0; sj < 2; ++sj) epi(2 * si + sj, bi + 16 * si + 4 * g, bj + 16 * sj + c, acc[si][sj]);
 }
 
 template <int MP, int PR>
@@ -281,33 +280,56 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
                                           int iters, float scale, int bh, unsigned char* smem_raw) {
   LandSmem<MP>& sm = *reinterpret_cast<LandSmem<MP>*>(smem_raw);
   using Mat = float (*)[MP + 4];
-  constexpr int NTH = LandTiles<MP>::NTH;
+  constexpr int NTH = LandTiles<MP>::NTH, NQ = LandTiles<MP>::NQ;
   const int tid = threadIdx.x;
   const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m;
 
-  // A, zero padded.
-  for (int e = tid; e < MP * MP; e += NTH) {
-    const int i = e / MP, j = e % MP;
-    sm.A[i][j] = (i < m && j < m) ? Aw[mm + i * m + j] : 0.f;
-  }
-
-  // dZ = dW BV^T (dW is the sum of the query-side partials) on the matrix
-  // cores, over MP-feature slices staged in LDS (the T1 and dT2 slots are
-  // free until the iterates): T1[i][cc] = dW[i][c0 + cc], dT2[j][cc] =
-  // BV[j][c0 + cc], zero padded.
-  for (int c0 = 0; c0 < D; c0 += MP) {
-    __syncthreads();
-    for (int e = tid; e < MP * MP; e += NTH) {
-      const int i = e / MP, cc = e % MP;
-      const bool in = i < m && c0 + cc < D;
-      sm.T1[i][cc] = in ? dWg[md + (size_t)i * D + c0 + cc] : 0.f;
-      sm.dT2[i][cc] = in ? BV[md + (size_t)i * D + c0 + cc] : 0.f;
+  constexpr int ZPT = MP * MP / NTH;  // entries e = tid + NTH * q of an MP x MP matrix
+  // A (zero padded), and dZ = dW BV^T (dW is the sum of the query-side
+  // partials) on the matrix cores over MP-feature slices staged in LDS (the
+  // T1 and dT2 slots are free until the iterates): T1[i][cc] = dW[i][c0 +
+  // cc], dT2[j][cc] = BV[j][c0 + cc], zero padded.  A and the first slice
+  // are loaded together.
+  {
+    float ar[ZPT], wr[ZPT], br[ZPT];
+    auto slice = [&](int c0) {
+#pragma unroll
+      for (int q = 0; q < ZPT; ++q) {
+        const int e = tid + NTH * q, i = e / MP, cc = e % MP;
+        const bool in = i < m && c0 + cc < D;
+        wr[q] = in ? dWg[md + (size_t)i * D + c0 + cc] : 0.f;
+        br[q] = in ? BV[md + (size_t)i * D + c0 + cc] : 0.f;
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q) {
+      const int e = tid + NTH * q, i = e / MP, j = e % MP;
+      ar[q] = (i < m && j < m) ? Aw[mm + i * m + j] : 0.f;
     }
-    __syncthreads();
-    land_mm<MP, PR, false, true>(sm.T1, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
-      for (int i = 0; i < 4; ++i) sm.dZ[r0 + i][cc] = (c0 == 0 ? 0.f : sm.dZ[r0 + i][cc]) + v[i];
-    });
+    slice(0);
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q) {
+      const int e = tid + NTH * q;
+      sm.A[e / MP][e % MP] = ar[q];
+    }
+    for (int c0 = 0; c0 < D; c0 += MP) {
+      if (c0 > 0) {
+        __syncthreads();
+        slice(c0);
+      }
+#pragma unroll
+      for (int q = 0; q < ZPT; ++q) {
+        const int e = tid + NTH * q;
+        sm.T1[e / MP][e % MP] = wr[q];
+        sm.dT2[e / MP][e % MP] = br[q];
+      }
+      __syncthreads();
+      land_mm<MP, PR, false, true>(0, sm.T1, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+        for (int i = 0; i < 4; ++i) sm.dZ[r0 + i][cc] = (c0 == 0 ? 0.f : sm.dZ[r0 + i][cc]) + v[i];
+      });
+    }
   }
+  __syncthreads();
 
   // Start Z0 = c A^T; column and row sums of A (entries are positive), one
   // wave per row and column, lane = the summed index.
@@ -364,8 +386,8 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
   // level-1 results, the old dZ slot dX).
   Mat dZ = sm.dZ, fa = sm.T2, fb = sm.dT2, fc = sm.dX;
   // Z_k, X_k, T1_k, T2_k of step k, read one step ahead into registers.
-  constexpr int ZPT = MP * MP / NTH;
   float zr[4][ZPT];
+
   auto zfetch = [&](int k) {
 #pragma unroll
     for (int q = 0; q < ZPT; ++q)
@@ -385,37 +407,38 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     __syncthreads();
     if (k > 0) zfetch(k - 1);
     // Level 1: dT2 = -Z_k^T dZ / 4 -> fb;  dZ_k = dZ (13I - T2)^T / 4 -> fc.
-    land_mm<MP, PR, true, false>(sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, true, false>(0, sm.Zk, -0.25f, 0.f, dZ, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) fb[r0 + i][cc] = v[i];
     });
-    land_mm<MP, PR, false, true>(dZ, 0.25f, 0.f, fa, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, false, true>(NQ, dZ, 0.25f, 0.f, fa, -1.f, 13.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) fc[r0 + i][cc] = v[i];
     });
     __syncthreads();
     // Level 2: dX = dT2 (15I - T1)^T -> the old dZ slot;  dT1 = -X^T dT2 -> fa.
     Mat dX = dZ;
-    land_mm<MP, PR, false, true>(fb, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, false, true>(0, fb, 1.f, 0.f, sm.T1, -1.f, 15.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) dX[r0 + i][cc] = v[i];
     });
-    land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, fb, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, true, false>(NQ, sm.X, -1.f, 0.f, fb, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) fa[r0 + i][cc] = v[i];
     });
     __syncthreads();
-    // Level 3: dX += dT1 (7I - X)^T - X^T dT1.
+    // Level 3: dX += dT1 (7I - X)^T - X^T dT1 (both products by the same
+    // waves, the first kept in registers).
     {
-      f32x4_t keep[LandTiles<MP>::PER];
-      land_mm<MP, PR, false, true>(fa, 1.f, 0.f, sm.X, -1.f, 7.f, m,
+      f32x4_t keep[4];
+      land_mm<MP, PR, false, true>(0, fa, 1.f, 0.f, sm.X, -1.f, 7.f, m,
                                    [&](int q, int, int, const f32x4_t& v) { keep[q] = v; });
-      land_mm<MP, PR, true, false>(sm.X, -1.f, 0.f, fa, 1.f, 0.f, m, [&](int q, int r0, int cc, const f32x4_t& v) {
+      land_mm<MP, PR, true, false>(0, sm.X, -1.f, 0.f, fa, 1.f, 0.f, m, [&](int q, int r0, int cc, const f32x4_t& v) {
         for (int i = 0; i < 4; ++i) dX[r0 + i][cc] += keep[q][i] + v[i];
       });
     }
     __syncthreads();
     // Level 4: dA += dX Z_k^T;  dZ_k += A^T dX.
-    land_mm<MP, PR, false, true>(dX, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, false, true>(0, dX, 1.f, 0.f, sm.Zk, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) sm.dA[r0 + i][cc] += v[i];
     });
-    land_mm<MP, PR, true, false>(sm.A, 1.f, 0.f, dX, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, true, false>(NQ, sm.A, 1.f, 0.f, dX, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       for (int i = 0; i < 4; ++i) fc[r0 + i][cc] += v[i];
     });
     __syncthreads();
@@ -424,6 +447,21 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     dZ = fc;
     fc = old_dz;
   }
+
+  // The first feature slice of Kt, Qt and dKt for the end, in flight while
+  // the start's gradient and the softmax backward run.
+  float er[3][ZPT];
+  auto efetch = [&]() {
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q) {
+      const int e = tid + NTH * q, k = e / MP, cc = e % MP;
+      const bool in = k < m && cc < D;
+      er[0][q] = in ? Kt[md + (size_t)k * D + cc] : 0.f;
+      er[1][q] = in ? Qt[md + (size_t)k * D + cc] : 0.f;
+      er[2][q] = in ? dKt[md + (size_t)k * D + cc] : 0.f;
+    }
+  };
+  efetch();
 
   // The start Z0 = cz A^T: dA += cz dZ^T, and through cz = 1/(n1 ninf):
   // dcz = sum dZ * A^T; n1 = column sum jstar adds -dcz cz / n1 to column
@@ -458,25 +496,38 @@ __device__ __forceinline__ void land_body(const float* __restrict__ Qt, const fl
     sm.dA[i][j] = sm.A[i][j] * (sm.dA[i][j] - sm.row[i]);
   }
   // dQt_A = s dS_A Kt;  dKt += s dS_A^T Qt, on the matrix cores over
-  // MP-feature slices of Kt and Qt staged in the T1 and dT2 slots.
+  // MP-feature slices of Kt and Qt staged in the T1 and dT2 slots, dKt's
+  // values so far in the Zk slot (the first slice was read during the last
+  // step).
   for (int c0 = 0; c0 < D; c0 += MP) {
-    __syncthreads();
-    for (int e = tid; e < MP * MP; e += NTH) {
-      const int k = e / MP, cc = e % MP;
-      const bool in = k < m && c0 + cc < D;
-      sm.T1[k][cc] = in ? Kt[md + (size_t)k * D + c0 + cc] : 0.f;
-      sm.dT2[k][cc] = in ? Qt[md + (size_t)k * D + c0 + cc] : 0.f;
+    if (c0 > 0) {
+#pragma unroll
+      for (int q = 0; q < ZPT; ++q) {
+        const int e = tid + NTH * q, k = e / MP, cc = e % MP;
+        const bool in = k < m && c0 + cc < D;
+        er[0][q] = in ? Kt[md + (size_t)k * D + c0 + cc] : 0.f;
+        er[1][q] = in ? Qt[md + (size_t)k * D + c0 + cc] : 0.f;
+        er[2][q] = in ? dKt[md + (size_t)k * D + c0 + cc] : 0.f;
+      }
     }
     __syncthreads();
-    land_mm<MP, PR, false, false>(sm.dA, 1.f, 0.f, sm.T1, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+#pragma unroll
+    for (int q = 0; q < ZPT; ++q) {
+      const int e = tid + NTH * q, k = e / MP, cc = e % MP;
+      sm.T1[k][cc] = er[0][q];
+      sm.dT2[k][cc] = er[1][q];
+      sm.Zk[k][cc] = er[2][q];
+    }
+    __syncthreads();
+    land_mm<MP, PR, false, false>(0, sm.dA, 1.f, 0.f, sm.T1, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       if (c0 + cc < D)
         for (int i = 0; i < 4; ++i)
           if (r0 + i < m) dQtA[md + (size_t)(r0 + i) * D + c0 + cc] = scale * v[i];
     });
-    land_mm<MP, PR, true, false>(sm.dA, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
+    land_mm<MP, PR, true, false>(NQ, sm.dA, 1.f, 0.f, sm.dT2, 1.f, 0.f, m, [&](int, int r0, int cc, const f32x4_t& v) {
       if (c0 + cc < D)
         for (int i = 0; i < 4; ++i)
-          if (r0 + i < m) dKt[md + (size_t)(r0 + i) * D + c0 + cc] += scale * v[i];
+          if (r0 + i < m) dKt[md + (size_t)(r0 + i) * D + c0 + cc] = sm.Zk[r0 + i][cc] + scale * v[i];
     });
   }
 }
