@@ -1439,8 +1439,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   const LandArgs la{w.Qt, w.Kt, w.A, w.BV, F(L.dw), F(L.dkt), F(L.dqta), F(L.zs), p.m, D, p.iters, scale};
   auto land = [&]() -> hipError_t {
     auto go = [&](auto kern, int nth, int bytes) -> hipError_t {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
       if (e != hipSuccess) return e;
       KernelTimer kt_("bwd_landmarks", s);
       kern<<<BH, nth, bytes, s>>>(la);
