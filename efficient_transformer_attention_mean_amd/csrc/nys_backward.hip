@@ -845,17 +845,32 @@ __global__ __launch_bounds__(256) void k_flip_taps(const float* __restrict__ w, 
   wf[e] = w[e - t + (k - 1 - t)];
 }
 
-// Fixed-order sum over chunks of p[ch * stride], sixteen loads in flight at
-// a time (the loads past the last chunk read nothing and add zero, which
-// leaves the sum's bits unchanged).
-__device__ __forceinline__ float chunk_sum(const float* __restrict__ p, size_t stride, int nchunks, float a) {
-  for (int ch = 0; ch < nchunks; ch += 16) {
-    float x[16];
+// Fixed-order sums over chunks of p[ch * stride] and p2[ch * stride] (p2
+// may be null), 24 chunks' loads of both in flight at a time (the loads past
+// the last chunk read nothing and add zero, which leaves the sums' bits
+// unchanged).
+__device__ __forceinline__ void chunk_sum2(const float* __restrict__ p, const float* __restrict__ p2, size_t stride,
+                                           int nchunks, float& a, float& a2) {
+  constexpr int NB = 24;
+  for (int ch = 0; ch < nchunks; ch += NB) {
+    float x[NB], y[NB];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) x[u] = ch + u < nchunks ? p[(size_t)(ch + u) * stride] : 0.f;
+    for (int u = 0; u < NB; ++u) {
+      const bool in = ch + u < nchunks;
+      x[u] = in ? p[(size_t)(ch + u) * stride] : 0.f;
+      y[u] = (in && p2) ? p2[(size_t)(ch + u) * stride] : 0.f;
+    }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) a += x[u];
+    for (int u = 0; u < NB; ++u) {
+      a += x[u];
+      a2 += y[u];
+    }
   }
+}
+
+__device__ __forceinline__ float chunk_sum(const float* __restrict__ p, size_t stride, int nchunks, float a) {
+  float unused = 0.f;
+  chunk_sum2(p, nullptr, stride, nchunks, a, unused);
   return a;
 }
 
@@ -872,22 +887,31 @@ __global__ __launch_bounds__(1024) void k_bwd_land_prep(const float* __restrict_
   const int tid = threadIdx.x, bh = blockIdx.y, c0 = blockIdx.x * 16;
   const int j = tid >> 4, cl = tid & 15;
   const size_t md = (size_t)bh * m * D, mm = (size_t)bh * m * m, stride = (size_t)m * D;
-  for (int e = tid; e < 64 * 64; e += 1024) {
-    const int r = e / 64, cc = e % 64;
-    zl[r][cc] = (r < m && cc < m) ? Zw[mm + (size_t)r * m + cc] : 0.f;
+  // Z's loads and the partials' are in flight together.
+  float zr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 1024 * q, r = e / 64, cc = e % 64;
+    zr[q] = (r < m && cc < m) ? Zw[mm + (size_t)r * m + cc] : 0.f;
   }
-  float a = 0.f;
+  float a = 0.f, k = 0.f;
   if (j < m) {
     const size_t o = (size_t)bh * nchunks * stride + (size_t)j * D + c0 + cl;
-    a = chunk_sum(pdw + o, stride, nchunks, 0.f);
+    chunk_sum2(pdw + o, pdkt + o, stride, nchunks, a, k);
     dWg[md + (size_t)j * D + c0 + cl] = a;
-    dKt[md + (size_t)j * D + c0 + cl] = chunk_sum(pdkt + o, stride, nchunks, 0.f);
+    dKt[md + (size_t)j * D + c0 + cl] = k;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 1024 * q;
+    zl[e / 64][e % 64] = zr[q];
   }
   wl[j][cl] = a;
   __syncthreads();
   if (j < m) {
     float b = 0.f;
-    for (int i = 0; i < m; ++i) b = fmaf(zl[i][j], wl[i][cl], b);
+#pragma unroll 8
+    for (int i = 0; i < 64; ++i) b = fmaf(zl[i][j], wl[i][cl], b);  // rows past m are zero
     dBV[md + (size_t)j * D + c0 + cl] = b;
   }
 }
