@@ -372,8 +372,10 @@ __device__ __forceinline__ void chain_mm(const B8 (&ph)[MP / 16][MP / 32], const
   }
 }
 
-// Pseudoinverse of one head, run by a block of 4 * MP threads.
-template <int MP, int D>
+// Pseudoinverse of one head, run by a block of 4 * MP threads.  SAVE: also
+// write each step's Z_k, X_k, T1_k, T2_k to zsave (for the backward pass);
+// the plain forward's kernel is compiled without that code.
+template <int MP, int D, bool SAVE>
 __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float* __restrict__ Qt,
                                           const float* __restrict__ Kt, float* __restrict__ Aout,
                                           float* __restrict__ Zout, int m, float sl2e, int iters,
@@ -547,10 +549,10 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
   for (int it = 0; it < iters; ++it) {
     f32x4_t acc[RT];
     B8 Th[KC], Tl[KC];
-    if (zsave) save(zf, it, 0);
+    if constexpr (SAVE) save(zf, it, 0);
     // X = A Z: store X for every wave; keep T1 = 7I - X (own columns).
     chain_mm<MP>(Ah, Al, Zh, Zl, acc);
-    if (zsave) save(acc, it, 1);
+    if constexpr (SAVE) save(acc, it, 1);
     {
       B8 xh[KC], xl[KC];
       to_bop<MP>(acc, 1.f, 0.f, wave, xh, xl);
@@ -562,10 +564,10 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
     load_aop<MP>(sm.xp[0], sm.xp[1], Ph, Pl);
     load_aop<MP>(sm.zp[0], sm.zp[1], Rh, Rl);  // in flight during the two X products
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T1
-    if (zsave) save(acc, it, 2);
+    if constexpr (SAVE) save(acc, it, 2);
     to_bop<MP>(acc, -1.f, 15.f, wave, Th, Tl);
     chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T3
-    if (zsave) save(acc, it, 3);
+    if constexpr (SAVE) save(acc, it, 3);
     to_bop<MP>(acc, -1.f, 13.f, wave, Th, Tl);
     chain_mm<MP>(Rh, Rl, Th, Tl, acc);  // Z T5
 #pragma unroll
@@ -1036,14 +1038,14 @@ union LandmarkPassSmem<false, B> {
   B b;
 };
 
-template <typename IO, int D, int NTW, bool PINV>
+template <typename IO, int D, int NTW, bool PINV, bool SAVE>
 __global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
   using T = typename IO::T;
   __shared__ LandmarkPassSmem<PINV, BvSmem<IO, D>> sm;
   int blk = blockIdx.x;
   if constexpr (PINV) {
     if (blk < a.npinv) {
-      pinv_head<64, D>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters, a.zsave, a.zmp);
+      pinv_head<64, D, SAVE>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters, a.zsave, a.zmp);
       return;
     }
     blk -= a.npinv;
@@ -1345,7 +1347,13 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.sl2e = kLog2e / sqrtf((float)D);
   const int grid = a.npinv + a.nconv + w.nchunks * BH;
   KernelTimer kt_("landmark_pass", s);
-  k_landmark_pass<IO, D, NTW, PINV><<<grid, 256, 0, s>>>(a);
+  if constexpr (PINV) {
+    if (p.zsave) {
+      k_landmark_pass<IO, D, NTW, true, true><<<grid, 256, 0, s>>>(a);
+      return;
+    }
+  }
+  k_landmark_pass<IO, D, NTW, PINV, false><<<grid, 256, 0, s>>>(a);
 }
 
 template <typename IO, int D>
