@@ -991,8 +991,6 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
   f32x4_t aq[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) aq[u] = zero4();
-  const int seg = (n + m - 1) / m;
-  const float inv_seg = 1.f / (float)seg;
 
   const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
   // K and V rows of a tile, 16 bytes per load; the next tile's are in flight
@@ -1104,6 +1102,10 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
   }
 }
 
+// Query side on the matrix cores; grid (chunks, batch*heads), tiles of 64
+// rows.  DQ = false: partials of dW = F^T dO and dKt_F = s dS_F^T Q per chunk.
+// DQ = true: dQ_i = s dS_i Kt + dQt[seg(i)] / l, and dK of key i (same index)
+// += dKt[seg(i)] / l, the landmark term the key pass leaves out.
 template <int D, bool DQ>
 struct RowMmSmem {
   static constexpr int PD = D + 8, PK = 64 + 8;
