@@ -66,22 +66,32 @@ def algorithmic_bytes(wl, kernel: str, token_rows=None) -> int:
 
 
 def backward_flops(wl, kernel: str) -> float:
-    """fp32 vector flops each backward kernel performs per launch (2 per
-    multiply-add; per-row figure x rows over all heads)."""
+    """Flops each backward kernel performs per launch (2 per multiply-add;
+    per-row figure x rows over all heads)."""
     rows = float(wl.batch * wl.heads * wl.n)
     md, kd = wl.m * wl.d, wl.conv_k * wl.d
+    # bf16 I/O at d = 32, 64: matrix-core passes, with the skip in kernels of its own.
+    mm = wl.dtype == "bf16" and wl.d in (32, 64)
     if kernel == "bwd_rows_reduce":
         return rows * 2 * 4 * md           # scores, dO W^T, F^T dO, dS^T Q
     if kernel == "bwd_keys":
-        return rows * 2 * (5 * md + 2 * kd)  # scores, dBV V^T, dS^T Qt, B^T dBV, dS K; skip transpose, filter gradient
+        # scores, dBV V^T, dS^T Qt, B^T dBV, dS K; the vector path also runs
+        # the skip's transpose and filter gradient here
+        return rows * 2 * (5 * md + (0 if mm else 2 * kd))
+    if kernel == "bwd_skip_grad":
+        return rows * 2 * kd               # filter gradient
+    if kernel == "dconv":
+        return rows * 2 * kd               # the skip's transpose (the forward's convolution)
     if kernel == "bwd_rows_dq":
         return rows * 2 * 3 * md           # scores, dO W^T, dS Kt
+    if kernel == "bwd_land_prep":
+        return wl.batch * wl.heads * 2.0 * wl.m * wl.m * wl.d  # dBV = Z^T dW
     if kernel == "bwd_landmarks":
         # per head: 8 products per step of the reverse pass (m x m x m each;
-        # the forward steps are saved by the recomputed forward), dZ, dBV,
-        # dQt_A, dKt_A (m x m x d each)
+        # the forward steps are saved by the recomputed forward), dZ, dQt_A,
+        # dKt_A (m x m x d each)
         m3, steps = float(wl.m) ** 3, wl.iters
-        per_head = 2 * m3 * 8 * steps + 8.0 * wl.m * wl.m * wl.d
+        per_head = 2 * m3 * 8 * steps + 6.0 * wl.m * wl.m * wl.d
         return wl.batch * wl.heads * per_head
     return 0.0
 
@@ -620,8 +630,10 @@ def backward_bench(args, wl, dev) -> int:
         if fl:
             # bf16 I/O at d = 32, 64 runs the products on the matrix cores
             # (bf16 peak); otherwise they are fp32 vector work.  The
-            # landmark-side block always uses the matrix cores.
-            mm = (wl.dtype == "bf16" and wl.d in (32, 64)) or dom == "bwd_landmarks"
+            # landmark-side block always uses the matrix cores; the skip's
+            # filter gradient and the prep kernel are vector work.
+            mm = ((wl.dtype == "bf16" and wl.d in (32, 64)) or dom == "bwd_landmarks") and \
+                dom not in ("bwd_skip_grad", "bwd_land_prep")
             peak = MFMA_BF16_PEAK_TFLOPS if mm else FP32_VECTOR_PEAK_TFLOPS
             achieved = fl / avg_s / 1e12
             roof = {"bound": "mfma" if mm else "alu", "achieved": round(achieved, 2), "peak": peak,
