@@ -27,8 +27,10 @@
 // dBV, so it runs on a second stream beside k_bwd_land (one block per head),
 // after the skip's share, forked there at the start of the call (it reads
 // only inputs): dV = DConv^T(dO) by the forward's convolution with the taps
-// reversed, and the filter gradient (k_bwd_skip_grad).  k_bwd_key_mm leaves
-// out the seg^T dKt term of dK; the dQ pass adds it once dKt is complete.
+// reversed, and the filter gradient (k_bwd_skip_grad).  The query-side pass
+// k_bwd_rows_mm also writes dQ's first term s dS_F Kt, and k_bwd_key_mm
+// leaves out the seg^T dKt term of dK; once the landmark side is done,
+// k_bwd_spread adds seg^T dQt to dQ and seg^T dKt to dK.
 //
 // The n-sized passes run in fp32 on the vector units with their operands in
 // LDS; the m x m products of the pseudoinverse backward use the matrix cores
@@ -1103,28 +1105,26 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
 }
 
 // Query side on the matrix cores; grid (chunks, batch*heads), tiles of 64
-// rows.  DQ = false: partials of dW = F^T dO and dKt_F = s dS_F^T Q per chunk.
-// DQ = true: dQ_i = s dS_i Kt + dQt[seg(i)] / l, and dK of key i (same index)
-// += dKt[seg(i)] / l, the landmark term the key pass leaves out.
-template <int D, bool DQ>
+// rows: partials of dW = F^T dO and dKt_F = s dS_F^T Q per chunk, and
+// dQ_i = s dS_i Kt, written as the first dQ (the landmark term seg^T dQt
+// needs the pseudoinverse backward; k_bwd_spread adds it).
+template <int D>
 struct RowMmSmem {
   static constexpr int PD = D + 8, PK = 64 + 8;
   uint16_t ka[64][PD];   // Kt * log2(e)/sqrt(d) rows (A of the scores)
   uint16_t wa[64][PD];   // W rows (A of dF)
-  uint16_t kT[DQ ? D : 1][PK];  // Kt^T in mm_slot order (A of dQ^T; the dQ pass only)
   uint16_t qr[kMmTile][PD], gr[kMmTile][PD];  // Q and dO rows of the tile
-  uint16_t qT[DQ ? 1 : D][PK], gT[DQ ? 1 : D][PK];  // the same transposed (B of dKt, dW)
-  uint16_t fT[DQ ? 1 : 64][PK], sT[DQ ? 1 : 64][PK];  // F^T, dS^T of the tile (A of dW, dKt)
+  uint16_t qT[D][PK], gT[D][PK];              // the same transposed (B of dKt, dW)
+  uint16_t fT[64][PK], sT[64][PK];            // F^T, dS^T of the tile (A of dW, dKt); Kt^T before the first tile
 };
 
-template <int D, bool DQ>
+template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ Kt, const float* __restrict__ W,
-                                                     const float* __restrict__ dqt, uint16_t* __restrict__ dQ,
-                                                     const float* __restrict__ dkt, uint16_t* __restrict__ dK,
-                                                     float* __restrict__ pdw, float* __restrict__ pdkt, int n, int m,
-                                                     int chunk, int nchunks, float sl2e, float scale) {
-  using SM = RowMmSmem<D, DQ>;
+                                                     uint16_t* __restrict__ dQ, float* __restrict__ pdw,
+                                                     float* __restrict__ pdkt, int n, int m, int chunk, int nchunks,
+                                                     float sl2e, float scale) {
+  using SM = RowMmSmem<D>;
   constexpr int KC = D / 32, ND = D / 16, PER = ND;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
@@ -1137,13 +1137,19 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
     const float k = j < m ? Kt[md + e] : 0.f;
     sm.ka[j][f] = bf(k * sl2e);
     sm.wa[j][f] = bf(j < m ? W[md + e] : 0.f);
-    if constexpr (DQ) sm.kT[f][mm_slot(j)] = bf(k);
+    sm.fT[f][mm_slot(j)] = bf(k);  // Kt^T, landmarks in mm_slot order (f < D <= 64)
   }
+  __syncthreads();
+  // Kt^T fragments (A of dQ^T = Kt^T dS^T) to registers; the tile loop's
+  // first barrier comes before fT is written again.
+  B8 kfr[ND][2];
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) kfr[nd][kk] = lds8(&sm.fT[nd * 16 + c][kk * 32 + 8 * g]);
   f32x4_t aw[PER], ak[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) aw[u] = ak[u] = zero4();
-  const int seg = (n + m - 1) / m;
-  const float inv_seg = 1.f / (float)seg;
 
   const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
   // Q and dO rows of a tile, 16 bytes per load; the next tile's are in
@@ -1170,12 +1176,10 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
       gv.q = gn[l];
       *reinterpret_cast<uint4*>(&sm.qr[rr][c8]) = q.q;
       *reinterpret_cast<uint4*>(&sm.gr[rr][c8]) = gv.q;
-      if constexpr (!DQ) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          sm.qT[c8 + u][rr] = q.h[u];
-          sm.gT[c8 + u][rr] = gv.h[u];
-        }
+      for (int u = 0; u < 8; ++u) {
+        sm.qT[c8 + u][rr] = q.h[u];
+        sm.gT[c8 + u][rr] = gv.h[u];
       }
     }
     __syncthreads();
@@ -1183,13 +1187,6 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
 
     const int rl = 16 * wave + c, row = t0 + rl;
     const bool live = row < rend;
-    // dQ pass: the key pass's dK of key `row`, read now, updated at the end.
-    uint2 kp[DQ ? ND : 1];
-    if constexpr (DQ) {
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd)
-        kp[nd] = live ? *reinterpret_cast<const uint2*>(dK + hoff + (size_t)row * D + nd * 16 + 4 * g) : make_uint2(0, 0);
-    }
     f32x4_t sc[4], df[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -1236,70 +1233,87 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
         if (!live) sc[mt][i] = 0.f;
       }
 
-    if constexpr (DQ) {
-      // The products run on every lane (a matrix-core instruction reads the
-      // operands of the whole wave); only the stores are per row.
-      const size_t sro = md + (size_t)min(row / seg, m - 1) * D;
-      const float* qtr = dqt + sro;
-      const float* ktr = dkt + sro;
+    // dQ^T of the tile = Kt^T dS^T.  The products run on every lane (a
+    // matrix-core instruction reads the operands of the whole wave); only
+    // the stores are per row.
 #pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        f32x4_t a = zero4();
+    for (int nd = 0; nd < ND; ++nd) {
+      f32x4_t a = zero4();
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          a = mfma(lds8(&sm.kT[nd * 16 + c][kk * 32 + 8 * g]), pack_b(df[2 * kk], df[2 * kk + 1]), a);
-        if (live) {
-          const int f0 = nd * 16 + 4 * g;
-          const float4 q4 = *reinterpret_cast<const float4*>(qtr + f0);
-          const float v0 = fmaf(scale, a[0], q4.x * inv_seg), v1 = fmaf(scale, a[1], q4.y * inv_seg);
-          const float v2 = fmaf(scale, a[2], q4.z * inv_seg), v3 = fmaf(scale, a[3], q4.w * inv_seg);
-          *reinterpret_cast<uint2*>(dQ + hoff + (size_t)row * D + f0) =
-              make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-          // dK of key `row` += dKt[seg(row)] / l (the key pass wrote the rest).
-          const float4 k4 = *reinterpret_cast<const float4*>(ktr + f0);
-          uint2* kd = reinterpret_cast<uint2*>(dK + hoff + (size_t)row * D + f0);
-          const float k0 = __uint_as_float(kp[nd].x << 16) + k4.x * inv_seg;
-          const float k1 = __uint_as_float(kp[nd].x & 0xffff0000u) + k4.y * inv_seg;
-          const float k2 = __uint_as_float(kp[nd].y << 16) + k4.z * inv_seg;
-          const float k3 = __uint_as_float(kp[nd].y & 0xffff0000u) + k4.w * inv_seg;
-          *kd = make_uint2(pack_bf16x2(k0, k1), pack_bf16x2(k2, k3));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sm.fT[mt * 16 + 4 * g + i][rl] = bf(sc[mt][i]);
-          sm.sT[mt * 16 + 4 * g + i][rl] = bf(df[mt][i]);
-        }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          aw[u] = mfma(lds8(&sm.fT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.gT[nd * 16 + c][kc * 32 + 8 * g]), aw[u]);
-          ak[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.qT[nd * 16 + c][kc * 32 + 8 * g]), ak[u]);
-        }
-      }
+      for (int kk = 0; kk < 2; ++kk) a = mfma(kfr[nd][kk], pack_b(df[2 * kk], df[2 * kk + 1]), a);
+      if (live)
+        *reinterpret_cast<uint2*>(dQ + hoff + (size_t)row * D + nd * 16 + 4 * g) =
+            make_uint2(pack_bf16x2(scale * a[0], scale * a[1]), pack_bf16x2(scale * a[2], scale * a[3]));
     }
-  }
-  if constexpr (!DQ) {
-    const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sm.fT[mt * 16 + 4 * g + i][rl] = bf(sc[mt][i]);
+        sm.sT[mt * 16 + 4 * g + i][rl] = bf(df[mt][i]);
+      }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = mt * 16 + 4 * g + i;
-        if (j < m) {
-          pdw[base + (size_t)j * D + nd * 16 + c] = aw[u][i];
-          pdkt[base + (size_t)j * D + nd * 16 + c] = scale * ak[u][i];
-        }
+      for (int kc = 0; kc < 2; ++kc) {
+        aw[u] = mfma(lds8(&sm.fT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.gT[nd * 16 + c][kc * 32 + 8 * g]), aw[u]);
+        ak[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.qT[nd * 16 + c][kc * 32 + 8 * g]), ak[u]);
       }
     }
   }
+  const size_t base = ((size_t)bh * nchunks + ch) * m * D;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = mt * 16 + 4 * g + i;
+      if (j < m) {
+        pdw[base + (size_t)j * D + nd * 16 + c] = aw[u][i];
+        pdkt[base + (size_t)j * D + nd * 16 + c] = scale * ak[u][i];
+      }
+    }
+  }
+}
+
+// The landmark terms of the matrix-core path, once dQt and dKt are complete:
+// dQ_i += dQt[seg(i)] / l and dK_i += dKt[seg(i)] / l, rows i of the
+// segment of landmark min(i / l, m - 1).  One thread per 16-byte vector of 8
+// bf16 features of dQ and of dK; grid over batch*heads*n*D/8.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_spread(const float* __restrict__ dqt, const float* __restrict__ dkt,
+                                                    uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, int n,
+                                                    int m, long long total) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  constexpr int V = D / 8;
+  const int c8 = (int)(e % V) * 8;
+  const long long r = e / V;  // bh * n + row
+  const int row = (int)(r % n);
+  const long long bh = r / n;
+  const int seg = (n + m - 1) / m;
+  const float inv_seg = 1.f / (float)seg;
+  const size_t so = ((size_t)bh * m + min(row / seg, m - 1)) * D + c8;
+  const float4 qa = *reinterpret_cast<const float4*>(dqt + so), qb = *reinterpret_cast<const float4*>(dqt + so + 4);
+  const float4 ka = *reinterpret_cast<const float4*>(dkt + so), kb = *reinterpret_cast<const float4*>(dkt + so + 4);
+  uint4* qp = reinterpret_cast<uint4*>(dQ) + e;
+  uint4* kp = reinterpret_cast<uint4*>(dK) + e;
+  B8 qv, kv, qo, ko;
+  qv.q = *qp;
+  kv.q = *kp;
+  const float qf[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+  const float kf[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    qo.u[u] = pack_bf16x2(bf16_to_f32(qv.h[2 * u]) + qf[2 * u] * inv_seg,
+                          bf16_to_f32(qv.h[2 * u + 1]) + qf[2 * u + 1] * inv_seg);
+    ko.u[u] = pack_bf16x2(bf16_to_f32(kv.h[2 * u]) + kf[2 * u] * inv_seg,
+                          bf16_to_f32(kv.h[2 * u + 1]) + kf[2 * u + 1] * inv_seg);
+  }
+  *qp = qo.q;
+  *kp = ko.q;
 }
 
 // dQt = dQt_A + sum of the key-side partials (chunk order); grid
@@ -1433,17 +1447,18 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   constexpr int P = D + 1;
 
   constexpr bool MM = IO::kBf16 && (D == 32 || D == 64);  // matrix-core n-sized passes
-  // Query side, partials of dW and dKt_F.
+  // Query side, partials of dW and dKt_F (on the matrix-core path also the
+  // first dQ, s dS_F Kt).
   if constexpr (MM) {
-    const int bytes = (int)sizeof(RowMmSmem<D, false>);
-    auto kern = &k_bwd_rows_mm<D, false>;
+    const int bytes = (int)sizeof(RowMmSmem<D>);
+    auto kern = &k_bwd_rows_mm<D>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("bwd_rows_reduce", s);
     kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                            w.Kt, w.W, nullptr, nullptr, nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n,
-                                            p.m, L.qchunk, L.nq, sl2e, scale);
+                                            w.Kt, w.W, static_cast<uint16_t*>(bp.dQ), F(L.pdw), F(L.pdkt), p.n, p.m,
+                                            L.qchunk, L.nq, sl2e, scale);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, false>;
@@ -1541,20 +1556,13 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     KernelTimer kt_("bwd_finish", s);
     k_bwd_qt_finish<<<dim3(cdivi(p.m * D, 256), BH), 256, 0, s>>>(F(L.dqta), F(L.pdqt), F(L.dqt), p.m * D, L.nk);
   }
-  // Query side again: dQ.
+  // The landmark terms of dQ and dK (matrix-core path), or the query side
+  // again for dQ (vector path).
   if constexpr (MM) {
-    const int bytes = (int)sizeof(RowMmSmem<D, true>);
-    auto kern = &k_bwd_rows_mm<D, true>;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (attr != hipSuccess) return attr;
-    // One chunk of rows per block, as in the reduction pass: the landmark
-    // planes are built once per block rather than once per 64-row tile.
-    KernelTimer kt_("bwd_rows_dq", s);
-    kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                            w.Kt, w.W, F(L.dqt), static_cast<uint16_t*>(bp.dQ), F(L.dkt),
-                                            static_cast<uint16_t*>(bp.dK), nullptr, nullptr, p.n, p.m, L.qchunk,
-                                            L.nq, sl2e, scale);
+    const long long total = (long long)BH * p.n * (D / 8);
+    KernelTimer kt_("bwd_spread", s);
+    k_bwd_spread<D><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(F(L.dqt), F(L.dkt), static_cast<uint16_t*>(bp.dQ),
+                                                                     static_cast<uint16_t*>(bp.dK), p.n, p.m, total);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, true>;
