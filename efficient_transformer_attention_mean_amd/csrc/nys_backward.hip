@@ -723,6 +723,30 @@ __device__ __forceinline__ B8 lds8(const uint16_t* p) {
   return b;
 }
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// B operand of a 16x16x32 product, M[kb + 8g + u][nb + c] for lane (c, g),
+// read from a row-major bf16 tile in LDS (pitch PD) with two transpose reads:
+// in each group of 16 lanes, lane j gives the address of 4 consecutive
+// elements of row kb + 8g + j/4 (+ 4 for the second read), columns
+// nb + 4(j % 4) .. +3, and lane i of the group receives column nb + i of
+// the four rows the group read.
+template <int PD>
+__device__ __forceinline__ B8 tr_b(const uint16_t (*M)[PD], int kb, int nb) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
+  const uint16_t* p0 = &M[kb + 8 * g + (j >> 2)][nb + 4 * (j & 3)];
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p0));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p0 + 4 * PD));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  B8 b;
+  b.u[0] = l2.x;
+  b.u[1] = l2.y;
+  b.u[2] = h2.x;
+  b.u[3] = h2.y;
+  return b;
+}
+
 // C-layout values of landmark tiles 2kk and 2kk+1 as a B operand.
 __device__ __forceinline__ B8 pack_b(const f32x4_t& lo, const f32x4_t& hi) {
   B8 b;
@@ -941,8 +965,7 @@ struct KeyMmSmem {
   uint16_t da[64][PD];       // dBV rows (A of dB)
   uint16_t qT[D][PK];        // Qt^T, landmarks in mm_slot order (A of dK^T)
   uint16_t dT[D][PK];        // dBV^T, mm_slot order (A of dV^T)
-  uint16_t kr[kMmTile][PD];  // key rows of the tile
-  uint16_t kT[D][PK];        // the same transposed (B of dQt)
+  uint16_t kr[kMmTile][PD];  // key rows of the tile (also B of dQt, read transposed)
   uint16_t vr[kMmTile][PD];  // V rows of the tile
   uint16_t sT[64][PK];       // dS^T of the tile (A of dQt)
   float stm[64], stl[64], dlt[64];
@@ -1014,11 +1037,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
       const int e = tid + 256 * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8;
-      B8 v;
-      v.q = kn[l];
-      *reinterpret_cast<uint4*>(&sm.kr[rr][c8]) = v.q;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) sm.kT[c8 + q][rr] = v.h[q];
+      *reinterpret_cast<uint4*>(&sm.kr[rr][c8]) = kn[l];
       *reinterpret_cast<uint4*>(&sm.vr[rr][c8]) = vn[l];
     }
     __syncthreads();
@@ -1089,7 +1108,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
       const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
-        aq[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.kT[nd * 16 + c][kc * 32 + 8 * g]), aq[u]);
+        aq[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), tr_b<SM::PD>(sm.kr, kc * 32, nd * 16), aq[u]);
     }
   }
   const size_t base = ((size_t)bh * nchunks + ch) * m * D;
@@ -1113,8 +1132,7 @@ struct RowMmSmem {
   static constexpr int PD = D + 8, PK = 64 + 8;
   uint16_t ka[64][PD];   // Kt * log2(e)/sqrt(d) rows (A of the scores)
   uint16_t wa[64][PD];   // W rows (A of dF)
-  uint16_t qr[kMmTile][PD], gr[kMmTile][PD];  // Q and dO rows of the tile
-  uint16_t qT[D][PK], gT[D][PK];              // the same transposed (B of dKt, dW)
+  uint16_t qr[kMmTile][PD], gr[kMmTile][PD];  // Q and dO rows of the tile (also B of dKt, dW, read transposed)
   uint16_t fT[64][PK], sT[64][PK];            // F^T, dS^T of the tile (A of dW, dKt); Kt^T before the first tile
 };
 
@@ -1176,11 +1194,6 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
       gv.q = gn[l];
       *reinterpret_cast<uint4*>(&sm.qr[rr][c8]) = q.q;
       *reinterpret_cast<uint4*>(&sm.gr[rr][c8]) = gv.q;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        sm.qT[c8 + u][rr] = q.h[u];
-        sm.gT[c8 + u][rr] = gv.h[u];
-      }
     }
     __syncthreads();
     if (t0 + kMmTile < rend) fetch(t0 + kMmTile);
@@ -1258,8 +1271,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
       const int t = wave + 4 * u, mt = t & 3, nd = t >> 2;
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        aw[u] = mfma(lds8(&sm.fT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.gT[nd * 16 + c][kc * 32 + 8 * g]), aw[u]);
-        ak[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), lds8(&sm.qT[nd * 16 + c][kc * 32 + 8 * g]), ak[u]);
+        aw[u] = mfma(lds8(&sm.fT[mt * 16 + c][kc * 32 + 8 * g]), tr_b<SM::PD>(sm.gr, kc * 32, nd * 16), aw[u]);
+        ak[u] = mfma(lds8(&sm.sT[mt * 16 + c][kc * 32 + 8 * g]), tr_b<SM::PD>(sm.qr, kc * 32, nd * 16), ak[u]);
       }
     }
   }
