@@ -25,9 +25,10 @@
 //
 // On the matrix-core path (bf16 I/O, d = 32 or 64) the key side needs only
 // dBV, so it runs on a second stream beside k_bwd_land (one block per head),
-// after the skip's share, forked there at the start of the call (it reads
-// only inputs): dV = DConv^T(dO) by the forward's convolution with the taps
-// reversed, and the filter gradient (k_bwd_skip_grad).  The query-side pass
+// after the skip's share, which reads only inputs: the filter gradient
+// (k_bwd_skip_grad, forked at the start of the call, beside the forward's
+// stages) and dV = DConv^T(dO) by the forward's convolution with the taps
+// reversed (forked after them, beside the query-side reduction).  The query-side pass
 // k_bwd_rows_mm also writes dQ's first term s dS_F Kt, and k_bwd_key_mm
 // leaves out the seg^T dKt term of dK; once the landmark side is done,
 // k_bwd_spread adds seg^T dQt to dQ and seg^T dKt to dK.
@@ -1358,7 +1359,7 @@ static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
 // several host threads cannot take each other's event records.
 struct SideStream {
   hipStream_t st = nullptr;
-  hipEvent_t start = nullptr, fork = nullptr, join = nullptr;
+  hipEvent_t start = nullptr, mid = nullptr, fork = nullptr, join = nullptr;
 };
 // One call's use of the side stream: `pending` while work forked onto it has
 // not been joined back to the caller's stream.
@@ -1377,9 +1378,9 @@ hipError_t side_stream_locked(SideStream** out) {
   SideStream& ss = g_side[dev];
   if (!ss.st) {
     hipStream_t st = nullptr;
-    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
       if ((e = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming)) != hipSuccess) {
         for (int k = 0; k < i; ++k) (void)hipEventDestroy(ev[k]);
         (void)hipStreamDestroy(st);
@@ -1387,8 +1388,9 @@ hipError_t side_stream_locked(SideStream** out) {
       }
     }
     ss.start = ev[0];
-    ss.fork = ev[1];
-    ss.join = ev[2];
+    ss.mid = ev[1];
+    ss.fork = ev[2];
+    ss.join = ev[3];
     ss.st = st;
   }
   *out = &ss;
@@ -1591,17 +1593,22 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
   return hipGetLastError();
 }
 
-// The skip's share of the matrix-core path, on the side stream: dV =
-// DConv^T(dO) (the forward's convolution with the taps reversed, written as
-// the initial dV) and the filter-gradient partials.  It reads only inputs.
+// The skip's share of the matrix-core path, on the side stream; it reads
+// only inputs.  dV = DConv^T(dO): the forward's convolution with the taps
+// reversed, written as the initial dV.
 template <int D>
-static hipError_t skip_side(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
+static hipError_t skip_transpose(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
   const Problem& p = bp.fwd;
   float* wf = reinterpret_cast<float*>(ws + L.wflip);
   const int total = p.heads * D * p.conv_k;
   k_flip_taps<<<cdivi(total, 256), 256, 0, ks>>>(p.conv_w, wf, p.conv_k, total);
-  hipError_t e = launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks);
-  if (e != hipSuccess) return e;
+  return launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks);
+}
+
+// The filter-gradient partials.
+template <int D>
+static hipError_t skip_grad(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
+  const Problem& p = bp.fwd;
   KernelTimer kt_("bwd_skip_grad", ks);
   k_bwd_skip_grad<D><<<dim3(L.nk, p.batch * p.heads), 4 * D, (int)sizeof(SkipSmem<D>), ks>>>(
       static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), reinterpret_cast<float*>(ws + L.pdwc),
@@ -1613,14 +1620,15 @@ static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* 
   const Problem& p = bp.fwd;
   const Ws w = resolve(L.fwd, ws);
   hipError_t e;
+  const bool skip = sc.ss && p.conv_w && p.conv_k > 0;
   if (sc.ss) {
-    // Fork: the skip's share needs only the inputs, so it runs beside the
-    // forward's stages and the query-side reduction.
+    // Fork: the skip's filter gradient needs only the inputs; it runs
+    // beside the forward's stages.
     if ((e = hipEventRecord(sc.ss->start, s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(sc.ss->st, sc.ss->start, 0)) != hipSuccess) return e;
     sc.pending = true;
-    if (p.conv_w && p.conv_k > 0) {
-      e = p.d == 32 ? skip_side<32>(bp, L, ws, sc.ss->st) : skip_side<64>(bp, L, ws, sc.ss->st);
+    if (skip) {
+      e = p.d == 32 ? skip_grad<32>(bp, L, ws, sc.ss->st) : skip_grad<64>(bp, L, ws, sc.ss->st);
       if (e != hipSuccess) return e;
     }
   }
@@ -1629,6 +1637,14 @@ static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* 
   if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
   if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
   if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
+  if (skip) {
+    // The skip's transpose (a streaming convolution that would slow the
+    // landmark pass) runs beside the query-side reduction.
+    if ((e = hipEventRecord(sc.ss->mid, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sc.ss->st, sc.ss->mid, 0)) != hipSuccess) return e;
+    e = p.d == 32 ? skip_transpose<32>(bp, L, ws, sc.ss->st) : skip_transpose<64>(bp, L, ws, sc.ss->st);
+    if (e != hipSuccess) return e;
+  }
   switch (p.d) {
     case 16: return p.bf16 ? bwd_t<BF16, 16>(bp, L, ws, s, sc) : bwd_t<F32, 16>(bp, L, ws, s, sc);
     case 32: return p.bf16 ? bwd_t<BF16, 32>(bp, L, ws, s, sc) : bwd_t<F32, 32>(bp, L, ws, s, sc);
