@@ -102,3 +102,49 @@ def test_backward_rejects_unsupported():
                                None, 0, None)
     assert rc == _lib.NYS_EUNSUPPORTED
     assert _lib.nystrom_attn_bwd_workspace_bytes(1, 1, 128, 16, 80, 6, 0) == 0
+
+
+def test_backward_two_host_threads():
+    """Two host threads call the bf16 d = 64 backward at once, each on its own
+    stream with its own buffers.  The library shares one side stream per
+    device between them, and enqueues each call's fork and join under a lock.
+    Every result must equal the single-thread result bit for bit."""
+    import threading
+
+    wl = WORKLOADS["headline"].with_(name="bwd_threads", batch=1, heads=2, n=2048)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 17)
+    ref = run_backward(inp, dO, wl.m, wl.iters, wl.dtype)
+    nbytes = _lib.nystrom_attn_bwd_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m, wl.iters, wl.conv_k)
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                Q, K, V, G = (to_dev(x, wl.dtype) for x in (inp["Q"], inp["K"], inp["V"], dO))
+                w = torch.from_numpy(np.ascontiguousarray(inp["conv_w"], np.float32)).cuda()
+                dQ, dK, dV, dW = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V), torch.empty_like(w)
+                ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+                outs = []
+                for _ in range(4):
+                    rc = _lib.nystrom_attn_bwd(Q, K, V, w, G, wl.n, wl.d, wl.m, wl.heads, wl.iters, dQ, dK, dV, dW,
+                                               wl.batch, wl.conv_k, dtype_code(wl.dtype), ws, nbytes, stream)
+                    assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+                    stream.synchronize()
+                    outs.append((to_host(dQ), to_host(dK), to_host(dV), dW.cpu().numpy()))
+                results[tid] = outs
+        except Exception as exc:  # reported by the main thread
+            errors.append(repr(exc))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=90)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for outs in results.values():
+        for got in outs:
+            for x, y in zip(got, ref):
+                assert np.array_equal(x, y)
