@@ -60,6 +60,8 @@ CASES = [
     (2, 12, 512, 64, 64, 6, 33, "f32"),     # BERT-base-shaped layer
     (1, 3, 777, 32, 48, 6, 33, "bf16"),     # m = 48 (padded to 64), ragged
     (2, 12, 8192, 64, 64, 6, 33, "bf16"),   # headline shape
+    (1, 2, 512, 64, 64, 6, 0, "bf16"),      # matrix-core path without the skip
+    (2, 2, 300, 32, 16, 6, 1, "bf16"),      # matrix-core path, one-tap skip, ragged n
 ]
 
 
