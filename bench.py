@@ -654,6 +654,41 @@ def backward_bench(args, wl, dev) -> int:
         "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
         "compulsory_bytes": io_bytes, "wall_s": round(wall, 4), "roofline": roof, "kernels": per_kernel,
     }
+
+    # The training pair: nystrom_attn_fwd_save once per input set (each set
+    # keeps its own saved state), then nystrom_attn_bwd_saved timed over the
+    # same rotation: the backward without recomputing the forward's landmark side.
+    saved = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(sets)]
+    for i in range(sets):
+        Q, K, V, G, W, dQ, dK, dV, dW = bufs[i]
+        rc = _lib.nystrom_attn_fwd_save(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, torch.empty_like(Q),
+                                        wl.batch, conv_k, code, saved[i], ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    def step_saved(i):
+        Q, K, V, G, W, dQ, dK, dV, dW = bufs[i % sets]
+        rc = _lib.nystrom_attn_bwd_saved(Q, K, V, W, G, wl.n, wl.d, wl.m, wl.heads, wl.iters, dQ, dK, dV, dW,
+                                         wl.batch, conv_k, code, saved[i % sets], ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+
+    for i in range(args.warmup):
+        step_saved(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step_saved(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    saved_s = ev0.elapsed_time(ev1) / 1e3
+    result["backward_from_saved_forward"] = {
+        "ms_per_step": round(1e3 * saved_s / args.steps, 5),
+        "value": round(tokens * args.steps / saved_s, 1), "unit": "tokens/s",
+        "note": "nystrom_attn_bwd_saved after nystrom_attn_fwd_save: the forward's landmark-side state is reused, "
+                "not recomputed",
+    }
+    del saved
     if not args.no_cpu_baseline or not args.no_parity:
         from oracle import nystrom_attention_backward
         threads = blas_threads()

@@ -127,11 +127,19 @@ size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int 
   return L.total > Lb.total ? L.total : Lb.total;
 }
 
-int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d,
-                     int m, int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k,
-                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward entry points: saved = false recomputes the forward's landmark
+// side in `workspace` (allocated when NULL); saved = true takes it from
+// `workspace` as nystrom_attn_fwd_save left it (which must then be given).
+int backward(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d, int m,
+             int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream, bool saved) {
   try {
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return NYS_EINVAL;
+    if (saved && !workspace) return NYS_EINVAL;
     if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
     if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
     const int rc = check_shape(batch, heads, n, d, m, iters);
@@ -150,7 +158,7 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
     }
     nys::BwdProblem p{{Q, K, V, conv_w, nullptr, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16}, dO, dQ, dK,
                       dV, conv_w ? dconv_w : nullptr};
-    hipError_t e = nys::launch_backward(p, L, ws, s);
+    hipError_t e = nys::launch_backward(p, L, ws, s, !saved);
     if (owned) {
       hipError_t f = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = f;
@@ -159,6 +167,45 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
   } catch (...) {
     return NYS_EHIP;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d,
+                     int m, int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, workspace,
+                  workspace_bytes, stream, false);
+}
+
+int nystrom_attn_fwd_save(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
+                          int heads, int iters, void* out, int batch, int conv_k, int dtype, void* saved,
+                          size_t saved_bytes, void* stream) {
+  try {
+    if (!Q || !K || !V || !out || !saved) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    const int ck = conv_w ? conv_k : 0;
+    nys::BwdLayout L;
+    if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
+    if (saved_bytes < L.total) return NYS_EWORKSPACE;
+    nys::Problem p{Q, K, V, conv_w, out, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16};
+    const hipError_t e = nys::launch_forward_save(p, L, static_cast<char*>(saved), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NYS_OK : NYS_EHIP;
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
+
+int nystrom_attn_bwd_saved(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n,
+                           int d, int m, int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch,
+                           int conv_k, int dtype, void* saved, size_t saved_bytes, void* stream) {
+  return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, saved,
+                  saved_bytes, stream, true);
 }
 
 size_t nystrom_layer_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype) {

@@ -1616,7 +1616,8 @@ static hipError_t skip_grad(const BwdProblem& bp, const BwdLayout& L, char* ws, 
   return hipSuccess;
 }
 
-static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc) {
+static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc,
+                                bool recompute) {
   const Problem& p = bp.fwd;
   const Ws w = resolve(L.fwd, ws);
   hipError_t e;
@@ -1632,11 +1633,14 @@ static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* 
       if (e != hipSuccess) return e;
     }
   }
-  // The forward's landmark side: Qt, Kt, A, Z, BV, W and B's statistics.
-  if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
-  if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
-  if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
-  if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
+  // The forward's landmark side: Qt, Kt, A, Z, BV, W and B's statistics
+  // (already in ws when the forward saved them).
+  if (recompute) {
+    if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
+    if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
+    if ((e = stage_pinv(p, w, s)) != hipSuccess) return e;
+    if ((e = stage_bv_finish(p, w, s)) != hipSuccess) return e;
+  }
   if (skip) {
     // The skip's transpose (a streaming convolution that would slow the
     // landmark pass) runs beside the query-side reduction.
@@ -1654,7 +1658,14 @@ static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* 
   }
 }
 
-hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s) {
+hipError_t launch_forward_save(const Problem& p0, const BwdLayout& L, char* ws, hipStream_t s) {
+  Problem p = p0;
+  p.zsave = reinterpret_cast<float*>(ws + L.zs);
+  p.zmp = L.mp;
+  return launch_forward(p, L.fwd, ws, s);
+}
+
+hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s, bool recompute) {
   // The forward's pseudoinverse kernel also saves its steps for the reverse pass.
   BwdProblem bp = bp0;
   bp.fwd.zsave = reinterpret_cast<float*>(ws + L.zs);
@@ -1662,14 +1673,14 @@ hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, 
   const Problem& p = bp.fwd;
   if (!(p.bf16 && (p.d == 32 || p.d == 64))) {
     SideCall none;
-    return backward_body(bp, L, ws, s, none);
+    return backward_body(bp, L, ws, s, none, recompute);
   }
   // Matrix-core path: this call's forks and joins are enqueued under the lock.
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideCall sc;
   hipError_t e = side_stream_locked(&sc.ss);
   if (e != hipSuccess) return e;
-  e = backward_body(bp, L, ws, s, sc);
+  e = backward_body(bp, L, ws, s, sc, recompute);
   if (sc.pending) {
     // An error left work on the side stream: join it all the same.
     if (hipEventRecord(sc.ss->join, sc.ss->st) == hipSuccess) (void)hipStreamWaitEvent(s, sc.ss->join, 0);

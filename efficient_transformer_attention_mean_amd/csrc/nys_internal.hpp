@@ -105,7 +105,12 @@ struct BwdProblem {
   float* dconv_w;  // fp32 [heads][d][conv_k] or nullptr
 };
 
-hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, char* ws, hipStream_t s);
+// recompute = false: the forward's landmark-side state (and its saved
+// pseudoinverse steps) is already in ws, written by launch_forward_save.
+hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, char* ws, hipStream_t s, bool recompute = true);
+// The forward pass on the forward regions of a backward workspace, saving the
+// pseudoinverse steps there too, so that launch_backward can skip its recompute.
+hipError_t launch_forward_save(const Problem& p, const BwdLayout& L, char* ws, hipStream_t s);
 
 // Full layer (projections around the attention): the forward's regions, then
 // the fused QKV projection (reused for the attention output and the merged

@@ -162,6 +162,34 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
                      int batch, int conv_k, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training pair: the forward pass that keeps its landmark-side state, and
+ * the backward pass that starts from it instead of recomputing it (the same
+ * method and results as nystrom_attn_fwd and nystrom_attn_bwd, bit for bit).
+ *   nystrom_attn_fwd_save  arguments as for nystrom_attn_fwd; O is written to
+ *                          `out`, and Q~, K~, A, Z, BV, W, the row statistics
+ *                          of B~ and each Lemma-1 step (Z_k, X_k, T1_k, T2_k)
+ *                          to `saved`
+ *   nystrom_attn_bwd_saved arguments as for nystrom_attn_bwd, with `saved`
+ *                          in place of the workspace
+ *   saved        DEVICE buffer of at least nystrom_attn_bwd_workspace_bytes(),
+ *                owned by the caller, not NULL (NYS_EINVAL).  Between the two
+ *                calls it must stay untouched, and the two calls must get the
+ *                same Q, K, V, conv_w, shape, iters, conv_k and dtype; the
+ *                backward may be called more than once on one saved forward.
+ *                The buffer's contents are the library's; its layout is
+ *                not part of this interface.
+ * Supported shapes, return codes and stream behaviour as for
+ * nystrom_attn_bwd. */
+int nystrom_attn_fwd_save(const void* Q, const void* K, const void* V, const float* conv_w,
+                          int n, int d, int m, int heads, int iters, void* out,
+                          int batch, int conv_k, int dtype,
+                          void* saved, size_t saved_bytes, void* stream);
+int nystrom_attn_bwd_saved(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
+                           int n, int d, int m, int heads, int iters,
+                           void* dQ, void* dK, void* dV, float* dconv_w,
+                           int batch, int conv_k, int dtype,
+                           void* saved, size_t saved_bytes, void* stream);
+
 /* Full self-attention layer: the learned projections around the attention
  * ("Nyströmformer: ...", "Standard Self-Attention": Q = X W_Q, K = X W_K,
  * V = X W_V, with no bias; the attention-output projection the page mentions

@@ -142,6 +142,35 @@ def test_bwd_rejects_bad_arguments_before_launch(lib, kw, code):
     assert _lib.nystrom_attn_bwd(**args) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(saved=None), _lib.NYS_EINVAL),                  # the saved state is the caller's buffer
+    (dict(out=None), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=4), _lib.NYS_EINVAL),
+    (dict(m=80, n=640), _lib.NYS_EUNSUPPORTED),
+    (dict(saved_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_fwd_save_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, n=64, d=16, m=8, heads=1, iters=6, out=FAKE, batch=1, conv_k=0,
+                dtype=_lib.NYS_BF16, saved=FAKE, saved_bytes=1 << 30, stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_fwd_save(**args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(saved=None), _lib.NYS_EINVAL),                  # no allocation: the forward's state must be given
+    (dict(dO=None), _lib.NYS_EINVAL),
+    (dict(dtype=3), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=35), _lib.NYS_EUNSUPPORTED),
+    (dict(saved_bytes=16), _lib.NYS_EWORKSPACE),
+])
+def test_bwd_saved_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, dO=FAKE, n=64, d=16, m=8, heads=1, iters=6, dQ=FAKE, dK=FAKE,
+                dV=FAKE, dconv_w=None, batch=1, conv_k=0, dtype=_lib.NYS_F32, saved=FAKE, saved_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_bwd_saved(**args) == code
+
+
 def test_bwd_workspace_covers_the_forward_layout(lib):
     for shape in ((1, 1, 64, 16, 8), (2, 12, 8192, 64, 64), (1, 3, 777, 32, 48)):
         fwd = _lib.nystrom_attn_workspace_bytes(*shape)

@@ -150,3 +150,43 @@ def test_backward_two_host_threads():
         for got in outs:
             for x, y in zip(got, ref):
                 assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("case", [(2, 2, 1000, 64, 64, 6, 33, "bf16"), (1, 2, 256, 32, 32, 6, 33, "f32")],
+                         ids=["bf16_d64", "f32_d32"])
+def test_saved_forward_pair_matches_plain_calls(case):
+    """nystrom_attn_fwd_save + nystrom_attn_bwd_saved give the plain forward's
+    output and the plain backward's gradients bit for bit (the same kernels
+    on the same data; the backward only skips recomputing the forward's
+    landmark side), also when the backward runs twice on one saved forward."""
+    from ._gpu_util import run_forward
+
+    B, H, n, d, m, iters, k, dt = case
+    wl = WORKLOADS["tiny"].with_(name="saved", batch=B, heads=H, n=n, d=d, m=m, iters=iters, conv_k=k, dtype=dt,
+                                 seed=41)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 43)
+    ref_grads = run_backward(inp, dO, m, iters, dt)
+    ref_out = run_forward(inp, m, iters, dt)[0]
+
+    Q, K, V, G = (to_dev(x, dt) for x in (inp["Q"], inp["K"], inp["V"], dO))
+    w = torch.from_numpy(np.ascontiguousarray(inp["conv_w"], np.float32)).cuda()
+    O = torch.empty_like(Q)
+    dQ, dK, dV, dW = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V), torch.empty_like(w)
+    nbytes = _lib.nystrom_attn_bwd_workspace_bytes(B, H, n, d, m, iters, k)
+    saved = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+    rc = _lib.nystrom_attn_fwd_save(Q, K, V, w, n, d, m, H, iters, O, B, k, dtype_code(dt), saved, nbytes, st)
+    assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(O), ref_out)
+    for _ in range(2):
+        for t in (dQ, dK, dV, dW):
+            t.fill_(float("nan"))
+        rc = _lib.nystrom_attn_bwd_saved(Q, K, V, w, G, n, d, m, H, iters, dQ, dK, dV, dW, B, k, dtype_code(dt),
+                                         saved, nbytes, st)
+        assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+        torch.cuda.synchronize()
+        got = (to_host(dQ), to_host(dK), to_host(dV), dW.cpu().numpy())
+        for x, y in zip(got, ref_grads):
+            assert np.array_equal(x, y)
