@@ -2,6 +2,8 @@
 
 ``attention`` and ``dconv`` validate torch tensors, allocate the output (and,
 if asked, a workspace), and call the library on the current torch stream.
+``attention_train`` is the same forward with autograd: its backward is the
+library's exact backward pass, started from the state the forward kept.
 They raise ``NystromError`` on any non-zero return code.
 """
 from __future__ import annotations
@@ -78,6 +80,62 @@ def attention(Q, K, V, m, iters=6, conv_w=None, out=None, workspace=None, stream
     if rc != _lib.NYS_OK:
         raise NystromError(rc, "nystrom_attn_fwd_masked")
     return out
+
+
+def _conv_k(conv_w, heads, d) -> int:
+    if conv_w is None:
+        return 0
+    if conv_w.dtype != torch.float32 or conv_w.dim() != 3 or tuple(conv_w.shape[:2]) != (heads, d):
+        raise ValueError("conv_w must be float32 [heads, d, k]")
+    if not conv_w.is_contiguous() or conv_w.device.type != "cuda":
+        raise ValueError("conv_w must be a contiguous GPU tensor")
+    return conv_w.shape[2]
+
+
+class _NystromAttention(torch.autograd.Function):
+    """Forward: nystrom_attn_fwd_save, which keeps the landmark-side state in
+    a buffer held by the autograd context; backward: nystrom_attn_bwd_saved
+    from that state (gradients of Q, K, V and the filters)."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, conv_w, m, iters):
+        _check_io(Q, K, V)
+        batch, heads, n, d = Q.shape
+        conv_k = _conv_k(conv_w, heads, d)
+        nbytes = _lib.nystrom_attn_bwd_workspace_bytes(batch, heads, n, d, m, iters, conv_k)
+        if nbytes == 0:
+            raise NystromError(_lib.NYS_EUNSUPPORTED, "nystrom_attn_bwd_workspace_bytes")
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+        out = torch.empty_like(Q)
+        rc = _lib.nystrom_attn_fwd_save(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k,
+                                        _DTYPES[Q.dtype], saved, nbytes, torch.cuda.current_stream())
+        if rc != _lib.NYS_OK:
+            raise NystromError(rc, "nystrom_attn_fwd_save")
+        ctx.save_for_backward(Q, K, V, conv_w)
+        ctx.state, ctx.nbytes, ctx.m, ctx.iters, ctx.conv_k = saved, nbytes, m, iters, conv_k
+        return out
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, conv_w = ctx.saved_tensors
+        batch, heads, n, d = Q.shape
+        dO = dO.to(Q.dtype).contiguous()
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        dW = torch.empty_like(conv_w) if conv_w is not None and ctx.needs_input_grad[3] else None
+        rc = _lib.nystrom_attn_bwd_saved(Q, K, V, conv_w, dO, n, d, ctx.m, heads, ctx.iters, dQ, dK, dV, dW, batch,
+                                         ctx.conv_k, _DTYPES[Q.dtype], ctx.state, ctx.nbytes,
+                                         torch.cuda.current_stream())
+        if rc != _lib.NYS_OK:
+            raise NystromError(rc, "nystrom_attn_bwd_saved")
+        return dQ, dK, dV, dW, None, None
+
+
+def attention_train(Q, K, V, m, iters=6, conv_w=None):
+    """Nyström attention forward with autograd.  Q, K, V: [batch, heads, n, d]
+    (fp32 or bf16, m <= 64); conv_w: fp32 [heads, d, k] (k <= 33) or None.
+    Backpropagating through the result runs the library's exact backward
+    pass from the state this forward kept (no recompute)."""
+    return _NystromAttention.apply(Q, K, V, conv_w, m, iters)
 
 
 def dconv(V, conv_w, out=None, stream=None):

@@ -190,3 +190,26 @@ def test_saved_forward_pair_matches_plain_calls(case):
         got = (to_host(dQ), to_host(dK), to_host(dV), dW.cpu().numpy())
         for x, y in zip(got, ref_grads):
             assert np.array_equal(x, y)
+
+
+def test_attention_train_autograd_matches_plain_backward():
+    """api.attention_train under torch autograd: the output equals the plain
+    forward and the gradients equal nystrom_attn_bwd, bit for bit."""
+    from efficient_transformer_attention_mean_amd import api
+    from ._gpu_util import run_forward
+
+    wl = WORKLOADS["tiny"].with_(name="autograd", batch=2, heads=2, n=1000, d=64, m=64, iters=6, conv_k=33,
+                                 dtype="bf16", seed=51)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 53)
+    ref_grads = run_backward(inp, dO, wl.m, wl.iters, wl.dtype)
+    ref_out = run_forward(inp, wl.m, wl.iters, wl.dtype)[0]
+    Q, K, V = (to_dev(inp[k], wl.dtype).requires_grad_() for k in ("Q", "K", "V"))
+    w = torch.from_numpy(np.ascontiguousarray(inp["conv_w"], np.float32)).cuda().requires_grad_()
+    out = api.attention_train(Q, K, V, wl.m, wl.iters, conv_w=w)
+    out.backward(to_dev(dO, wl.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out.detach()), ref_out)
+    got = (to_host(Q.grad), to_host(K.grad), to_host(V.grad), w.grad.cpu().numpy())
+    for x, y in zip(got, ref_grads):
+        assert np.array_equal(x, y)
