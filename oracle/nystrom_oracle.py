@@ -50,6 +50,9 @@ the design notes):
   right-padded sequences is given by one length L_b per batch entry, and
   entry b is the method on its first L_b rows alone; its pad rows are never
   read and their output rows are zero (``nystrom_attention``'s ``lengths``).
+  A sequence shorter than m is zero-padded to m rows like any other (l = 1):
+  its first L_b landmarks are its rows, the rest are zero vectors, and B~
+  spans its L_b keys.  An empty sequence (L_b = 0) has no output rows.
 
 Parity pins: every function here is pinned in ``tests/test_oracle_pins.py``
 against closed forms, brute force on tiny inputs, or library routines.
@@ -82,15 +85,18 @@ def segment_means(X, m):
     Eq. 16, with the divisor read as the segment length; [HF] "How do we
     select landmarks?").
 
-    X: (n, d), 1 <= m <= n.  X is first padded at its end with zero rows to
-    n' = m * ceil(n/m) (the section assumes n divisible by m and says padding
-    ensures it); with l = n'/m, row j of the result is the mean of padded
-    rows j*l .. j*l+l-1.  For n divisible by m there is no pad.
+    X: (n, d), n >= 1, m >= 1.  X is first padded at its end with zero rows
+    to n' = m * ceil(n/m) (the section assumes n divisible by m and says
+    padding ensures it); with l = n'/m, row j of the result is the mean of
+    padded rows j*l .. j*l+l-1.  For n divisible by m there is no pad; for
+    n < m, l = 1 and rows n .. m-1 of the result are zero (landmarks of pad
+    only, which only a key-padding mask produces: the unmasked entry point
+    asks for m <= n).
     """
     X = _f64(X)
     n, d = X.shape
-    if m < 1 or m > n:
-        raise ValueError("need 1 <= m <= n")
+    if m < 1 or n < 1:
+        raise ValueError("need m >= 1 and n >= 1")
     seg = -(-n // m)
     Xp = np.zeros((m * seg, d))
     Xp[:n] = X
@@ -215,18 +221,28 @@ def nystrom_attention(Q, K, V, m, iters, conv_w=None, with_intermediates=False, 
     out ([HF] "How is Nyströmformer implemented?"); the reading taken is
     that padding tokens are not part of the sequence: entry b is the method
     on its first L_b rows alone (with the zero padding to a multiple of m of
-    ``segment_means`` when m does not divide L_b), its rows L_b .. n-1 are
-    never read, and its output rows there are zero.  Each L_b is clamped to
-    [m, n].
+    ``segment_means`` when m does not divide L_b, to m rows when L_b < m),
+    its rows L_b .. n-1 are never read, and its output rows there are zero.
+    Each L_b is clamped to [0, n]; an entry with L_b = 0 has an all-zero
+    output and NaN intermediates (it has no keys, so B~ is undefined).
     Returns O of shape (batch, heads, n, d) in fp64 and, if asked, a dict of
     stacked intermediates (each with leading (batch, heads) axes).
     """
     Q, K, V = map(_f64, (Q, K, V))
     Bt, H, n, d = Q.shape
+    if lengths is None and m > n:
+        raise ValueError("need m <= n without a key-padding mask")
     O = np.zeros((Bt, H, n, d))
     inter_all = {}
+    shapes = dict(Qt=(m, d), Kt=(m, d), A=(m, m), Z=(m, m), BV=(m, d), W=(m, d))
     for b in range(Bt):
-        L = n if lengths is None else int(min(max(int(lengths[b]), m), n))
+        L = n if lengths is None else int(min(max(int(lengths[b]), 0), n))
+        if L == 0:
+            if with_intermediates:
+                for key, shp in shapes.items():
+                    inter_all.setdefault(key, np.empty((Bt, H) + shp))[b] = np.nan
+                inter_all.setdefault("O_att", np.zeros((Bt, H, n, d)))
+            continue
         for h in range(H):
             w = None if conv_w is None else _f64(conv_w)[h]
             O[b, h, :L], inter = nystrom_head(Q[b, h, :L], K[b, h, :L], V[b, h, :L], m, iters, w)

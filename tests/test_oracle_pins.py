@@ -60,10 +60,13 @@ def test_segment_means_special_cases():
     # Constant segments give their own value back (a divisor m != l would not).
     C = np.repeat(rng.standard_normal((2, 4)), 8, axis=0)
     np.testing.assert_allclose(segment_means(C, 2), C[::8], atol=1e-15)
-    with pytest.raises(ValueError):
-        segment_means(X, 17)  # more landmarks than rows
+    # More landmarks than rows (only a key-padding mask asks for it): l = 1,
+    # the rows themselves, then landmarks of pad only.
+    np.testing.assert_array_equal(segment_means(X, 17), np.vstack([X, np.zeros((1, 4))]))
     with pytest.raises(ValueError):
         segment_means(X, 0)
+    with pytest.raises(ValueError):
+        segment_means(X[:0], 4)
 
 
 def test_segment_means_padded_by_hand():
@@ -439,12 +442,75 @@ def test_lengths_pad_rows_are_never_read():
     np.testing.assert_array_equal(O1[1], O3[1])  # full length: same as no mask
 
 
-def test_lengths_are_clamped_to_m_and_n():
+def test_lengths_are_clamped_to_zero_and_n():
     rng = np.random.default_rng(30)
-    Bt, H, n, d, m = 2, 1, 20, 2, 5
+    Bt, H, n, d, m = 3, 1, 20, 2, 5
     Q, K, V = (rng.standard_normal((Bt, H, n, d)) for _ in range(3))
-    np.testing.assert_array_equal(nystrom_attention(Q, K, V, m, 6, lengths=[2, 99]),
-                                  nystrom_attention(Q, K, V, m, 6, lengths=[5, 20]))
+    np.testing.assert_array_equal(nystrom_attention(Q, K, V, m, 6, lengths=[-3, 99, 2]),
+                                  nystrom_attention(Q, K, V, m, 6, lengths=[0, 20, 2]))
+
+
+def test_lengths_below_m_pad_the_landmarks_by_hand():
+    # L_b = 3 < m = 5: padded to m rows (l = 1), so the landmarks are the three
+    # rows and two zero vectors; B~ spans the three real keys.  Written out
+    # here with explicit loops (softmaxes by hand) on one head.
+    rng = np.random.default_rng(31)
+    n, d, m, L = 12, 2, 5, 3
+    Q, K, V = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    O, inter = nystrom_attention(Q, K, V, m, 30, with_intermediates=True, lengths=[L])
+    q, k, v = Q[0, 0], K[0, 0], V[0, 0]
+    lm_q = np.zeros((m, d))
+    lm_k = np.zeros((m, d))
+    lm_q[:L], lm_k[:L] = q[:L], k[:L]
+    np.testing.assert_array_equal(inter["Qt"][0, 0], lm_q)
+    np.testing.assert_array_equal(inter["Kt"][0, 0], lm_k)
+    s = 1.0 / math.sqrt(d)
+
+    def softmax_row(x):
+        e = [math.exp(t - max(x)) for t in x]
+        return [t / sum(e) for t in e]
+
+    F = np.array([softmax_row([s * float(q[i] @ lm_k[j]) for j in range(m)]) for i in range(L)])
+    A = np.array([softmax_row([s * float(lm_q[i] @ lm_k[j]) for j in range(m)]) for i in range(m)])
+    B = np.array([softmax_row([s * float(lm_q[i] @ k[j]) for j in range(L)]) for i in range(m)])
+    np.testing.assert_allclose(inter["A"][0, 0], A, rtol=0, atol=1e-15)
+    # 30 steps converge, so the pseudoinverse is the library's.
+    expect = F @ np.linalg.pinv(A) @ (B @ v[:L])
+    np.testing.assert_allclose(O[0, 0, :L], expect, rtol=0, atol=1e-9)
+    assert not O[0, 0, L:].any()
+
+
+def test_lengths_below_m_zero_queries_and_nan_pad():
+    # Zero queries: every softmax is uniform, the pseudoinverse of the uniform
+    # m x m matrix is itself, and each output row below L_b is the mean of the
+    # L_b real value rows (counting the zero landmarks' pad rows as keys would
+    # not give this).  The pad rows hold NaN and must never be read.
+    rng = np.random.default_rng(32)
+    Bt, H, n, d, m = 4, 2, 24, 3, 8
+    K, V = rng.standard_normal((Bt, H, n, d)), rng.standard_normal((Bt, H, n, d))
+    lengths = [5, 1, 0, 24]
+    Q = np.zeros((Bt, H, n, d))
+    for X in (Q, K, V):
+        for b, L in enumerate(lengths):
+            X[b, :, L:] = np.nan
+    O = nystrom_attention(Q, K, V, m, 6, lengths=lengths)
+    assert np.all(np.isfinite(O))
+    for b, L in enumerate(lengths):
+        for h in range(H):
+            if L:
+                np.testing.assert_allclose(O[b, h, :L], np.broadcast_to(V[b, h, :L].mean(0), (L, d)),
+                                           rtol=0, atol=1e-13)
+            assert not O[b, h, L:].any()
+
+
+def test_empty_sequence_has_zero_output_and_undefined_intermediates():
+    rng = np.random.default_rng(33)
+    Q, K, V = (rng.standard_normal((2, 1, 16, 2)) for _ in range(3))
+    w = rng.standard_normal((1, 2, 3))
+    O, inter = nystrom_attention(Q, K, V, 4, 6, w, with_intermediates=True, lengths=[0, 16])
+    assert not O[0].any()
+    assert np.all(np.isnan(inter["Z"][0])) and np.all(np.isfinite(inter["Z"][1]))
+    np.testing.assert_array_equal(O[1], nystrom_attention(Q[1:], K[1:], V[1:], 4, 6, w)[0])
 
 
 # ---------------------------------------------------------------- approximation error
