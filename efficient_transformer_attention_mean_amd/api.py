@@ -9,6 +9,7 @@ They raise ``NystromError`` on any non-zero return code.
 from __future__ import annotations
 
 import torch
+from torch.autograd.function import once_differentiable
 
 from . import _lib
 
@@ -116,7 +117,11 @@ class _NystromAttention(torch.autograd.Function):
         return out
 
     @staticmethod
+    @once_differentiable
     def backward(ctx, dO):
+        # The gradients come from the library, outside autograd: a second
+        # derivative through them (create_graph=True) raises instead of
+        # silently missing terms.
         Q, K, V, conv_w = ctx.saved_tensors
         batch, heads, n, d = Q.shape
         dO = dO.to(Q.dtype).contiguous()

@@ -1,5 +1,6 @@
 // C ABI of the Nyström attention library: argument validation, workspace
-// contract and the stream-ordered launch of the kernels in nys_kernels.hip.
+// contract and the stream-ordered launch of the kernels (nys_landmarks.hip,
+// nys_apply.hip, nys_backward.hip, nys_layer.hip, nys_error.hip).
 #include <hip/hip_runtime.h>
 
 #include <new>

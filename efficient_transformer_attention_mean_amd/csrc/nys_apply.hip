@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // Bytes of head bh's rows that hold tokens (the row pitch of a head is n
   // rows; with per-sequence lengths only the first ones are real): Q and V
   // rows past them read as zero through the range check.
-  auto token_bytes = [&](int bh) { return (lens ? min(max(lens[bh / heads], m), n) : n) * (D * ES); };
+  auto token_bytes = [&](int bh) { return seq_rows(lens, bh / heads, n) * (D * ES); };
 
   // Run of tiles of this block.
   const long long G = gridDim.x, L = blockIdx.x;
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 
     // A tile wholly inside a sequence's padding only writes zeros (its loads
     // past the tokens read zeros and move no data).
-    const int nb = seq_rows(lens, bh / heads, n, m);
+    const int nb = seq_rows(lens, bh / heads, n);
     const bool live = t0 < nb;
     if (live) skip(h);
     f32x4_t o[ND];

@@ -65,6 +65,11 @@ class KernelTimer {
   hipEvent_t start_ = nullptr;
 };
 
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) once per
+// (kernel, device); later calls return the first call's result.  Safe to call
+// from several host threads.
+hipError_t ensure_dynamic_smem(const void* fn, int bytes);
+
 // Stages of the forward pass, in stream order.
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  // Qt, Kt, Kt planes
 // Split-n partials of B V; with bf16 I/O and m <= 64 also A and Z (the

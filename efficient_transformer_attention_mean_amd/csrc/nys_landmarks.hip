@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   constexpr int RS = 256 / SLOTS;  // rows covered per pass
   __shared__ float part[4][D];
   const int j = blockIdx.x, bh = blockIdx.y;
-  const int nb = seq_rows(lens, bh / heads, n, m);
-  const int seg = (nb + m - 1) / m;
+  const int nb = seq_rows(lens, bh / heads, n);
+  const int seg = max(1, (nb + m - 1) / m);  // l = 1 for a sequence shorter than m (empty included)
   const int rows = max(0, min(seg, nb - j * seg));  // real rows of this segment
   const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
   float* out = (blockIdx.z == 0 ? Qt : Kt) + ((size_t)bh * m + j) * D;
@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
   blk -= a.nconv;
   const int bh = blk / a.nchunks;
   bv_chunk<IO, D, NTW>(sm.b, blk % a.nchunks, bh, static_cast<const T*>(a.K), static_cast<const T*>(a.V), a.Qt,
-                       a.pacc, a.pmax, a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n, a.m), a.m, a.chunk,
+                       a.pacc, a.pmax, a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk,
                        a.nchunks, a.sl2e);
 }
 
@@ -1160,7 +1160,12 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
 #pragma unroll
           for (int k = 0; k < 4; ++k) St[k] += reds[pp][jl][q][k] * e;
         }
-        const float inv = 1.f / Lt;
+        // A sequence with no keys (length 0) has every chunk empty: BV = 0.
+        const float inv = Mt == -INFINITY ? 0.f : 1.f / Lt;
+        if (Mt == -INFINITY) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) St[k] = 0.f;
+        }
         float4 v = make_float4(St[0] * inv, St[1] * inv, St[2] * inv, St[3] * inv);
         sbv[j][4 * q] = v.x;
         sbv[j][4 * q + 1] = v.y;

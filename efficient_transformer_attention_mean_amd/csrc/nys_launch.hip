@@ -1,7 +1,26 @@
 // Workspace layout and the stream-ordered sequence of forward stages.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "nys_internal.hpp"
 
 namespace nys {
+
+hipError_t ensure_dynamic_smem(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, hipError_t> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(fn, dev);
+  auto it = done.find(key);
+  if (it != done.end()) return it->second;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done.emplace(key, e);
+  return e;
+}
 
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 

@@ -22,8 +22,13 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     keeps no data between calls, never frees caller memory and creates no
- *     streams: every kernel runs on `stream`, in order.
+ *     never frees caller memory and keeps no tensor data between calls.  The
+ *     forward entry points create no streams or events: every kernel runs on
+ *     `stream`, in order.  Three per-device objects are created on first use
+ *     and kept for the life of the process: by nystrom_attn_bwd (bf16,
+ *     d = 32 or 64) a second stream and four events, which it forks from and
+ *     joins back to `stream`; by nystrom_layer_fwd a rocBLAS handle; and,
+ *     while nystrom_timing_enable is on, timing events.
  *   - Q, K, V, out: [batch][heads][n][d], contiguous, element type `dtype`
  *     (NYS_F32 = IEEE fp32, NYS_BF16 = bfloat16).  conv_w: fp32
  *     [heads][d][conv_k], contiguous, or NULL for no skip.
@@ -114,16 +119,21 @@ int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* c
  * masking out ("Approximating self-attention in linear time and memory via
  * the Nyström method", "How is Nyströmformer implemented?"); the reading
  * taken is that padding tokens are not part of a sequence: batch entry b is
- * what nystrom_attn_fwd computes for its first L_b rows alone (padded to a
- * multiple of m as described at the top when m does not divide L_b).
+ * what nystrom_attn_fwd computes for its first L_b rows alone, padded with
+ * zero rows to a multiple of m as described at the top when m does not
+ * divide L_b.  A sequence shorter than m is padded to m rows the same way
+ * (l = 1): its landmarks are its L_b rows followed by zero vectors, and B
+ * spans its L_b keys.
  *   lengths     DEVICE pointer to int32 [batch], L_b = tokens of entry b;
- *               read on the device only, each clamped to [m, n] there (the
+ *               read on the device only, each clamped to [0, n] there (the
  *               host cannot check them without a synchronisation).  NULL =
  *               every entry has n tokens, the same as nystrom_attn_fwd.
- * Rows L_b .. n-1 of Q, K and V are never read (they may hold anything);
- * rows L_b .. n-1 of out are written as zero; the workspace intermediates of
- * entry b are those of its own sequence.  All other arguments, the workspace
- * size, the return codes and the stream behaviour are those of
+ * Rows L_b .. n-1 of Q, K and V are never read (they may hold anything,
+ * NaN included); rows L_b .. n-1 of out are written as zero; the workspace
+ * intermediates of entry b are those of its own sequence.  An entry with
+ * L_b = 0 has an all-zero output; its B V and W are zero and its other
+ * intermediates are those of zero landmarks.  All other arguments, the
+ * workspace size, the return codes and the stream behaviour are those of
  * nystrom_attn_fwd. */
 int nystrom_attn_fwd_masked(const void* Q, const void* K, const void* V, const float* conv_w,
                             int n, int d, int m, int heads, int iters, void* out,

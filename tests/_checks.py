@@ -78,7 +78,10 @@ def parity_metrics(got, ref, tile_rows: int = TILE_ROWS, rtol: float = 0.0, atol
     out["tile_at"] = (int(worst[0]), int(worst[1]) * tile_rows)
     if rtol > 0 or atol > 0:
         g3, r3 = _as3(got), _as3(ref)
-        rms = np.sqrt(np.mean(r3 * r3, axis=(1, 2)))[:, None, None]
+        # rms over the rows that hold values (the all-zero rows of a padded
+        # sequence would deflate it).
+        live = np.maximum(np.sum(np.any(r3 != 0, axis=2), axis=1) * r3.shape[2], 1)
+        rms = np.sqrt(np.sum(r3 * r3, axis=(1, 2)) / live)[:, None, None]
         bound = rtol * np.abs(r3) + atol * rms
         ratio = np.abs(g3 - r3) / np.maximum(bound, 1e-300)
         # Exact matches (zeros of masked rows included) never fail.
@@ -136,11 +139,13 @@ def check_parity(got, ref, bars: Bars, name: str = "", report=print) -> dict:
 # tile: the same bar per 64-row tile (rounding errors are relative per element,
 # so a tile's relative error is the tensor's up to sampling noise).
 # Elementwise: the bf16 output is rounded to nearest (<= 2^-9 |x|) after fp32
-# arithmetic whose single-bf16 attention products leave an absolute error of
-# order 2^-9 times the attention's magnitude, well under 1e-2 of the output's
-# rms; so |d| <= 2^-7 |ref| + 1e-2 rms(ref).  fp32: every product keeps about
-# 2^-17 or better, so |d| <= 1e-4 |ref| + 1e-4 rms(ref).
+# arithmetic whose single-bf16 attention products (F~ and W rounded to bf16)
+# leave an error of order 2^-9 times the magnitude of the terms summed over
+# the landmarks, which can exceed |O| where they cancel: measured up to
+# 1.5e-2 rms(O) on the small parity shapes, so |d| <= 2^-7 |ref| + 3e-2 rms.
+# fp32: every product keeps about 2^-17 or better (measured |d| up to about
+# 1e-4 (|ref| + rms)), so |d| <= 2e-4 |ref| + 2e-4 rms(ref).
 OUT_BARS = {
-    "f32": Bars(rel=1e-4, tile=1e-4, rtol=1e-4, atol=1e-4),
-    "bf16": Bars(rel=2e-2, tile=2e-2, rtol=2.0 ** -7, atol=1e-2),
+    "f32": Bars(rel=1e-4, tile=1e-4, rtol=2e-4, atol=2e-4),
+    "bf16": Bars(rel=2e-2, tile=2e-2, rtol=2.0 ** -7, atol=3e-2),
 }

@@ -222,3 +222,40 @@ def test_layer_and_error_workspaces_cover_the_forward(lib):
             assert err >= fwd + B * H * n * d * es
     assert _lib.nystrom_layer_workspace_bytes(1, 1, 64, 16, 8, 9) == 0
     assert _lib.nystrom_attn_error_workspace_bytes(1, 1, 64, 24, 8, 0) == 0
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: only where no GPU is visible")
+def test_failed_hip_call_maps_to_nys_ehip(lib):
+    # With no device visible, a call that passes validation fails at its first
+    # HIP call (the stream-ordered workspace allocation, or the launch) and
+    # reports NYS_EHIP; nothing reaches a device.
+    P = 0x10000
+    assert _lib.nystrom_attn_fwd(P, P, P, None, 128, 16, 8, 1, 6, P, 1, 0, _lib.NYS_F32) == _lib.NYS_EHIP
+    assert _lib.nystrom_attn_fwd(P, P, P, None, 128, 16, 8, 1, 6, P, 1, 0, _lib.NYS_BF16, P, 1 << 30) == _lib.NYS_EHIP
+    assert _lib.nystrom_attn_bwd(P, P, P, None, P, 128, 16, 8, 1, 6, P, P, P, None, 1, 0, _lib.NYS_F32) == _lib.NYS_EHIP
+    assert _lib.nystrom_layer_fwd(P, P, P, None, 128, 16, 8, 1, 6, P, 1, 0, _lib.NYS_F32) == _lib.NYS_EHIP
+    assert _lib.nystrom_attn_error(P, P, P, 128, 16, 8, 1, 6, P, 1, _lib.NYS_F32) == _lib.NYS_EHIP
+    assert _lib.nystrom_dconv_fwd(P, P, 128, 16, 1, 1, 3, _lib.NYS_F32, P) == _lib.NYS_EHIP
+    assert "HIP" in _lib.nystrom_strerror(_lib.NYS_EHIP)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device pointers: only where no GPU is visible")
+def test_host_code_under_address_and_undefined_behaviour_sanitizers():
+    # The library's host code (validation, workspace layout, error mapping,
+    # timing switches) built with -fsanitize=address,undefined on the host side
+    # and driven by tests/sanitize/host_checks.cpp; objects are cached under
+    # the package's _build folder and rebuilt when a source changes.
+    import subprocess
+    out = os.path.join(ROOT, "efficient_transformer_attention_mean_amd", "_build", "host_sanitize")
+    r = subprocess.run([os.path.join(ROOT, "tests", "sanitize", "build_and_run.sh"), out], capture_output=True,
+                       text=True, timeout=900)
+    assert r.returncode == 0, r.stdout[-4000:] + r.stderr[-4000:]
+    assert "host checks passed" in r.stdout
