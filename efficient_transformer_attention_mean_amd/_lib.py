@@ -28,6 +28,7 @@ EXPORTS = (
     "nystrom_attn_workspace_offset",
     "nystrom_attn_fwd",
     "nystrom_attn_fwd_masked",
+    "nystrom_attn_fwd_noalloc",
     "nystrom_attn_bwd_workspace_bytes",
     "nystrom_attn_bwd",
     "nystrom_attn_fwd_save",
@@ -64,6 +65,8 @@ def load():
     lib.nystrom_attn_fwd.restype = i
     lib.nystrom_attn_fwd_masked.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, vp, sz, vp]
     lib.nystrom_attn_fwd_masked.restype = i
+    lib.nystrom_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp]
+    lib.nystrom_attn_fwd_noalloc.restype = i
     lib.nystrom_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.nystrom_attn_bwd_workspace_bytes.restype = sz
     lib.nystrom_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz, vp]
@@ -136,6 +139,12 @@ def nystrom_attn_fwd_masked(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, 
     return int(load().nystrom_attn_fwd_masked(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), n, d, m, heads, iters,
                                               _ptr(out), batch, conv_k, dtype, _ptr(lengths), _ptr(workspace),
                                               workspace_bytes, _stream(stream)))
+
+
+def nystrom_attn_fwd_noalloc(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype,
+                             stream=None) -> int:
+    return int(load().nystrom_attn_fwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), n, d, m, heads, iters,
+                                               _ptr(out), batch, conv_k, dtype, _stream(stream)))
 
 
 def nystrom_attn_bwd_workspace_bytes(batch, heads, n, d, m, iters, conv_k) -> int:

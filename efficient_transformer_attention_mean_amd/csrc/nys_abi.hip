@@ -3,6 +3,7 @@
 // nys_apply.hip, nys_backward.hip, nys_layer.hip, nys_error.hip).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/nystrom.h"
@@ -102,7 +103,59 @@ int forward(const void* Q, const void* K, const void* V, const float* conv_w, in
 
 }  // namespace
 
+namespace {
+
+// Scratch of nystrom_attn_fwd_noalloc: the forward's workspace regions, one
+// copy per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: every
+// host use goes through the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[NYS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's `scratch`, looked up once per device (with
+// that device current), or nullptr if the lookup failed.
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  static hipError_t status[kMaxDevices] = {};
+  static bool looked[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!looked[dev]) {
+    void* p = nullptr;
+    status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = status[dev] == hipSuccess ? p : nullptr;
+    looked[dev] = true;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
 extern "C" {
+
+int nystrom_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
+                             int heads, int iters, void* out, int batch, int conv_k, int dtype, void* stream) {
+  try {
+    // Validation first: an invalid call returns its code before any HIP call.
+    if (!Q || !K || !V || !out) return NYS_EINVAL;
+    if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
+    if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
+    const int rc = check_shape(batch, heads, n, d, m, iters);
+    if (rc != NYS_OK) return rc;
+    nys::WsLayout L;
+    if (!nys::make_layout(batch, heads, n, d, m, &L)) return NYS_EUNSUPPORTED;
+    if (L.total > NYS_NOALLOC_SCRATCH_BYTES) return NYS_EWORKSPACE;
+    void* ws = scratch_address();
+    if (!ws) return NYS_EHIP;
+    return forward(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype, nullptr, ws,
+                   NYS_NOALLOC_SCRATCH_BYTES, stream);
+  } catch (...) {
+    return NYS_EHIP;
+  }
+}
 
 int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,
                      int heads, int iters, void* out, int batch, int conv_k, int dtype, void* workspace,

@@ -114,6 +114,29 @@ int nystrom_attn_fwd(const void* Q, const void* K, const void* V, const float* c
                      int batch, int conv_k, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the built-in scratch of nystrom_attn_fwd_noalloc (per GPU). */
+#define NYS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* nystrom_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, bit for bit, with
+ * the workspace taken from a scratch array of NYS_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  The call
+ * never allocates or frees device memory.
+ *   Arguments as for nystrom_attn_fwd, without the workspace.
+ * Returns NYS_EWORKSPACE when the shape's workspace
+ * (nystrom_attn_workspace_bytes) exceeds NYS_NOALLOC_SCRATCH_BYTES (every
+ * workload up to batch 1 x 16 heads, n = 32768, d = 128, m = 256 fits);
+ * NYS_EHIP if the scratch's device address cannot be looked up; otherwise as
+ * nystrom_attn_fwd.  All calls on one GPU share that GPU's scratch: calls
+ * that overlap on one GPU (other streams, other host threads) race and must
+ * be serialised by the caller.  The scratch keeps the last call's
+ * intermediates (laid out as nystrom_attn_workspace_offset describes) until
+ * the next call overwrites them. */
+int nystrom_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const float* conv_w,
+                             int n, int d, int m, int heads, int iters, void* out,
+                             int batch, int conv_k, int dtype, void* stream);
+
 /* Nyström self-attention forward over a batch of right-padded sequences, the
  * key-padding mask given as one length per batch entry.  The pages leave
  * masking out ("Approximating self-attention in linear time and memory via

@@ -71,7 +71,12 @@ int main() {
          NYS_EINVAL);
   EXPECT(nystrom_dconv_fwd(P, nullptr, 128, 16, 1, 1, 3, NYS_F32, P, nullptr) == NYS_EINVAL);
   EXPECT(nystrom_dconv_fwd(P, W, 128, 16, 1, 1, 2, NYS_F32, P, nullptr) == NYS_EINVAL);
+  EXPECT(nystrom_attn_fwd_noalloc(P, P, P, nullptr, 32768, 128, 256, 12, 8, P, 8, 0, NYS_BF16, nullptr) ==
+         NYS_EWORKSPACE);  // beyond NYS_NOALLOC_SCRATCH_BYTES
+  EXPECT(nystrom_attn_fwd_noalloc(P, nullptr, P, nullptr, 128, 16, 8, 1, 6, P, 1, 0, NYS_F32, nullptr) ==
+         NYS_EINVAL);
   // Valid calls: with no device the first HIP call fails -> NYS_EHIP.
+  EXPECT(nystrom_attn_fwd_noalloc(P, P, P, W, 128, 16, 8, 1, 6, P, 1, 3, NYS_F32, nullptr) == NYS_EHIP);
   EXPECT(nystrom_attn_fwd(P, P, P, W, 128, 16, 8, 1, 6, P, 1, 3, NYS_F32, nullptr, 0, nullptr) == NYS_EHIP);
   EXPECT(nystrom_attn_fwd(P, P, P, nullptr, 128, 16, 8, 1, 6, P, 1, 0, NYS_BF16, P, size_t(1) << 30, nullptr) ==
          NYS_EHIP);
