@@ -13,6 +13,7 @@ struct WsLayout {
   size_t z2, x, t, u;              // fp32 pseudoinverse scratch for m > 64
   size_t pacc, pmax, psum;         // fp32 split-n partials of softmax(Qt K^T) V
   size_t kt_hi, kt_lo;             // bf16 planes of Kt * log2(e)/sqrt(d), [bh][mpa][d]
+  size_t qt_hi, qt_lo;             // bf16 planes of Qt, [bh][mpa][d] (rows m..mpa-1 zero)
   size_t wt_hi, wt_lo;             // bf16 planes of W^T, [bh][d][mpa], landmark order permuted
   size_t cwop;                     // matrix-core operands of the skip filters, [heads][d][4][9] x 16 B
   size_t total;
@@ -28,7 +29,7 @@ struct Ws {
   float *Qt, *Kt, *A, *Z, *BV, *W;
   float *Z2, *X, *T, *U;
   float *pacc, *pmax, *psum;
-  uint16_t *kt_hi, *kt_lo, *wt_hi, *wt_lo;
+  uint16_t *kt_hi, *kt_lo, *qt_hi, *qt_lo, *wt_hi, *wt_lo;
   uint4* cwop;
   int nchunks, chunk, mpa;
 };

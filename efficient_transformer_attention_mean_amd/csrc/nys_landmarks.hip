@@ -28,14 +28,16 @@ namespace nys {
 // m*l: a segment reads only its rows below n and still divides by l.  With
 // per-sequence lengths, n is that batch entry's length (the row pitch of a
 // head stays the buffer's n).
-// Key landmarks are also written, pre-multiplied by log2(e)/sqrt(d), as bf16
-// hi/lo planes [bh][mpa][D] (rows m..mpa-1 zero), the operand layout of the
-// output stage, whose scores then come out in base-2 units.
+// Both landmark sets are also written as bf16 hi/lo planes [bh][mpa][D] (rows
+// m..mpa-1 zero), the operand layout of the pseudoinverse's scores and of the
+// output stage: Qt as it is, Kt pre-multiplied by log2(e)/sqrt(d), so that
+// scores come out in base-2 units.
 template <typename IO, int D>
 __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __restrict__ Q,
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
                                                       uint16_t* __restrict__ kt_hi, uint16_t* __restrict__ kt_lo,
+                                                      uint16_t* __restrict__ qt_hi, uint16_t* __restrict__ qt_lo,
                                                       const int* __restrict__ lens, int heads, int n, int m,
                                                       int mpa, float sl2e) {
   using T = typename IO::T;
@@ -92,17 +94,17 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
     const float s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
     const float mean = s / (float)seg;
     out[threadIdx.x] = mean;
-    if (blockIdx.z == 1) {
-      uint16_t hi, lo;
-      split_hi_lo(mean * sl2e, hi, lo);
-      const size_t o = ((size_t)bh * mpa + j) * D + threadIdx.x;
-      kt_hi[o] = hi;
-      kt_lo[o] = lo;
-      if (j == m - 1) {
-        for (int r = m; r < mpa; ++r) {
-          kt_hi[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
-          kt_lo[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
-        }
+    uint16_t* ph = blockIdx.z == 1 ? kt_hi : qt_hi;
+    uint16_t* pl = blockIdx.z == 1 ? kt_lo : qt_lo;
+    uint16_t hi, lo;
+    split_hi_lo(blockIdx.z == 1 ? mean * sl2e : mean, hi, lo);
+    const size_t o = ((size_t)bh * mpa + j) * D + threadIdx.x;
+    ph[o] = hi;
+    pl[o] = lo;
+    if (j == m - 1) {
+      for (int r = m; r < mpa; ++r) {
+        ph[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
+        pl[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
       }
     }
   }
@@ -280,164 +282,190 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 }
 
 // ---------------------------------------------------------------------------
-// Pseudoinverse for m <= 64 with bf16x3 products (bf16 I/O).  One block of
-// MP/16 waves per head; wave j owns column block j (16 columns, all MP rows)
-// of every iterate.  In C = P R the right operand's column block comes from
-// the wave's own registers: a result in the matrix-core C layout (lane (c, g)
-// holds rows 4g..4g+3 of column c of each 16-row tile) is already a B operand
-// once the contraction index of every 32-chunk is taken in the order
-//   slot 8g + q  <->  k = 4g + q (q < 4),  16 + 4g + (q - 4) (q >= 4).
-// Only the left operands X = A Z and Z, which every wave needs whole, go
-// through LDS, as bf16 hi/lo planes, row-major with each row's columns stored
-// in that slot order (so a left-operand fragment is one 16-byte read per
-// plane).  A stays in registers.  One iteration
-//   X = A Z;  T = 7I - X;  T = 15I - X T;  T = 13I - X T;  Z = Z T / 4
-// has two barriers: after X is stored, and after every wave has loaded the X
-// and Z fragments it needs (before Z is overwritten).
+// Pseudoinverse for m <= MP (MP = 32 or 64) with bf16x3 products (bf16 I/O),
+// one block of 8 waves per head.
+//
+// Lemma 1's step Z <- Z (13I - X(15I - X(7I - X))) / 4 with X = A Z is run
+// through the residual E = I - A Z.  Since 13 - 15x + 7x^2 - x^3 = 4 (1 + e +
+// e^2 + e^3/4) and 1 - x (13 - 15x + 7x^2 - x^3)/4 = (3e^3 + e^4)/4 for
+// x = 1 - e, the same iterates follow from
+//   E_0 = I - A Z_0,  Z_0 = A^T / (||A||_1 ||A||_inf),
+//   Z_{t+1} = Z_t P_t,  P_t = I + E_t + E_t^2 + E_t^3 / 4,
+//   E_{t+1} = (3 E_t^3 + E_t^4) / 4 = E_t^2 N_t,  N_t = (3 E_t + E_t^2) / 4,
+// an identity of the printed iteration, not an approximation.  (I is the
+// identity on the m real landmarks: the zero padding up to MP stays zero.)
+//
+// E_t and every polynomial in it are symmetric, so the right operand of a
+// product reads its columns as rows, and Z_{t+1}^T = P_t Z_t^T reads Z by
+// rows too: every matrix sits in LDS as row-major bf16 hi/lo planes and every
+// operand fragment is one 16-byte read per plane.  A result tile (lane (c, g)
+// holds rows 4g..4g+3 of column c) is stored as the rows of the transposed
+// tile (8-byte writes), which for a symmetric result is the result itself and
+// for Z^T is Z.
+//
+// Two groups of 4 waves, each wave owning one quadrant of tiles (rows of
+// tiles TA.., columns TB..) of the products its group forms, so that two
+// waves share each SIMD and one's conversions and LDS traffic overlap the
+// other's matrix-core work.  Per step, two product levels and two barriers:
+//   level 1: E group: E^2 = E E, N = (3E + E^2)/4      Z group: Z_t^T = P_{t-1} Z_{t-1}^T
+//   level 2: E group: E^3 = E E^2, P_t = I + E + E^2 + E^3/4
+//            Z group: E_{t+1} = E^2 N (also handed to the E group in fp32)
 template <int MP>
-struct PinvSmem2 {
-  static constexpr int LD = MP + 8;  // plane row pitch (bf16): rows stay 16-byte aligned
+struct PinvSmemE {
+  static constexpr int LD = MP + 8;  // plane row pitch (bf16): 16-byte aligned rows, rows spread over banks
   static constexpr int PL = MP * LD;
   static constexpr int SP = MP + 4;  // fp32 score row pitch
-  __align__(16) uint16_t xp[2][PL];  // X planes [hi, lo]; the fp32 scores alias them before the iterations
-  __align__(16) uint16_t zp[2][PL];  // Z planes [hi, lo]
-  float colp[4][MP];                 // partial column sums of A
+  static constexpr int NW = MP / 32; // tiles per dimension of a quadrant
+  __align__(16) uint16_t e[2][PL];   // E_t planes [hi, lo]
+  __align__(16) uint16_t e2[2][PL];  // E_t^2; the fp32 scores and A alias it before the iterations
+  __align__(16) uint16_t nn[2][PL];  // N_t
+  __align__(16) uint16_t p[2][PL];   // P_t; A's planes before the iterations
+  __align__(16) uint16_t z[2][PL];   // Z_t
+  float ex[4][NW * NW * 4][64];      // E_{t+1} in fp32, quadrant by quadrant, handed from the Z group to the E group
+  float colp[256 / MP][MP];          // partial column sums of A
   float rows[MP];                    // row sums of A
-  __device__ float* S() { return reinterpret_cast<float*>(&xp[0][0]); }
-  static_assert(sizeof(float) * MP * SP <= sizeof(uint16_t) * 2 * PL, "scores do not fit the X planes");
+  __device__ float* S() { return reinterpret_cast<float*>(&e2[0][0]); }
+  static_assert(sizeof(float) * MP * SP <= sizeof(uint16_t) * 2 * PL, "scores do not fit the E^2 planes");
 };
 
-// B operand (chunks kc) of this wave's column block j from C-layout tiles v:
-// slot q of chunk kc is element q % 4 of tile 2kc + q / 4, as
-// scale * v + alpha * (row == column), split into bf16 hi/lo.
 template <int MP>
-__device__ __forceinline__ void to_bop(const f32x4_t (&v)[MP / 16], float scale, float alpha, int j,
-                                       B8 (&bh)[MP / 32], B8 (&bl)[MP / 32]) {
+struct PinvQuad {
+  static constexpr int NT = MP / 16;  // 16-row tiles per dimension
+  static constexpr int NW = NT / 2;   // tiles per dimension of a wave's quadrant
+  static constexpr int KC = MP / 32;  // 32-wide contraction chunks
+};
+
+// Row fragments of rows 16 t0 + 16 u + c (u < NW), every contraction chunk,
+// from a plane pair.
+template <int MP>
+__device__ __forceinline__ void rows_frag(const uint16_t (&pl)[2][PinvSmemE<MP>::PL], int t0,
+                                          B8 (&h)[PinvQuad<MP>::NW][PinvQuad<MP>::KC],
+                                          B8 (&l)[PinvQuad<MP>::NW][PinvQuad<MP>::KC]) {
+  constexpr int LD = PinvSmemE<MP>::LD, NW = PinvQuad<MP>::NW, KC = PinvQuad<MP>::KC;
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-  const int col = 16 * j + c;
 #pragma unroll
-  for (int kc = 0; kc < MP / 32; ++kc)
+  for (int u = 0; u < NW; ++u)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int t = 2 * kc + q / 4, i = q % 4;
-      const float x = scale * v[t][i] + (16 * t + 4 * g + i == col ? alpha : 0.f);
-      split_hi_lo(x, bh[kc].h[q], bl[kc].h[q]);
+    for (int kc = 0; kc < KC; ++kc) {
+      const int o = (16 * (t0 + u) + c) * LD + 32 * kc + 8 * g;
+      h[u][kc].q = *reinterpret_cast<const uint4*>(&pl[0][o]);
+      l[u][kc].q = *reinterpret_cast<const uint4*>(&pl[1][o]);
     }
 }
 
-// Stores a column block held as B-operand planes into row-major planes with
-// slot-ordered columns (2-byte writes).
+// acc[u][v] = (left rows) (right rows)^T for the wave's quadrant (bf16x3).
 template <int MP>
-__device__ __forceinline__ void store_bop(uint16_t* h, uint16_t* l, const B8 (&bh)[MP / 32],
-                                          const B8 (&bl)[MP / 32], int j) {
-  constexpr int LD = PinvSmem2<MP>::LD;
-  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
-  const int slot = 32 * (j >> 1) + 8 * (c >> 2) + 4 * (j & 1) + (c & 3);
+__device__ __forceinline__ void quad_mm(const B8 (&ah)[PinvQuad<MP>::NW][PinvQuad<MP>::KC],
+                                        const B8 (&al)[PinvQuad<MP>::NW][PinvQuad<MP>::KC],
+                                        const B8 (&bh)[PinvQuad<MP>::NW][PinvQuad<MP>::KC],
+                                        const B8 (&bl)[PinvQuad<MP>::NW][PinvQuad<MP>::KC],
+                                        f32x4_t (&acc)[PinvQuad<MP>::NW][PinvQuad<MP>::NW]) {
+  constexpr int NW = PinvQuad<MP>::NW, KC = PinvQuad<MP>::KC;
 #pragma unroll
-  for (int kc = 0; kc < MP / 32; ++kc)
+  for (int u = 0; u < NW; ++u)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int o = (16 * (2 * kc + q / 4) + 4 * g + q % 4) * LD + slot;
-      h[o] = bh[kc].h[q];
-      l[o] = bl[kc].h[q];
+    for (int v = 0; v < NW; ++v) {
+      acc[u][v] = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) acc[u][v] = mfma3(ah[u][kc], al[u][kc], bh[v][kc], bl[v][kc], acc[u][v]);
     }
 }
 
-// Left-operand fragments of all row tiles from slot-ordered planes.
+// Stores the quadrant's tiles transposed (rows of tile (TB + v, TA + u)) into
+// a plane pair, split into bf16 hi/lo.
 template <int MP>
-__device__ __forceinline__ void load_aop(const uint16_t* h, const uint16_t* l, B8 (&ah)[MP / 16][MP / 32],
-                                         B8 (&al)[MP / 16][MP / 32]) {
-  constexpr int LD = PinvSmem2<MP>::LD;
+__device__ __forceinline__ void quad_store_t(uint16_t (&pl)[2][PinvSmemE<MP>::PL], int TA, int TB,
+                                             const f32x4_t (&v)[PinvQuad<MP>::NW][PinvQuad<MP>::NW]) {
+  constexpr int LD = PinvSmemE<MP>::LD, NW = PinvQuad<MP>::NW;
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < MP / 16; ++t)
+  for (int u = 0; u < NW; ++u)
 #pragma unroll
-    for (int kc = 0; kc < MP / 32; ++kc) {
-      const int o = (16 * t + c) * LD + 32 * kc + 8 * g;
-      ah[t][kc].q = *reinterpret_cast<const uint4*>(h + o);
-      al[t][kc].q = *reinterpret_cast<const uint4*>(l + o);
+    for (int w = 0; w < NW; ++w) {
+      uint2 hv, lv;
+      split_pair(v[u][w][0], v[u][w][1], hv.x, lv.x);
+      split_pair(v[u][w][2], v[u][w][3], hv.y, lv.y);
+      const int o = (16 * (TB + w) + c) * LD + 16 * (TA + u) + 4 * g;
+      *reinterpret_cast<uint2*>(&pl[0][o]) = hv;
+      *reinterpret_cast<uint2*>(&pl[1][o]) = lv;
     }
 }
 
-// acc[t] = P(t) R for every row tile t (bf16x3).
-template <int MP>
-__device__ __forceinline__ void chain_mm(const B8 (&ph)[MP / 16][MP / 32], const B8 (&pl)[MP / 16][MP / 32],
-                                         const B8 (&rh)[MP / 32], const B8 (&rl)[MP / 32],
-                                         f32x4_t (&acc)[MP / 16]) {
-#pragma unroll
-  for (int t = 0; t < MP / 16; ++t) {
-    acc[t] = zero4();
-#pragma unroll
-    for (int kc = 0; kc < MP / 32; ++kc) acc[t] = mfma3(ph[t][kc], pl[t][kc], rh[kc], rl[kc], acc[t]);
-  }
-}
-
-// Pseudoinverse of one head, run by a block of 4 * MP threads.  SAVE: also
-// write each step's Z_k, X_k, T1_k, T2_k to zsave (for the backward pass);
-// the plain forward's kernel is compiled without that code.
+// Pseudoinverse of one head, run by a block of 512 threads.  The landmarks
+// come as the bf16 hi/lo planes the segment means wrote ([bh][MP][D], Kt
+// pre-scaled by log2(e)/sqrt(d)).  SAVE: also write each step's Z_k,
+// X_k = A Z_k, T1_k = X_k (7I - X_k) and T2_k = X_k (15I - T1_k) to zsave
+// ([zmp][zmp] fp32 each, zero beyond m) for the backward pass; in the residual
+// form X = I - E, T1 = 6I - 5E - E^2 and T2 = 9I - 4E - 4E^2 - E^3.  The plain
+// forward's kernel has none of it.
 template <int MP, int D, bool SAVE>
-__device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float* __restrict__ Qt,
-                                          const float* __restrict__ Kt, float* __restrict__ Aout,
-                                          float* __restrict__ Zout, int m, float sl2e, int iters,
-                                          float* __restrict__ zsave, int zmp) {
-  using SM = PinvSmem2<MP>;
-  constexpr int SP = SM::SP, RT = MP / 16, KC = MP / 32, CPT = MP / 4;
-  constexpr int KCD = (D + 31) / 32;  // 32-wide chunks of the head dimension
+__device__ __forceinline__ void pinv_head(PinvSmemE<MP>& sm, int bh, const uint16_t* __restrict__ qt_hi,
+                                          const uint16_t* __restrict__ qt_lo, const uint16_t* __restrict__ kt_hi,
+                                          const uint16_t* __restrict__ kt_lo, float* __restrict__ Aout,
+                                          float* __restrict__ Zout, int m, int iters, float* __restrict__ zsave,
+                                          int zmp) {
+  using SM = PinvSmemE<MP>;
+  using QD = PinvQuad<MP>;
+  constexpr int SP = SM::SP, NW = QD::NW, KC = QD::KC;
+  constexpr int TPR = 256 / MP, CPT = MP / TPR;  // softmax (threads 0..255): threads per row, columns per thread
+  constexpr int KCD = (D + 31) / 32;             // 32-wide chunks of the head dimension
   float* const S = sm.S();
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const float* qt = Qt + (size_t)bh * m * D;
-  const float* kt = Kt + (size_t)bh * m * D;
+  const bool egrp = wave < 4;  // E group (waves 0..3) or Z group (waves 4..7); wave-uniform
+  const int qd = wave & 3;
+  const int TA = NW * (qd >> 1), TB = NW * (qd & 1);  // the wave's quadrant: row tiles TA.., column tiles TB..
 
-  // Scaled scores of row block `wave`, computed transposed ((Kt Qt^T)^T) so
-  // that lane (c, g) of tile tj ends with row 16*wave+c, columns 16tj+4g..+3.
-  // Every fragment load is issued before the first product (rows and columns
-  // are clamped in bounds and masked to zero outside).
-  {
-    const int rq = 16 * wave + c;
-    float4 qv[KCD][2], kv[RT][KCD][2];
+  // Diagonal of the m real landmarks within the quadrant: element i of tile
+  // (u, v) is on it iff the quadrant is diagonal, u == v, 4g + i == c, and the
+  // row is below m.
+  float dgv[NW][4];
 #pragma unroll
-    for (int kc = 0; kc < KCD; ++kc) {
-      const int k0 = min(32 * kc + 8 * g, D - 8);
-      const float* src = qt + (size_t)min(rq, m - 1) * D + k0;
-      qv[kc][0] = *reinterpret_cast<const float4*>(src);
-      qv[kc][1] = *reinterpret_cast<const float4*>(src + 4);
+  for (int u = 0; u < NW; ++u)
 #pragma unroll
-      for (int tj = 0; tj < RT; ++tj) {
-        const float* ks = kt + (size_t)min(16 * tj + c, m - 1) * D + k0;
-        kv[tj][kc][0] = *reinterpret_cast<const float4*>(ks);
-        kv[tj][kc][1] = *reinterpret_cast<const float4*>(ks + 4);
-      }
-    }
-    auto frag = [](const float4 (&v)[2], bool ok, B8& h, B8& l) {
-      const float x[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
-      float y[8];
+    for (int i = 0; i < 4; ++i) dgv[u][i] = (TA == TB && 4 * g + i == c && 16 * (TA + u) + c < m) ? 1.f : 0.f;
+  auto dg = [&](int u, int v, int i) { return u == v ? dgv[u][i] : 0.f; };
+
+  // Scores in base-2 units (E group), computed transposed (S^T = Kt' Qt^T) so
+  // that a lane ends with row 16 (TB + v) + c, columns 16 (TA + u) + 4g .. +3:
+  // one 16-byte store per tile.  Fragments are 16-byte loads of the planes
+  // (rows past m are zero there), all issued before the first product.
+  if (egrp) {
+    B8 kh[NW][KCD], kl[NW][KCD], qh[NW][KCD], ql[NW][KCD];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) y[q] = ok ? x[q] : 0.f;
-      split8(y, h, l);
-    };
-    B8 qh[KCD], ql[KCD];
-#pragma unroll
-    for (int kc = 0; kc < KCD; ++kc) frag(qv[kc], rq < m && 32 * kc + 8 * g < D, qh[kc], ql[kc]);
-#pragma unroll
-    for (int tj = 0; tj < RT; ++tj) {
-      f32x4_t acc = zero4();
+    for (int u = 0; u < NW; ++u)
 #pragma unroll
       for (int kc = 0; kc < KCD; ++kc) {
-        B8 kh, kl;
-        frag(kv[tj][kc], 16 * tj + c < m && 32 * kc + 8 * g < D, kh, kl);
-        acc = mfma3(kh, kl, qh[kc], ql[kc], acc);
+        const int col = min(32 * kc + 8 * g, D - 8);
+        const size_t ok_ = ((size_t)bh * MP + 16 * (TA + u) + c) * D + col;
+        const size_t oq_ = ((size_t)bh * MP + 16 * (TB + u) + c) * D + col;
+        kh[u][kc].q = *reinterpret_cast<const uint4*>(kt_hi + ok_);
+        kl[u][kc].q = *reinterpret_cast<const uint4*>(kt_lo + ok_);
+        qh[u][kc].q = *reinterpret_cast<const uint4*>(qt_hi + oq_);
+        ql[u][kc].q = *reinterpret_cast<const uint4*>(qt_lo + oq_);
+        if (32 * kc + 8 * g >= D) {  // d = 16: lanes past the head dimension contribute zero
+          kh[u][kc].q = kl[u][kc].q = make_uint4(0, 0, 0, 0);
+        }
       }
-      *reinterpret_cast<float4*>(&S[rq * SP + 16 * tj + 4 * g]) =
-          make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
-    }
+#pragma unroll
+    for (int u = 0; u < NW; ++u)
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kc = 0; kc < KCD; ++kc) acc = mfma3(kh[u][kc], kl[u][kc], qh[v][kc], ql[v][kc], acc);
+        *reinterpret_cast<float4*>(&S[(16 * (TB + v) + c) * SP + 16 * (TA + u) + 4 * g]) =
+            make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
   }
   __syncthreads();
 
-  // Row softmax: four adjacent lanes per row, CPT columns each.  Padded rows
-  // and columns become 0.
-  {
-    const int r = tid >> 2, sub = tid & 3, j0 = sub * CPT;
+  // Row softmax (threads 0..255): TPR adjacent lanes per row, CPT columns
+  // each; padded rows and columns become 0.  A goes to global memory, to S
+  // (fp32, in place, for the column sums) and to the P planes (bf16 hi/lo,
+  // row-major); row sums to sm.rows.
+  if (tid < 256) {
+    const int r = tid / TPR, sub = tid % TPR, j0 = sub * CPT;
     float a[CPT];
 #pragma unroll
     for (int u = 0; u < CPT / 4; ++u) {
@@ -448,16 +476,16 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
 #pragma unroll
     for (int q = 0; q < CPT; ++q)
       if (j0 + q < m) mx = fmaxf(mx, a[q]);
-    mx = fmaxf(mx, shfl_xor(mx, 1));
-    mx = fmaxf(mx, shfl_xor(mx, 2));
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
     float sum = 0.f;
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
-      a[q] = (r < m && j0 + q < m) ? exp2f(a[q] - mx) : 0.f;
+      a[q] = (r < m && j0 + q < m) ? __builtin_amdgcn_exp2f(a[q] - mx) : 0.f;  // arguments <= 0
       sum += a[q];
     }
-    sum += shfl_xor(sum, 1);
-    sum += shfl_xor(sum, 2);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) sum += shfl_xor(sum, o);
     const float inv = r < m ? 1.f / sum : 0.f;
     float rs = 0.f;
 #pragma unroll
@@ -465,11 +493,17 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
       a[q] *= inv;
       rs += a[q];
     }
-    rs += shfl_xor(rs, 1);
-    rs += shfl_xor(rs, 2);
 #pragma unroll
-    for (int u = 0; u < CPT / 4; ++u)
+    for (int o = 1; o < TPR; o <<= 1) rs += shfl_xor(rs, o);
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u) {
       *reinterpret_cast<float4*>(&S[r * SP + j0 + 4 * u]) = make_float4(a[4 * u], a[4 * u + 1], a[4 * u + 2], a[4 * u + 3]);
+      uint2 hv, lv;
+      split_pair(a[4 * u], a[4 * u + 1], hv.x, lv.x);
+      split_pair(a[4 * u + 2], a[4 * u + 3], hv.y, lv.y);
+      *reinterpret_cast<uint2*>(&sm.p[0][r * SM::LD + j0 + 4 * u]) = hv;
+      *reinterpret_cast<uint2*>(&sm.p[1][r * SM::LD + j0 + 4 * u]) = lv;
+    }
     if (sub == 0) sm.rows[r] = rs;
     if (r < m) {
       float* ao = Aout + (size_t)bh * m * m + (size_t)r * m;
@@ -485,19 +519,26 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
     }
   }
   __syncthreads();
-  {  // partial column sums over quarters of the rows
+  if (tid < 256) {  // partial column sums over parts of the rows
     const int col = tid % MP, part = tid / MP;
+    constexpr int RPP = MP * MP / 256;  // rows per part
     float s = 0.f;
 #pragma unroll 4
-    for (int rr = 0; rr < MP / 4; ++rr) s += S[(part * (MP / 4) + rr) * SP + col];
+    for (int rr = 0; rr < RPP; ++rr) s += S[(part * RPP + rr) * SP + col];
     sm.colp[part][col] = s;
   }
+  // A's row fragments (the A planes are complete since the last barrier).
+  B8 aah[NW][KC], aal[NW][KC];
+  rows_frag<MP>(sm.p, TA, aah, aal);
   __syncthreads();
   // ||A||_1 (max column sum) and ||A||_inf (max row sum; entries are >= 0).
   float cz;
   {
+    constexpr int NP = 256 / MP;  // parts of the column sums
     const int k = lane % MP;
-    float cs = sm.colp[0][k] + sm.colp[1][k] + sm.colp[2][k] + sm.colp[3][k];
+    float cs = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) cs += sm.colp[pp][k];
     float rm = sm.rows[k];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -507,86 +548,172 @@ __device__ __forceinline__ void pinv_head(PinvSmem2<MP>& sm, int bh, const float
     cz = 1.f / (cs * rm);
   }
 
-  // A as register-resident left operand (all row tiles, slot-ordered
-  // columns); Z0 = cz A^T, column block `wave` = cz * (row block `wave` of A).
-  B8 Ah[RT][KC], Al[RT][KC];
-  B8 Zh[KC], Zl[KC];
-  f32x4_t zf[RT];
+  // E group: E_0 = I - cz A A^T.  Z group: Z_0^T = cz A, in the layout of
+  // every later Z^T product, as A times the identity on the matrix cores (hi
+  // and lo planes of A; the identity is exact in bf16), so that its tiles are
+  // stored transposed as Z_0's rows like any other product.  Neither buffer
+  // is read before the next barrier.
+  f32x4_t ef[NW][NW], zt[NW][NW];
+  if (egrp) {
+    B8 abh[NW][KC], abl[NW][KC];
+    rows_frag<MP>(sm.p, TB, abh, abl);
+    quad_mm<MP>(aah, aal, abh, abl, ef);
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+    for (int u = 0; u < NW; ++u)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const float* src = &S[(16 * t + c) * SP + 32 * kc + 4 * g];
-      const float4 u0 = *reinterpret_cast<const float4*>(src);
-      const float4 u1 = *reinterpret_cast<const float4*>(src + 16);
-      const float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-      split8(x, Ah[t][kc], Al[t][kc]);
-      if (t == wave) {
+      for (int v = 0; v < NW; ++v)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float z = cz * x[q];
-          split_hi_lo(z, Zh[kc].h[q], Zl[kc].h[q]);
-          zf[2 * kc + q / 4][q % 4] = z;
+        for (int i = 0; i < 4; ++i) ef[u][v][i] = dg(u, v, i) - cz * ef[u][v][i];
+    quad_store_t<MP>(sm.e, TA, TB, ef);
+  } else {
+    B8 id[NW][KC];
+#pragma unroll
+    for (int v = 0; v < NW; ++v)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) id[v][kc].h[q] = 32 * kc + 8 * g + q == 16 * (TB + v) + c ? 0x3F80 : 0;
+#pragma unroll
+    for (int u = 0; u < NW; ++u)
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          acc = mfma(aal[u][kc], id[v][kc], acc);
+          acc = mfma(aah[u][kc], id[v][kc], acc);
         }
+        zt[u][v] = cz * acc;
       }
-    }
-  store_bop<MP>(sm.zp[0], sm.zp[1], Zh, Zl, wave);
-  __syncthreads();  // every wave has read the scores before X overwrites them
-
-  // For the backward pass: the column block `wave` of Z_k, X_k, T1_k =
-  // X_k (7I - X_k) and T2_k = X_k (15I - T1_k), fp32 [zmp][zmp] each.
-  auto save = [&](const f32x4_t (&v)[RT], int it, int which) {
-    float* zs = zsave + (((size_t)bh * iters + it) * 4 + which) * zmp * zmp;
-    const int col = 16 * wave + c;
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * t + 4 * g + i;
-        if (row < zmp && col < zmp) zs[(size_t)row * zmp + col] = v[t][i];
-      }
-  };
-  for (int it = 0; it < iters; ++it) {
-    f32x4_t acc[RT];
-    B8 Th[KC], Tl[KC];
-    if constexpr (SAVE) save(zf, it, 0);
-    // X = A Z: store X for every wave; keep T1 = 7I - X (own columns).
-    chain_mm<MP>(Ah, Al, Zh, Zl, acc);
-    if constexpr (SAVE) save(acc, it, 1);
-    {
-      B8 xh[KC], xl[KC];
-      to_bop<MP>(acc, 1.f, 0.f, wave, xh, xl);
-      store_bop<MP>(sm.xp[0], sm.xp[1], xh, xl, wave);
-    }
-    to_bop<MP>(acc, -1.f, 7.f, wave, Th, Tl);
-    __syncthreads();
-    B8 Ph[RT][KC], Pl[RT][KC], Rh[RT][KC], Rl[RT][KC];
-    load_aop<MP>(sm.xp[0], sm.xp[1], Ph, Pl);
-    load_aop<MP>(sm.zp[0], sm.zp[1], Rh, Rl);  // in flight during the two X products
-    chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T1
-    if constexpr (SAVE) save(acc, it, 2);
-    to_bop<MP>(acc, -1.f, 15.f, wave, Th, Tl);
-    chain_mm<MP>(Ph, Pl, Th, Tl, acc);  // X T3
-    if constexpr (SAVE) save(acc, it, 3);
-    to_bop<MP>(acc, -1.f, 13.f, wave, Th, Tl);
-    chain_mm<MP>(Rh, Rl, Th, Tl, acc);  // Z T5
-#pragma unroll
-    for (int t = 0; t < RT; ++t) zf[t] = acc[t] * 0.25f;
-    to_bop<MP>(zf, 1.f, 0.f, wave, Zh, Zl);
-    __syncthreads();  // every wave holds its X and Z fragments
-    store_bop<MP>(sm.zp[0], sm.zp[1], Zh, Zl, wave);
+    quad_store_t<MP>(sm.z, TA, TB, zt);
   }
 
-  // Z in fp32 straight from the last product.
-  const int col = 16 * wave + c;
-  if (col < m) {
+  // For the backward pass: the quadrant of a step's matrix ([zmp][zmp] fp32);
+  // trans: v holds tiles of the transpose (Z^T).
+  auto save = [&](const f32x4_t (&v)[NW][NW], int it, int which, bool trans) {
+    float* zs = zsave + (((size_t)bh * iters + it) * 4 + which) * zmp * zmp;
+#pragma unroll
+    for (int u = 0; u < NW; ++u)
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a = 16 * (TA + u) + 4 * g + i, b = 16 * (TB + w) + c;
+          const int row = trans ? b : a, col = trans ? a : b;
+          if (row < zmp && col < zmp) zs[(size_t)row * zmp + col] = v[u][w][i];
+        }
+  };
+
+  __syncthreads();  // E_0 and Z_0 planes visible
+  for (int it = 0; it < iters; ++it) {
+    // Level 1.
+    B8 eah[NW][KC], eal[NW][KC];  // E rows TA (E group), kept for level 2
+    f32x4_t e2[NW][NW];
+    if (egrp) {
+      B8 ebh[NW][KC], ebl[NW][KC];
+      rows_frag<MP>(sm.e, TA, eah, eal);
+      rows_frag<MP>(sm.e, TB, ebh, ebl);
+      quad_mm<MP>(eah, eal, ebh, ebl, e2);
+      f32x4_t nt[NW][NW];
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int v = 0; v < NW; ++v) nt[u][v] = 0.75f * ef[u][v] + 0.25f * e2[u][v];
+      // Neither E^2 nor N is read again before the next barrier (their
+      // readers of the last step finished before its closing barrier).
+      quad_store_t<MP>(sm.e2, TA, TB, e2);
+      quad_store_t<MP>(sm.nn, TA, TB, nt);
+    } else if (it > 0) {  // Z_t^T = P_{t-1} Z_{t-1}^T (Z_0 is given)
+      B8 pah[NW][KC], pal[NW][KC], zbh[NW][KC], zbl[NW][KC];
+      rows_frag<MP>(sm.p, TA, pah, pal);
+      rows_frag<MP>(sm.z, TB, zbh, zbl);
+      quad_mm<MP>(pah, pal, zbh, zbl, zt);
+    }
+    if constexpr (SAVE) {
+      if (!egrp) save(zt, it, 0, true);
+    }
+    __syncthreads();  // E^2 and N visible; every read of Z_{t-1} and P_{t-1} done
+    // Level 2.
+    if (egrp) {
+      B8 fbh[NW][KC], fbl[NW][KC];
+      rows_frag<MP>(sm.e2, TB, fbh, fbl);
+      f32x4_t e3[NW][NW];
+      quad_mm<MP>(eah, eal, fbh, fbl, e3);
+      f32x4_t pt[NW][NW];
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pt[u][v][i] = dg(u, v, i) + ef[u][v][i] + e2[u][v][i] + 0.25f * e3[u][v][i];
+      if constexpr (SAVE) {
+        f32x4_t x[NW][NW], t1[NW][NW], t2[NW][NW];
+#pragma unroll
+        for (int u = 0; u < NW; ++u)
+#pragma unroll
+          for (int v = 0; v < NW; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float d1 = dg(u, v, i);
+              x[u][v][i] = d1 - ef[u][v][i];
+              t1[u][v][i] = 6.f * d1 - 5.f * ef[u][v][i] - e2[u][v][i];
+              t2[u][v][i] = 9.f * d1 - 4.f * ef[u][v][i] - 4.f * e2[u][v][i] - e3[u][v][i];
+            }
+        save(x, it, 1, false);
+        save(t1, it, 2, false);
+        save(t2, it, 3, false);
+      }
+      quad_store_t<MP>(sm.p, TA, TB, pt);  // P_{t-1}'s readers finished before the last barrier
+    } else {
+      if (it > 0) quad_store_t<MP>(sm.z, TA, TB, zt);  // Z_{t-1}'s readers finished before the last barrier
+      B8 fah[NW][KC], fal[NW][KC], nbh[NW][KC], nbl[NW][KC];
+      rows_frag<MP>(sm.e2, TA, fah, fal);
+      rows_frag<MP>(sm.nn, TB, nbh, nbl);
+      f32x4_t en[NW][NW];
+      quad_mm<MP>(fah, fal, nbh, nbl, en);
+      // E's planes are not read in this level (the E group keeps its row
+      // fragments from level 1).
+      quad_store_t<MP>(sm.e, TA, TB, en);
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sm.ex[qd][(u * NW + v) * 4 + i][lane] = en[u][v][i];
+    }
+    __syncthreads();  // E_{t+1}, P_t (and Z_t) visible
+    if (egrp) {
+#pragma unroll
+      for (int u = 0; u < NW; ++u)
+#pragma unroll
+        for (int v = 0; v < NW; ++v)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ef[u][v][i] = sm.ex[qd][(u * NW + v) * 4 + i][lane];
+    }
+  }
+  if (!egrp) {
+    if (iters > 0) {  // Z = Z_iters, Z_iters^T = P_{iters-1} Z_{iters-1}^T
+      B8 pah[NW][KC], pal[NW][KC], zbh[NW][KC], zbl[NW][KC];
+      rows_frag<MP>(sm.p, TA, pah, pal);
+      rows_frag<MP>(sm.z, TB, zbh, zbl);
+      quad_mm<MP>(pah, pal, zbh, zbl, zt);
+    }
+    // Z in fp32: tile element i of (u, v) is Z[16 (TB + v) + c][16 (TA + u) + 4g + i].
     float* zo = Zout + (size_t)bh * m * m;
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int u = 0; u < NW; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * t + 4 * g + i;
-        if (row < m) zo[(size_t)row * m + col] = zf[t][i];
+      for (int v = 0; v < NW; ++v) {
+        const int row = 16 * (TB + v) + c, col = 16 * (TA + u) + 4 * g;
+        if (row >= m) continue;
+        if (m == MP) {
+          *reinterpret_cast<float4*>(zo + (size_t)row * m + col) =
+              make_float4(zt[u][v][0], zt[u][v][1], zt[u][v][2], zt[u][v][3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (col + i < m) zo[(size_t)row * m + col + i] = zt[u][v][i];
+        }
       }
   }
 }
@@ -767,7 +894,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   using SM = BvSmem<IO, D>;
   constexpr int KC = (D + 31) / 32;  // 32-wide k chunks over the head dimension
   constexpr int MD = D / 16;         // 16-row tiles of V^T
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;  // the chunk's group of 4 waves (two groups per 512-thread block)
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   // Keys [kbeg, kend) of this chunk; nb <= n is the head's number of real
   // keys (chunks past it are empty and leave max -inf, sum 0).
@@ -809,8 +936,8 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   constexpr int SLOTS = D / 8;
   constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
   constexpr int TPT = (TASKS + 255) / 256;         // tasks per thread
-  BvStage<IO> st[TPT];
-  auto load_tile = [&](int k0) {
+  BvStage<IO> stage[TPT];
+  auto load_tile = [&](BvStage<IO> (&st)[TPT], int k0) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int e = tid + 256 * u;
@@ -827,7 +954,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const BvStage<IO> (&st)[TPT]) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int e = tid + 256 * u;
@@ -872,12 +999,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
     }
   };
 
-  load_tile(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += 64) {
-    store_tile();
-    __syncthreads();
-    if (k0 + 64 < kend) load_tile(k0 + 64);
-
+  auto compute_tile = [&](int k0) {
     // K operand fragments for the 4 key tiles of 16 (shared by all landmark tiles).
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
@@ -968,6 +1090,19 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
         }
       }
     }
+  };
+
+  // Both groups of the block run the same number of steps (their barriers
+  // are the block's); a group past its chunk's end only waits.
+  const int ntile = (chunk + 63) / 64;
+  if (kbeg < kend) load_tile(stage, kbeg);
+  for (int t = 0; t < ntile; ++t) {
+    const int kt = kbeg + 64 * t;
+    const bool live = kt < kend;  // uniform over the group
+    if (live) store_tile(stage);
+    __syncthreads();
+    if (kt + 64 < kend) load_tile(stage, kt + 64);
+    if (live) compute_tile(kt);
     __syncthreads();
   }
 
@@ -1020,6 +1155,7 @@ struct LandmarkPassArgs {
   float* zsave;  // the pseudoinverse steps for the backward pass, or nullptr
   int zmp;
   const float *Qt, *Kt;
+  const uint16_t *qt_hi, *qt_lo, *kt_hi, *kt_lo;  // landmark planes (pseudoinverse blocks)
   float *A, *Z, *pacc, *pmax, *psum;
   const float* conv_w;
   uint4* cwop;
@@ -1028,38 +1164,41 @@ struct LandmarkPassArgs {
   float sl2e;
 };
 
-template <bool PINV, typename B>
+template <int PMP, typename B>
 union LandmarkPassSmem {
-  PinvSmem2<64> p;
-  B b;
+  PinvSmemE<PMP> p;
+  B b[2];
 };
 template <typename B>
-union LandmarkPassSmem<false, B> {
-  B b;
+union LandmarkPassSmem<0, B> {
+  B b[2];
 };
 
-template <typename IO, int D, int NTW, bool PINV, bool SAVE>
-__global__ __launch_bounds__(256) void k_landmark_pass(LandmarkPassArgs a) {
+// PMP: landmarks padded to 32 or 64 for the pseudoinverse blocks, 0 for none.
+template <typename IO, int D, int NTW, int PMP, bool SAVE>
+__global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   using T = typename IO::T;
-  __shared__ LandmarkPassSmem<PINV, BvSmem<IO, D>> sm;
+  __shared__ LandmarkPassSmem<PMP, BvSmem<IO, D>> sm;
   int blk = blockIdx.x;
-  if constexpr (PINV) {
+  if constexpr (PMP > 0) {
     if (blk < a.npinv) {
-      pinv_head<64, D, SAVE>(sm.p, blk, a.Qt, a.Kt, a.A, a.Z, a.m, a.sl2e, a.iters, a.zsave, a.zmp);
+      pinv_head<PMP, D, SAVE>(sm.p, blk, a.qt_hi, a.qt_lo, a.kt_hi, a.kt_lo, a.A, a.Z, a.m, a.iters, a.zsave,
+                              a.zmp);
       return;
     }
     blk -= a.npinv;
   }
   if (blk < a.nconv) {
-    const int idx = blk * 256 + (int)threadIdx.x;
+    const int idx = blk * 512 + (int)threadIdx.x;
     if (idx < a.conv_total) conv_operand(a.conv_w, a.cwop, idx, a.conv_k);
     return;
   }
   blk -= a.nconv;
-  const int bh = blk / a.nchunks;
-  bv_chunk<IO, D, NTW>(sm.b, blk % a.nchunks, bh, static_cast<const T*>(a.K), static_cast<const T*>(a.V), a.Qt,
-                       a.pacc, a.pmax, a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk,
-                       a.nchunks, a.sl2e);
+  // Key blocks: chunks 2 j and 2 j + 1 of a head, one per group of 4 waves.
+  const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 8;
+  bv_chunk<IO, D, NTW>(sm.b[grp], 2 * (blk % half) + grp, bh, static_cast<const T*>(a.K),
+                       static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
+                       seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
 }
 
 // Finish of the split-n pass, one block per (16-feature slice, head):
@@ -1250,7 +1389,8 @@ static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   KernelTimer kt_("segment_mean", s);
   k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
-                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, p.lens, p.heads, p.n,
+                                                         w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo, p.lens,
+                                                         p.heads, p.n,
                                                          p.m, w.mpa,
                                                          kLog2e / sqrtf((float)D));
 }
@@ -1321,7 +1461,7 @@ hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
 
 static bool conv_uses_ops(const Problem& p) { return p.bf16 && p.conv_w && p.conv_k > 1 && p.conv_k <= 33; }
 
-template <typename IO, int D, int NTW, bool PINV>
+template <typename IO, int D, int NTW, int PMP>
 static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   LandmarkPassArgs a;
@@ -1331,6 +1471,10 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.zmp = p.zmp;
   a.Qt = w.Qt;
   a.Kt = w.Kt;
+  a.qt_hi = w.qt_hi;
+  a.qt_lo = w.qt_lo;
+  a.kt_hi = w.kt_hi;
+  a.kt_lo = w.kt_lo;
   a.A = w.A;
   a.Z = w.Z;
   a.pacc = w.pacc;
@@ -1345,33 +1489,34 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.chunk = w.chunk;
   a.nchunks = w.nchunks;
   a.iters = p.iters;
-  a.npinv = PINV ? BH : 0;
+  a.npinv = PMP > 0 ? BH : 0;
   a.conv_total = conv_uses_ops(p) ? p.heads * p.d * 4 * 9 : 0;
-  a.nconv = ceil_div(a.conv_total, 256);
+  a.nconv = ceil_div(a.conv_total, 512);
   a.conv_k = p.conv_k;
   a.sl2e = kLog2e / sqrtf((float)D);
-  const int grid = a.npinv + a.nconv + w.nchunks * BH;
+  const int grid = a.npinv + a.nconv + (w.nchunks / 2) * BH;
   KernelTimer kt_("landmark_pass", s);
-  if constexpr (PINV) {
+  if constexpr (PMP > 0) {
     if (p.zsave) {
-      k_landmark_pass<IO, D, NTW, true, true><<<grid, 256, 0, s>>>(a);
+      k_landmark_pass<IO, D, NTW, PMP, true><<<grid, 512, 0, s>>>(a);
       return;
     }
   }
-  k_landmark_pass<IO, D, NTW, PINV, false><<<grid, 256, 0, s>>>(a);
+  k_landmark_pass<IO, D, NTW, PMP, false><<<grid, 512, 0, s>>>(a);
 }
 
 template <typename IO, int D>
 static void landmark_pass_t(const Problem& p, const Ws& w, hipStream_t s) {
   if constexpr (IO::kBf16) {
-    if (p.m <= 64) return landmark_pass_launch<IO, D, 1, true>(p, w, s);
+    if (p.m <= 32) return landmark_pass_launch<IO, D, 1, 32>(p, w, s);
+    if (p.m <= 64) return landmark_pass_launch<IO, D, 1, 64>(p, w, s);
   }
   if (p.m <= 64)
-    landmark_pass_launch<IO, D, 1, false>(p, w, s);
+    landmark_pass_launch<IO, D, 1, 0>(p, w, s);
   else if (p.m <= 128)
-    landmark_pass_launch<IO, D, 2, false>(p, w, s);
+    landmark_pass_launch<IO, D, 2, 0>(p, w, s);
   else
-    landmark_pass_launch<IO, D, 4, false>(p, w, s);
+    landmark_pass_launch<IO, D, 4, 0>(p, w, s);
 }
 
 hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {

@@ -28,15 +28,16 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   if (batch < 1 || heads < 1 || n < 1 || m < 1 || m > n) return false;
   if (!(d == 16 || d == 32 || d == 64 || d == 128) || m > 256 || n > (1 << 24)) return false;
   const long long BH = (long long)batch * heads;
-  // Key chunking for the split-n pass: about 2 blocks per CU over 256 CUs
-  // together with the one pseudoinverse block per head that shares the
-  // launch; chunks are a multiple of the 64-key tile.
-  long long want = (512 - (BH < 256 ? BH : 256)) / BH;
+  // Key chunking for the split-n pass: 512-thread blocks of two chunks each,
+  // one block per CU over 256 CUs together with the one pseudoinverse block
+  // per head that shares the launch; chunks are a multiple of the 64-key
+  // tile, and their count is even (a trailing chunk may be empty).
+  long long want = 2 * ((256 - (BH < 256 ? BH : 256)) / BH);
   long long maxch = cdiv(n, 64);
   long long nch = want < 1 ? 1 : (want > maxch ? maxch : want);
   long long chunk = cdiv(cdiv(n, nch), 64) * 64;
   nch = cdiv(n, chunk);
-  L->nchunks = (int)nch;
+  L->nchunks = (int)(nch + (nch & 1));
   L->chunk = (int)chunk;
   L->mpa = m <= 32 ? 32 : m <= 64 ? 64 : m <= 128 ? 128 : 256;
   size_t off = 0;
@@ -57,11 +58,13 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   L->x = take(big ? mm : 0);
   L->t = take(big ? mm : 0);
   L->u = take(big ? mm : 0);
-  L->pacc = take((size_t)BH * nch * m * d * 4);
-  L->pmax = take((size_t)BH * nch * m * 4);
-  L->psum = take((size_t)BH * nch * m * 4);
+  L->pacc = take((size_t)BH * L->nchunks * m * d * 4);
+  L->pmax = take((size_t)BH * L->nchunks * m * 4);
+  L->psum = take((size_t)BH * L->nchunks * m * 4);
   L->kt_hi = take((size_t)BH * L->mpa * d * 2);
   L->kt_lo = take((size_t)BH * L->mpa * d * 2);
+  L->qt_hi = take((size_t)BH * L->mpa * d * 2);
+  L->qt_lo = take((size_t)BH * L->mpa * d * 2);
   L->wt_hi = take((size_t)BH * d * L->mpa * 2);
   L->wt_lo = take((size_t)BH * d * L->mpa * 2);
   L->cwop = take((size_t)heads * d * 4 * 9 * 16);
@@ -86,6 +89,8 @@ Ws resolve(const WsLayout& L, char* b) {
   w.psum = reinterpret_cast<float*>(b + L.psum);
   w.kt_hi = reinterpret_cast<uint16_t*>(b + L.kt_hi);
   w.kt_lo = reinterpret_cast<uint16_t*>(b + L.kt_lo);
+  w.qt_hi = reinterpret_cast<uint16_t*>(b + L.qt_hi);
+  w.qt_lo = reinterpret_cast<uint16_t*>(b + L.qt_lo);
   w.wt_hi = reinterpret_cast<uint16_t*>(b + L.wt_hi);
   w.wt_lo = reinterpret_cast<uint16_t*>(b + L.wt_lo);
   w.cwop = reinterpret_cast<uint4*>(b + L.cwop);
