@@ -39,32 +39,6 @@ typedef short bf16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
 constexpr int kTQ = 64;     // rows per tile: 4 waves x 16 queries
 constexpr int kConvNS = 9;  // 4-tap steps of the matrix-core skip (33 taps)
 
-// Buffer resource over the rows of one head: 32-bit byte offsets, range
-// checked by the hardware (loads at offsets >= `bytes` return zero, stores
-// there are dropped; a negative offset reads as a huge unsigned one).  The
-// third word sets a 32-bit data format, under which untyped dword accesses
-// are range checked.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (unsigned)off, 0, 0));
-}
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (unsigned)off, 0, 0);
-}
-
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (unsigned)off, 0, 0);
-}
-
 // Shared-memory layout (bytes) of one block.
 // KW: 0 = no skip, 1 = one tap, 33 = up to 33 taps (zero-padded, centred),
 //     -1 = wider filters (taps and rows read from global memory; slow path).

@@ -1536,7 +1536,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
       kern<<<dim3(L.nk, BH), 256, bytes, ks>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
                                                w.Qt, w.BV, F(L.dbv), w.pmax, w.psum, static_cast<uint16_t*>(bp.dK),
                                                static_cast<uint16_t*>(bp.dV), F(L.pdqt), p.n, p.m, ck > 0 ? 1 : 0,
-                                               L.kchunk, L.nk, w.nchunks, sl2e, scale);
+                                               L.kchunk, L.nk, forward_partials(p, w), sl2e, scale);
     }
     dw_finish(ks);
     if ((e = hipEventRecord(ss->join, ks)) != hipSuccess) return e;
@@ -1563,7 +1563,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                               static_cast<const T*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv), F(L.dkt),
                                               w.pmax, w.psum, static_cast<T*>(bp.dK), static_cast<T*>(bp.dV),
                                               F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads, ck, L.kchunk, L.nk,
-                                              w.nchunks, sl2e, scale);
+                                              forward_partials(p, w), sl2e, scale);
     }
     dw_finish(s);
   }

@@ -189,6 +189,56 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Buffer resource over `bytes` bytes from `base`: 32-bit byte offsets, range
+// checked by the hardware (loads at offsets >= `bytes` return zero, stores
+// there are dropped; a negative offset reads as a huge unsigned one).  The
+// third word sets a 32-bit data format, under which untyped dword accesses
+// are range checked.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawBufferWord3);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (unsigned)off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (unsigned)off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (unsigned)off, 0, 0);
+}
+
+// Device-coherent accesses: the cache policy that agent-scope atomic loads
+// and stores carry (the sc1 scope bit, 16 in the buffer instructions' aux
+// operand).  The L2 of each XCD is not coherent with the others; with these,
+// a block reads what another block of the same launch wrote, on any XCD,
+// once the writer's stores have completed (wait_stores) before it signals
+// through an agent-scope atomic, with no L2 writeback or invalidation.
+constexpr int kDeviceCoherent = 16;
+
+__device__ __forceinline__ void st_coh(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (unsigned)off, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ void st_coh4(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (unsigned)off, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ float ld_coh(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (unsigned)off, 0, kDeviceCoherent));
+}
+__device__ __forceinline__ float4 ld_coh4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (unsigned)off, 0, kDeviceCoherent));
+}
+
+// Waits until every memory access this lane issued has completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Rows of batch entry b that are tokens: lens[b] clamped to [0, n] for a

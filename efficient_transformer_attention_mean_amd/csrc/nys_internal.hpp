@@ -16,6 +16,7 @@ struct WsLayout {
   size_t qt_hi, qt_lo;             // bf16 planes of Qt, [bh][mpa][d] (rows m..mpa-1 zero)
   size_t wt_hi, wt_lo;             // bf16 planes of W^T, [bh][d][mpa], landmark order permuted
   size_t cwop;                     // matrix-core operands of the skip filters, [heads][d][4][9] x 16 B
+  size_t sync;                     // uint32 [2][bh]: per-head arrival counters of the landmark pass
   size_t total;
   int nchunks, chunk;              // split-n: blocks per head, keys per block
   int mpa;                         // landmarks padded for the output stage: 32, 64, 128 or 256
@@ -31,6 +32,7 @@ struct Ws {
   float *pacc, *pmax, *psum;
   uint16_t *kt_hi, *kt_lo, *qt_hi, *qt_lo, *wt_hi, *wt_lo;
   uint4* cwop;
+  unsigned* sync;
   int nchunks, chunk, mpa;
 };
 
@@ -78,6 +80,9 @@ hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s);  /
 hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s);
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s);           // A, Z when not in the pass above
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s);      // B V, W, W^T planes (needs Z)
+// Split-n partial entries (pmax, psum, pacc) per head that the forward leaves:
+// one per key chunk, or one per pair of chunks when the landmark pass merges them.
+int forward_partials(const Problem& p, const Ws& w);
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);

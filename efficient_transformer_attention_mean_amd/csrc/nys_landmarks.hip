@@ -39,8 +39,13 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
                                                       uint16_t* __restrict__ kt_hi, uint16_t* __restrict__ kt_lo,
                                                       uint16_t* __restrict__ qt_hi, uint16_t* __restrict__ qt_lo,
                                                       const int* __restrict__ lens, int heads, int n, int m,
-                                                      int mpa, float sl2e) {
+                                                      int mpa, float sl2e, unsigned* __restrict__ sync,
+                                                      int nsync) {
   using T = typename IO::T;
+  // The landmark pass's per-head counters start at zero (it runs after this
+  // launch on the same stream).
+  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0)
+    for (int i = threadIdx.x; i < nsync; i += 256) sync[i] = 0u;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int SLOTS = D / VEC;   // 16-byte vectors per row
   constexpr int RS = 256 / SLOTS;  // rows covered per pass
@@ -398,12 +403,16 @@ __device__ __forceinline__ void quad_store_t(uint16_t (&pl)[2][PinvSmemE<MP>::PL
 // ([zmp][zmp] fp32 each, zero beyond m) for the backward pass; in the residual
 // form X = I - E, T1 = 6I - 5E - E^2 and T2 = 9I - 4E - 4E^2 - E^3.  The plain
 // forward's kernel has none of it.
+//
+// The final Z goes to Zout with device-coherent stores and, as bf16 hi/lo
+// row planes (pitch MP + 8), to zdst: LDS that aliases only the E planes,
+// which no wave reads after the last step.
 template <int MP, int D, bool SAVE>
 __device__ __forceinline__ void pinv_head(PinvSmemE<MP>& sm, int bh, const uint16_t* __restrict__ qt_hi,
                                           const uint16_t* __restrict__ qt_lo, const uint16_t* __restrict__ kt_hi,
                                           const uint16_t* __restrict__ kt_lo, float* __restrict__ Aout,
                                           float* __restrict__ Zout, int m, int iters, float* __restrict__ zsave,
-                                          int zmp) {
+                                          int zmp, uint16_t (*zdst)[PinvSmemE<MP>::PL]) {
   using SM = PinvSmemE<MP>;
   using QD = PinvQuad<MP>;
   constexpr int SP = SM::SP, NW = QD::NW, KC = QD::KC;
@@ -699,7 +708,8 @@ __device__ __forceinline__ void pinv_head(PinvSmemE<MP>& sm, int bh, const uint1
       quad_mm<MP>(pah, pal, zbh, zbl, zt);
     }
     // Z in fp32: tile element i of (u, v) is Z[16 (TB + v) + c][16 (TA + u) + 4g + i].
-    float* zo = Zout + (size_t)bh * m * m;
+    // Device-coherent stores: a key block of the same launch reads Z.
+    const __amdgpu_buffer_rsrc_t rz = head_rsrc(Zout + (size_t)bh * m * m, m * m * 4);
 #pragma unroll
     for (int u = 0; u < NW; ++u)
 #pragma unroll
@@ -707,14 +717,14 @@ __device__ __forceinline__ void pinv_head(PinvSmemE<MP>& sm, int bh, const uint1
         const int row = 16 * (TB + v) + c, col = 16 * (TA + u) + 4 * g;
         if (row >= m) continue;
         if (m == MP) {
-          *reinterpret_cast<float4*>(zo + (size_t)row * m + col) =
-              make_float4(zt[u][v][0], zt[u][v][1], zt[u][v][2], zt[u][v][3]);
+          st_coh4(rz, 4 * (row * m + col), make_float4(zt[u][v][0], zt[u][v][1], zt[u][v][2], zt[u][v][3]));
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (col + i < m) zo[(size_t)row * m + col + i] = zt[u][v][i];
+            if (col + i < m) st_coh(rz, 4 * (row * m + col + i), zt[u][v][i]);
         }
       }
+    quad_store_t<MP>(*reinterpret_cast<uint16_t(*)[2][SM::PL]>(zdst), TA, TB, zt);
   }
 }
 
@@ -884,8 +894,15 @@ struct BvStage {
 };
 
 // One (key chunk, head) of the split-n pass, run by a block of 256 threads.
-template <typename IO, int D, int NTW>
-__device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, const typename IO::T* __restrict__ Kin,
+// PAIR: the block's two groups run chunks 2j and 2j + 1 of one head; group 1
+// hands its partial to group 0 through `xch` (the block's LDS, free once both
+// groups are past their last tile), which merges the two and writes one partial, entry
+// j of nchunks / 2 per head, with device-coherent stores (the head's last key
+// block of the same launch reads them).  Otherwise each group writes its own
+// chunk's partial, entry ch of nchunks, with plain stores.
+template <typename IO, int D, int NTW, bool PAIR>
+__device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, int bh,
+                                         const typename IO::T* __restrict__ Kin,
                                          const typename IO::T* __restrict__ Vin, const float* __restrict__ Qt,
                                          float* __restrict__ pacc, float* __restrict__ pmax,
                                          float* __restrict__ psum, int n, int nb, int m, int chunk, int nchunks,
@@ -931,12 +948,14 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
     for (int md = 0; md < MD; ++md) acc[t][md] = zero4();
   }
 
-  // Staging is software-pipelined: the next tile's K and V rows are loaded
-  // into registers while the current tile is computed from LDS.
+  // Staging is software-pipelined: the K and V rows of the next tile (with
+  // one landmark tile per wave, of the next two tiles) are loaded into
+  // registers while the current tile is computed from LDS.
   constexpr int SLOTS = D / 8;
   constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
   constexpr int TPT = (TASKS + 255) / 256;         // tasks per thread
-  BvStage<IO> stage[TPT];
+  constexpr bool DEEP = NTW == 1;
+  BvStage<IO> stage[TPT], stage2[DEEP ? TPT : 1];
   auto load_tile = [&](BvStage<IO> (&st)[TPT], int k0) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
@@ -1095,32 +1114,288 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, int ch, int bh, cons
   // Both groups of the block run the same number of steps (their barriers
   // are the block's); a group past its chunk's end only waits.
   const int ntile = (chunk + 63) / 64;
-  if (kbeg < kend) load_tile(stage, kbeg);
-  for (int t = 0; t < ntile; ++t) {
-    const int kt = kbeg + 64 * t;
-    const bool live = kt < kend;  // uniform over the group
-    if (live) store_tile(stage);
+  if constexpr (DEEP) {
+    auto step = [&](BvStage<IO> (&st)[TPT], int kt) {
+      const bool live = kt < kend;  // uniform over the group
+      if (live) store_tile(st);
+      __syncthreads();
+      if (kt + 128 < kend) load_tile(st, kt + 128);
+      if (live) compute_tile(kt);
+      __syncthreads();
+    };
+    if (kbeg < kend) load_tile(stage, kbeg);
+    if (kbeg + 64 < kend) load_tile(stage2, kbeg + 64);
+    for (int t = 0; t < ntile; t += 2) {
+      step(stage, kbeg + 64 * t);
+      if (t + 1 < ntile) step(stage2, kbeg + 64 * (t + 1));
+    }
+  } else {
+    if (kbeg < kend) load_tile(stage, kbeg);
+    for (int t = 0; t < ntile; ++t) {
+      const int kt = kbeg + 64 * t;
+      const bool live = kt < kend;  // uniform over the group
+      if (live) store_tile(stage);
+      __syncthreads();
+      if (kt + 64 < kend) load_tile(stage, kt + 64);
+      if (live) compute_tile(kt);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (PAIR) {
+    // Group 1's partial -> group 0, which merges it into its own:
+    // M = max(M0, M1), sum = sum0 2^(M0 - M) + sum1 2^(M1 - M), likewise the
+    // accumulators (an empty chunk has M = -inf and contributes nothing).
+    constexpr int NV = NTW * (MD * 4 + 2);  // floats per lane
+    const int grp = threadIdx.x >> 8;
+    float* xw = xch + wave * NV * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        float* x = xw + t * (MD * 4 + 2) * 64;
+        x[0] = run_max[t];
+        x[64] = run_sum[t];
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[(2 + 4 * md + i) * 64] = acc[t][md][i];
+      }
+    }
     __syncthreads();
-    if (kt + 64 < kend) load_tile(stage, kt + 64);
-    if (live) compute_tile(kt);
-    __syncthreads();
+    if (grp == 1) return;  // no barrier follows in this function
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const float* x = xw + t * (MD * 4 + 2) * 64;
+      const float m1 = x[0], s1 = x[64];
+      const float M = fmaxf(run_max[t], m1);
+      const float e0 = run_max[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(run_max[t] - M);
+      const float e1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      run_sum[t] = run_sum[t] * e0 + s1 * e1;
+      run_max[t] = M;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][md][i] = acc[t][md][i] * e0 + x[(2 + 4 * md + i) * 64] * e1;
+    }
   }
 
   // Partials for landmarks < m.
+  constexpr bool COH = PAIR;
+  const int np = PAIR ? nchunks / 2 : nchunks;  // partial entries per head
+  const size_t hb = (size_t)bh * np * m;        // the head's first (entry, landmark)
+  const __amdgpu_buffer_rsrc_t ra = head_rsrc(pacc + hb * D, np * m * D * 4);
+  const __amdgpu_buffer_rsrc_t rm = head_rsrc(pmax + hb, np * m * 4);
+  const __amdgpu_buffer_rsrc_t rs = head_rsrc(psum + hb, np * m * 4);
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int lm = (wave * NTW + t) * 16 + c;
     if (lm >= m) continue;
-    const size_t base = ((size_t)bh * nchunks + ch) * m + lm;
+    const int e = (PAIR ? ch >> 1 : ch) * m + lm;
     if (g == 0) {
-      pmax[base] = run_max[t];
-      psum[base] = run_sum[t];
+      if constexpr (COH) {
+        st_coh(rm, 4 * e, run_max[t]);
+        st_coh(rs, 4 * e, run_sum[t]);
+      } else {
+        pmax[hb + e] = run_max[t];
+        psum[hb + e] = run_sum[t];
+      }
     }
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
       float4 v = make_float4(acc[t][md][0], acc[t][md][1], acc[t][md][2], acc[t][md][3]);
-      *reinterpret_cast<float4*>(&pacc[base * D + md * 16 + 4 * g]) = v;
+      if constexpr (COH)
+        st_coh4(ra, 4 * (e * D + md * 16 + 4 * g), v);
+      else
+        *reinterpret_cast<float4*>(&pacc[(hb + e) * D + md * 16 + 4 * g]) = v;
     }
+  }
+}
+
+// Finish of the split-n pass for one head, inside the landmark pass (blocks
+// of 512 threads):
+//   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
+//   (M_j = max_c pmax_c[j]; entries folded in order, in batches with a running
+//   maximum), computed by the head's last key block to arrive; and
+//   W = Z BV on the matrix cores (bf16x3) with the W^T bf16 plane [bh][D][MP]
+//   the output stage reads (within each chunk of 32 landmarks, position
+//   8g + q holds landmark 4g + q (q < 4) or 16 + 4g + q - 4 (q >= 4), the
+//   order in which that stage's softmax lanes hold their landmarks; padding
+//   is zero), computed by whichever of that block and the head's
+//   pseudoinverse block arrives second: it holds one operand in LDS and reads
+//   the other, which the first left in global memory with device-coherent
+//   stores.  No block waits for another.
+template <int MP, int D>
+struct FinishSmem {
+  static constexpr int LD = MP + 8;      // plane row pitch (bf16): 16-byte aligned rows
+  __align__(16) uint16_t z[2][MP * LD];  // Z rows, hi / lo (zero past m)
+  __align__(16) uint16_t bt[2][D * LD];  // BV^T rows (feature-major), hi / lo (zero past m)
+};
+
+// BV of head bh from np partial entries -> BV (device-coherent stores) and
+// the BV^T planes.
+template <int MP, int D>
+__device__ __forceinline__ void combine_bv(FinishSmem<MP, D>& sm, int bh, const float* __restrict__ pacc,
+                                           const float* __restrict__ pmax, const float* __restrict__ psum,
+                                           float* __restrict__ BV, int m, int np) {
+  constexpr int LD = FinishSmem<MP, D>::LD, NQ = D / 4, ITEMS = MP * NQ;
+  constexpr int IPT = (ITEMS + 511) / 512;                    // (landmark, feature quad) items per thread
+  constexpr int NB = IPT >= 4 ? 4 : (IPT == 2 ? 10 : 16);     // entries per batch of loads
+  const int tid = threadIdx.x;
+  const size_t hb = (size_t)bh * np * m;
+  const __amdgpu_buffer_rsrc_t ra = head_rsrc(pacc + hb * D, np * m * D * 4);
+  const __amdgpu_buffer_rsrc_t rm = head_rsrc(pmax + hb, np * m * 4);
+  const __amdgpu_buffer_rsrc_t rs = head_rsrc(psum + hb, np * m * 4);
+  float M[IPT], L[IPT];
+  float4 S[IPT];
+  int jj[IPT], qq[IPT];
+#pragma unroll
+  for (int r = 0; r < IPT; ++r) {
+    const int it = min(tid + 512 * r, ITEMS - 1);
+    jj[r] = it / NQ;
+    qq[r] = it % NQ;
+    M[r] = -INFINITY;
+    L[r] = 0.f;
+    S[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int c0 = 0; c0 < np; c0 += NB) {
+    float pm[IPT][NB], ps[IPT][NB];
+    float4 pa[IPT][NB];
+#pragma unroll
+    for (int r = 0; r < IPT; ++r)
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = min(c0 + u, np - 1) * m + min(jj[r], m - 1);
+        pm[r][u] = ld_coh(rm, 4 * e);
+        ps[r][u] = ld_coh(rs, 4 * e);
+        pa[r][u] = ld_coh4(ra, 4 * (e * D + 4 * qq[r]));
+      }
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      float Mb = M[r];
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (c0 + u < np) Mb = fmaxf(Mb, pm[r][u]);
+      // Arguments <= 0.  Entries past a sequence's end are empty (max -inf):
+      // a batch of only those keeps M = Mb = -inf and must not form -inf - -inf.
+      const float sc = M[r] == Mb ? 1.f : __builtin_amdgcn_exp2f(M[r] - Mb);
+      L[r] *= sc;
+      S[r].x *= sc;
+      S[r].y *= sc;
+      S[r].z *= sc;
+      S[r].w *= sc;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        if (c0 + u < np) {
+          const float e = pm[r][u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pm[r][u] - Mb);
+          L[r] += ps[r][u] * e;
+          S[r].x += pa[r][u].x * e;
+          S[r].y += pa[r][u].y * e;
+          S[r].z += pa[r][u].z * e;
+          S[r].w += pa[r][u].w * e;
+        }
+      }
+      M[r] = Mb;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rb = head_rsrc(BV + (size_t)bh * m * D, m * D * 4);
+#pragma unroll
+  for (int r = 0; r < IPT; ++r) {
+    if (tid + 512 * r >= ITEMS) continue;
+    const int j = jj[r], q = qq[r];
+    // A sequence with no keys (length 0) has every entry empty: BV = 0.
+    const bool ok = j < m && M[r] != -INFINITY;
+    const float inv = ok ? 1.f / L[r] : 0.f;
+    const float v[4] = {ok ? S[r].x * inv : 0.f, ok ? S[r].y * inv : 0.f, ok ? S[r].z * inv : 0.f,
+                        ok ? S[r].w * inv : 0.f};
+    if (j < m) st_coh4(rb, 4 * (j * D + 4 * q), make_float4(v[0], v[1], v[2], v[3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hi_lo(v[i], sm.bt[0][(4 * q + i) * LD + j], sm.bt[1][(4 * q + i) * LD + j]);
+  }
+}
+
+// Z of head bh (device-coherent loads) -> the Z planes.
+template <int MP, int D>
+__device__ __forceinline__ void load_z_planes(FinishSmem<MP, D>& sm, int bh, const float* __restrict__ Z, int m) {
+  constexpr int LD = FinishSmem<MP, D>::LD;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rz = head_rsrc(Z + (size_t)bh * m * m, m * m * 4);
+#pragma unroll
+  for (int k = 0; k < (MP * MP / 4 + 511) / 512; ++k) {
+    const int e4 = tid + 512 * k;
+    if (e4 >= MP * MP / 4) break;
+    const int r = e4 / (MP / 4), c4 = 4 * (e4 % (MP / 4));
+    float v[4];
+    if (m == MP) {
+      const float4 x = ld_coh4(rz, 4 * (r * m + c4));
+      v[0] = x.x;
+      v[1] = x.y;
+      v[2] = x.z;
+      v[3] = x.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = ld_coh(rz, 4 * (min(r, m - 1) * m + min(c4 + i, m - 1)));
+        v[i] = (r < m && c4 + i < m) ? x : 0.f;
+      }
+    }
+    uint2 hv, lv;
+    split_pair(v[0], v[1], hv.x, lv.x);
+    split_pair(v[2], v[3], hv.y, lv.y);
+    *reinterpret_cast<uint2*>(&sm.z[0][r * LD + c4]) = hv;
+    *reinterpret_cast<uint2*>(&sm.z[1][r * LD + c4]) = lv;
+  }
+}
+
+// BV of head bh (device-coherent loads) -> the BV^T planes.
+template <int MP, int D>
+__device__ __forceinline__ void load_bv_planes(FinishSmem<MP, D>& sm, int bh, const float* __restrict__ BV, int m) {
+  constexpr int LD = FinishSmem<MP, D>::LD, NQ = D / 4;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rb = head_rsrc(BV + (size_t)bh * m * D, m * D * 4);
+#pragma unroll
+  for (int k = 0; k < (MP * NQ + 511) / 512; ++k) {
+    const int it = tid + 512 * k;
+    if (it >= MP * NQ) break;
+    const int j = it / NQ, q = it % NQ;
+    const float4 x = ld_coh4(rb, 4 * (min(j, m - 1) * D + 4 * q));
+    const float v[4] = {j < m ? x.x : 0.f, j < m ? x.y : 0.f, j < m ? x.z : 0.f, j < m ? x.w : 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hi_lo(v[i], sm.bt[0][(4 * q + i) * LD + j], sm.bt[1][(4 * q + i) * LD + j]);
+  }
+}
+
+// W = Z BV from the planes -> W (fp32) and the W^T bf16 plane.  8 waves; tile
+// (row tile ti of landmarks, feature tile nd): lane (c, g) ends with
+// W[16 ti + 4g + i][16 nd + c].
+template <int MP, int D>
+__device__ __forceinline__ void form_w(const FinishSmem<MP, D>& sm, int bh, float* __restrict__ W,
+                                       uint16_t* __restrict__ wt_hi, int m) {
+  constexpr int LD = FinishSmem<MP, D>::LD, NTR = MP / 16, NTF = D / 16, KC = MP / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = wave; t < NTR * NTF; t += 8) {
+    const int ti = t % NTR, nd = t / NTR;
+    f32x4_t acc = zero4();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      B8 ah, al, bh8, bl8;
+      const int oa = (16 * ti + c) * LD + 32 * kc + 8 * g, ob = (16 * nd + c) * LD + 32 * kc + 8 * g;
+      ah.q = *reinterpret_cast<const uint4*>(&sm.z[0][oa]);
+      al.q = *reinterpret_cast<const uint4*>(&sm.z[1][oa]);
+      bh8.q = *reinterpret_cast<const uint4*>(&sm.bt[0][ob]);
+      bl8.q = *reinterpret_cast<const uint4*>(&sm.bt[1][ob]);
+      acc = mfma3(ah, al, bh8, bl8, acc);
+    }
+    const int f = 16 * nd + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * ti + 4 * g + i;
+      if (r < m) W[((size_t)bh * m + r) * D + f] = acc[i];
+    }
+    // Landmarks 16 ti + 4g .. +3 sit at positions 32 (ti / 2) + 8g + 4 (ti % 2) .. +3.
+    const size_t o = ((size_t)bh * D + f) * MP + 32 * (ti >> 1) + 8 * g + 4 * (ti & 1);
+    *reinterpret_cast<uint2*>(&wt_hi[o]) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
   }
 }
 
@@ -1160,17 +1435,25 @@ struct LandmarkPassArgs {
   const float* conv_w;
   uint4* cwop;
   const int* lens;  // tokens per sequence, or nullptr
+  // With the pseudoinverse in the launch: per-head arrival counters ([0, bhn):
+  // key blocks; [bhn, 2 bhn): Z and BV complete), zero at the start, and the
+  // finish's outputs.
+  unsigned* sync;
+  float *BV, *W;
+  uint16_t* wt_hi;
+  int bhn;
   int n, heads, m, chunk, nchunks, iters, npinv, nconv, conv_total, conv_k;
   float sl2e;
 };
 
-template <int PMP, typename B>
+template <int PMP, int D, typename B>
 union LandmarkPassSmem {
   PinvSmemE<PMP> p;
+  FinishSmem<PMP, D> f;
   B b[2];
 };
-template <typename B>
-union LandmarkPassSmem<0, B> {
+template <int D, typename B>
+union LandmarkPassSmem<0, D, B> {
   B b[2];
 };
 
@@ -1178,12 +1461,27 @@ union LandmarkPassSmem<0, B> {
 template <typename IO, int D, int NTW, int PMP, bool SAVE>
 __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   using T = typename IO::T;
-  __shared__ LandmarkPassSmem<PMP, BvSmem<IO, D>> sm;
+  constexpr bool FOLD = PMP > 0;  // the split-n finish runs in this launch
+  __shared__ LandmarkPassSmem<PMP, D, BvSmem<IO, D>> sm;
+  __shared__ unsigned last;
   int blk = blockIdx.x;
-  if constexpr (PMP > 0) {
+  if constexpr (FOLD) {
     if (blk < a.npinv) {
+      static_assert(sizeof(sm.f.z) == sizeof(sm.p.e), "the Z planes of the finish alias the E planes");
       pinv_head<PMP, D, SAVE>(sm.p, blk, a.qt_hi, a.qt_lo, a.kt_hi, a.kt_lo, a.A, a.Z, a.m, a.iters, a.zsave,
-                              a.zmp);
+                              a.zmp, sm.f.z);
+      // Z complete (every lane's stores done): arrive; the second to arrive
+      // (this block or the head's last key block, with BV) forms W.
+      wait_stores();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        last = __hip_atomic_fetch_add(&a.sync[a.bhn + blk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u;
+      __syncthreads();
+      if (last) {
+        load_bv_planes<PMP, D>(sm.f, blk, a.BV, a.m);
+        __syncthreads();
+        form_w<PMP, D>(sm.f, blk, a.W, a.wt_hi, a.m);
+      }
       return;
     }
     blk -= a.npinv;
@@ -1196,9 +1494,32 @@ __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   blk -= a.nconv;
   // Key blocks: chunks 2 j and 2 j + 1 of a head, one per group of 4 waves.
   const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 8;
-  bv_chunk<IO, D, NTW>(sm.b[grp], 2 * (blk % half) + grp, bh, static_cast<const T*>(a.K),
-                       static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
-                       seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+  bv_chunk<IO, D, NTW, FOLD>(sm.b[grp], reinterpret_cast<float*>(&sm), 2 * (blk % half) + grp, bh,
+                             static_cast<const T*>(a.K), static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax,
+                             a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+  if constexpr (FOLD) {
+    static_assert(sizeof(float) * 4 * (D / 16 * 4 + 2) * 64 <= sizeof(sm), "the pair exchange fits the LDS");
+    // The head's last key block to arrive combines its partials into BV,
+    // then arrives at the head's second counter; the second to arrive (this
+    // block or the pseudoinverse block, with Z) forms W.
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&a.sync[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(half - 1);
+    __syncthreads();
+    if (!last) return;
+    combine_bv<PMP, D>(sm.f, bh, a.pacc, a.pmax, a.psum, a.BV, a.m, half);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&a.sync[a.bhn + bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u;
+    __syncthreads();
+    if (!last) return;
+    load_z_planes<PMP, D>(sm.f, bh, a.Z, a.m);
+    __syncthreads();
+    form_w<PMP, D>(sm.f, bh, a.W, a.wt_hi, a.m);
+  }
 }
 
 // Finish of the split-n pass, one block per (16-feature slice, head):
@@ -1390,9 +1711,8 @@ static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
   KernelTimer kt_("segment_mean", s);
   k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
                                                          w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo, p.lens,
-                                                         p.heads, p.n,
-                                                         p.m, w.mpa,
-                                                         kLog2e / sqrtf((float)D));
+                                                         p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D),
+                                                         w.sync, 2 * BH);
 }
 
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
@@ -1454,6 +1774,8 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
 
 bool pinv_in_landmark_pass(const Problem& p) { return p.bf16 && p.m <= 64; }
 
+int forward_partials(const Problem& p, const Ws& w) { return pinv_in_landmark_pass(p) ? w.nchunks / 2 : w.nchunks; }
+
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
   if (pinv_in_landmark_pass(p)) return hipSuccess;
   return p.bf16 ? pinv_t<3>(p, w, s) : pinv_t<6>(p, w, s);
@@ -1494,6 +1816,11 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.nconv = ceil_div(a.conv_total, 512);
   a.conv_k = p.conv_k;
   a.sl2e = kLog2e / sqrtf((float)D);
+  a.sync = w.sync;
+  a.BV = w.BV;
+  a.W = w.W;
+  a.wt_hi = w.wt_hi;
+  a.bhn = BH;
   const int grid = a.npinv + a.nconv + (w.nchunks / 2) * BH;
   KernelTimer kt_("landmark_pass", s);
   if constexpr (PMP > 0) {
@@ -1531,6 +1858,7 @@ hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {
 }
 
 hipError_t stage_bv_finish(const Problem& p, const Ws& w, hipStream_t s) {
+  if (pinv_in_landmark_pass(p)) return hipSuccess;  // folded into the landmark pass
   const int BH = p.batch * p.heads;
   KernelTimer kt_("bv_finish", s);
   if (p.m <= 64 && p.bf16)

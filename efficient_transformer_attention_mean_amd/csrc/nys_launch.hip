@@ -35,6 +35,7 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   long long want = 2 * ((256 - (BH < 256 ? BH : 256)) / BH);
   long long maxch = cdiv(n, 64);
   long long nch = want < 1 ? 1 : (want > maxch ? maxch : want);
+  if (nch > 32) nch = 32;  // bounds the partials one block combines per head
   long long chunk = cdiv(cdiv(n, nch), 64) * 64;
   nch = cdiv(n, chunk);
   L->nchunks = (int)(nch + (nch & 1));
@@ -68,6 +69,7 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   L->wt_hi = take((size_t)BH * d * L->mpa * 2);
   L->wt_lo = take((size_t)BH * d * L->mpa * 2);
   L->cwop = take((size_t)heads * d * 4 * 9 * 16);
+  L->sync = take((size_t)BH * 2 * 4);
   L->total = off;
   return true;
 }
@@ -94,6 +96,7 @@ Ws resolve(const WsLayout& L, char* b) {
   w.wt_hi = reinterpret_cast<uint16_t*>(b + L.wt_hi);
   w.wt_lo = reinterpret_cast<uint16_t*>(b + L.wt_lo);
   w.cwop = reinterpret_cast<uint4*>(b + L.cwop);
+  w.sync = reinterpret_cast<unsigned*>(b + L.sync);
   w.nchunks = L.nchunks;
   w.chunk = L.chunk;
   w.mpa = L.mpa;
