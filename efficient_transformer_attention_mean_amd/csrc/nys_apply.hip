@@ -49,7 +49,14 @@ struct ApplyLayout {
   static constexpr int HALO = KW == 33 ? 16 : 0;
   static constexpr int VCOLS = kTQ + 2 * HALO;
   static constexpr bool STAGE = KW == 1 || KW == 33;  // V rows staged in LDS; the skip goes through Ot
-  static constexpr int VP = VCOLS + 4;  // Vt row pitch (elements; 8/16-byte aligned rows)
+  // Matrix-core skip (bf16, up to 33 taps): row pitch 56 dwords (8 x odd)
+  // plus 8 dwords before every group of 8 feature rows (vt_row), so that
+  // both the staging writes (8 features 8 apart, 4 row groups per half wave)
+  // and the skip's operand reads (8 consecutive features, 4 row groups) hit
+  // 64 distinct LDS banks.  Otherwise a plain pitch.
+  static constexpr bool PADG = IO::kBf16 && KW == 33;
+  static constexpr int VP = PADG ? 112 : VCOLS + 4;  // Vt row pitch (elements; 8/16-byte aligned rows)
+  static constexpr int VTE = D * VP + (PADG ? 16 * (D / 8) : 0);  // Vt elements
   static constexpr int OP = D + 4;      // Ot row pitch (floats)
   static constexpr int KP = D + 8;      // Kt plane row pitch (bf16): 16-byte reads of 16 rows hit distinct banks
   static constexpr int WP = MPA + 8;    // W^T plane row pitch (bf16)
@@ -61,7 +68,7 @@ struct ApplyLayout {
   static constexpr bool KWL = ATT && 2 * NPL * (MPA * KP + D * WP) <= 72 * 1024;
   static constexpr int OT = 0;
   static constexpr int VT = OT + (STAGE ? 4 * kTQ * OP : 0);
-  static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * D * VP : 0);
+  static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * VTE : 0);
   static constexpr int WT = KT + (KWL ? 2 * NPL * MPA * KP : 0);
   static constexpr int BYTES = WT + (KWL ? 2 * NPL * D * WP : 0) + 16;
   // V tile loads: task = 4 rows x one 16-byte chunk.
@@ -71,6 +78,12 @@ struct ApplyLayout {
   static constexpr int NTK = STAGE ? (TASKS + 255) / 256 : 1;
   static constexpr int QW = IO::kBf16 ? 1 : 2;  // 16-byte words per 8 head-dim elements
 };
+
+// First element of feature f's Vt row.
+template <typename LY>
+__device__ __forceinline__ int vt_row(int f) {
+  return f * LY::VP + (LY::PADG ? 16 * (f >> 3) : 0);
+}
 
 // Issues the loads of the V rows [t0 - HALO, t0 + 64 + HALO) of one head into
 // registers; rows outside the head read as zero (buffer range check).  Every
@@ -254,8 +267,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                         __builtin_amdgcn_perm(w3[dw], w2[dw], 0x05040100u));
             const uint2 hi = make_uint2(__builtin_amdgcn_perm(w1[dw], w0[dw], 0x07060302u),
                                         __builtin_amdgcn_perm(w3[dw], w2[dw], 0x07060302u));
-            *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw) * VP + 4 * rq]) = lo;
-            *reinterpret_cast<uint2*>(&vt[(8 * oc + 2 * dw + 1) * VP + 4 * rq]) = hi;
+            const int f = 8 * oc + 2 * dw;
+            *reinterpret_cast<uint2*>(&vt[vt_row<LY>(f) + 4 * rq]) = lo;
+            *reinterpret_cast<uint2*>(&vt[vt_row<LY>(f + 1) + 4 * rq]) = hi;
           }
         } else {
           const float4 r0 = __builtin_bit_cast(float4, vr[k][0]), r1 = __builtin_bit_cast(float4, vr[k][1]);
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         const int f = fg * 16 + b;
         // B_s for lane column j = q4: Vt[f][rb*16 + 4(j + s) .. +3];
         // consecutive row blocks share 5 of 9 operands.
-        const T* vf = &vt[f * VP];
+        const T* vf = &vt[vt_row<LY>(f)];
         bf16x4_t bw[kConvNS + 4 * (NRB - 1)];
 #pragma unroll
         for (int st = 0; st < kConvNS + 4 * (NRB - 1); ++st)
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     // 32-landmark chunk in the order {4g..4g+3, 16+4g..16+4g+3}, the order
     // this lane holds its query's probabilities in.  Row c of tile nd is
     // feature (c/4)*FPG + 4nd + c%4, so that a lane's output features are
-    // contiguous.
+    // contiguous; in LDS that feature's row is 16 nd + c.
     const uint16_t* wth = LY::KWL ? wp : wt_hi + (size_t)bh * D * MPA;
     const uint16_t* wtl = LY::KWL ? wp + D * WP : wt_lo + (size_t)bh * D * MPA;
     constexpr int WPI = LY::KWL ? WP : MPA;
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       }
 #pragma unroll
       for (int nd = 0; nd < ND; ++nd) {
-        const int frow = (c >> 2) * FPG + 4 * nd + (c & 3);
+        const int frow = LY::KWL ? 16 * nd + c : (c >> 2) * FPG + 4 * nd + (c & 3);
         const int off = frow * WPI + kk * 32 + 8 * g;
         B8 wh, wl;
         wh.q = *reinterpret_cast<const uint4*>(wth + off);
@@ -540,7 +554,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                               reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
         for (int e = tid; e < LY::NPL * D * MPA / 8; e += 256) {
           const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
-          *reinterpret_cast<uint4*>(wp + (pl * D + r) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
+          // Feature r = a FPG + 4 nd + b sits in row 16 nd + 4a + b, so that the
+          // 16 rows one product step reads are consecutive (distinct banks).
+          const int rr = 16 * ((r % FPG) >> 2) + 4 * (r / FPG) + (r & 3);
+          *reinterpret_cast<uint4*>(wp + (pl * D + rr) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
         }
       }
       if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
