@@ -111,6 +111,54 @@ def blas_threads() -> int:
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
+def measured_copy_gbs(torch, dev, stream) -> float:
+    """Device copy bandwidth (GB/s, bytes read + written) of a plain 256 MiB
+    fp32 copy, best of five timed launches: the practical ceiling the HBM
+    fraction is also quoted against."""
+    src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    return 2 * 256 * 2 ** 20 / best / 1e9
+
+
+def single_thread_oracle(wl, host0, lengths, budget_s: float):
+    """Tokens/s of the oracle with its BLAS limited to one thread, on the
+    first (batch, head) slice of the workload (the oracle's work is per
+    slice), or None where threadpoolctl is missing."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        return None
+    from oracle import nystrom_attention
+    q, k, v = (host0[x][:1, :1] for x in ("Q", "K", "V"))
+    w = None if host0["conv_w"] is None else host0["conv_w"][:1]
+    ln = None if lengths is None else lengths[:1]
+    rows = wl.n if ln is None else min(max(ln[0], 0), wl.n)
+    reps = 0
+    with threadpool_limits(limits=1, user_api="blas"):
+        c0 = time.perf_counter()
+        while True:
+            nystrom_attention(q, k, v, wl.m, wl.iters, w, lengths=ln)
+            reps += 1
+            if time.perf_counter() - c0 >= budget_s:
+                break
+        dt = time.perf_counter() - c0
+    # A token of the workload needs every head's work: one slice covers
+    # `rows` tokens of one head, so whole-workload tokens/s divides by heads.
+    return {"value": round(rows * reps / dt / wl.heads, 1), "unit": "tokens/s", "cores": 1,
+            "sample": f"{reps} call(s) on one (batch, head) slice, n={wl.n}, {dt:.1f} s, "
+                      f"scaled to whole tokens ({wl.heads} heads)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,7 +209,7 @@ def main() -> int:
         if len(lengths) != wl.batch:
             print(f"--lengths needs {wl.batch} values for workload {wl.name}", file=sys.stderr)
             return 2
-        eff = [min(max(x, wl.m), wl.n) for x in lengths]
+        eff = [min(max(x, 0), wl.n) for x in lengths]
     token_rows = sum(eff) * wl.heads
     # Read Q, K, V token rows once, write every row of O once, plus the filters.
     io_bytes = wl.compulsory_bytes() - 3 * (wl.batch * wl.n * wl.heads - token_rows) * wl.d * wl.elem_bytes
@@ -274,6 +322,19 @@ def main() -> int:
         for _ in range(3):
             torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
+    copy_gbs = measured_copy_gbs(torch, dev, stream)
+    if roof is not None and roof["unit"] == "GB/s":
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs, 4)
+    if roof is not None:
+        # The committed kernel trace of this workload, when made from these
+        # sources: its mean duration excludes the dispatch and completion
+        # time that the events around each launch include.
+        from efficient_transformer_attention_mean_amd.profiling import read_kernel_mean_us
+        traced = read_kernel_mean_us(os.path.join(ROOT, "profiles", f"kernels_{wl.name}.txt"), roof["kernel"])
+        if traced:
+            roof["traced_avg_us"] = traced
+            if roof["unit"] == "GB/s":
+                roof["traced_frac"] = round(roof["algorithmic_bytes"] / (traced * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -284,6 +345,8 @@ def main() -> int:
                    **({} if lengths is None else {"lengths": lengths})},
         "hbm_roofline_frac_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
         "compulsory_bytes": io_bytes,
+        "measured_copy_gbs": round(copy_gbs, 1),
+        "frac_of_measured_copy_end_to_end": round(io_bytes / (ms_per_step / 1e3) / (copy_gbs * 1e9), 4),
         "per_call_us": {"median": round(float(np.median(per_call_us)), 2),
                         "p10": round(float(np.percentile(per_call_us, 10)), 2),
                         "p90": round(float(np.percentile(per_call_us, 90)), 2)},
@@ -312,6 +375,11 @@ def main() -> int:
                 "sample": f"{reps} whole call(s) of the workload (batch {wl.batch} x {wl.heads} heads, n={wl.n}"
                           f"{'' if lengths is None else ', lengths ' + args.lengths}), "
                           f"fp64 NumPy, {cpu_s:.1f} s, host has {os.cpu_count()} logical CPUs"}
+            # The same oracle with its BLAS held to one thread, on one
+            # (batch, head) slice of set 0 repeated within a third of the budget.
+            one = single_thread_oracle(wl, host0, lengths, args.cpu_seconds / 3)
+            if one is not None:
+                result["cpu_baseline"]["single_thread"] = one
         if not args.no_parity:
             Q, K, V, W, O = bufs[0]
             step(0)  # recompute set 0 into its own output

@@ -20,6 +20,12 @@ Usage::
     python -m efficient_transformer_attention_mean_amd.profiling stats CSV --command CMD --out FILE
     python -m efficient_transformer_attention_mean_amd.profiling traffic --fetch DIR --write DIR \\
         --fetch-command CMD --write-command CMD --out FILE
+    python -m efficient_transformer_attention_mean_amd.profiling counters --run DIR CMD [--run DIR CMD ...] \\
+        --out FILE
+
+A third summary, ``counters``, lists the mean of every counter per kernel
+from any number of ``--pmc`` runs with figures derived from them (matrix-core
+busy share, L2 hit rate, LDS bank conflicts).
 """
 from __future__ import annotations
 
@@ -126,6 +132,72 @@ def traffic_summary(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: s
                      ["    " + s for s in lines]) + "\n"
 
 
+# Derived figures of a counter summary: (label, numerator, denominator,
+# factor).  SQ_BUSY_CU_CYCLES sums busy cycles over compute units and
+# SQ_VALU_MFMA_BUSY_CYCLES busy cycles over the 4 SIMDs of each, so their ratio
+# over 4 is the matrix cores' busy share while the kernel occupies the CUs.
+DERIVED = [
+    ("MFMA busy (% of SIMD cycles while CUs busy)", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", 25.0),
+    ("L2 hit rate (%)", "TCC_HIT_sum", "TCC_HIT_sum+TCC_MISS_sum", 100.0),
+    ("LDS bank-conflict cycles per LDS instruction", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", 1.0),
+    ("LDS bank-conflict cycles (% of CU busy cycles)", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", 100.0),
+    ("LDS wait (% of CU busy cycles)", "SQ_WAIT_INST_LDS", "SQ_BUSY_CU_CYCLES", 100.0),
+]
+
+
+def counters_summary(runs: list[tuple[str, str]], title: str, kernels: str | None = None) -> str:
+    """Mean of every counter per kernel over its dispatches, from one or
+    more ``--pmc`` runs (directory, command), plus the DERIVED figures."""
+    per: dict[str, dict[str, list[float]]] = {}
+    for directory, _ in runs:
+        for r in _rows(os.path.join(directory, "**", "*counter_collection.csv")):
+            k = short_name(r["Kernel_Name"])
+            if kernels and not re.search(kernels, k):
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        raise SystemExit("no counter rows")
+    out = [f"# {title}", "", "Commands (run from the repository root; one rocprofv3 pass each):", ""]
+    out += [f"    {cmd}" for _, cmd in runs]
+    out += ["", f"Kernel sources sha256: {sources_digest()}", "",
+            "Counters are means per dispatch, summed over the device's units as rocprofv3 reports them.", ""]
+    for k in sorted(per):
+        cs = {c: statistics.fmean(v) for c, v in per[k].items()}
+        out += [f"## {k}", "", "| counter | mean per dispatch |", "|---|---|"]
+        out += [f"| {c} | {v:.6g} |" for c, v in sorted(cs.items())]
+        rows = []
+        for label, num, den, fac in DERIVED:
+            if num in cs and all(d in cs for d in den.split("+")):
+                dv = sum(cs[d] for d in den.split("+"))
+                if dv > 0:
+                    rows.append(f"| {label} | {fac * cs[num] / dv:.4g} |")
+        if rows:
+            out += ["", "| derived | value |", "|---|---|"] + rows
+        out.append("")
+    return "\n".join(out)
+
+
+def read_kernel_mean_us(path: str, kernel_family: str) -> float | None:
+    """Mean traced duration (us) of a kernel family from a stats summary, or
+    None when the file is missing or was made from other kernel sources."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"Kernel sources sha256: ([0-9a-f]+)", text)
+    if not m or m.group(1) != sources_digest():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] and family(cells[0]) == kernel_family:
+            try:
+                return float(cells[2])
+            except ValueError:
+                return None
+    return None
+
+
 def read_traffic(path: str, kernel_family: str) -> float | None:
     """Scaled bytes per dispatch for a kernel family from a traffic summary,
     or None when the file is missing or was made from other kernel sources."""
@@ -156,9 +228,17 @@ def main(argv=None) -> int:
     t.add_argument("--write-command", required=True)
     t.add_argument("--title", default="HBM traffic per dispatch")
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--run", nargs=2, action="append", metavar=("DIR", "COMMAND"), required=True,
+                   help="directory of one --pmc run and the command that made it (repeatable)")
+    c.add_argument("--kernels", default=None, help="regular expression: keep only matching kernel names")
+    c.add_argument("--title", default="Hardware counters per dispatch")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_summary(a.csv, a.command, a.title)
+    elif a.cmd == "counters":
+        text = counters_summary([tuple(r) for r in a.run], a.title, a.kernels)
     else:
         text = traffic_summary(a.fetch, a.write, a.fetch_command, a.write_command, a.title)
     with open(a.out, "w") as f:

@@ -59,3 +59,43 @@ def test_stats_summary_and_names(tmp_path):
     anon = "void nys::(anonymous namespace)::k_bwd_key_mm<64>(unsigned short const*, float const*)"
     assert profiling.short_name(anon) == "k_bwd_key_mm<64>"
     assert profiling.family(anon) == "bwd_key_mm"
+
+
+def test_stats_mean_lookup_and_guard(tmp_path):
+    p = tmp_path / "run_kernel_stats.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                                          "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow({"Name": APPLY, "Calls": 2, "TotalDurationNs": 44000, "AverageNs": 22000, "Percentage": 100,
+                    "MinNs": 21000, "MaxNs": 23000, "StdDev": 1})
+    out = tmp_path / "kernels.txt"
+    out.write_text(profiling.stats_summary(str(p), "cmd", "t"))
+    assert profiling.read_kernel_mean_us(str(out), "apply") == 22.0
+    assert profiling.read_kernel_mean_us(str(out), "landmark_pass") is None
+    out.write_text(out.read_text().replace(profiling.sources_digest(), "f" * 64))
+    assert profiling.read_kernel_mean_us(str(out), "apply") is None
+
+
+def test_counters_summary_derived_figures(tmp_path):
+    # Two passes: SQ counters in one, L2 counters in the other; the derived
+    # figures combine them per kernel.
+    _write_counters(tmp_path / "a", "SQ_BUSY_CU_CYCLES", {APPLY: [1000.0, 1000.0]})
+    with open(tmp_path / "a" / "run_counter_collection.csv", "a", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerow({"Kernel_Name": APPLY, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": 800.0})
+        w.writerow({"Kernel_Name": APPLY, "Counter_Name": "SQ_LDS_BANK_CONFLICT", "Counter_Value": 150.0})
+        w.writerow({"Kernel_Name": APPLY, "Counter_Name": "SQ_INSTS_LDS", "Counter_Value": 50.0})
+    _write_counters(tmp_path / "b", "TCC_HIT_sum", {APPLY: [30.0]})
+    with open(tmp_path / "b" / "run_counter_collection.csv", "a", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerow({"Kernel_Name": APPLY, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 10.0})
+        w.writerow({"Kernel_Name": FILL, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 10.0})
+    text = profiling.counters_summary([(str(tmp_path / "a"), "cmd a"), (str(tmp_path / "b"), "cmd b")], "t",
+                                      kernels="k_apply")
+    assert "    cmd a" in text and "    cmd b" in text
+    assert "## k_apply<BF16, 64, 4, 33, true>" in text and "FillFunctor" not in text
+    assert "| MFMA busy (% of SIMD cycles while CUs busy) | 20 |" in text  # 800 / (4 x 1000)
+    assert "| L2 hit rate (%) | 75 |" in text
+    assert "| LDS bank-conflict cycles per LDS instruction | 3 |" in text
+    assert "| LDS bank-conflict cycles (% of CU busy cycles) | 15 |" in text
