@@ -10,7 +10,8 @@ namespace nys {
 // Byte offsets of every region in the caller's workspace (256-byte aligned).
 struct WsLayout {
   size_t qt, kt, a, z, bv, w;      // documented fp32 intermediates (NYS_WS_*)
-  size_t z2, x, t, u;              // fp32 pseudoinverse scratch for m > 64
+  size_t z2, x, t, u, v;           // fp32 pseudoinverse scratch for m > 64 (X, T, U; Z ping-pong in v)
+  size_t colp, rsum;               // fp32 m > 64: A's column sums per 16-row block, row sums
   size_t pacc, pmax, psum;         // fp32 split-n partials of softmax(Qt K^T) V
   size_t kt_hi, kt_lo;             // bf16 planes of Kt * log2(e)/sqrt(d), [bh][mpa][d]
   size_t qt_hi, qt_lo;             // bf16 planes of Qt, [bh][mpa][d] (rows m..mpa-1 zero)
@@ -28,7 +29,8 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L);
 // The same regions as device pointers.
 struct Ws {
   float *Qt, *Kt, *A, *Z, *BV, *W;
-  float *Z2, *X, *T, *U;
+  float *Z2, *X, *T, *U, *V;
+  float *colp, *rsum;
   float *pacc, *pmax, *psum;
   uint16_t *kt_hi, *kt_lo, *qt_hi, *qt_lo, *wt_hi, *wt_lo;
   uint4* cwop;

@@ -6,7 +6,7 @@
 //   A = softmax(Qt Kt^T / sqrt d), Z = Lemma-1 iterations from the
 //   Pan-Schreiber start                    -> pinv_head inside k_landmark_pass (m <= 64,
 //                                             bf16 I/O), k_pinv_lds (m <= 64, fp32 I/O) or
-//                                             k_landmark_softmax + k_pinv_start + k_mm chain
+//                                             k_landmark_softmax + a k_mmr chain (m > 64)
 //   B V = softmax(Qt K^T / sqrt d) V       -> bv_chunk inside k_landmark_pass (split over
 //                                             keys, online softmax), then k_bv_finish
 //   W = Z (B V), W^T bf16 planes           -> k_bv_finish
@@ -731,11 +731,15 @@ __device__ __forceinline__ void pinv_head(PinvSmemE<MP>& sm, int bh, const uint1
 // ---------------------------------------------------------------------------
 // Pseudoinverse for 64 < m <= 256, step 1: A rows.  grid (ceil(m/16), batch*heads).
 // Each block computes 16 rows of the scaled scores with the matrix cores,
-// then row softmax in LDS.
+// then row softmax in LDS.  For the starting scale it also writes its rows'
+// sums (rsum[bh][row]) and the column sums over its 16 rows
+// (colp[bh][block][col]); summed in block order they give ||A||_inf and
+// ||A||_1 without atomics.
 template <int PR>
 __global__ __launch_bounds__(256) void k_landmark_softmax(const float* __restrict__ Qt,
                                                           const float* __restrict__ Kt,
-                                                          float* __restrict__ Aout, int m, int d,
+                                                          float* __restrict__ Aout, float* __restrict__ colp,
+                                                          float* __restrict__ rsum, int m, int d,
                                                           float sl2e) {
   __shared__ __align__(16) float S[16][256 + 4];
   const int bh = blockIdx.y, r0 = blockIdx.x * 16, tid = threadIdx.x;
@@ -772,95 +776,237 @@ __global__ __launch_bounds__(256) void k_landmark_softmax(const float* __restric
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) s += shfl_xor(s, o);
   const float inv = 1.f / s;
-  if (r0 + r < m) {
+  const bool live = r0 + r < m;
+  float rs = 0.f;
+  for (int j = sub; j < m; j += 16) {
+    const float a = live ? S[r][j] * inv : 0.f;
+    S[r][j] = a;
+    rs += a;
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) rs += shfl_xor(rs, o);
+  if (live) {
     float* ao = Aout + ((size_t)bh * m + r0 + r) * m;
-    for (int j = sub; j < m; j += 16) ao[j] = S[r][j] * inv;
+    for (int j = sub; j < m; j += 16) ao[j] = S[r][j];
+    if (sub == 0) rsum[(size_t)bh * m + r0 + r] = rs;
   }
-}
-
-// Step 2: Z0 = A^T / (||A||_1 ||A||_inf).  grid (batch*heads).
-__global__ __launch_bounds__(256) void k_pinv_start(const float* __restrict__ A, float* __restrict__ Z0, int m) {
-  __shared__ float red[2][256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const float* a = A + (size_t)bh * m * m;
-  float cs = 0.f, rs = 0.f;
-  if (tid < m) {
-    for (int i = 0; i < m; ++i) {
-      cs += fabsf(a[(size_t)i * m + tid]);
-      rs += fabsf(a[(size_t)tid * m + i]);
-    }
-  }
-  red[0][tid] = cs;
-  red[1][tid] = rs;
   __syncthreads();
-  float n1 = 0.f, ninf = 0.f;
-  for (int i = 0; i < m; ++i) {
-    n1 = fmaxf(n1, red[0][i]);
-    ninf = fmaxf(ninf, red[1][i]);
-  }
-  const float cz = 1.f / (n1 * ninf);
-  float* z = Z0 + (size_t)bh * m * m;
-  for (int e = tid; e < m * m; e += 256) {
-    const int i = e / m, j = e % m;
-    z[e] = cz * a[(size_t)j * m + i];
+  for (int j = tid; j < m; j += 256) {
+    float cs = 0.f;
+#pragma unroll 4
+    for (int rr = 0; rr < 16; ++rr) cs += S[rr][j];
+    colp[((size_t)bh * gridDim.x + blockIdx.x) * m + j] = cs;
   }
 }
 
-// Batched fp32 product with an affine epilogue:
-//   C1 = a1 * (P Q) + d1 * I,  and if C2 != null also C2 = a2 * (P Q) + d2 * I.
-// P: M x K, Q: K x N, row-major, per batch entry strides sP, sQ, sC (elements).
-// grid (ceil(N/64), ceil(M/64), batch); 4 waves, each 16 rows x 64 columns.
-struct MMArgs {
-  const float* P;
-  const float* Q;
-  float* C1;
-  float* C2;
-  int M, N, K;
-  long long sP, sQ, sC;
-  float a1, d1, a2, d2;
+// Step 2 onwards: Z_0 = cz A^T, cz = 1 / (||A||_1 ||A||_inf) (the
+// Pan-Schreiber start), then the Lemma-1 iteration as the pages write it,
+// four dependent products per step:
+//   X = A Z, T = 7X - X X, U = 15X - X T, Z' = (13Z - Z U) / 4,
+// each one launch of batched m x m products on the matrix cores.  (The
+// residual form the m <= 64 blocks use, E = I - A Z carried from step to
+// step, holds I - A Z only to the absolute precision of E; at m = 256 that
+// loses the small singular directions of A Z, so this path recomputes X.)
+// One block = one 64 x 64 output tile of one head and job (4 waves, 16 rows
+// each).  The contraction runs in chunks of 128 whose operand panels are
+// staged in LDS in fp32 (left rows; right operand by columns), and the
+// fragments are split into bf16 parts as they are read (PR = 3: bf16x3;
+// PR = 6: three-way split, fp32-grade).
+enum MmrMode { kMmProduct = 0, kMmZ0 = 1 };
+
+struct MmrJob {
+  int mode;
+  const float *X, *Y;  // left and right operands, [bh][m][m] row-major
+  float* C;            // output
+  const float* F;      // C = alpha (X Y) + beta F (F unused when beta = 0)
+  float alpha, beta;
 };
 
-template <int PR>
-__global__ __launch_bounds__(256) void k_mm(MMArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
-  const int bz = blockIdx.z;
-  const float* P = a.P + bz * a.sP;
-  const float* Qm = a.Q + bz * a.sQ;
-  const int row0 = blockIdx.y * 64 + wave * 16, col0 = blockIdx.x * 64;
-  if (row0 >= a.M) return;
-  f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
-  for (int kc = 0; kc < a.K; kc += 32) {
-    float x[8];
-    const int r = row0 + c;
+struct MmrArgs {
+  MmrJob job;
+  const float *colp, *rsum;  // kMmZ0: A's column sums per 16-row block and row sums
+  int m, nb;
+};
+
+constexpr int kMmrK = 128;           // contraction chunk
+constexpr int kMmrP = kMmrK + 4;     // LDS panel row pitch (floats)
+
+constexpr int kMmrSmem = 2 * 64 * kMmrP * 4;  // the two operand panels
+
+// One chunk of the operand panels in registers: X rows [i0, i0 + 64) x
+// columns [k0, k0 + kMmrK), Y rows [k0, k0 + kMmrK) x columns [j0, j0 + 64),
+// 16-byte loads (m a multiple of 4), zero outside the matrices.  All loads of
+// a chunk are issued before any is used.
+struct MmrChunk {
+  float4 x[8], y[8];
+};
+
+__device__ __forceinline__ void mmr_load(MmrChunk& r, const float* __restrict__ X, const float* __restrict__ Y, int m,
+                                         int i0, int j0, int k0) {
+  const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int kk = kc + 8 * g + q;
-      x[q] = (r < a.M && kk < a.K) ? P[(size_t)r * a.K + kk] : 0.f;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int col = col0 + nt * 16 + c;
-      float y[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kk = kc + 8 * g + q;
-        y[q] = (col < a.N && kk < a.K) ? Qm[(size_t)kk * a.N + col] : 0.f;
-      }
-      acc[nt] = mma_f32<PR>(x, y, acc[nt]);
-    }
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + 256 * u;
+    const int xr = e / (kMmrK / 4), xq = 4 * (e % (kMmrK / 4));  // 64 rows x 32 quads
+    const int yk = e / 16, yq = 4 * (e % 16);                     // 128 rows x 16 quads
+    const bool xin = i0 + xr < m && k0 + xq < m, yin = k0 + yk < m && j0 + yq < m;
+    r.x[u] = xin ? *reinterpret_cast<const float4*>(&X[(size_t)(i0 + xr) * m + k0 + xq]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    r.y[u] = yin ? *reinterpret_cast<const float4*>(&Y[(size_t)(k0 + yk) * m + j0 + yq]) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+}
+
+// The chunk into LDS: X rows [64][kMmrP], Y by columns [64][kMmrP].
+__device__ __forceinline__ void mmr_store(const MmrChunk& r, float* __restrict__ sx, float* __restrict__ sy) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = col0 + nt * 16 + c;
-    if (col >= a.N) continue;
+  for (int u = 0; u < 8; ++u) {
+    const int e = tid + 256 * u;
+    const int xr = e / (kMmrK / 4), xq = 4 * (e % (kMmrK / 4));
+    const int yk = e / 16, yq = 4 * (e % 16);
+    *reinterpret_cast<float4*>(&sx[xr * kMmrP + xq]) = r.x[u];
+    sy[(yq + 0) * kMmrP + yk] = r.y[u].x;
+    sy[(yq + 1) * kMmrP + yk] = r.y[u].y;
+    sy[(yq + 2) * kMmrP + yk] = r.y[u].z;
+    sy[(yq + 3) * kMmrP + yk] = r.y[u].w;
+  }
+}
+
+// The same for any m (element loads), used when m is not a multiple of 4.
+__device__ __forceinline__ void mmr_stage_scalar(float* __restrict__ sx, float* __restrict__ sy,
+                                                 const float* __restrict__ X, const float* __restrict__ Y, int m,
+                                                 int i0, int j0, int k0) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * kMmrK; e += 256) {
+    const int r = e / kMmrK, q = e % kMmrK;
+    sx[r * kMmrP + q] = (i0 + r < m && k0 + q < m) ? X[(size_t)(i0 + r) * m + k0 + q] : 0.f;
+    const int k = e / 64, cc = e % 64;
+    sy[cc * kMmrP + k] = (k0 + k < m && j0 + cc < m) ? Y[(size_t)(k0 + k) * m + j0 + cc] : 0.f;
+  }
+}
+
+template <int PR>
+__global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
+  extern __shared__ __align__(16) float smr[];
+  const int bh = blockIdx.z;
+  const MmrJob& J = a.job;
+  const int m = a.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const size_t hb = (size_t)bh * m * m;
+  if (J.mode == kMmZ0) {
+    // cz = 1 / (max column sum x max row sum); column sums in block order.
+    __shared__ float red[2][4];
+    float cs = 0.f, rs = 0.f;
+    if (tid < m) {
+      for (int b = 0; b < a.nb; ++b) cs += a.colp[((size_t)bh * a.nb + b) * m + tid];
+      rs = a.rsum[(size_t)bh * m + tid];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      cs = fmaxf(cs, shfl_xor(cs, o));
+      rs = fmaxf(rs, shfl_xor(rs, o));
+    }
+    if (lane == 0) {
+      red[0][wave] = cs;
+      red[1][wave] = rs;
+    }
+    __syncthreads();
+    cs = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    rs = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float cz = 1.f / (cs * rs);
+    // Z_0 tile (i0.., j0..) = cz A^T: rows j0.. of A through LDS.
+    float* tr = smr;  // [64][65]
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e / 64, cc = e % 64;
+      tr[r * 65 + cc] = (j0 + r < m && i0 + cc < m) ? J.X[hb + (size_t)(j0 + r) * m + i0 + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int r = e / 64, cc = e % 64;
+      if (i0 + r < m && j0 + cc < m) J.C[hb + (size_t)(i0 + r) * m + j0 + cc] = cz * tr[cc * 65 + r];
+    }
+    return;
+  }
+  float* sx = smr;
+  float* sy = smr + 64 * kMmrP;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+  auto compute = [&](int kn) {
+    for (int kc = 0; kc < kn; kc += 32) {
+      float x[8];
+      const float* px = &sx[(16 * wave + c) * kMmrP + kc + 8 * g];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = px[q];
+      if constexpr (PR == 3) {
+        B8 xh, xl;
+        split8(x, xh, xl);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          float y[8];
+          const float* py = &sy[(16 * nt + c) * kMmrP + kc + 8 * g];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) y[q] = py[q];
+          B8 yh, yl;
+          split8(y, yh, yl);
+          acc[nt] = mfma3(xh, xl, yh, yl, acc[nt]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          float y[8];
+          const float* py = &sy[(16 * nt + c) * kMmrP + kc + 8 * g];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) y[q] = py[q];
+          acc[nt] = mma_f32<PR>(x, y, acc[nt]);
+        }
+      }
+    }
+  };
+  const float* X = J.X + hb;
+  const float* Y = J.Y + hb;
+  // The epilogue's F values of this lane's outputs, loaded up front.
+  float fv[4][4];
+  const bool withf = J.beta != 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = row0 + 4 * g + i;
-      if (r >= a.M) continue;
-      const float v = acc[nt][i];
-      const float diag = (r == col) ? 1.f : 0.f;
-      a.C1[bz * a.sC + (size_t)r * a.N + col] = a.a1 * v + a.d1 * diag;
-      if (a.C2) a.C2[bz * a.sC + (size_t)r * a.N + col] = a.a2 * v + a.d2 * diag;
+      const int r = min(i0 + 16 * wave + 4 * g + i, m - 1), col = min(j0 + 16 * nt + c, m - 1);
+      fv[nt][i] = withf ? J.F[hb + (size_t)r * m + col] : 0.f;
+    }
+  if ((m & 3) == 0) {
+    // m <= 256: at most two chunks, both loaded before the first is used.
+    MmrChunk ra, rb;
+    const bool two = m > kMmrK;
+    mmr_load(ra, X, Y, m, i0, j0, 0);
+    if (two) mmr_load(rb, X, Y, m, i0, j0, kMmrK);
+    mmr_store(ra, sx, sy);
+    __syncthreads();
+    compute(min(kMmrK, m));
+    if (two) {
+      __syncthreads();  // the first chunk's readers are done
+      mmr_store(rb, sx, sy);
+      __syncthreads();
+      compute(m - kMmrK);
+    }
+  } else {
+    for (int k0 = 0; k0 < m; k0 += kMmrK) {
+      if (k0 > 0) __syncthreads();
+      mmr_stage_scalar(sx, sy, X, Y, m, i0, j0, k0);
+      __syncthreads();
+      compute(min(kMmrK, m - k0));
+    }
+  }
+  // Lane (c, g) of wave w holds rows i0 + 16w + 4g + i, column j0 + 16nt + c.
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = j0 + 16 * nt + c;
+    if (col >= m) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = i0 + 16 * wave + 4 * g + i;
+      if (r >= m) continue;
+      J.C[hb + (size_t)r * m + col] = J.alpha * acc[nt][i] + J.beta * fv[nt][i];
     }
   }
 }
@@ -1747,26 +1893,36 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   } else {
     {
       KernelTimer kt_("landmark_softmax", s);
-      k_landmark_softmax<PR><<<dim3(ceil_div(m, 16), BH), 256, 0, s>>>(w.Qt, w.Kt, w.A, m, D, sl2e);
+      k_landmark_softmax<PR><<<dim3(ceil_div(m, 16), BH), 256, 0, s>>>(w.Qt, w.Kt, w.A, w.colp, w.rsum, m, D, sl2e);
     }
-    // Ping-pong so that the last iterate lands in Z.
-    float* zc = (p.iters % 2 == 0) ? w.Z : w.Z2;
-    float* zn = (p.iters % 2 == 0) ? w.Z2 : w.Z;
-    {
-      KernelTimer kt_("pinv_start", s);
-      k_pinv_start<<<BH, 256, 0, s>>>(w.A, zc, m);
-    }
-    const long long st = (long long)m * m;
-    const dim3 grid(ceil_div(m, 64), ceil_div(m, 64), BH);
-    for (int it = 0; it < p.iters; ++it) {
+    const hipError_t attr = ensure_dynamic_smem(reinterpret_cast<const void*>(&k_mmr<PR>), kMmrSmem);
+    if (attr != hipSuccess) return attr;
+    const int T = p.iters, tiles = ceil_div(m, 64);
+    // Z_t lives in Zb[t % 2]; the last, Z_T, in Zb[T % 2] = Z.
+    float* Zb[2] = {T % 2 == 0 ? w.Z : w.V, T % 2 == 0 ? w.V : w.Z};
+    auto launch = [&](int mode, const float* X, const float* Y, float* C, const float* F, float alpha, float beta) {
+      MmrArgs ma;
+      ma.job.mode = mode;
+      ma.job.X = X;
+      ma.job.Y = Y;
+      ma.job.C = C;
+      ma.job.F = F;
+      ma.job.alpha = alpha;
+      ma.job.beta = beta;
+      ma.colp = w.colp;
+      ma.rsum = w.rsum;
+      ma.m = m;
+      ma.nb = ceil_div(m, 16);
       KernelTimer kt_("pinv_mm", s);
-      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.A, zc, w.X, w.T, m, m, m, st, st, st, 1.f, 0.f, -1.f, 7.f});
-      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.X, w.T, w.U, nullptr, m, m, m, st, st, st, -1.f, 15.f, 0.f, 0.f});
-      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{w.X, w.U, w.T, nullptr, m, m, m, st, st, st, -1.f, 13.f, 0.f, 0.f});
-      k_mm<PR><<<grid, 256, 0, s>>>(MMArgs{zc, w.T, zn, nullptr, m, m, m, st, st, st, 0.25f, 0.f, 0.f, 0.f});
-      float* tmp = zc;
-      zc = zn;
-      zn = tmp;
+      k_mmr<PR><<<dim3(tiles, tiles, BH), 256, kMmrSmem, s>>>(ma);
+    };
+    launch(kMmZ0, w.A, nullptr, Zb[0], nullptr, 0.f, 0.f);
+    for (int t = 0; t < T; ++t) {
+      float* Zt = Zb[t % 2];
+      launch(kMmProduct, w.A, Zt, w.X, nullptr, 1.f, 0.f);                  // X = A Z
+      launch(kMmProduct, w.X, w.X, w.T, w.X, -1.f, 7.f);                   // T = 7X - X X
+      launch(kMmProduct, w.X, w.T, w.U, w.X, -1.f, 15.f);                  // U = 15X - X T
+      launch(kMmProduct, Zt, w.U, Zb[(t + 1) % 2], Zt, -0.25f, 3.25f);     // Z' = (13Z - Z U) / 4
     }
   }
   return hipGetLastError();

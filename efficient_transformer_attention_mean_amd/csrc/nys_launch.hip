@@ -59,6 +59,9 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   L->x = take(big ? mm : 0);
   L->t = take(big ? mm : 0);
   L->u = take(big ? mm : 0);
+  L->v = take(big ? mm : 0);
+  L->colp = take(big ? (size_t)BH * cdiv(m, 16) * m * 4 : 0);
+  L->rsum = take(big ? (size_t)BH * m * 4 : 0);
   L->pacc = take((size_t)BH * L->nchunks * m * d * 4);
   L->pmax = take((size_t)BH * L->nchunks * m * 4);
   L->psum = take((size_t)BH * L->nchunks * m * 4);
@@ -86,6 +89,9 @@ Ws resolve(const WsLayout& L, char* b) {
   w.X = reinterpret_cast<float*>(b + L.x);
   w.T = reinterpret_cast<float*>(b + L.t);
   w.U = reinterpret_cast<float*>(b + L.u);
+  w.V = reinterpret_cast<float*>(b + L.v);
+  w.colp = reinterpret_cast<float*>(b + L.colp);
+  w.rsum = reinterpret_cast<float*>(b + L.rsum);
   w.pacc = reinterpret_cast<float*>(b + L.pacc);
   w.pmax = reinterpret_cast<float*>(b + L.pmax);
   w.psum = reinterpret_cast<float*>(b + L.psum);

@@ -123,6 +123,9 @@ EDGE = [
     (1, 2, 1000, 64, 64, 6, 33, "bf16"),  # l = 16, one segment of pad only
     (1, 1, 203, 32, 10, 6, 7, "f32"),     # l = 21, 14 real rows in the last segment
     (1, 2, 777, 128, 96, 8, 33, "f32"),   # m > 64 path, l = 9
+    (1, 1, 500, 32, 75, 6, 5, "f32"),     # m > 64 path, m odd: rows not 16-byte aligned
+    (2, 1, 600, 64, 130, 7, 33, "bf16"),  # m > 64 path, three 64-landmark tiles, m = 2 mod 4
+    (1, 1, 300, 16, 70, 0, 0, "f32"),     # m > 64 path, iters = 0: Z is the start Z0
     (2, 3, 8191, 64, 64, 6, 33, "bf16"),  # headline shape less one row
     (1, 2, 4097, 64, 32, 6, 33, "f32"),   # one real row in the last segment
     (1, 1, 130, 32, 64, 6, 3, "bf16"),    # l = 3: 20 segments of pad only (equal rows in A)
