@@ -64,8 +64,10 @@ struct ApplyLayout {
   // fp32 accumulation (hi plane only), fp32 I/O the three-product split.
   static constexpr int NPL = IO::kBf16 ? 1 : 2;
   // The current head's Kt and W^T planes are kept in LDS when they fit
-  // (KWL), else read from global memory.
-  static constexpr bool KWL = ATT && 2 * NPL * (MPA * KP + D * WP) <= 72 * 1024;
+  // (KWL), else read from global memory: beside the skip's buffers within
+  // 72 KB; without them (no skip staged) within the LDS of a CU.
+  static constexpr int PLANES = 2 * NPL * (MPA * KP + D * WP);
+  static constexpr bool KWL = ATT && PLANES <= (STAGE ? 72 * 1024 : 159 * 1024);
   static constexpr int OT = 0;
   static constexpr int VT = OT + (STAGE ? 4 * kTQ * OP : 0);
   static constexpr int KT = VT + (STAGE ? (int)sizeof(T) * VTE : 0);
@@ -137,7 +139,9 @@ __device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amd
 //     issued.
 // The Q fragments of a tile are likewise loaded two tiles ahead.
 // WPE: waves per SIMD the register allocation is held to (1 = no limit).
-template <typename IO, int D, int NTM, int KW, bool ATT, int WPE>
+// ACC: add the attention to what `out` holds (the skip, written by an
+// earlier launch) instead of overwriting it.
+template <typename IO, int D, int NTM, int KW, bool ATT, int WPE, bool ACC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
                                                const uint16_t* __restrict__ kt_hi,
@@ -515,6 +519,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
     }
     const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, n * D * ES);
     const int base = (row * D + f0) * ES;
+    if constexpr (ACC) {
+      // Rows past the tokens stay zero; rows past n read zero (range check).
+      if (row < nb) {
+        if constexpr (IO::kBf16) {
+          if constexpr (FPG >= 8) {
+#pragma unroll
+            for (int j = 0; j < FPG / 8; ++j) {
+              B8 o8;
+              o8.q = buf_load16(ro, base + 16 * j);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) v[8 * j + q] += bf16_to_f32(o8.h[q]);
+            }
+          } else {
+            const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ro, (unsigned)base, 0, 0));
+            v[0] += __uint_as_float(x.x << 16);
+            v[1] += __uint_as_float(x.x & 0xffff0000u);
+            v[2] += __uint_as_float(x.y << 16);
+            v[3] += __uint_as_float(x.y & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < FPG / 4; ++j) {
+            const float4 x = __builtin_bit_cast(float4, buf_load16(ro, base + 16 * j));
+            v[4 * j] += x.x;
+            v[4 * j + 1] += x.y;
+            v[4 * j + 2] += x.z;
+            v[4 * j + 3] += x.w;
+          }
+        }
+      }
+    }
     if constexpr (IO::kBf16) {
       if constexpr (FPG >= 8) {
 #pragma unroll
@@ -627,7 +662,7 @@ static int multiprocessors() {
   return cus;
 }
 
-template <typename IO, int D, int NTM, int KW, bool ATT>
+template <typename IO, int D, int NTM, int KW, bool ATT, bool ACC = false>
 static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
@@ -635,7 +670,7 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   // CU (LDS ~48 KB) when the registers are held to 168 per lane, without
   // spills; other instantiations keep the compiler's choice.
   constexpr int WPE = (IO::kBf16 && KW == 33 && ATT && D <= 64 && NTM <= 4) ? 3 : 1;
-  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE>;
+  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE, ACC>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
   if (attr != hipSuccess) return attr;
@@ -666,14 +701,37 @@ static hipError_t pick_kw(const Problem& p, const Ws* w, hipStream_t s) {
   return launch_one<IO, D, NTM, -1, ATT>(p, w, s);
 }
 
+// With a skip of up to 33 taps whose fused kernel cannot keep the head's
+// Kt and W^T planes in LDS (they do not fit beside the skip's buffers) but
+// whose attention-only kernel can, the skip runs first as the standalone
+// convolution (out = DConv(V)) and the attention pass adds into out: two
+// more passes over rows of out, against re-reading every plane from L2 for
+// each 64-row tile.
+template <typename IO, int D, int NTM>
+static hipError_t apply_m(const Problem& p, const Ws& w, hipStream_t s) {
+  if constexpr (!ApplyLayout<IO, D, NTM, 33, true>::KWL && ApplyLayout<IO, D, NTM, 0, true>::KWL) {
+    if (p.conv_w && p.conv_k > 1 && p.conv_k <= 33) {
+      hipError_t e;
+      {
+        KernelTimer kt_("dconv", s);
+        e = launch_one<IO, D, 2, 33, false>(p, nullptr, s);
+      }
+      if (e != hipSuccess) return e;
+      KernelTimer kt_("apply", s);
+      return launch_one<IO, D, NTM, 0, true, true>(p, &w, s);
+    }
+  }
+  KernelTimer kt_("apply", s);
+  return pick_kw<IO, D, NTM, true>(p, &w, s);
+}
+
 template <typename IO, int D>
 static hipError_t apply_t(const Problem& p, const Ws& w, hipStream_t s) {
-  KernelTimer kt_("apply", s);
   switch (w.mpa) {  // landmark tiles of 16 = mpa / 16
-    case 32: return pick_kw<IO, D, 2, true>(p, &w, s);
-    case 64: return pick_kw<IO, D, 4, true>(p, &w, s);
-    case 128: return pick_kw<IO, D, 8, true>(p, &w, s);
-    default: return pick_kw<IO, D, 16, true>(p, &w, s);
+    case 32: return apply_m<IO, D, 2>(p, w, s);
+    case 64: return apply_m<IO, D, 4>(p, w, s);
+    case 128: return apply_m<IO, D, 8>(p, w, s);
+    default: return apply_m<IO, D, 16>(p, w, s);
   }
 }
 
