@@ -116,8 +116,11 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
 }
 
 // ---------------------------------------------------------------------------
-// Pseudoinverse for m <= 64: one block (4 waves) per head, every iterate in LDS.
-// Products are bf16x3 on the matrix cores with fp32 accumulation.
+// Pseudoinverse for m <= 64: one block (16 waves) per head, every iterate in LDS.
+// Products are split-bf16 on the matrix cores with fp32 accumulation (PR = 6,
+// the three-way split, for fp32 I/O).
+constexpr int kPinvWaves = 16;  // one 16 x 16 output tile per wave and product at m = 64
+
 template <int MP>
 struct PinvSmem {
   __align__(16) float A[MP][MP + 4];
@@ -136,7 +139,7 @@ __device__ __forceinline__ void lds_mm(const float (*P)[MP + 4], const float (*Q
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   constexpr int NT = MP / 16;
-  for (int t = wave; t < NT * NT; t += 4) {
+  for (int t = wave; t < NT * NT; t += kPinvWaves) {
     const int ti = t / NT, tj = t % NT;  // C rows ti*16.., columns tj*16..
     f32x4_t acc = zero4();
 #pragma unroll
@@ -162,7 +165,7 @@ __device__ __forceinline__ float4 plus_diag(int row, int col0, const f32x4_t& v,
 }
 
 template <int MP, int PR>
-__global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, const float* __restrict__ Kt,
+__global__ __launch_bounds__(64 * kPinvWaves) void k_pinv_lds(const float* __restrict__ Qt, const float* __restrict__ Kt,
                                                   float* __restrict__ Aout, float* __restrict__ Zout, int m,
                                                   int d, float sl2e, int iters, float* __restrict__ zsave,
                                                   int zmp) {
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 
   // Scaled scores Qt Kt^T * log2(e)/sqrt(d); rows/cols >= m are zero padding.
   // Computed as (Kt Qt^T)^T: a lane ends with row ti*16+c, columns tj*16+4g..+3.
-  for (int t = wave; t < NT * NT; t += 4) {
+  for (int t = wave; t < NT * NT; t += kPinvWaves) {
     const int ti = t / NT, tj = t % NT;
     const int rq = ti * 16 + c, rk = tj * 16 + c;
     f32x4_t acc = zero4();
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
   __syncthreads();
 
   // Row softmax over the m real columns; padded rows and columns become 0.
-  {
+  if (tid < 256) {
     constexpr int TPR = 256 / MP;
     const int r = tid / TPR, sub = tid % TPR;
     float mx = -INFINITY;
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
     ninf = fmaxf(ninf, sm.red[1][i]);
   }
   const float cz = 1.f / (n1 * ninf);
-  for (int e = tid; e < MP * MP; e += 256) {
+  for (int e = tid; e < MP * MP; e += 64 * kPinvWaves) {
     const int i = e / MP, j = e % MP;
     sm.Z[i][j] = cz * sm.A[j][i];
   }
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
       // For the backward pass: Z_k, X_k, T1_k = 15I - U, T2_k = 13I - T
       // ([zmp][zmp] fp32 each, zero beyond m).
       float* zs = zsave + ((size_t)bh * iters + it) * 4 * zmp * zmp;
-      for (int e = tid; e < zmp * zmp; e += 256) {
+      for (int e = tid; e < zmp * zmp; e += 64 * kPinvWaves) {
         const int i = e / zmp, j = e % zmp;
         const bool in = i < MP && j < MP;
         const float dg = i == j ? 1.f : 0.f;
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(256) void k_pinv_lds(const float* __restrict__ Qt, 
 
   float* ao = Aout + (size_t)bh * m * m;
   float* zo = Zout + (size_t)bh * m * m;
-  for (int e = tid; e < m * m; e += 256) {
+  for (int e = tid; e < m * m; e += 64 * kPinvWaves) {
     const int i = e / m, j = e % m;
     ao[e] = sm.A[i][j];
     zo[e] = Z[i][j];
@@ -1880,7 +1883,7 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
   const float sl2e = kLog2e / sqrtf((float)D);
   if (m <= 32) {
     KernelTimer kt_("pinv", s);
-    k_pinv_lds<32, PR><<<BH, 256, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
+    k_pinv_lds<32, PR><<<BH, 64 * kPinvWaves, sizeof(PinvSmem<32>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
                                                              p.zmp);
   } else if (m <= 64) {
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pinv_lds<64, PR>),
@@ -1888,7 +1891,7 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
                                                        (int)sizeof(PinvSmem<64>));
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("pinv", s);
-    k_pinv_lds<64, PR><<<BH, 256, sizeof(PinvSmem<64>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
+    k_pinv_lds<64, PR><<<BH, 64 * kPinvWaves, sizeof(PinvSmem<64>), s>>>(w.Qt, w.Kt, w.A, w.Z, m, D, sl2e, p.iters, p.zsave,
                                                              p.zmp);
   } else {
     {
