@@ -182,13 +182,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 
   // Skip filter operands (matrix-core path): one 16-feature group per
   // segment; kept in registers across tiles of one head when a wave has a
-  // single segment.
+  // single segment, or (no attention part, registers to spare) for all of
+  // its segments.
   constexpr int FG = D / 16, RB = kTQ / 16, UPW = FG * RB / 4;
   constexpr int NRB = UPW >= RB ? RB : UPW;  // consecutive row blocks per segment
   constexpr int NSEG = UPW / NRB;
   constexpr bool MMCONV = KW == 33 && IO::kBf16;
-  bf16x4_t ah[kConvNS], al[kConvNS];
-  auto conv_operands = [&](int h, int seg) {
+  constexpr int NSR = (MMCONV && NSEG > 1 && !ATT) ? NSEG : 1;  // operand sets held
+  bf16x4_t ah[NSR][kConvNS], al[NSR][kConvNS];
+  auto conv_operands = [&](int h, int seg, int slot) {
     const int b = lane >> 2, q4 = lane & 3;
     const int f = ((wave * UPW + seg * NRB) / RB) * 16 + b;
     if constexpr (ATT) {
@@ -196,8 +198,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
 #pragma unroll
       for (int st = 0; st < kConvNS; ++st) {
         const uint4 v = src[st];
-        ah[st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.x, v.y));
-        al[st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.z, v.w));
+        ah[slot][st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.x, v.y));
+        al[slot][st] = __builtin_bit_cast(bf16x4_t, make_uint2(v.z, v.w));
       }
     } else {
       const int off = (33 - conv_k) / 2;
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           const float wv = (tt >= 0 && tt < conv_k) ? wl : 0.f;
           uint16_t hi, lo;
           split_hi_lo(wv, hi, lo);
-          ah[st][k] = (short)hi;
-          al[st][k] = (short)lo;
+          ah[slot][st][k] = (short)hi;
+          al[slot][st][k] = (short)lo;
         }
     }
   };
@@ -298,7 +300,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       const int b = lane >> 2, q4 = lane & 3;
 #pragma unroll
       for (int seg = 0; seg < NSEG; ++seg) {
-        if constexpr (NSEG > 1) conv_operands(h, seg);
+        if constexpr (NSEG > 1 && NSR == 1) conv_operands(h, seg, 0);
+        const int sl = NSR > 1 ? seg : 0;
         const int u0 = wave * UPW + seg * NRB;
         const int fg = u0 / RB, rb0 = u0 % RB;
         const int f = fg * 16 + b;
@@ -314,8 +317,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           f32x4_t acc = zero4();
 #pragma unroll
           for (int st = 0; st < kConvNS; ++st) {
-            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(al[st], bw[4 * r + st], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ah[st], bw[4 * r + st], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(al[sl][st], bw[4 * r + st], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ah[sl][st], bw[4 * r + st], acc, 0, 0, 0);
           }
           // Lane (b, q4) holds rows (rb0 + r)*16 + 4*q4 + i of feature f.
           float* dst = &ot[((rb0 + r) * 16 + 4 * q4) * OP + f];
@@ -595,7 +598,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
           *reinterpret_cast<uint4*>(wp + (pl * D + rr) * WP + 8 * cc) = sw[pl][r * (MPA / 8) + cc];
         }
       }
-      if constexpr (MMCONV && NSEG == 1) conv_operands(h, 0);
+      if constexpr (MMCONV && (NSEG == 1 || NSR > 1)) {
+#pragma unroll
+        for (int sg = 0; sg < NSR; ++sg) conv_operands(h, sg, sg);
+      }
       cur = bh;
       // Rare path: settle its loads here so that the counts of the tile loads
       // in flight stay exact past the merge.

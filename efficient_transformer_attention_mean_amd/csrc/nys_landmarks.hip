@@ -1049,7 +1049,8 @@ struct BvStage {
 // j of nchunks / 2 per head, with device-coherent stores (the head's last key
 // block of the same launch reads them).  Otherwise each group writes its own
 // chunk's partial, entry ch of nchunks, with plain stores.
-template <typename IO, int D, int NTW, bool PAIR>
+// NWC: waves per chunk (4: two chunks per 512-thread block; 8: one).
+template <typename IO, int D, int NTW, bool PAIR, int NWC = 4>
 __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, int bh,
                                          const typename IO::T* __restrict__ Kin,
                                          const typename IO::T* __restrict__ Vin, const float* __restrict__ Qt,
@@ -1060,7 +1061,9 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   using SM = BvSmem<IO, D>;
   constexpr int KC = (D + 31) / 32;  // 32-wide k chunks over the head dimension
   constexpr int MD = D / 16;         // 16-row tiles of V^T
-  const int tid = threadIdx.x & 255;  // the chunk's group of 4 waves (two groups per 512-thread block)
+  static_assert(!PAIR || NWC == 4, "pairs are the two 4-wave groups of a block");
+  constexpr int NTH = 64 * NWC;           // threads per chunk
+  const int tid = threadIdx.x & (NTH - 1);  // the chunk's group of waves
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   // Keys [kbeg, kend) of this chunk; nb <= n is the head's number of real
   // keys (chunks past it are empty and leave max -inf, sum 0).
@@ -1102,13 +1105,13 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   // registers while the current tile is computed from LDS.
   constexpr int SLOTS = D / 8;
   constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
-  constexpr int TPT = (TASKS + 255) / 256;         // tasks per thread
+  constexpr int TPT = (TASKS + NTH - 1) / NTH;     // tasks per thread
   constexpr bool DEEP = NTW == 1;
   BvStage<IO> stage[TPT], stage2[DEEP ? TPT : 1];
   auto load_tile = [&](BvStage<IO> (&st)[TPT], int k0) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NTH * u;
       const int rp = e / SLOTS, s8 = (e % SLOTS) * 8;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1125,7 +1128,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   auto store_tile = [&](const BvStage<IO> (&st)[TPT]) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + NTH * u;
       if (e >= TASKS) continue;
       const int rp = e / SLOTS, s8 = (e % SLOTS) * 8;
       B8 kh[2], kl[2], vh[2], vl[2];
@@ -1607,7 +1610,9 @@ union LandmarkPassSmem<0, D, B> {
 };
 
 // PMP: landmarks padded to 32 or 64 for the pseudoinverse blocks, 0 for none.
-template <typename IO, int D, int NTW, int PMP, bool SAVE>
+// CPB: key chunks per block (2: one per group of 4 waves; 1: one chunk on all
+// 8 waves, for m > 128, where 4 waves would hold too many accumulators).
+template <typename IO, int D, int NTW, int PMP, bool SAVE, int CPB = 2>
 __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   using T = typename IO::T;
   constexpr bool FOLD = PMP > 0;  // the split-n finish runs in this launch
@@ -1641,6 +1646,13 @@ __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
     return;
   }
   blk -= a.nconv;
+  if constexpr (CPB == 1) {
+    const int bh = blk / a.nchunks;
+    bv_chunk<IO, D, NTW, false, 8>(sm.b[0], nullptr, blk % a.nchunks, bh, static_cast<const T*>(a.K),
+                                   static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
+                                   seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+    return;
+  }
   // Key blocks: chunks 2 j and 2 j + 1 of a head, one per group of 4 waves.
   const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 8;
   bv_chunk<IO, D, NTW, FOLD>(sm.b[grp], reinterpret_cast<float*>(&sm), 2 * (blk % half) + grp, bh,
@@ -1942,7 +1954,7 @@ hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
 
 static bool conv_uses_ops(const Problem& p) { return p.bf16 && p.conv_w && p.conv_k > 1 && p.conv_k <= 33; }
 
-template <typename IO, int D, int NTW, int PMP>
+template <typename IO, int D, int NTW, int PMP, int CPB = 2>
 static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   const int BH = p.batch * p.heads;
   LandmarkPassArgs a;
@@ -1980,7 +1992,7 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.W = w.W;
   a.wt_hi = w.wt_hi;
   a.bhn = BH;
-  const int grid = a.npinv + a.nconv + (w.nchunks / 2) * BH;
+  const int grid = a.npinv + a.nconv + (CPB == 2 ? w.nchunks / 2 : w.nchunks) * BH;
   KernelTimer kt_("landmark_pass", s);
   if constexpr (PMP > 0) {
     if (p.zsave) {
@@ -1988,7 +2000,7 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
       return;
     }
   }
-  k_landmark_pass<IO, D, NTW, PMP, false><<<grid, 512, 0, s>>>(a);
+  k_landmark_pass<IO, D, NTW, PMP, false, CPB><<<grid, 512, 0, s>>>(a);
 }
 
 template <typename IO, int D>
@@ -2002,7 +2014,7 @@ static void landmark_pass_t(const Problem& p, const Ws& w, hipStream_t s) {
   else if (p.m <= 128)
     landmark_pass_launch<IO, D, 2, 0>(p, w, s);
   else
-    landmark_pass_launch<IO, D, 4, 0>(p, w, s);
+    landmark_pass_launch<IO, D, 2, 0, 1>(p, w, s);  // 8 waves x 2 landmark tiles per chunk
 }
 
 hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {

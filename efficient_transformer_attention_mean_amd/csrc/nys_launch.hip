@@ -32,13 +32,16 @@ bool make_layout(int batch, int heads, int n, int d, int m, WsLayout* L) {
   // one block per CU over 256 CUs together with the one pseudoinverse block
   // per head that shares the launch; chunks are a multiple of the 64-key
   // tile, and their count is even (a trailing chunk may be empty).
-  long long want = 2 * ((256 - (BH < 256 ? BH : 256)) / BH);
+  // For m > 128 a chunk takes a whole block (8 waves) and no pseudoinverse
+  // blocks share the launch.
+  const bool one = m > 128;
+  long long want = one ? 256 / BH : 2 * ((256 - (BH < 256 ? BH : 256)) / BH);
   long long maxch = cdiv(n, 64);
   long long nch = want < 1 ? 1 : (want > maxch ? maxch : want);
   if (nch > 32) nch = 32;  // bounds the partials one block combines per head
   long long chunk = cdiv(cdiv(n, nch), 64) * 64;
   nch = cdiv(n, chunk);
-  L->nchunks = (int)(nch + (nch & 1));
+  L->nchunks = (int)(one ? nch : nch + (nch & 1));
   L->chunk = (int)chunk;
   L->mpa = m <= 32 ? 32 : m <= 64 ? 64 : m <= 128 ? 128 : 256;
   size_t off = 0;
