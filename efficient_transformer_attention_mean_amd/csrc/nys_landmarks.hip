@@ -810,8 +810,8 @@ __global__ __launch_bounds__(256) void k_landmark_softmax(const float* __restric
 // residual form the m <= 64 blocks use, E = I - A Z carried from step to
 // step, holds I - A Z only to the absolute precision of E; at m = 256 that
 // loses the small singular directions of A Z, so this path recomputes X.)
-// One block = one 64 x 64 output tile of one head and job (4 waves, 16 rows
-// each).  The contraction runs in chunks of 128 whose operand panels are
+// One block = one 64 x 64 output tile of one head (8 waves, each 16 rows x
+// 32 columns).  The contraction runs in chunks of 128 whose operand panels are
 // staged in LDS in fp32 (left rows; right operand by columns), and the
 // fragments are split into bf16 parts as they are read (PR = 3: bf16x3;
 // PR = 6: three-way split, fp32-grade).
@@ -841,20 +841,24 @@ constexpr int kMmrSmem = 2 * 64 * kMmrP * 4;  // the two operand panels
 // 16-byte loads (m a multiple of 4), zero outside the matrices.  All loads of
 // a chunk are issued before any is used.
 struct MmrChunk {
-  float4 x[8], y[8];
+  float4 x[4], y[4];
 };
 
-__device__ __forceinline__ void mmr_load(MmrChunk& r, const float* __restrict__ X, const float* __restrict__ Y, int m,
+// Byte offset the buffer range check drops (stores) or reads as zero (loads):
+// masked elements use it instead of a branch per access.
+constexpr int kMmrOut = 0x7ffffff0;
+
+__device__ __forceinline__ void mmr_load(MmrChunk& r, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ry, int m,
                                          int i0, int j0, int k0) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + 256 * u;
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + 512 * u;
     const int xr = e / (kMmrK / 4), xq = 4 * (e % (kMmrK / 4));  // 64 rows x 32 quads
     const int yk = e / 16, yq = 4 * (e % 16);                     // 128 rows x 16 quads
     const bool xin = i0 + xr < m && k0 + xq < m, yin = k0 + yk < m && j0 + yq < m;
-    r.x[u] = xin ? *reinterpret_cast<const float4*>(&X[(size_t)(i0 + xr) * m + k0 + xq]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    r.y[u] = yin ? *reinterpret_cast<const float4*>(&Y[(size_t)(k0 + yk) * m + j0 + yq]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    r.x[u] = __builtin_bit_cast(float4, buf_load16(rx, xin ? 4 * ((i0 + xr) * m + k0 + xq) : kMmrOut));
+    r.y[u] = __builtin_bit_cast(float4, buf_load16(ry, yin ? 4 * ((k0 + yk) * m + j0 + yq) : kMmrOut));
   }
 }
 
@@ -862,8 +866,8 @@ __device__ __forceinline__ void mmr_load(MmrChunk& r, const float* __restrict__ 
 __device__ __forceinline__ void mmr_store(const MmrChunk& r, float* __restrict__ sx, float* __restrict__ sy) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = tid + 256 * u;
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + 512 * u;
     const int xr = e / (kMmrK / 4), xq = 4 * (e % (kMmrK / 4));
     const int yk = e / 16, yq = 4 * (e % 16);
     *reinterpret_cast<float4*>(&sx[xr * kMmrP + xq]) = r.x[u];
@@ -879,7 +883,7 @@ __device__ __forceinline__ void mmr_stage_scalar(float* __restrict__ sx, float* 
                                                  const float* __restrict__ X, const float* __restrict__ Y, int m,
                                                  int i0, int j0, int k0) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < 64 * kMmrK; e += 256) {
+  for (int e = tid; e < 64 * kMmrK; e += 512) {
     const int r = e / kMmrK, q = e % kMmrK;
     sx[r * kMmrP + q] = (i0 + r < m && k0 + q < m) ? X[(size_t)(i0 + r) * m + k0 + q] : 0.f;
     const int k = e / 64, cc = e % 64;
@@ -887,17 +891,23 @@ __device__ __forceinline__ void mmr_stage_scalar(float* __restrict__ sx, float* 
   }
 }
 
+// Grid: one block per (head, output tile), numbered so that each XCD (block
+// L runs on XCD L mod 8) takes a contiguous run of them: a head's tiles share
+// their operand panels through that XCD's L2.
 template <int PR>
-__global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
+__global__ __launch_bounds__(512) void k_mmr(MmrArgs a) {
   extern __shared__ __align__(16) float smr[];
-  const int bh = blockIdx.z;
+  const int tiles = (a.m + 63) / 64;
+  const int G = gridDim.x, L = blockIdx.x, xcd = L & 7, per = G >> 3, rem = G & 7;
+  const int rank = xcd * per + (xcd < rem ? xcd : rem) + (L >> 3);
+  const int bh = rank / (tiles * tiles), tt = rank % (tiles * tiles);
   const MmrJob& J = a.job;
   const int m = a.m, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int i0 = (tt / tiles) * 64, j0 = (tt % tiles) * 64;
   const size_t hb = (size_t)bh * m * m;
   if (J.mode == kMmZ0) {
     // cz = 1 / (max column sum x max row sum); column sums in block order.
-    __shared__ float red[2][4];
+    __shared__ float red[2][8];
     float cs = 0.f, rs = 0.f;
     if (tid < m) {
       for (int b = 0; b < a.nb; ++b) cs += a.colp[((size_t)bh * a.nb + b) * m + tid];
@@ -913,17 +923,22 @@ __global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
       red[1][wave] = rs;
     }
     __syncthreads();
-    cs = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    rs = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    cs = red[0][0];
+    rs = red[1][0];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; ++w2) {
+      cs = fmaxf(cs, red[0][w2]);
+      rs = fmaxf(rs, red[1][w2]);
+    }
     const float cz = 1.f / (cs * rs);
     // Z_0 tile (i0.., j0..) = cz A^T: rows j0.. of A through LDS.
     float* tr = smr;  // [64][65]
-    for (int e = tid; e < 64 * 64; e += 256) {
+    for (int e = tid; e < 64 * 64; e += 512) {
       const int r = e / 64, cc = e % 64;
       tr[r * 65 + cc] = (j0 + r < m && i0 + cc < m) ? J.X[hb + (size_t)(j0 + r) * m + i0 + cc] : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
+    for (int e = tid; e < 64 * 64; e += 512) {
       const int r = e / 64, cc = e % 64;
       if (i0 + r < m && j0 + cc < m) J.C[hb + (size_t)(i0 + r) * m + j0 + cc] = cz * tr[cc * 65 + r];
     }
@@ -931,22 +946,25 @@ __global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
   }
   float* sx = smr;
   float* sy = smr + 64 * kMmrP;
-  f32x4_t acc[4];
+  const int rw = 16 * (wave & 3), ct0 = 2 * (wave >> 2);  // the wave's rows and first column tile
+  f32x4_t acc[2];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
+  for (int nt = 0; nt < 2; ++nt) acc[nt] = zero4();
   auto compute = [&](int kn) {
-    for (int kc = 0; kc < kn; kc += 32) {
+#pragma unroll
+    for (int kc = 0; kc < kMmrK; kc += 32) {
+      if (kc >= kn) break;
       float x[8];
-      const float* px = &sx[(16 * wave + c) * kMmrP + kc + 8 * g];
+      const float* px = &sx[(rw + c) * kMmrP + kc + 8 * g];
 #pragma unroll
       for (int q = 0; q < 8; ++q) x[q] = px[q];
       if constexpr (PR == 3) {
         B8 xh, xl;
         split8(x, xh, xl);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
           float y[8];
-          const float* py = &sy[(16 * nt + c) * kMmrP + kc + 8 * g];
+          const float* py = &sy[(16 * (ct0 + nt) + c) * kMmrP + kc + 8 * g];
 #pragma unroll
           for (int q = 0; q < 8; ++q) y[q] = py[q];
           B8 yh, yl;
@@ -955,9 +973,9 @@ __global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
         }
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < 2; ++nt) {
           float y[8];
-          const float* py = &sy[(16 * nt + c) * kMmrP + kc + 8 * g];
+          const float* py = &sy[(16 * (ct0 + nt) + c) * kMmrP + kc + 8 * g];
 #pragma unroll
           for (int q = 0; q < 8; ++q) y[q] = py[q];
           acc[nt] = mma_f32<PR>(x, y, acc[nt]);
@@ -967,22 +985,25 @@ __global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
   };
   const float* X = J.X + hb;
   const float* Y = J.Y + hb;
-  // The epilogue's F values of this lane's outputs, loaded up front.
-  float fv[4][4];
-  const bool withf = J.beta != 0.f;
+  const int mb = m * m * 4;  // bytes of one head's matrix
+  // The epilogue's F values of this lane's outputs, loaded up front (F is
+  // C's own input only through other launches).
+  float fv[2][4];
+  const __amdgpu_buffer_rsrc_t rf = head_rsrc(J.F ? J.F + hb : J.C + hb, J.F ? mb : 0);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = min(i0 + 16 * wave + 4 * g + i, m - 1), col = min(j0 + 16 * nt + c, m - 1);
-      fv[nt][i] = withf ? J.F[hb + (size_t)r * m + col] : 0.f;
+      const int r = i0 + 16 * (wave & 3) + 4 * g + i, col = j0 + 16 * (2 * (wave >> 2) + nt) + c;
+      fv[nt][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rf, (unsigned)(r < m && col < m ? 4 * (r * m + col) : kMmrOut), 0, 0));
     }
   if ((m & 3) == 0) {
     // m <= 256: at most two chunks, both loaded before the first is used.
     MmrChunk ra, rb;
     const bool two = m > kMmrK;
-    mmr_load(ra, X, Y, m, i0, j0, 0);
-    if (two) mmr_load(rb, X, Y, m, i0, j0, kMmrK);
+    const __amdgpu_buffer_rsrc_t rx = head_rsrc(X, mb), ry = head_rsrc(Y, mb);
+    mmr_load(ra, rx, ry, m, i0, j0, 0);
+    if (two) mmr_load(rb, rx, ry, m, i0, j0, kMmrK);
     mmr_store(ra, sx, sy);
     __syncthreads();
     compute(min(kMmrK, m));
@@ -1000,18 +1021,19 @@ __global__ __launch_bounds__(256) void k_mmr(MmrArgs a) {
       compute(min(kMmrK, m - k0));
     }
   }
-  // Lane (c, g) of wave w holds rows i0 + 16w + 4g + i, column j0 + 16nt + c.
+  // Lane (c, g) of wave w holds rows i0 + 16 (w % 4) + 4g + i, columns
+  // j0 + 16 (2 (w / 4) + nt) + c.  Unconditional stores: elements outside the
+  // matrix go to the dropped offset.
+  const __amdgpu_buffer_rsrc_t rc = head_rsrc(J.C + hb, mb);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int col = j0 + 16 * nt + c;
-    if (col >= m) continue;
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = i0 + 16 * wave + 4 * g + i;
-      if (r >= m) continue;
-      J.C[hb + (size_t)r * m + col] = J.alpha * acc[nt][i] + J.beta * fv[nt][i];
+      const int r = i0 + rw + 4 * g + i, col = j0 + 16 * (ct0 + nt) + c;
+      const float v = J.alpha * acc[nt][i] + J.beta * fv[nt][i];
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rc, (unsigned)(r < m && col < m ? 4 * (r * m + col)
+                                                                                              : kMmrOut), 0, 0);
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1929,7 +1951,7 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
       ma.m = m;
       ma.nb = ceil_div(m, 16);
       KernelTimer kt_("pinv_mm", s);
-      k_mmr<PR><<<dim3(tiles, tiles, BH), 256, kMmrSmem, s>>>(ma);
+      k_mmr<PR><<<tiles * tiles * BH, 512, kMmrSmem, s>>>(ma);
     };
     launch(kMmZ0, w.A, nullptr, Zb[0], nullptr, 0.f, 0.f);
     for (int t = 0; t < T; ++t) {
