@@ -129,6 +129,7 @@ struct PinvSmem {
   float T[MP][MP + 4];
   float U[MP][MP + 4];
   float red[2][MP];
+  float colp[64 * kPinvWaves / MP][MP];  // column sums of A over parts of its rows
 };
 
 // C = P * Qm over MP x MP LDS matrices, computed as C^T = Qm^T P^T so that a
@@ -179,61 +180,102 @@ __global__ __launch_bounds__(64 * kPinvWaves) void k_pinv_lds(const float* __res
 
   // Scaled scores Qt Kt^T * log2(e)/sqrt(d); rows/cols >= m are zero padding.
   // Computed as (Kt Qt^T)^T: a lane ends with row ti*16+c, columns tj*16+4g..+3.
+  // Every fragment load (clamped in bounds, masked) is issued before the
+  // first product.
   for (int t = wave; t < NT * NT; t += kPinvWaves) {
     const int ti = t / NT, tj = t % NT;
     const int rq = ti * 16 + c, rk = tj * 16 + c;
+    float a[4][8], b[4][8];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+      if (32 * kq < d) {
+        load8_masked(kt, rk, m, 32 * kq + 8 * g, d, d, a[kq]);
+        load8_masked(qt, rq, m, 32 * kq + 8 * g, d, d, b[kq]);
+      }
     f32x4_t acc = zero4();
-    for (int kc = 0; kc < d; kc += 32) {
-      float a[8], b[8];
-      load8_masked(kt, rk, m, kc + 8 * g, d, d, a);
-      load8_masked(qt, rq, m, kc + 8 * g, d, d, b);
-      acc = mma_f32<PR>(a, b, acc);
-    }
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+      if (32 * kq < d) acc = mma_f32<PR>(a[kq], b[kq], acc);
     *reinterpret_cast<float4*>(&sm.A[rq][tj * 16 + 4 * g]) =
         make_float4(acc[0] * sl2e, acc[1] * sl2e, acc[2] * sl2e, acc[3] * sl2e);
   }
   __syncthreads();
 
-  // Row softmax over the m real columns; padded rows and columns become 0.
+  // Row softmax over the m real columns (padded rows and columns become 0),
+  // in registers: TPR threads per row, CPT consecutive columns each; the
+  // row sums of A go to red[1].
   if (tid < 256) {
-    constexpr int TPR = 256 / MP;
-    const int r = tid / TPR, sub = tid % TPR;
+    constexpr int TPR = 256 / MP, CPT = MP / TPR;
+    const int r = tid / TPR, j0 = (tid % TPR) * CPT;
+    float v[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u) {
+      const float4 x = *reinterpret_cast<const float4*>(&sm.A[r][j0 + 4 * u]);
+      v[4 * u] = x.x;
+      v[4 * u + 1] = x.y;
+      v[4 * u + 2] = x.z;
+      v[4 * u + 3] = x.w;
+    }
     float mx = -INFINITY;
-    for (int j = sub; j < m; j += TPR) mx = fmaxf(mx, sm.A[r][j]);
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+      if (j0 + q < m) mx = fmaxf(mx, v[q]);
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
     float s = 0.f;
-    for (int j = sub; j < MP; j += TPR) {
-      const float e = (r < m && j < m) ? exp2f(sm.A[r][j] - mx) : 0.f;
-      sm.A[r][j] = e;
-      s += e;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      v[q] = (r < m && j0 + q < m) ? exp2f(v[q] - mx) : 0.f;
+      s += v[q];
     }
 #pragma unroll
     for (int o = 1; o < TPR; o <<= 1) s += shfl_xor(s, o);
-    if (r < m) {
-      const float inv = 1.f / s;
-      for (int j = sub; j < m; j += TPR) sm.A[r][j] *= inv;
+    const float inv = r < m ? 1.f / s : 0.f;
+    float rs = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      v[q] *= inv;
+      rs += v[q];
     }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) rs += shfl_xor(rs, o);
+#pragma unroll
+    for (int u = 0; u < CPT / 4; ++u)
+      *reinterpret_cast<float4*>(&sm.A[r][j0 + 4 * u]) = make_float4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+    if (tid % TPR == 0) sm.red[1][r] = rs;
   }
   __syncthreads();
 
-  // Z0 = A^T / (max column abs sum * max row abs sum).
-  if (tid < MP) {
-    float cs = 0.f, rs = 0.f;
-    for (int i = 0; i < MP; ++i) {
-      cs += fabsf(sm.A[i][tid]);
-      rs += fabsf(sm.A[tid][i]);
+  // Z0 = A^T / (max column abs sum * max row abs sum) (entries are >= 0).
+  // Column sums in parts of RPP rows (fixed order), then over the parts.
+  {
+    constexpr int NPART = 64 * kPinvWaves / MP, RPP = MP / NPART > 0 ? MP / NPART : 1;
+    const int col = tid % MP, part = tid / MP;
+    if (part < NPART && part * RPP < MP) {
+      float cs = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPP; ++rr) cs += sm.A[part * RPP + rr][col];
+      sm.colp[part][col] = cs;
     }
-    sm.red[0][tid] = cs;
-    sm.red[1][tid] = rs;
   }
   __syncthreads();
-  float n1 = 0.f, ninf = 0.f;
-  for (int i = 0; i < MP; ++i) {
-    n1 = fmaxf(n1, sm.red[0][i]);
-    ninf = fmaxf(ninf, sm.red[1][i]);
+  if (wave == 0) {
+    constexpr int NPART = 64 * kPinvWaves / MP;
+    float cs = 0.f, rs = 0.f;
+    if (lane < MP) {
+#pragma unroll
+      for (int pp = 0; pp < NPART; ++pp) cs += sm.colp[pp][lane];
+      rs = sm.red[1][lane];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      cs = fmaxf(cs, shfl_xor(cs, o));
+      rs = fmaxf(rs, shfl_xor(rs, o));
+    }
+    if (lane == 0) sm.red[0][0] = 1.f / (cs * rs);
   }
-  const float cz = 1.f / (n1 * ninf);
+  __syncthreads();
+  const float cz = sm.red[0][0];
   for (int e = tid; e < MP * MP; e += 64 * kPinvWaves) {
     const int i = e / MP, j = e % MP;
     sm.Z[i][j] = cz * sm.A[j][i];
