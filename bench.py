@@ -308,7 +308,10 @@ def main() -> int:
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if tr is None else round(tr),
                     "kernel": dom, "algorithmic_bytes": ab, "avg_us": round(avg_s * 1e6, 3)}
         else:
-            fl = pinv_flops(wl)
+            # The pseudoinverse's flops per call, spread over that call's
+            # launches of the kernel (for m > 64 every launch but the first
+            # runs one m x m product, so this is the average per launch).
+            fl = pinv_flops(wl) / max(launches / args.steps, 1.0)
             achieved = fl / avg_s / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 6), "traffic": None,
