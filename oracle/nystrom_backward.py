@@ -29,6 +29,9 @@ notes):
   landmark j goes to the real rows of segment j, divided by the padded length.
 * The skip filters are shared by the batch: their gradient sums over batch
   entries and positions.
+* Key-padding mask: as in the forward oracle, entry b is the method on its
+  first L_b rows (zero-padded to m rows when L_b < m), so its gradients are
+  the gradients of that problem, and zero on its pad rows.
 
 Parity pins (``tests/test_oracle_backward_pins.py``): central finite
 differences of the forward oracle, closed forms at Q = 0, the exact-attention
@@ -176,19 +179,29 @@ def nystrom_head_backward(Q, K, V, m, iters, dO, w=None):
     return dQ, dK, dV, dw
 
 
-def nystrom_attention_backward(Q, K, V, m, iters, dO, conv_w=None):
+def nystrom_attention_backward(Q, K, V, m, iters, dO, conv_w=None, lengths=None):
     """Batched gradients: Q, K, V, dO of shape (batch, heads, n, d), conv_w
     (heads, d, k) or None.  Returns (dQ, dK, dV, dconv_w or None); dconv_w
-    sums over the batch."""
+    sums over the batch.
+
+    lengths: None, or one sequence length per batch entry, as for the
+    forward oracle's key-padding mask.  Entry b's forward is the method on
+    its first L_b rows alone, so its gradients are those of that shorter
+    problem on rows 0 .. L_b-1 and exactly zero on the pad rows, whose
+    values (and dO there) are never read; an empty entry contributes nothing,
+    to the filter gradient included."""
     Q, K, V, dO = map(_f64, (Q, K, V, dO))
     Bt, H, n, d = Q.shape
-    dQ, dK, dV = (np.empty((Bt, H, n, d)) for _ in range(3))
+    dQ, dK, dV = (np.zeros((Bt, H, n, d)) for _ in range(3))
     dW = None if conv_w is None else np.zeros(np.shape(conv_w))
     for b in range(Bt):
+        L = n if lengths is None else int(min(max(int(lengths[b]), 0), n))
+        if L == 0:
+            continue
         for h in range(H):
             w = None if conv_w is None else _f64(conv_w)[h]
-            dQ[b, h], dK[b, h], dV[b, h], dw = nystrom_head_backward(Q[b, h], K[b, h], V[b, h], m, iters,
-                                                                     dO[b, h], w)
+            dQ[b, h, :L], dK[b, h, :L], dV[b, h, :L], dw = nystrom_head_backward(
+                Q[b, h, :L], K[b, h, :L], V[b, h, :L], m, iters, dO[b, h, :L], w)
             if dw is not None:
                 dW[h] += dw
     return dQ, dK, dV, dW

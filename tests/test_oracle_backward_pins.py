@@ -147,3 +147,34 @@ def test_batched_backward_linear_in_dO_and_sums_filters():
     O = nystrom_attention(Q, K, V, m, 6, w)
     np.testing.assert_allclose(O[1, 0], nystrom_head(Q[1, 0], K[1, 0], V[1, 0], m, 6, w[0])[0], atol=1e-14)
     assert segment_means(Q[0, 0], m).shape == (m, d)
+
+
+@pytest.mark.parametrize("lengths,m", [((7, 12), 4), ((3, 0), 4), ((12, 5), 6)])
+def test_masked_backward_matches_finite_differences(lengths, m):
+    """The masked backward against central differences of the masked forward
+    oracle (a sequence shorter than m, one m does not divide, an empty one),
+    with NaN in every pad row of Q, K, V and dO: the pad rows must not be
+    read, their gradients are exactly zero, and the filter gradient sums the
+    real rows of every entry only."""
+    rng = np.random.default_rng(46 + sum(lengths) + m)
+    Bt, H, n, d, k, iters = 2, 2, 12, 3, 3, 6
+    Q, K, V, dO = (rng.standard_normal((Bt, H, n, d)) for _ in range(4))
+    w = rng.standard_normal((H, d, k)) * 0.3
+    lens = np.array(lengths)
+    pad = np.arange(n)[None, None, :, None] >= lens[:, None, None, None]
+    Qn, Kn, Vn, dOn = (np.where(pad, np.nan, X) for X in (Q, K, V, dO))
+    dQ, dK, dV, dw = nystrom_attention_backward(Qn, Kn, Vn, m, iters, dOn, w, lengths=lens)
+    for G in (dQ, dK, dV):
+        assert np.all(G[np.broadcast_to(pad, G.shape)] == 0.0)
+    assert np.all(np.isfinite(dw))
+
+    def loss(Q_=Q, K_=K, V_=V, w_=w):
+        O = nystrom_attention(Q_, K_, V_, m, iters, w_, lengths=lens)
+        return float((np.where(pad, 0.0, O) * np.where(pad, 0.0, dO)).sum())
+
+    live = ~np.broadcast_to(pad, Q.shape)
+    for G, X, key in ((dQ, Q, "Q_"), (dK, K, "K_"), (dV, V, "V_")):
+        fd = _fd(lambda Y: loss(**{key: Y}), X.copy())
+        assert rel(G[live], fd[live]) < 1e-6
+        assert np.all(np.abs(fd[~live]) < 1e-9)  # the forward does not depend on the pad rows
+    assert rel(dw, _fd(lambda Y: loss(w_=Y), w.copy())) < 1e-6
