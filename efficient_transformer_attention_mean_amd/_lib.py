@@ -31,6 +31,7 @@ EXPORTS = (
     "nystrom_attn_fwd_noalloc",
     "nystrom_attn_bwd_workspace_bytes",
     "nystrom_attn_bwd",
+    "nystrom_attn_bwd_masked",
     "nystrom_attn_fwd_save",
     "nystrom_attn_bwd_saved",
     "nystrom_layer_workspace_bytes",
@@ -71,6 +72,8 @@ def load():
     lib.nystrom_attn_bwd_workspace_bytes.restype = sz
     lib.nystrom_attn_bwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.nystrom_attn_bwd.restype = i
+    lib.nystrom_attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, vp, sz, vp]
+    lib.nystrom_attn_bwd_masked.restype = i
     lib.nystrom_attn_fwd_save.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, sz, vp]
     lib.nystrom_attn_fwd_save.restype = i
     lib.nystrom_attn_bwd_saved.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz, vp]
@@ -156,6 +159,14 @@ def nystrom_attn_bwd(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dco
     return int(load().nystrom_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), _ptr(dO), n, d, m, heads, iters,
                                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dconv_w), batch, conv_k, dtype,
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def nystrom_attn_bwd_masked(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype,
+                            lengths, workspace=None, workspace_bytes=0, stream=None) -> int:
+    return int(load().nystrom_attn_bwd_masked(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), _ptr(dO), n, d, m, heads,
+                                              iters, _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dconv_w), batch, conv_k,
+                                              dtype, _ptr(lengths), _ptr(workspace), workspace_bytes,
+                                              _stream(stream)))
 
 
 def nystrom_attn_fwd_save(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k, dtype, saved, saved_bytes,

@@ -135,11 +135,49 @@ class _NystromAttention(torch.autograd.Function):
         return dQ, dK, dV, dW, None, None
 
 
-def attention_train(Q, K, V, m, iters=6, conv_w=None):
+class _NystromAttentionMasked(torch.autograd.Function):
+    """Under a key-padding mask: forward nystrom_attn_fwd_masked, backward
+    nystrom_attn_bwd_masked (which recomputes the landmark side)."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, conv_w, m, iters, lengths):
+        _conv_k(conv_w, Q.shape[1], Q.shape[3])
+        out = attention(Q, K, V, m, iters, conv_w=conv_w, lengths=lengths)
+        ctx.save_for_backward(Q, K, V, conv_w, lengths)
+        ctx.m, ctx.iters = m, iters
+        return out
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, dO):
+        Q, K, V, conv_w, lengths = ctx.saved_tensors
+        batch, heads, n, d = Q.shape
+        conv_k = _conv_k(conv_w, heads, d)
+        dO = dO.to(Q.dtype).contiguous()
+        dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+        dW = torch.empty_like(conv_w) if conv_w is not None and ctx.needs_input_grad[3] else None
+        nbytes = _lib.nystrom_attn_bwd_workspace_bytes(batch, heads, n, d, ctx.m, ctx.iters, conv_k)
+        if nbytes == 0:
+            raise NystromError(_lib.NYS_EUNSUPPORTED, "nystrom_attn_bwd_workspace_bytes")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+        rc = _lib.nystrom_attn_bwd_masked(Q, K, V, conv_w, dO, n, d, ctx.m, heads, ctx.iters, dQ, dK, dV, dW, batch,
+                                          conv_k, _DTYPES[Q.dtype], lengths, ws, nbytes,
+                                          torch.cuda.current_stream())
+        if rc != _lib.NYS_OK:
+            raise NystromError(rc, "nystrom_attn_bwd_masked")
+        return dQ, dK, dV, dW, None, None, None
+
+
+def attention_train(Q, K, V, m, iters=6, conv_w=None, lengths=None):
     """Nyström attention forward with autograd.  Q, K, V: [batch, heads, n, d]
     (fp32 or bf16, m <= 64); conv_w: fp32 [heads, d, k] (k <= 33) or None.
     Backpropagating through the result runs the library's exact backward
-    pass from the state this forward kept (no recompute)."""
+    pass from the state this forward kept (no recompute).  lengths: None, or
+    a contiguous int32 GPU tensor [batch] of sequence lengths (key-padding
+    mask, as for ``attention``); the backward then recomputes the landmark
+    side, and the gradients of every pad row are zero."""
+    if lengths is not None:
+        return _NystromAttentionMasked.apply(Q, K, V, conv_w, m, iters, lengths)
     return _NystromAttention.apply(Q, K, V, conv_w, m, iters)
 
 

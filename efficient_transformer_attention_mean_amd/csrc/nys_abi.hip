@@ -188,9 +188,10 @@ namespace {
 // The backward entry points: saved = false recomputes the forward's landmark
 // side in `workspace` (allocated when NULL); saved = true takes it from
 // `workspace` as nystrom_attn_fwd_save left it (which must then be given).
+// lengths: device int32 [batch] of sequence lengths, or NULL.
 int backward(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d, int m,
              int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k, int dtype,
-             void* workspace, size_t workspace_bytes, void* stream, bool saved) {
+             void* workspace, size_t workspace_bytes, void* stream, bool saved, const int* lengths = nullptr) {
   try {
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return NYS_EINVAL;
     if (saved && !workspace) return NYS_EINVAL;
@@ -212,6 +213,7 @@ int backward(const void* Q, const void* K, const void* V, const float* conv_w, c
     }
     nys::BwdProblem p{{Q, K, V, conv_w, nullptr, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16}, dO, dQ, dK,
                       dV, conv_w ? dconv_w : nullptr};
+    p.fwd.lens = lengths;
     hipError_t e = nys::launch_backward(p, L, ws, s, !saved);
     if (owned) {
       hipError_t f = hipFreeAsync(ws, s);
@@ -232,6 +234,14 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, workspace,
                   workspace_bytes, stream, false);
+}
+
+int nystrom_attn_bwd_masked(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n,
+                            int d, int m, int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w,
+                            int batch, int conv_k, int dtype, const int* lengths, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, workspace,
+                  workspace_bytes, stream, false, lengths);
 }
 
 int nystrom_attn_fwd_save(const void* Q, const void* K, const void* V, const float* conv_w, int n, int d, int m,

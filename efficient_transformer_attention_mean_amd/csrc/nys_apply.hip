@@ -760,8 +760,9 @@ static hipError_t dconv_t(const Problem& p, hipStream_t s) {
 }
 
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n, int d, int k,
-                        bool bf16, hipStream_t s) {
+                        bool bf16, hipStream_t s, const int* lens) {
   Problem p{nullptr, nullptr, V, conv_w, out, batch, heads, n, d, 1, 0, k, bf16};
+  p.lens = lens;
   hipError_t e;
   switch (d) {
     case 16: e = bf16 ? dconv_t<BF16, 16>(p, s) : dconv_t<F32, 16>(p, s); break;

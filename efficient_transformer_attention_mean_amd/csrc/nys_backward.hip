@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const typename IO::T* __restri
                                                   const typename IO::T* __restrict__ dO,
                                                   const float* __restrict__ Kt, const float* __restrict__ W,
                                                   const float* __restrict__ dqt, typename IO::T* __restrict__ dQ,
-                                                  float* __restrict__ pdw, float* __restrict__ pdkt, int n, int m,
+                                                  float* __restrict__ pdw, float* __restrict__ pdkt,
+                                                  const int* __restrict__ lens, int heads, int n, int m,
                                                   int chunk, int nchunks, float sl2e, float scale) {
   constexpr int P = D + 1;  // LDS pitch of d-wide rows
   constexpr int NE = 64 * D / 256;
@@ -90,10 +91,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const typename IO::T* __restri
   float aw[NE], ak[NE];
 #pragma unroll
   for (int v = 0; v < NE; ++v) aw[v] = ak[v] = 0.f;
-  const int seg = (n + m - 1) / m;
+  // Rows of the sequence (all n without a mask); the segment length is
+  // that of the sequence's own padding to m rows.
+  const int nb = seq_rows(lens, bh / heads, n);
+  const int seg = max(1, (nb + m - 1) / m);
   const float inv_seg = 1.f / (float)seg;
 
-  const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
+  const int rbeg = ch * chunk, rend = min(nb, rbeg + chunk);
   for (int t0 = rbeg; t0 < rend; t0 += kRowTile) {
     __syncthreads();  // previous tile's readers done (and the landmark rows visible)
     for (int e = tid; e < kRowTile * D; e += 256) {
@@ -553,8 +557,9 @@ __global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restric
                                                  const float* __restrict__ dKt, const float* __restrict__ pmax,
                                                  const float* __restrict__ psum, typename IO::T* __restrict__ dK,
                                                  typename IO::T* __restrict__ dV, float* __restrict__ pdqt,
-                                                 float* __restrict__ pdwc, int n, int m, int heads, int conv_k,
-                                                 int chunk, int nchunks, int fchunks, float sl2e, float scale) {
+                                                 float* __restrict__ pdwc, const int* __restrict__ lens, int n,
+                                                 int m, int heads, int conv_k, int chunk, int nchunks, int fchunks,
+                                                 float sl2e, float scale) {
   constexpr int P = D + 1;
   constexpr int NE = 64 * D / 256;
   const int R = conv_k > 0 ? (conv_k - 1) / 2 : 0;
@@ -603,11 +608,13 @@ __global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restric
   float awc[17];  // filter-gradient entries tid + 256 v (d * conv_k <= 128 * 33)
 #pragma unroll
   for (int v = 0; v < 17; ++v) awc[v] = 0.f;
-  const int seg = (n + m - 1) / m;
+  // Keys of the sequence; V and dO rows past them read as zero in the skip.
+  const int nb = seq_rows(lens, bh / heads, n);
+  const int seg = max(1, (nb + m - 1) / m);
   const float inv_seg = 1.f / (float)seg;
   const int r = tid >> 4, jl = tid & 15;
 
-  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  const int kbeg = ch * chunk, kend = min(nb, kbeg + chunk);
   for (int i0 = kbeg; i0 < kend; i0 += kKeyTile) {
     __syncthreads();
     for (int e = tid; e < kKeyTile * D; e += 256) {
@@ -616,7 +623,7 @@ __global__ __launch_bounds__(256) void k_bwd_key(const typename IO::T* __restric
     }
     for (int e = tid; e < HR * D; e += 256) {
       const int rr = e / D, c = e % D, row = i0 - R + rr;
-      const bool in = row >= 0 && row < n;
+      const bool in = row >= 0 && row < nb;
       vv[rr * P + c] = in ? ld<IO>(V + hoff + (size_t)row * D + c) : 0.f;
       gg[rr * P + c] = in ? ld<IO>(dO + hoff + (size_t)row * D + c) : 0.f;
     }
@@ -776,7 +783,8 @@ struct SkipSmem {
 template <int D>
 __global__ __launch_bounds__(4 * D) void k_bwd_skip_grad(const uint16_t* __restrict__ V,
                                                          const uint16_t* __restrict__ dO, float* __restrict__ pdwc,
-                                                         int n, int conv_k, int chunk, int nchunks) {
+                                                         const int* __restrict__ lens, int heads, int n, int conv_k,
+                                                         int chunk, int nchunks) {
   using SM = SkipSmem<D>;
   constexpr int NTH = 4 * D, KPT = 16, RG = 4, WN = KPT + 32;
   constexpr int NV = SM::HR * (D / 8) / NTH, NG = kMmTile * (D / 8) / NTH;
@@ -791,7 +799,10 @@ __global__ __launch_bounds__(4 * D) void k_bwd_skip_grad(const uint16_t* __restr
 #pragma unroll
   for (int t = 0; t < 33; ++t) acc[t] = 0.f;
 
-  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  // Rows of the sequence: V rows past them read as zero, dO rows past them
+  // are not output rows.
+  const int nb = seq_rows(lens, bh / heads, n);
+  const int kbeg = ch * chunk, kend = min(nb, kbeg + chunk);
   // V rows (with the halo) and dO rows of a tile, 16 bytes per load; dO rows
   // past the chunk's end belong to the next chunk and read as zero.  The
   // next tile's are in flight while the current one is computed.
@@ -800,7 +811,7 @@ __global__ __launch_bounds__(4 * D) void k_bwd_skip_grad(const uint16_t* __restr
 #pragma unroll
     for (int l = 0; l < NV; ++l) {
       const int e = tid + NTH * l, rr = e / (D / 8), c8 = (e % (D / 8)) * 8, row = t0 - 16 + rr;
-      vn[l] = (row >= 0 && row < n) ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8)
+      vn[l] = (row >= 0 && row < nb) ? *reinterpret_cast<const uint4*>(V + hoff + (size_t)row * D + c8)
                                     : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -981,8 +992,9 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
                                                     const float* __restrict__ Qt, const float* __restrict__ BV,
                                                     const float* __restrict__ dBVg, const float* __restrict__ pmax, const float* __restrict__ psum,
                                                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                                                    float* __restrict__ pdqt, int n, int m, int skip_in_dv, int chunk,
-                                                    int nchunks, int fchunks, float sl2e, float scale) {
+                                                    float* __restrict__ pdqt, const int* __restrict__ lens, int heads,
+                                                    int n, int m, int skip_in_dv, int chunk, int nchunks, int fchunks,
+                                                    float sl2e, float scale) {
   using SM = KeyMmSmem<D>;
   constexpr int KC = D / 32, ND = D / 16, PER = ND;  // dQt tiles per wave: 4 * ND / 4
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1018,7 +1030,7 @@ __global__ __launch_bounds__(256) void k_bwd_key_mm(const uint16_t* __restrict__
 #pragma unroll
   for (int u = 0; u < PER; ++u) aq[u] = zero4();
 
-  const int kbeg = ch * chunk, kend = min(n, kbeg + chunk);
+  const int kbeg = ch * chunk, kend = min(seq_rows(lens, bh / heads, n), kbeg + chunk);  // keys of the sequence
   // K and V rows of a tile, 16 bytes per load; the next tile's are in flight
   // while the current one is computed.
   constexpr int NL = kMmTile * (D / 8) / 256;
@@ -1141,8 +1153,8 @@ template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ Kt, const float* __restrict__ W,
                                                      uint16_t* __restrict__ dQ, float* __restrict__ pdw,
-                                                     float* __restrict__ pdkt, int n, int m, int chunk, int nchunks,
-                                                     float sl2e, float scale) {
+                                                     float* __restrict__ pdkt, const int* __restrict__ lens, int heads,
+                                                     int n, int m, int chunk, int nchunks, float sl2e, float scale) {
   using SM = RowMmSmem<D>;
   constexpr int KC = D / 32, ND = D / 16, PER = ND;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -1170,7 +1182,7 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
 #pragma unroll
   for (int u = 0; u < PER; ++u) aw[u] = ak[u] = zero4();
 
-  const int rbeg = ch * chunk, rend = min(n, rbeg + chunk);
+  const int rbeg = ch * chunk, rend = min(seq_rows(lens, bh / heads, n), rbeg + chunk);  // rows of the sequence
   // Q and dO rows of a tile, 16 bytes per load; the next tile's are in
   // flight while the current one is computed.
   constexpr int NL = kMmTile * (D / 8) / 256;
@@ -1295,11 +1307,13 @@ __global__ __launch_bounds__(256) void k_bwd_rows_mm(const uint16_t* __restrict_
 // The landmark terms of the matrix-core path, once dQt and dKt are complete:
 // dQ_i += dQt[seg(i)] / l and dK_i += dKt[seg(i)] / l, rows i of the
 // segment of landmark min(i / l, m - 1).  One thread per 16-byte vector of 8
-// bf16 features of dQ and of dK; grid over batch*heads*n*D/8.
+// bf16 features of dQ and of dK; grid over batch*heads*n*D/8.  Rows past a
+// sequence's end are left as they are.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_spread(const float* __restrict__ dqt, const float* __restrict__ dkt,
-                                                    uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, int n,
-                                                    int m, long long total) {
+                                                    uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK,
+                                                    const int* __restrict__ lens, int heads, int n, int m,
+                                                    long long total) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e >= total) return;
   constexpr int V = D / 8;
@@ -1307,7 +1321,9 @@ __global__ __launch_bounds__(256) void k_bwd_spread(const float* __restrict__ dq
   const long long r = e / V;  // bh * n + row
   const int row = (int)(r % n);
   const long long bh = r / n;
-  const int seg = (n + m - 1) / m;
+  const int nb = seq_rows(lens, (int)(bh / heads), n);
+  if (row >= nb) return;
+  const int seg = max(1, (nb + m - 1) / m);
   const float inv_seg = 1.f / (float)seg;
   const size_t so = ((size_t)bh * m + min(row / seg, m - 1)) * D + c8;
   const float4 qa = *reinterpret_cast<const float4*>(dqt + so), qb = *reinterpret_cast<const float4*>(dqt + so + 4);
@@ -1348,6 +1364,22 @@ __global__ __launch_bounds__(256) void k_bwd_dw_finish(const float* __restrict__
   float a = 0.f;
   for (int b = 0; b < batch; ++b) a = chunk_sum(pdwc + ((size_t)(b * heads + h)) * nchunks * dk + e, dk, nchunks, a);
   dw[(size_t)h * dk + e] = a;
+}
+
+// Masked calls: rows past each sequence's end of dQ, dK and dV are zero.
+// One thread per 16-byte vector of a row; grid over batch*heads*n*VPR.
+__global__ __launch_bounds__(256) void k_bwd_zero_pad(uint4* __restrict__ dQ, uint4* __restrict__ dK,
+                                                      uint4* __restrict__ dV, const int* __restrict__ lens, int heads,
+                                                      int n, int vpr, long long total) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const long long r = e / vpr;  // bh * n + row
+  const int row = (int)(r % n), b = (int)(r / n / heads);
+  if (row < seq_rows(lens, b, n)) return;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  dQ[e] = z;
+  dK[e] = z;
+  dV[e] = z;
 }
 
 static int cdivi(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -1472,8 +1504,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("bwd_rows_reduce", s);
     kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const uint16_t*>(p.Q), static_cast<const uint16_t*>(bp.dO),
-                                            w.Kt, w.W, static_cast<uint16_t*>(bp.dQ), F(L.pdw), F(L.pdkt), p.n, p.m,
-                                            L.qchunk, L.nq, sl2e, scale);
+                                            w.Kt, w.W, static_cast<uint16_t*>(bp.dQ), F(L.pdw), F(L.pdkt), p.lens,
+                                            p.heads, p.n, p.m, L.qchunk, L.nq, sl2e, scale);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, false>;
@@ -1482,8 +1514,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     if (attr != hipSuccess) return attr;
     KernelTimer kt_("bwd_rows_reduce", s);
     kern<<<dim3(L.nq, BH), 256, bytes, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(bp.dO), w.Kt, w.W,
-                                            nullptr, nullptr, F(L.pdw), F(L.pdkt), p.n, p.m, L.qchunk, L.nq, sl2e,
-                                            scale);
+                                            nullptr, nullptr, F(L.pdw), F(L.pdkt), p.lens, p.heads, p.n, p.m,
+                                            L.qchunk, L.nq, sl2e, scale);
   }
   // dW, dKt_F and dBV from the partials.
   {
@@ -1535,8 +1567,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
       KernelTimer kt_("bwd_keys", ks);
       kern<<<dim3(L.nk, BH), 256, bytes, ks>>>(static_cast<const uint16_t*>(p.K), static_cast<const uint16_t*>(p.V),
                                                w.Qt, w.BV, F(L.dbv), w.pmax, w.psum, static_cast<uint16_t*>(bp.dK),
-                                               static_cast<uint16_t*>(bp.dV), F(L.pdqt), p.n, p.m, ck > 0 ? 1 : 0,
-                                               L.kchunk, L.nk, forward_partials(p, w), sl2e, scale);
+                                               static_cast<uint16_t*>(bp.dV), F(L.pdqt), p.lens, p.heads, p.n, p.m,
+                                               ck > 0 ? 1 : 0, L.kchunk, L.nk, forward_partials(p, w), sl2e, scale);
     }
     dw_finish(ks);
     if ((e = hipEventRecord(ss->join, ks)) != hipSuccess) return e;
@@ -1562,7 +1594,7 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
       kern<<<dim3(L.nk, BH), 256, bytes, s>>>(static_cast<const T*>(p.K), static_cast<const T*>(p.V),
                                               static_cast<const T*>(bp.dO), p.conv_w, w.Qt, w.BV, F(L.dbv), F(L.dkt),
                                               w.pmax, w.psum, static_cast<T*>(bp.dK), static_cast<T*>(bp.dV),
-                                              F(L.pdqt), F(L.pdwc), p.n, p.m, p.heads, ck, L.kchunk, L.nk,
+                                              F(L.pdqt), F(L.pdwc), p.lens, p.n, p.m, p.heads, ck, L.kchunk, L.nk,
                                               forward_partials(p, w), sl2e, scale);
     }
     dw_finish(s);
@@ -1577,7 +1609,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     const long long total = (long long)BH * p.n * (D / 8);
     KernelTimer kt_("bwd_spread", s);
     k_bwd_spread<D><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(F(L.dqt), F(L.dkt), static_cast<uint16_t*>(bp.dQ),
-                                                                     static_cast<uint16_t*>(bp.dK), p.n, p.m, total);
+                                                                     static_cast<uint16_t*>(bp.dK), p.lens, p.heads,
+                                                                     p.n, p.m, total);
   } else {
     const int bytes = (2 * 64 * P + 2 * kRowTile * P + 2 * kRowTile * 65) * 4;
     auto kern = &k_bwd_rows<IO, D, true>;
@@ -1587,8 +1620,17 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
     const int nt = cdivi(p.n, kRowTile);
     KernelTimer kt_("bwd_rows_dq", s);
     kern<<<dim3(nt, BH), 256, bytes, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(bp.dO), w.Kt, w.W,
-                                          F(L.dqt), static_cast<T*>(bp.dQ), nullptr, nullptr, p.n, p.m, kRowTile,
-                                          nt, sl2e, scale);
+                                          F(L.dqt), static_cast<T*>(bp.dQ), nullptr, nullptr, p.lens, p.heads, p.n,
+                                          p.m, kRowTile, nt, sl2e, scale);
+  }
+  if (p.lens) {
+    // The passes above leave the rows past each sequence's end alone.
+    const int vpr = D * (int)sizeof(T) / 16;
+    const long long total = (long long)BH * p.n * vpr;
+    KernelTimer kt_("bwd_zero_pad", s);
+    k_bwd_zero_pad<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+        static_cast<uint4*>(bp.dQ), static_cast<uint4*>(bp.dK), static_cast<uint4*>(bp.dV), p.lens, p.heads, p.n,
+        vpr, total);
   }
   return hipGetLastError();
 }
@@ -1602,7 +1644,7 @@ static hipError_t skip_transpose(const BwdProblem& bp, const BwdLayout& L, char*
   float* wf = reinterpret_cast<float*>(ws + L.wflip);
   const int total = p.heads * D * p.conv_k;
   k_flip_taps<<<cdivi(total, 256), 256, 0, ks>>>(p.conv_w, wf, p.conv_k, total);
-  return launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks);
+  return launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks, p.lens);
 }
 
 // The filter-gradient partials.
@@ -1612,7 +1654,7 @@ static hipError_t skip_grad(const BwdProblem& bp, const BwdLayout& L, char* ws, 
   KernelTimer kt_("bwd_skip_grad", ks);
   k_bwd_skip_grad<D><<<dim3(L.nk, p.batch * p.heads), 4 * D, (int)sizeof(SkipSmem<D>), ks>>>(
       static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), reinterpret_cast<float*>(ws + L.pdwc),
-      p.n, p.conv_k, L.kchunk, L.nk);
+      p.lens, p.heads, p.n, p.conv_k, L.kchunk, L.nk);
   return hipSuccess;
 }
 

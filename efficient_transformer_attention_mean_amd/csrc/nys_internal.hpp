@@ -157,7 +157,9 @@ struct ErrLayout {
 
 bool make_error_layout(int batch, int heads, int n, int d, int m, bool bf16, ErrLayout* L);
 hipError_t launch_error(const Problem& p, const ErrLayout& L, char* ws, float* err, hipStream_t s);
+// lens (device int32 [batch], or none): rows past each sequence's end read
+// as zero and are written as zero.
 hipError_t launch_dconv(const void* V, const float* conv_w, void* out, int batch, int heads, int n,
-                        int d, int conv_k, bool bf16, hipStream_t s);
+                        int d, int conv_k, bool bf16, hipStream_t s, const int* lens = nullptr);
 
 }  // namespace nys

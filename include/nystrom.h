@@ -195,6 +195,25 @@ int nystrom_attn_bwd(const void* Q, const void* K, const void* V, const float* c
                      int batch, int conv_k, int dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass under a key-padding mask: the gradients of
+ * nystrom_attn_fwd_masked's output (the method on the first L_b rows of
+ * each batch entry, the pages leaving masking to the implementation), so
+ * that entry b's gradients are those of its own sequence.
+ *   lengths     DEVICE pointer to int32 [batch], as for
+ *               nystrom_attn_fwd_masked (each L_b clamped to [0, n] on the
+ *               device); NULL = the same as nystrom_attn_bwd.
+ * Rows L_b .. n-1 of Q, K, V and dO are never read (they may hold anything,
+ * NaN included); rows L_b .. n-1 of dQ, dK and dV are written as zero; the
+ * filter gradient sums over the real rows of every entry (an empty entry
+ * adds nothing).  All other arguments, the workspace size
+ * (nystrom_attn_bwd_workspace_bytes), the supported shapes, the return
+ * codes and the stream behaviour are those of nystrom_attn_bwd. */
+int nystrom_attn_bwd_masked(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
+                            int n, int d, int m, int heads, int iters,
+                            void* dQ, void* dK, void* dV, float* dconv_w,
+                            int batch, int conv_k, int dtype, const int* lengths,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Training pair: the forward pass that keeps its landmark-side state, and
  * the backward pass that starts from it instead of recomputing it (the same
  * method and results as nystrom_attn_fwd and nystrom_attn_bwd, bit for bit).

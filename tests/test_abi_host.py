@@ -140,6 +140,8 @@ def test_bwd_rejects_bad_arguments_before_launch(lib, kw, code):
                 stream=None)
     args.update(kw)
     assert _lib.nystrom_attn_bwd(**args) == code
+    # The masked entry point checks the same arguments the same way.
+    assert _lib.nystrom_attn_bwd_masked(**args, lengths=FAKE) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -42,7 +42,9 @@ def upstream(wl, seed):
     return round_to_bf16(g) if wl.dtype == "bf16" else g
 
 
-def run_backward(inp, dO, m, iters, dtype, use_conv=True, own_workspace=True, want_dw=True):
+def run_backward(inp, dO, m, iters, dtype, use_conv=True, own_workspace=True, want_dw=True, lengths=False):
+    """lengths: False = nystrom_attn_bwd; None or a sequence = nystrom_attn_bwd_masked
+    with no lengths or those lengths."""
     Q, K, V, G = (to_dev(x, dtype) for x in (inp["Q"], inp["K"], inp["V"], dO))
     B, H, n, d = inp["Q"].shape
     w = inp["conv_w"] if use_conv else None
@@ -55,8 +57,13 @@ def run_backward(inp, dO, m, iters, dtype, use_conv=True, own_workspace=True, wa
         nbytes = _lib.nystrom_attn_bwd_workspace_bytes(B, H, n, d, m, iters, conv_k)
         assert nbytes > 0
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    rc = _lib.nystrom_attn_bwd(Q, K, V, wdev, G, n, d, m, H, iters, dQ, dK, dV, dW, B, conv_k, dtype_code(dtype),
-                               ws, nbytes, torch.cuda.current_stream())
+    if lengths is False:
+        rc = _lib.nystrom_attn_bwd(Q, K, V, wdev, G, n, d, m, H, iters, dQ, dK, dV, dW, B, conv_k,
+                                   dtype_code(dtype), ws, nbytes, torch.cuda.current_stream())
+    else:
+        lens = None if lengths is None else torch.tensor(list(lengths), dtype=torch.int32, device="cuda")
+        rc = _lib.nystrom_attn_bwd_masked(Q, K, V, wdev, G, n, d, m, H, iters, dQ, dK, dV, dW, B, conv_k,
+                                          dtype_code(dtype), lens, ws, nbytes, torch.cuda.current_stream())
     assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
     torch.cuda.synchronize()
     return to_host(dQ), to_host(dK), to_host(dV), None if dW is None else dW.cpu().numpy()
@@ -95,6 +102,86 @@ def test_backward_parity(case):
     if ref[3] is not None:
         g("dconv_w", got[3], ref[3], DW_BARS[dt])
     g.close()
+
+
+# One-token sequences (fp32): largest absolute error against the rms gradient
+# of the batch's other entries.
+ONE_TOKEN_TOL = {"f32": 1e-4}
+
+MASKED = [
+    # (batch, heads, n, d, m, iters, conv_k, dtype, lengths)
+    (3, 2, 300, 64, 16, 6, 33, "bf16", (300, 173, 40)),      # matrix-core path
+    (2, 2, 1000, 32, 64, 6, 33, "f32", (1000, 517)),
+    (4, 1, 256, 16, 8, 6, 5, "f32", (3, 999, 129, 64)),      # 3 < m; 999 clamped to n
+    (4, 2, 512, 64, 64, 6, 33, "bf16", (0, 17, 63, 512)),    # empty, and two sequences shorter than m
+    (2, 2, 4096, 32, 32, 6, 0, "bf16", (2, 4096)),           # matrix-core d = 32, no skip, two tokens
+    (3, 2, 1024, 32, 32, 6, 3, "f32", (1, 2, 1000)),         # one and two tokens
+    (2, 2, 300, 128, 16, 6, 9, "bf16", (300, 100)),          # bf16 on the vector path
+    (2, 12, 8192, 64, 64, 6, 33, "bf16", (8192, 5000)),      # headline shape, one entry padded
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"B{c[0]}H{c[1]}n{c[2]}d{c[3]}m{c[4]}k{c[6]}{c[7]}L{'-'.join(map(str, c[8]))}"
+                                              for c in MASKED])
+def test_masked_backward_parity(case):
+    """Gradients under a key-padding mask against the masked oracle, with NaN
+    in every pad row of Q, K, V and dO (never read); pad rows of dQ, dK and
+    dV must be exactly zero.
+
+    A one-token sequence is gated in fp32, against the gradient scale of the
+    batch's other entries instead of its own: its landmarks are the token and
+    m - 1 zero vectors, so A~ is singular (m - 1 equal rows) and the output
+    hardly depends on the token's q and k.  Its dQ and dK are a remainder of
+    about 1e-3 of the terms the softmax backward of A~ sums (the oracle gives
+    |dA| ~ 9 against |dS_A| ~ 0.01 and |dQ| ~ 2e-3), so rounding is a large
+    share of so small a result.  In bf16 it is larger still: with one key
+    every row of B~ is exactly 1 and dS_B is exactly 0, but the backward's
+    single-bf16 scores differ from the forward's row statistics by 2^-8,
+    which leaves B~ = 1 + O(2^-8) and a dS_B of that order; the bf16 cases
+    start at two tokens."""
+    B, H, n, d, m, iters, k, dt, lengths = case
+    wl = WORKLOADS["tiny"].with_(name=f"bwd_masked{case}", batch=B, heads=H, n=n, d=d, m=m, iters=iters, conv_k=k,
+                                 dtype=dt, seed=400 + n + m)
+    inp = dict(make_inputs(wl))
+    dO = np.array(upstream(wl, 700 + n), copy=True)
+    eff = [min(max(L, 0), n) for L in lengths]
+    for key in ("Q", "K", "V"):
+        x = np.array(inp[key], copy=True)
+        for b, L in enumerate(eff):
+            x[b, :, L:] = np.nan
+        inp[key] = x
+    for b, L in enumerate(eff):
+        dO[b, :, L:] = np.nan
+    ref = nystrom_attention_backward(inp["Q"], inp["K"], inp["V"], m, iters, dO, inp["conv_w"], lengths=lengths)
+    got = run_backward(inp, dO, m, iters, dt, use_conv=k > 0, lengths=lengths)
+    for x in got[:3]:
+        for b, L in enumerate(eff):
+            assert np.all(x[b, :, L:] == 0.0), b
+    one = [b for b, L in enumerate(eff) if L == 1]
+    rest = [b for b in range(B) if b not in one]
+    rows = np.arange(n)[None, :] < np.array([eff[b] for b in rest])[:, None]  # live rows of `rest`
+    g = Gate(f"masked backward {case}")
+    for nm, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        g(nm, x[rest], r[rest], GRAD_BARS[dt])
+        if one:
+            scale = float(np.sqrt(np.mean(r[rest].transpose(0, 2, 1, 3)[rows] ** 2)))
+            err = float(np.max(np.abs(x[one] - r[one])))
+            assert err <= ONE_TOKEN_TOL[dt] * scale, (nm, err, scale)
+    if ref[3] is not None:
+        g("dconv_w", got[3], ref[3], DW_BARS[dt])
+    g.close()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_masked_backward_full_lengths_equal_unmasked_bitwise(dt):
+    wl = WORKLOADS["long"].with_(name=f"bwd_masked_full_{dt}", batch=2, heads=3, n=1500, dtype=dt)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 23)
+    a = run_backward(inp, dO, wl.m, wl.iters, dt)
+    b = run_backward(inp, dO, wl.m, wl.iters, dt, lengths=None)
+    c = run_backward(inp, dO, wl.m, wl.iters, dt, lengths=(1500, 1500))
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
 
 
 def test_backward_deterministic_and_workspace_forms():
@@ -228,6 +315,33 @@ def test_attention_train_autograd_matches_plain_backward():
     got = (to_host(Q.grad), to_host(K.grad), to_host(V.grad), w.grad.cpu().numpy())
     for x, y in zip(got, ref_grads):
         assert np.array_equal(x, y)
+
+
+def test_attention_train_masked_matches_masked_calls():
+    """api.attention_train with lengths: the output equals
+    nystrom_attn_fwd_masked and the gradients equal nystrom_attn_bwd_masked,
+    bit for bit; pad rows of every gradient are zero."""
+    from efficient_transformer_attention_mean_amd import api
+    from ._gpu_util import run_forward
+
+    lengths = (1000, 357)
+    wl = WORKLOADS["tiny"].with_(name="autograd_masked", batch=2, heads=2, n=1000, d=64, m=64, iters=6, conv_k=33,
+                                 dtype="bf16", seed=57)
+    inp = make_inputs(wl)
+    dO = upstream(wl, 59)
+    ref_grads = run_backward(inp, dO, wl.m, wl.iters, wl.dtype, lengths=lengths)
+    ref_out = run_forward(inp, wl.m, wl.iters, wl.dtype, lengths=lengths)[0]
+    Q, K, V = (to_dev(inp[k], wl.dtype).requires_grad_() for k in ("Q", "K", "V"))
+    w = torch.from_numpy(np.ascontiguousarray(inp["conv_w"], np.float32)).cuda().requires_grad_()
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    out = api.attention_train(Q, K, V, wl.m, wl.iters, conv_w=w, lengths=lens)
+    out.backward(to_dev(dO, wl.dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out.detach()), ref_out)
+    got = (to_host(Q.grad), to_host(K.grad), to_host(V.grad), w.grad.cpu().numpy())
+    for x, y in zip(got, ref_grads):
+        assert np.array_equal(x, y)
+    assert np.all(got[0][1, :, 357:] == 0.0)
 
 
 def test_attention_train_rejects_second_derivatives():
