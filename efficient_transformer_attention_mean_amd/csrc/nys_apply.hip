@@ -141,8 +141,12 @@ __device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amd
 // WPE: waves per SIMD the register allocation is held to (1 = no limit).
 // ACC: add the attention to what `out` holds (the skip, written by an
 // earlier launch) instead of overwriting it.
-template <typename IO, int D, int NTM, int KW, bool ATT, int WPE, bool ACC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void k_apply(const typename IO::T* __restrict__ Qin,
+// NWV: waves per block, 16 rows each (tiles of 16 NWV rows).  Without the
+// skip's staging the waves share only the head's planes, so when those fill
+// the LDS a block of more waves hides more latency per CU; the tile's
+// barriers are then needed only where a block moves to another head.
+template <typename IO, int D, int NTM, int KW, bool ATT, int WPE, bool ACC, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE))) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
                                                const uint16_t* __restrict__ kt_hi,
                                                const uint16_t* __restrict__ kt_lo,
@@ -154,6 +158,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
                                                int conv_k, int ntile, long long ntotal) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
+  static_assert(NWV == 4 || !LY::STAGE, "the staged skip is laid out for 4 waves");
+  constexpr int TQ = 16 * NWV, NTH = 64 * NWV;  // rows per tile, threads per block
   constexpr int KC = (D + 31) / 32;  // 32-wide chunks of the head dimension
   constexpr int ND = D / 16;         // 16-feature tiles
   constexpr int FPG = D / 4;         // output features per lane (lane group g owns [g FPG, (g+1) FPG))
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   };
   auto issue_q = [&](Pos q, uint4 (&qr)[KC][LY::QW]) {
     if constexpr (ATT)
-      load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * kTQ + 16 * wave + c);
+      load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * TQ + 16 * wave + c);
   };
 
   // V rows (registers) -> Vt[feature][row].
@@ -577,20 +583,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
   // Tile t at `pos`: Q fragments in qr (two tiles ahead); vn holds the V rows
   // of tile t + 1, staged at the end, then refilled with tile t + 3's.
   auto tile = [&](int t, Pos pos, uint4 (&qr)[KC][LY::QW], uint4 (&vn)[NTK][4]) {
-    const int bh = pos.bh, t0 = pos.ti * kTQ, h = bh % heads;
-    if (bh != cur) {
+    const int bh = pos.bh, t0 = pos.ti * TQ, h = bh % heads;
+    const bool fresh = bh != cur;  // block-uniform
+    if (fresh) {
       // New head: its Kt / W^T planes -> LDS (the previous tile's readers
-      // are past its second barrier), filter operands.
+      // are past its second barrier, or past this one without the skip's
+      // staging), filter operands.
+      if constexpr (!LY::STAGE && LY::KWL) __syncthreads();
       if constexpr (LY::KWL) {
         const uint4* sk[2] = {reinterpret_cast<const uint4*>(kt_hi + (size_t)bh * MPA * D),
                               reinterpret_cast<const uint4*>(kt_lo + (size_t)bh * MPA * D)};
-        for (int e = tid; e < LY::NPL * MPA * D / 8; e += 256) {
+        for (int e = tid; e < LY::NPL * MPA * D / 8; e += NTH) {
           const int pl = e / (MPA * D / 8), r = (e % (MPA * D / 8)) / (D / 8), cc = e % (D / 8);
           *reinterpret_cast<uint4*>(kp + (pl * MPA + r) * KP + 8 * cc) = sk[pl][r * (D / 8) + cc];
         }
         const uint4* sw[2] = {reinterpret_cast<const uint4*>(wt_hi + (size_t)bh * D * MPA),
                               reinterpret_cast<const uint4*>(wt_lo + (size_t)bh * D * MPA)};
-        for (int e = tid; e < LY::NPL * D * MPA / 8; e += 256) {
+        for (int e = tid; e < LY::NPL * D * MPA / 8; e += NTH) {
           const int pl = e / (D * MPA / 8), r = (e % (D * MPA / 8)) / (MPA / 8), cc = e % (MPA / 8);
           // Feature r = a FPG + 4 nd + b sits in row 16 nd + 4a + b, so that the
           // 16 rows one product step reads are consecutive (distinct banks).
@@ -607,7 +616,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
       // in flight stay exact past the merge.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
-    __syncthreads();  // Vt of this tile and the planes visible; the previous epilogue's Ot reads done
+    // Vt of this tile and the planes visible; the previous epilogue's Ot reads done.
+    if (LY::STAGE || fresh) __syncthreads();
 
     // A tile wholly inside a sequence's padding only writes zeros (its loads
     // past the tokens read zeros and move no data).
@@ -624,7 +634,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void
         for (int nd = 0; nd < ND; ++nd) o[nd] = zero4();
       }
     }
-    __syncthreads();  // Ot visible; the skip's Vt reads and the attention's plane reads done
+    if constexpr (LY::STAGE) __syncthreads();  // Ot visible; the skip's Vt reads and the attention's plane reads done
 
     epilogue(bh, h, t0, nb, o);
     if constexpr (LY::STAGE) {
@@ -676,23 +686,29 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   // CU (LDS ~48 KB) when the registers are held to 168 per lane, without
   // spills; other instantiations keep the compiler's choice.
   constexpr int WPE = (IO::kBf16 && KW == 33 && ATT && D <= 64 && NTM <= 4) ? 3 : 1;
-  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE, ACC>;
+  // Without the skip, planes that leave room for at most one block per CU
+  // get blocks of as many waves as the registers allow: 12 (three per SIMD)
+  // for bf16 I/O, 8 for fp32 (stress shape: 767 -> 701 -> 690 us per call
+  // for 4, 8 and 12 waves).
+  constexpr int NWV = (KW == 0 && LY::KWL && LY::BYTES > 80 * 1024) ? (IO::kBf16 ? 12 : 8) : 4;
+  constexpr int NTH = 64 * NWV;
+  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE, ACC, NWV>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
   if (attr != hipSuccess) return attr;
   static const int per_cu = [&] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), 256, LY::BYTES) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern), NTH, LY::BYTES) !=
             hipSuccess ||
         nb < 1)
       nb = 1;
     return nb;
   }();
-  const int ntile = cdiv(p.n, kTQ);
+  const int ntile = cdiv(p.n, 16 * NWV);
   const long long total = (long long)ntile * p.batch * p.heads;
   const long long want = (long long)per_cu * multiprocessors();
   const int grid = (int)(total < want ? total : want);
-  kern<<<grid, 256, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
+  kern<<<grid, NTH, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
                                     w ? w->kt_lo : nullptr, w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w,
                                     w ? w->cwop : nullptr, static_cast<T*>(p.out), p.lens, p.n, p.m, p.heads, p.conv_k,
                                     ntile, total);

@@ -1768,7 +1768,6 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
   __shared__ float sw[256][17];
   __shared__ __align__(16) float sz[ZLDS ? 64 * 68 : 4];
   const int bh = blockIdx.y, f0 = blockIdx.x * 16, tid = threadIdx.x;
-  const int f = tid & 15;
   const float* z = Z + (size_t)bh * m * m;
   // Z (m <= 64: at most 4 values per thread) is loaded first, beside the
   // partials, and stored to LDS after the combine.
@@ -1902,13 +1901,54 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
     return;
   }
   __syncthreads();
-  for (int i = tid >> 4; i < m; i += 64) {
-    // Four interleaved partial sums (fixed order) keep the loads in flight.
-    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < m; ++k) acc4[k & 3] = fmaf(z[(size_t)i * m + k], sbv[k][f], acc4[k & 3]);
-    const float acc = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    sw[i][f] = acc;
-    W[((size_t)bh * m + i) * D + f0 + f] = acc;
+  {
+    // W slice (m x 16) = Z (m x m) BV slice (m x 16) on the matrix cores,
+    // three-way split (fp32-grade): wave ti computes row tile ti (m <= 256:
+    // at most 16 tiles for the 16 waves); lane (c, g) ends with
+    // W[16 ti + 4g + i][f0 + c].  Z rows are read from global memory, every
+    // chunk's loads issued before the first product; rows and columns past
+    // m read as zero.
+    const int lane = tid & 63, ti = tid >> 6, c = lane & 15, g = lane >> 4;
+    if (16 * ti < m) {
+      const int r = 16 * ti + c;
+      const bool rin = r < m;
+      const bool vec = (m & 3) == 0;
+      constexpr int NK = 8;  // 32-wide chunks of m <= 256
+      float a[NK][8];
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) {
+        const int k0 = 32 * kc + 8 * g;
+        if (vec && rin && k0 + 8 <= m) {
+          const float4 u0 = *reinterpret_cast<const float4*>(&z[(size_t)r * m + k0]);
+          const float4 u1 = *reinterpret_cast<const float4*>(&z[(size_t)r * m + k0 + 4]);
+          a[kc][0] = u0.x; a[kc][1] = u0.y; a[kc][2] = u0.z; a[kc][3] = u0.w;
+          a[kc][4] = u1.x; a[kc][5] = u1.y; a[kc][6] = u1.z; a[kc][7] = u1.w;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) a[kc][q] = (rin && k0 + q < m) ? z[(size_t)r * m + k0 + q] : 0.f;
+        }
+      }
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int kc = 0; kc < NK; ++kc) {
+        if (32 * kc >= m) break;
+        float b[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int k = 32 * kc + 8 * g + q;
+          b[q] = k < m ? sbv[k][c] : 0.f;
+        }
+        acc = mma_f32<PR>(a[kc], b, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * ti + 4 * g + i;
+        if (rr < m) {
+          sw[rr][c] = acc[i];
+          W[((size_t)bh * m + rr) * D + f0 + c] = acc[i];
+        }
+      }
+    }
   }
   __syncthreads();
   for (int e = tid; e < 16 * mpa; e += 1024) {
