@@ -1170,7 +1170,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   constexpr int SLOTS = D / 8;
   constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
   constexpr int TPT = (TASKS + NTH - 1) / NTH;     // tasks per thread
-  constexpr bool DEEP = NTW == 1;
+  constexpr bool DEEP = NTW == 1 && NWC <= 8;  // 16 waves hide latency with one tile of loads ahead
   BvStage<IO> stage[TPT], stage2[DEEP ? TPT : 1];
   auto load_tile = [&](BvStage<IO> (&st)[TPT], int k0) {
 #pragma unroll
@@ -1747,6 +1747,27 @@ __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   }
 }
 
+// The split-n pass for 128 < m <= 256 in blocks of 16 waves, one key chunk
+// each, one 16-landmark tile per wave (the 8-wave form holds two tiles per
+// wave, whose accumulators leave room for two waves per SIMD; here four fit).
+// Blocks [0, nconv) write the skip-filter operands (1024 entries each).
+template <typename IO, int D>
+__global__ __launch_bounds__(1024) void k_key_pass16(LandmarkPassArgs a) {
+  using T = typename IO::T;
+  __shared__ BvSmem<IO, D> sm;
+  int blk = blockIdx.x;
+  if (blk < a.nconv) {
+    const int idx = blk * 1024 + (int)threadIdx.x;
+    if (idx < a.conv_total) conv_operand(a.conv_w, a.cwop, idx, a.conv_k);
+    return;
+  }
+  blk -= a.nconv;
+  const int bh = blk / a.nchunks;
+  bv_chunk<IO, D, 1, false, 16>(sm, nullptr, blk % a.nchunks, bh, static_cast<const T*>(a.K),
+                                static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
+                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+}
+
 // Finish of the split-n pass, one block per (16-feature slice, head):
 //   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
 //   (M_j = max_c pmax_c[j]; chunks in fixed order), then W = Z BV for the
@@ -2096,8 +2117,13 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.W = w.W;
   a.wt_hi = w.wt_hi;
   a.bhn = BH;
-  const int grid = a.npinv + a.nconv + (CPB == 2 ? w.nchunks / 2 : w.nchunks) * BH;
   KernelTimer kt_("landmark_pass", s);
+  if constexpr (CPB == 1 && PMP == 0 && (IO::kBf16 || D <= 64)) {  // fp32 at d = 128 needs more registers
+    a.nconv = ceil_div(a.conv_total, 1024);
+    k_key_pass16<IO, D><<<a.nconv + w.nchunks * BH, 1024, 0, s>>>(a);
+    return;
+  }
+  const int grid = a.npinv + a.nconv + (CPB == 2 ? w.nchunks / 2 : w.nchunks) * BH;
   if constexpr (PMP > 0) {
     if (p.zsave) {
       k_landmark_pass<IO, D, NTW, PMP, true><<<grid, 512, 0, s>>>(a);
