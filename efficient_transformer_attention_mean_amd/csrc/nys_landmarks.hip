@@ -32,7 +32,11 @@ namespace nys {
 // m..mpa-1 zero), the operand layout of the pseudoinverse's scores and of the
 // output stage: Qt as it is, Kt pre-multiplied by log2(e)/sqrt(d), so that
 // scores come out in base-2 units.
-template <typename IO, int D>
+// WS (short segments): one wave per segment, four segments per
+// block, grid (ceil(m/4), batch*heads, 2); the lanes of a wave cover whole
+// rows, so a short segment is one round of loads and the sum needs only lane
+// shuffles (no LDS, no barrier).
+template <typename IO, int D, bool WS = false>
 __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __restrict__ Q,
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
@@ -48,15 +52,16 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
     for (int i = threadIdx.x; i < nsync; i += 256) sync[i] = 0u;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int SLOTS = D / VEC;   // 16-byte vectors per row
-  constexpr int RS = 256 / SLOTS;  // rows covered per pass
+  constexpr int RS = (WS ? 64 : 256) / SLOTS;  // rows covered per pass (by a wave with WS)
   __shared__ float part[4][D];
-  const int j = blockIdx.x, bh = blockIdx.y;
+  const int j = WS ? 4 * blockIdx.x + (threadIdx.x >> 6) : blockIdx.x, bh = blockIdx.y;
+  if (WS && j >= m) return;  // wave-uniform; no barrier follows with WS
   const int nb = seq_rows(lens, bh / heads, n);
   const int seg = max(1, (nb + m - 1) / m);  // l = 1 for a sequence shorter than m (empty included)
   const int rows = max(0, min(seg, nb - j * seg));  // real rows of this segment
   const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
   float* out = (blockIdx.z == 0 ? Qt : Kt) + ((size_t)bh * m + j) * D;
-  const int slot = threadIdx.x % SLOTS, r0 = threadIdx.x / SLOTS;
+  const int slot = threadIdx.x % SLOTS, r0 = (WS ? threadIdx.x & 63 : threadIdx.x) / SLOTS;
   float acc[VEC];
 #pragma unroll
   for (int q = 0; q < VEC; ++q) acc[q] = 0.f;
@@ -90,6 +95,30 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
 #pragma unroll
     for (int q = 0; q < VEC; ++q) acc[q] += shfl_xor(acc[q], o);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto emit = [&](int f, float s) {  // feature f of this segment's mean, sum s
+    const float mean = s / (float)seg;
+    out[f] = mean;
+    uint16_t* ph = blockIdx.z == 1 ? kt_hi : qt_hi;
+    uint16_t* pl = blockIdx.z == 1 ? kt_lo : qt_lo;
+    uint16_t hi, lo;
+    split_hi_lo(blockIdx.z == 1 ? mean * sl2e : mean, hi, lo);
+    const size_t o = ((size_t)bh * mpa + j) * D + f;
+    ph[o] = hi;
+    pl[o] = lo;
+    if (j == m - 1) {
+      for (int r = m; r < mpa; ++r) {
+        ph[((size_t)bh * mpa + r) * D + f] = 0;
+        pl[((size_t)bh * mpa + r) * D + f] = 0;
+      }
+    }
+  };
+  if constexpr (WS) {
+    if (lane < SLOTS) {
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) emit(slot * VEC + q, acc[q]);
+    }
+    return;
+  }
   if (lane < SLOTS) {
 #pragma unroll
     for (int q = 0; q < VEC; ++q) part[wave][slot * VEC + q] = acc[q];
@@ -97,21 +126,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   __syncthreads();
   if (threadIdx.x < D) {
     const float s = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
-    const float mean = s / (float)seg;
-    out[threadIdx.x] = mean;
-    uint16_t* ph = blockIdx.z == 1 ? kt_hi : qt_hi;
-    uint16_t* pl = blockIdx.z == 1 ? kt_lo : qt_lo;
-    uint16_t hi, lo;
-    split_hi_lo(blockIdx.z == 1 ? mean * sl2e : mean, hi, lo);
-    const size_t o = ((size_t)bh * mpa + j) * D + threadIdx.x;
-    ph[o] = hi;
-    pl[o] = lo;
-    if (j == m - 1) {
-      for (int r = m; r < mpa; ++r) {
-        ph[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
-        pl[((size_t)bh * mpa + r) * D + threadIdx.x] = 0;
-      }
-    }
+    emit(threadIdx.x, s);
   }
 }
 
@@ -1995,6 +2010,12 @@ static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
   using T = typename IO::T;
   const int BH = p.batch * p.heads;
   KernelTimer kt_("segment_mean", s);
+  if ((p.n + p.m - 1) / p.m <= 32) {  // segments of at most 32 rows: a wave each (bert 123.3 -> 120.8 us)
+    k_segment_mean<IO, D, true><<<dim3((p.m + 3) / 4, BH, 2), 256, 0, s>>>(
+        static_cast<const T*>(p.Q), static_cast<const T*>(p.K), w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo,
+        p.lens, p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D), w.sync, 2 * BH);
+    return;
+  }
   k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
                                                          w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo, p.lens,
                                                          p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D),
