@@ -180,14 +180,14 @@ __device__ __forceinline__ float4 plus_diag(int row, int col0, const f32x4_t& v,
   return make_float4(r[0], r[1], r[2], r[3]);
 }
 
+// The pseudoinverse of head bh by a block of 64 * kPinvWaves threads.
 template <int MP, int PR>
-__global__ __launch_bounds__(64 * kPinvWaves) void k_pinv_lds(const float* __restrict__ Qt, const float* __restrict__ Kt,
-                                                  float* __restrict__ Aout, float* __restrict__ Zout, int m,
-                                                  int d, float sl2e, int iters, float* __restrict__ zsave,
-                                                  int zmp) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+__device__ __forceinline__ void pinv_lds_head(unsigned char* smem_raw, int bh, const float* __restrict__ Qt,
+                                              const float* __restrict__ Kt, float* __restrict__ Aout,
+                                              float* __restrict__ Zout, int m, int d, float sl2e, int iters,
+                                              float* __restrict__ zsave, int zmp) {
   PinvSmem<MP>& sm = *reinterpret_cast<PinvSmem<MP>*>(smem_raw);
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const float* qt = Qt + (size_t)bh * m * d;
   const float* kt = Kt + (size_t)bh * m * d;
@@ -344,6 +344,15 @@ __global__ __launch_bounds__(64 * kPinvWaves) void k_pinv_lds(const float* __res
     ao[e] = sm.A[i][j];
     zo[e] = Z[i][j];
   }
+}
+
+template <int MP, int PR>
+__global__ __launch_bounds__(64 * kPinvWaves) void k_pinv_lds(const float* __restrict__ Qt, const float* __restrict__ Kt,
+                                                  float* __restrict__ Aout, float* __restrict__ Zout, int m,
+                                                  int d, float sl2e, int iters, float* __restrict__ zsave,
+                                                  int zmp) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  pinv_lds_head<MP, PR>(smem_raw, (int)blockIdx.x, Qt, Kt, Aout, Zout, m, d, sl2e, iters, zsave, zmp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1185,7 +1194,7 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   constexpr int SLOTS = D / 8;
   constexpr int TASKS = 32 * SLOTS;               // (key pair, 8-feature slot)
   constexpr int TPT = (TASKS + NTH - 1) / NTH;     // tasks per thread
-  constexpr bool DEEP = NTW == 1 && NWC <= 8;  // 16 waves hide latency with one tile of loads ahead
+  constexpr bool DEEP = NTW == 1 && NWC == 4;  // larger groups hide latency with one tile of loads ahead
   BvStage<IO> stage[TPT], stage2[DEEP ? TPT : 1];
   auto load_tile = [&](BvStage<IO> (&st)[TPT], int k0) {
 #pragma unroll
@@ -1783,6 +1792,27 @@ __global__ __launch_bounds__(1024) void k_key_pass16(LandmarkPassArgs a) {
                                 seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
 }
 
+// fp32 I/O, m <= 64, d <= 64: the pseudoinverse (blocks [0, npinv), one
+// head each, as k_pinv_lds) and the split-n key pass (two chunks per block,
+// 8 waves each; partial entry per chunk, combined by k_bv_finish) in one
+// launch, since the pseudoinverse needs only the landmarks.
+template <int PMP, int D>
+__global__ __launch_bounds__(64 * kPinvWaves) void k_landmark_pass_f32(LandmarkPassArgs a, float sl2e_d) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  static_assert(64 * kPinvWaves == 1024, "two 8-wave chunk groups per block");
+  int blk = blockIdx.x;
+  if (blk < a.npinv) {
+    pinv_lds_head<PMP, 6>(smem_raw, blk, a.Qt, a.Kt, a.A, a.Z, a.m, D, sl2e_d, a.iters, a.zsave, a.zmp);
+    return;
+  }
+  blk -= a.npinv;
+  const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 9;
+  BvSmem<F32, D>& sm = reinterpret_cast<BvSmem<F32, D>*>(smem_raw)[grp];
+  bv_chunk<F32, D, 1, false, 8>(sm, nullptr, 2 * (blk % half) + grp, bh, static_cast<const float*>(a.K),
+                                static_cast<const float*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
+                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+}
+
 // Finish of the split-n pass, one block per (16-feature slice, head):
 //   BV[j][f] = sum_c pacc_c[j][f] 2^(pmax_c[j] - M_j) / sum_c psum_c[j] 2^(pmax_c[j] - M_j)
 //   (M_j = max_c pmax_c[j]; chunks in fixed order), then W = Z BV for the
@@ -2091,10 +2121,14 @@ static hipError_t pinv_t(const Problem& p, const Ws& w, hipStream_t s) {
 
 bool pinv_in_landmark_pass(const Problem& p) { return p.bf16 && p.m <= 64; }
 
+// fp32 I/O: the pseudoinverse in the same launch as the key pass (its LDS
+// holds two key groups beside it for d <= 64).
+static bool pinv_beside_keys(const Problem& p) { return !p.bf16 && p.m <= 64 && p.d <= 64; }
+
 int forward_partials(const Problem& p, const Ws& w) { return pinv_in_landmark_pass(p) ? w.nchunks / 2 : w.nchunks; }
 
 hipError_t stage_pinv(const Problem& p, const Ws& w, hipStream_t s) {
-  if (pinv_in_landmark_pass(p)) return hipSuccess;
+  if (pinv_in_landmark_pass(p) || pinv_beside_keys(p)) return hipSuccess;
   return p.bf16 ? pinv_t<3>(p, w, s) : pinv_t<6>(p, w, s);
 }
 
@@ -2154,6 +2188,40 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   k_landmark_pass<IO, D, NTW, PMP, false, CPB><<<grid, 512, 0, s>>>(a);
 }
 
+
+template <int PMP, int D>
+static hipError_t landmark_pass_f32_launch(const Problem& p, const Ws& w, hipStream_t s) {
+  const int BH = p.batch * p.heads;
+  LandmarkPassArgs a{};
+  a.K = p.K;
+  a.V = p.V;
+  a.zsave = p.zsave;
+  a.zmp = p.zmp;
+  a.Qt = w.Qt;
+  a.Kt = w.Kt;
+  a.A = w.A;
+  a.Z = w.Z;
+  a.pacc = w.pacc;
+  a.pmax = w.pmax;
+  a.psum = w.psum;
+  a.lens = p.lens;
+  a.n = p.n;
+  a.heads = p.heads;
+  a.m = p.m;
+  a.chunk = w.chunk;
+  a.nchunks = w.nchunks;
+  a.iters = p.iters;
+  a.npinv = BH;
+  a.sl2e = kLog2e / sqrtf((float)D);
+  constexpr int SMEM = sizeof(PinvSmem<PMP>) > 2 * sizeof(BvSmem<F32, D>) ? (int)sizeof(PinvSmem<PMP>)
+                                                                            : (int)(2 * sizeof(BvSmem<F32, D>));
+  const hipError_t attr = ensure_dynamic_smem(reinterpret_cast<const void*>(&k_landmark_pass_f32<PMP, D>), SMEM);
+  if (attr != hipSuccess) return attr;
+  KernelTimer kt_("landmark_pass", s);
+  k_landmark_pass_f32<PMP, D><<<BH + (w.nchunks / 2) * BH, 64 * kPinvWaves, SMEM, s>>>(a, kLog2e / sqrtf((float)D));
+  return hipSuccess;
+}
+
 template <typename IO, int D>
 static void landmark_pass_t(const Problem& p, const Ws& w, hipStream_t s) {
   if constexpr (IO::kBf16) {
@@ -2169,6 +2237,16 @@ static void landmark_pass_t(const Problem& p, const Ws& w, hipStream_t s) {
 }
 
 hipError_t stage_landmark_pass(const Problem& p, const Ws& w, hipStream_t s) {
+  if (pinv_beside_keys(p)) {
+    hipError_t e;
+    const bool small = p.m <= 32;
+    switch (p.d) {
+      case 16: e = small ? landmark_pass_f32_launch<32, 16>(p, w, s) : landmark_pass_f32_launch<64, 16>(p, w, s); break;
+      case 32: e = small ? landmark_pass_f32_launch<32, 32>(p, w, s) : landmark_pass_f32_launch<64, 32>(p, w, s); break;
+      default: e = small ? landmark_pass_f32_launch<32, 64>(p, w, s) : landmark_pass_f32_launch<64, 64>(p, w, s); break;
+    }
+    return e != hipSuccess ? e : hipGetLastError();
+  }
   switch (p.d) {
     case 16: p.bf16 ? landmark_pass_t<BF16, 16>(p, w, s) : landmark_pass_t<F32, 16>(p, w, s); break;
     case 32: p.bf16 ? landmark_pass_t<BF16, 32>(p, w, s) : landmark_pass_t<F32, 32>(p, w, s); break;
