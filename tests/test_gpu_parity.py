@@ -228,6 +228,8 @@ MASKED = [
     (2, 2, 4096, 64, 32, 6, 0, "bf16", (1, 4096)),           # no skip; a one-token sequence
     (4, 2, 512, 64, 64, 6, 33, "bf16", (0, 17, 63, 512)),    # empty, and two sequences shorter than m
     (3, 1, 300, 128, 96, 8, 9, "f32", (95, 0, 300)),         # m > 64 path, shorter than m, empty
+    (2, 2, 1500, 128, 256, 8, 33, "bf16", (1500, 700)),      # stress layout: 16-wave key pass, 12-wave output stage
+    (3, 1, 600, 128, 256, 8, 33, "bf16", (600, 200, 0)),     # the same, shorter than m, empty
 ]
 
 
