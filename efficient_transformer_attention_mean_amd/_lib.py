@@ -34,6 +34,8 @@ EXPORTS = (
     "nystrom_attn_bwd_masked",
     "nystrom_attn_fwd_save",
     "nystrom_attn_bwd_saved",
+    "nystrom_attn_bwd_state_bytes",
+    "nystrom_attn_bwd_from_state",
     "nystrom_layer_workspace_bytes",
     "nystrom_layer_fwd",
     "nystrom_attn_error_workspace_bytes",
@@ -78,6 +80,11 @@ def load():
     lib.nystrom_attn_fwd_save.restype = i
     lib.nystrom_attn_bwd_saved.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.nystrom_attn_bwd_saved.restype = i
+    lib.nystrom_attn_bwd_state_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.nystrom_attn_bwd_state_bytes.restype = sz
+    lib.nystrom_attn_bwd_from_state.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, i, i, i, vp, sz,
+                                                vp, sz, vp]
+    lib.nystrom_attn_bwd_from_state.restype = i
     lib.nystrom_layer_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.nystrom_layer_workspace_bytes.restype = sz
     lib.nystrom_layer_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, i, i, i, vp, sz, vp]
@@ -180,6 +187,18 @@ def nystrom_attn_bwd_saved(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, d
     return load().nystrom_attn_bwd_saved(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), _ptr(dO), n, d, m, heads, iters,
                                          _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dconv_w), batch, conv_k, dtype,
                                          _ptr(saved), saved_bytes, _stream(stream))
+
+
+def nystrom_attn_bwd_state_bytes(batch, heads, n, d, m, iters, conv_k) -> int:
+    return int(load().nystrom_attn_bwd_state_bytes(batch, heads, n, d, m, iters, conv_k))
+
+
+def nystrom_attn_bwd_from_state(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k,
+                                dtype, state, state_bytes, scratch=None, scratch_bytes=0, stream=None) -> int:
+    return load().nystrom_attn_bwd_from_state(_ptr(Q), _ptr(K), _ptr(V), _ptr(conv_w), _ptr(dO), n, d, m, heads,
+                                              iters, _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dconv_w), batch, conv_k,
+                                              dtype, _ptr(state), state_bytes, _ptr(scratch), scratch_bytes,
+                                              _stream(stream))
 
 
 def nystrom_layer_workspace_bytes(batch, heads, n, d, m, dtype) -> int:

@@ -95,17 +95,19 @@ def _conv_k(conv_w, heads, d) -> int:
 
 class _NystromAttention(torch.autograd.Function):
     """Forward: nystrom_attn_fwd_save, which keeps the landmark-side state in
-    a buffer held by the autograd context; backward: nystrom_attn_bwd_saved
-    from that state (gradients of Q, K, V and the filters)."""
+    a buffer held by the autograd context (the state alone, not the
+    backward's scratch); backward: nystrom_attn_bwd_from_state from that state
+    with a scratch buffer that lives only during the call (gradients of Q, K,
+    V and the filters)."""
 
     @staticmethod
     def forward(ctx, Q, K, V, conv_w, m, iters):
         _check_io(Q, K, V)
         batch, heads, n, d = Q.shape
         conv_k = _conv_k(conv_w, heads, d)
-        nbytes = _lib.nystrom_attn_bwd_workspace_bytes(batch, heads, n, d, m, iters, conv_k)
+        nbytes = _lib.nystrom_attn_bwd_state_bytes(batch, heads, n, d, m, iters, conv_k)
         if nbytes == 0:
-            raise NystromError(_lib.NYS_EUNSUPPORTED, "nystrom_attn_bwd_workspace_bytes")
+            raise NystromError(_lib.NYS_EUNSUPPORTED, "nystrom_attn_bwd_state_bytes")
         saved = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
         out = torch.empty_like(Q)
         rc = _lib.nystrom_attn_fwd_save(Q, K, V, conv_w, n, d, m, heads, iters, out, batch, conv_k,
@@ -127,11 +129,13 @@ class _NystromAttention(torch.autograd.Function):
         dO = dO.to(Q.dtype).contiguous()
         dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
         dW = torch.empty_like(conv_w) if conv_w is not None and ctx.needs_input_grad[3] else None
-        rc = _lib.nystrom_attn_bwd_saved(Q, K, V, conv_w, dO, n, d, ctx.m, heads, ctx.iters, dQ, dK, dV, dW, batch,
-                                         ctx.conv_k, _DTYPES[Q.dtype], ctx.state, ctx.nbytes,
-                                         torch.cuda.current_stream())
+        total = _lib.nystrom_attn_bwd_workspace_bytes(batch, heads, n, d, ctx.m, ctx.iters, ctx.conv_k)
+        scratch = torch.empty(total - ctx.nbytes, dtype=torch.uint8, device=Q.device)
+        rc = _lib.nystrom_attn_bwd_from_state(Q, K, V, conv_w, dO, n, d, ctx.m, heads, ctx.iters, dQ, dK, dV, dW,
+                                              batch, ctx.conv_k, _DTYPES[Q.dtype], ctx.state, ctx.nbytes, scratch,
+                                              scratch.numel(), torch.cuda.current_stream())
         if rc != _lib.NYS_OK:
-            raise NystromError(rc, "nystrom_attn_bwd_saved")
+            raise NystromError(rc, "nystrom_attn_bwd_from_state")
         return dQ, dK, dV, dW, None, None
 
 

@@ -181,6 +181,15 @@ size_t nystrom_attn_bwd_workspace_bytes(int batch, int heads, int n, int d, int 
   return L.total > Lb.total ? L.total : Lb.total;
 }
 
+size_t nystrom_attn_bwd_state_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k) {
+  if (check_shape(batch, heads, n, d, m, iters) != NYS_OK) return 0;
+  nys::BwdLayout L, Lb;
+  const int ck = conv_k < 0 ? 0 : conv_k;
+  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, false, &L)) return 0;
+  if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, true, &Lb)) return 0;
+  return L.state > Lb.state ? L.state : Lb.state;
+}
+
 }  // extern "C"
 
 namespace {
@@ -188,13 +197,16 @@ namespace {
 // The backward entry points: saved = false recomputes the forward's landmark
 // side in `workspace` (allocated when NULL); saved = true takes it from
 // `workspace` as nystrom_attn_fwd_save left it (which must then be given).
+// With `state` given, the saved state is there instead (state_bytes long) and
+// `workspace` is only the scratch (allocated when NULL).
 // lengths: device int32 [batch] of sequence lengths, or NULL.
 int backward(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO, int n, int d, int m,
              int heads, int iters, void* dQ, void* dK, void* dV, float* dconv_w, int batch, int conv_k, int dtype,
-             void* workspace, size_t workspace_bytes, void* stream, bool saved, const int* lengths = nullptr) {
+             void* workspace, size_t workspace_bytes, void* stream, bool saved, const int* lengths = nullptr,
+             const void* state = nullptr, size_t state_bytes = 0) {
   try {
     if (!Q || !K || !V || !dO || !dQ || !dK || !dV) return NYS_EINVAL;
-    if (saved && !workspace) return NYS_EINVAL;
+    if (saved && !workspace && !state) return NYS_EINVAL;
     if (dtype != NYS_F32 && dtype != NYS_BF16) return NYS_EINVAL;
     if (conv_w && (conv_k < 1 || conv_k % 2 == 0)) return NYS_EINVAL;
     const int rc = check_shape(batch, heads, n, d, m, iters);
@@ -203,18 +215,24 @@ int backward(const void* Q, const void* K, const void* V, const float* conv_w, c
     nys::BwdLayout L;
     if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // Bytes the caller's `workspace` must hold: everything, or the scratch alone.
+    const size_t need = state ? L.total - L.state : L.total;
+    if (state && state_bytes < L.state) return NYS_EWORKSPACE;
     char* ws = static_cast<char*>(workspace);
     bool owned = false;
     if (!ws) {
-      if (hipMallocAsync(reinterpret_cast<void**>(&ws), L.total, s) != hipSuccess) return NYS_EHIP;
+      if (hipMallocAsync(reinterpret_cast<void**>(&ws), need, s) != hipSuccess) return NYS_EHIP;
       owned = true;
-    } else if (workspace_bytes < L.total) {
+    } else if (workspace_bytes < need) {
       return NYS_EWORKSPACE;
     }
     nys::BwdProblem p{{Q, K, V, conv_w, nullptr, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16}, dO, dQ, dK,
                       dV, conv_w ? dconv_w : nullptr};
     p.fwd.lens = lengths;
-    hipError_t e = nys::launch_backward(p, L, ws, s, !saved);
+    // The backward reads the saved state and writes only the scratch.
+    const nys::BwdBuf buf = state ? nys::BwdBuf{static_cast<char*>(const_cast<void*>(state)), ws, L.state}
+                                  : nys::BwdBuf{ws, ws + L.state, L.state};
+    hipError_t e = nys::launch_backward(p, L, buf, s, !saved);
     if (owned) {
       hipError_t f = hipFreeAsync(ws, s);
       if (e == hipSuccess) e = f;
@@ -256,7 +274,7 @@ int nystrom_attn_fwd_save(const void* Q, const void* K, const void* V, const flo
     const int ck = conv_w ? conv_k : 0;
     nys::BwdLayout L;
     if (!nys::make_bwd_layout(batch, heads, n, d, m, iters, ck, dtype == NYS_BF16, &L)) return NYS_EUNSUPPORTED;
-    if (saved_bytes < L.total) return NYS_EWORKSPACE;
+    if (saved_bytes < L.state) return NYS_EWORKSPACE;
     nys::Problem p{Q, K, V, conv_w, out, batch, heads, n, d, m, iters, ck, dtype == NYS_BF16};
     const hipError_t e = nys::launch_forward_save(p, L, static_cast<char*>(saved), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NYS_OK : NYS_EHIP;
@@ -270,6 +288,15 @@ int nystrom_attn_bwd_saved(const void* Q, const void* K, const void* V, const fl
                            int conv_k, int dtype, void* saved, size_t saved_bytes, void* stream) {
   return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, saved,
                   saved_bytes, stream, true);
+}
+
+int nystrom_attn_bwd_from_state(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
+                                int n, int d, int m, int heads, int iters, void* dQ, void* dK, void* dV,
+                                float* dconv_w, int batch, int conv_k, int dtype, const void* state,
+                                size_t state_bytes, void* scratch, size_t scratch_bytes, void* stream) {
+  if (!state) return NYS_EINVAL;
+  return backward(Q, K, V, conv_w, dO, n, d, m, heads, iters, dQ, dK, dV, dconv_w, batch, conv_k, dtype, scratch,
+                  scratch_bytes, stream, true, nullptr, state, state_bytes);
 }
 
 size_t nystrom_layer_workspace_bytes(int batch, int heads, int n, int d, int m, int dtype) {

@@ -1468,6 +1468,10 @@ bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int c
     return o;
   };
   const size_t md = (size_t)BH * m * d * 4;
+  // The saved state first (the forward's regions, then its steps), so that
+  // the training pair can keep it apart from the backward's scratch.
+  L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * 4 * L->mp * L->mp * 4);
+  L->state = off;
   L->pdw = take(md * L->nq);
   L->pdkt = take(md * L->nq);
   L->dw = take(md);
@@ -1477,18 +1481,17 @@ bool make_bwd_layout(int batch, int heads, int n, int d, int m, int iters, int c
   L->pdqt = take(md * L->nk);
   L->dqt = take(md);
   L->pdwc = take((size_t)BH * L->nk * d * (conv_k > 0 ? conv_k : 1) * 4);
-  L->zs = take((size_t)BH * (iters > 0 ? iters : 1) * 4 * L->mp * L->mp * 4);
   L->wflip = take((size_t)heads * d * (conv_k > 0 ? conv_k : 1) * 4);
   L->total = off;
   return true;
 }
 
 template <typename IO, int D>
-static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc) {
+static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, const BwdBuf& ws, hipStream_t s, SideCall& sc) {
   using T = typename IO::T;
   const Problem& p = bp.fwd;
-  const Ws w = resolve(L.fwd, ws);
-  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  const Ws w = resolve(L.fwd, ws.st);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws.scratch(o)); };  // scratch regions
   const int BH = p.batch * p.heads;
   const float sl2e = kLog2e / sqrtf((float)D), scale = 1.f / sqrtf((float)D);
   constexpr int P = D + 1;
@@ -1524,7 +1527,8 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
                                                      L.nq);
   }
   // Landmark side: the pseudoinverse backward, dKt and dQt_A.
-  const LandArgs la{w.Qt, w.Kt, w.A, w.BV, F(L.dw), F(L.dkt), F(L.dqta), F(L.zs), p.m, D, p.iters, scale};
+  const LandArgs la{w.Qt,      w.Kt,     w.A,     w.BV, F(L.dw), F(L.dkt), F(L.dqta),
+                    reinterpret_cast<const float*>(ws.state(L.zs)), p.m, D,  p.iters, scale};
   auto land = [&]() -> hipError_t {
     auto go = [&](auto kern, int nth, int bytes) -> hipError_t {
       // One attribute per kernel variant: the four variants share go's type.
@@ -1639,9 +1643,9 @@ static hipError_t bwd_t(const BwdProblem& bp, const BwdLayout& L, char* ws, hipS
 // only inputs.  dV = DConv^T(dO): the forward's convolution with the taps
 // reversed, written as the initial dV.
 template <int D>
-static hipError_t skip_transpose(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
+static hipError_t skip_transpose(const BwdProblem& bp, const BwdLayout& L, const BwdBuf& ws, hipStream_t ks) {
   const Problem& p = bp.fwd;
-  float* wf = reinterpret_cast<float*>(ws + L.wflip);
+  float* wf = reinterpret_cast<float*>(ws.scratch(L.wflip));
   const int total = p.heads * D * p.conv_k;
   k_flip_taps<<<cdivi(total, 256), 256, 0, ks>>>(p.conv_w, wf, p.conv_k, total);
   return launch_dconv(bp.dO, wf, bp.dV, p.batch, p.heads, p.n, D, p.conv_k, true, ks, p.lens);
@@ -1649,19 +1653,19 @@ static hipError_t skip_transpose(const BwdProblem& bp, const BwdLayout& L, char*
 
 // The filter-gradient partials.
 template <int D>
-static hipError_t skip_grad(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t ks) {
+static hipError_t skip_grad(const BwdProblem& bp, const BwdLayout& L, const BwdBuf& ws, hipStream_t ks) {
   const Problem& p = bp.fwd;
   KernelTimer kt_("bwd_skip_grad", ks);
   k_bwd_skip_grad<D><<<dim3(L.nk, p.batch * p.heads), 4 * D, (int)sizeof(SkipSmem<D>), ks>>>(
-      static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), reinterpret_cast<float*>(ws + L.pdwc),
+      static_cast<const uint16_t*>(p.V), static_cast<const uint16_t*>(bp.dO), reinterpret_cast<float*>(ws.scratch(L.pdwc)),
       p.lens, p.heads, p.n, p.conv_k, L.kchunk, L.nk);
   return hipSuccess;
 }
 
-static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* ws, hipStream_t s, SideCall& sc,
+static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, const BwdBuf& ws, hipStream_t s, SideCall& sc,
                                 bool recompute) {
   const Problem& p = bp.fwd;
-  const Ws w = resolve(L.fwd, ws);
+  const Ws w = resolve(L.fwd, ws.st);
   hipError_t e;
   const bool skip = sc.ss && p.conv_w && p.conv_k > 0;
   if (sc.ss) {
@@ -1676,7 +1680,7 @@ static hipError_t backward_body(const BwdProblem& bp, const BwdLayout& L, char* 
     }
   }
   // The forward's landmark side: Qt, Kt, A, Z, BV, W and B's statistics
-  // (already in ws when the forward saved them).
+  // (already in the state part when the forward saved them).
   if (recompute) {
     if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;
     if ((e = stage_landmark_pass(p, w, s)) != hipSuccess) return e;
@@ -1707,10 +1711,11 @@ hipError_t launch_forward_save(const Problem& p0, const BwdLayout& L, char* ws, 
   return launch_forward(p, L.fwd, ws, s);
 }
 
-hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, char* ws, hipStream_t s, bool recompute) {
+hipError_t launch_backward(const BwdProblem& bp0, const BwdLayout& L, const BwdBuf& ws, hipStream_t s,
+                           bool recompute) {
   // The forward's pseudoinverse kernel also saves its steps for the reverse pass.
   BwdProblem bp = bp0;
-  bp.fwd.zsave = reinterpret_cast<float*>(ws + L.zs);
+  bp.fwd.zsave = reinterpret_cast<float*>(ws.state(L.zs));
   bp.fwd.zmp = L.mp;
   const Problem& p = bp.fwd;
   if (!(p.bf16 && (p.d == 32 || p.d == 64))) {

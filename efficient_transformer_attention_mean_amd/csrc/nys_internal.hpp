@@ -100,6 +100,7 @@ struct BwdLayout {
   size_t pdwc;         // fp32 [bh][nk][d][conv_k] partials of the filter gradient
   size_t zs;           // fp32 [bh][iters][4][mp][mp] forward steps: Z_k, X_k, T1_k, T2_k
   size_t wflip;        // fp32 [heads][d][conv_k] skip filters with their taps reversed
+  size_t state;        // bytes of the saved state: the forward's regions and zs come first
   size_t total;
   int qchunk, nq;      // query rows per block of the reduction pass, blocks per head
   int kchunk, nk;      // keys per block of the key pass, blocks per head
@@ -118,9 +119,22 @@ struct BwdProblem {
   float* dconv_w;  // fp32 [heads][d][conv_k] or nullptr
 };
 
+// Where the regions of a backward workspace live: the saved state (offsets
+// below L.state) from st, the scratch (offsets from L.state on) from scr,
+// which may be a buffer of its own.  One buffer: st = ws, scr = ws + L.state.
+struct BwdBuf {
+  char* st;
+  char* scr;
+  size_t scr_off;
+  char* state(size_t o) const { return st + o; }
+  char* scratch(size_t o) const { return scr + (o - scr_off); }
+};
+
 // recompute = false: the forward's landmark-side state (and its saved
-// pseudoinverse steps) is already in ws, written by launch_forward_save.
-hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, char* ws, hipStream_t s, bool recompute = true);
+// pseudoinverse steps) is already in the state part, written by
+// launch_forward_save.
+hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, const BwdBuf& b, hipStream_t s,
+                           bool recompute = true);
 // The forward pass on the forward regions of a backward workspace, saving the
 // pseudoinverse steps there too, so that launch_backward can skip its recompute.
 hipError_t launch_forward_save(const Problem& p, const BwdLayout& L, char* ws, hipStream_t s);

@@ -223,15 +223,32 @@ int nystrom_attn_bwd_masked(const void* Q, const void* K, const void* V, const f
  *                          to `saved`
  *   nystrom_attn_bwd_saved arguments as for nystrom_attn_bwd, with `saved`
  *                          in place of the workspace
- *   saved        DEVICE buffer of at least nystrom_attn_bwd_workspace_bytes(),
- *                owned by the caller, not NULL (NYS_EINVAL).  Between the two
- *                calls it must stay untouched, and the two calls must get the
- *                same Q, K, V, conv_w, shape, iters, conv_k and dtype; the
- *                backward may be called more than once on one saved forward.
- *                The buffer's contents are the library's; its layout is
- *                not part of this interface.
+ *   saved        DEVICE buffer owned by the caller, not NULL (NYS_EINVAL):
+ *                for nystrom_attn_bwd_saved at least
+ *                nystrom_attn_bwd_workspace_bytes() (the state, then the
+ *                backward's scratch); nystrom_attn_fwd_save writes only its
+ *                first nystrom_attn_bwd_state_bytes() and needs no more
+ *                (NYS_EWORKSPACE below that).  Between the two calls it must
+ *                stay untouched, and the two calls must get the same Q, K, V,
+ *                conv_w, shape, iters, conv_k and dtype; the backward may be
+ *                called more than once on one saved forward.  The buffer's
+ *                contents are the library's; its layout is not part of this
+ *                interface.
+ *   nystrom_attn_bwd_from_state  the same backward with the saved state and
+ *                the scratch in separate buffers, so that a caller keeps only
+ *                the state between the two calls: `state` as
+ *                nystrom_attn_fwd_save left it (state_bytes >=
+ *                nystrom_attn_bwd_state_bytes(), else NYS_EWORKSPACE; read
+ *                only, not written), `scratch` a DEVICE buffer of at least
+ *                nystrom_attn_bwd_workspace_bytes() - nystrom_attn_bwd_state_bytes()
+ *                bytes (NYS_EWORKSPACE below that), or NULL for the library to
+ *                allocate it on `stream`.  Results are bitwise those of
+ *                nystrom_attn_bwd_saved.
+ *   nystrom_attn_bwd_state_bytes  the state's size for the shape (either
+ *                dtype); 0 for shapes the backward does not handle.
  * Supported shapes, return codes and stream behaviour as for
  * nystrom_attn_bwd. */
+size_t nystrom_attn_bwd_state_bytes(int batch, int heads, int n, int d, int m, int iters, int conv_k);
 int nystrom_attn_fwd_save(const void* Q, const void* K, const void* V, const float* conv_w,
                           int n, int d, int m, int heads, int iters, void* out,
                           int batch, int conv_k, int dtype,
@@ -241,6 +258,12 @@ int nystrom_attn_bwd_saved(const void* Q, const void* K, const void* V, const fl
                            void* dQ, void* dK, void* dV, float* dconv_w,
                            int batch, int conv_k, int dtype,
                            void* saved, size_t saved_bytes, void* stream);
+int nystrom_attn_bwd_from_state(const void* Q, const void* K, const void* V, const float* conv_w, const void* dO,
+                                int n, int d, int m, int heads, int iters,
+                                void* dQ, void* dK, void* dV, float* dconv_w,
+                                int batch, int conv_k, int dtype,
+                                const void* state, size_t state_bytes,
+                                void* scratch, size_t scratch_bytes, void* stream);
 
 /* Full self-attention layer: the learned projections around the attention
  * ("Nyströmformer: ...", "Standard Self-Attention": Q = X W_Q, K = X W_K,

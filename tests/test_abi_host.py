@@ -173,6 +173,36 @@ def test_bwd_saved_rejects_bad_arguments_before_launch(lib, kw, code):
     assert _lib.nystrom_attn_bwd_saved(**args) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), _lib.NYS_EINVAL),                  # the forward's state must be given
+    (dict(dO=None), _lib.NYS_EINVAL),
+    (dict(conv_w=FAKE, conv_k=35), _lib.NYS_EUNSUPPORTED),
+    (dict(state_bytes=16), _lib.NYS_EWORKSPACE),
+    (dict(scratch_bytes=16), _lib.NYS_EWORKSPACE),         # a scratch buffer that is too small
+])
+def test_bwd_from_state_rejects_bad_arguments_before_launch(lib, kw, code):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, dO=FAKE, n=64, d=16, m=8, heads=1, iters=6, dQ=FAKE, dK=FAKE,
+                dV=FAKE, dconv_w=None, batch=1, conv_k=0, dtype=_lib.NYS_F32, state=FAKE, state_bytes=1 << 30,
+                scratch=FAKE, scratch_bytes=1 << 30, stream=None)
+    args.update(kw)
+    assert _lib.nystrom_attn_bwd_from_state(**args) == code
+
+
+def test_bwd_state_is_a_prefix_of_the_workspace(lib):
+    # The training pair keeps only the state; fwd_save accepts a buffer of
+    # exactly that size and rejects one byte less before launching.
+    for shape in ((1, 1, 64, 16, 8), (2, 12, 8192, 64, 64), (1, 3, 777, 32, 48)):
+        state = _lib.nystrom_attn_bwd_state_bytes(*shape, 6, 33)
+        total = _lib.nystrom_attn_bwd_workspace_bytes(*shape, 6, 33)
+        assert 0 < state < total
+        assert state > _lib.nystrom_attn_workspace_bytes(*shape)  # the forward's regions and its steps
+    assert _lib.nystrom_attn_bwd_state_bytes(1, 1, 640, 16, 80, 6, 0) == 0  # m > 64: no backward
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, conv_w=None, n=64, d=16, m=8, heads=1, iters=6, out=FAKE, batch=1, conv_k=0,
+                dtype=_lib.NYS_BF16, saved=FAKE, stream=None)
+    state = _lib.nystrom_attn_bwd_state_bytes(1, 1, 64, 16, 8, 6, 0)
+    assert _lib.nystrom_attn_fwd_save(**args, saved_bytes=state - 1) == _lib.NYS_EWORKSPACE
+
+
 def test_bwd_workspace_covers_the_forward_layout(lib):
     for shape in ((1, 1, 64, 16, 8), (2, 12, 8192, 64, 64), (1, 3, 777, 32, 48)):
         fwd = _lib.nystrom_attn_workspace_bytes(*shape)

@@ -293,6 +293,24 @@ def test_saved_forward_pair_matches_plain_calls(case):
         for x, y in zip(got, ref_grads):
             assert np.array_equal(x, y)
 
+    # The state alone (a buffer of exactly its size) and the scratch apart,
+    # given by the caller or allocated by the library: the same bits.
+    sbytes = _lib.nystrom_attn_bwd_state_bytes(B, H, n, d, m, iters, k)
+    state = torch.empty(sbytes, dtype=torch.uint8, device="cuda")
+    rc = _lib.nystrom_attn_fwd_save(Q, K, V, w, n, d, m, H, iters, O, B, k, dtype_code(dt), state, sbytes, st)
+    assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+    scratch = torch.empty(nbytes - sbytes, dtype=torch.uint8, device="cuda")
+    for sc in (scratch, None):
+        for t in (dQ, dK, dV, dW):
+            t.fill_(float("nan"))
+        rc = _lib.nystrom_attn_bwd_from_state(Q, K, V, w, G, n, d, m, H, iters, dQ, dK, dV, dW, B, k,
+                                              dtype_code(dt), state, sbytes, sc, 0 if sc is None else sc.numel(), st)
+        assert rc == _lib.NYS_OK, _lib.nystrom_strerror(rc)
+        torch.cuda.synchronize()
+        got = (to_host(dQ), to_host(dK), to_host(dV), dW.cpu().numpy())
+        for x, y in zip(got, ref_grads):
+            assert np.array_equal(x, y)
+
 
 def test_attention_train_autograd_matches_plain_backward():
     """api.attention_train under torch autograd: the output equals the plain
