@@ -80,13 +80,18 @@ __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 // Three-way split x = hi + mid + lo (each bf16; both differences are exact in
 // fp32), leaving about 2^-24 |x|: fp32-grade products from six bf16 products.
+// Pairs of elements per packed conversion (the same RNE values as one at a time).
 __device__ __forceinline__ void split8x3(const float (&x)[8], B8& hi, B8& mid, B8& lo) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    hi.h[q] = f32_to_bf16(x[q]);
-    const float r = x[q] - bf16_to_f32(hi.h[q]);
-    mid.h[q] = f32_to_bf16(r);
-    lo.h[q] = f32_to_bf16(r - bf16_to_f32(mid.h[q]));
+  for (int q = 0; q < 4; ++q) {
+    const float x0 = x[2 * q], x1 = x[2 * q + 1];
+    const uint32_t h = pack_bf16x2(x0, x1);
+    const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+    const uint32_t md = pack_bf16x2(r0, r1);
+    const float s0 = r0 - __uint_as_float(md << 16), s1 = r1 - __uint_as_float(md & 0xffff0000u);
+    hi.u[q] = h;
+    mid.u[q] = md;
+    lo.u[q] = pack_bf16x2(s0, s1);
   }
 }
 
