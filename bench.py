@@ -572,7 +572,7 @@ def layer_bench(args, wl, dev) -> int:
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
                     "algorithmic_flops": gemm_flops[dom], "avg_us": round(avg_s * 1e6, 3)}
         else:
-            ab = {"split_heads": 6 * rows * E * e, "merge_heads": 2 * rows * E * e}.get(dom) or \
+            ab = {"split_heads": 6 * rows * E * e}.get(dom) or \
                 algorithmic_bytes(wl, dom)
             if ab:
                 achieved = ab / avg_s / 1e9

@@ -155,7 +155,8 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
                                                const float* __restrict__ conv_w, const uint4* __restrict__ cwop,
                                                typename IO::T* __restrict__ out,
                                                const int* __restrict__ lens, int n, int m, int heads,
-                                               int conv_k, int ntile, long long ntotal) {
+                                               int conv_k, int ntile, long long ntotal, int out_ld,
+                                               long long out_hs, long long out_bs) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
   static_assert(NWV == 4 || !LY::STAGE, "the staged skip is laid out for 4 waves");
@@ -526,8 +527,11 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
       for (int q = 0; q < FPG; ++q) v[q] = 0.f;
     }
-    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (size_t)bh * n * D, n * D * ES);
-    const int base = (row * D + f0) * ES;
+    // Head bh's rows in `out`: out_ld elements apart; the range check ends
+    // after the last row's d elements (rows past n are dropped).
+    const __amdgpu_buffer_rsrc_t ro = head_rsrc(out + (bh / heads) * out_bs + (bh % heads) * out_hs,
+                                                ((n - 1) * out_ld + D) * ES);
+    const int base = (row * out_ld + f0) * ES;
     if constexpr (ACC) {
       // Rows past the tokens stay zero; rows past n read zero (range check).
       if (row < nb) {
@@ -711,7 +715,9 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   kern<<<grid, NTH, LY::BYTES, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.V), w ? w->kt_hi : nullptr,
                                     w ? w->kt_lo : nullptr, w ? w->wt_hi : nullptr, w ? w->wt_lo : nullptr, p.conv_w,
                                     w ? w->cwop : nullptr, static_cast<T*>(p.out), p.lens, p.n, p.m, p.heads, p.conv_k,
-                                    ntile, total);
+                                    ntile, total, p.out_merged ? p.heads * D : D,
+                                    p.out_merged ? (long long)D : (long long)p.n * D,
+                                    (long long)p.n * p.heads * D);
   return hipSuccess;
 }
 

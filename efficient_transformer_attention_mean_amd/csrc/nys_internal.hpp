@@ -53,6 +53,9 @@ struct Problem {
   // (Z_k, X_k, T1_k, T2_k as fp32 [zmp][zmp], per head and step), or none.
   float* zsave = nullptr;
   int zmp = 0;
+  // out as [batch][n][heads][d] (the heads merged per token) instead of
+  // [batch][heads][n][d].
+  bool out_merged = false;
 };
 
 // Brackets the kernel launched inside its scope with events when per-kernel

@@ -7,11 +7,13 @@
 // For a batch of sequences X [batch][n][E], E = heads * d:
 //   QKV = X [W_Q | W_K | W_V]            one library GEMM, [batch*n][3E]
 //   Q, K, V = per-head split              k_split_heads -> [batch][heads][n][d]
-//   O = Nyström attention + DConv skip    the forward kernels
-//   Y = concat_heads(O) W_O               k_merge_heads, one library GEMM
+//   O = Nyström attention + DConv skip    the forward kernels; the output
+//                                         stage writes O with the heads
+//                                         concatenated per token, [batch*n][E]
+//   Y = concat_heads(O) W_O               one library GEMM
 // The two projections are plain GEMMs and run on rocBLAS (bf16 operands with
-// fp32 accumulation for bf16 I/O, fp32 otherwise); the head split and merge
-// are 16-byte streaming copies.
+// fp32 accumulation for bf16 I/O, fp32 otherwise); the head split is a
+// 16-byte streaming copy.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -74,19 +76,6 @@ __global__ __launch_bounds__(256) void k_split_heads(const uint4* __restrict__ q
   dst[((b * heads + h) * n + i) * dv + jv] = qkv[e];
 }
 
-// O [batch][heads][n][d] -> [batch*n][heads][d]; written in destination order.
-__global__ __launch_bounds__(256) void k_merge_heads(const uint4* __restrict__ o, uint4* __restrict__ oc, int n,
-                                                     int heads, int dv, long long total) {
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int jv = (int)(e % dv);
-  long long r = e / dv;
-  const int h = (int)(r % heads);
-  const long long tok = r / heads;
-  const long long b = tok / n, i = tok % n;
-  oc[e] = o[((b * heads + h) * n + i) * dv + jv];
-}
-
 }  // namespace
 
 bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, LayerLayout* L) {
@@ -98,7 +87,7 @@ bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, Lay
     off += (bytes + 255) & ~(size_t)255;
     return o;
   };
-  L->qkv = take(3 * elems * es);  // later: O (first third) and the merged heads (second third)
+  L->qkv = take(3 * elems * es);  // later: O with the heads merged (first third)
   L->q = take(elems * es);
   L->k = take(elems * es);
   L->v = take(elems * es);
@@ -125,21 +114,17 @@ hipError_t launch_layer(const LayerProblem& lp, const LayerLayout& L, char* ws, 
         reinterpret_cast<const uint4*>(qkv), reinterpret_cast<uint4*>(ws + L.q), reinterpret_cast<uint4*>(ws + L.k),
         reinterpret_cast<uint4*>(ws + L.v), p.n, p.heads, dv, total);
   }
+  // The output stage writes the heads merged per token ([batch*n][heads*d]),
+  // the output projection's input, into the first third of the QKV region.
   Problem a = p;
   a.Q = ws + L.q;
   a.K = ws + L.k;
   a.V = ws + L.v;
-  a.out = qkv;  // O reuses the first third of the QKV region
+  a.out = qkv;
+  a.out_merged = true;
   hipError_t e = launch_forward(a, L.fwd, ws, s);
   if (e != hipSuccess) return e;
-  char* oc = qkv + elems * es;
-  {
-    const long long total = (long long)elems * es / 16;
-    KernelTimer kt_("merge_heads", s);
-    k_merge_heads<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(reinterpret_cast<const uint4*>(qkv),
-                                                                  reinterpret_cast<uint4*>(oc), p.n, p.heads, dv,
-                                                                  total);
-  }
+  char* oc = qkv;
   {
     KernelTimer kt_("out_gemm", s);
     if (!gemm_rm(h, p.bf16, rows, E, E, oc, lp.Wo, lp.Y)) return hipErrorUnknown;
