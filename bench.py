@@ -572,8 +572,7 @@ def layer_bench(args, wl, dev) -> int:
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
                     "algorithmic_flops": gemm_flops[dom], "avg_us": round(avg_s * 1e6, 3)}
         else:
-            ab = {"split_heads": 6 * rows * E * e}.get(dom) or \
-                algorithmic_bytes(wl, dom)
+            ab = {"split_heads": 6 * rows * E * e}.get(dom) or algorithmic_bytes(wl, dom)
             if ab:
                 achieved = ab / avg_s / 1e9
                 roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -91,8 +91,7 @@ __device__ __forceinline__ int vt_row(int f) {
 // registers; rows outside the head read as zero (buffer range check).  Every
 // load is unconditional, so the compiler keeps exact counts of loads in flight.
 template <typename LY>
-__device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], __amdgpu_buffer_rsrc_t rs, int t0) {
-  constexpr int D = LY::NCH * LY::FPC;
+__device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], __amdgpu_buffer_rsrc_t rs, int t0, int ld) {
   constexpr int ES = 16 / LY::FPC;
 #pragma unroll
   for (int k = 0; k < LY::NTK; ++k) {
@@ -103,7 +102,7 @@ __device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], __amdgpu_buffer_
       // Each row's offset stays in the address register: the range check
       // then sees the row itself (a row past the end inside a group of four
       // must not be reached through the instruction's immediate offset).
-      int off = ((t0 - LY::HALO + 4 * rq + q) * D + LY::FPC * oc) * ES;
+      int off = ((t0 - LY::HALO + 4 * rq + q) * ld + LY::FPC * oc) * ES;
       asm volatile("" : "+v"(off));
       vr[k][q] = buf_load16(rs, off);
     }
@@ -112,15 +111,17 @@ __device__ __forceinline__ void load_v(uint4 (&vr)[LY::NTK][4], __amdgpu_buffer_
 
 // Issues the loads of this lane's query fragments (row qrow, head-dim
 // elements 32kc + 8g .. +7 for every chunk kc); rows past the end read as zero.
+// Rows are ld elements apart.
 template <typename LY, int D>
-__device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amdgpu_buffer_rsrc_t rs, int qrow) {
+__device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amdgpu_buffer_rsrc_t rs, int qrow,
+                                       int ld) {
   constexpr int ES = 16 / LY::FPC;
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int kc = 0; kc < (D + 31) / 32; ++kc) {
     const int dd = min(kc * 32 + 8 * g, D - 8);
 #pragma unroll
-    for (int w = 0; w < LY::QW; ++w) qr[kc][w] = buf_load16(rs, (qrow * D + dd) * ES + 16 * w);
+    for (int w = 0; w < LY::QW; ++w) qr[kc][w] = buf_load16(rs, (qrow * ld + dd) * ES + 16 * w);
   }
 }
 
@@ -145,7 +146,9 @@ __device__ __forceinline__ void load_q(uint4 (&qr)[(D + 31) / 32][LY::QW], __amd
 // skip's staging the waves share only the head's planes, so when those fill
 // the LDS a block of more waves hides more latency per CU; the tile's
 // barriers are then needed only where a block moves to another head.
-template <typename IO, int D, int NTM, int KW, bool ATT, int WPE, bool ACC, int NWV = 4>
+// SIN: Q and V rows where il says (the layer's QKV product); otherwise the
+// [batch][heads][n][d] layout with its strides known at compile time.
+template <typename IO, int D, int NTM, int KW, bool ATT, int WPE, bool ACC, int NWV = 4, bool SIN = false>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE))) void k_apply(const typename IO::T* __restrict__ Qin,
                                                const typename IO::T* __restrict__ Vin,
                                                const uint16_t* __restrict__ kt_hi,
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
                                                typename IO::T* __restrict__ out,
                                                const int* __restrict__ lens, int n, int m, int heads,
                                                int conv_k, int ntile, long long ntotal, int out_ld,
-                                               long long out_hs, long long out_bs) {
+                                               long long out_hs, long long out_bs, InLayout il) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
   static_assert(NWV == 4 || !LY::STAGE, "the staged skip is laid out for 4 waves");
@@ -178,7 +181,16 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
   // Bytes of head bh's rows that hold tokens (the row pitch of a head is n
   // rows; with per-sequence lengths only the first ones are real): Q and V
   // rows past them read as zero through the range check.
-  auto token_bytes = [&](int bh) { return seq_rows(lens, bh / heads, n) * (D * ES); };
+  // Q and V: head bh's first element, and the bytes from there to the end
+  // of its last token row (rows il.ld elements apart).
+  const int ild = SIN ? il.ld : D;
+  auto in_off = [&](int bh) -> long long {
+    if constexpr (SIN) return (bh / heads) * il.bs + (bh % heads) * il.hs; else return (long long)bh * n * D;
+  };
+  auto token_bytes = [&](int bh) {
+    const int nb = seq_rows(lens, bh / heads, n);
+    if constexpr (SIN) return nb > 0 ? ((nb - 1) * il.ld + D) * ES : 0; else return nb * (D * ES);
+  };
 
   // Run of tiles of this block.
   const long long G = gridDim.x, L = blockIdx.x;
@@ -252,11 +264,11 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
     return Pos{__builtin_amdgcn_readfirstlane(q.bh), __builtin_amdgcn_readfirstlane(q.ti)};
   };
   auto issue_v = [&](Pos q, uint4 (&vr)[NTK][4]) {
-    if constexpr (LY::STAGE) load_v<LY>(vr, head_rsrc(Vin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * kTQ);
+    if constexpr (LY::STAGE) load_v<LY>(vr, head_rsrc(Vin + in_off(q.bh), token_bytes(q.bh)), q.ti * kTQ, ild);
   };
   auto issue_q = [&](Pos q, uint4 (&qr)[KC][LY::QW]) {
     if constexpr (ATT)
-      load_q<LY, D>(qr, head_rsrc(Qin + (size_t)q.bh * n * D, token_bytes(q.bh)), q.ti * TQ + 16 * wave + c);
+      load_q<LY, D>(qr, head_rsrc(Qin + in_off(q.bh), token_bytes(q.bh)), q.ti * TQ + 16 * wave + c, ild);
   };
 
   // V rows (registers) -> Vt[feature][row].
@@ -512,13 +524,13 @@ __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE)))
     }
     if constexpr (KW == -1) {
       if (row < nb) {
-        const T* Vh = Vin + (size_t)bh * n * D;
+        const T* Vh = Vin + in_off(bh);
         const int R = (conv_k - 1) / 2;
         const int tb = max(0, R - row), te = min(conv_k, nb - row + R);
         for (int q = 0; q < FPG; ++q) {
           const float* wq = conv_w + ((size_t)h * D + f0 + q) * conv_k;
           float s = 0.f;
-          for (int tt = tb; tt < te; ++tt) s = fmaf(wq[tt], load_elem<IO>(Vh + (size_t)(row + tt - R) * D + f0 + q), s);
+          for (int tt = tb; tt < te; ++tt) s = fmaf(wq[tt], load_elem<IO>(Vh + (size_t)(row + tt - R) * ild + f0 + q), s);
           v[q] += s;
         }
       }
@@ -682,8 +694,8 @@ static int multiprocessors() {
   return cus;
 }
 
-template <typename IO, int D, int NTM, int KW, bool ATT, bool ACC = false>
-static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
+template <typename IO, int D, int NTM, int KW, bool ATT, bool ACC, bool SIN>
+static hipError_t launch_one_k(const Problem& p, const Ws* w, hipStream_t s) {
   using T = typename IO::T;
   using LY = ApplyLayout<IO, D, NTM, KW, ATT>;
   // bf16 with the matrix-core skip at d <= 64, m <= 64 fits three blocks per
@@ -696,7 +708,7 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
   // for 4, 8 and 12 waves).
   constexpr int NWV = (KW == 0 && LY::KWL && LY::BYTES > 80 * 1024) ? (IO::kBf16 ? 12 : 8) : 4;
   constexpr int NTH = 64 * NWV;
-  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE, ACC, NWV>;
+  auto kern = &k_apply<IO, D, NTM, KW, ATT, WPE, ACC, NWV, SIN>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
   if (attr != hipSuccess) return attr;
@@ -717,8 +729,26 @@ static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
                                     w ? w->cwop : nullptr, static_cast<T*>(p.out), p.lens, p.n, p.m, p.heads, p.conv_k,
                                     ntile, total, p.out_merged ? p.heads * D : D,
                                     p.out_merged ? (long long)D : (long long)p.n * D,
-                                    (long long)p.n * p.heads * D);
+                                    (long long)p.n * p.heads * D, in_layout(p));
   return hipSuccess;
+}
+
+// Q, K, V read in place from another layout (in_ld > 0) are compiled for the
+// layer's common shapes only (apply_in_place); elsewhere the strides stay
+// compile-time constants.
+template <typename IO, int D, int NTM, int KW, bool ATT, bool ACC = false>
+static hipError_t launch_one(const Problem& p, const Ws* w, hipStream_t s) {
+  if (p.in_ld > 0) {
+    if constexpr (ATT && !ACC && (KW == 0 || KW == 33) && (D == 32 || D == 64) && NTM <= 4)
+      return launch_one_k<IO, D, NTM, KW, ATT, ACC, true>(p, w, s);
+    else
+      return hipErrorInvalidValue;
+  }
+  return launch_one_k<IO, D, NTM, KW, ATT, ACC, false>(p, w, s);
+}
+
+bool apply_in_place(const Problem& p) {
+  return (p.d == 32 || p.d == 64) && p.m <= 64 && (!p.conv_w || p.conv_k <= 0 || (p.conv_k > 1 && p.conv_k <= 33));
 }
 
 template <typename IO, int D, int NTM, bool ATT>

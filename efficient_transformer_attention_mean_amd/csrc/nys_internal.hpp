@@ -40,6 +40,13 @@ struct Ws {
 
 Ws resolve(const WsLayout& L, char* base);
 
+// Where an input tensor's rows are: head bh = b * heads + h starts
+// b * bs + h * hs elements in, its rows ld elements apart.
+struct InLayout {
+  int ld;
+  long long hs, bs;
+};
+
 struct Problem {
   const void* Q;
   const void* K;
@@ -56,7 +63,16 @@ struct Problem {
   // out as [batch][n][heads][d] (the heads merged per token) instead of
   // [batch][heads][n][d].
   bool out_merged = false;
+  // Q, K, V in a layout of their own (in_ld > 0: rows in_ld elements apart,
+  // heads in_hs and batch entries in_bs apart), or [batch][heads][n][d].
+  int in_ld = 0;
+  long long in_hs = 0, in_bs = 0;
 };
+
+inline InLayout in_layout(const Problem& p) {
+  if (p.in_ld > 0) return InLayout{p.in_ld, p.in_hs, p.in_bs};
+  return InLayout{p.d, (long long)p.n * p.d, (long long)p.heads * p.n * p.d};
+}
 
 // Brackets the kernel launched inside its scope with events when per-kernel
 // timing is on (nystrom_timing_enable); otherwise does nothing.
@@ -91,6 +107,9 @@ int forward_partials(const Problem& p, const Ws& w);
 hipError_t stage_apply(const Problem& p, const Ws& w, hipStream_t s);          // out
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s);
+// Whether the forward reads Q, K, V in place from a layout of their own
+// (Problem::in_ld) for this shape: d = 32 or 64, m <= 64, no skip or 3..33 taps.
+bool apply_in_place(const Problem& p);
 
 // Backward pass: the forward's workspace regions (recomputed landmark side)
 // followed by its own (byte offsets, 256-byte aligned).
@@ -143,11 +162,12 @@ hipError_t launch_backward(const BwdProblem& p, const BwdLayout& L, const BwdBuf
 hipError_t launch_forward_save(const Problem& p, const BwdLayout& L, char* ws, hipStream_t s);
 
 // Full layer (projections around the attention): the forward's regions, then
-// the fused QKV projection (reused for the attention output and the merged
-// heads) and the per-head Q, K, V.
+// the fused QKV projection, read in place by the attention, and the attention
+// output with the heads merged.
 struct LayerLayout {
   WsLayout fwd;
-  size_t qkv, q, k, v;
+  size_t qkv, o;  // the QKV product [batch*n][3E]; the attention output, heads merged
+  size_t q, k, v;  // head-major copies of Q, K, V (shapes not read in place)
   size_t total;
 };
 

@@ -36,7 +36,8 @@ namespace nys {
 // block, grid (ceil(m/4), batch*heads, 2); the lanes of a wave cover whole
 // rows, so a short segment is one round of loads and the sum needs only lane
 // shuffles (no LDS, no barrier).
-template <typename IO, int D, bool WS = false>
+// SIN: Q and K rows where il says; otherwise the [batch][heads][n][d] layout.
+template <typename IO, int D, bool WS = false, bool SIN = false>
 __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __restrict__ Q,
                                                       const typename IO::T* __restrict__ K,
                                                       float* __restrict__ Qt, float* __restrict__ Kt,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
                                                       uint16_t* __restrict__ qt_hi, uint16_t* __restrict__ qt_lo,
                                                       const int* __restrict__ lens, int heads, int n, int m,
                                                       int mpa, float sl2e, unsigned* __restrict__ sync,
-                                                      int nsync) {
+                                                      int nsync, InLayout il) {
   using T = typename IO::T;
   // The landmark pass's per-head counters start at zero (it runs after this
   // launch on the same stream).
@@ -59,7 +60,10 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
   const int nb = seq_rows(lens, bh / heads, n);
   const int seg = max(1, (nb + m - 1) / m);  // l = 1 for a sequence shorter than m (empty included)
   const int rows = max(0, min(seg, nb - j * seg));  // real rows of this segment
-  const T* X = (blockIdx.z == 0 ? Q : K) + ((size_t)bh * n + (size_t)j * seg) * D;
+  const int ild = SIN ? il.ld : D;
+  const T* X = (blockIdx.z == 0 ? Q : K) +
+               (SIN ? (bh / heads) * il.bs + (bh % heads) * il.hs + (size_t)j * seg * il.ld
+                    : ((size_t)bh * n + (size_t)j * seg) * D);
   float* out = (blockIdx.z == 0 ? Qt : Kt) + ((size_t)bh * m + j) * D;
   const int slot = threadIdx.x % SLOTS, r0 = (WS ? threadIdx.x & 63 : threadIdx.x) / SLOTS;
   float acc[VEC];
@@ -71,7 +75,7 @@ __global__ __launch_bounds__(256) void k_segment_mean(const typename IO::T* __re
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int rr = r + u * RS;
-      v[u] = rr < rows ? *reinterpret_cast<const uint4*>(X + (size_t)rr * D + slot * VEC) : make_uint4(0, 0, 0, 0);
+      v[u] = rr < rows ? *reinterpret_cast<const uint4*>(X + (size_t)rr * ild + slot * VEC) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -1138,13 +1142,14 @@ struct BvStage {
 // block of the same launch reads them).  Otherwise each group writes its own
 // chunk's partial, entry ch of nchunks, with plain stores.
 // NWC: waves per chunk (4: two chunks per 512-thread block; 8: one).
-template <typename IO, int D, int NTW, bool PAIR, int NWC = 4>
+// SIN: K and V rows where il says; otherwise the [batch][heads][n][d] layout.
+template <typename IO, int D, int NTW, bool PAIR, int NWC = 4, bool SIN = false>
 __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, int bh,
                                          const typename IO::T* __restrict__ Kin,
                                          const typename IO::T* __restrict__ Vin, const float* __restrict__ Qt,
                                          float* __restrict__ pacc, float* __restrict__ pmax,
                                          float* __restrict__ psum, int n, int nb, int m, int chunk, int nchunks,
-                                         float sl2e) {
+                                         float sl2e, const InLayout& il, int heads) {
   using T = typename IO::T;
   using SM = BvSmem<IO, D>;
   constexpr int KC = (D + 31) / 32;  // 32-wide k chunks over the head dimension
@@ -1156,8 +1161,10 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
   // Keys [kbeg, kend) of this chunk; nb <= n is the head's number of real
   // keys (chunks past it are empty and leave max -inf, sum 0).
   const int kbeg = ch * chunk, kend = min(nb, kbeg + chunk);
-  const T* Kh = Kin + (size_t)bh * n * D;
-  const T* Vh = Vin + (size_t)bh * n * D;
+  const long long hoff = SIN ? (bh / heads) * il.bs + (bh % heads) * il.hs : (long long)bh * n * D;
+  const int ild = SIN ? il.ld : D;
+  const T* Kh = Kin + hoff;
+  const T* Vh = Vin + hoff;
   const float* qt = Qt + (size_t)bh * m * D;
 
   // Landmark-query operands (B of S^T = K Qt^T), pre-multiplied by
@@ -1207,8 +1214,8 @@ __device__ __forceinline__ void bv_chunk(BvSmem<IO, D>& sm, float* xch, int ch, 
         const bool in = e < TASKS && key < kend;
 #pragma unroll
         for (int w = 0; w < BvStage<IO>::W; ++w) {
-          st[u].k[h][w] = in ? reinterpret_cast<const uint4*>(Kh + (size_t)key * D + s8)[w] : make_uint4(0, 0, 0, 0);
-          st[u].v[h][w] = in ? reinterpret_cast<const uint4*>(Vh + (size_t)key * D + s8)[w] : make_uint4(0, 0, 0, 0);
+          st[u].k[h][w] = in ? reinterpret_cast<const uint4*>(Kh + (size_t)key * ild + s8)[w] : make_uint4(0, 0, 0, 0);
+          st[u].v[h][w] = in ? reinterpret_cast<const uint4*>(Vh + (size_t)key * ild + s8)[w] : make_uint4(0, 0, 0, 0);
         }
       }
     }
@@ -1684,6 +1691,7 @@ struct LandmarkPassArgs {
   int bhn;
   int n, heads, m, chunk, nchunks, iters, npinv, nconv, conv_total, conv_k;
   float sl2e;
+  InLayout il;  // where K's and V's rows are
 };
 
 template <int PMP, int D, typename B>
@@ -1700,7 +1708,7 @@ union LandmarkPassSmem<0, D, B> {
 // PMP: landmarks padded to 32 or 64 for the pseudoinverse blocks, 0 for none.
 // CPB: key chunks per block (2: one per group of 4 waves; 1: one chunk on all
 // 8 waves, for m > 128, where 4 waves would hold too many accumulators).
-template <typename IO, int D, int NTW, int PMP, bool SAVE, int CPB = 2>
+template <typename IO, int D, int NTW, int PMP, bool SAVE, int CPB = 2, bool SIN = false>
 __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   using T = typename IO::T;
   constexpr bool FOLD = PMP > 0;  // the split-n finish runs in this launch
@@ -1736,16 +1744,16 @@ __global__ __launch_bounds__(512) void k_landmark_pass(LandmarkPassArgs a) {
   blk -= a.nconv;
   if constexpr (CPB == 1) {
     const int bh = blk / a.nchunks;
-    bv_chunk<IO, D, NTW, false, 8>(sm.b[0], nullptr, blk % a.nchunks, bh, static_cast<const T*>(a.K),
+    bv_chunk<IO, D, NTW, false, 8, SIN>(sm.b[0], nullptr, blk % a.nchunks, bh, static_cast<const T*>(a.K),
                                    static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
-                                   seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+                                   seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e, a.il, a.heads);
     return;
   }
   // Key blocks: chunks 2 j and 2 j + 1 of a head, one per group of 4 waves.
   const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 8;
-  bv_chunk<IO, D, NTW, FOLD>(sm.b[grp], reinterpret_cast<float*>(&sm), 2 * (blk % half) + grp, bh,
+  bv_chunk<IO, D, NTW, FOLD, 4, SIN>(sm.b[grp], reinterpret_cast<float*>(&sm), 2 * (blk % half) + grp, bh,
                              static_cast<const T*>(a.K), static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax,
-                             a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+                             a.psum, a.n, seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e, a.il, a.heads);
   if constexpr (FOLD) {
     static_assert(sizeof(float) * 4 * (D / 16 * 4 + 2) * 64 <= sizeof(sm), "the pair exchange fits the LDS");
     // The head's last key block to arrive combines its partials into BV,
@@ -1789,14 +1797,14 @@ __global__ __launch_bounds__(1024) void k_key_pass16(LandmarkPassArgs a) {
   const int bh = blk / a.nchunks;
   bv_chunk<IO, D, 1, false, 16>(sm, nullptr, blk % a.nchunks, bh, static_cast<const T*>(a.K),
                                 static_cast<const T*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
-                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e, a.il, a.heads);
 }
 
 // fp32 I/O, m <= 64, d <= 64: the pseudoinverse (blocks [0, npinv), one
 // head each, as k_pinv_lds) and the split-n key pass (two chunks per block,
 // 8 waves each; partial entry per chunk, combined by k_bv_finish) in one
 // launch, since the pseudoinverse needs only the landmarks.
-template <int PMP, int D>
+template <int PMP, int D, bool SIN = false>
 __global__ __launch_bounds__(64 * kPinvWaves) void k_landmark_pass_f32(LandmarkPassArgs a, float sl2e_d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   static_assert(64 * kPinvWaves == 1024, "two 8-wave chunk groups per block");
@@ -1808,9 +1816,9 @@ __global__ __launch_bounds__(64 * kPinvWaves) void k_landmark_pass_f32(LandmarkP
   blk -= a.npinv;
   const int half = a.nchunks / 2, bh = blk / half, grp = threadIdx.x >> 9;
   BvSmem<F32, D>& sm = reinterpret_cast<BvSmem<F32, D>*>(smem_raw)[grp];
-  bv_chunk<F32, D, 1, false, 8>(sm, nullptr, 2 * (blk % half) + grp, bh, static_cast<const float*>(a.K),
+  bv_chunk<F32, D, 1, false, 8, SIN>(sm, nullptr, 2 * (blk % half) + grp, bh, static_cast<const float*>(a.K),
                                 static_cast<const float*>(a.V), a.Qt, a.pacc, a.pmax, a.psum, a.n,
-                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e);
+                                seq_rows(a.lens, bh / a.heads, a.n), a.m, a.chunk, a.nchunks, a.sl2e, a.il, a.heads);
 }
 
 // Finish of the split-n pass, one block per (16-feature slice, head):
@@ -2035,21 +2043,26 @@ __global__ __launch_bounds__(1024) void k_bv_finish(const float* __restrict__ pa
 
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-template <typename IO, int D>
-static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
+template <typename IO, int D, bool SIN>
+static void seg_means_k(const Problem& p, const Ws& w, hipStream_t s) {
   using T = typename IO::T;
   const int BH = p.batch * p.heads;
   KernelTimer kt_("segment_mean", s);
   if ((p.n + p.m - 1) / p.m <= 32) {  // segments of at most 32 rows: a wave each (bert 123.3 -> 120.8 us)
-    k_segment_mean<IO, D, true><<<dim3((p.m + 3) / 4, BH, 2), 256, 0, s>>>(
+    k_segment_mean<IO, D, true, SIN><<<dim3((p.m + 3) / 4, BH, 2), 256, 0, s>>>(
         static_cast<const T*>(p.Q), static_cast<const T*>(p.K), w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo,
-        p.lens, p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D), w.sync, 2 * BH);
+        p.lens, p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D), w.sync, 2 * BH, in_layout(p));
     return;
   }
-  k_segment_mean<IO, D><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
+  k_segment_mean<IO, D, false, SIN><<<dim3(p.m, BH, 2), 256, 0, s>>>(static_cast<const T*>(p.Q), static_cast<const T*>(p.K),
                                                          w.Qt, w.Kt, w.kt_hi, w.kt_lo, w.qt_hi, w.qt_lo, p.lens,
                                                          p.heads, p.n, p.m, w.mpa, kLog2e / sqrtf((float)D),
-                                                         w.sync, 2 * BH);
+                                                         w.sync, 2 * BH, in_layout(p));
+}
+
+template <typename IO, int D>
+static void seg_means_t(const Problem& p, const Ws& w, hipStream_t s) {
+  if (p.in_ld > 0) seg_means_k<IO, D, true>(p, w, s); else seg_means_k<IO, D, false>(p, w, s);
 }
 
 hipError_t stage_segment_means(const Problem& p, const Ws& w, hipStream_t s) {
@@ -2172,6 +2185,7 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
   a.W = w.W;
   a.wt_hi = w.wt_hi;
   a.bhn = BH;
+  a.il = in_layout(p);
   KernelTimer kt_("landmark_pass", s);
   if constexpr (CPB == 1 && PMP == 0 && (IO::kBf16 || D <= 64)) {  // fp32 at d = 128 needs more registers
     a.nconv = ceil_div(a.conv_total, 1024);
@@ -2179,6 +2193,12 @@ static void landmark_pass_launch(const Problem& p, const Ws& w, hipStream_t s) {
     return;
   }
   const int grid = a.npinv + a.nconv + (CPB == 2 ? w.nchunks / 2 : w.nchunks) * BH;
+  if constexpr (PMP > 0 && CPB == 2 && (D == 32 || D == 64)) {
+    if (p.in_ld > 0) {  // K, V read in place (launch_forward admits no other shape)
+      k_landmark_pass<IO, D, NTW, PMP, false, CPB, true><<<grid, 512, 0, s>>>(a);
+      return;
+    }
+  }
   if constexpr (PMP > 0) {
     if (p.zsave) {
       k_landmark_pass<IO, D, NTW, PMP, true><<<grid, 512, 0, s>>>(a);
@@ -2213,13 +2233,20 @@ static hipError_t landmark_pass_f32_launch(const Problem& p, const Ws& w, hipStr
   a.iters = p.iters;
   a.npinv = BH;
   a.sl2e = kLog2e / sqrtf((float)D);
+  a.il = in_layout(p);
   constexpr int SMEM = sizeof(PinvSmem<PMP>) > 2 * sizeof(BvSmem<F32, D>) ? (int)sizeof(PinvSmem<PMP>)
                                                                             : (int)(2 * sizeof(BvSmem<F32, D>));
-  const hipError_t attr = ensure_dynamic_smem(reinterpret_cast<const void*>(&k_landmark_pass_f32<PMP, D>), SMEM);
-  if (attr != hipSuccess) return attr;
-  KernelTimer kt_("landmark_pass", s);
-  k_landmark_pass_f32<PMP, D><<<BH + (w.nchunks / 2) * BH, 64 * kPinvWaves, SMEM, s>>>(a, kLog2e / sqrtf((float)D));
-  return hipSuccess;
+  auto go = [&](auto kern) -> hipError_t {
+    const hipError_t attr = ensure_dynamic_smem(reinterpret_cast<const void*>(kern), SMEM);
+    if (attr != hipSuccess) return attr;
+    KernelTimer kt_("landmark_pass", s);
+    kern<<<BH + (w.nchunks / 2) * BH, 64 * kPinvWaves, SMEM, s>>>(a, kLog2e / sqrtf((float)D));
+    return hipSuccess;
+  };
+  if constexpr (D == 32 || D == 64) {
+    if (p.in_ld > 0) return go(&k_landmark_pass_f32<PMP, D, true>);  // K, V read in place
+  }
+  return go(&k_landmark_pass_f32<PMP, D, false>);
 }
 
 template <typename IO, int D>

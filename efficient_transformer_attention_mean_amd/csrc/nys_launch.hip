@@ -113,6 +113,8 @@ Ws resolve(const WsLayout& L, char* b) {
 }
 
 hipError_t launch_forward(const Problem& p, const WsLayout& L, char* ws, hipStream_t s) {
+  // strided inputs: kernels compiled for these shapes only, forward-only (no saved steps)
+  if (p.in_ld > 0 && (!apply_in_place(p) || p.zsave)) return hipErrorInvalidValue;
   const Ws w = resolve(L, ws);
   hipError_t e;
   if ((e = stage_segment_means(p, w, s)) != hipSuccess) return e;

@@ -6,14 +6,16 @@
 //
 // For a batch of sequences X [batch][n][E], E = heads * d:
 //   QKV = X [W_Q | W_K | W_V]            one library GEMM, [batch*n][3E]
-//   Q, K, V = per-head split              k_split_heads -> [batch][heads][n][d]
-//   O = Nyström attention + DConv skip    the forward kernels; the output
-//                                         stage writes O with the heads
+//   O = Nyström attention + DConv skip    the forward kernels, reading each
+//                                         head's Q, K, V in place in QKV (rows
+//                                         3E apart; d = 32 or 64, m <= 64, no
+//                                         skip or 3..33 taps, else after a
+//                                         head-major copy, k_split_heads) and
+//                                         writing O with the heads
 //                                         concatenated per token, [batch*n][E]
 //   Y = concat_heads(O) W_O               one library GEMM
 // The two projections are plain GEMMs and run on rocBLAS (bf16 operands with
-// fp32 accumulation for bf16 I/O, fp32 otherwise); the head split is a
-// 16-byte streaming copy.
+// fp32 accumulation for bf16 I/O, fp32 otherwise).
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 
@@ -58,6 +60,7 @@ bool gemm_rm(rocblas_handle h, bool bf16, int rows, int cols, int k, const void*
                          0) == rocblas_status_success;
 }
 
+
 // QKV [batch*n][3][heads][d] -> Q, K, V [batch][heads][n][d]; one 16-byte
 // vector per thread, read in source order (coalesced), written per head row.
 __global__ __launch_bounds__(256) void k_split_heads(const uint4* __restrict__ qkv, uint4* __restrict__ q,
@@ -87,8 +90,9 @@ bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, Lay
     off += (bytes + 255) & ~(size_t)255;
     return o;
   };
-  L->qkv = take(3 * elems * es);  // later: O with the heads merged (first third)
-  L->q = take(elems * es);
+  L->qkv = take(3 * elems * es);
+  L->o = take(elems * es);
+  L->q = take(elems * es);  // Q, K, V head-major, for shapes the attention cannot read in place
   L->k = take(elems * es);
   L->v = take(elems * es);
   L->total = off;
@@ -98,8 +102,7 @@ bool make_layer_layout(int batch, int heads, int n, int d, int m, bool bf16, Lay
 hipError_t launch_layer(const LayerProblem& lp, const LayerLayout& L, char* ws, hipStream_t s) {
   const Problem& p = lp.attn;
   const int E = p.heads * p.d, rows = p.batch * p.n;
-  const size_t es = p.bf16 ? 2 : 4, elems = (size_t)rows * E;
-  const int dv = (int)(p.d * es / 16);
+  const size_t es = p.bf16 ? 2 : 4;
   rocblas_handle h = handle_for_current_device(s);
   if (!h) return hipErrorUnknown;
   char* qkv = ws + L.qkv;
@@ -107,24 +110,34 @@ hipError_t launch_layer(const LayerProblem& lp, const LayerLayout& L, char* ws, 
     KernelTimer kt_("qkv_gemm", s);
     if (!gemm_rm(h, p.bf16, rows, 3 * E, E, lp.X, lp.Wqkv, qkv)) return hipErrorUnknown;
   }
-  {
-    const long long total = 3 * (long long)elems * es / 16;
+  // The attention reads each head's Q, K and V where the product left them:
+  // token rows 3E elements apart, head h at column h*d of its block.  The
+  // output stage writes the heads merged per token ([batch*n][E]), the output
+  // projection's input.
+  Problem a = p;
+  if (apply_in_place(p)) {
+    a.Q = qkv;
+    a.K = qkv + (size_t)E * es;
+    a.V = qkv + (size_t)2 * E * es;
+    a.in_ld = 3 * E;
+    a.in_hs = p.d;
+    a.in_bs = (long long)p.n * 3 * E;
+  } else {
+    // Other shapes: Q, K, V copied out head-major first.
+    const long long total = 3LL * rows * E * (long long)es / 16;
     KernelTimer kt_("split_heads", s);
     k_split_heads<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
         reinterpret_cast<const uint4*>(qkv), reinterpret_cast<uint4*>(ws + L.q), reinterpret_cast<uint4*>(ws + L.k),
-        reinterpret_cast<uint4*>(ws + L.v), p.n, p.heads, dv, total);
+        reinterpret_cast<uint4*>(ws + L.v), p.n, p.heads, (int)(p.d * es / 16), total);
+    a.Q = ws + L.q;
+    a.K = ws + L.k;
+    a.V = ws + L.v;
   }
-  // The output stage writes the heads merged per token ([batch*n][heads*d]),
-  // the output projection's input, into the first third of the QKV region.
-  Problem a = p;
-  a.Q = ws + L.q;
-  a.K = ws + L.k;
-  a.V = ws + L.v;
-  a.out = qkv;
+  char* oc = ws + L.o;
+  a.out = oc;
   a.out_merged = true;
   hipError_t e = launch_forward(a, L.fwd, ws, s);
   if (e != hipSuccess) return e;
-  char* oc = qkv;
   {
     KernelTimer kt_("out_gemm", s);
     if (!gemm_rm(h, p.bf16, rows, E, E, oc, lp.Wo, lp.Y)) return hipErrorUnknown;
