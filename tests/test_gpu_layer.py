@@ -65,6 +65,8 @@ CASES = [
     (2, 256, 4, 64, 64, 6, 33, "f32"),
     (8, 512, 12, 64, 64, 6, 33, "bf16"),   # BERT-base-shaped layer
     (1, 300, 2, 128, 32, 6, 0, "bf16"),    # d = 128, no skip
+    (2, 300, 3, 64, 64, 6, 33, "bf16"),    # Q, K, V read in place, ragged n (5-row segments, 60-row tail)
+    (1, 512, 2, 64, 128, 6, 33, "bf16"),   # m > 64: heads copied out of the QKV product first
 ]
 
 
