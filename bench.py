@@ -758,6 +758,51 @@ def backward_bench(args, wl, dev) -> int:
         "note": "nystrom_attn_bwd_saved after nystrom_attn_fwd_save: the forward's landmark-side state is reused, "
                 "not recomputed",
     }
+
+    # A whole training step's attention work, both ways: the plain forward
+    # then the backward that recomputes the landmark side, against the saving
+    # forward (its pseudoinverse also stores every step) then the backward
+    # from that state.
+    outs = [torch.empty_like(b[0]) for b in bufs]
+    fws_bytes = _lib.nystrom_attn_workspace_bytes(wl.batch, wl.heads, wl.n, wl.d, wl.m)
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
+
+    def step_plain_pair(i):
+        Q, K, V, G, W, dQ, dK, dV, dW = bufs[i % sets]
+        rc = _lib.nystrom_attn_fwd(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, outs[i % sets], wl.batch,
+                                   conv_k, code, fws, fws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+        step(i)
+
+    def step_saved_pair(i):
+        Q, K, V, G, W, dQ, dK, dV, dW = bufs[i % sets]
+        rc = _lib.nystrom_attn_fwd_save(Q, K, V, W, wl.n, wl.d, wl.m, wl.heads, wl.iters, outs[i % sets],
+                                        wl.batch, conv_k, code, saved[i % sets], ws_bytes, stream)
+        if rc != 0:
+            raise RuntimeError(_lib.nystrom_strerror(rc))
+        step_saved(i)
+
+    def time_steps(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps
+
+    plain_ms = time_steps(step_plain_pair)
+    saved_ms = time_steps(step_saved_pair)
+    result["training_step"] = {
+        "fwd_then_bwd_ms": round(plain_ms, 5),
+        "fwd_save_then_bwd_saved_ms": round(saved_ms, 5),
+        "note": "one forward and one backward per step over the same input rotation: nystrom_attn_fwd + "
+                "nystrom_attn_bwd (landmark side recomputed) against nystrom_attn_fwd_save + "
+                "nystrom_attn_bwd_saved (landmark side and pseudoinverse steps kept)",
+    }
     del saved
     if not args.no_cpu_baseline or not args.no_parity:
         from oracle import nystrom_attention_backward
